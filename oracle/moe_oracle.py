@@ -1,0 +1,357 @@
+"""Plain CPU oracle of one mixture-of-experts (MoE) layer's hot path on one GPU.
+
+TEST INFRASTRUCTURE. This module is the slow, obviously correct reference that
+the HIP path is checked against. Only the test suite, the package smoke check
+and the benchmark's CPU-baseline leg may import it; the product path never
+does, and this module imports nothing from the HIP package.
+
+What is computed, in the pages' own order (sources are cited per function):
+
+  1. router logits, one fp32 score per (token, expert);
+  2. top-k expert choice per token and the k gate weights;
+  3. expert capacity C and the stable token-order slot of every routed copy,
+     with copies beyond C dropped;
+  4. the fixed-capacity per-expert buckets (and their view as P contiguous
+     per-rank send buffers);
+  5. each expert's SwiGLU MLP on the copies it keeps;
+  6. the combine: the inverse permutation, gate-weighted and summed onto the
+     residual, with fully dropped tokens passed through unchanged;
+  7. routing statistics.
+
+All floating point here is fp64 (numpy), from the exact values of the inputs;
+results are rounded once to the precision the path fixes (fp32 for logits and
+gates, the input dtype for the layer output). Where the pages leave a step
+open, the reading taken is stated in the function's docstring.
+
+Page keys used in citations:
+  [EP-glossary]   "Expert Parallelism", klaylearn.com glossary
+  [EP-inferensys] "Expert Parallelism", inferensys.com glossary
+  [EP-guide]      "Expert Parallelism", infra.bea.ai guide
+  [EP-A2A]        "Expert Parallelism & All-to-All", neelmishra.github.io
+  [EP-vs-TP]      "Expert parallelism vs tensor parallelism for MoE", fanout.sh
+
+Parity status: every function below is pinned by the CPU test suite (brute
+force on tiny inputs, closed forms, invariants and the printed bandwidth table
+of [EP-A2A]); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_to_f64", "f64_to_bf16_bits", "f64_to_f32", "encode", "silu",
+    "decode", "capacity", "router_logits", "topk_experts", "gate_weights",
+    "assign_slots", "dispatch_buckets", "send_counts", "expert_mlp",
+    "combine", "routing_stats", "dispatch_bytes", "layer_forward",
+]
+
+
+# ---------------------------------------------------------------------------
+# number formats (bf16 is the top half of an IEEE binary32 word)
+# ---------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns (uint16/int16) as float64."""
+    u = np.asarray(bits).view(np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def f64_to_f32(v: np.ndarray) -> np.ndarray:
+    """Round float64 to float32, nearest-even (numpy's cast is IEEE RNE)."""
+    return np.asarray(v, dtype=np.float64).astype(np.float32)
+
+
+def f64_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """Round float64 to bf16 bit patterns, nearest-even, in one step.
+
+    A value is rounded straight from fp64 (not via fp32, which could round
+    twice): its significand is scaled so one bf16 ulp is 1, rounded half to
+    even, and scaled back. Normal bf16 range only (no overflow or subnormals
+    arise in this layer's outputs).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    # bf16 has 8 significant bits; scale each value's ulp to 1 and use RNE.
+    with np.errstate(divide="ignore", invalid="ignore"):
+        m, e = np.frexp(v)                         # v = m * 2**e, 0.5 <= |m| < 1
+        r = np.ldexp(np.round(np.ldexp(m, 8)), e - 8)   # np.round is half-to-even
+    r = np.where(v == 0.0, v, r)                   # keep the sign of zero
+    f = r.astype(np.float32)                       # exact: r has <= 8 significant bits
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def decode(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Inputs as float64: bf16 arrays arrive as raw 16-bit patterns."""
+    if dtype == "bf16":
+        return bf16_bits_to_f64(a)
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def encode(v64: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 results once to the layer's dtype (bf16 as bit patterns)."""
+    if dtype == "bf16":
+        return f64_to_bf16_bits(v64)
+    return f64_to_f32(v64)
+
+
+# ---------------------------------------------------------------------------
+# 1. router logits
+# ---------------------------------------------------------------------------
+
+def router_logits(x64: np.ndarray, wr64: np.ndarray, bias=None) -> np.ndarray:
+    """Router scores: one linear score per (token, expert), fp32 result.
+
+    [EP-glossary] body and [EP-inferensys] gating-network entry: the router is a
+    small (typically linear) network scoring each token against every expert.
+    logits[t, e] = sum_i x[t, i] * Wr[e, i] + b[e], with Wr stored [E, d] as an
+    [out, in] linear layer. The sum is taken in fp64 and rounded once to fp32.
+    The bias b (fp32, optional) is added before rounding; it is part of the
+    score used both for the choice and for the gates.
+    """
+    s = x64 @ wr64.T
+    if bias is not None:
+        s = s + np.asarray(bias, dtype=np.float32).astype(np.float64)[None, :]
+    return f64_to_f32(s)
+
+
+# ---------------------------------------------------------------------------
+# 2. top-k choice and gate weights
+# ---------------------------------------------------------------------------
+
+def topk_experts(logits32: np.ndarray, k: int) -> np.ndarray:
+    """Per token, the k experts with the highest scores, best first.
+
+    [EP-inferensys] gating-network entry (top-k gating) and [EP-guide] section 2
+    (the router assigns each token its top-k experts). Ties are not settled on
+    the pages; the reading taken: order by score descending, then expert index
+    ascending, so the lowest index wins a tie. +0.0 and -0.0 compare equal.
+    """
+    l = np.asarray(logits32, dtype=np.float32) + np.float32(0.0)  # -0.0 -> +0.0
+    T, E = l.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    # stable sort of -score: equal scores keep ascending expert order
+    order = np.argsort(-l, axis=1, kind="stable")
+    return order[:, :k].astype(np.int32)
+
+
+def gate_weights(logits32: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Gate weights of the k chosen experts: a softmax over their scores.
+
+    [EP-glossary] body and [EP-A2A] "All-to-all: the distributed transpose": the
+    router also yields the weights that combine a token's k expert outputs. The
+    pages give no formula; the reading taken is the softmax over the k chosen
+    fp32 scores, w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), in fp64 and
+    rounded once to fp32.
+    """
+    l = np.take_along_axis(np.asarray(logits32, np.float32), idx, axis=1).astype(np.float64)
+    z = np.exp(l - l[:, :1])
+    return f64_to_f32(z / z.sum(axis=1, keepdims=True))
+
+
+# ---------------------------------------------------------------------------
+# 3. capacity and slots
+# ---------------------------------------------------------------------------
+
+def capacity(T: int, E: int, k: int, cf: float) -> int:
+    """Expert capacity C = ceil(cf * k * T / E).
+
+    [EP-inferensys] capacity entry and [EP-A2A] "Why fixed-size buffers matter
+    here": the per-expert buffer holds cf * k * T / E tokens. ([EP-guide]
+    section 4 writes it without k; the k form is taken.) Rounding is not
+    stated; the reading taken is ceil, evaluated in IEEE double as
+    ((cf * k) * T) / E with cf the fp32 value the caller passes. No clamp.
+    """
+    cf64 = float(np.float32(cf))
+    if T < 0 or E < 1 or k < 1 or not (cf64 > 0.0) or not math.isfinite(cf64):
+        raise ValueError("bad capacity arguments")
+    return int(math.ceil(cf64 * k * T / E))
+
+
+def assign_slots(idx: np.ndarray, E: int, C: int):
+    """Stable token-order slots, drops and the inverse map.
+
+    [EP-inferensys] capacity entry: an expert processes at most C tokens and the
+    excess is dropped. Priority among an expert's tokens is not stated; the
+    reading taken is token order over the flattened copies i = t*k + j: copy i
+    of expert e gets slot s = #{i' < i : expert(i') = e}; it is kept iff s < C.
+
+    Returns slot[T, k] (-1 = dropped), src[E*C] (flattened copy id held by each
+    kept slot, -1 on padding), routed[E] and kept[E] (int32/int64 counts).
+    """
+    T, k = idx.shape
+    flat = idx.reshape(-1).astype(np.int64)
+    n = flat.size
+    order = np.argsort(flat, kind="stable")            # groups by expert, token order inside
+    routed = np.bincount(flat, minlength=E).astype(np.int64)
+    start = np.concatenate(([0], np.cumsum(routed)[:-1]))
+    rank = np.empty(n, dtype=np.int64)
+    rank[order] = np.arange(n, dtype=np.int64) - start[flat[order]]
+    keep = rank < C
+    slot = np.where(keep, rank, -1).astype(np.int32).reshape(T, k)
+    src = np.full(E * C, -1, dtype=np.int32)
+    ids = np.nonzero(keep)[0]
+    src[flat[ids] * C + rank[ids]] = ids.astype(np.int32)
+    kept = np.minimum(routed, C)
+    return slot, src, routed, kept
+
+
+# ---------------------------------------------------------------------------
+# 4. buckets and per-rank send buffers
+# ---------------------------------------------------------------------------
+
+def dispatch_buckets(x: np.ndarray, idx: np.ndarray, slot: np.ndarray, E: int, C: int) -> np.ndarray:
+    """Fixed-capacity per-expert buffers [E, C, d] holding bit copies of x rows.
+
+    [EP-inferensys] memory entry (pre-allocated contiguous buffers of maximum
+    capacity) and [EP-A2A] "Why fixed-size buffers matter here" (per-expert
+    buffer of C rows; underflow is padding). Kept copy (t, j) lands at
+    [idx[t, j], slot[t, j]]. Padding rows are zero here and carry no meaning.
+    """
+    T, k = idx.shape
+    out = np.zeros((E, C) + x.shape[1:], dtype=x.dtype)
+    for j in range(k):
+        kept = slot[:, j] >= 0
+        t = np.nonzero(kept)[0]
+        out[idx[t, j], slot[t, j]] = x[t]
+    return out
+
+
+def send_counts(kept: np.ndarray, P: int) -> np.ndarray:
+    """Valid rows per destination rank when E experts sit on P ranks.
+
+    [EP-A2A] "Why MoE forces a new axis": each of P devices owns E/P whole
+    experts. Reading taken: rank p owns the contiguous experts
+    [p*E/P, (p+1)*E/P), so its send buffer is a contiguous slice of the
+    buckets.
+    """
+    E = kept.size
+    if P < 1 or E % P:
+        raise ValueError("E must be a multiple of P")
+    return kept.reshape(P, E // P).sum(axis=1).astype(np.int64)
+
+
+def dispatch_bytes(T: int, k: int, d: int, P: int, elem_bytes: int = 2) -> float:
+    """Bytes one rank sends in one dispatch under balanced routing.
+
+    [EP-A2A] "The bandwidth bill": each rank sends the (P-1)/P fraction of its
+    T*k routed copies off-rank, each a d-wide row. (The formula itself is lost
+    from the page's text; this is the form its table follows.)
+    """
+    return (P - 1) / P * T * k * d * elem_bytes
+
+
+# ---------------------------------------------------------------------------
+# 5. experts
+# ---------------------------------------------------------------------------
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    return z / (1.0 + np.exp(-z))
+
+
+def expert_mlp(X: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
+    """One expert's SwiGLU MLP applied to each row of X (fp64).
+
+    [EP-guide] section 1 (three weight matrices per expert) and [EP-A2A] "Tensor
+    parallelism for experts" (gate, up and down projections). Reading taken:
+    SwiGLU with no biases, Wg/Wu stored [d_ff, d] and Wd [d, d_ff] as
+    [out, in] linear layers: y = Wd (silu(Wg x) * (Wu x)). Each row is
+    independent; the matrix product just applies this to every row.
+    """
+    g = X @ wg.T
+    u = X @ wu.T
+    return (silu(g) * u) @ wd.T
+
+
+# ---------------------------------------------------------------------------
+# 6. combine
+# ---------------------------------------------------------------------------
+
+def combine(x64: np.ndarray, y_copies: np.ndarray, w: np.ndarray, slot: np.ndarray) -> np.ndarray:
+    """Weighted sum of each token's kept expert outputs onto the residual (fp64).
+
+    [EP-A2A] "All-to-all: the distributed transpose": the combine is the exact
+    inverse of the dispatch; a token's k outputs are weighted by their gates
+    and added to the residual stream. [EP-inferensys] capacity entry: a dropped
+    copy contributes nothing (no renormalisation of the remaining gates).
+    y_copies[t, j] is the output of copy (t, j) (any value where dropped).
+    out[t] = x[t] + sum_j [slot[t, j] >= 0] * w[t, j] * y_copies[t, j].
+    """
+    keep = (slot >= 0).astype(np.float64) * w.astype(np.float64)
+    return x64 + np.einsum("tj,tjd->td", keep, y_copies)
+
+
+# ---------------------------------------------------------------------------
+# 7. statistics
+# ---------------------------------------------------------------------------
+
+def routing_stats(slot: np.ndarray, routed: np.ndarray, kept: np.ndarray, C: int, P: int,
+                  d: int, elem_bytes: int) -> dict:
+    """Counts the pages use to talk about balance and traffic.
+
+    [EP-inferensys] capacity entry (drop rate), [EP-vs-TP] "Decide from expert
+    shape, batch, and fabric" (routed tokens per expert), [EP-A2A] "The
+    bandwidth bill" (off-rank bytes). Rank 0 is taken as the sending rank.
+    """
+    T, k = slot.shape
+    E = routed.size
+    sc = send_counts(kept, P)
+    n_kept = int(kept.sum())
+    return {
+        "routed": routed.astype(np.int64),
+        "kept": kept.astype(np.int64),
+        "send_count": sc,
+        "dropped": T * k - n_kept,
+        "fully_dropped_tokens": int(np.all(slot < 0, axis=1).sum()) if k else 0,
+        "padded_rows": E * C - n_kept,
+        "offrank_bytes": int(sc[1:].sum()) * d * elem_bytes,
+    }
+
+
+# ---------------------------------------------------------------------------
+# the whole layer
+# ---------------------------------------------------------------------------
+
+def layer_forward(x, wr, expert_weights, T, d, d_ff, E, k, cf, dtype, P=1, bias=None,
+                  tokens=None):
+    """The layer as the plain per-token definition, steps 1 to 7 above.
+
+    x [T, d] and wr [E, d] are the inputs (bf16 as bit patterns, or fp32).
+    expert_weights(e) returns (Wg [d_ff, d], Wu [d_ff, d], Wd [d, d_ff]) of
+    expert e in the same format, so a caller can supply them lazily.
+    Routing, slots and statistics are computed for all T tokens; the layer
+    output only for `tokens` (all when None), since each output row depends
+    only on its own token once the slots are known.
+
+    Returns a dict: logits, idx, w, C, slot, src, routed, kept, stats,
+    tokens, out64 (fp64, unrounded), out (rounded once to dtype; a token with
+    every copy dropped is a bit copy of its input row).
+    """
+    x = np.asarray(x)
+    x64 = decode(x, dtype)
+    logits = router_logits(x64, decode(wr, dtype), bias)
+    idx = topk_experts(logits, k)
+    w = gate_weights(logits, idx)
+    C = capacity(T, E, k, cf)
+    slot, src, routed, kept = assign_slots(idx, E, C)
+    eb = 2 if dtype == "bf16" else 4
+    stats = routing_stats(slot, routed, kept, C, P, d, eb)
+
+    tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    y = np.zeros((tok.size, k, d), dtype=np.float64)
+    sub_idx, sub_slot = idx[tok], slot[tok]
+    for e in np.unique(sub_idx[sub_slot >= 0]):
+        rows, js = np.nonzero((sub_idx == e) & (sub_slot >= 0))
+        wg, wu, wd = (decode(a, dtype) for a in expert_weights(int(e)))
+        y[rows, js] = expert_mlp(x64[tok[rows]], wg, wu, wd)
+    out64 = combine(x64[tok], y, w[tok], sub_slot)
+    out = encode(out64, dtype)
+    passthru = np.all(sub_slot < 0, axis=1)
+    out[passthru] = x[tok[passthru]]
+    return {"logits": logits, "idx": idx, "w": w, "C": C, "slot": slot, "src": src,
+            "routed": routed, "kept": kept, "stats": stats, "tokens": tok,
+            "out64": out64, "out": out}
