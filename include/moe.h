@@ -1,0 +1,181 @@
+/*
+ * moe.h - C ABI of the single-GPU mixture-of-experts (MoE) layer hot path on
+ * MI355X (gfx950): top-k router, capacity-bounded permutation into per-expert
+ * buckets (viewable as P per-rank send buffers), SwiGLU experts as a grouped
+ * GEMM, and the gate-weighted inverse permutation (combine).
+ *
+ * Sources (pages, cited by title and section):
+ *   [EP-glossary]   "Expert Parallelism" (klaylearn.com glossary): router scores,
+ *                   top-k choice and combine weights; permute, run local experts
+ *                   on buckets, restore order and weight.
+ *   [EP-inferensys] "Expert Parallelism" (inferensys.com glossary): top-k gating;
+ *                   expert capacity = cf * k * T / E; overflowing tokens dropped
+ *                   and passed through unchanged; pre-allocated contiguous
+ *                   buffers of maximum capacity.
+ *   [EP-guide]      "Expert Parallelism" (infra.bea.ai guide), section 2 "The
+ *                   Dispatch Pattern": router -> dispatch -> local experts ->
+ *                   combine -> weighted sum.
+ *   [EP-A2A]        "Expert Parallelism & All-to-All" (neelmishra.github.io):
+ *                   "All-to-all: the distributed transpose" (combine is the exact
+ *                   inverse permutation; gate-weighted sum into the residual),
+ *                   "Why fixed-size buffers matter here" (C = cf * k * T / E;
+ *                   drops on overflow, padding on underflow), "Why MoE forces a
+ *                   new axis" (E/P whole experts per device).
+ *
+ * Conventions for every entry point:
+ *  - Every array argument is a caller-owned, contiguous, row-major DEVICE
+ *    pointer unless stated otherwise. The library never allocates, frees or
+ *    keeps memory between calls; scratch memory is the caller's `workspace`.
+ *  - bf16 arrays hold IEEE bfloat16 bit patterns; fp32 arrays hold IEEE binary32.
+ *    `dtype` selects the element type of x, weights, buckets, h, y and out;
+ *    logits, gates are always fp32, indices and counts int32, totals int64.
+ *  - Weight layouts are [out, in]: W_router [E, d], W_gate and W_up [E, d_ff, d],
+ *    W_down [E, d, d_ff].
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    is asynchronous: outputs are valid once the caller synchronises the stream.
+ *    No call synchronises or copies device memory to the host.
+ *  - Argument errors are detected on the host before any HIP call, and then no
+ *    output is touched. A HIP launch failure returns MOE_ERR_HIP; its message
+ *    is available from moe_last_error() on the same thread.
+ *  - T == 0 returns MOE_OK and enqueues nothing. Capacity overflow is not an
+ *    error: it drops copies. Inputs must be finite (NaN/Inf give unspecified
+ *    routing).
+ *  - Limits (else MOE_ERR_UNSUPPORTED): d and d_ff multiples of 8 (fp32: of 4),
+ *    E <= 4096, k <= 32, T * k < 2^31, E * C < 2^31.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,
+  MOE_ERR_UNSUPPORTED = -2,
+  MOE_ERR_WORKSPACE = -3,
+  MOE_ERR_HIP = -4
+} moe_status_t;
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
+
+/* Indices into moe_stats_t.totals. */
+enum {
+  MOE_TOTAL_DROPPED = 0,        /* k*T - sum(kept): copies dropped on overflow */
+  MOE_TOTAL_FULLY_DROPPED = 1,  /* tokens whose k copies were all dropped */
+  MOE_TOTAL_PADDED_ROWS = 2,    /* E*C - sum(kept): unused bucket rows */
+  MOE_TOTAL_OFFRANK_BYTES = 3,  /* sum over p != 0 of send_count[p] * d * elem bytes */
+  MOE_NUM_TOTALS = 4
+};
+
+/* Optional outputs of moe_layer_forward. Each pointer is caller-owned device
+ * memory of the size given, or NULL, in which case the layer keeps that array
+ * in the workspace. */
+typedef struct {
+  int32_t* topk_idx;     /* [T, k] chosen experts, best first */
+  float* topk_w;         /* [T, k] gate weights */
+  int32_t* slot;         /* [T, k] row in the expert's bucket, -1 = dropped */
+  int32_t* src;          /* [E, C] copy id t*k+j held by each bucket row, -1 = padding */
+  int32_t* routed_count; /* [E] copies routed to each expert */
+  int32_t* kept_count;   /* [E] min(routed, C) */
+  int32_t* send_count;   /* [P] kept rows in each rank's send buffer */
+  int64_t* totals;       /* [MOE_NUM_TOTALS] */
+  void* buckets;         /* [E, C, d] dtype; rank p's send buffer is experts
+                            [p*E/P, (p+1)*E/P), a contiguous slice */
+} moe_stats_t;
+
+/* Expert capacity C = ceil(cf * k * T / E), evaluated in IEEE double as
+ * ((cf * k) * T) / E ([EP-inferensys] capacity entry; [EP-A2A] "Why
+ * fixed-size buffers matter here"). Host only; touches no device state.
+ * Errors: T < 0, E < 1, k < 1, cf not finite or <= 0, NULL C_out. */
+int moe_capacity(int64_t T, int32_t E, int32_t k, float cf, int64_t* C_out);
+
+/* Bytes of workspace moe_layer_forward needs for these sizes (host only). */
+int moe_workspace_size(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k, float cf,
+                       int32_t P, moe_dtype_t dtype, size_t* bytes);
+
+/* The whole layer ([EP-guide] section 2; [EP-glossary]):
+ *   logits = x W_router^T (+ router_bias)                      fp32 [T, E]
+ *   topk_idx, topk_w = top-k of logits (ties: lower index first), softmax of
+ *                      the k chosen logits
+ *   C = moe_capacity(T, E, k, cf); slot = stable token-order rank of each copy
+ *   among its expert's copies, dropped (-1) if >= C
+ *   buckets[e, s] = x[t] for each kept copy (t, j) of expert e at slot s
+ *   h = silu(X_e W_gate[e]^T) * (X_e W_up[e]^T);  y = h W_down[e]^T  (rows < kept)
+ *   out[t] = x[t] + sum_j [slot >= 0] topk_w[t,j] * y[idx[t,j], slot[t,j]];
+ *   a token with every copy dropped is copied through bit for bit.
+ * x [T, d], out [T, d] (must not overlap x), router_bias [E] fp32 or NULL,
+ * P >= 1 with E % P == 0 (send-buffer view only; no communication).
+ * stats may be NULL. workspace must hold moe_workspace_size() bytes, 256-byte
+ * aligned. */
+int moe_layer_forward(const void* x, const void* W_router, const float* router_bias,
+                      const void* W_gate, const void* W_up, const void* W_down,
+                      int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k, float cf,
+                      int32_t P, moe_dtype_t dtype, void* out, moe_stats_t* stats,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Router stage ([EP-inferensys] gating-network entry): logits on the matrix
+ * cores, then top-k and gates as in moe_route. logits_out [T, E] fp32 may be
+ * NULL; otherwise it receives the scores. workspace needs T*E*4 bytes when
+ * logits_out is NULL, else may be NULL. */
+int moe_router(const void* x, const void* W_router, const float* router_bias, int64_t T,
+               int64_t d, int32_t E, int32_t k, moe_dtype_t dtype, int32_t* topk_idx,
+               float* topk_w, float* logits_out, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/* Top-k and gates from given fp32 logits [T, E]: per token the k experts in
+ * order of score descending, then index ascending (+0 == -0); gates
+ * w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), evaluated in fp64, rounded to
+ * fp32. */
+int moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_idx,
+              float* topk_w, void* stream);
+
+/* Permutation stage ([EP-inferensys] capacity and memory entries; [EP-A2A]
+ * "Why fixed-size buffers matter here"): from topk_idx [T, k] computes
+ * routed/kept counts, slot [T, k], src [E, C], buckets [E, C, d] (kept rows
+ * only; padding rows are not written), send_count [P] and totals. C is given
+ * (normally moe_capacity()). Any of src, send_count, totals may be NULL.
+ * workspace: moe_permute_workspace_size() bytes. */
+int moe_permute_workspace_size(int64_t T, int32_t E, size_t* bytes);
+int moe_permute(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, int32_t E,
+                int32_t k, int64_t C, int32_t P, moe_dtype_t dtype, void* buckets,
+                int32_t* slot, int32_t* src, int32_t* routed_count, int32_t* kept_count,
+                int32_t* send_count, int64_t* totals, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* Expert stage ([EP-guide] section 1, three matrices per expert; [EP-A2A]
+ * "Tensor parallelism for experts", gate/up/down): for every expert e and
+ * bucket row s < kept_count[e]:
+ *   h[e, s] = silu(buckets[e, s] W_gate[e]^T) * (buckets[e, s] W_up[e]^T)
+ *   y[e, s] = h[e, s] W_down[e]^T
+ * Rows >= kept_count[e] are neither read for results nor written. bf16 runs
+ * on the matrix cores with fp32 accumulation, h and y rounded to bf16.
+ * workspace: moe_grouped_gemm_workspace_size() bytes. */
+int moe_grouped_gemm_workspace_size(int32_t E, int64_t C, size_t* bytes);
+int moe_grouped_gemm(const void* buckets, const int32_t* kept_count, const void* W_gate,
+                     const void* W_up, const void* W_down, int32_t E, int64_t C, int64_t d,
+                     int64_t d_ff, moe_dtype_t dtype, void* h, void* y, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Combine stage ([EP-A2A] "All-to-all: the distributed transpose"):
+ *   out[t] = x[t] + sum_j [slot[t,j] >= 0] topk_w[t,j] * y[topk_idx[t,j], slot[t,j]]
+ * summed in fp32 over j ascending and rounded once; tokens with every slot -1
+ * are copied bit for bit ([EP-inferensys] capacity entry). y is [E, C, d]. */
+int moe_combine(const void* x, const void* y, const int32_t* topk_idx, const float* topk_w,
+                const int32_t* slot, int64_t T, int64_t d, int32_t E, int32_t k, int64_t C,
+                moe_dtype_t dtype, void* out, void* stream);
+
+/* Static description of a status code. */
+const char* moe_status_string(int status);
+
+/* Message of the last MOE_ERR_HIP (or argument error) on the calling thread. */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

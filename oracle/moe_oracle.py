@@ -43,7 +43,7 @@ import numpy as np
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "f64_to_f32", "encode", "silu",
     "decode", "capacity", "router_logits", "topk_experts", "gate_weights",
-    "assign_slots", "dispatch_buckets", "send_counts", "expert_mlp",
+    "assign_slots", "dispatch_buckets", "send_counts", "expert_hidden", "expert_mlp",
     "combine", "routing_stats", "dispatch_bytes", "layer_forward",
 ]
 
@@ -253,6 +253,13 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
+def expert_hidden(X: np.ndarray, wg: np.ndarray, wu: np.ndarray) -> np.ndarray:
+    """The gated hidden activation of one expert: h = silu(Wg x) * (Wu x), per row."""
+    g = X @ wg.T
+    u = X @ wu.T
+    return silu(g) * u
+
+
 def expert_mlp(X: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
     """One expert's SwiGLU MLP applied to each row of X (fp64).
 
@@ -262,9 +269,7 @@ def expert_mlp(X: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) ->
     [out, in] linear layers: y = Wd (silu(Wg x) * (Wu x)). Each row is
     independent; the matrix product just applies this to every row.
     """
-    g = X @ wg.T
-    u = X @ wu.T
-    return (silu(g) * u) @ wd.T
+    return expert_hidden(X, wg, wu) @ wd.T
 
 
 # ---------------------------------------------------------------------------

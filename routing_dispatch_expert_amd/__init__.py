@@ -1,0 +1,251 @@
+"""Python binding of libmoe_hip.so, the MI355X (gfx950) MoE-layer hot path.
+
+Thin ctypes marshalling over the C ABI in include/moe.h: every function below
+has the C entry point's name and argument order, turns torch tensors (device
+memory), ints and None into pointers and sizes, and raises MoeError on a
+non-zero status. All computation happens in the HIP library; torch provides
+device memory and streams only. There is no fallback: if the library is not
+built, loading fails with an error that says so.
+
+`forward()` is a convenience on top: it allocates outputs and the workspace
+with torch and calls moe_layer_forward once.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_hip.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
+TOTALS = ("dropped", "fully_dropped_tokens", "padded_rows", "offrank_bytes")
+
+EXPORTS = ("moe_capacity", "moe_workspace_size", "moe_layer_forward", "moe_router", "moe_route",
+           "moe_permute_workspace_size", "moe_permute", "moe_grouped_gemm_workspace_size",
+           "moe_grouped_gemm", "moe_combine", "moe_status_string", "moe_last_error")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({detail})")
+
+
+class moe_stats_t(ctypes.Structure):
+    _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("slot", ctypes.c_void_p),
+                ("src", ctypes.c_void_p), ("routed_count", ctypes.c_void_p),
+                ("kept_count", ctypes.c_void_p), ("send_count", ctypes.c_void_p),
+                ("totals", ctypes.c_void_p), ("buckets", ctypes.c_void_p)]
+
+
+_lib = None
+_P, _I32, _I64, _F32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "moe_capacity": [_I64, _I32, _I32, _F32, _P],
+    "moe_workspace_size": [_I64, _I64, _I64, _I32, _I32, _F32, _I32, ctypes.c_int, _P],
+    "moe_layer_forward": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _F32, _I32, ctypes.c_int,
+                          _P, ctypes.POINTER(moe_stats_t), _P, _SZ, _P],
+    "moe_router": [_P, _P, _P, _I64, _I64, _I32, _I32, ctypes.c_int, _P, _P, _P, _P, _SZ, _P],
+    "moe_route": [_P, _I64, _I32, _I32, _P, _P, _P],
+    "moe_permute_workspace_size": [_I64, _I32, _P],
+    "moe_permute": [_P, _P, _I64, _I64, _I32, _I32, _I64, _I32, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P,
+                    _P, _SZ, _P],
+    "moe_grouped_gemm_workspace_size": [_I32, _I64, _P],
+    "moe_grouped_gemm": [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P, _SZ, _P],
+    "moe_combine": [_P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I64, ctypes.c_int, _P, _P],
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m routing_dispatch_expert_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def moe_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoeError(status, where, moe_last_error())
+
+
+def _ptr(a):
+    """Device pointer of a torch tensor, an int address, or None (NULL)."""
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a or None
+    return a.data_ptr() or None
+
+
+def _dtype(dt) -> int:
+    if isinstance(dt, int):
+        return dt
+    s = str(dt)
+    if s in ("bf16", "torch.bfloat16"):
+        return MOE_DTYPE_BF16
+    if s in ("f32", "fp32", "torch.float32"):
+        return MOE_DTYPE_F32
+    raise ValueError(f"unsupported dtype {dt!r}")
+
+
+def _stream(stream):
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream or None
+    return stream.cuda_stream or None
+
+
+# ----------------------------------------------------------------- C entry points
+
+def moe_capacity(T: int, E: int, k: int, cf: float) -> int:
+    C = ctypes.c_int64(0)
+    _check(lib().moe_capacity(T, E, k, cf, ctypes.byref(C)), "moe_capacity")
+    return C.value
+
+
+def moe_workspace_size(T, d, d_ff, E, k, cf, P, dtype) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_workspace_size(T, d, d_ff, E, k, cf, P, _dtype(dtype), ctypes.byref(n)),
+           "moe_workspace_size")
+    return n.value
+
+
+def _stats(stats) -> "ctypes.POINTER(moe_stats_t) | None":
+    if stats is None:
+        return None
+    s = moe_stats_t()
+    for name, _ in moe_stats_t._fields_:
+        setattr(s, name, _ptr(stats.get(name)))
+    return ctypes.pointer(s)
+
+
+def moe_layer_forward(x, W_router, router_bias, W_gate, W_up, W_down, T, d, d_ff, E, k, cf, P, dtype,
+                      out, stats, workspace, workspace_bytes, stream=None):
+    """stats: None or a dict of moe_stats_t field name -> tensor (or None)."""
+    _check(lib().moe_layer_forward(_ptr(x), _ptr(W_router), _ptr(router_bias), _ptr(W_gate), _ptr(W_up),
+                                   _ptr(W_down), T, d, d_ff, E, k, cf, P, _dtype(dtype), _ptr(out),
+                                   _stats(stats), _ptr(workspace), workspace_bytes, _stream(stream)),
+           "moe_layer_forward")
+
+
+def moe_router(x, W_router, router_bias, T, d, E, k, dtype, topk_idx, topk_w, logits_out, workspace,
+               workspace_bytes, stream=None):
+    _check(lib().moe_router(_ptr(x), _ptr(W_router), _ptr(router_bias), T, d, E, k, _dtype(dtype),
+                            _ptr(topk_idx), _ptr(topk_w), _ptr(logits_out), _ptr(workspace),
+                            workspace_bytes, _stream(stream)), "moe_router")
+
+
+def moe_route(logits, T, E, k, topk_idx, topk_w, stream=None):
+    _check(lib().moe_route(_ptr(logits), T, E, k, _ptr(topk_idx), _ptr(topk_w), _stream(stream)),
+           "moe_route")
+
+
+def moe_permute_workspace_size(T, E) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_permute_workspace_size(T, E, ctypes.byref(n)), "moe_permute_workspace_size")
+    return n.value
+
+
+def moe_permute(x, topk_idx, T, d, E, k, C, P, dtype, buckets, slot, src, routed_count, kept_count,
+                send_count, totals, workspace, workspace_bytes, stream=None):
+    _check(lib().moe_permute(_ptr(x), _ptr(topk_idx), T, d, E, k, C, P, _dtype(dtype), _ptr(buckets),
+                             _ptr(slot), _ptr(src), _ptr(routed_count), _ptr(kept_count),
+                             _ptr(send_count), _ptr(totals), _ptr(workspace), workspace_bytes,
+                             _stream(stream)), "moe_permute")
+
+
+def moe_grouped_gemm_workspace_size(E, C) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_grouped_gemm_workspace_size(E, C, ctypes.byref(n)), "moe_grouped_gemm_workspace_size")
+    return n.value
+
+
+def moe_grouped_gemm(buckets, kept_count, W_gate, W_up, W_down, E, C, d, d_ff, dtype, h, y, workspace,
+                     workspace_bytes, stream=None):
+    _check(lib().moe_grouped_gemm(_ptr(buckets), _ptr(kept_count), _ptr(W_gate), _ptr(W_up), _ptr(W_down),
+                                  E, C, d, d_ff, _dtype(dtype), _ptr(h), _ptr(y), _ptr(workspace),
+                                  workspace_bytes, _stream(stream)), "moe_grouped_gemm")
+
+
+def moe_combine(x, y, topk_idx, topk_w, slot, T, d, E, k, C, dtype, out, stream=None):
+    _check(lib().moe_combine(_ptr(x), _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(slot), T, d, E, k, C,
+                             _dtype(dtype), _ptr(out), _stream(stream)), "moe_combine")
+
+
+# ----------------------------------------------------------------- convenience
+
+def _require(t, name, torch_dtype, shape):
+    if t.device.type != "cuda" or not t.is_contiguous() or t.dtype != torch_dtype or tuple(t.shape) != shape:
+        raise ValueError(f"{name}: need a contiguous {torch_dtype} cuda tensor of shape {shape}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def forward(x, W_router, W_gate, W_up, W_down, k, cf, P=1, router_bias=None, stream=None,
+            want_buckets=False, want_src=False, workspace=None):
+    """Run the layer once on torch device tensors; returns a dict of outputs.
+
+    x [T, d]; W_router [E, d]; W_gate, W_up [E, d_ff, d]; W_down [E, d, d_ff]
+    (bf16 or fp32, all the same dtype); router_bias [E] fp32 or None.
+    """
+    import torch
+    T, d = x.shape
+    E = W_router.shape[0]
+    d_ff = W_gate.shape[1]
+    dt = x.dtype
+    for t, n, s in ((x, "x", (T, d)), (W_router, "W_router", (E, d)), (W_gate, "W_gate", (E, d_ff, d)),
+                    (W_up, "W_up", (E, d_ff, d)), (W_down, "W_down", (E, d, d_ff))):
+        _require(t, n, dt, s)
+    if router_bias is not None:
+        _require(router_bias, "router_bias", torch.float32, (E,))
+    C = moe_capacity(T, E, k, cf)
+    dev = x.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    res = {
+        "C": C,
+        "out": torch.empty_like(x),
+        "topk_idx": torch.empty((T, k), **i32),
+        "topk_w": torch.empty((T, k), dtype=torch.float32, device=dev),
+        "slot": torch.empty((T, k), **i32),
+        "routed_count": torch.empty(E, **i32),
+        "kept_count": torch.empty(E, **i32),
+        "send_count": torch.empty(P, **i32),
+        "totals": torch.empty(4, dtype=torch.int64, device=dev),
+    }
+    if want_buckets:
+        res["buckets"] = torch.empty((E, C, d), dtype=dt, device=dev)
+    if want_src:
+        res["src"] = torch.empty((E, C), **i32)
+    nbytes = moe_workspace_size(T, d, d_ff, E, k, cf, P, dt)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    moe_layer_forward(x, W_router, router_bias, W_gate, W_up, W_down, T, d, d_ff, E, k, cf, P, dt,
+                      res["out"], res, workspace, nbytes, stream)
+    res["workspace"] = workspace
+    return res

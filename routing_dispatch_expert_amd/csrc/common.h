@@ -1,0 +1,67 @@
+// Internal declarations shared by the HIP kernels and the host library of the
+// MoE-layer hot path (gfx950). Not part of the C ABI (see include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace moe {
+
+using bf16_t = uint16_t;  // bfloat16 bit pattern
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Tokens per tile of the expert histogram, its scan and the slot kernel.
+constexpr int kTileTokens = 64;
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+__device__ inline float bf16_to_f32(bf16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ inline bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// ---- router (router.hip) ----
+hipError_t launch_router_logits(const void* x, const void* wr, const float* bias, int64_t T,
+                                int64_t d, int E, bool bf16, float* logits, hipStream_t s);
+hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w,
+                        hipStream_t s);
+
+// ---- permutation (permute.hip) ----
+hipError_t launch_tile_hist(const int32_t* idx, int64_t T, int k, int E, int32_t* tile_cnt,
+                            hipStream_t s);
+// Exclusive scan of the tile histogram over tiles, per expert; then counts,
+// totals, send counts and (if mtile_off != nullptr) the GEMM row-tile prefix
+// for row tiles of `bm` rows.
+hipError_t launch_scan(const int32_t* tile_cnt, int64_t nt, int E, int64_t C, int P,
+                       int64_t row_bytes, int k, int64_t T, int32_t* tile_off, int32_t* routed,
+                       int32_t* kept, int32_t* send, int64_t* totals, int bm, int32_t* mtile_off,
+                       int32_t* src, hipStream_t s);
+hipError_t launch_mtile_map(const int32_t* kept, int E, int bm, int32_t* mtile_off, hipStream_t s);
+hipError_t launch_slots(const int32_t* idx, const int32_t* tile_off, int64_t T, int k, int E,
+                        int64_t C, int32_t* slot, int32_t* src, int64_t* totals, hipStream_t s);
+hipError_t launch_scatter_rows(const void* x, const int32_t* idx, const int32_t* slot, int64_t T,
+                               int k, int64_t C, int64_t row_bytes, void* buckets, hipStream_t s);
+
+// ---- experts (grouped_gemm.hip) ----
+// Row-tile height the grouped GEMM uses for these sizes (the mtile map must
+// be built for the same value).
+int grouped_gemm_bm(bool bf16, int64_t C);
+hipError_t launch_grouped_gemm(const void* buckets, const int32_t* kept, const int32_t* mtile_off,
+                               const void* wg, const void* wu, const void* wd, int E, int64_t C,
+                               int64_t d, int64_t d_ff, bool bf16, void* h, void* y, hipStream_t s);
+
+// ---- combine (combine.hip) ----
+hipError_t launch_combine(const void* x, const void* y, const int32_t* idx, const float* w,
+                          const int32_t* slot, int64_t T, int64_t d, int k, int64_t C, bool bf16,
+                          void* out, hipStream_t s);
+
+}  // namespace moe

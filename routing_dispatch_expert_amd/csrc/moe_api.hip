@@ -1,0 +1,362 @@
+// Host side of the C ABI in include/moe.h: argument checks, workspace layout
+// and the launch sequence of the MoE-layer hot path on the caller's stream.
+// No device memory is allocated, no stream is synchronised and nothing is
+// copied back to the host here.
+#include "moe.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  snprintf(g_err, sizeof(g_err), "%s: %s", what, hipGetErrorString(e));
+  return MOE_ERR_HIP;
+}
+
+#define MOE_HIP_TRY(call, what)                      \
+  do {                                               \
+    hipError_t err_ = (call);                        \
+    if (err_ != hipSuccess) return hip_fail(err_, what); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxE = 4096;
+constexpr int kMaxK = 32;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Sequential carving of one workspace block into 256-byte aligned arrays.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t count) {
+    off = align_up(off);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+int elem_bytes(moe_dtype_t dt) { return dt == MOE_DTYPE_BF16 ? 2 : 4; }
+
+bool valid_dtype(int dt) { return dt == MOE_DTYPE_F32 || dt == MOE_DTYPE_BF16; }
+
+int check_width(int64_t n, moe_dtype_t dt, const char* name) {
+  const int64_t q = dt == MOE_DTYPE_BF16 ? 8 : 4;  // whole 16-byte words per row
+  if (n % q) return fail(MOE_ERR_UNSUPPORTED, "%s=%lld must be a multiple of %lld", name,
+                         static_cast<long long>(n), static_cast<long long>(q));
+  return MOE_OK;
+}
+
+int capacity_of(int64_t T, int32_t E, int32_t k, float cf, int64_t* C) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%lld < 0", static_cast<long long>(T));
+  if (E < 1) return fail(MOE_ERR_INVALID_ARG, "E=%d < 1", E);
+  if (k < 1) return fail(MOE_ERR_INVALID_ARG, "k=%d < 1", k);
+  if (!std::isfinite(cf) || !(cf > 0.f)) return fail(MOE_ERR_INVALID_ARG, "cf must be finite and > 0");
+  // ((cf * k) * T) / E in IEEE double, then ceil.
+  const double c = std::ceil(static_cast<double>(cf) * static_cast<double>(k) * static_cast<double>(T) /
+                             static_cast<double>(E));
+  if (c > 9.0e15) return fail(MOE_ERR_UNSUPPORTED, "capacity too large");
+  *C = static_cast<int64_t>(c);
+  return MOE_OK;
+}
+
+// Checks shared by the layer entry points. Returns MOE_OK or an error status.
+int check_layer_shape(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k, float cf, int32_t P,
+                      int dtype, int64_t* C) {
+  if (!valid_dtype(dtype)) return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (d < 1 || d_ff < 1) return fail(MOE_ERR_INVALID_ARG, "d and d_ff must be >= 1");
+  int st = capacity_of(T, E, k, cf, C);
+  if (st != MOE_OK) return st;
+  if (k > E) return fail(MOE_ERR_INVALID_ARG, "k=%d > E=%d", k, E);
+  if (P < 1 || E % P) return fail(MOE_ERR_INVALID_ARG, "P=%d must be >= 1 and divide E=%d", P, E);
+  const auto dt = static_cast<moe_dtype_t>(dtype);
+  if ((st = check_width(d, dt, "d")) != MOE_OK) return st;
+  if ((st = check_width(d_ff, dt, "d_ff")) != MOE_OK) return st;
+  if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "E=%d > %d", E, kMaxE);
+  if (k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "k=%d > %d", k, kMaxK);
+  if (T * k >= (int64_t{1} << 31) || static_cast<int64_t>(E) * *C >= (int64_t{1} << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T*k and E*C must stay below 2^31");
+  return MOE_OK;
+}
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  const auto pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return an && bn && pa < pb + bn && pb < pa + an;
+}
+
+struct LayerPlan {
+  float* logits;
+  int32_t *idx, *slot, *tile_cnt, *tile_off, *routed, *kept, *send, *mtile, *src;
+  float* w;
+  int64_t* totals;
+  void *buckets, *h, *y;
+  size_t bytes;
+};
+
+LayerPlan plan_layer(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k, int64_t C,
+                     int32_t P, int eb) {
+  Carver c(ws);
+  LayerPlan p;
+  const int64_t nt = moe::ceil_div(T, moe::kTileTokens);
+  p.logits = c.take<float>(static_cast<size_t>(T) * E);
+  p.idx = c.take<int32_t>(static_cast<size_t>(T) * k);
+  p.w = c.take<float>(static_cast<size_t>(T) * k);
+  p.slot = c.take<int32_t>(static_cast<size_t>(T) * k);
+  p.tile_cnt = c.take<int32_t>(static_cast<size_t>(nt) * E);
+  p.tile_off = c.take<int32_t>(static_cast<size_t>(nt) * E);
+  p.routed = c.take<int32_t>(E);
+  p.kept = c.take<int32_t>(E);
+  p.send = c.take<int32_t>(P);
+  p.totals = c.take<int64_t>(MOE_NUM_TOTALS);
+  p.mtile = c.take<int32_t>(static_cast<size_t>(E) + 1);
+  p.src = c.take<int32_t>(static_cast<size_t>(E) * C);
+  p.buckets = c.take<char>(static_cast<size_t>(E) * C * d * eb);
+  p.h = c.take<char>(static_cast<size_t>(E) * C * d_ff * eb);
+  p.y = c.take<char>(static_cast<size_t>(E) * C * d * eb);
+  p.bytes = align_up(c.off);
+  return p;
+}
+
+template <class T>
+T* pick(T* user, T* fallback) {
+  return user ? user : fallback;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or size";
+    case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_capacity(int64_t T, int32_t E, int32_t k, float cf, int64_t* C_out) {
+  if (!C_out) return fail(MOE_ERR_INVALID_ARG, "C_out is NULL");
+  int64_t C;
+  const int st = capacity_of(T, E, k, cf, &C);
+  if (st == MOE_OK) *C_out = C;
+  return st;
+}
+
+int moe_workspace_size(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k, float cf, int32_t P,
+                       moe_dtype_t dtype, size_t* bytes) {
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  int64_t C;
+  const int st = check_layer_shape(T, d, d_ff, E, k, cf, P, dtype, &C);
+  if (st != MOE_OK) return st;
+  *bytes = plan_layer(nullptr, T, d, d_ff, E, k, C, P, elem_bytes(dtype)).bytes;
+  return MOE_OK;
+}
+
+int moe_layer_forward(const void* x, const void* W_router, const float* router_bias,
+                      const void* W_gate, const void* W_up, const void* W_down, int64_t T,
+                      int64_t d, int64_t d_ff, int32_t E, int32_t k, float cf, int32_t P,
+                      moe_dtype_t dtype, void* out, moe_stats_t* stats, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int64_t C;
+  int st = check_layer_shape(T, d, d_ff, E, k, cf, P, dtype, &C);
+  if (st != MOE_OK) return st;
+  if (!x || !W_router || !W_gate || !W_up || !W_down || !out)
+    return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
+  const int eb = elem_bytes(dtype);
+  if (overlaps(x, static_cast<size_t>(T * d * eb), out, static_cast<size_t>(T * d * eb)))
+    return fail(MOE_ERR_INVALID_ARG, "out overlaps x");
+  if (T == 0) return MOE_OK;
+  const LayerPlan need = plan_layer(nullptr, T, d, d_ff, E, k, C, P, eb);
+  if (!workspace || workspace_bytes < need.bytes || reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need.bytes);
+  LayerPlan p = plan_layer(workspace, T, d, d_ff, E, k, C, P, eb);
+  moe_stats_t none;
+  std::memset(&none, 0, sizeof(none));
+  const moe_stats_t& S = stats ? *stats : none;
+  int32_t* idx = pick(S.topk_idx, p.idx);
+  float* w = pick(S.topk_w, p.w);
+  int32_t* slot = pick(S.slot, p.slot);
+  int32_t* routed = pick(S.routed_count, p.routed);
+  int32_t* kept = pick(S.kept_count, p.kept);
+  int32_t* send = pick(S.send_count, p.send);
+  int64_t* totals = pick(S.totals, p.totals);
+  void* buckets = pick(S.buckets, p.buckets);
+  int32_t* src = S.src;  // only built when asked for
+  const bool bf16 = dtype == MOE_DTYPE_BF16;
+  auto s = static_cast<hipStream_t>(stream);
+  const int64_t nt = moe::ceil_div(T, moe::kTileTokens);
+  const int bm = moe::grouped_gemm_bm(bf16, C);
+
+  MOE_HIP_TRY(moe::launch_router_logits(x, W_router, router_bias, T, d, E, bf16, p.logits, s),
+              "router logits");
+  MOE_HIP_TRY(moe::launch_route(p.logits, T, E, k, idx, w, s), "route");
+  MOE_HIP_TRY(moe::launch_tile_hist(idx, T, k, E, p.tile_cnt, s), "tile histogram");
+  MOE_HIP_TRY(moe::launch_scan(p.tile_cnt, nt, E, C, P, d * eb, k, T, p.tile_off, routed, kept, send,
+                               totals, bm, p.mtile, src, s),
+              "scan");
+  MOE_HIP_TRY(moe::launch_slots(idx, p.tile_off, T, k, E, C, slot, src, totals, s), "slots");
+  MOE_HIP_TRY(moe::launch_scatter_rows(x, idx, slot, T, k, C, d * eb, buckets, s), "scatter");
+  MOE_HIP_TRY(moe::launch_grouped_gemm(buckets, kept, p.mtile, W_gate, W_up, W_down, E, C, d, d_ff,
+                                       bf16, p.h, p.y, s),
+              "grouped gemm");
+  MOE_HIP_TRY(moe::launch_combine(x, p.y, idx, w, slot, T, d, k, C, bf16, out, s), "combine");
+  return MOE_OK;
+}
+
+int moe_router(const void* x, const void* W_router, const float* router_bias, int64_t T, int64_t d,
+               int32_t E, int32_t k, moe_dtype_t dtype, int32_t* topk_idx, float* topk_w,
+               float* logits_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (T < 0 || d < 1 || E < 1 || k < 1 || k > E)
+    return fail(MOE_ERR_INVALID_ARG, "need T >= 0, d >= 1, 1 <= k <= E");
+  int st = check_width(d, dtype, "d");
+  if (st != MOE_OK) return st;
+  if (E > kMaxE || k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "E or k too large");
+  if (T * k >= (int64_t{1} << 31)) return fail(MOE_ERR_UNSUPPORTED, "T*k must stay below 2^31");
+  if (!x || !W_router || !topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (T == 0) return MOE_OK;
+  float* logits = logits_out;
+  if (!logits) {
+    const size_t need = static_cast<size_t>(T) * E * sizeof(float);
+    if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % kAlign)
+      return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+    logits = static_cast<float*>(workspace);
+  }
+  auto s = static_cast<hipStream_t>(stream);
+  MOE_HIP_TRY(moe::launch_router_logits(x, W_router, router_bias, T, d, E, dtype == MOE_DTYPE_BF16,
+                                        logits, s),
+              "router logits");
+  MOE_HIP_TRY(moe::launch_route(logits, T, E, k, topk_idx, topk_w, s), "route");
+  return MOE_OK;
+}
+
+int moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_idx, float* topk_w,
+              void* stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E) return fail(MOE_ERR_INVALID_ARG, "need T >= 0, 1 <= k <= E");
+  if (E > kMaxE || k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "E or k too large");
+  if (T * k >= (int64_t{1} << 31)) return fail(MOE_ERR_UNSUPPORTED, "T*k must stay below 2^31");
+  if (!logits || !topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (T == 0) return MOE_OK;
+  MOE_HIP_TRY(moe::launch_route(logits, T, E, k, topk_idx, topk_w, static_cast<hipStream_t>(stream)),
+              "route");
+  return MOE_OK;
+}
+
+int moe_permute_workspace_size(int64_t T, int32_t E, size_t* bytes) {
+  if (!bytes || T < 0 || E < 1) return fail(MOE_ERR_INVALID_ARG, "need bytes, T >= 0, E >= 1");
+  const size_t nt = static_cast<size_t>(moe::ceil_div(T, moe::kTileTokens));
+  *bytes = 2 * align_up(nt * E * sizeof(int32_t));
+  return MOE_OK;
+}
+
+int moe_permute(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, int32_t E, int32_t k,
+                int64_t C, int32_t P, moe_dtype_t dtype, void* buckets, int32_t* slot, int32_t* src,
+                int32_t* routed_count, int32_t* kept_count, int32_t* send_count, int64_t* totals,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (T < 0 || d < 1 || E < 1 || k < 1 || k > E || C < 1)
+    return fail(MOE_ERR_INVALID_ARG, "need T >= 0, d >= 1, 1 <= k <= E, C >= 1");
+  if (P < 1 || E % P) return fail(MOE_ERR_INVALID_ARG, "P=%d must be >= 1 and divide E=%d", P, E);
+  int st = check_width(d, dtype, "d");
+  if (st != MOE_OK) return st;
+  if (E > kMaxE || k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "E or k too large");
+  if (T * k >= (int64_t{1} << 31) || E * C >= (int64_t{1} << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T*k and E*C must stay below 2^31");
+  if (!x || !topk_idx || !buckets || !slot || !routed_count || !kept_count)
+    return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (T == 0) return MOE_OK;
+  size_t need;
+  moe_permute_workspace_size(T, E, &need);
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+  const int64_t nt = moe::ceil_div(T, moe::kTileTokens);
+  Carver c(workspace);
+  int32_t* tile_cnt = c.take<int32_t>(static_cast<size_t>(nt) * E);
+  int32_t* tile_off = c.take<int32_t>(static_cast<size_t>(nt) * E);
+  auto s = static_cast<hipStream_t>(stream);
+  const int64_t eb = elem_bytes(dtype);
+  MOE_HIP_TRY(moe::launch_tile_hist(topk_idx, T, k, E, tile_cnt, s), "tile histogram");
+  MOE_HIP_TRY(moe::launch_scan(tile_cnt, nt, E, C, P, d * eb, k, T, tile_off, routed_count, kept_count,
+                               send_count, totals, 0, nullptr, src, s),
+              "scan");
+  MOE_HIP_TRY(moe::launch_slots(topk_idx, tile_off, T, k, E, C, slot, src, totals, s), "slots");
+  MOE_HIP_TRY(moe::launch_scatter_rows(x, topk_idx, slot, T, k, C, d * eb, buckets, s), "scatter");
+  return MOE_OK;
+}
+
+int moe_grouped_gemm_workspace_size(int32_t E, int64_t C, size_t* bytes) {
+  if (!bytes || E < 1 || C < 1) return fail(MOE_ERR_INVALID_ARG, "need bytes, E >= 1, C >= 1");
+  *bytes = align_up((static_cast<size_t>(E) + 1) * sizeof(int32_t));
+  return MOE_OK;
+}
+
+int moe_grouped_gemm(const void* buckets, const int32_t* kept_count, const void* W_gate,
+                     const void* W_up, const void* W_down, int32_t E, int64_t C, int64_t d,
+                     int64_t d_ff, moe_dtype_t dtype, void* h, void* y, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (E < 1 || C < 1 || d < 1 || d_ff < 1) return fail(MOE_ERR_INVALID_ARG, "need E, C, d, d_ff >= 1");
+  int st = check_width(d, dtype, "d");
+  if (st != MOE_OK || (st = check_width(d_ff, dtype, "d_ff")) != MOE_OK) return st;
+  if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "E=%d > %d", E, kMaxE);
+  if (E * C >= (int64_t{1} << 31)) return fail(MOE_ERR_UNSUPPORTED, "E*C must stay below 2^31");
+  if (!buckets || !kept_count || !W_gate || !W_up || !W_down || !h || !y)
+    return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
+  size_t need;
+  moe_grouped_gemm_workspace_size(E, C, &need);
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
+  auto s = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == MOE_DTYPE_BF16;
+  auto* mtile = static_cast<int32_t*>(workspace);
+  MOE_HIP_TRY(moe::launch_mtile_map(kept_count, E, moe::grouped_gemm_bm(bf16, C), mtile, s), "tile map");
+  MOE_HIP_TRY(moe::launch_grouped_gemm(buckets, kept_count, mtile, W_gate, W_up, W_down, E, C, d, d_ff,
+                                       bf16, h, y, s),
+              "grouped gemm");
+  return MOE_OK;
+}
+
+int moe_combine(const void* x, const void* y, const int32_t* topk_idx, const float* topk_w,
+                const int32_t* slot, int64_t T, int64_t d, int32_t E, int32_t k, int64_t C,
+                moe_dtype_t dtype, void* out, void* stream) {
+  if (!valid_dtype(dtype)) return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (T < 0 || d < 1 || E < 1 || k < 1 || k > E || C < 1)
+    return fail(MOE_ERR_INVALID_ARG, "need T >= 0, d >= 1, 1 <= k <= E, C >= 1");
+  const int st = check_width(d, dtype, "d");
+  if (st != MOE_OK) return st;
+  if (k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "k=%d > %d", k, kMaxK);
+  if (!x || !y || !topk_idx || !topk_w || !slot || !out)
+    return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
+  const size_t row = static_cast<size_t>(d) * elem_bytes(dtype);
+  if (overlaps(x, T * row, out, T * row)) return fail(MOE_ERR_INVALID_ARG, "out overlaps x");
+  if (T == 0) return MOE_OK;
+  MOE_HIP_TRY(moe::launch_combine(x, y, topk_idx, topk_w, slot, T, d, k, C, dtype == MOE_DTYPE_BF16, out,
+                                  static_cast<hipStream_t>(stream)),
+              "combine");
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,323 @@
+// Capacity-bounded permutation of the MoE layer (gfx950): expert histogram,
+// exclusive scan, capacity, stable token-order slots, drop mask, and the row
+// scatter into fixed-capacity per-expert buckets.
+//
+// Sources: "Expert Parallelism" (inferensys.com glossary), capacity entry
+// (an expert takes at most C = cf*k*T/E tokens; the excess is dropped) and
+// memory entry (pre-allocated contiguous buffers of maximum capacity);
+// "Expert Parallelism & All-to-All" (neelmishra.github.io), "Why fixed-size
+// buffers matter here" (fixed per-expert buffer; drops on overflow, padding on
+// underflow) and "Why MoE forces a new axis" (E/P whole experts per device).
+//
+// Slot of copy i = t*k + j of expert e: the number of earlier copies (in
+// flattened token order) of the same expert. It is found as
+//   tile offset (scan of per-tile counts over earlier tiles)
+// + rank inside the tile (wave ballots over the expert-id bits).
+// Positions never come from atomics; only the order-free per-tile counts do.
+#include <algorithm>
+
+#include "common.h"
+
+namespace moe {
+namespace {
+
+// Per-tile expert histogram: tile_cnt[b][e] = copies of expert e among tokens
+// [64 b, 64 b + 64).
+__global__ __launch_bounds__(256) void tile_hist_kernel(const int32_t* __restrict__ idx,
+                                                        int64_t T, int k, int E,
+                                                        int32_t* __restrict__ tile_cnt) {
+  extern __shared__ int hist[];
+  const int64_t b = blockIdx.x;
+  const int64_t t0 = b * kTileTokens;
+  const int n = static_cast<int>(min<int64_t>(kTileTokens, T - t0)) * k;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&hist[idx[t0 * k + i]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) tile_cnt[b * E + e] = hist[e];
+}
+
+// Exclusive scan over tiles, per expert. A block serves 16 experts with 16
+// lanes each; lane ly owns a contiguous run of tiles. routed[e] = total.
+__global__ __launch_bounds__(256) void scan_tiles_kernel(const int32_t* __restrict__ tile_cnt,
+                                                         int64_t nt, int E,
+                                                         int32_t* __restrict__ tile_off,
+                                                         int32_t* __restrict__ routed) {
+  __shared__ int part[16][17];
+  const int ex = threadIdx.x & 15;
+  const int ly = threadIdx.x >> 4;
+  const int e = blockIdx.x * 16 + ex;
+  const int64_t chunk = ceil_div(nt, 16);
+  const int64_t b0 = min(nt, ly * chunk);
+  const int64_t b1 = min(nt, b0 + chunk);
+  int sum = 0;
+  if (e < E)
+    for (int64_t b = b0; b < b1; ++b) sum += tile_cnt[b * E + e];
+  part[ly][ex] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int l = 0; l < ly; ++l) run += part[l][ex];
+  if (e >= E) return;
+  for (int64_t b = b0; b < b1; ++b) {
+    const int v = tile_cnt[b * E + e];
+    tile_off[b * E + e] = run;
+    run += v;
+  }
+  if (ly == 15) routed[e] = run;
+}
+
+// Exclusive scan of one int per thread over a block of 1024 threads.
+__device__ int block_exclusive_scan_1024(int v, int* total, int* sh /* >= 17 ints */) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int t = sh[w];
+      sh[w] = run;
+      run += t;
+    }
+    sh[16] = run;
+  }
+  __syncthreads();
+  const int out = sh[wave] + incl - v;
+  *total = sh[16];
+  __syncthreads();
+  return out;
+}
+
+// mtile_off[e] = sum over e' < e of ceil(kept[e'] / bm); mtile_off[E] = total.
+// Block of 1024 threads, 4 experts per thread (E <= 4096).
+__device__ void mtile_prefix(const int* kept_s, int E, int bm, int32_t* mtile_off, int* sh) {
+  int v[4];
+  int local = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = threadIdx.x * 4 + q;
+    v[q] = e < E ? (kept_s[e] + bm - 1) / bm : 0;
+    local += v[q];
+  }
+  int total;
+  int run = block_exclusive_scan_1024(local, &total, sh);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = threadIdx.x * 4 + q;
+    if (e < E) mtile_off[e] = run;
+    run += v[q];
+  }
+  if (threadIdx.x == 0) mtile_off[E] = total;
+}
+
+// Counts, totals, send counts and the GEMM row-tile map. One block of 1024.
+__global__ __launch_bounds__(1024) void finalize_kernel(const int32_t* __restrict__ routed, int E,
+                                                        int64_t C, int P, int64_t row_bytes, int k,
+                                                        int64_t T, int32_t* __restrict__ kept,
+                                                        int32_t* __restrict__ send,
+                                                        int64_t* __restrict__ totals, int bm,
+                                                        int32_t* __restrict__ mtile_off) {
+  __shared__ int kept_s[4096];
+  __shared__ int sh[17];
+  __shared__ unsigned long long ksum;
+  if (threadIdx.x == 0) ksum = 0;
+  __syncthreads();
+  unsigned long long local = 0;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const int kv = static_cast<int>(min<int64_t>(routed[e], C));
+    kept[e] = kv;
+    kept_s[e] = kv;
+    local += static_cast<unsigned long long>(kv);
+  }
+  atomicAdd(&ksum, local);  // integer sum: order-free
+  __syncthreads();
+  const int per = E / P;
+  if (send)
+    for (int p = threadIdx.x; p < P; p += blockDim.x) {
+      int s = 0;
+      for (int e = p * per; e < (p + 1) * per; ++e) s += kept_s[e];
+      send[p] = s;
+    }
+  if (totals && threadIdx.x == 0) {
+    const int64_t n_kept = static_cast<int64_t>(ksum);
+    int64_t rank0 = 0;
+    for (int e = 0; e < per; ++e) rank0 += kept_s[e];
+    totals[0] = T * k - n_kept;
+    totals[1] = 0;  // fully dropped tokens: accumulated by the slot kernel
+    totals[2] = static_cast<int64_t>(E) * C - n_kept;
+    totals[3] = (n_kept - rank0) * row_bytes;
+  }
+  if (mtile_off) mtile_prefix(kept_s, E, bm, mtile_off, sh);
+}
+
+__global__ __launch_bounds__(1024) void mtile_map_kernel(const int32_t* __restrict__ kept, int E,
+                                                         int bm, int32_t* __restrict__ mtile_off) {
+  __shared__ int kept_s[4096];
+  __shared__ int sh[17];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) kept_s[e] = kept[e];
+  __syncthreads();
+  mtile_prefix(kept_s, E, bm, mtile_off, sh);
+}
+
+// src[e][s] = -1 on padding rows s >= kept[e] (kept rows come from the slot kernel).
+__global__ __launch_bounds__(256) void src_padding_kernel(const int32_t* __restrict__ kept,
+                                                          int64_t C, int E,
+                                                          int32_t* __restrict__ src) {
+  const int e = blockIdx.y;
+  for (int64_t s = kept[e] + static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; s < C;
+       s += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    src[e * C + s] = -1;
+}
+
+// Slots of one 64-token tile, one wave. Copies are taken 64 at a time in
+// flattened order; lanes with the same expert form a group found by ballots
+// over the expert-id bits; a lane's rank is the number of group lanes below
+// it. The group's highest lane advances the expert's running count.
+__global__ __launch_bounds__(64) void slots_kernel(const int32_t* __restrict__ idx,
+                                                   const int32_t* __restrict__ tile_off,
+                                                   int64_t T, int k, int E, int64_t C,
+                                                   int32_t* __restrict__ slot,
+                                                   int32_t* __restrict__ src,
+                                                   int64_t* __restrict__ totals) {
+  extern __shared__ int sm[];
+  int* cnt = sm;          // [E]
+  int* sbuf = sm + E;     // [64 * k]
+  const int lane = threadIdx.x;
+  const int64_t b = blockIdx.x;
+  const int64_t t0 = b * kTileTokens;
+  const int n = static_cast<int>(min<int64_t>(kTileTokens, T - t0));
+  const int ncp = n * k;
+  for (int e = lane; e < E; e += 64) cnt[e] = tile_off[b * E + e];
+  __syncthreads();
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int base = 0; base < ncp; base += 64) {
+    const int i = base + lane;
+    const bool active = i < ncp;
+    const int e = active ? idx[t0 * k + i] : 0;
+    unsigned long long mask = __ballot(active);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = (e >> bit) & 1;
+      const unsigned long long m = __ballot(active && set);
+      mask &= set ? m : ~m;
+    }
+    const int rank = __popcll(mask & below);
+    const int s = active ? cnt[e] + rank : 0;
+    __syncthreads();
+    if (active && (63 - __clzll(mask)) == lane) cnt[e] = s + 1;
+    __syncthreads();
+    if (active) {
+      const int sl = s < C ? s : -1;
+      slot[t0 * k + i] = sl;
+      sbuf[i] = sl;
+      if (src && sl >= 0) src[static_cast<int64_t>(e) * C + s] = static_cast<int32_t>(t0 * k + i);
+    }
+  }
+  __syncthreads();
+  if (totals) {
+    bool all_dropped = lane < n;
+    for (int j = 0; j < k && all_dropped; ++j) all_dropped = sbuf[lane * k + j] < 0;
+    const int c = __popcll(__ballot(all_dropped));
+    if (lane == 0 && c) atomicAdd(reinterpret_cast<unsigned long long*>(&totals[1]),
+                                  static_cast<unsigned long long>(c));
+  }
+}
+
+// Row scatter: block b moves token b's row (16-byte words) to each kept
+// destination bucket row; the row is read once and written k' <= k times.
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restrict__ x,
+                                                           const int32_t* __restrict__ idx,
+                                                           const int32_t* __restrict__ slot,
+                                                           int k, int64_t C, int64_t V,
+                                                           uint4* __restrict__ buckets) {
+  __shared__ int64_t dst[32];
+  __shared__ int nk;
+  const int64_t t = blockIdx.x;
+  if (threadIdx.x == 0) {
+    int c = 0;
+    for (int j = 0; j < k; ++j) {
+      const int s = slot[t * k + j];
+      if (s >= 0) dst[c++] = (static_cast<int64_t>(idx[t * k + j]) * C + s) * V;
+    }
+    nk = c;
+  }
+  __syncthreads();
+  const int c = nk;
+  if (c == 0) return;
+  const uint4* xr = x + t * V;
+  for (int64_t v0 = threadIdx.x; v0 < V; v0 += 4 * blockDim.x) {
+    uint4 val[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t v = v0 + u * blockDim.x;
+      if (v < V) val[u] = xr[v];
+    }
+    for (int j = 0; j < c; ++j) {
+      uint4* d = buckets + dst[j];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t v = v0 + u * blockDim.x;
+        if (v < V) d[v] = val[u];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tile_hist(const int32_t* idx, int64_t T, int k, int E, int32_t* tile_cnt,
+                            hipStream_t s) {
+  const int64_t nt = ceil_div(T, kTileTokens);
+  if (nt == 0) return hipSuccess;
+  tile_hist_kernel<<<dim3(static_cast<unsigned>(nt)), dim3(256), E * sizeof(int), s>>>(idx, T, k, E,
+                                                                                     tile_cnt);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const int32_t* tile_cnt, int64_t nt, int E, int64_t C, int P,
+                       int64_t row_bytes, int k, int64_t T, int32_t* tile_off, int32_t* routed,
+                       int32_t* kept, int32_t* send, int64_t* totals, int bm, int32_t* mtile_off,
+                       int32_t* src, hipStream_t s) {
+  scan_tiles_kernel<<<dim3(static_cast<unsigned>(ceil_div(E, 16))), dim3(256), 0, s>>>(
+      tile_cnt, nt, E, tile_off, routed);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  finalize_kernel<<<dim3(1), dim3(1024), 0, s>>>(routed, E, C, P, row_bytes, k, T, kept, send,
+                                                 totals, bm, mtile_off);
+  err = hipGetLastError();
+  if (err != hipSuccess || !src) return err;
+  const unsigned gx = static_cast<unsigned>(std::min<int64_t>(ceil_div(C, 256), 64));
+  src_padding_kernel<<<dim3(gx, static_cast<unsigned>(E)), dim3(256), 0, s>>>(kept, C, E, src);
+  return hipGetLastError();
+}
+
+hipError_t launch_mtile_map(const int32_t* kept, int E, int bm, int32_t* mtile_off, hipStream_t s) {
+  mtile_map_kernel<<<dim3(1), dim3(1024), 0, s>>>(kept, E, bm, mtile_off);
+  return hipGetLastError();
+}
+
+hipError_t launch_slots(const int32_t* idx, const int32_t* tile_off, int64_t T, int k, int E,
+                        int64_t C, int32_t* slot, int32_t* src, int64_t* totals, hipStream_t s) {
+  const int64_t nt = ceil_div(T, kTileTokens);
+  if (nt == 0) return hipSuccess;
+  const size_t shm = (static_cast<size_t>(E) + static_cast<size_t>(kTileTokens) * k) * sizeof(int);
+  slots_kernel<<<dim3(static_cast<unsigned>(nt)), dim3(64), shm, s>>>(idx, tile_off, T, k, E, C,
+                                                                     slot, src, totals);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_rows(const void* x, const int32_t* idx, const int32_t* slot, int64_t T,
+                               int k, int64_t C, int64_t row_bytes, void* buckets, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  scatter_rows_kernel<<<dim3(static_cast<unsigned>(T)), dim3(256), 0, s>>>(
+      static_cast<const uint4*>(x), idx, slot, k, C, row_bytes / 16, static_cast<uint4*>(buckets));
+  return hipGetLastError();
+}
+
+}  // namespace moe

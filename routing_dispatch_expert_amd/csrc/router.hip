@@ -1,0 +1,222 @@
+// Router of the MoE layer: scores, top-k choice and gate weights (gfx950).
+//
+// Sources: "Expert Parallelism" (klaylearn.com glossary) - the router scores
+// each token against every expert, keeps the top k and yields the weights
+// that combine their outputs; "Expert Parallelism" (inferensys.com glossary),
+// gating-network entry - a small linear router with top-k gating.
+//
+// logits[t, e] = sum_i x[t, i] W_router[e, i] (+ bias[e]), fp32.
+// Top-k: order by score descending, then expert index ascending (the pages
+// leave ties open; the lower index wins). Gates: softmax over the k chosen
+// scores, evaluated in fp64 and rounded to fp32.
+#include <climits>
+
+#include "common.h"
+
+namespace moe {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Scores on the matrix cores: one wave computes 16 tokens x (16*NT) experts
+// with v_mfma_f32_16x16x32_bf16, K-loop over d. Both operands come straight
+// from global memory (x is read once; W_router is small and stays in L2).
+// Lane l of an A/B operand holds row (l % 16), K elements 8*(l/16) .. +8;
+// the accumulator of lane l holds rows 4*(l/16) + r, column l % 16.
+// ---------------------------------------------------------------------------
+template <int NT>
+__global__ __launch_bounds__(256) void router_logits_bf16(const bf16_t* __restrict__ x,
+                                                          const bf16_t* __restrict__ wr,
+                                                          const float* __restrict__ bias,
+                                                          int64_t T, int64_t d, int E,
+                                                          float* __restrict__ logits) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 64 + wave * 16;
+  const int e0 = blockIdx.y * (16 * NT);
+  const int kg = (lane >> 4) * 8;
+  const int64_t trow = min(t0 + (lane & 15), T - 1);  // rows past T are computed, not stored
+  const bf16_t* xp = x + trow * d + kg;
+  const bf16_t* wp[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int e = min(e0 + 16 * j + (lane & 15), E - 1);
+    wp[j] = wr + static_cast<int64_t>(e) * d + kg;
+  }
+  f32x4 acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll 4
+  for (int64_t k0 = 0; k0 < d; k0 += 32) {
+    const bool in = k0 + kg < d;  // d is a multiple of 8: whole 8-element groups
+    bf16x8 a = {};
+    if (in) a = *reinterpret_cast<const bf16x8*>(xp + k0);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      bf16x8 b = {};
+      if (in) b = *reinterpret_cast<const bf16x8*>(wp[j] + k0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int e = e0 + 16 * j + (lane & 15);
+    if (e >= E) continue;
+    const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t t = t0 + 4 * (lane >> 4) + r;
+      if (t < T) logits[t * E + e] = acc[j][r] + b;
+    }
+  }
+}
+
+// fp32 scores: one thread per (token, expert), plain fused multiply-adds.
+__global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict__ x,
+                                                         const float* __restrict__ wr,
+                                                         const float* __restrict__ bias, int64_t T,
+                                                         int64_t d, int E,
+                                                         float* __restrict__ logits) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= T * E) return;
+  const int64_t t = i / E;
+  const int e = static_cast<int>(i % E);
+  const float* xr = x + t * d;
+  const float* wrow = wr + static_cast<int64_t>(e) * d;
+  float acc = 0.f;
+  for (int64_t c = 0; c < d; ++c) acc = fmaf(xr[c], wrow[c], acc);
+  logits[i] = acc + (bias ? bias[e] : 0.f);
+}
+
+// ---------------------------------------------------------------------------
+// Top-k and gates. A group of L lanes serves one token: lane g keeps a sorted
+// list of its best KMAX scores among experts g, g+L, ...; then k rounds pick
+// the group's best head (score desc, index asc) with a butterfly reduction and
+// pop it from its owner. Lane j < k of the group ends with the j-th choice.
+// ---------------------------------------------------------------------------
+__device__ inline bool better(float v, int e, float ov, int oe) {
+  return v > ov || (v == ov && e < oe);
+}
+
+template <int L, int KMAX>
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int64_t T,
+                                                    int E, int k, int32_t* __restrict__ idx,
+                                                    float* __restrict__ w) {
+  constexpr int kTokensPerBlock = 256 / L;
+  const int g = threadIdx.x % L;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + threadIdx.x / L;
+  const bool valid = t < T;
+
+  float lv[KMAX];
+  int li[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    lv[j] = -INFINITY;
+    li[j] = INT_MAX;
+  }
+  if (valid) {
+    const float* row = logits + t * E;
+    for (int e = g; e < E; e += L) {
+      float v = row[e] + 0.0f;  // -0.0 -> +0.0 (they compare equal anyway)
+      int ei = e;
+      bool ins = false;
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        const bool take = ins || better(v, ei, lv[j], li[j]);
+        if (take) {
+          const float tv = lv[j];
+          const int te = li[j];
+          lv[j] = v;
+          li[j] = ei;
+          v = tv;
+          ei = te;
+        }
+        ins = ins || take;
+      }
+    }
+  }
+
+  float sel_v = -INFINITY, v0 = 0.f;
+  int sel_e = 0;
+  for (int r = 0; r < k; ++r) {
+    float bv = lv[0];
+    int be = li[0];
+#pragma unroll
+    for (int off = L / 2; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, L);
+      const int oe = __shfl_xor(be, off, L);
+      if (better(ov, oe, bv, be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if (r == 0) v0 = bv;
+    if (g == r) {
+      sel_v = bv;
+      sel_e = be;
+    }
+    if (li[0] == be) {  // the owner pops its head
+#pragma unroll
+      for (int j = 0; j + 1 < KMAX; ++j) {
+        lv[j] = lv[j + 1];
+        li[j] = li[j + 1];
+      }
+      lv[KMAX - 1] = -INFINITY;
+      li[KMAX - 1] = INT_MAX;
+    }
+  }
+
+  const double z = g < k ? exp(static_cast<double>(sel_v) - static_cast<double>(v0)) : 0.0;
+  double sum = z;
+#pragma unroll
+  for (int off = L / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, L);
+  sum = __shfl(sum, 0, L);  // one denominator for the whole group
+  if (valid && g < k) {
+    idx[t * k + g] = sel_e;
+    w[t * k + g] = static_cast<float>(z / sum);
+  }
+}
+
+template <int L, int KMAX>
+hipError_t route_launch(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w,
+                        hipStream_t s) {
+  const int64_t tpb = 256 / L;
+  route_kernel<L, KMAX><<<dim3(static_cast<unsigned>(ceil_div(T, tpb))), dim3(256), 0, s>>>(
+      logits, T, E, k, idx, w);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_router_logits(const void* x, const void* wr, const float* bias, int64_t T,
+                                int64_t d, int E, bool bf16, float* logits, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (!bf16) {
+    const int64_t n = T * E;
+    router_logits_f32<<<dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, s>>>(
+        static_cast<const float*>(x), static_cast<const float*>(wr), bias, T, d, E, logits);
+    return hipGetLastError();
+  }
+  const int nt = E <= 16 ? 1 : (E <= 32 ? 2 : 4);
+  const dim3 grid(static_cast<unsigned>(ceil_div(T, 64)), static_cast<unsigned>(ceil_div(E, 16 * nt)));
+  const auto* xb = static_cast<const bf16_t*>(x);
+  const auto* wb = static_cast<const bf16_t*>(wr);
+  if (nt == 1)
+    router_logits_bf16<1><<<grid, dim3(256), 0, s>>>(xb, wb, bias, T, d, E, logits);
+  else if (nt == 2)
+    router_logits_bf16<2><<<grid, dim3(256), 0, s>>>(xb, wb, bias, T, d, E, logits);
+  else
+    router_logits_bf16<4><<<grid, dim3(256), 0, s>>>(xb, wb, bias, T, d, E, logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w,
+                        hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (k <= 2) return route_launch<16, 2>(logits, T, E, k, idx, w, s);
+  if (k <= 8) return route_launch<16, 8>(logits, T, E, k, idx, w, s);
+  if (k <= 16) return route_launch<16, 16>(logits, T, E, k, idx, w, s);
+  return route_launch<32, 32>(logits, T, E, k, idx, w, s);
+}
+
+}  // namespace moe

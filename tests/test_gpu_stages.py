@@ -1,0 +1,252 @@
+"""Parity of each stage of the HIP path with the CPU oracle, through the C ABI.
+
+Routing indices, counts, slots, drop masks, inverse maps and bucket rows are
+compared bit for bit; floating-point results within bounds derived from the
+arithmetic (stated at each check).
+"""
+import numpy as np
+import pytest
+
+import moe_inputs
+import oracle
+import routing_dispatch_expert_amd as moe
+from tests.gpu_util import U, bits_to_f64, gpu_available, logits_tolerance, row_rel_err, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    assert gpu_available(), "GPU tests need an MI355X; run them with -m gpu on a GPU host"
+    moe.lib()
+
+
+def _i32(*shape):
+    return torch.empty(shape, dtype=torch.int32, device="cuda")
+
+
+def _f32(*shape):
+    return torch.empty(shape, dtype=torch.float32, device="cuda")
+
+
+# ------------------------------------------------------------------ routing ---
+
+ROUTE_CASES = [
+    (1000, 8, 2, "ties"), (333, 256, 8, "ties"), (64, 64, 6, "zeros"), (50, 16, 16, "equal"),
+    (77, 5, 5, "normal"), (4096, 1, 1, "normal"), (1000, 300, 32, "normal"), (129, 40, 12, "ties"),
+    (8192, 256, 8, "normal"), (3, 2048, 20, "ties"),
+]
+
+
+@pytest.mark.parametrize("T,E,k,kind", ROUTE_CASES)
+def test_route_given_logits_is_exact(T, E, k, kind):
+    say(f"route T={T} E={E} k={k} {kind}")
+    rng = np.random.default_rng(T * 31 + E * 7 + k)
+    if kind == "ties":
+        l = rng.integers(-3, 4, (T, E)).astype(np.float32)
+    elif kind == "zeros":
+        l = rng.choice(np.array([0.0, -0.0, 1.0, -1.0], np.float32), (T, E))
+    elif kind == "equal":
+        l = np.full((T, E), 0.5, np.float32)
+    else:
+        l = (rng.standard_normal((T, E)) * 2).astype(np.float32)
+    idx_ref = oracle.topk_experts(l, k)
+    w_ref = oracle.gate_weights(l, idx_ref)
+    idx, w = _i32(T, k), _f32(T, k)
+    moe.moe_route(torch.from_numpy(l).cuda(), T, E, k, idx, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    # both sides evaluate the softmax in fp64 and round once: at most 1 ulp apart
+    assert np.all(np.abs(w.cpu().numpy() - w_ref) <= np.spacing(np.abs(w_ref)))
+
+
+ROUTER_CASES = [
+    (300, 256, 8, 2, "bf16", None), (200, 1024, 64, 6, "bf16", "zipf1.2"), (130, 520, 256, 8, "bf16", None),
+    (100, 128, 8, 2, "f32", None), (65, 72, 20, 3, "bf16", None), (1, 4096, 8, 2, "bf16", None),
+]
+
+
+@pytest.mark.parametrize("T,d,E,k,dtype,bias", ROUTER_CASES)
+def test_router_scores_choice_and_gates(T, d, E, k, dtype, bias):
+    say(f"router T={T} d={d} E={E} k={k} {dtype} bias={bias}")
+    std = (1 / np.sqrt(d)) if dtype == "f32" else 1.0
+    wl = moe_inputs.custom(T=T, d=d, E=E, k=k, d_ff=8, cf=1.0, dtype=dtype, seed=T + d + E,
+                           x_std=std, wr_std=(1 / np.sqrt(d)) if dtype == "f32" else 0.02, bias=bias)
+    x64, wr64 = oracle.decode(wl.x, dtype), oracle.decode(wl.wr, dtype)
+    l_ref = oracle.router_logits(x64, wr64, wl.bias_vec)
+    idx_ref = oracle.topk_experts(l_ref, k)
+    w_ref = oracle.gate_weights(l_ref, idx_ref)
+    logits, idx, w = _f32(T, E), _i32(T, k), _f32(T, k)
+    b = None if wl.bias_vec is None else torch.from_numpy(wl.bias_vec).cuda()
+    moe.moe_router(to_dev(wl.x, dtype), to_dev(wl.wr, dtype), b, T, d, E, k, dtype, idx, w, logits, None, 0)
+    torch.cuda.synchronize()
+    tol = logits_tolerance(x64, wr64, wl.bias_vec)
+    err = np.abs(logits.cpu().numpy().astype(np.float64) - l_ref)
+    assert np.all(err <= tol), f"max err/tol {np.max(err / tol)}"
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    # softmax sensitivity: |dw_j| <= 2 w_j max|dl|, plus one rounding
+    wtol = w_ref.astype(np.float64) * (2 * tol.max(axis=1, keepdims=True) + 2 * U)
+    assert np.all(np.abs(w.cpu().numpy().astype(np.float64) - w_ref) <= wtol)
+
+
+# -------------------------------------------------------------- permutation ---
+
+def _random_routes(rng, T, E, k, skew):
+    if skew:
+        p = 1.0 / np.arange(1, E + 1) ** 1.2
+        p /= p.sum()
+        return np.array([rng.choice(E, k, replace=False, p=p) for _ in range(T)], np.int32).reshape(T, k)
+    return np.array([rng.permutation(E)[:k] for _ in range(T)], np.int32).reshape(T, k)
+
+
+PERMUTE_CASES = [
+    (1000, 8, 2, 1.25, 1, 64, "bf16", False), (777, 64, 6, 1.0, 4, 40, "bf16", True),
+    (300, 256, 8, 1.25, 8, 16, "bf16", False), (65, 4, 2, 0.3, 2, 8, "f32", True),
+    (64, 8, 2, 1.25, 1, 128, "f32", False), (1, 3, 2, 1.0, 1, 8, "bf16", False),
+    (129, 1, 1, 2.0, 1, 8, "bf16", False), (5000, 32, 4, 0.5, 8, 24, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("T,E,k,cf,P,d,dtype,skew", PERMUTE_CASES)
+def test_permute_is_exact(T, E, k, cf, P, d, dtype, skew):
+    say(f"permute T={T} E={E} k={k} cf={cf} P={P} d={d} {dtype} skew={skew}")
+    rng = np.random.default_rng(T + E + k)
+    idx = _random_routes(rng, T, E, k, skew)
+    x = moe_inputs.custom(T=T, d=d, E=E, k=k, d_ff=8, cf=cf, dtype=dtype, seed=5, reject=False).x
+    C = oracle.capacity(T, E, k, cf)
+    assert moe.moe_capacity(T, E, k, cf) == C
+    slot_r, src_r, routed_r, kept_r = oracle.assign_slots(idx, E, C)
+    st = oracle.routing_stats(slot_r, routed_r, kept_r, C, P, d, 2 if dtype == "bf16" else 4)
+    b_ref = oracle.dispatch_buckets(x, idx, slot_r, E, C)
+
+    eb = 2 if dtype == "bf16" else 4
+    sentinel = 0x7F7F if dtype == "bf16" else np.float32(-12345.5)
+    buckets = to_dev(np.full((E, C, d), sentinel, dtype=np.uint16 if dtype == "bf16" else np.float32), dtype)
+    slot, src, routed, kept, send = _i32(T, k), _i32(E, C), _i32(E), _i32(E), _i32(P)
+    totals = torch.empty(4, dtype=torch.int64, device="cuda")
+    ws_n = moe.moe_permute_workspace_size(T, E)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    moe.moe_permute(to_dev(x, dtype), torch.from_numpy(idx).cuda(), T, d, E, k, C, P, dtype, buckets, slot,
+                    src, routed, kept, send, totals, ws, ws_n)
+    torch.cuda.synchronize()
+    assert np.array_equal(slot.cpu().numpy(), slot_r)
+    assert np.array_equal(src.cpu().numpy().reshape(-1), src_r)
+    assert np.array_equal(routed.cpu().numpy(), routed_r)
+    assert np.array_equal(kept.cpu().numpy(), kept_r)
+    assert np.array_equal(send.cpu().numpy(), st["send_count"])
+    assert totals.cpu().numpy().tolist() == [st["dropped"], st["fully_dropped_tokens"], st["padded_rows"],
+                                             st["offrank_bytes"]]
+    got = to_host(buckets, dtype)
+    for e in range(E):
+        n = kept_r[e]
+        assert np.array_equal(got[e, :n].view(np.uint8), b_ref[e, :n].view(np.uint8)), f"expert {e}"
+        assert np.all(got[e, n:].view(np.uint8) == np.full((C - n, d), sentinel, got.dtype).view(np.uint8)), \
+            f"padding of expert {e} was written"
+    assert eb in (2, 4)
+
+
+# ------------------------------------------------------------- grouped GEMM ---
+
+GEMM_CASES = [
+    (4, 200, 256, 320, "bf16"), (8, 64, 128, 256, "f32"), (3, 300, 520, 136, "bf16"),
+    (16, 5, 128, 128, "bf16"), (2, 128, 64, 64, "bf16"), (1, 1, 8, 8, "bf16"), (5, 40, 36, 20, "f32"),
+]
+
+
+@pytest.mark.parametrize("E,C,d,d_ff,dtype", GEMM_CASES)
+def test_grouped_gemm_rows_below_kept(E, C, d, d_ff, dtype):
+    say(f"gemm E={E} C={C} d={d} d_ff={d_ff} {dtype}")
+    rng = np.random.default_rng(E * C + d)
+    kept = rng.integers(0, C + 1, E).astype(np.int32)
+    kept[0] = C
+    if E > 2:
+        kept[1] = 0
+    wl = moe_inputs.custom(T=E * C, d=d, E=E, k=1, d_ff=d_ff, cf=1.0, dtype=dtype, seed=E + d, reject=False,
+                           x_std=1.0)
+    X = wl.x.reshape(E, C, d).copy()
+    nan = 0x7FC0 if dtype == "bf16" else np.float32(np.nan)
+    for e in range(E):
+        X[e, kept[e]:] = nan                       # padding rows must not reach any result
+    wg, wu, wd = wl.all_expert_weights()
+    h_ref = np.zeros((E, C, d_ff))
+    y_ref = np.zeros((E, C, d))
+    for e in range(E):
+        n = kept[e]
+        if n:
+            Xe = bits_to_f64(X[e, :n], dtype)
+            h_ref[e, :n] = oracle.expert_hidden(Xe, oracle.decode(wg[e], dtype), oracle.decode(wu[e], dtype))
+            y_ref[e, :n] = oracle.expert_mlp(Xe, oracle.decode(wg[e], dtype), oracle.decode(wu[e], dtype),
+                                             oracle.decode(wd[e], dtype))
+    sent = 0x1234 if dtype == "bf16" else np.float32(777.0)
+    npdt = np.uint16 if dtype == "bf16" else np.float32
+    h = to_dev(np.full((E, C, d_ff), sent, npdt), dtype)
+    y = to_dev(np.full((E, C, d), sent, npdt), dtype)
+    ws_n = moe.moe_grouped_gemm_workspace_size(E, C)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    moe.moe_grouped_gemm(to_dev(X, dtype), torch.from_numpy(kept).cuda(), to_dev(wg, dtype), to_dev(wu, dtype),
+                         to_dev(wd, dtype), E, C, d, d_ff, dtype, h, y, ws, ws_n)
+    torch.cuda.synchronize()
+    hg, yg = to_host(h, dtype), to_host(y, dtype)
+    # bf16: h, y rounded to bf16 (2^-9 relative) and y consumes the rounded h;
+    # fp32: fp32 accumulation only.
+    tol_h, tol_y = (4e-3, 1e-2) if dtype == "bf16" else (1e-5, 1e-5)
+    for e in range(E):
+        n = kept[e]
+        if n:
+            assert row_rel_err(bits_to_f64(hg[e, :n], dtype), h_ref[e, :n]).max() <= tol_h, f"h expert {e}"
+            assert row_rel_err(bits_to_f64(yg[e, :n], dtype), y_ref[e, :n]).max() <= tol_y, f"y expert {e}"
+        assert np.all(hg[e, n:] == np.full((C - n, d_ff), sent, npdt)), f"h padding of expert {e} written"
+        assert np.all(yg[e, n:] == np.full((C - n, d), sent, npdt)), f"y padding of expert {e} written"
+
+
+# ------------------------------------------------------------------ combine ---
+
+COMBINE_CASES = [(500, 64, 8, 2, 1.0, "bf16"), (300, 40, 16, 4, 0.5, "bf16"), (64, 128, 8, 2, 1.25, "f32"),
+                 (200, 8, 4, 4, 0.25, "bf16"), (1, 16, 2, 1, 1.0, "f32")]
+
+
+@pytest.mark.parametrize("T,d,E,k,cf,dtype", COMBINE_CASES)
+def test_combine_inverse_and_passthrough(T, d, E, k, cf, dtype):
+    say(f"combine T={T} d={d} E={E} k={k} cf={cf} {dtype}")
+    rng = np.random.default_rng(T + d)
+    idx = _random_routes(rng, T, E, k, skew=True)
+    w = rng.random((T, k)).astype(np.float32)
+    w /= w.sum(1, keepdims=True)
+    C = oracle.capacity(T, E, k, cf)
+    slot, _, _, _ = oracle.assign_slots(idx, E, C)
+    wl = moe_inputs.custom(T=T, d=d, E=E, k=k, d_ff=8, cf=cf, dtype=dtype, seed=T, reject=False)
+    x = wl.x.copy()
+    x[:, 0] = 0x8000 if dtype == "bf16" else np.float32(-0.0)     # -0.0 must pass through untouched
+    ybits = moe_inputs.custom(T=E * C, d=d, E=E, k=k, d_ff=8, cf=cf, dtype=dtype, seed=T + 1,
+                              reject=False).x.reshape(E, C, d)
+    y64 = bits_to_f64(ybits, dtype)
+    x64 = bits_to_f64(x, dtype)
+    ycop = np.zeros((T, k, d))
+    for t in range(T):
+        for j in range(k):
+            if slot[t, j] >= 0:
+                ycop[t, j] = y64[idx[t, j], slot[t, j]]
+    ref = oracle.combine(x64, ycop, w, slot)
+    out = to_dev(np.zeros_like(x), dtype)
+    moe.moe_combine(to_dev(x, dtype), to_dev(ybits, dtype), torch.from_numpy(idx).cuda(),
+                    torch.from_numpy(w).cuda(), torch.from_numpy(slot).cuda(), T, d, E, k, C, dtype, out)
+    torch.cuda.synchronize()
+    got = to_host(out, dtype)
+    dropped = np.all(slot < 0, axis=1)
+    assert np.array_equal(got[dropped].view(np.uint8), x[dropped].view(np.uint8))
+    mag = np.abs(x64) + np.einsum("tj,tjd->td", np.where(slot >= 0, w, 0.0), np.abs(ycop))
+    # fp32 sum of k + 1 terms (k + 1 roundings), then one rounding to the output type
+    out_ulp = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -24
+    tol = out_ulp * np.abs(ref) + (k + 2) * U * mag + 1e-30
+    keep = ~dropped
+    assert np.all(np.abs(bits_to_f64(got[keep], dtype) - ref[keep]) <= tol[keep])
+
+
+def test_zero_tokens_is_a_no_op():
+    moe.moe_route(torch.zeros(1, device="cuda"), 0, 8, 2, _i32(1), _f32(1))
+    out = torch.full((4,), 3.0, device="cuda")
+    moe.moe_combine(out, out, _i32(1), _f32(1), _i32(1), 0, 4, 8, 2, 1, "f32", out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
