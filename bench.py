@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE-layer hot path on one MI355X.
+
+One step is one call of moe_layer_forward (router, top-k and gates, slots,
+bucket scatter, grouped SwiGLU GEMMs, combine) over one batch of tokens, with
+inputs and weights already resident in HBM. Default workload: the
+Mixtral-shaped prefill layer (T=4096 tokens, d=4096, E=8 experts, top-2,
+d_ff=14336, cf=1.25, bf16), synthetic seeded inputs.
+
+Prints one JSON line: routed tokens/s per layer (whole job), per-stage GPU
+times from HIP events recorded by the library around each stage, the
+roofline of the dominant kernel, and the CPU oracle timed on a bounded sample
+of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+METRIC = "routed tokens/s per MoE layer; grouped-GEMM % MFMA peak; permute % HBM BW"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_mixtral_prefill_traffic.txt")
+GEMM_SOURCE = os.path.join(ROOT, "routing_dispatch_expert_amd", "csrc", "grouped_gemm.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens whose output the oracle computes")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true", help="skip the per-stage event loop")
+    return ap.parse_args()
+
+
+def stage_work(wl, n_kept: int, touched: int):
+    """Algorithmic HBM bytes (and flops) of each stage for this run: kept rows
+    only, touched experts' weights only, every operand moved once."""
+    T, d, f, E, k = wl.T, wl.d, wl.d_ff, wl.E, wl.k
+    b = wl.elem_bytes
+    nt = -(-T // 64)
+    return {
+        "router": dict(bytes=T * d * b + E * d * b + T * E * 4, flops=2 * T * d * E, bound="hbm"),
+        "route": dict(bytes=T * E * 4 + T * k * 8, flops=0, bound="hbm"),
+        "slots": dict(bytes=3 * T * k * 4 + 4 * nt * E * 4, flops=0, bound="hbm"),
+        "scatter": dict(bytes=(T + n_kept) * d * b + T * k * 8, flops=0, bound="hbm"),
+        "gate_up": dict(bytes=touched * 2 * f * d * b + n_kept * (d + f) * b, flops=4 * n_kept * d * f,
+                        bound="mfma"),
+        "down": dict(bytes=touched * f * d * b + n_kept * (f + d) * b, flops=2 * n_kept * d * f, bound="mfma"),
+        "combine": dict(bytes=(n_kept + 2 * T) * d * b + T * k * 12, flops=0, bound="hbm"),
+    }
+
+
+def read_traffic(gemm_src_sha: str):
+    """HBM bytes per launch of the gate/up GEMM from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    txt = open(TRAFFIC_FILE).read()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not (m_sha and m_b) or m_sha.group(1) != gemm_src_sha:
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(wl, host_w, sample: int):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    tokens = np.arange(min(sample, wl.T))
+    t0 = time.perf_counter()
+    oracle.layer_forward(wl.x, wl.wr, lambda e: (host_w[0][e], host_w[1][e], host_w[2][e]), wl.T, wl.d,
+                         wl.d_ff, wl.E, wl.k, wl.cf, wl.dtype, P=wl.P, bias=wl.bias_vec, tokens=tokens)
+    dt = time.perf_counter() - t0
+    return {"value": round(tokens.size / dt, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"layer outputs of the first {tokens.size} of {wl.T} tokens (routing and slots of all "
+                      f"{wl.T}), fp64 numpy, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the layer here has no multi-GPU path (asked for --gpus "
+              f"{args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import moe_inputs
+    import routing_dispatch_expert_amd as moe
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    moe.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = moe_inputs.workload(args.workload)
+    print(f"[bench] workload {wl.name}: T={wl.T} d={wl.d} E={wl.E} k={wl.k} d_ff={wl.d_ff} cf={wl.cf} "
+          f"P={wl.P} {wl.dtype}", file=sys.stderr, flush=True)
+
+    def to_dev(a):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    host_w = wl.all_expert_weights()
+    x, wr = to_dev(wl.x), to_dev(wl.wr)
+    wg, wu, wd = (to_dev(a) for a in host_w)
+    bias = None if wl.bias_vec is None else torch.from_numpy(wl.bias_vec).to(dev)
+    T, d, d_ff, E, k, cf, P = wl.T, wl.d, wl.d_ff, wl.E, wl.k, wl.cf, wl.P
+    C = moe.moe_capacity(T, E, k, cf)
+    i32 = dict(dtype=torch.int32, device=dev)
+    outs = {"out": torch.empty_like(x), "topk_idx": torch.empty((T, k), **i32),
+            "topk_w": torch.empty((T, k), dtype=torch.float32, device=dev), "slot": torch.empty((T, k), **i32),
+            "routed_count": torch.empty(E, **i32), "kept_count": torch.empty(E, **i32),
+            "send_count": torch.empty(P, **i32), "totals": torch.empty(4, dtype=torch.int64, device=dev)}
+    ws_bytes = moe.moe_workspace_size(T, d, d_ff, E, k, cf, P, wl.dtype)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.moe_layer_forward(x, wr, bias, wg, wu, wd, T, d, d_ff, E, k, cf, P, wl.dtype, outs["out"], outs, ws,
+                              ws_bytes, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1) / args.steps
+    print(f"[bench] timed {args.steps} steps: {wall * 1e3 / args.steps:.3f} ms/step wall, {gpu_ms:.3f} ms/step "
+          f"GPU", file=sys.stderr, flush=True)
+
+    kept = outs["kept_count"].cpu().numpy()
+    n_kept, touched = int(kept.sum()), int((kept > 0).sum())
+    totals = outs["totals"].cpu().numpy().tolist()
+    work = stage_work(wl, n_kept, touched)
+
+    stages = {}
+    if not args.no_profile:
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(moe.STAGES))]
+        for e in evs:
+            e.record(stream)           # creates the underlying hipEvent_t
+        torch.cuda.synchronize()
+        moe.moe_set_stage_events([e.cuda_event for e in evs])
+        acc = np.zeros(len(moe.STAGES))
+        try:
+            for _ in range(args.steps):
+                step()
+                torch.cuda.synchronize()
+                acc += [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(len(moe.STAGES))]
+        finally:
+            moe.moe_set_stage_events(None)
+        for i, name in enumerate(moe.STAGES):
+            ms = acc[i] / args.steps
+            w = work[name]
+            s = {"ms": round(ms, 5), "algo_bytes": int(w["bytes"]),
+                 "GB_per_s": round(w["bytes"] / ms / 1e6, 1) if ms > 0 else None,
+                 "hbm_frac": round(w["bytes"] / ms / 1e6 / PEAK_HBM_GBS, 4) if ms > 0 else None}
+            if w["flops"]:
+                s["TFLOP_per_s"] = round(w["flops"] / ms / 1e9, 1) if ms > 0 else None
+                s["mfma_frac"] = round(w["flops"] / ms / 1e9 / PEAK_TFLOPS[wl.dtype], 4) if ms > 0 else None
+            stages[name] = s
+            print(f"[bench] stage {name:8s} {ms:8.4f} ms  " + " ".join(f"{a}={b}" for a, b in s.items()
+                                                                       if a != "ms"), file=sys.stderr, flush=True)
+
+    roofline = None
+    if stages:
+        dom = max(stages, key=lambda n: stages[n]["ms"])
+        w, s = work[dom], stages[dom]
+        sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+        traffic = read_traffic(sha) if (dom == "gate_up" and wl.name == "mixtral_prefill") else None
+        if w["bound"] == "mfma":
+            roofline = {"bound": "mfma", "achieved": s["TFLOP_per_s"], "peak": PEAK_TFLOPS[wl.dtype],
+                        "unit": "TFLOP/s", "frac": s["mfma_frac"], "traffic": traffic, "kernel": dom,
+                        "algo_flops_per_launch": int(w["flops"]), "avg_launch_ms": s["ms"]}
+        else:
+            roofline = {"bound": "hbm", "achieved": s["GB_per_s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": s["hbm_frac"], "traffic": traffic, "kernel": dom,
+                        "algo_bytes_per_launch": int(w["bytes"]), "avg_launch_ms": s["ms"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print(f"[bench] timing the CPU oracle on {min(args.cpu_sample, T)} tokens", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, host_w, args.cpu_sample)
+
+    line = {
+        "metric": METRIC, "value": round(T * args.steps / wall, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded Gaussian inputs and random-init weights of the named shape)",
+        "config": {"workload": wl.name, "T": T, "d": d, "E": E, "k": k, "d_ff": d_ff, "cf": cf, "P": P, "C": C,
+                   "N_kept": n_kept, "touched_experts": touched, "dropped": totals[0]},
+        "gpu_ms_per_step": round(gpu_ms, 4),
+        "grouped_gemm_mfma_frac": None if not stages else round(
+            (work["gate_up"]["flops"] + work["down"]["flops"]) /
+            ((stages["gate_up"]["ms"] + stages["down"]["ms"]) * 1e9) / PEAK_TFLOPS[wl.dtype], 4),
+        "permute_hbm_frac": None if not stages else stages["scatter"]["hbm_frac"],
+        "combine_hbm_frac": None if not stages else stages["combine"]["hbm_frac"],
+        "stages": stages, "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -169,6 +169,25 @@ int moe_combine(const void* x, const void* y, const int32_t* topk_idx, const flo
                 const int32_t* slot, int64_t T, int64_t d, int32_t E, int32_t k, int64_t C,
                 moe_dtype_t dtype, void* out, void* stream);
 
+/* Stages of moe_layer_forward, in launch order. */
+enum {
+  MOE_STAGE_ROUTER = 0,   /* scores on the matrix cores */
+  MOE_STAGE_ROUTE = 1,    /* top-k and gates */
+  MOE_STAGE_SLOTS = 2,    /* tile histogram, scan, capacity, counts, slots */
+  MOE_STAGE_SCATTER = 3,  /* row copies into the buckets */
+  MOE_STAGE_GATE_UP = 4,  /* grouped GEMM 1 with the SwiGLU product */
+  MOE_STAGE_DOWN = 5,     /* grouped GEMM 2 */
+  MOE_STAGE_COMBINE = 6,  /* inverse permutation and weighted sum */
+  MOE_NUM_STAGES = 7
+};
+
+/* Profiling aid. With events set (2 * MOE_NUM_STAGES caller-created
+ * hipEvent_t handles), moe_layer_forward on the calling thread records
+ * events[2 i] on its stream just before stage i and events[2 i + 1] just
+ * after, so the caller can read each stage's GPU time. events = NULL turns
+ * this off (the default). Error: n_events != 2 * MOE_NUM_STAGES. */
+int moe_set_stage_events(void* const* events, int n_events);
+
 /* Static description of a status code. */
 const char* moe_status_string(int status);
 

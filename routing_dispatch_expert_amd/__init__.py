@@ -24,7 +24,8 @@ TOTALS = ("dropped", "fully_dropped_tokens", "padded_rows", "offrank_bytes")
 
 EXPORTS = ("moe_capacity", "moe_workspace_size", "moe_layer_forward", "moe_router", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_grouped_gemm_workspace_size",
-           "moe_grouped_gemm", "moe_combine", "moe_status_string", "moe_last_error")
+           "moe_grouped_gemm", "moe_combine", "moe_set_stage_events", "moe_status_string", "moe_last_error")
+STAGES = ("router", "route", "slots", "scatter", "gate_up", "down", "combine")
 
 
 class MoeError(RuntimeError):
@@ -55,6 +56,7 @@ _SIGS = {
     "moe_grouped_gemm_workspace_size": [_I32, _I64, _P],
     "moe_grouped_gemm": [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P, _SZ, _P],
     "moe_combine": [_P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I64, ctypes.c_int, _P, _P],
+    "moe_set_stage_events": [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int],
 }
 
 
@@ -197,6 +199,15 @@ def moe_grouped_gemm(buckets, kept_count, W_gate, W_up, W_down, E, C, d, d_ff, d
 def moe_combine(x, y, topk_idx, topk_w, slot, T, d, E, k, C, dtype, out, stream=None):
     _check(lib().moe_combine(_ptr(x), _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(slot), T, d, E, k, C,
                              _dtype(dtype), _ptr(out), _stream(stream)), "moe_combine")
+
+
+def moe_set_stage_events(events):
+    """events: None (off) or 2 * len(STAGES) raw hipEvent_t handles (ints)."""
+    if events is None:
+        _check(lib().moe_set_stage_events(None, 0), "moe_set_stage_events")
+        return
+    arr = (ctypes.c_void_p * len(events))(*events)
+    _check(lib().moe_set_stage_events(arr, len(events)), "moe_set_stage_events")
 
 
 # ----------------------------------------------------------------- convenience

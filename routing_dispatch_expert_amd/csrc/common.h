@@ -55,9 +55,14 @@ hipError_t launch_scatter_rows(const void* x, const int32_t* idx, const int32_t*
 // Row-tile height the grouped GEMM uses for these sizes (the mtile map must
 // be built for the same value).
 int grouped_gemm_bm(bool bf16, int64_t C);
-hipError_t launch_grouped_gemm(const void* buckets, const int32_t* kept, const int32_t* mtile_off,
-                               const void* wg, const void* wu, const void* wd, int E, int64_t C,
-                               int64_t d, int64_t d_ff, bool bf16, void* h, void* y, hipStream_t s);
+// GEMM 1: h = silu(X Wg^T) * (X Wu^T) on rows < kept.
+hipError_t launch_gemm_gate_up(const void* buckets, const int32_t* kept, const int32_t* mtile_off,
+                               const void* wg, const void* wu, int E, int64_t C, int64_t d,
+                               int64_t d_ff, bool bf16, void* h, hipStream_t s);
+// GEMM 2: y = h Wd^T on rows < kept.
+hipError_t launch_gemm_down(const void* h, const int32_t* kept, const int32_t* mtile_off,
+                            const void* wd, int E, int64_t C, int64_t d, int64_t d_ff, bool bf16,
+                            void* y, hipStream_t s);
 
 // ---- combine (combine.hip) ----
 hipError_t launch_combine(const void* x, const void* y, const int32_t* idx, const float* w,

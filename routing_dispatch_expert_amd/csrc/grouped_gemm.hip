@@ -252,34 +252,37 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 int grouped_gemm_bm(bool bf16, int64_t /*C*/) { return bf16 ? 128 : 64; }
 
-hipError_t launch_grouped_gemm(const void* buckets, const int32_t* kept, const int32_t* mtile_off,
-                               const void* wg, const void* wu, const void* wd, int E, int64_t C,
-                               int64_t d, int64_t d_ff, bool bf16, void* h, void* y,
-                               hipStream_t s) {
+hipError_t launch_gemm_gate_up(const void* buckets, const int32_t* kept, const int32_t* mtile_off,
+                               const void* wg, const void* wu, int E, int64_t C, int64_t d,
+                               int64_t d_ff, bool bf16, void* h, hipStream_t s) {
   const int bm = grouped_gemm_bm(bf16, C);
   const unsigned mtiles = static_cast<unsigned>(E * ceil_div(C, bm));  // upper bound of live tiles
   if (mtiles == 0) return hipSuccess;
-  if (bf16) {
-    const auto* X = static_cast<const bf16_t*>(buckets);
+  if (bf16)
     gemm_bf16_kernel<true><<<dim3(mtiles, static_cast<unsigned>(ceil_div(d_ff, 64))), dim3(256), 0, s>>>(
-        X, static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu), static_cast<bf16_t*>(h),
-        kept, mtile_off, E, C, d, d_ff);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+        static_cast<const bf16_t*>(buckets), static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu),
+        static_cast<bf16_t*>(h), kept, mtile_off, E, C, d, d_ff);
+  else
+    gemm_f32_kernel<true><<<dim3(mtiles, static_cast<unsigned>(ceil_div(d_ff, 64))), dim3(256), 0, s>>>(
+        static_cast<const float*>(buckets), static_cast<const float*>(wg), static_cast<const float*>(wu),
+        static_cast<float*>(h), kept, mtile_off, E, C, d, d_ff);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_down(const void* h, const int32_t* kept, const int32_t* mtile_off,
+                            const void* wd, int E, int64_t C, int64_t d, int64_t d_ff, bool bf16,
+                            void* y, hipStream_t s) {
+  const int bm = grouped_gemm_bm(bf16, C);
+  const unsigned mtiles = static_cast<unsigned>(E * ceil_div(C, bm));
+  if (mtiles == 0) return hipSuccess;
+  if (bf16)
     gemm_bf16_kernel<false><<<dim3(mtiles, static_cast<unsigned>(ceil_div(d, 128))), dim3(256), 0, s>>>(
-        static_cast<const bf16_t*>(h), static_cast<const bf16_t*>(wd), nullptr,
-        static_cast<bf16_t*>(y), kept, mtile_off, E, C, d_ff, d);
-    return hipGetLastError();
-  }
-  const auto* X = static_cast<const float*>(buckets);
-  gemm_f32_kernel<true><<<dim3(mtiles, static_cast<unsigned>(ceil_div(d_ff, 64))), dim3(256), 0, s>>>(
-      X, static_cast<const float*>(wg), static_cast<const float*>(wu), static_cast<float*>(h), kept,
-      mtile_off, E, C, d, d_ff);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  gemm_f32_kernel<false><<<dim3(mtiles, static_cast<unsigned>(ceil_div(d, 64))), dim3(256), 0, s>>>(
-      static_cast<const float*>(h), static_cast<const float*>(wd), nullptr, static_cast<float*>(y),
-      kept, mtile_off, E, C, d_ff, d);
+        static_cast<const bf16_t*>(h), static_cast<const bf16_t*>(wd), nullptr, static_cast<bf16_t*>(y), kept,
+        mtile_off, E, C, d_ff, d);
+  else
+    gemm_f32_kernel<false><<<dim3(mtiles, static_cast<unsigned>(ceil_div(d, 64))), dim3(256), 0, s>>>(
+        static_cast<const float*>(h), static_cast<const float*>(wd), nullptr, static_cast<float*>(y), kept,
+        mtile_off, E, C, d_ff, d);
   return hipGetLastError();
 }
 

@@ -14,6 +14,14 @@
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local hipEvent_t g_stage_ev[2 * MOE_NUM_STAGES];
+thread_local bool g_stage_ev_on = false;
+
+// Records the start (end = false) or end event of a stage when profiling is on.
+hipError_t stage_mark(int stage, bool end, hipStream_t s) {
+  if (!g_stage_ev_on) return hipSuccess;
+  return hipEventRecord(g_stage_ev[2 * stage + (end ? 1 : 0)], s);
+}
 
 int fail(int status, const char* fmt, ...) {
   va_list ap;
@@ -157,6 +165,21 @@ const char* moe_status_string(int status) {
 
 const char* moe_last_error(void) { return g_err; }
 
+int moe_set_stage_events(void* const* events, int n_events) {
+  if (!events) {
+    g_stage_ev_on = false;
+    return MOE_OK;
+  }
+  if (n_events != 2 * MOE_NUM_STAGES)
+    return fail(MOE_ERR_INVALID_ARG, "need %d events, got %d", 2 * MOE_NUM_STAGES, n_events);
+  for (int i = 0; i < n_events; ++i) {
+    if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "event %d is NULL", i);
+    g_stage_ev[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  g_stage_ev_on = true;
+  return MOE_OK;
+}
+
 int moe_capacity(int64_t T, int32_t E, int32_t k, float cf, int64_t* C_out) {
   if (!C_out) return fail(MOE_ERR_INVALID_ARG, "C_out is NULL");
   int64_t C;
@@ -210,19 +233,34 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
   const int64_t nt = moe::ceil_div(T, moe::kTileTokens);
   const int bm = moe::grouped_gemm_bm(bf16, C);
 
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTER, false, s), "event");
   MOE_HIP_TRY(moe::launch_router_logits(x, W_router, router_bias, T, d, E, bf16, p.logits, s),
               "router logits");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTER, true, s), "event");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTE, false, s), "event");
   MOE_HIP_TRY(moe::launch_route(p.logits, T, E, k, idx, w, s), "route");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTE, true, s), "event");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_SLOTS, false, s), "event");
   MOE_HIP_TRY(moe::launch_tile_hist(idx, T, k, E, p.tile_cnt, s), "tile histogram");
   MOE_HIP_TRY(moe::launch_scan(p.tile_cnt, nt, E, C, P, d * eb, k, T, p.tile_off, routed, kept, send,
                                totals, bm, p.mtile, src, s),
               "scan");
   MOE_HIP_TRY(moe::launch_slots(idx, p.tile_off, T, k, E, C, slot, src, totals, s), "slots");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_SLOTS, true, s), "event");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, false, s), "event");
   MOE_HIP_TRY(moe::launch_scatter_rows(x, idx, slot, T, k, C, d * eb, buckets, s), "scatter");
-  MOE_HIP_TRY(moe::launch_grouped_gemm(buckets, kept, p.mtile, W_gate, W_up, W_down, E, C, d, d_ff,
-                                       bf16, p.h, p.y, s),
-              "grouped gemm");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, true, s), "event");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, false, s), "event");
+  MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, p.mtile, W_gate, W_up, E, C, d, d_ff, bf16, p.h, s),
+              "grouped gemm (gate, up)");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, true, s), "event");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, false, s), "event");
+  MOE_HIP_TRY(moe::launch_gemm_down(p.h, kept, p.mtile, W_down, E, C, d, d_ff, bf16, p.y, s),
+              "grouped gemm (down)");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, true, s), "event");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_COMBINE, false, s), "event");
   MOE_HIP_TRY(moe::launch_combine(x, p.y, idx, w, slot, T, d, k, C, bf16, out, s), "combine");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_COMBINE, true, s), "event");
   return MOE_OK;
 }
 
@@ -333,9 +371,10 @@ int moe_grouped_gemm(const void* buckets, const int32_t* kept_count, const void*
   const bool bf16 = dtype == MOE_DTYPE_BF16;
   auto* mtile = static_cast<int32_t*>(workspace);
   MOE_HIP_TRY(moe::launch_mtile_map(kept_count, E, moe::grouped_gemm_bm(bf16, C), mtile, s), "tile map");
-  MOE_HIP_TRY(moe::launch_grouped_gemm(buckets, kept_count, mtile, W_gate, W_up, W_down, E, C, d, d_ff,
-                                       bf16, h, y, s),
-              "grouped gemm");
+  MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept_count, mtile, W_gate, W_up, E, C, d, d_ff, bf16, h, s),
+              "grouped gemm (gate, up)");
+  MOE_HIP_TRY(moe::launch_gemm_down(h, kept_count, mtile, W_down, E, C, d, d_ff, bf16, y, s),
+              "grouped gemm (down)");
   return MOE_OK;
 }
 
