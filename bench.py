@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens whose output the oracle computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-stage event loop")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first copy a buffer of this many MiB on the device (a reference kernel of known "
+                         "traffic for hardware counters)")
     return ap.parse_args()
 
 
@@ -138,6 +141,13 @@ def main():
     def step():
         moe.moe_layer_forward(x, wr, bias, wg, wu, wd, T, d, d_ff, E, k, cf, P, wl.dtype, outs["out"], outs, ws,
                               ws_bytes, stream)
+
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

@@ -41,7 +41,8 @@
  *    error: it drops copies. Inputs must be finite (NaN/Inf give unspecified
  *    routing).
  *  - Limits (else MOE_ERR_UNSUPPORTED): d and d_ff multiples of 8 (fp32: of 4),
- *    E <= 4096, k <= 32, T * k < 2^31, E * C < 2^31.
+ *    E <= 4096, k <= 32, T * k < 2^31, E * C < 2^31, and per expert
+ *    (C + 256) * max(d, d_ff) * 4 < 2^31 and d * d_ff * 4 < 2^31 bytes.
  */
 #ifndef MOE_H_
 #define MOE_H_

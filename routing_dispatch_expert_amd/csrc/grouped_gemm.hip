@@ -14,6 +14,8 @@
 // padding rows beyond kept[e] cost no tiles: a work-group maps its row-tile id
 // to (expert, tile) by binary search over that prefix and exits when the id
 // is past the last live tile.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -35,132 +37,442 @@ __device__ inline int owner_expert(const int32_t* __restrict__ mtile_off, int E,
 __device__ inline float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // ---------------------------------------------------------------------------
-// bf16 matrix-core GEMM: a 128 x 128 block of A B^T per work-group (4 waves,
-// 2 x 2, each 64 x 64 as 2 x 2 tiles of v_mfma_f32_32x32x16_bf16), K in steps
-// of 64 through double-buffered LDS (rows padded by 8 elements). With SWIGLU,
-// the 128 B rows are 64 gate rows then the same 64 up rows, and each wave
-// holds gate and up accumulators of the same 32 output columns, so the SwiGLU
-// product is taken in registers and only h is stored.
+// bf16 matrix-core GEMM, one BM x BN block of A B^T per work-group of 4 waves
+// (2 x 2). Each wave owns a (BM/2) x (BN/2) block as TM x TN tiles of
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulators. K advances 64 at a time
+// through two LDS buffers: the next step's tile is fetched into registers
+// while the current one feeds the matrix cores, so one barrier per step.
+// LDS rows are 64 elements (eight 16-byte chunks) with chunk c of row r kept
+// at position c ^ (r % 8), so the 32 rows a wave reads at once spread over
+// all banks.
+// With SWIGLU the BN rows of B are BN/2 gate rows then the same BN/2 up rows,
+// and each wave holds gate and up accumulators of the same output columns, so
+// silu(g) * u is taken in registers and only h is stored.
 // Operand lane layout: lane l holds row (l % 32), K elements 8*(l/32) .. +8;
-// accumulator element r of lane l is row 8*(r/4) + 4*(l/32) + r%4, col l%32.
+// accumulator element q of lane l is row 8*(q/4) + 4*(l/32) + q%4, col l%32.
+// Tile order: the live tiles (kept rows only) are numbered expert by expert;
+// inside an expert, column tiles come in groups of kGroupN, and each group
+// walks all of the expert's row tiles. Hardware hands block b to XCD b % 8;
+// block b takes tile (b % 8) * ceil(L / 8) + b / 8 of the L live tiles, so
+// each XCD works through one contiguous eighth, and the blocks running
+// together on an XCD share the expert's row tiles (A) and a group of weight
+// tiles (B) in its L2.
 // ---------------------------------------------------------------------------
-template <bool SWIGLU>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const bf16_t* __restrict__ A,
-                                                        const bf16_t* __restrict__ B0,
-                                                        const bf16_t* __restrict__ B1,
-                                                        bf16_t* __restrict__ out,
-                                                        const int32_t* __restrict__ kept,
-                                                        const int32_t* __restrict__ mtile_off,
-                                                        int E, int64_t C, int64_t K, int64_t N) {
-  constexpr int BM = 128, BK = 64, LDK = BK + 8;
-  constexpr int BNO = SWIGLU ? 64 : 128;  // output columns per work-group
-  __shared__ bf16_t As[2][BM][LDK];
-  __shared__ bf16_t Bs[2][128][LDK];
+constexpr int kGroupN = 8;
 
-  const int mt = blockIdx.x;
-  if (mt >= mtile_off[E]) return;
-  const int e = owner_expert(mtile_off, E, mt);
-  const int m0 = (mt - mtile_off[e]) * BM;
-  const int rows = kept[e];
-  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BNO;
+template <int BM>
+__device__ inline bool tile_of_block(const int32_t* __restrict__ mtile_off, int E, int nt_count,
+                                     int* e_out, int* m0_out, int* nt_out, int* lid_out = nullptr) {
+  const int64_t live = static_cast<int64_t>(mtile_off[E]) * nt_count;
+  const int64_t per_xcd = (live + 7) / 8;
+  const int64_t slot = blockIdx.x / 8;
+  if (slot >= per_xcd) return false;
+  const int64_t lid = (blockIdx.x % 8) * per_xcd + slot;
+  if (lid >= live) return false;
+  const int e = owner_expert(mtile_off, E, static_cast<int>(lid / nt_count));
+  const int mte = mtile_off[e + 1] - mtile_off[e];
+  const int64_t li = lid - static_cast<int64_t>(mtile_off[e]) * nt_count;
+  const int64_t grp = li / (static_cast<int64_t>(mte) * kGroupN);
+  const int r = static_cast<int>(li - grp * mte * kGroupN);
+  *e_out = e;
+  *m0_out = (r % mte) * BM;
+  *nt_out = static_cast<int>(grp * kGroupN + r / mte);
+  if (lid_out) *lid_out = static_cast<int>(lid);
+  return true;
+}
 
+// Raw buffer resource over [base, base + bytes): loads past `bytes` return 0.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+__device__ inline uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+  return uint4{static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1]), static_cast<uint32_t>(v[2]),
+               static_cast<uint32_t>(v[3])};
+}
+
+// Scheduling hints: instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
+
+template <int BM, int BN, bool SWIGLU>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BM >= 256 ? 1 : 2))) void gemm_bf16_kernel(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
+    bf16_t* __restrict__ out, const int32_t* __restrict__ kept, const int32_t* __restrict__ mtile_off,
+    int E, int64_t C, int64_t K, int64_t N, int nt_count) {
+  constexpr int BK = 64;
+  constexpr int TM = BM / 64, TN = BN / 64;      // 32 x 32 tiles per wave
+  constexpr int AL = BM * (BK / 8) / 256;        // 16-byte chunks per thread
+  constexpr int BL = BN * (BK / 8) / 256;
+  constexpr int BNO = SWIGLU ? BN / 2 : BN;      // output columns per work-group
+  constexpr int NMFMA = TM * TN;                 // MFMAs per 16-wide K step
+  constexpr int NFRAG = TM + TN;                 // LDS fragment reads per K step
+  __shared__ uint4 As[2][BM * 8];
+  __shared__ uint4 Bs[2][BN * 8];
+
+  int e, m0, nt;
+  if (!tile_of_block<BM>(mtile_off, E, nt_count, &e, &m0, &nt)) return;
+  // the tile is the same for the whole work-group: keep it in scalar registers
+  e = __builtin_amdgcn_readfirstlane(e);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  const int rows = __builtin_amdgcn_readfirstlane(kept[e]);
+  const int64_t n0 = static_cast<int64_t>(nt) * BNO;
+
+  // Global operands through raw buffer loads: one 32-bit offset per chunk,
+  // the K position in a scalar offset. Rows past C (A) or N (B) and K past
+  // the end read as zero; rows in [kept, C) are padding whose results are
+  // never stored.
   const int tid = threadIdx.x;
-  const bf16_t* Ae = A + static_cast<int64_t>(e) * C * K;
-  const bf16_t* a_ptr[4];
-  const bf16_t* b_ptr[4];
-  int ld_row[4], ld_col[4];
+  const int lrow = tid >> 3;   // first row this thread loads; then every 32nd
+  const int lch = tid & 7;     // 16-byte chunk within the 64-element row
+  const uint32_t a_bytes = static_cast<uint32_t>(C * K * 2);
+  const uint32_t b_bytes = static_cast<uint32_t>(N * K * 2);
+  const auto ra_src = buffer_rsrc(A + static_cast<int64_t>(e) * C * K, a_bytes);
+  const auto rb_src0 = buffer_rsrc(B0 + static_cast<int64_t>(e) * N * K, b_bytes);
+  const auto rb_src1 = buffer_rsrc((SWIGLU ? B1 : B0) + static_cast<int64_t>(e) * N * K, b_bytes);
+  uint32_t a_off[AL], b_off[BL];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int c = tid + 256 * r;
-    ld_row[r] = c >> 3;
-    ld_col[r] = (c & 7) * 8;
-    const int64_t ar = min(m0 + ld_row[r], rows - 1);  // rows past kept: computed, never stored
-    a_ptr[r] = Ae + ar * K + ld_col[r];
-    const bf16_t* bsrc;
-    int64_t br;
-    if (SWIGLU) {
-      bsrc = ld_row[r] < 64 ? B0 : B1;
-      br = n0 + (ld_row[r] & 63);
-    } else {
-      bsrc = B0;
-      br = n0 + ld_row[r];
-    }
-    br = min(br, N - 1);
-    b_ptr[r] = bsrc + (static_cast<int64_t>(e) * N + br) * K + ld_col[r];
+  for (int r = 0; r < AL; ++r) a_off[r] = static_cast<uint32_t>((m0 + lrow + 32 * r) * K * 2 + lch * 16);
+#pragma unroll
+  for (int r = 0; r < BL; ++r) {
+    const int br = lrow + 32 * r;
+    const int64_t bn = n0 + (SWIGLU ? (br % (BN / 2)) : br);
+    b_off[r] = bn < N ? static_cast<uint32_t>(bn * K * 2 + lch * 16) : 0x80000000u;
   }
-
-  uint4 ra[4], rb[4];
+  uint4 ra[AL], rb[BL];
   auto gload = [&](int64_t k0) {
+    const uint32_t mask = (k0 + lch * 8 < K) ? 0u : 0x80000000u;  // K is a multiple of 8
+    const uint32_t soff = static_cast<uint32_t>(k0 * 2);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool in = k0 + ld_col[r] < K;  // K is a multiple of 8
-      ra[r] = in ? *reinterpret_cast<const uint4*>(a_ptr[r] + k0) : uint4{0, 0, 0, 0};
-      rb[r] = in ? *reinterpret_cast<const uint4*>(b_ptr[r] + k0) : uint4{0, 0, 0, 0};
-    }
+    for (int r = 0; r < AL; ++r) ra[r] = buffer_load16(ra_src, a_off[r] | mask, soff);
+#pragma unroll
+    for (int r = 0; r < BL; ++r)
+      rb[r] = buffer_load16((SWIGLU && r >= BL / 2) ? rb_src1 : rb_src0, b_off[r] | mask, soff);
   };
+  // LDS rows are eight 16-byte chunks; chunk c of row r sits at c ^ ((r / 2) % 8)
+  // so 16 lanes reading 16 consecutive rows hit 16 distinct bank groups.
+  const int swz = lch ^ ((lrow >> 1) & 7);  // rows lrow + 32 r share (row / 2) % 8
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      *reinterpret_cast<uint4*>(&As[buf][ld_row[r]][ld_col[r]]) = ra[r];
-      *reinterpret_cast<uint4*>(&Bs[buf][ld_row[r]][ld_col[r]]) = rb[r];
-    }
+    for (int r = 0; r < AL; ++r) As[buf][(lrow + 32 * r) * 8 + swz] = ra[r];
+#pragma unroll
+    for (int r = 0; r < BL; ++r) Bs[buf][(lrow + 32 * r) * 8 + swz] = rb[r];
   };
 
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int lr = lane & 31, lk = (lane >> 5) * 8;
-  f32x16 acc[2][2];
+  const int lr = lane & 31, lk = lane >> 5;
+  int a_row[TM], b_row[TN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i) a_row[i] = (wm * (BM / 2) + i * 32 + lr) * 8;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < TN; ++j) {
+    int br;
+    if (SWIGLU)
+      br = (j < TN / 2) ? (wn * (BN / 4) + j * 32) : (BN / 2 + wn * (BN / 4) + (j - TN / 2) * 32);
+    else
+      br = wn * (BN / 2) + j * 32;
+    b_row[j] = (br + lr) * 8;
+  }
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
+  // Fragments of one 16-wide K step, double-buffered in registers so the
+  // next step's LDS reads are in flight while this step's MFMAs issue.
+  bf16x8 fa[2][TM], fb[2][TN];
+  const int rsw = (lr >> 1) & 7;  // (row / 2) % 8 of every row this lane reads
+  auto fload = [&](int buf, int ks, int slot) {
+    const int pc = (ks * 2 + lk) ^ rsw;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[slot][i] = *reinterpret_cast<const bf16x8*>(&As[buf][a_row[i] + pc]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[slot][j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][b_row[j] + pc]);
+  };
+  auto mfmas = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+  };
+
+  // Per 64-wide K stage kt (LDS buffer cur holds it; the fragments of its
+  // first 16-wide step are in slot 0; the registers ra/rb hold stage kt + 1,
+  // fetched one stage earlier):
+  //   step 0: read step 1's fragments
+  //   step 1: read step 2's fragments
+  //   step 2: read step 3's fragments; store stage kt + 1 into the other LDS
+  //           buffer, then fetch stage kt + 2 into ra/rb
+  //   barrier; read stage kt + 1's step 0 fragments
+  //   step 3: MFMAs only (they overlap the barrier and those reads)
+  // A fetch thus has a whole stage of MFMAs to arrive.
   const int64_t nk = ceil_div(K, BK);
+  auto stage = [&](int64_t kt, bool store_next, bool fetch) {
+    const int cur = static_cast<int>(kt & 1);
+    fload(cur, 1, 1);
+    mfmas(0);
+#pragma unroll
+    for (int g = 0; g < NFRAG; ++g) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA / NFRAG, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    fload(cur, 2, 0);
+    mfmas(1);
+#pragma unroll
+    for (int g = 0; g < NFRAG; ++g) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA / NFRAG, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    fload(cur, 3, 1);
+    if (store_next) sstore(cur ^ 1);
+    if (fetch) gload((kt + 2) * BK);
+    mfmas(0);
+    if (store_next && fetch) {
+#pragma unroll
+      for (int g = 0; g < NFRAG; ++g) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA / NFRAG, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, (AL + BL) / NFRAG, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, (AL + BL) / NFRAG, 0);
+      }
+    }
+    if (store_next) {
+      __builtin_amdgcn_sched_barrier(0);  // nothing moves across the barrier
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      fload(cur ^ 1, 0, 0);
+    }
+    mfmas(1);
+#pragma unroll
+    for (int g = 0; g < NFRAG; ++g) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA / NFRAG, 0);
+    }
+  };
+
   gload(0);
   sstore(0);
+  if (nk > 1) gload(BK);
   __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int cur = static_cast<int>(kt & 1);
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(&As[cur][wm * 64 + i * 32 + lr][ks * 16 + lk]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int brow = SWIGLU ? (j * 64 + wn * 32) : (wn * 64 + j * 32);
-        b[j] = *reinterpret_cast<const bf16x8*>(&Bs[cur][brow + lr][ks * 16 + lk]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
-  }
+  fload(0, 0, 0);
+  int64_t kt = 0;
+  for (; kt + 2 < nk; ++kt) stage(kt, true, true);  // no branches inside a stage
+  if (kt + 1 < nk) stage(kt++, true, false);
+  stage(kt, false, false);
 
   bf16_t* oute = out + static_cast<int64_t>(e) * C * N;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    for (int q = 0; q < 16; ++q) {
+      const int row = m0 + wm * (BM / 2) + i * 32 + 8 * (q >> 2) + 4 * lk + (q & 3);
       if (row >= rows) continue;
       if (SWIGLU) {
-        const int64_t col = n0 + wn * 32 + lr;
-        if (col < N) oute[row * N + col] = f32_to_bf16(silu(acc[i][0][r]) * acc[i][1][r]);
+#pragma unroll
+        for (int j = 0; j < TN / 2; ++j) {
+          const int64_t col = n0 + wn * (BN / 4) + j * 32 + lr;
+          if (col < N) oute[row * N + col] = f32_to_bf16(silu(acc[i][j][q]) * acc[i][j + TN / 2][q]);
+        }
       } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int64_t col = n0 + wn * 64 + j * 32 + lr;
-          if (col < N) oute[row * N + col] = f32_to_bf16(acc[i][j][r]);
+        for (int j = 0; j < TN; ++j) {
+          const int64_t col = n0 + wn * (BN / 2) + j * 32 + lr;
+          if (col < N) oute[row * N + col] = f32_to_bf16(acc[i][j][q]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 matrix-core GEMM with the operands brought into LDS by the buffer
+// unit itself (buffer_load_dwordx4 ... lds), bypassing registers. 256 x 256
+// block, 4 waves (2 x 2) of 128 x 128, each as 4 x 4 v_mfma_f32_32x32x16_bf16
+// tiles; K in 64-wide stages (every row a whole 128-byte line) through two
+// LDS slots: stage k + 1 streams in while stage k feeds the matrix cores.
+// Needs K % 128 == 0.
+// LDS rows are 64 elements (eight 16-byte chunks); chunk c of row r sits at
+// c ^ ((r / 2) % 8), so 16 lanes reading 16 consecutive rows hit 16 distinct
+// bank groups. One DMA instruction of a wave fills 8 rows (1 KiB): lane L
+// writes row L / 8, position L % 8, and so fetches the chunk that belongs
+// there. Each slot is its own LDS array, so the compiler can tell the stages
+// apart and the only waits on the DMA are the explicit ones below.
+// ---------------------------------------------------------------------------
+#define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt encodings (gfx9 family): vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8; a field at its maximum does not wait.
+template <int VM>
+__device__ inline void wait_vm_lgkm0() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
+}
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_dma_kernel(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
+    bf16_t* __restrict__ out, const int32_t* __restrict__ kept, const int32_t* __restrict__ mtile_off,
+    int E, int64_t C, int64_t K, int64_t N, int nt_count) {
+  constexpr int BM = 256, BN = 256, BK = 64, TM = 4, TN = 4;
+  constexpr int CH = BK / 8;                    // 16-byte chunks per LDS row
+  constexpr int BNO = SWIGLU ? BN / 2 : BN;
+  constexpr int PER_WAVE = BM / 8 / 4;          // 8-row DMA blocks per wave and operand
+  constexpr int NMFMA = TM * TN, NFRAG = TM + TN;
+  __shared__ uint4 As0[BM * CH], As1[BM * CH];
+  __shared__ uint4 Bs0[BN * CH], Bs1[BN * CH];
+
+  int e, m0, nt;
+  if (!tile_of_block<BM>(mtile_off, E, nt_count, &e, &m0, &nt)) return;
+  e = __builtin_amdgcn_readfirstlane(e);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  const int rows = __builtin_amdgcn_readfirstlane(kept[e]);
+  const int64_t n0 = static_cast<int64_t>(nt) * BNO;
+  const int64_t nk = K / BK;  // even, at least 2
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const auto ra_src = buffer_rsrc(A + static_cast<int64_t>(e) * C * K, static_cast<uint32_t>(C * K * 2));
+  // B rows 0..127 of a SwiGLU block are gate rows, 128..255 up rows: waves 0-1
+  // load the first half, waves 2-3 the second
+  const bf16_t* bbase = (SWIGLU && wave >= 2) ? B1 : B0;
+  const auto rb_src = buffer_rsrc(bbase + static_cast<int64_t>(e) * N * K, static_cast<uint32_t>(N * K * 2));
+  uint32_t a_voff[PER_WAVE], b_voff[PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int row = (wave * PER_WAVE + i) * 8 + (lane >> 3);
+    const int ch = (lane & 7) ^ ((row >> 1) & 7);  // the chunk stored at position lane % 8
+    a_voff[i] = static_cast<uint32_t>((m0 + row) * K * 2 + ch * 16);  // rows past C read as zero
+    const int64_t bn = n0 + (SWIGLU ? (row % (BN / 2)) : row);
+    b_voff[i] = bn < N ? static_cast<uint32_t>(bn * K * 2 + ch * 16) : 0x80000000u;
+  }
+  auto dma = [&](uint4* as, uint4* bs, int64_t ks) {  // ks: stage number
+    const uint32_t soff = static_cast<uint32_t>(ks * BK * 2);
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_src, MOE_LDS(as + (wave * PER_WAVE + i) * 8 * CH), 16,
+                                               a_voff[i], soff, 0, 0);
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_src, MOE_LDS(bs + (wave * PER_WAVE + i) * 8 * CH), 16,
+                                               b_voff[i], soff, 0, 0);
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lk = lane >> 5;
+  int a_row[TM], b_row[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) a_row[i] = (wm * (BM / 2) + i * 32 + lr) * CH;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int br = SWIGLU ? ((j < TN / 2) ? (wn * (BN / 4) + j * 32) : (BN / 2 + wn * (BN / 4) + (j - TN / 2) * 32))
+                          : (wn * (BN / 2) + j * 32);
+    b_row[j] = (br + lr) * CH;
+  }
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  bf16x8 fa[2][TM], fb[2][TN];
+  const int rsw = (lr >> 1) & 7;
+  auto fload = [&](const uint4* as, const uint4* bs, int ks, int slot) {
+    const int pc = (ks * 2 + lk) ^ rsw;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[slot][i] = *reinterpret_cast<const bf16x8*>(&as[a_row[i] + pc]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[slot][j] = *reinterpret_cast<const bf16x8*>(&bs[b_row[j] + pc]);
+  };
+  auto mfmas = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+  };
+  // Stage k in (as, bs); stage k + 1 goes to (an, bn_) unless this is the last.
+  auto stage = [&](auto has_next, const uint4* as, const uint4* bs, uint4* an, uint4* bn_, int64_t k) {
+    if constexpr (decltype(has_next)::value) dma(an, bn_, k + 1);
+    fload(as, bs, 1, 1);
+    mfmas(0);
+#pragma unroll
+    for (int g = 0; g < NFRAG; ++g) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA / NFRAG, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    fload(as, bs, 2, 0);
+    mfmas(1);
+#pragma unroll
+    for (int g = 0; g < NFRAG; ++g) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA / NFRAG, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    fload(as, bs, 3, 1);
+    mfmas(0);
+#pragma unroll
+    for (int g = 0; g < NFRAG; ++g) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA / NFRAG, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    if constexpr (decltype(has_next)::value) {
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm_lgkm0<0>();            // own DMA of stage k + 1 landed, reads of stage k done ...
+      __builtin_amdgcn_s_barrier();  // ... and everyone else's
+      __builtin_amdgcn_sched_barrier(0);
+      fload(an, bn_, 0, 0);
+    }
+    mfmas(1);
+#pragma unroll
+    for (int g = 0; g < NFRAG; ++g) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA / NFRAG, 0);
+    }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+
+  dma(As0, Bs0, 0);
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  fload(As0, Bs0, 0, 0);
+  int64_t k = 0;
+  for (; k + 2 < nk; k += 2) {
+    stage(T_{}, As0, Bs0, As1, Bs1, k);
+    stage(T_{}, As1, Bs1, As0, Bs0, k + 1);
+  }
+  stage(T_{}, As0, Bs0, As1, Bs1, k);
+  stage(F_{}, As1, Bs1, As0, Bs0, k + 1);
+
+  bf16_t* oute = out + static_cast<int64_t>(e) * C * N;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = m0 + wm * (BM / 2) + i * 32 + 8 * (q >> 2) + 4 * lk + (q & 3);
+      if (row >= rows) continue;
+      if (SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < TN / 2; ++j) {
+          const int64_t col = n0 + wn * (BN / 4) + j * 32 + lr;
+          if (col < N) oute[row * N + col] = f32_to_bf16(silu(acc[i][j][q]) * acc[i][j + TN / 2][q]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int64_t col = n0 + wn * (BN / 2) + j * 32 + lr;
+          if (col < N) oute[row * N + col] = f32_to_bf16(acc[i][j][q]);
         }
       }
     }
@@ -250,39 +562,67 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 }  // namespace
 
-int grouped_gemm_bm(bool bf16, int64_t /*C*/) { return bf16 ? 128 : 64; }
+// Block shape of the bf16 kernel: 256 x 256 once experts hold enough rows to
+// fill it, else 128 x 128.
+constexpr int kBigTileMinC = 512;
+
+int grouped_gemm_bm(bool bf16, int64_t C) {
+  if (!bf16) return 64;
+  return C >= kBigTileMinC ? 256 : 128;
+}
+
+namespace {
+
+template <int BM, int BN, bool SWIGLU>
+hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out, const int32_t* kept,
+                       const int32_t* mtile_off, int E, int64_t C, int64_t K, int64_t N, hipStream_t s) {
+  const int64_t mt_max = E * ceil_div(C, BM);  // upper bound of live row tiles
+  const int64_t nt = ceil_div(N, SWIGLU ? BN / 2 : BN);
+  const int64_t blocks = ceil_div(mt_max * nt, 8) * 8;  // whole rounds over the 8 XCDs
+  const auto* pa = static_cast<const bf16_t*>(a);
+  const auto* pb0 = static_cast<const bf16_t*>(b0);
+  const auto* pb1 = static_cast<const bf16_t*>(b1);
+  auto* po = static_cast<bf16_t*>(out);
+  if (BM == 256 && BN == 256 && K % 128 == 0)
+    gemm_bf16_dma_kernel<SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
+        pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt));
+  else
+    gemm_bf16_kernel<BM, BN, SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
+        pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt));
+  return hipGetLastError();
+}
+
+}  // namespace
 
 hipError_t launch_gemm_gate_up(const void* buckets, const int32_t* kept, const int32_t* mtile_off,
                                const void* wg, const void* wu, int E, int64_t C, int64_t d,
                                int64_t d_ff, bool bf16, void* h, hipStream_t s) {
-  const int bm = grouped_gemm_bm(bf16, C);
-  const unsigned mtiles = static_cast<unsigned>(E * ceil_div(C, bm));  // upper bound of live tiles
-  if (mtiles == 0) return hipSuccess;
-  if (bf16)
-    gemm_bf16_kernel<true><<<dim3(mtiles, static_cast<unsigned>(ceil_div(d_ff, 64))), dim3(256), 0, s>>>(
-        static_cast<const bf16_t*>(buckets), static_cast<const bf16_t*>(wg), static_cast<const bf16_t*>(wu),
-        static_cast<bf16_t*>(h), kept, mtile_off, E, C, d, d_ff);
-  else
-    gemm_f32_kernel<true><<<dim3(mtiles, static_cast<unsigned>(ceil_div(d_ff, 64))), dim3(256), 0, s>>>(
-        static_cast<const float*>(buckets), static_cast<const float*>(wg), static_cast<const float*>(wu),
-        static_cast<float*>(h), kept, mtile_off, E, C, d, d_ff);
+  if (E * C == 0) return hipSuccess;
+  if (bf16) {
+    if (grouped_gemm_bm(true, C) == 256)
+      return launch_bf16<256, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, s);
+    return launch_bf16<128, 128, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, s);
+  }
+  const unsigned mtiles = static_cast<unsigned>(E * ceil_div(C, 64));
+  gemm_f32_kernel<true><<<dim3(mtiles, static_cast<unsigned>(ceil_div(d_ff, 64))), dim3(256), 0, s>>>(
+      static_cast<const float*>(buckets), static_cast<const float*>(wg), static_cast<const float*>(wu),
+      static_cast<float*>(h), kept, mtile_off, E, C, d, d_ff);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_down(const void* h, const int32_t* kept, const int32_t* mtile_off,
                             const void* wd, int E, int64_t C, int64_t d, int64_t d_ff, bool bf16,
                             void* y, hipStream_t s) {
-  const int bm = grouped_gemm_bm(bf16, C);
-  const unsigned mtiles = static_cast<unsigned>(E * ceil_div(C, bm));
-  if (mtiles == 0) return hipSuccess;
-  if (bf16)
-    gemm_bf16_kernel<false><<<dim3(mtiles, static_cast<unsigned>(ceil_div(d, 128))), dim3(256), 0, s>>>(
-        static_cast<const bf16_t*>(h), static_cast<const bf16_t*>(wd), nullptr, static_cast<bf16_t*>(y), kept,
-        mtile_off, E, C, d_ff, d);
-  else
-    gemm_f32_kernel<false><<<dim3(mtiles, static_cast<unsigned>(ceil_div(d, 64))), dim3(256), 0, s>>>(
-        static_cast<const float*>(h), static_cast<const float*>(wd), nullptr, static_cast<float*>(y), kept,
-        mtile_off, E, C, d_ff, d);
+  if (E * C == 0) return hipSuccess;
+  if (bf16) {
+    if (grouped_gemm_bm(true, C) == 256)
+      return launch_bf16<256, 256, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, s);
+    return launch_bf16<128, 128, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, s);
+  }
+  const unsigned mtiles = static_cast<unsigned>(E * ceil_div(C, 64));
+  gemm_f32_kernel<false><<<dim3(mtiles, static_cast<unsigned>(ceil_div(d, 64))), dim3(256), 0, s>>>(
+      static_cast<const float*>(h), static_cast<const float*>(wd), nullptr, static_cast<float*>(y), kept,
+      mtile_off, E, C, d_ff, d);
   return hipGetLastError();
 }
 

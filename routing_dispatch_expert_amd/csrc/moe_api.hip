@@ -4,6 +4,7 @@
 // copied back to the host here.
 #include "moe.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -86,6 +87,15 @@ int capacity_of(int64_t T, int32_t E, int32_t k, float cf, int64_t* C) {
   return MOE_OK;
 }
 
+// The grouped GEMM addresses one expert's rows and weights with 32-bit byte
+// offsets: (C + 256) rows of max(d, d_ff) elements and d x d_ff weights.
+int check_expert_extent(int64_t C, int64_t d, int64_t d_ff) {
+  const int64_t lim = int64_t{1} << 31;
+  if ((C + 256) * std::max(d, d_ff) * 4 >= lim || d * d_ff * 4 >= lim)
+    return fail(MOE_ERR_UNSUPPORTED, "one expert's bucket or weight matrix exceeds 2^31 bytes");
+  return MOE_OK;
+}
+
 // Checks shared by the layer entry points. Returns MOE_OK or an error status.
 int check_layer_shape(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k, float cf, int32_t P,
                       int dtype, int64_t* C) {
@@ -102,7 +112,7 @@ int check_layer_shape(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k, 
   if (k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "k=%d > %d", k, kMaxK);
   if (T * k >= (int64_t{1} << 31) || static_cast<int64_t>(E) * *C >= (int64_t{1} << 31))
     return fail(MOE_ERR_UNSUPPORTED, "T*k and E*C must stay below 2^31");
-  return MOE_OK;
+  return check_expert_extent(*C, d, d_ff);
 }
 
 bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
@@ -361,6 +371,7 @@ int moe_grouped_gemm(const void* buckets, const int32_t* kept_count, const void*
   if (st != MOE_OK || (st = check_width(d_ff, dtype, "d_ff")) != MOE_OK) return st;
   if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "E=%d > %d", E, kMaxE);
   if (E * C >= (int64_t{1} << 31)) return fail(MOE_ERR_UNSUPPORTED, "E*C must stay below 2^31");
+  if ((st = check_expert_extent(C, d, d_ff)) != MOE_OK) return st;
   if (!buckets || !kept_count || !W_gate || !W_up || !W_down || !h || !y)
     return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
   size_t need;

@@ -152,6 +152,8 @@ def test_permute_is_exact(T, E, k, cf, P, d, dtype, skew):
 GEMM_CASES = [
     (4, 200, 256, 320, "bf16"), (8, 64, 128, 256, "f32"), (3, 300, 520, 136, "bf16"),
     (16, 5, 128, 128, "bf16"), (2, 128, 64, 64, "bf16"), (1, 1, 8, 8, "bf16"), (5, 40, 36, 20, "f32"),
+    (3, 600, 256, 384, "bf16"), (2, 1100, 520, 264, "bf16"), (4, 512, 64, 1032, "bf16"),
+    (3, 700, 384, 640, "bf16"), (2, 513, 128, 128, "bf16"), (5, 900, 1024, 256, "bf16"),
 ]
 
 
