@@ -89,13 +89,16 @@ def cpu_baseline(wl, host_w, sample: int):
     except Exception:  # pragma: no cover
         cores = 1
     tokens = np.arange(min(sample, wl.T))
-    t0 = time.perf_counter()
-    oracle.layer_forward(wl.x, wl.wr, lambda e: (host_w[0][e], host_w[1][e], host_w[2][e]), wl.T, wl.d,
-                         wl.d_ff, wl.E, wl.k, wl.cf, wl.dtype, P=wl.P, bias=wl.bias_vec, tokens=tokens)
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(3):  # median of three runs
+        t0 = time.perf_counter()
+        oracle.layer_forward(wl.x, wl.wr, lambda e: (host_w[0][e], host_w[1][e], host_w[2][e]), wl.T, wl.d,
+                             wl.d_ff, wl.E, wl.k, wl.cf, wl.dtype, P=wl.P, bias=wl.bias_vec, tokens=tokens)
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[1]
     return {"value": round(tokens.size / dt, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"layer outputs of the first {tokens.size} of {wl.T} tokens (routing and slots of all "
-                      f"{wl.T}), fp64 numpy, {dt:.1f} s"}
+                      f"{wl.T}), fp64 numpy, median of 3 runs: {dt:.1f} s each ({sum(times):.1f} s total)"}
 
 
 def main():

@@ -121,8 +121,10 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
 
 /* Router stage ([EP-inferensys] gating-network entry): logits on the matrix
  * cores, then top-k and gates as in moe_route. logits_out [T, E] fp32 may be
- * NULL; otherwise it receives the scores. workspace needs T*E*4 bytes when
- * logits_out is NULL, else may be NULL. */
+ * NULL; otherwise it receives the scores (bias included). The scores are
+ * summed over slices of d in a fixed order, so results do not depend on
+ * scheduling. workspace: moe_router_workspace_size() bytes, 256-byte aligned. */
+int moe_router_workspace_size(int64_t T, int64_t d, int32_t E, moe_dtype_t dtype, size_t* bytes);
 int moe_router(const void* x, const void* W_router, const float* router_bias, int64_t T,
                int64_t d, int32_t E, int32_t k, moe_dtype_t dtype, int32_t* topk_idx,
                float* topk_w, float* logits_out, void* workspace, size_t workspace_bytes,

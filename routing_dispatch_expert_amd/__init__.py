@@ -22,7 +22,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 TOTALS = ("dropped", "fully_dropped_tokens", "padded_rows", "offrank_bytes")
 
-EXPORTS = ("moe_capacity", "moe_workspace_size", "moe_layer_forward", "moe_router", "moe_route",
+EXPORTS = ("moe_capacity", "moe_workspace_size", "moe_layer_forward", "moe_router_workspace_size",
+           "moe_router", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_grouped_gemm_workspace_size",
            "moe_grouped_gemm", "moe_combine", "moe_set_stage_events", "moe_status_string", "moe_last_error")
 STAGES = ("router", "route", "slots", "scatter", "gate_up", "down", "combine")
@@ -48,6 +49,7 @@ _SIGS = {
     "moe_workspace_size": [_I64, _I64, _I64, _I32, _I32, _F32, _I32, ctypes.c_int, _P],
     "moe_layer_forward": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _F32, _I32, ctypes.c_int,
                           _P, ctypes.POINTER(moe_stats_t), _P, _SZ, _P],
+    "moe_router_workspace_size": [_I64, _I64, _I32, ctypes.c_int, _P],
     "moe_router": [_P, _P, _P, _I64, _I64, _I32, _I32, ctypes.c_int, _P, _P, _P, _P, _SZ, _P],
     "moe_route": [_P, _I64, _I32, _I32, _P, _P, _P],
     "moe_permute_workspace_size": [_I64, _I32, _P],
@@ -155,6 +157,12 @@ def moe_layer_forward(x, W_router, router_bias, W_gate, W_up, W_down, T, d, d_ff
                                    _ptr(W_down), T, d, d_ff, E, k, cf, P, _dtype(dtype), _ptr(out),
                                    _stats(stats), _ptr(workspace), workspace_bytes, _stream(stream)),
            "moe_layer_forward")
+
+
+def moe_router_workspace_size(T, d, E, dtype) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_router_workspace_size(T, d, E, _dtype(dtype), ctypes.byref(n)), "moe_router_workspace_size")
+    return n.value
 
 
 def moe_router(x, W_router, router_bias, T, d, E, k, dtype, topk_idx, topk_w, logits_out, workspace,

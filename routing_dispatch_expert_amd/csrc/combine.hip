@@ -16,73 +16,89 @@
 namespace moe {
 namespace {
 
-// One work-group per token; threads walk the row in 16-byte words
-// (8 bf16 or 4 fp32 values).
-template <bool BF16>
+// One wave per token; lanes walk the row in 16-byte words (8 bf16 or 4 fp32
+// values), U words in flight. The token's slots, experts and gates are
+// wave-uniform scalar loads.
+template <bool BF16, int WPT>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ x,
                                                       const uint4* __restrict__ y,
                                                       const int32_t* __restrict__ idx,
                                                       const float* __restrict__ w,
-                                                      const int32_t* __restrict__ slot, int k,
-                                                      int64_t C, int64_t V,
-                                                      uint4* __restrict__ out) {
-  __shared__ int64_t src[32];
-  __shared__ float wt[32];
-  __shared__ int nk;
-  const int64_t t = blockIdx.x;
-  if (threadIdx.x == 0) {
-    int c = 0;
-    for (int j = 0; j < k; ++j) {
-      const int s = slot[t * k + j];
-      if (s >= 0) {
-        src[c] = (static_cast<int64_t>(idx[t * k + j]) * C + s) * V;
-        wt[c] = w[t * k + j];
-        ++c;
-      }
-    }
-    nk = c;
-  }
-  __syncthreads();
-  const int c = nk;
+                                                      const int32_t* __restrict__ slot, int64_t T, int k,
+                                                      int64_t C, int64_t V, uint4* __restrict__ out) {
+  constexpr int U = 4;
+  constexpr int NE = BF16 ? 8 : 4;
+  constexpr int LANES = 64 * WPT;  // threads sharing one token
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (4 / WPT) + threadIdx.x / LANES;
+  if (t >= T) return;
+  const int lane = threadIdx.x % LANES;
+  const int32_t* st = slot + t * k;
+  const int32_t* it = idx + t * k;
+  const float* wt = w + t * k;
+  bool any = false;
+  for (int j = 0; j < k; ++j) any = any || st[j] >= 0;
   const uint4* xr = x + t * V;
   uint4* orow = out + t * V;
-  for (int64_t v = threadIdx.x; v < V; v += blockDim.x) {
-    const uint4 xv = xr[v];
-    if (c == 0) {
-      orow[v] = xv;
+  for (int64_t v0 = lane; v0 < V; v0 += LANES * U) {
+    uint4 xv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + LANES * u;
+      if (v < V) xv[u] = xr[v];
+    }
+    if (!any) {  // every copy dropped: the row passes through bit for bit
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t v = v0 + LANES * u;
+        if (v < V) orow[v] = xv[u];
+      }
       continue;
     }
-    constexpr int NE = BF16 ? 8 : 4;
-    float acc[NE];
+    float acc[U][NE];
 #pragma unroll
-    for (int q = 0; q < NE; ++q) acc[q] = 0.f;
-    for (int j = 0; j < c; ++j) {
-      const uint4 yv = y[src[j] + v];
-      const float wj = wt[j];
-      const uint32_t yw[4] = {yv.x, yv.y, yv.z, yv.w};
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (BF16) {
-          acc[2 * q] = fmaf(wj, __uint_as_float(yw[q] << 16), acc[2 * q]);
-          acc[2 * q + 1] = fmaf(wj, __uint_as_float(yw[q] & 0xffff0000u), acc[2 * q + 1]);
-        } else {
-          acc[q] = fmaf(wj, __uint_as_float(yw[q]), acc[q]);
+      for (int q = 0; q < NE; ++q) acc[u][q] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int sl = __builtin_amdgcn_readfirstlane(st[j]);
+      if (sl < 0) continue;
+      const float wj = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wt[j])));
+      const uint4* src = y + (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(it[j])) * C + sl) * V;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t v = v0 + LANES * u;
+        if (v >= V) continue;
+        const uint4 yv = src[v];
+        const uint32_t yw[4] = {yv.x, yv.y, yv.z, yv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (BF16) {
+            acc[u][2 * q] = fmaf(wj, __uint_as_float(yw[q] << 16), acc[u][2 * q]);
+            acc[u][2 * q + 1] = fmaf(wj, __uint_as_float(yw[q] & 0xffff0000u), acc[u][2 * q + 1]);
+          } else {
+            acc[u][q] = fmaf(wj, __uint_as_float(yw[q]), acc[u][q]);
+          }
         }
       }
     }
-    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-    uint32_t ow[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (BF16) {
-        const float lo = __uint_as_float(xw[q] << 16) + acc[2 * q];
-        const float hi = __uint_as_float(xw[q] & 0xffff0000u) + acc[2 * q + 1];
-        ow[q] = static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
-      } else {
-        ow[q] = __float_as_uint(__uint_as_float(xw[q]) + acc[q]);
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + LANES * u;
+      if (v >= V) continue;
+      const uint32_t xw[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+      uint32_t ow[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (BF16) {
+          const float lo = __uint_as_float(xw[q] << 16) + acc[u][2 * q];
+          const float hi = __uint_as_float(xw[q] & 0xffff0000u) + acc[u][2 * q + 1];
+          ow[q] = static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+        } else {
+          ow[q] = __float_as_uint(__uint_as_float(xw[q]) + acc[u][q]);
+        }
       }
+      orow[v] = uint4{ow[0], ow[1], ow[2], ow[3]};
     }
-    orow[v] = uint4{ow[0], ow[1], ow[2], ow[3]};
   }
 }
 
@@ -93,14 +109,18 @@ hipError_t launch_combine(const void* x, const void* y, const int32_t* idx, cons
                           void* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int64_t V = d * (bf16 ? 2 : 4) / 16;
-  const dim3 grid(static_cast<unsigned>(T));
+  const int wpt = row_waves_per_token(T);
+  const dim3 grid(static_cast<unsigned>(ceil_div(T, 4 / wpt)));
   const auto* xv = static_cast<const uint4*>(x);
   const auto* yv = static_cast<const uint4*>(y);
   auto* ov = static_cast<uint4*>(out);
-  if (bf16)
-    combine_kernel<true><<<grid, dim3(256), 0, s>>>(xv, yv, idx, w, slot, k, C, V, ov);
-  else
-    combine_kernel<false><<<grid, dim3(256), 0, s>>>(xv, yv, idx, w, slot, k, C, V, ov);
+#define MOE_COMBINE(B, W) combine_kernel<B, W><<<grid, dim3(256), 0, s>>>(xv, yv, idx, w, slot, T, k, C, V, ov)
+  if (bf16) {
+    if (wpt == 1) MOE_COMBINE(true, 1); else if (wpt == 2) MOE_COMBINE(true, 2); else MOE_COMBINE(true, 4);
+  } else {
+    if (wpt == 1) MOE_COMBINE(false, 1); else if (wpt == 2) MOE_COMBINE(false, 2); else MOE_COMBINE(false, 4);
+  }
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 

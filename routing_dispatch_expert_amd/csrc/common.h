@@ -19,6 +19,11 @@ constexpr int kTileTokens = 64;
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Waves that share one token's row in the row-moving kernels (scatter,
+// combine): 1 when there are many tokens, up to 4 (a whole 256-thread block)
+// when there are few, so short batches still keep enough loads in flight.
+inline int row_waves_per_token(int64_t T) { return T >= 1024 ? 1 : (T >= 256 ? 2 : 4); }
+
 __device__ inline float bf16_to_f32(bf16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
 // fp32 -> bf16, round to nearest even (NaN stays NaN).
@@ -30,10 +35,16 @@ __device__ inline bf16_t f32_to_bf16(float f) {
 }
 
 // ---- router (router.hip) ----
-hipError_t launch_router_logits(const void* x, const void* wr, const float* bias, int64_t T,
-                                int64_t d, int E, bool bf16, float* logits, hipStream_t s);
-hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w,
-                        hipStream_t s);
+// Number of d-slices S the scores are split into (partials part[S][T][E]).
+int router_splits(int64_t T, int64_t d, int E, bool bf16);
+hipError_t launch_router_logits(const void* x, const void* wr, int64_t T, int64_t d, int E, bool bf16,
+                                int S, float* part, hipStream_t s);
+// Sums the S partials (slice order) and the bias, writes logits_out if given,
+// then top-k and gates; with tile_cnt, also the per-64-token-tile histogram
+// (only when route_builds_histogram(k)).
+bool route_builds_histogram(int k);
+hipError_t launch_route(const float* part, int S, const float* bias, int64_t T, int E, int k,
+                        float* logits_out, int32_t* idx, float* w, int32_t* tile_cnt, hipStream_t s);
 
 // ---- permutation (permute.hip) ----
 hipError_t launch_tile_hist(const int32_t* idx, int64_t T, int k, int E, int32_t* tile_cnt,

@@ -480,6 +480,79 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ---------------------------------------------------------------------------
+// Few rows per expert (decode): the run is a stream of each touched expert's
+// weights, each element used by at most 16 rows. A work-group takes one
+// expert's rows (16 at most) and 64 output columns; each wave owns 16 columns
+// as 16 x 16 v_mfma_f32_16x16x32_bf16 tiles (for SWIGLU a gate and an up
+// tile), K in steps of 32. Weights go straight from HBM to registers, eight
+// K steps in flight per lane; the few activation rows come from L2.
+// Operand lane layout: lane l holds row (l % 16), K elements 8*(l/16) .. +8;
+// accumulator element r of lane l is row 4*(l/16) + r, column l % 16.
+// ---------------------------------------------------------------------------
+constexpr int kSkinnyRows = 16;
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void gemm_bf16_skinny_kernel(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
+    bf16_t* __restrict__ out, const int32_t* __restrict__ kept, const int32_t* __restrict__ mtile_off,
+    int E, int64_t C, int64_t K, int64_t N, int nch) {
+  constexpr int U = 8;  // K steps in flight
+  const int mt = blockIdx.x / nch;
+  const int nc = blockIdx.x - mt * nch;
+  if (mt >= mtile_off[E]) return;
+  const int e = __builtin_amdgcn_readfirstlane(owner_expert(mtile_off, E, mt));
+  const int m0 = __builtin_amdgcn_readfirstlane((mt - mtile_off[e]) * kSkinnyRows);
+  const int rows = __builtin_amdgcn_readfirstlane(kept[e]);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t col0 = static_cast<int64_t>(nc) * 64 + wave * 16;
+  if (col0 >= N) return;
+  const int kg = (lane >> 4) * 8;
+  const int arow = m0 + (lane & 15);
+  const bool a_in = arow < rows;
+  const bf16_t* ap = A + (static_cast<int64_t>(e) * C + (a_in ? arow : 0)) * K + kg;
+  const int64_t bcol = min(col0 + (lane & 15), N - 1);
+  const bf16_t* b0p = B0 + (static_cast<int64_t>(e) * N + bcol) * K + kg;
+  const bf16_t* b1p = SWIGLU ? B1 + (static_cast<int64_t>(e) * N + bcol) * K + kg : nullptr;
+
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const int64_t nk = K / 32;  // K is a multiple of 32 here
+  int64_t ks = 0;
+  for (; ks + U <= nk; ks += U) {
+    bf16x8 a[U], b0[U], b1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      b0[u] = *reinterpret_cast<const bf16x8*>(b0p + (ks + u) * 32);
+      if (SWIGLU) b1[u] = *reinterpret_cast<const bf16x8*>(b1p + (ks + u) * 32);
+      a[u] = a_in ? *reinterpret_cast<const bf16x8*>(ap + (ks + u) * 32) : bf16x8{};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b0[u], acc0, 0, 0, 0);
+      if (SWIGLU) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b1[u], acc1, 0, 0, 0);
+    }
+  }
+  for (; ks < nk; ++ks) {
+    const bf16x8 b0v = *reinterpret_cast<const bf16x8*>(b0p + ks * 32);
+    const bf16x8 av = a_in ? *reinterpret_cast<const bf16x8*>(ap + ks * 32) : bf16x8{};
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b0v, acc0, 0, 0, 0);
+    if (SWIGLU) {
+      const bf16x8 b1v = *reinterpret_cast<const bf16x8*>(b1p + ks * 32);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b1v, acc1, 0, 0, 0);
+    }
+  }
+  const int64_t col = col0 + (lane & 15);
+  if (col >= N) return;
+  bf16_t* oute = out + static_cast<int64_t>(e) * C * N;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = m0 + 4 * (lane >> 4) + r;
+    if (row < rows)
+      oute[row * N + col] = f32_to_bf16(SWIGLU ? silu(acc0[r]) * acc1[r] : acc0[r]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 GEMM on the vector ALUs (fused multiply-add): 64 x 64 outputs per
 // work-group, 4 x 4 per thread, K in steps of 16 through LDS. With SWIGLU the
 // thread keeps gate and up sums of the same outputs.
@@ -566,12 +639,27 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 // fill it, else 128 x 128.
 constexpr int kBigTileMinC = 512;
 
+// Row tiles of the skinny kernel when every expert holds this few rows.
+constexpr int kSkinnyMaxC = kSkinnyRows;
+
 int grouped_gemm_bm(bool bf16, int64_t C) {
   if (!bf16) return 64;
+  if (C <= kSkinnyMaxC) return kSkinnyRows;
   return C >= kBigTileMinC ? 256 : 128;
 }
 
 namespace {
+
+template <bool SWIGLU>
+hipError_t launch_skinny(const void* a, const void* b0, const void* b1, void* out, const int32_t* kept,
+                         const int32_t* mtile_off, int E, int64_t C, int64_t K, int64_t N, hipStream_t s) {
+  const int64_t nch = ceil_div(N, 64);
+  const int64_t blocks = E * ceil_div(C, kSkinnyRows) * nch;
+  gemm_bf16_skinny_kernel<SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
+      static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0), static_cast<const bf16_t*>(b1),
+      static_cast<bf16_t*>(out), kept, mtile_off, E, C, K, N, static_cast<int>(nch));
+  return hipGetLastError();
+}
 
 template <int BM, int BN, bool SWIGLU>
 hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out, const int32_t* kept,
@@ -599,6 +687,8 @@ hipError_t launch_gemm_gate_up(const void* buckets, const int32_t* kept, const i
                                int64_t d_ff, bool bf16, void* h, hipStream_t s) {
   if (E * C == 0) return hipSuccess;
   if (bf16) {
+    if (grouped_gemm_bm(true, C) == kSkinnyRows && d % 32 == 0)
+      return launch_skinny<true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, s);
     if (grouped_gemm_bm(true, C) == 256)
       return launch_bf16<256, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, s);
     return launch_bf16<128, 128, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, s);
@@ -615,6 +705,8 @@ hipError_t launch_gemm_down(const void* h, const int32_t* kept, const int32_t* m
                             void* y, hipStream_t s) {
   if (E * C == 0) return hipSuccess;
   if (bf16) {
+    if (grouped_gemm_bm(true, C) == kSkinnyRows && d_ff % 32 == 0)
+      return launch_skinny<false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, s);
     if (grouped_gemm_bm(true, C) == 256)
       return launch_bf16<256, 256, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, s);
     return launch_bf16<128, 128, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, s);

@@ -134,7 +134,8 @@ LayerPlan plan_layer(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E, in
   Carver c(ws);
   LayerPlan p;
   const int64_t nt = moe::ceil_div(T, moe::kTileTokens);
-  p.logits = c.take<float>(static_cast<size_t>(T) * E);
+  const int S = moe::router_splits(T, d, E, eb == 2);
+  p.logits = c.take<float>(static_cast<size_t>(S) * T * E);  // partial scores, S slices of d
   p.idx = c.take<int32_t>(static_cast<size_t>(T) * k);
   p.w = c.take<float>(static_cast<size_t>(T) * k);
   p.slot = c.take<int32_t>(static_cast<size_t>(T) * k);
@@ -243,15 +244,18 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
   const int64_t nt = moe::ceil_div(T, moe::kTileTokens);
   const int bm = moe::grouped_gemm_bm(bf16, C);
 
+  const int splits = moe::router_splits(T, d, E, bf16);
+  const bool fused_hist = moe::route_builds_histogram(k);
   MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTER, false, s), "event");
-  MOE_HIP_TRY(moe::launch_router_logits(x, W_router, router_bias, T, d, E, bf16, p.logits, s),
-              "router logits");
+  MOE_HIP_TRY(moe::launch_router_logits(x, W_router, T, d, E, bf16, splits, p.logits, s), "router logits");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTER, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTE, false, s), "event");
-  MOE_HIP_TRY(moe::launch_route(p.logits, T, E, k, idx, w, s), "route");
+  MOE_HIP_TRY(moe::launch_route(p.logits, splits, router_bias, T, E, k, nullptr, idx, w,
+                                fused_hist ? p.tile_cnt : nullptr, s),
+              "route");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTE, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SLOTS, false, s), "event");
-  MOE_HIP_TRY(moe::launch_tile_hist(idx, T, k, E, p.tile_cnt, s), "tile histogram");
+  if (!fused_hist) MOE_HIP_TRY(moe::launch_tile_hist(idx, T, k, E, p.tile_cnt, s), "tile histogram");
   MOE_HIP_TRY(moe::launch_scan(p.tile_cnt, nt, E, C, P, d * eb, k, T, p.tile_off, routed, kept, send,
                                totals, bm, p.mtile, src, s),
               "scan");
@@ -274,6 +278,14 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
   return MOE_OK;
 }
 
+int moe_router_workspace_size(int64_t T, int64_t d, int32_t E, moe_dtype_t dtype, size_t* bytes) {
+  if (!bytes || !valid_dtype(dtype) || T < 0 || d < 1 || E < 1)
+    return fail(MOE_ERR_INVALID_ARG, "need bytes, a dtype, T >= 0, d >= 1, E >= 1");
+  const int S = moe::router_splits(T, d, E, dtype == MOE_DTYPE_BF16);
+  *bytes = align_up(static_cast<size_t>(S) * T * E * sizeof(float));
+  return MOE_OK;
+}
+
 int moe_router(const void* x, const void* W_router, const float* router_bias, int64_t T, int64_t d,
                int32_t E, int32_t k, moe_dtype_t dtype, int32_t* topk_idx, float* topk_w,
                float* logits_out, void* workspace, size_t workspace_bytes, void* stream) {
@@ -286,18 +298,17 @@ int moe_router(const void* x, const void* W_router, const float* router_bias, in
   if (T * k >= (int64_t{1} << 31)) return fail(MOE_ERR_UNSUPPORTED, "T*k must stay below 2^31");
   if (!x || !W_router || !topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
   if (T == 0) return MOE_OK;
-  float* logits = logits_out;
-  if (!logits) {
-    const size_t need = static_cast<size_t>(T) * E * sizeof(float);
-    if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % kAlign)
-      return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
-    logits = static_cast<float*>(workspace);
-  }
+  size_t need;
+  moe_router_workspace_size(T, d, E, dtype, &need);
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
   auto s = static_cast<hipStream_t>(stream);
-  MOE_HIP_TRY(moe::launch_router_logits(x, W_router, router_bias, T, d, E, dtype == MOE_DTYPE_BF16,
-                                        logits, s),
-              "router logits");
-  MOE_HIP_TRY(moe::launch_route(logits, T, E, k, topk_idx, topk_w, s), "route");
+  const bool bf16 = dtype == MOE_DTYPE_BF16;
+  const int S = moe::router_splits(T, d, E, bf16);
+  auto* part = static_cast<float*>(workspace);
+  MOE_HIP_TRY(moe::launch_router_logits(x, W_router, T, d, E, bf16, S, part, s), "router logits");
+  MOE_HIP_TRY(moe::launch_route(part, S, router_bias, T, E, k, logits_out, topk_idx, topk_w, nullptr, s),
+              "route");
   return MOE_OK;
 }
 
@@ -308,7 +319,8 @@ int moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* top
   if (T * k >= (int64_t{1} << 31)) return fail(MOE_ERR_UNSUPPORTED, "T*k must stay below 2^31");
   if (!logits || !topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
   if (T == 0) return MOE_OK;
-  MOE_HIP_TRY(moe::launch_route(logits, T, E, k, topk_idx, topk_w, static_cast<hipStream_t>(stream)),
+  MOE_HIP_TRY(moe::launch_route(logits, 1, nullptr, T, E, k, nullptr, topk_idx, topk_w, nullptr,
+                                static_cast<hipStream_t>(stream)),
               "route");
   return MOE_OK;
 }

@@ -37,35 +37,6 @@ __global__ __launch_bounds__(256) void tile_hist_kernel(const int32_t* __restric
   for (int e = threadIdx.x; e < E; e += blockDim.x) tile_cnt[b * E + e] = hist[e];
 }
 
-// Exclusive scan over tiles, per expert. A block serves 16 experts with 16
-// lanes each; lane ly owns a contiguous run of tiles. routed[e] = total.
-__global__ __launch_bounds__(256) void scan_tiles_kernel(const int32_t* __restrict__ tile_cnt,
-                                                         int64_t nt, int E,
-                                                         int32_t* __restrict__ tile_off,
-                                                         int32_t* __restrict__ routed) {
-  __shared__ int part[16][17];
-  const int ex = threadIdx.x & 15;
-  const int ly = threadIdx.x >> 4;
-  const int e = blockIdx.x * 16 + ex;
-  const int64_t chunk = ceil_div(nt, 16);
-  const int64_t b0 = min(nt, ly * chunk);
-  const int64_t b1 = min(nt, b0 + chunk);
-  int sum = 0;
-  if (e < E)
-    for (int64_t b = b0; b < b1; ++b) sum += tile_cnt[b * E + e];
-  part[ly][ex] = sum;
-  __syncthreads();
-  int run = 0;
-  for (int l = 0; l < ly; ++l) run += part[l][ex];
-  if (e >= E) return;
-  for (int64_t b = b0; b < b1; ++b) {
-    const int v = tile_cnt[b * E + e];
-    tile_off[b * E + e] = run;
-    run += v;
-  }
-  if (ly == 15) routed[e] = run;
-}
-
 // Exclusive scan of one int per thread over a block of 1024 threads.
 __device__ int block_exclusive_scan_1024(int v, int* total, int* sh /* >= 17 ints */) {
   const int lane = threadIdx.x & 63;
@@ -116,33 +87,54 @@ __device__ void mtile_prefix(const int* kept_s, int E, int bm, int32_t* mtile_of
   if (threadIdx.x == 0) mtile_off[E] = total;
 }
 
-// Counts, totals, send counts and the GEMM row-tile map. One block of 1024.
-__global__ __launch_bounds__(1024) void finalize_kernel(const int32_t* __restrict__ routed, int E,
-                                                        int64_t C, int P, int64_t row_bytes, int k,
-                                                        int64_t T, int32_t* __restrict__ kept,
-                                                        int32_t* __restrict__ send,
-                                                        int64_t* __restrict__ totals, int bm,
-                                                        int32_t* __restrict__ mtile_off) {
+// Exclusive scan over tiles per expert, then counts, totals, send counts and
+// the GEMM row-tile map; one block of 1024 threads. The scan takes 64 experts
+// at a time with 16 lanes each; lane ly owns a contiguous run of tiles.
+__global__ __launch_bounds__(1024) void scan_finalize_kernel(
+    const int32_t* __restrict__ tile_cnt, int64_t nt, int E, int64_t C, int P, int64_t row_bytes, int k,
+    int64_t T, int32_t* __restrict__ tile_off, int32_t* __restrict__ routed, int32_t* __restrict__ kept,
+    int32_t* __restrict__ send, int64_t* __restrict__ totals, int bm, int32_t* __restrict__ mtile_off) {
+  __shared__ int part[16][65];
   __shared__ int kept_s[4096];
   __shared__ int sh[17];
   __shared__ unsigned long long ksum;
+  const int ex = threadIdx.x & 63;
+  const int ly = threadIdx.x >> 6;
+  const int64_t chunk = ceil_div(nt, 16);
+  const int64_t b0 = min(nt, ly * chunk);
+  const int64_t b1 = min(nt, b0 + chunk);
   if (threadIdx.x == 0) ksum = 0;
-  __syncthreads();
-  unsigned long long local = 0;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    const int kv = static_cast<int>(min<int64_t>(routed[e], C));
-    kept[e] = kv;
-    kept_s[e] = kv;
-    local += static_cast<unsigned long long>(kv);
+  for (int eb = 0; eb < E; eb += 64) {
+    const int e = eb + ex;
+    int sum = 0;
+    if (e < E)
+      for (int64_t b = b0; b < b1; ++b) sum += tile_cnt[b * E + e];
+    part[ly][ex] = sum;
+    __syncthreads();
+    int run = 0;
+    for (int l = 0; l < ly; ++l) run += part[l][ex];
+    if (e < E) {
+      for (int64_t b = b0; b < b1; ++b) {
+        const int v = tile_cnt[b * E + e];
+        tile_off[b * E + e] = run;
+        run += v;
+      }
+      if (ly == 15) {
+        routed[e] = run;
+        const int kv = static_cast<int>(min<int64_t>(run, C));
+        kept[e] = kv;
+        kept_s[e] = kv;
+        atomicAdd(&ksum, static_cast<unsigned long long>(kv));  // integer sum: order-free
+      }
+    }
+    __syncthreads();
   }
-  atomicAdd(&ksum, local);  // integer sum: order-free
-  __syncthreads();
   const int per = E / P;
   if (send)
     for (int p = threadIdx.x; p < P; p += blockDim.x) {
-      int s = 0;
-      for (int e = p * per; e < (p + 1) * per; ++e) s += kept_s[e];
-      send[p] = s;
+      int sp = 0;
+      for (int e = p * per; e < (p + 1) * per; ++e) sp += kept_s[e];
+      send[p] = sp;
     }
   if (totals && threadIdx.x == 0) {
     const int64_t n_kept = static_cast<int64_t>(ksum);
@@ -197,10 +189,20 @@ __global__ __launch_bounds__(64) void slots_kernel(const int32_t* __restrict__ i
   __syncthreads();
   const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
   const unsigned long long below = (1ull << lane) - 1ull;
-  for (int base = 0; base < ncp; base += 64) {
+  // every copy of the tile up front: at most 64 * 32 / 64 = 32 per lane
+  int ev[32];
+#pragma unroll
+  for (int c = 0; c < 32; ++c) {
+    const int i = c * 64 + lane;
+    ev[c] = i < ncp ? idx[t0 * k + i] : 0;
+  }
+#pragma unroll
+  for (int c = 0; c < 32; ++c) {
+    const int base = c * 64;
+    if (base >= ncp) break;
     const int i = base + lane;
     const bool active = i < ncp;
-    const int e = active ? idx[t0 * k + i] : 0;
+    const int e = ev[c];
     unsigned long long mask = __ballot(active);
     for (int bit = 0; bit < nbits; ++bit) {
       const bool set = (e >> bit) & 1;
@@ -229,41 +231,38 @@ __global__ __launch_bounds__(64) void slots_kernel(const int32_t* __restrict__ i
   }
 }
 
-// Row scatter: block b moves token b's row (16-byte words) to each kept
-// destination bucket row; the row is read once and written k' <= k times.
+// Row scatter: one wave per token moves its row (16-byte words, U per lane in
+// flight) to each kept destination bucket row; the row is read once and
+// written k' <= k times. The token's slots are wave-uniform scalar loads.
+template <int WPT>
 __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restrict__ x,
                                                            const int32_t* __restrict__ idx,
-                                                           const int32_t* __restrict__ slot,
+                                                           const int32_t* __restrict__ slot, int64_t T,
                                                            int k, int64_t C, int64_t V,
                                                            uint4* __restrict__ buckets) {
-  __shared__ int64_t dst[32];
-  __shared__ int nk;
-  const int64_t t = blockIdx.x;
-  if (threadIdx.x == 0) {
-    int c = 0;
-    for (int j = 0; j < k; ++j) {
-      const int s = slot[t * k + j];
-      if (s >= 0) dst[c++] = (static_cast<int64_t>(idx[t * k + j]) * C + s) * V;
-    }
-    nk = c;
-  }
-  __syncthreads();
-  const int c = nk;
-  if (c == 0) return;
+  constexpr int U = 4;
+  constexpr int LANES = 64 * WPT;  // threads sharing one token
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (4 / WPT) + threadIdx.x / LANES;
+  if (t >= T) return;
+  const int lane = threadIdx.x % LANES;
+  const int32_t* st = slot + t * k;
+  const int32_t* it = idx + t * k;
   const uint4* xr = x + t * V;
-  for (int64_t v0 = threadIdx.x; v0 < V; v0 += 4 * blockDim.x) {
-    uint4 val[4];
+  for (int64_t v0 = lane; v0 < V; v0 += LANES * U) {
+    uint4 val[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t v = v0 + u * blockDim.x;
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + LANES * u;
       if (v < V) val[u] = xr[v];
     }
-    for (int j = 0; j < c; ++j) {
-      uint4* d = buckets + dst[j];
+    for (int j = 0; j < k; ++j) {
+      const int sl = __builtin_amdgcn_readfirstlane(st[j]);
+      if (sl < 0) continue;
+      uint4* dst = buckets + (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(it[j])) * C + sl) * V;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t v = v0 + u * blockDim.x;
-        if (v < V) d[v] = val[u];
+      for (int u = 0; u < U; ++u) {
+        const int64_t v = v0 + LANES * u;
+        if (v < V) dst[v] = val[u];
       }
     }
   }
@@ -284,13 +283,9 @@ hipError_t launch_scan(const int32_t* tile_cnt, int64_t nt, int E, int64_t C, in
                        int64_t row_bytes, int k, int64_t T, int32_t* tile_off, int32_t* routed,
                        int32_t* kept, int32_t* send, int64_t* totals, int bm, int32_t* mtile_off,
                        int32_t* src, hipStream_t s) {
-  scan_tiles_kernel<<<dim3(static_cast<unsigned>(ceil_div(E, 16))), dim3(256), 0, s>>>(
-      tile_cnt, nt, E, tile_off, routed);
+  scan_finalize_kernel<<<dim3(1), dim3(1024), 0, s>>>(tile_cnt, nt, E, C, P, row_bytes, k, T, tile_off, routed,
+                                                      kept, send, totals, bm, mtile_off);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  finalize_kernel<<<dim3(1), dim3(1024), 0, s>>>(routed, E, C, P, row_bytes, k, T, kept, send,
-                                                 totals, bm, mtile_off);
-  err = hipGetLastError();
   if (err != hipSuccess || !src) return err;
   const unsigned gx = static_cast<unsigned>(std::min<int64_t>(ceil_div(C, 256), 64));
   src_padding_kernel<<<dim3(gx, static_cast<unsigned>(E)), dim3(256), 0, s>>>(kept, C, E, src);
@@ -315,8 +310,17 @@ hipError_t launch_slots(const int32_t* idx, const int32_t* tile_off, int64_t T, 
 hipError_t launch_scatter_rows(const void* x, const int32_t* idx, const int32_t* slot, int64_t T,
                                int k, int64_t C, int64_t row_bytes, void* buckets, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  scatter_rows_kernel<<<dim3(static_cast<unsigned>(T)), dim3(256), 0, s>>>(
-      static_cast<const uint4*>(x), idx, slot, k, C, row_bytes / 16, static_cast<uint4*>(buckets));
+  const auto* xv = static_cast<const uint4*>(x);
+  auto* bv = static_cast<uint4*>(buckets);
+  const int64_t V = row_bytes / 16;
+  const int wpt = row_waves_per_token(T);
+  const dim3 grid(static_cast<unsigned>(ceil_div(T, 4 / wpt)));
+  if (wpt == 1)
+    scatter_rows_kernel<1><<<grid, dim3(256), 0, s>>>(xv, idx, slot, T, k, C, V, bv);
+  else if (wpt == 2)
+    scatter_rows_kernel<2><<<grid, dim3(256), 0, s>>>(xv, idx, slot, T, k, C, V, bv);
+  else
+    scatter_rows_kernel<4><<<grid, dim3(256), 0, s>>>(xv, idx, slot, T, k, C, V, bv);
   return hipGetLastError();
 }
 

@@ -9,6 +9,7 @@
 // Top-k: order by score descending, then expert index ascending (the pages
 // leave ties open; the lower index wins). Gates: softmax over the k chosen
 // scores, evaluated in fp64 and rounded to fp32.
+#include <algorithm>
 #include <climits>
 
 #include "common.h"
@@ -16,23 +17,32 @@
 namespace moe {
 namespace {
 
+constexpr int kMaxRouterSplits = 8;  // d-slices of the router scores (partials summed in order)
+
 // ---------------------------------------------------------------------------
-// Scores on the matrix cores: one wave computes 16 tokens x (16*NT) experts
-// with v_mfma_f32_16x16x32_bf16, K-loop over d. Both operands come straight
-// from global memory (x is read once; W_router is small and stays in L2).
+// Scores on the matrix cores. Each wave is one work item: 16 tokens x (16*NT)
+// experts over one of S slices of d, with v_mfma_f32_16x16x32_bf16; it writes
+// fp32 partial sums part[s][t][e]. The route kernel adds the S partials in
+// slice order (a fixed order: the result does not depend on scheduling), so
+// few tokens still spread over many waves. Both operands come straight from
+// global memory (x is read once; W_router is small and stays in L2).
 // Lane l of an A/B operand holds row (l % 16), K elements 8*(l/16) .. +8;
 // the accumulator of lane l holds rows 4*(l/16) + r, column l % 16.
 // ---------------------------------------------------------------------------
 template <int NT>
 __global__ __launch_bounds__(256) void router_logits_bf16(const bf16_t* __restrict__ x,
-                                                          const bf16_t* __restrict__ wr,
-                                                          const float* __restrict__ bias,
-                                                          int64_t T, int64_t d, int E,
-                                                          float* __restrict__ logits) {
+                                                          const bf16_t* __restrict__ wr, int64_t T,
+                                                          int64_t d, int E, int S, int64_t kper,
+                                                          float* __restrict__ part) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 64 + wave * 16;
-  const int e0 = blockIdx.y * (16 * NT);
+  const int64_t tt = ceil_div(T, 16);
+  const int64_t ec = ceil_div(E, 16 * NT);
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (item >= tt * ec * S) return;
+  const int64_t t0 = (item % tt) * 16;
+  const int e0 = static_cast<int>((item / tt) % ec) * 16 * NT;
+  const int s = static_cast<int>(item / (tt * ec));
+  const int64_t k_lo = s * kper, k_hi = min(d, k_lo + kper);
   const int kg = (lane >> 4) * 8;
   const int64_t trow = min(t0 + (lane & 15), T - 1);  // rows past T are computed, not stored
   const bf16_t* xp = x + trow * d + kg;
@@ -46,9 +56,22 @@ __global__ __launch_bounds__(256) void router_logits_bf16(const bf16_t* __restri
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll 4
-  for (int64_t k0 = 0; k0 < d; k0 += 32) {
-    const bool in = k0 + kg < d;  // d is a multiple of 8: whole 8-element groups
+  int64_t k0 = k_lo;
+  for (; k0 + 4 * 32 <= k_hi; k0 += 4 * 32) {  // four steps in flight
+    bf16x8 a[4], b[4][NT];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a[u] = *reinterpret_cast<const bf16x8*>(xp + k0 + 32 * u);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) b[u][j] = *reinterpret_cast<const bf16x8*>(wp[j] + k0 + 32 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][j], acc[j], 0, 0, 0);
+  }
+  for (; k0 < k_hi; k0 += 32) {
+    const bool in = k0 + kg < k_hi;  // d is a multiple of 8: whole 8-element groups
     bf16x8 a = {};
     if (in) a = *reinterpret_cast<const bf16x8*>(xp + k0);
 #pragma unroll
@@ -58,25 +81,23 @@ __global__ __launch_bounds__(256) void router_logits_bf16(const bf16_t* __restri
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
     }
   }
+  float* ps = part + static_cast<int64_t>(s) * T * E;
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const int e = e0 + 16 * j + (lane & 15);
     if (e >= E) continue;
-    const float b = bias ? bias[e] : 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t t = t0 + 4 * (lane >> 4) + r;
-      if (t < T) logits[t * E + e] = acc[j][r] + b;
+      if (t < T) ps[t * E + e] = acc[j][r];
     }
   }
 }
 
 // fp32 scores: one thread per (token, expert), plain fused multiply-adds.
 __global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict__ x,
-                                                         const float* __restrict__ wr,
-                                                         const float* __restrict__ bias, int64_t T,
-                                                         int64_t d, int E,
-                                                         float* __restrict__ logits) {
+                                                         const float* __restrict__ wr, int64_t T,
+                                                         int64_t d, int E, float* __restrict__ part) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= T * E) return;
   const int64_t t = i / E;
@@ -85,7 +106,7 @@ __global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict
   const float* wrow = wr + static_cast<int64_t>(e) * d;
   float acc = 0.f;
   for (int64_t c = 0; c < d; ++c) acc = fmaf(xr[c], wrow[c], acc);
-  logits[i] = acc + (bias ? bias[e] : 0.f);
+  part[i] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -98,14 +119,22 @@ __device__ inline bool better(float v, int e, float ov, int oe) {
   return v > ov || (v == ov && e < oe);
 }
 
-template <int L, int KMAX>
-__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int64_t T,
-                                                    int E, int k, int32_t* __restrict__ idx,
-                                                    float* __restrict__ w) {
-  constexpr int kTokensPerBlock = 256 / L;
+template <int L, int KMAX, bool HIST>
+__global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ part, int S,
+                                                     const float* __restrict__ bias, int64_t T, int E,
+                                                     int k, float* __restrict__ logits_out,
+                                                     int32_t* __restrict__ idx, float* __restrict__ w,
+                                                     int32_t* __restrict__ tile_cnt) {
+  constexpr int kTokensPerBlock = 1024 / L;
+  static_assert(!HIST || kTokensPerBlock == kTileTokens, "one block per histogram tile");
+  extern __shared__ int hist[];
   const int g = threadIdx.x % L;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + threadIdx.x / L;
   const bool valid = t < T;
+  if (HIST) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+    __syncthreads();
+  }
 
   float lv[KMAX];
   int li[KMAX];
@@ -115,23 +144,51 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     li[j] = INT_MAX;
   }
   if (valid) {
-    const float* row = logits + t * E;
-    for (int e = g; e < E; e += L) {
-      float v = row[e] + 0.0f;  // -0.0 -> +0.0 (they compare equal anyway)
-      int ei = e;
-      bool ins = false;
+    const int64_t TE = T * E;
+    constexpr int G = 4;  // experts whose scores are fetched together (loads in flight)
+    for (int eb = g; eb < E; eb += G * L) {
+      float vv[G];
 #pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        const bool take = ins || better(v, ei, lv[j], li[j]);
-        if (take) {
-          const float tv = lv[j];
-          const int te = li[j];
-          lv[j] = v;
-          li[j] = ei;
-          v = tv;
-          ei = te;
+      for (int q = 0; q < G; ++q) {
+        const int e = eb + q * L;
+        vv[q] = e < E ? part[t * E + e] : 0.f;
+      }
+      float pv[kMaxRouterSplits - 1][G];  // all slices' loads in flight at once
+#pragma unroll
+      for (int s = 1; s < kMaxRouterSplits; ++s)
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+          const int e = eb + q * L;
+          pv[s - 1][q] = (s < S && e < E) ? part[s * TE + t * E + e] : 0.f;
         }
-        ins = ins || take;
+#pragma unroll
+      for (int s = 1; s < kMaxRouterSplits; ++s)  // slice order
+#pragma unroll
+        for (int q = 0; q < G; ++q)
+          if (s < S) vv[q] += pv[s - 1][q];
+#pragma unroll
+      for (int q = 0; q < G; ++q) {
+        const int e = eb + q * L;
+        if (e >= E) break;
+        float v = vv[q];
+        if (bias) v += bias[e];
+        if (logits_out) logits_out[t * E + e] = v;
+        v += 0.0f;  // -0.0 -> +0.0 (they compare equal anyway)
+        int ei = e;
+        bool ins = false;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+          const bool take = ins || better(v, ei, lv[j], li[j]);
+          if (take) {
+            const float tv = lv[j];
+            const int te = li[j];
+            lv[j] = v;
+            li[j] = ei;
+            v = tv;
+            ei = te;
+          }
+          ins = ins || take;
+        }
       }
     }
   }
@@ -174,49 +231,74 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   if (valid && g < k) {
     idx[t * k + g] = sel_e;
     w[t * k + g] = static_cast<float>(z / sum);
+    if (HIST) atomicAdd(&hist[sel_e], 1);  // integer counts: order-free
+  }
+  if (HIST) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) tile_cnt[static_cast<int64_t>(blockIdx.x) * E + e] = hist[e];
   }
 }
 
-template <int L, int KMAX>
-hipError_t route_launch(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w,
-                        hipStream_t s) {
-  const int64_t tpb = 256 / L;
-  route_kernel<L, KMAX><<<dim3(static_cast<unsigned>(ceil_div(T, tpb))), dim3(256), 0, s>>>(
-      logits, T, E, k, idx, w);
+template <int L, int KMAX, bool HIST>
+hipError_t route_launch(const float* part, int S, const float* bias, int64_t T, int E, int k,
+                        float* logits_out, int32_t* idx, float* w, int32_t* tile_cnt, hipStream_t s) {
+  const int64_t tpb = 1024 / L;
+  route_kernel<L, KMAX, HIST><<<dim3(static_cast<unsigned>(ceil_div(T, tpb))), dim3(1024),
+                                HIST ? E * sizeof(int) : 0, s>>>(part, S, bias, T, E, k, logits_out, idx, w,
+                                                                 tile_cnt);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_router_logits(const void* x, const void* wr, const float* bias, int64_t T,
-                                int64_t d, int E, bool bf16, float* logits, hipStream_t s) {
+int router_splits(int64_t T, int64_t d, int E, bool bf16) {
+  if (!bf16 || T == 0) return 1;
+  const int nt = E <= 16 ? 1 : (E <= 32 ? 2 : 4);
+  const int64_t items = ceil_div(T, 16) * ceil_div(E, 16 * nt);
+  const int64_t by_work = ceil_div(2048, items);        // aim at >= 2048 waves
+  const int64_t by_len = std::max<int64_t>(1, d / 256);  // at least 256 of d per slice
+  return static_cast<int>(std::max<int64_t>(1, std::min({by_work, by_len, int64_t{kMaxRouterSplits}})));
+}
+
+hipError_t launch_router_logits(const void* x, const void* wr, int64_t T, int64_t d, int E, bool bf16,
+                                int S, float* part, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (!bf16) {
     const int64_t n = T * E;
     router_logits_f32<<<dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, s>>>(
-        static_cast<const float*>(x), static_cast<const float*>(wr), bias, T, d, E, logits);
+        static_cast<const float*>(x), static_cast<const float*>(wr), T, d, E, part);
     return hipGetLastError();
   }
   const int nt = E <= 16 ? 1 : (E <= 32 ? 2 : 4);
-  const dim3 grid(static_cast<unsigned>(ceil_div(T, 64)), static_cast<unsigned>(ceil_div(E, 16 * nt)));
+  const int64_t kper = ceil_div(ceil_div(d, S), 32) * 32;
+  const int64_t items = ceil_div(T, 16) * ceil_div(E, 16 * nt) * S;
+  const dim3 grid(static_cast<unsigned>(ceil_div(items, 4)));
   const auto* xb = static_cast<const bf16_t*>(x);
   const auto* wb = static_cast<const bf16_t*>(wr);
   if (nt == 1)
-    router_logits_bf16<1><<<grid, dim3(256), 0, s>>>(xb, wb, bias, T, d, E, logits);
+    router_logits_bf16<1><<<grid, dim3(256), 0, s>>>(xb, wb, T, d, E, S, kper, part);
   else if (nt == 2)
-    router_logits_bf16<2><<<grid, dim3(256), 0, s>>>(xb, wb, bias, T, d, E, logits);
+    router_logits_bf16<2><<<grid, dim3(256), 0, s>>>(xb, wb, T, d, E, S, kper, part);
   else
-    router_logits_bf16<4><<<grid, dim3(256), 0, s>>>(xb, wb, bias, T, d, E, logits);
+    router_logits_bf16<4><<<grid, dim3(256), 0, s>>>(xb, wb, T, d, E, S, kper, part);
   return hipGetLastError();
 }
 
-hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* idx, float* w,
-                        hipStream_t s) {
+bool route_builds_histogram(int k) { return k <= 16; }
+
+hipError_t launch_route(const float* part, int S, const float* bias, int64_t T, int E, int k,
+                        float* logits_out, int32_t* idx, float* w, int32_t* tile_cnt, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (k <= 2) return route_launch<16, 2>(logits, T, E, k, idx, w, s);
-  if (k <= 8) return route_launch<16, 8>(logits, T, E, k, idx, w, s);
-  if (k <= 16) return route_launch<16, 16>(logits, T, E, k, idx, w, s);
-  return route_launch<32, 32>(logits, T, E, k, idx, w, s);
+  if (tile_cnt && !route_builds_histogram(k)) return hipErrorInvalidValue;
+  if (tile_cnt) {
+    if (k <= 2) return route_launch<16, 2, true>(part, S, bias, T, E, k, logits_out, idx, w, tile_cnt, s);
+    if (k <= 8) return route_launch<16, 8, true>(part, S, bias, T, E, k, logits_out, idx, w, tile_cnt, s);
+    return route_launch<16, 16, true>(part, S, bias, T, E, k, logits_out, idx, w, tile_cnt, s);
+  }
+  if (k <= 2) return route_launch<16, 2, false>(part, S, bias, T, E, k, logits_out, idx, w, nullptr, s);
+  if (k <= 8) return route_launch<16, 8, false>(part, S, bias, T, E, k, logits_out, idx, w, nullptr, s);
+  if (k <= 16) return route_launch<16, 16, false>(part, S, bias, T, E, k, logits_out, idx, w, nullptr, s);
+  return route_launch<32, 32, false>(part, S, bias, T, E, k, logits_out, idx, w, nullptr, s);
 }
 
 }  // namespace moe

@@ -99,6 +99,7 @@ def test_zero_tokens_returns_ok_without_launching():
     _layer(T=0, workspace=None, workspace_bytes=0)
     moe.moe_route(FAKE, 0, 8, 2, FAKE, FAKE)
     moe.moe_router(FAKE, FAKE, None, 0, 128, 8, 2, "bf16", FAKE, FAKE, None, None, 0)
+    assert moe.moe_router_workspace_size(64, 7168, 256, "bf16") >= 64 * 256 * 4
     moe.moe_permute(FAKE, FAKE, 0, 128, 8, 2, 20, 1, "bf16", FAKE, FAKE, None, FAKE, FAKE, None, None, None, 0)
     moe.moe_combine(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 128, 8, 2, 20, "bf16", FAKE * 2)
 

@@ -65,6 +65,7 @@ def test_route_given_logits_is_exact(T, E, k, kind):
 ROUTER_CASES = [
     (300, 256, 8, 2, "bf16", None), (200, 1024, 64, 6, "bf16", "zipf1.2"), (130, 520, 256, 8, "bf16", None),
     (100, 128, 8, 2, "f32", None), (65, 72, 20, 3, "bf16", None), (1, 4096, 8, 2, "bf16", None),
+    (64, 7168, 256, 8, "bf16", None), (40, 2048, 64, 20, "bf16", "zipf1.2"), (4100, 4096, 8, 2, "bf16", None),
 ]
 
 
@@ -80,7 +81,9 @@ def test_router_scores_choice_and_gates(T, d, E, k, dtype, bias):
     w_ref = oracle.gate_weights(l_ref, idx_ref)
     logits, idx, w = _f32(T, E), _i32(T, k), _f32(T, k)
     b = None if wl.bias_vec is None else torch.from_numpy(wl.bias_vec).cuda()
-    moe.moe_router(to_dev(wl.x, dtype), to_dev(wl.wr, dtype), b, T, d, E, k, dtype, idx, w, logits, None, 0)
+    ws_n = moe.moe_router_workspace_size(T, d, E, dtype)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    moe.moe_router(to_dev(wl.x, dtype), to_dev(wl.wr, dtype), b, T, d, E, k, dtype, idx, w, logits, ws, ws_n)
     torch.cuda.synchronize()
     tol = logits_tolerance(x64, wr64, wl.bias_vec)
     err = np.abs(logits.cpu().numpy().astype(np.float64) - l_ref)
@@ -154,6 +157,7 @@ GEMM_CASES = [
     (16, 5, 128, 128, "bf16"), (2, 128, 64, 64, "bf16"), (1, 1, 8, 8, "bf16"), (5, 40, 36, 20, "f32"),
     (3, 600, 256, 384, "bf16"), (2, 1100, 520, 264, "bf16"), (4, 512, 64, 1032, "bf16"),
     (3, 700, 384, 640, "bf16"), (2, 513, 128, 128, "bf16"), (5, 900, 1024, 256, "bf16"),
+    (40, 12, 256, 96, "bf16"), (8, 16, 4096, 1024, "bf16"), (3, 3, 40, 24, "bf16"),
 ]
 
 
