@@ -10,9 +10,11 @@ thread, with identical bits. bf16 tensors are returned as uint16 bit patterns
 Near-tie rejection: a token whose top k+1 router scores have an adjacent gap
 of at most 1e-3 is redrawn (stream keyed by the token and the attempt), so the
 ordered top-k choice is unambiguous between an fp64 reference and an fp32
-accumulation. That check is the only score this module computes, and only to
-accept or redraw an input row; no result of it is ever used as an expected
-value.
+accumulation. With a rank limit M (a token may use experts of at most M of the
+P ranks) the gaps are also required between the P ranks' best scores, and the
+top k+1 are taken over the experts of the M ranks with the best scores. That
+check is the only score this module computes, and only to accept or redraw an
+input row; no result of it is ever used as an expected value.
 
 Workloads (shapes of the models the pages use as examples):
   tiny_f32            T=64    d=128  E=8   k=2 d_ff=256   cf=1.25 fp32, seed 0
@@ -22,6 +24,8 @@ Workloads (shapes of the models the pages use as examples):
                       router bias b_e = -1.2 ln(e+1) (log of Zipf(1.2) popularity)
   deepseek_v3_decode  T=64    d=7168 E=256 k=8 d_ff=2048  cf=2.0  bf16, seed 4,
                       expert weights shared with deepseek_v3_prefill
+  deepseek_v3_node_limited  as deepseek_v3_prefill with each token's experts
+                      on at most M=4 of the P=8 ranks, seed 5, same weights
 """
 from __future__ import annotations
 
@@ -84,6 +88,7 @@ class Workload:
     cf: float
     dtype: str = "bf16"
     P: int = 1
+    max_ranks: int = 0               # 0: no limit; else experts of at most this many ranks
     seed: int = 0
     weight_seed: int | None = None
     x_std: float = 1.0
@@ -118,11 +123,23 @@ class Workload:
         s = bits_to_f64(self.x[rows], self.dtype) @ bits_to_f64(self.wr, self.dtype).T
         if self.bias_vec is not None:
             s += self.bias_vec.astype(np.float64)[None, :]
-        m = min(self.k + 1, self.E)
+        bad = np.zeros(rows.size, dtype=bool)
+        if 0 < self.max_ranks < self.P:
+            per = self.E // self.P
+            best = s.reshape(rows.size, self.P, per).max(axis=2)
+            rb = -np.sort(-best, axis=1)
+            bad |= (rb[:, :-1] - rb[:, 1:]).min(axis=1) <= GAP
+            keep = np.argsort(-best, axis=1, kind="stable")[:, :self.max_ranks]
+            allowed = np.zeros_like(best, dtype=bool)
+            np.put_along_axis(allowed, keep, True, axis=1)
+            s = np.where(np.repeat(allowed, per, axis=1), s, -np.inf)
+            m = min(self.k + 1, self.max_ranks * per)
+        else:
+            m = min(self.k + 1, self.E)
         if m < 2:
-            return np.zeros(rows.size, dtype=bool)
+            return bad
         top = -np.sort(-s, axis=1)[:, :m]
-        return (top[:, :-1] - top[:, 1:]).min(axis=1) <= GAP
+        return bad | ((top[:, :-1] - top[:, 1:]).min(axis=1) <= GAP)
 
     def _reject_near_ties(self):
         bad = np.nonzero(self._near_tied(np.arange(self.T)))[0]
@@ -179,6 +196,8 @@ WORKLOADS = {
     "deepseek_v3_prefill": dict(T=8192, d=7168, E=256, k=8, d_ff=2048, cf=1.25, P=8, seed=2),
     "zipf_skew_drops": dict(T=16384, d=2048, E=64, k=6, d_ff=1408, cf=1.0, seed=3, bias="zipf1.2"),
     "deepseek_v3_decode": dict(T=64, d=7168, E=256, k=8, d_ff=2048, cf=2.0, seed=4, weight_seed=2),
+    "deepseek_v3_node_limited": dict(T=8192, d=7168, E=256, k=8, d_ff=2048, cf=1.25, P=8, max_ranks=4, seed=5,
+                                     weight_seed=2),
 }
 
 

@@ -8,7 +8,8 @@ does, and this module imports nothing from the HIP package.
 What is computed, in the pages' own order (sources are cited per function):
 
   1. router logits, one fp32 score per (token, expert);
-  2. top-k expert choice per token and the k gate weights;
+  2. top-k expert choice per token (optionally limited to the experts of at
+     most M of the P ranks) and the k gate weights;
   3. expert capacity C and the stable token-order slot of every routed copy,
      with copies beyond C dropped;
   4. the fixed-capacity per-expert buckets (and their view as P contiguous
@@ -42,7 +43,7 @@ import numpy as np
 
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "f64_to_f32", "encode", "silu",
-    "decode", "capacity", "router_logits", "topk_experts", "gate_weights",
+    "decode", "capacity", "router_logits", "topk_experts", "rank_limited_experts", "gate_weights",
     "assign_slots", "dispatch_buckets", "send_counts", "expert_hidden", "expert_mlp",
     "combine", "routing_stats", "dispatch_bytes", "layer_forward",
 ]
@@ -135,6 +136,36 @@ def topk_experts(logits32: np.ndarray, k: int) -> np.ndarray:
         raise ValueError("need 1 <= k <= E")
     # stable sort of -score: equal scores keep ascending expert order
     order = np.argsort(-l, axis=1, kind="stable")
+    return order[:, :k].astype(np.int32)
+
+
+def rank_limited_experts(logits32: np.ndarray, k: int, P: int, M: int) -> np.ndarray:
+    """Top-k choice restricted to experts held by at most M of the P ranks.
+
+    [EP-A2A] "The bandwidth bill" (node-limited routing: a token's experts must
+    sit on a small number of nodes, so that most all-to-all traffic stays on the
+    fast local fabric) and [EP-vs-TP] "Expert parallelism pays in all-to-all
+    dispatch" (DeepSeek-V3 allows at most 4 nodes per token). Rank p owns the
+    contiguous experts [p E/P, (p+1) E/P), as in the send buffers.
+
+    The pages name the constraint but not how the ranks are picked. Reading
+    taken: a rank's score is the best score among its experts; the M ranks with
+    the highest rank scores are allowed (lower rank index first on a tie); the
+    k experts are then the best of the allowed ranks' experts, ordered as in
+    topk_experts. M = 0 or M >= P is no limit. Needs M * (E/P) >= k.
+    """
+    l = np.asarray(logits32, dtype=np.float32) + np.float32(0.0)
+    T, E = l.shape
+    if M == 0 or M >= P:
+        return topk_experts(l, k)
+    if P < 1 or E % P or M < 0 or M * (E // P) < k:
+        raise ValueError("need E % P == 0 and M * (E / P) >= k")
+    rank_score = l.reshape(T, P, E // P).max(axis=2)
+    best_ranks = np.argsort(-rank_score, axis=1, kind="stable")[:, :M]
+    allowed = np.zeros((T, P), dtype=bool)
+    np.put_along_axis(allowed, best_ranks, True, axis=1)
+    masked = np.where(np.repeat(allowed, E // P, axis=1), l, np.float32(-np.inf))
+    order = np.argsort(-masked, axis=1, kind="stable")
     return order[:, :k].astype(np.int32)
 
 
@@ -322,7 +353,7 @@ def routing_stats(slot: np.ndarray, routed: np.ndarray, kept: np.ndarray, C: int
 # ---------------------------------------------------------------------------
 
 def layer_forward(x, wr, expert_weights, T, d, d_ff, E, k, cf, dtype, P=1, bias=None,
-                  tokens=None):
+                  tokens=None, max_ranks=0):
     """The layer as the plain per-token definition, steps 1 to 7 above.
 
     x [T, d] and wr [E, d] are the inputs (bf16 as bit patterns, or fp32).
@@ -330,7 +361,8 @@ def layer_forward(x, wr, expert_weights, T, d, d_ff, E, k, cf, dtype, P=1, bias=
     expert e in the same format, so a caller can supply them lazily.
     Routing, slots and statistics are computed for all T tokens; the layer
     output only for `tokens` (all when None), since each output row depends
-    only on its own token once the slots are known.
+    only on its own token once the slots are known. max_ranks > 0 limits each
+    token's experts to that many of the P ranks (rank_limited_experts).
 
     Returns a dict: logits, idx, w, C, slot, src, routed, kept, stats,
     tokens, out64 (fp64, unrounded), out (rounded once to dtype; a token with
@@ -339,7 +371,7 @@ def layer_forward(x, wr, expert_weights, T, d, d_ff, E, k, cf, dtype, P=1, bias=
     x = np.asarray(x)
     x64 = decode(x, dtype)
     logits = router_logits(x64, decode(wr, dtype), bias)
-    idx = topk_experts(logits, k)
+    idx = rank_limited_experts(logits, k, P, max_ranks)
     w = gate_weights(logits, idx)
     C = capacity(T, E, k, cf)
     slot, src, routed, kept = assign_slots(idx, E, C)

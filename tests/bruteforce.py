@@ -3,6 +3,9 @@
 Written independently of the oracle, with different algorithms wherever one
 exists, so that a slip in either shows up as a mismatch:
   * top-k by repeated arg-max (first maximum wins), not by sorting;
+  * rank-limited top-k two ways: a greedy walk down the experts that skips any
+    expert whose rank would be one too many, and an exhaustive search for the
+    allowed k-subset whose scores, best first, are lexicographically largest;
   * capacity as the smallest integer C with C*E >= cf*k*T in exact rationals;
   * slots from per-expert counters walked in token order, not from a sort;
   * every dot product as an explicit Python loop in double precision.
@@ -49,6 +52,42 @@ def topk(row, k):
     return chosen
 
 
+def rank_of(e, E, P):
+    return e // (E // P)
+
+
+def rank_limited_greedy(row, k, P, M):
+    """Walk experts best first; take one unless its rank would be rank M+1."""
+    E = len(row)
+    chosen, ranks = [], []
+    banned = set()
+    while len(chosen) < k:
+        e = argmax_first(row, banned)
+        banned.add(e)
+        r = rank_of(e, E, P)
+        if r in ranks or len(ranks) < M:
+            chosen.append(e)
+            if r not in ranks:
+                ranks.append(r)
+    return chosen
+
+
+def rank_limited_exhaustive(row, k, P, M):
+    """Among all k-subsets touching at most M ranks, the one whose members,
+    ordered best first (lower index first on equal scores), compare largest."""
+    import itertools
+    E = len(row)
+    best_key, best = None, None
+    for sub in itertools.combinations(range(E), k):
+        if len({rank_of(e, E, P) for e in sub}) > M:
+            continue
+        ordered = sorted(sub, key=lambda e: (-row[e], e))
+        key = [(-row[e], e) for e in ordered]
+        if best_key is None or key < best_key:
+            best_key, best = key, ordered
+    return best
+
+
 def gates(vals):
     m = vals[0]
     ex = [math.exp(v - m) for v in vals]
@@ -72,15 +111,19 @@ def mlp(xrow, wg, wu, wd):
     return [dot(r, h) for r in wd]
 
 
-def layer(x, wr, bias, wg, wu, wd, k, cf32):
+def layer(x, wr, bias, wg, wu, wd, k, cf32, P=1, M=0):
     """x: T lists of d doubles; wr: E lists; wg/wu: E x d_ff x d; wd: E x d x d_ff.
+    M > 0 limits every token to experts of at most M of the P ranks.
 
     Returns dict with logits, idx, w, C, slot, src, routed, kept, out (doubles).
     """
     T, E = len(x), len(wr)
     logits = [[f32(dot(x[t], wr[e]) + (bias[e] if bias is not None else 0.0)) for e in range(E)]
               for t in range(T)]
-    idx = [topk(logits[t], k) for t in range(T)]
+    if 0 < M < P:
+        idx = [rank_limited_greedy(logits[t], k, P, M) for t in range(T)]
+    else:
+        idx = [topk(logits[t], k) for t in range(T)]
     w = [gates([logits[t][e] for e in idx[t]]) for t in range(T)]
     C = capacity(T, E, k, cf32)
     fill = [0] * E

@@ -120,6 +120,62 @@ def test_topk_is_max_sum_subset():
         assert sum(l[0, idx]) == best
 
 
+# ------------------------------------------------------ rank-limited top-k ---
+
+def _rank_cases(seed, n, maxE=8):
+    rng = np.random.default_rng(seed)
+    for _ in range(n):
+        P = int(rng.choice([2, 3, 4]))
+        per = int(rng.integers(1, maxE // P + 1))
+        E = P * per
+        M = int(rng.integers(1, P))
+        k = int(rng.integers(1, min(E, M * per) + 1))
+        T = int(rng.integers(1, 5))
+        l = rng.integers(-2, 3, size=(T, E)).astype(np.float32)   # many ties
+        yield l, k, P, M
+
+
+def test_rank_limited_matches_greedy_walk_and_exhaustive_search():
+    for l, k, P, M in _rank_cases(11, 400):
+        idx = oracle.rank_limited_experts(l, k, P, M)
+        for t in range(l.shape[0]):
+            row = [float(v) for v in l[t]]
+            assert list(idx[t]) == bf.rank_limited_greedy(row, k, P, M)
+            assert list(idx[t]) == bf.rank_limited_exhaustive(row, k, P, M)
+
+
+def test_rank_limited_touches_at_most_M_ranks():
+    rng = np.random.default_rng(12)
+    T, E, P, k = 500, 256, 8, 8
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    for M in (1, 2, 4):
+        idx = oracle.rank_limited_experts(l, k, P, M)
+        ranks = idx // (E // P)
+        assert max(len(set(r)) for r in ranks.tolist()) <= M
+        assert all(len(set(r)) == k for r in idx.tolist())      # k distinct experts
+        # with M = 1 every pick lies in the rank of the token's best expert
+        if M == 1:
+            assert np.array_equal(ranks[:, 0], np.argmax(l, axis=1) // (E // P))
+            assert np.all(ranks == ranks[:, :1])
+    # unconstrained top-k that already spans <= M ranks is left as it is
+    plain = oracle.topk_experts(l, k)
+    lim = oracle.rank_limited_experts(l, k, P, 4)
+    fits = np.array([len(set(r)) <= 4 for r in (plain // (E // P)).tolist()])
+    assert fits.any() and np.array_equal(lim[fits], plain[fits])
+
+
+def test_rank_limited_special_cases_reduce_to_plain_topk():
+    rng = np.random.default_rng(13)
+    l = rng.integers(-3, 4, size=(50, 12)).astype(np.float32)
+    plain = oracle.topk_experts(l, 3)
+    assert np.array_equal(oracle.rank_limited_experts(l, 3, 4, 0), plain)     # M = 0: no limit
+    assert np.array_equal(oracle.rank_limited_experts(l, 3, 4, 4), plain)     # M = P
+    assert np.array_equal(oracle.rank_limited_experts(l, 3, 1, 1), plain)     # one rank
+    assert np.array_equal(oracle.rank_limited_experts(l, 3, 12, 3), plain)    # one expert per rank, M = k
+    with pytest.raises(ValueError):
+        oracle.rank_limited_experts(l, 5, 4, 1)                                # 1 rank holds 3 < 5
+
+
 # ------------------------------------------------------------------ gates ---
 
 def test_gates_closed_forms():
@@ -361,6 +417,30 @@ def test_layer_matches_bruteforce(case):
     assert np.allclose(r["out64"], np.array(b["out"]), rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("case", range(8))
+def test_rank_limited_layer_matches_bruteforce(case):
+    rng = np.random.default_rng(300 + case)
+    P = int(rng.choice([2, 3]))
+    E = P * int(rng.integers(1, 3))
+    M = int(rng.integers(1, P))
+    k = int(rng.integers(1, min(3, M * (E // P)) + 1))
+    T, d, f = int(rng.integers(1, 7)), int(rng.integers(2, 6)), int(rng.integers(1, 5))
+    cf = float(rng.choice([0.5, 1.0, 2.0]))
+    dtype = "bf16" if case % 2 else "f32"
+    wl = moe_inputs.custom(T=T, d=d, E=E, k=k, d_ff=f, cf=cf, dtype=dtype, seed=400 + case, wr_std=1.0,
+                           P=P, max_ranks=M)
+    r = oracle.layer_forward(wl.x, wl.wr, wl.expert, T, d, f, E, k, cf, dtype, P=P, max_ranks=M)
+    ex = [wl.expert(e) for e in range(E)]
+    b = bf.layer(_as_lists(wl.x, dtype), _as_lists(wl.wr, dtype), None,
+                 [_as_lists(e[0], dtype) for e in ex], [_as_lists(e[1], dtype) for e in ex],
+                 [_as_lists(e[2], dtype) for e in ex], k, float(np.float32(cf)), P=P, M=M)
+    assert r["idx"].tolist() == b["idx"]
+    assert max(len(set(row)) for row in (r["idx"] // (E // P)).tolist()) <= M
+    assert r["slot"].tolist() == b["slot"] and r["kept"].tolist() == b["kept"]
+    assert np.allclose(r["w"], np.array(b["w"], np.float32), rtol=2 ** -23, atol=0)
+    assert np.allclose(r["out64"], np.array(b["out"]), rtol=1e-12, atol=1e-13)
+
+
 def test_dense_special_case_single_expert():
     """E = 1, k = 1, cf >= 1: every token kept with gate 1, out = x + MLP(x)."""
     wl = moe_inputs.custom(T=9, d=5, E=1, k=1, d_ff=4, cf=1.0, dtype="f32", seed=13)
@@ -396,3 +476,13 @@ def test_generator_value_laws():
     wg, wu, wd = (oracle.decode(a, "bf16") for a in wl.expert(3))
     assert abs(wg.std() * math.sqrt(256) - 1) < 0.02 and abs(wd.std() * math.sqrt(128) - 1) < 0.02
     assert np.allclose(wl.bias_vec, -1.2 * np.log(np.arange(1, 9)), rtol=1e-6)
+
+
+def test_generator_rank_limited_gap_conditioning():
+    wl = moe_inputs.custom(T=300, d=64, E=32, k=4, d_ff=16, cf=1.0, seed=23, P=8, max_ranks=2)
+    l = oracle.router_logits(oracle.decode(wl.x, "bf16"), oracle.decode(wl.wr, "bf16")).astype(np.float64)
+    best = -np.sort(-l.reshape(300, 8, 4).max(axis=2), axis=1)
+    assert (best[:, :-1] - best[:, 1:]).min() > 1e-3 - 1e-6
+    idx = oracle.rank_limited_experts(l.astype(np.float32), 4, 8, 2)
+    chosen = np.take_along_axis(l, idx, axis=1)
+    assert (chosen[:, :-1] - chosen[:, 1:]).min() > 1e-3 - 1e-6
