@@ -93,7 +93,8 @@ def cpu_baseline(wl, host_w, sample: int):
     for _ in range(3):  # median of three runs
         t0 = time.perf_counter()
         oracle.layer_forward(wl.x, wl.wr, lambda e: (host_w[0][e], host_w[1][e], host_w[2][e]), wl.T, wl.d,
-                             wl.d_ff, wl.E, wl.k, wl.cf, wl.dtype, P=wl.P, bias=wl.bias_vec, tokens=tokens)
+                             wl.d_ff, wl.E, wl.k, wl.cf, wl.dtype, P=wl.P, bias=wl.bias_vec, tokens=tokens,
+                             max_ranks=wl.max_ranks)
         times.append(time.perf_counter() - t0)
     dt = sorted(times)[1]
     return {"value": round(tokens.size / dt, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
@@ -142,8 +143,8 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
-        moe.moe_layer_forward(x, wr, bias, wg, wu, wd, T, d, d_ff, E, k, cf, P, wl.dtype, outs["out"], outs, ws,
-                              ws_bytes, stream)
+        moe.moe_layer_forward(x, wr, bias, wg, wu, wd, T, d, d_ff, E, k, cf, P, wl.max_ranks, wl.dtype, outs["out"],
+                              outs, ws, ws_bytes, stream)
 
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
@@ -227,8 +228,9 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic (seeded Gaussian inputs and random-init weights of the named shape)",
-        "config": {"workload": wl.name, "T": T, "d": d, "E": E, "k": k, "d_ff": d_ff, "cf": cf, "P": P, "C": C,
-                   "N_kept": n_kept, "touched_experts": touched, "dropped": totals[0]},
+        "config": {"workload": wl.name, "T": T, "d": d, "E": E, "k": k, "d_ff": d_ff, "cf": cf, "P": P,
+                   "max_ranks": wl.max_ranks, "C": C, "N_kept": n_kept, "touched_experts": touched,
+                   "dropped": totals[0]},
         "gpu_ms_per_step": round(gpu_ms, 4),
         "grouped_gemm_mfma_frac": None if not stages else round(
             (work["gate_up"]["flops"] + work["down"]["flops"]) /

@@ -111,31 +111,41 @@ int moe_workspace_size(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k,
  *   a token with every copy dropped is copied through bit for bit.
  * x [T, d], out [T, d] (must not overlap x), router_bias [E] fp32 or NULL,
  * P >= 1 with E % P == 0 (send-buffer view only; no communication).
+ * max_ranks: 0 (or >= P) for plain top-k; otherwise each token's experts are
+ * limited to max_ranks of the P ranks, chosen as in moe_route.
  * stats may be NULL. workspace must hold moe_workspace_size() bytes, 256-byte
  * aligned. */
 int moe_layer_forward(const void* x, const void* W_router, const float* router_bias,
                       const void* W_gate, const void* W_up, const void* W_down,
                       int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k, float cf,
-                      int32_t P, moe_dtype_t dtype, void* out, moe_stats_t* stats,
-                      void* workspace, size_t workspace_bytes, void* stream);
+                      int32_t P, int32_t max_ranks, moe_dtype_t dtype, void* out,
+                      moe_stats_t* stats, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Router stage ([EP-inferensys] gating-network entry): logits on the matrix
- * cores, then top-k and gates as in moe_route. logits_out [T, E] fp32 may be
+ * cores, then top-k (with the rank limit P, max_ranks) and gates as in moe_route. logits_out [T, E] fp32 may be
  * NULL; otherwise it receives the scores (bias included). The scores are
  * summed over slices of d in a fixed order, so results do not depend on
  * scheduling. workspace: moe_router_workspace_size() bytes, 256-byte aligned. */
 int moe_router_workspace_size(int64_t T, int64_t d, int32_t E, moe_dtype_t dtype, size_t* bytes);
 int moe_router(const void* x, const void* W_router, const float* router_bias, int64_t T,
-               int64_t d, int32_t E, int32_t k, moe_dtype_t dtype, int32_t* topk_idx,
-               float* topk_w, float* logits_out, void* workspace, size_t workspace_bytes,
-               void* stream);
+               int64_t d, int32_t E, int32_t k, int32_t P, int32_t max_ranks,
+               moe_dtype_t dtype, int32_t* topk_idx, float* topk_w, float* logits_out,
+               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Top-k and gates from given fp32 logits [T, E]: per token the k experts in
  * order of score descending, then index ascending (+0 == -0); gates
  * w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), evaluated in fp64, rounded to
- * fp32. */
-int moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_idx,
-              float* topk_w, void* stream);
+ * fp32.
+ * Rank limit ([EP-A2A] "The bandwidth bill", node-limited routing; [EP-vs-TP]
+ * "Expert parallelism pays in all-to-all dispatch", at most 4 nodes per token
+ * in DeepSeek-V3): with 0 < max_ranks < P, rank p owning experts
+ * [p E/P, (p+1) E/P), a rank's score is its best expert score, the max_ranks
+ * best ranks are allowed (lower rank first on a tie) and the top k is taken
+ * over their experts only. max_ranks = 0 or >= P: no limit.
+ * Errors: P < 1 or E % P != 0, max_ranks < 0, or max_ranks * E/P < k
+ * (MOE_ERR_INVALID_ARG); a limit with P > 64 (MOE_ERR_UNSUPPORTED). */
+int moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t P, int32_t max_ranks,
+              int32_t* topk_idx, float* topk_w, void* stream);
 
 /* Permutation stage ([EP-inferensys] capacity and memory entries; [EP-A2A]
  * "Why fixed-size buffers matter here"): from topk_idx [T, k] computes

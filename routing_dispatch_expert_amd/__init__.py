@@ -47,11 +47,11 @@ _P, _I32, _I64, _F32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, cty
 _SIGS = {
     "moe_capacity": [_I64, _I32, _I32, _F32, _P],
     "moe_workspace_size": [_I64, _I64, _I64, _I32, _I32, _F32, _I32, ctypes.c_int, _P],
-    "moe_layer_forward": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _F32, _I32, ctypes.c_int,
+    "moe_layer_forward": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _F32, _I32, _I32, ctypes.c_int,
                           _P, ctypes.POINTER(moe_stats_t), _P, _SZ, _P],
     "moe_router_workspace_size": [_I64, _I64, _I32, ctypes.c_int, _P],
-    "moe_router": [_P, _P, _P, _I64, _I64, _I32, _I32, ctypes.c_int, _P, _P, _P, _P, _SZ, _P],
-    "moe_route": [_P, _I64, _I32, _I32, _P, _P, _P],
+    "moe_router": [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, ctypes.c_int, _P, _P, _P, _P, _SZ, _P],
+    "moe_route": [_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P],
     "moe_permute_workspace_size": [_I64, _I32, _P],
     "moe_permute": [_P, _P, _I64, _I64, _I32, _I32, _I64, _I32, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P,
                     _P, _SZ, _P],
@@ -150,11 +150,11 @@ def _stats(stats) -> "ctypes.POINTER(moe_stats_t) | None":
     return ctypes.pointer(s)
 
 
-def moe_layer_forward(x, W_router, router_bias, W_gate, W_up, W_down, T, d, d_ff, E, k, cf, P, dtype,
-                      out, stats, workspace, workspace_bytes, stream=None):
+def moe_layer_forward(x, W_router, router_bias, W_gate, W_up, W_down, T, d, d_ff, E, k, cf, P, max_ranks,
+                      dtype, out, stats, workspace, workspace_bytes, stream=None):
     """stats: None or a dict of moe_stats_t field name -> tensor (or None)."""
     _check(lib().moe_layer_forward(_ptr(x), _ptr(W_router), _ptr(router_bias), _ptr(W_gate), _ptr(W_up),
-                                   _ptr(W_down), T, d, d_ff, E, k, cf, P, _dtype(dtype), _ptr(out),
+                                   _ptr(W_down), T, d, d_ff, E, k, cf, P, max_ranks, _dtype(dtype), _ptr(out),
                                    _stats(stats), _ptr(workspace), workspace_bytes, _stream(stream)),
            "moe_layer_forward")
 
@@ -165,15 +165,15 @@ def moe_router_workspace_size(T, d, E, dtype) -> int:
     return n.value
 
 
-def moe_router(x, W_router, router_bias, T, d, E, k, dtype, topk_idx, topk_w, logits_out, workspace,
-               workspace_bytes, stream=None):
-    _check(lib().moe_router(_ptr(x), _ptr(W_router), _ptr(router_bias), T, d, E, k, _dtype(dtype),
+def moe_router(x, W_router, router_bias, T, d, E, k, P, max_ranks, dtype, topk_idx, topk_w, logits_out,
+               workspace, workspace_bytes, stream=None):
+    _check(lib().moe_router(_ptr(x), _ptr(W_router), _ptr(router_bias), T, d, E, k, P, max_ranks, _dtype(dtype),
                             _ptr(topk_idx), _ptr(topk_w), _ptr(logits_out), _ptr(workspace),
                             workspace_bytes, _stream(stream)), "moe_router")
 
 
-def moe_route(logits, T, E, k, topk_idx, topk_w, stream=None):
-    _check(lib().moe_route(_ptr(logits), T, E, k, _ptr(topk_idx), _ptr(topk_w), _stream(stream)),
+def moe_route(logits, T, E, k, P, max_ranks, topk_idx, topk_w, stream=None):
+    _check(lib().moe_route(_ptr(logits), T, E, k, P, max_ranks, _ptr(topk_idx), _ptr(topk_w), _stream(stream)),
            "moe_route")
 
 
@@ -227,11 +227,12 @@ def _require(t, name, torch_dtype, shape):
 
 
 def forward(x, W_router, W_gate, W_up, W_down, k, cf, P=1, router_bias=None, stream=None,
-            want_buckets=False, want_src=False, workspace=None):
+            want_buckets=False, want_src=False, workspace=None, max_ranks=0):
     """Run the layer once on torch device tensors; returns a dict of outputs.
 
     x [T, d]; W_router [E, d]; W_gate, W_up [E, d_ff, d]; W_down [E, d, d_ff]
-    (bf16 or fp32, all the same dtype); router_bias [E] fp32 or None.
+    (bf16 or fp32, all the same dtype); router_bias [E] fp32 or None;
+    max_ranks > 0 limits each token's experts to that many of the P ranks.
     """
     import torch
     T, d = x.shape
@@ -264,7 +265,7 @@ def forward(x, W_router, W_gate, W_up, W_down, k, cf, P=1, router_bias=None, str
     nbytes = moe_workspace_size(T, d, d_ff, E, k, cf, P, dt)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    moe_layer_forward(x, W_router, router_bias, W_gate, W_up, W_down, T, d, d_ff, E, k, cf, P, dt,
+    moe_layer_forward(x, W_router, router_bias, W_gate, W_up, W_down, T, d, d_ff, E, k, cf, P, max_ranks, dt,
                       res["out"], res, workspace, nbytes, stream)
     res["workspace"] = workspace
     return res

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t v = v0 + LANES * u;
-        if (v < V) orow[v] = xv[u];
+        if (v < V) store_stream(&orow[v], xv[u]);
       }
       continue;
     }
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
           ow[q] = __float_as_uint(__uint_as_float(xw[q]) + acc[u][q]);
         }
       }
-      orow[v] = uint4{ow[0], ow[1], ow[2], ow[3]};
+      store_stream(&orow[v], uint4{ow[0], ow[1], ow[2], ow[3]});
     }
   }
 }

@@ -34,6 +34,14 @@ __device__ inline bf16_t f32_to_bf16(float f) {
   return static_cast<bf16_t>(u >> 16);
 }
 
+// 16-byte store marked non-temporal: rows streamed out once (bucket scatter,
+// combined output) skip the caches' allocate-and-keep path.
+__device__ inline void store_stream(uint4* p, uint4 v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+}
+
 // ---- router (router.hip) ----
 // Number of d-slices S the scores are split into (partials part[S][T][E]).
 int router_splits(int64_t T, int64_t d, int E, bool bf16);
@@ -41,10 +49,15 @@ hipError_t launch_router_logits(const void* x, const void* wr, int64_t T, int64_
                                 int S, float* part, hipStream_t s);
 // Sums the S partials (slice order) and the bias, writes logits_out if given,
 // then top-k and gates; with tile_cnt, also the per-64-token-tile histogram
-// (only when route_builds_histogram(k)).
+// (only when route_builds_histogram(k)). When route_rank_limited(P, M) the
+// choice is limited to experts of the M best of P ranks (P <= 64, E % P == 0,
+// M * E/P >= k); with S > 1 or a bias and no logits_out, the summed scores are
+// then written over slice 0 of part.
 bool route_builds_histogram(int k);
+bool route_rank_limited(int P, int M);
 hipError_t launch_route(const float* part, int S, const float* bias, int64_t T, int E, int k,
-                        float* logits_out, int32_t* idx, float* w, int32_t* tile_cnt, hipStream_t s);
+                        float* logits_out, int32_t* idx, float* w, int32_t* tile_cnt, int P, int M,
+                        hipStream_t s);
 
 // ---- permutation (permute.hip) ----
 hipError_t launch_tile_hist(const int32_t* idx, int64_t T, int k, int E, int32_t* tile_cnt,

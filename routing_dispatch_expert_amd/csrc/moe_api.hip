@@ -46,6 +46,7 @@ int hip_fail(hipError_t e, const char* what) {
 constexpr size_t kAlign = 256;
 constexpr int kMaxE = 4096;
 constexpr int kMaxK = 32;
+constexpr int kMaxLimitRanks = 64;  // ranks of the rank-limited routing (one 64-bit mask)
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -93,6 +94,18 @@ int check_expert_extent(int64_t C, int64_t d, int64_t d_ff) {
   const int64_t lim = int64_t{1} << 31;
   if ((C + 256) * std::max(d, d_ff) * 4 >= lim || d * d_ff * 4 >= lim)
     return fail(MOE_ERR_UNSUPPORTED, "one expert's bucket or weight matrix exceeds 2^31 bytes");
+  return MOE_OK;
+}
+
+// Rank limit of the routing: max_ranks = 0 (or >= P) is no limit; otherwise
+// each token's experts lie on at most max_ranks of the P ranks.
+int check_rank_limit(int32_t E, int32_t k, int32_t P, int32_t max_ranks) {
+  if (P < 1 || E % P) return fail(MOE_ERR_INVALID_ARG, "P=%d must be >= 1 and divide E=%d", P, E);
+  if (max_ranks < 0) return fail(MOE_ERR_INVALID_ARG, "max_ranks=%d must be >= 0", max_ranks);
+  if (!moe::route_rank_limited(P, max_ranks)) return MOE_OK;
+  if (P > kMaxLimitRanks) return fail(MOE_ERR_UNSUPPORTED, "rank-limited routing needs P <= %d", kMaxLimitRanks);
+  if (static_cast<int64_t>(max_ranks) * (E / P) < k)
+    return fail(MOE_ERR_INVALID_ARG, "max_ranks=%d ranks of %d experts hold fewer than k=%d", max_ranks, E / P, k);
   return MOE_OK;
 }
 
@@ -212,11 +225,12 @@ int moe_workspace_size(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k,
 int moe_layer_forward(const void* x, const void* W_router, const float* router_bias,
                       const void* W_gate, const void* W_up, const void* W_down, int64_t T,
                       int64_t d, int64_t d_ff, int32_t E, int32_t k, float cf, int32_t P,
-                      moe_dtype_t dtype, void* out, moe_stats_t* stats, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      int32_t max_ranks, moe_dtype_t dtype, void* out, moe_stats_t* stats,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   int64_t C;
   int st = check_layer_shape(T, d, d_ff, E, k, cf, P, dtype, &C);
   if (st != MOE_OK) return st;
+  if ((st = check_rank_limit(E, k, P, max_ranks)) != MOE_OK) return st;
   if (!x || !W_router || !W_gate || !W_up || !W_down || !out)
     return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
   const int eb = elem_bytes(dtype);
@@ -251,7 +265,7 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
   MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTER, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTE, false, s), "event");
   MOE_HIP_TRY(moe::launch_route(p.logits, splits, router_bias, T, E, k, nullptr, idx, w,
-                                fused_hist ? p.tile_cnt : nullptr, s),
+                                fused_hist ? p.tile_cnt : nullptr, P, max_ranks, s),
               "route");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTE, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SLOTS, false, s), "event");
@@ -287,13 +301,15 @@ int moe_router_workspace_size(int64_t T, int64_t d, int32_t E, moe_dtype_t dtype
 }
 
 int moe_router(const void* x, const void* W_router, const float* router_bias, int64_t T, int64_t d,
-               int32_t E, int32_t k, moe_dtype_t dtype, int32_t* topk_idx, float* topk_w,
-               float* logits_out, void* workspace, size_t workspace_bytes, void* stream) {
+               int32_t E, int32_t k, int32_t P, int32_t max_ranks, moe_dtype_t dtype,
+               int32_t* topk_idx, float* topk_w, float* logits_out, void* workspace,
+               size_t workspace_bytes, void* stream) {
   if (!valid_dtype(dtype)) return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   if (T < 0 || d < 1 || E < 1 || k < 1 || k > E)
     return fail(MOE_ERR_INVALID_ARG, "need T >= 0, d >= 1, 1 <= k <= E");
   int st = check_width(d, dtype, "d");
   if (st != MOE_OK) return st;
+  if ((st = check_rank_limit(E, k, P, max_ranks)) != MOE_OK) return st;
   if (E > kMaxE || k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "E or k too large");
   if (T * k >= (int64_t{1} << 31)) return fail(MOE_ERR_UNSUPPORTED, "T*k must stay below 2^31");
   if (!x || !W_router || !topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
@@ -307,20 +323,23 @@ int moe_router(const void* x, const void* W_router, const float* router_bias, in
   const int S = moe::router_splits(T, d, E, bf16);
   auto* part = static_cast<float*>(workspace);
   MOE_HIP_TRY(moe::launch_router_logits(x, W_router, T, d, E, bf16, S, part, s), "router logits");
-  MOE_HIP_TRY(moe::launch_route(part, S, router_bias, T, E, k, logits_out, topk_idx, topk_w, nullptr, s),
+  MOE_HIP_TRY(moe::launch_route(part, S, router_bias, T, E, k, logits_out, topk_idx, topk_w, nullptr, P,
+                                max_ranks, s),
               "route");
   return MOE_OK;
 }
 
-int moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_idx, float* topk_w,
-              void* stream) {
+int moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t P, int32_t max_ranks,
+              int32_t* topk_idx, float* topk_w, void* stream) {
   if (T < 0 || E < 1 || k < 1 || k > E) return fail(MOE_ERR_INVALID_ARG, "need T >= 0, 1 <= k <= E");
+  const int st = check_rank_limit(E, k, P, max_ranks);
+  if (st != MOE_OK) return st;
   if (E > kMaxE || k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "E or k too large");
   if (T * k >= (int64_t{1} << 31)) return fail(MOE_ERR_UNSUPPORTED, "T*k must stay below 2^31");
   if (!logits || !topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
   if (T == 0) return MOE_OK;
-  MOE_HIP_TRY(moe::launch_route(logits, 1, nullptr, T, E, k, nullptr, topk_idx, topk_w, nullptr,
-                                static_cast<hipStream_t>(stream)),
+  MOE_HIP_TRY(moe::launch_route(logits, 1, nullptr, T, E, k, nullptr, topk_idx, topk_w, nullptr, P,
+                                max_ranks, static_cast<hipStream_t>(stream)),
               "route");
   return MOE_OK;
 }

@@ -233,7 +233,8 @@ __global__ __launch_bounds__(64) void slots_kernel(const int32_t* __restrict__ i
 
 // Row scatter: one wave per token moves its row (16-byte words, U per lane in
 // flight) to each kept destination bucket row; the row is read once and
-// written k' <= k times. The token's slots are wave-uniform scalar loads.
+// written k' <= k times with streaming stores. The token's slots are
+// wave-uniform scalar loads.
 template <int WPT>
 __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restrict__ x,
                                                            const int32_t* __restrict__ idx,
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restri
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t v = v0 + LANES * u;
-        if (v < V) dst[v] = val[u];
+        if (v < V) store_stream(&dst[v], val[u]);
       }
     }
   }

@@ -114,27 +114,69 @@ __global__ __launch_bounds__(256) void router_logits_f32(const float* __restrict
 // list of its best KMAX scores among experts g, g+L, ...; then k rounds pick
 // the group's best head (score desc, index asc) with a butterfly reduction and
 // pop it from its owner. Lane j < k of the group ends with the j-th choice.
+//
+// Rank-limited variant (LIMIT): "Expert Parallelism & All-to-All"
+// (neelmishra.github.io), "The bandwidth bill" - node-limited routing keeps a
+// token's experts on a few nodes; "Expert parallelism vs tensor parallelism for
+// MoE" (fanout.sh), "Expert parallelism pays in all-to-all dispatch" - at most
+// 4 nodes per token in DeepSeek-V3. Rank p owns experts [p E/P, (p+1) E/P); a
+// rank's score is its best expert score; the M best ranks (lower index on a
+// tie) are allowed and the top k is taken over their experts only. Pass 1 sums
+// the scores, keeps them (in lsum, or where they already are) and folds each
+// into its rank's best with an order-preserving integer max in LDS; pass 2
+// ranks the P ranks; pass 3 is the plain top-k over the allowed experts.
 // ---------------------------------------------------------------------------
+constexpr int kMaxLimitRanks = 64;  // P limit of the rank-limited variant (one 64-bit mask)
+
 __device__ inline bool better(float v, int e, float ov, int oe) {
   return v > ov || (v == ov && e < oe);
 }
 
-template <int L, int KMAX, bool HIST>
-__global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ part, int S,
-                                                     const float* __restrict__ bias, int64_t T, int E,
-                                                     int k, float* __restrict__ logits_out,
+// Monotone map of a float (not NaN) to uint32: a < b  <=>  key(a) < key(b).
+__device__ inline uint32_t order_key(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int KMAX>
+__device__ inline void insert_sorted(float (&lv)[KMAX], int (&li)[KMAX], float v, int ei) {
+  bool ins = false;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const bool take = ins || better(v, ei, lv[j], li[j]);
+    if (take) {
+      const float tv = lv[j];
+      const int te = li[j];
+      lv[j] = v;
+      li[j] = ei;
+      v = tv;
+      ei = te;
+    }
+    ins = ins || take;
+  }
+}
+
+template <int L, int KMAX, bool HIST, bool LIMIT>
+__global__ __launch_bounds__(1024) void route_kernel(const float* part, int S, const float* __restrict__ bias,
+                                                     int64_t T, int E, int k, float* logits_out,
                                                      int32_t* __restrict__ idx, float* __restrict__ w,
-                                                     int32_t* __restrict__ tile_cnt) {
+                                                     int32_t* __restrict__ tile_cnt, int P, int M,
+                                                     float* lsum, const float* lsrc) {
   constexpr int kTokensPerBlock = 1024 / L;
   static_assert(!HIST || kTokensPerBlock == kTileTokens, "one block per histogram tile");
-  extern __shared__ int hist[];
+  extern __shared__ int smem[];
+  int* hist = smem;                                                            // [E] when HIST
+  uint32_t* rbest = reinterpret_cast<uint32_t*>(smem + (HIST ? E : 0));        // [tokens][P] when LIMIT
   const int g = threadIdx.x % L;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + threadIdx.x / L;
+  const int tok = threadIdx.x / L;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + tok;
   const bool valid = t < T;
-  if (HIST) {
+  if (HIST)
     for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
-    __syncthreads();
-  }
+  if (LIMIT)
+    for (int i = threadIdx.x; i < kTokensPerBlock * P; i += blockDim.x) rbest[i] = 0u;  // below every key
+  if (HIST || LIMIT) __syncthreads();
+  const int per = LIMIT ? E / P : 1;  // experts per rank
 
   float lv[KMAX];
   int li[KMAX];
@@ -174,20 +216,49 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ p
         if (bias) v += bias[e];
         if (logits_out) logits_out[t * E + e] = v;
         v += 0.0f;  // -0.0 -> +0.0 (they compare equal anyway)
-        int ei = e;
-        bool ins = false;
+        if (LIMIT) {
+          if (lsum) lsum[t * E + e] = v;
+          atomicMax(&rbest[tok * P + e / per], order_key(v));
+        } else {
+          insert_sorted(lv, li, v, e);
+        }
+      }
+    }
+  }
+
+  if (LIMIT) {
+    __syncthreads();  // every rank's best is in LDS
+    uint64_t allowed = 0;
+    const uint32_t* rb = rbest + tok * P;
+    for (int p = g; p < P; p += L) {
+      const uint32_t kp = rb[p];
+      int pos = 0;  // ranks ahead of p: better score, or equal score and lower index
+      for (int q = 0; q < P; ++q) {
+        const uint32_t kq = rb[q];
+        pos += (kq > kp || (kq == kp && q < p)) ? 1 : 0;
+      }
+      if (pos < M) allowed |= uint64_t{1} << p;
+    }
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j) {
-          const bool take = ins || better(v, ei, lv[j], li[j]);
-          if (take) {
-            const float tv = lv[j];
-            const int te = li[j];
-            lv[j] = v;
-            li[j] = ei;
-            v = tv;
-            ei = te;
-          }
-          ins = ins || take;
+    for (int off = L / 2; off > 0; off >>= 1) {
+      const uint32_t lo = __shfl_xor(static_cast<uint32_t>(allowed), off, L);
+      const uint32_t hi = __shfl_xor(static_cast<uint32_t>(allowed >> 32), off, L);
+      allowed |= (static_cast<uint64_t>(hi) << 32) | lo;
+    }
+    if (valid) {
+      constexpr int G = 4;
+      for (int eb = g; eb < E; eb += G * L) {
+        float vv[G];
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+          const int e = eb + q * L;
+          vv[q] = e < E ? lsrc[t * E + e] : 0.f;  // written by this lane in pass 1, or an input
+        }
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+          const int e = eb + q * L;
+          if (e >= E) break;
+          if ((allowed >> (e / per)) & 1u) insert_sorted(lv, li, vv[q] + 0.0f, e);
         }
       }
     }
@@ -239,14 +310,41 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* __restrict__ p
   }
 }
 
-template <int L, int KMAX, bool HIST>
-hipError_t route_launch(const float* part, int S, const float* bias, int64_t T, int E, int k,
-                        float* logits_out, int32_t* idx, float* w, int32_t* tile_cnt, hipStream_t s) {
+struct RouteArgs {
+  const float* part;
+  int S;
+  const float* bias;
+  int64_t T;
+  int E, k;
+  float* logits_out;
+  int32_t* idx;
+  float* w;
+  int32_t* tile_cnt;
+  int P, M;
+  float* lsum;
+  const float* lsrc;
+};
+
+template <int L, int KMAX, bool HIST, bool LIMIT>
+hipError_t route_launch(const RouteArgs& a, hipStream_t s) {
   const int64_t tpb = 1024 / L;
-  route_kernel<L, KMAX, HIST><<<dim3(static_cast<unsigned>(ceil_div(T, tpb))), dim3(1024),
-                                HIST ? E * sizeof(int) : 0, s>>>(part, S, bias, T, E, k, logits_out, idx, w,
-                                                                 tile_cnt);
+  const size_t lds = (HIST ? a.E * sizeof(int) : 0) + (LIMIT ? tpb * a.P * sizeof(uint32_t) : 0);
+  route_kernel<L, KMAX, HIST, LIMIT><<<dim3(static_cast<unsigned>(ceil_div(a.T, tpb))), dim3(1024), lds, s>>>(
+      a.part, a.S, a.bias, a.T, a.E, a.k, a.logits_out, a.idx, a.w, a.tile_cnt, a.P, a.M, a.lsum, a.lsrc);
   return hipGetLastError();
+}
+
+template <bool LIMIT>
+hipError_t route_dispatch(const RouteArgs& a, hipStream_t s) {
+  if (a.tile_cnt) {
+    if (a.k <= 2) return route_launch<16, 2, true, LIMIT>(a, s);
+    if (a.k <= 8) return route_launch<16, 8, true, LIMIT>(a, s);
+    return route_launch<16, 16, true, LIMIT>(a, s);
+  }
+  if (a.k <= 2) return route_launch<16, 2, false, LIMIT>(a, s);
+  if (a.k <= 8) return route_launch<16, 8, false, LIMIT>(a, s);
+  if (a.k <= 16) return route_launch<16, 16, false, LIMIT>(a, s);
+  return route_launch<32, 32, false, LIMIT>(a, s);
 }
 
 }  // namespace
@@ -286,19 +384,27 @@ hipError_t launch_router_logits(const void* x, const void* wr, int64_t T, int64_
 
 bool route_builds_histogram(int k) { return k <= 16; }
 
+bool route_rank_limited(int P, int M) { return M > 0 && M < P; }
+
 hipError_t launch_route(const float* part, int S, const float* bias, int64_t T, int E, int k,
-                        float* logits_out, int32_t* idx, float* w, int32_t* tile_cnt, hipStream_t s) {
+                        float* logits_out, int32_t* idx, float* w, int32_t* tile_cnt, int P, int M,
+                        hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (tile_cnt && !route_builds_histogram(k)) return hipErrorInvalidValue;
-  if (tile_cnt) {
-    if (k <= 2) return route_launch<16, 2, true>(part, S, bias, T, E, k, logits_out, idx, w, tile_cnt, s);
-    if (k <= 8) return route_launch<16, 8, true>(part, S, bias, T, E, k, logits_out, idx, w, tile_cnt, s);
-    return route_launch<16, 16, true>(part, S, bias, T, E, k, logits_out, idx, w, tile_cnt, s);
+  RouteArgs a{part, S, bias, T, E, k, logits_out, idx, w, tile_cnt, P, M, nullptr, nullptr};
+  if (!route_rank_limited(P, M)) return route_dispatch<false>(a, s);
+  if (P > kMaxLimitRanks || E % P || static_cast<int64_t>(M) * (E / P) < k) return hipErrorInvalidValue;
+  // Where pass 3 finds the summed scores: logits_out when asked for, the single
+  // unbiased slice itself, else written back over slice 0 (workspace).
+  if (logits_out) {
+    a.lsrc = logits_out;
+  } else if (S == 1 && !bias) {
+    a.lsrc = part;
+  } else {
+    a.lsum = const_cast<float*>(part);
+    a.lsrc = part;
   }
-  if (k <= 2) return route_launch<16, 2, false>(part, S, bias, T, E, k, logits_out, idx, w, nullptr, s);
-  if (k <= 8) return route_launch<16, 8, false>(part, S, bias, T, E, k, logits_out, idx, w, nullptr, s);
-  if (k <= 16) return route_launch<16, 16, false>(part, S, bias, T, E, k, logits_out, idx, w, nullptr, s);
-  return route_launch<32, 32, false>(part, S, bias, T, E, k, logits_out, idx, w, nullptr, s);
+  return route_dispatch<true>(a, s);
 }
 
 }  // namespace moe

@@ -68,7 +68,7 @@ FAKE = 1 << 40   # a non-NULL address that is never dereferenced: every call bel
 
 def _layer(**kw):
     a = dict(x=FAKE, W_router=FAKE, router_bias=None, W_gate=FAKE, W_up=FAKE, W_down=FAKE, T=64, d=128, d_ff=256,
-             E=8, k=2, cf=1.25, P=1, dtype="bf16", out=FAKE * 2, stats=None, workspace=FAKE * 3,
+             E=8, k=2, cf=1.25, P=1, max_ranks=0, dtype="bf16", out=FAKE * 2, stats=None, workspace=FAKE * 3,
              workspace_bytes=1 << 40, stream=None)
     a.update(kw)
     return moe.moe_layer_forward(**a)
@@ -87,6 +87,9 @@ def _layer(**kw):
     (dict(T=1 << 30, k=2), moe.MOE_ERR_UNSUPPORTED),
     (dict(workspace=None), moe.MOE_ERR_WORKSPACE), (dict(workspace_bytes=100), moe.MOE_ERR_WORKSPACE),
     (dict(workspace=FAKE * 3 + 8), moe.MOE_ERR_WORKSPACE),
+    (dict(max_ranks=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(E=8, k=4, P=4, max_ranks=1), moe.MOE_ERR_INVALID_ARG),         # one rank holds 2 < k experts
+    (dict(E=256, k=8, P=128, max_ranks=4), moe.MOE_ERR_UNSUPPORTED),     # limit needs P <= 64
 ])
 def test_layer_rejects_bad_arguments_before_any_gpu_call(kw, status):
     with pytest.raises(moe.MoeError) as ei:
@@ -97,18 +100,22 @@ def test_layer_rejects_bad_arguments_before_any_gpu_call(kw, status):
 
 def test_zero_tokens_returns_ok_without_launching():
     _layer(T=0, workspace=None, workspace_bytes=0)
-    moe.moe_route(FAKE, 0, 8, 2, FAKE, FAKE)
-    moe.moe_router(FAKE, FAKE, None, 0, 128, 8, 2, "bf16", FAKE, FAKE, None, None, 0)
+    moe.moe_route(FAKE, 0, 8, 2, 1, 0, FAKE, FAKE)
+    moe.moe_router(FAKE, FAKE, None, 0, 128, 8, 2, 1, 0, "bf16", FAKE, FAKE, None, None, 0)
     assert moe.moe_router_workspace_size(64, 7168, 256, "bf16") >= 64 * 256 * 4
     moe.moe_permute(FAKE, FAKE, 0, 128, 8, 2, 20, 1, "bf16", FAKE, FAKE, None, FAKE, FAKE, None, None, None, 0)
     moe.moe_combine(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 128, 8, 2, 20, "bf16", FAKE * 2)
 
 
 @pytest.mark.parametrize("call", [
-    lambda: moe.moe_route(None, 4, 8, 2, FAKE, FAKE),
-    lambda: moe.moe_route(FAKE, 4, 8, 9, FAKE, FAKE),
-    lambda: moe.moe_router(FAKE, FAKE, None, 4, 12, 8, 2, "bf16", FAKE, FAKE, None, None, 0),
-    lambda: moe.moe_router(FAKE, FAKE, None, 4, 128, 8, 2, "bf16", FAKE, FAKE, None, None, 0),
+    lambda: moe.moe_route(None, 4, 8, 2, 1, 0, FAKE, FAKE),
+    lambda: moe.moe_route(FAKE, 4, 8, 9, 1, 0, FAKE, FAKE),
+    lambda: moe.moe_route(FAKE, 4, 8, 2, 3, 0, FAKE, FAKE),
+    lambda: moe.moe_route(FAKE, 4, 8, 4, 4, 1, FAKE, FAKE),
+    lambda: moe.moe_route(FAKE, 4, 8, 2, 2, -1, FAKE, FAKE),
+    lambda: moe.moe_router(FAKE, FAKE, None, 4, 128, 8, 4, 4, 1, "bf16", FAKE, FAKE, None, None, 0),
+    lambda: moe.moe_router(FAKE, FAKE, None, 4, 12, 8, 2, 1, 0, "bf16", FAKE, FAKE, None, None, 0),
+    lambda: moe.moe_router(FAKE, FAKE, None, 4, 128, 8, 2, 1, 0, "bf16", FAKE, FAKE, None, None, 0),
     lambda: moe.moe_permute(FAKE, FAKE, 4, 128, 8, 2, 0, 1, "bf16", FAKE, FAKE, None, FAKE, FAKE, None, None,
                             FAKE * 3, 1 << 30),
     lambda: moe.moe_permute(FAKE, FAKE, 4, 128, 8, 2, 4, 3, "bf16", FAKE, FAKE, None, FAKE, FAKE, None, None,

@@ -31,7 +31,7 @@ def _gpu():
 def run_layer(wl, wg, wu, wd, want_buckets=True):
     b = None if wl.bias_vec is None else torch.from_numpy(wl.bias_vec).cuda()
     r = moe.forward(to_dev(wl.x, wl.dtype), to_dev(wl.wr, wl.dtype), wg, wu, wd, wl.k, wl.cf, P=wl.P,
-                    router_bias=b, want_buckets=want_buckets, want_src=True)
+                    router_bias=b, want_buckets=want_buckets, want_src=True, max_ranks=wl.max_ranks)
     torch.cuda.synchronize()
     return r
 
@@ -88,6 +88,11 @@ SMALL = [
     dict(T=40, d=64, E=1, k=1, d_ff=64, cf=1.0),
     dict(T=500, d=64, E=4, k=1, d_ff=64, cf=0.1, bias="hot0"),
     dict(T=200, d=72, E=64, k=6, d_ff=40, cf=2.0),
+    # rank-limited routing: each token's experts on at most max_ranks of the P ranks
+    dict(T=300, d=256, E=32, k=4, d_ff=96, cf=1.0, P=8, max_ranks=2),
+    dict(T=130, d=1024, E=64, k=6, d_ff=72, cf=1.25, P=8, max_ranks=1, bias="zipf1.2"),
+    dict(T=64, d=128, E=8, k=2, d_ff=64, cf=1.25, P=4, max_ranks=1, dtype="f32", x_std=1 / np.sqrt(128),
+         wr_std=1 / np.sqrt(128)),
 ]
 
 
@@ -101,7 +106,7 @@ def test_layer_small_shapes_every_element(case):
     dw = tuple(to_dev(a, wl.dtype) for a in hw)
     r = run_layer(wl, *dw)
     ref = oracle.layer_forward(wl.x, wl.wr, lambda e: (hw[0][e], hw[1][e], hw[2][e]), wl.T, wl.d, wl.d_ff,
-                               wl.E, wl.k, wl.cf, wl.dtype, P=wl.P, bias=wl.bias_vec)
+                               wl.E, wl.k, wl.cf, wl.dtype, P=wl.P, bias=wl.bias_vec, max_ranks=wl.max_ranks)
     check_routing(wl, r, ref)
     check_buckets(wl, r, ref, range(wl.E))
     check_out(wl, r, ref)
@@ -134,28 +139,32 @@ def _sample_tokens(wl, ref_slot, n_rand, seed):
 
 
 WORKLOAD_SAMPLES = {"tiny_f32": None, "mixtral_prefill": 16, "deepseek_v3_prefill": 2,
-                    "deepseek_v3_decode": 6, "zipf_skew_drops": 16}
+                    "deepseek_v3_node_limited": 2, "deepseek_v3_decode": 6, "zipf_skew_drops": 16}
 
 
 @pytest.mark.parametrize("name", list(WORKLOAD_SAMPLES))
 def test_named_workload(name):
     wl = moe_inputs.workload(name)
     say(f"workload {name}: T={wl.T} d={wl.d} E={wl.E} k={wl.k} d_ff={wl.d_ff} cf={wl.cf} P={wl.P} "
-        f"{wl.dtype} (resampled {wl.resampled} near-tied tokens)")
+        f"max_ranks={wl.max_ranks} {wl.dtype} (resampled {wl.resampled} near-tied tokens)")
     host, dev = DeviceWeights.get(wl)
     r = run_layer(wl, *dev)
     # routing, slots and statistics for every token (cheap in the oracle)
     ref_route = oracle.layer_forward(wl.x, wl.wr, lambda e: (host[0][e], host[1][e], host[2][e]), wl.T, wl.d,
                                      wl.d_ff, wl.E, wl.k, wl.cf, wl.dtype, P=wl.P, bias=wl.bias_vec,
-                                     tokens=np.arange(0))
+                                     tokens=np.arange(0), max_ranks=wl.max_ranks)
     n = WORKLOAD_SAMPLES[name]
     tokens = None if n is None else _sample_tokens(wl, ref_route["slot"], n, seed=wl.seed)
     ref = oracle.layer_forward(wl.x, wl.wr, lambda e: (host[0][e], host[1][e], host[2][e]), wl.T, wl.d, wl.d_ff,
-                               wl.E, wl.k, wl.cf, wl.dtype, P=wl.P, bias=wl.bias_vec, tokens=tokens)
+                               wl.E, wl.k, wl.cf, wl.dtype, P=wl.P, bias=wl.bias_vec, tokens=tokens,
+                               max_ranks=wl.max_ranks)
     check_routing(wl, r, ref)
     rng = np.random.default_rng(3)
     check_buckets(wl, r, ref, sorted(set(rng.choice(wl.E, size=min(8, wl.E), replace=False).tolist())))
     check_out(wl, r, ref)
+    if wl.max_ranks:
+        ranks = r["topk_idx"].cpu().numpy() // (wl.E // wl.P)
+        assert max(len(set(row)) for row in ranks.tolist()) <= wl.max_ranks
     st = ref["stats"]
     say(f"  dropped {st['dropped']} fully {st['fully_dropped_tokens']} padded {st['padded_rows']} "
         f"offrank MiB {st['offrank_bytes'] / 2**20:.1f}")

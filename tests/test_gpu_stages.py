@@ -40,9 +40,17 @@ ROUTE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("T,E,k,kind", ROUTE_CASES)
-def test_route_given_logits_is_exact(T, E, k, kind):
-    say(f"route T={T} E={E} k={k} {kind}")
+# rank-limited routing (T, E, k, kind, P, M): ties within and across ranks, the
+# P <= 64 edge, one rank (M = 1), exactly k experts in the allowed ranks, and
+# the 32-lane path (k > 16)
+LIMIT_CASES = [
+    (1000, 256, 8, "normal", 8, 4), (500, 32, 4, "ties", 8, 2), (333, 64, 6, "zeros", 16, 2),
+    (70, 12, 3, "ties", 4, 1), (257, 256, 8, "normal", 64, 3), (100, 64, 20, "ties", 4, 2),
+    (64, 16, 8, "equal", 4, 2), (129, 40, 12, "normal", 10, 3), (8192, 256, 8, "ties", 8, 4),
+]
+
+
+def _route_logits(T, E, k, kind):
     rng = np.random.default_rng(T * 31 + E * 7 + k)
     if kind == "ties":
         l = rng.integers(-3, 4, (T, E)).astype(np.float32)
@@ -52,10 +60,17 @@ def test_route_given_logits_is_exact(T, E, k, kind):
         l = np.full((T, E), 0.5, np.float32)
     else:
         l = (rng.standard_normal((T, E)) * 2).astype(np.float32)
-    idx_ref = oracle.topk_experts(l, k)
+    return l
+
+
+@pytest.mark.parametrize("T,E,k,kind,P,M", [c + (1, 0) for c in ROUTE_CASES] + LIMIT_CASES)
+def test_route_given_logits_is_exact(T, E, k, kind, P, M):
+    say(f"route T={T} E={E} k={k} {kind} P={P} max_ranks={M}")
+    l = _route_logits(T, E, k, kind)
+    idx_ref = oracle.rank_limited_experts(l, k, P, M)
     w_ref = oracle.gate_weights(l, idx_ref)
     idx, w = _i32(T, k), _f32(T, k)
-    moe.moe_route(torch.from_numpy(l).cuda(), T, E, k, idx, w)
+    moe.moe_route(torch.from_numpy(l).cuda(), T, E, k, P, M, idx, w)
     torch.cuda.synchronize()
     assert np.array_equal(idx.cpu().numpy(), idx_ref)
     # both sides evaluate the softmax in fp64 and round once: at most 1 ulp apart
@@ -67,27 +82,41 @@ ROUTER_CASES = [
     (100, 128, 8, 2, "f32", None), (65, 72, 20, 3, "bf16", None), (1, 4096, 8, 2, "bf16", None),
     (64, 7168, 256, 8, "bf16", None), (40, 2048, 64, 20, "bf16", "zipf1.2"), (4100, 4096, 8, 2, "bf16", None),
 ]
+# rank-limited: (T, d, E, k, dtype, bias, P, M, logits wanted); without logits_out
+# and with several d-slices or a bias the summed scores go back over slice 0
+ROUTER_LIMIT_CASES = [
+    (300, 1024, 256, 8, "bf16", None, 8, 4, False), (200, 1024, 64, 6, "bf16", "zipf1.2", 8, 2, False),
+    (100, 128, 8, 2, "f32", None, 4, 1, True), (64, 7168, 256, 8, "bf16", None, 8, 4, True),
+    (40, 2048, 64, 20, "bf16", "zipf1.2", 4, 2, True), (1030, 512, 32, 4, "bf16", None, 8, 1, False),
+]
 
 
-@pytest.mark.parametrize("T,d,E,k,dtype,bias", ROUTER_CASES)
-def test_router_scores_choice_and_gates(T, d, E, k, dtype, bias):
-    say(f"router T={T} d={d} E={E} k={k} {dtype} bias={bias}")
+@pytest.mark.parametrize("T,d,E,k,dtype,bias,P,M,want_logits",
+                         [c + (1, 0, True) for c in ROUTER_CASES] + ROUTER_LIMIT_CASES)
+def test_router_scores_choice_and_gates(T, d, E, k, dtype, bias, P, M, want_logits):
+    say(f"router T={T} d={d} E={E} k={k} {dtype} bias={bias} P={P} max_ranks={M}")
     std = (1 / np.sqrt(d)) if dtype == "f32" else 1.0
     wl = moe_inputs.custom(T=T, d=d, E=E, k=k, d_ff=8, cf=1.0, dtype=dtype, seed=T + d + E,
-                           x_std=std, wr_std=(1 / np.sqrt(d)) if dtype == "f32" else 0.02, bias=bias)
+                           x_std=std, wr_std=(1 / np.sqrt(d)) if dtype == "f32" else 0.02, bias=bias,
+                           P=P, max_ranks=M)
     x64, wr64 = oracle.decode(wl.x, dtype), oracle.decode(wl.wr, dtype)
     l_ref = oracle.router_logits(x64, wr64, wl.bias_vec)
-    idx_ref = oracle.topk_experts(l_ref, k)
+    idx_ref = oracle.rank_limited_experts(l_ref, k, P, M)
     w_ref = oracle.gate_weights(l_ref, idx_ref)
     logits, idx, w = _f32(T, E), _i32(T, k), _f32(T, k)
     b = None if wl.bias_vec is None else torch.from_numpy(wl.bias_vec).cuda()
     ws_n = moe.moe_router_workspace_size(T, d, E, dtype)
     ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
-    moe.moe_router(to_dev(wl.x, dtype), to_dev(wl.wr, dtype), b, T, d, E, k, dtype, idx, w, logits, ws, ws_n)
+    moe.moe_router(to_dev(wl.x, dtype), to_dev(wl.wr, dtype), b, T, d, E, k, P, M, dtype, idx, w,
+                   logits if want_logits else None, ws, ws_n)
     torch.cuda.synchronize()
     tol = logits_tolerance(x64, wr64, wl.bias_vec)
-    err = np.abs(logits.cpu().numpy().astype(np.float64) - l_ref)
-    assert np.all(err <= tol), f"max err/tol {np.max(err / tol)}"
+    if want_logits:
+        err = np.abs(logits.cpu().numpy().astype(np.float64) - l_ref)
+        assert np.all(err <= tol), f"max err/tol {np.max(err / tol)}"
+    if M:
+        ranks = idx.cpu().numpy() // (E // P)
+        assert max(len(set(r)) for r in ranks.tolist()) <= M
     assert np.array_equal(idx.cpu().numpy(), idx_ref)
     # softmax sensitivity: |dw_j| <= 2 w_j max|dl|, plus one rounding
     wtol = w_ref.astype(np.float64) * (2 * tol.max(axis=1, keepdims=True) + 2 * U)
@@ -251,7 +280,7 @@ def test_combine_inverse_and_passthrough(T, d, E, k, cf, dtype):
 
 
 def test_zero_tokens_is_a_no_op():
-    moe.moe_route(torch.zeros(1, device="cuda"), 0, 8, 2, _i32(1), _f32(1))
+    moe.moe_route(torch.zeros(1, device="cuda"), 0, 8, 2, 1, 0, _i32(1), _f32(1))
     out = torch.full((4,), 3.0, device="cuda")
     moe.moe_combine(out, out, _i32(1), _f32(1), _i32(1), 0, 4, 8, 2, 1, "f32", out)
     torch.cuda.synchronize()
