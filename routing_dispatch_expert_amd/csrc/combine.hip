@@ -16,9 +16,11 @@
 namespace moe {
 namespace {
 
-// One wave per token; lanes walk the row in 16-byte words (8 bf16 or 4 fp32
-// values), U words in flight. The token's slots, experts and gates are
-// wave-uniform scalar loads.
+// One wave per token (WPT waves for short batches); lanes walk the row in
+// 16-byte words (8 bf16 or 4 fp32 values), U words per lane at a time. The
+// token's copies are taken JB at a time: their slots, experts and gates are
+// wave-uniform scalar loads, the words of every kept copy of the batch are in
+// flight before any arithmetic, and the sum runs in ascending j.
 template <bool BF16, int WPT>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ x,
                                                       const uint4* __restrict__ y,
@@ -27,8 +29,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
                                                       const int32_t* __restrict__ slot, int64_t T, int k,
                                                       int64_t C, int64_t V, uint4* __restrict__ out) {
   constexpr int U = 4;
+  constexpr int JB = 2;                  // copies whose words are in flight together
   constexpr int NE = BF16 ? 8 : 4;
-  constexpr int LANES = 64 * WPT;  // threads sharing one token
+  constexpr int LANES = 64 * WPT;        // threads sharing one token
   const int64_t t = static_cast<int64_t>(blockIdx.x) * (4 / WPT) + threadIdx.x / LANES;
   if (t >= T) return;
   const int lane = threadIdx.x % LANES;
@@ -59,24 +62,45 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int q = 0; q < NE; ++q) acc[u][q] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int sl = __builtin_amdgcn_readfirstlane(st[j]);
-      if (sl < 0) continue;
-      const float wj = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wt[j])));
-      const uint4* src = y + (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(it[j])) * C + sl) * V;
+    for (int j0 = 0; j0 < k; j0 += JB) {
+      int sl[JB];
+      float wj[JB];
+      const uint4* src[JB];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t v = v0 + LANES * u;
-        if (v >= V) continue;
-        const uint4 yv = src[v];
-        const uint32_t yw[4] = {yv.x, yv.y, yv.z, yv.w};
+      for (int jb = 0; jb < JB; ++jb) {
+        const int j = j0 + jb;
+        sl[jb] = j < k ? __builtin_amdgcn_readfirstlane(st[j]) : -1;
+        wj[jb] = 0.f;
+        src[jb] = y;
+        if (sl[jb] >= 0) {
+          wj[jb] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wt[j])));
+          src[jb] = y + (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(it[j])) * C + sl[jb]) * V;
+        }
+      }
+      uint4 yv[JB][U];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (BF16) {
-            acc[u][2 * q] = fmaf(wj, __uint_as_float(yw[q] << 16), acc[u][2 * q]);
-            acc[u][2 * q + 1] = fmaf(wj, __uint_as_float(yw[q] & 0xffff0000u), acc[u][2 * q + 1]);
-          } else {
-            acc[u][q] = fmaf(wj, __uint_as_float(yw[q]), acc[u][q]);
+      for (int jb = 0; jb < JB; ++jb) {
+        if (sl[jb] < 0) continue;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t v = v0 + LANES * u;
+          if (v < V) yv[jb][u] = src[jb][v];
+        }
+      }
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) {
+        if (sl[jb] < 0) continue;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t yw[4] = {yv[jb][u].x, yv[jb][u].y, yv[jb][u].z, yv[jb][u].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (BF16) {
+              acc[u][2 * q] = fmaf(wj[jb], __uint_as_float(yw[q] << 16), acc[u][2 * q]);
+              acc[u][2 * q + 1] = fmaf(wj[jb], __uint_as_float(yw[q] & 0xffff0000u), acc[u][2 * q + 1]);
+            } else {
+              acc[u][q] = fmaf(wj[jb], __uint_as_float(yw[q]), acc[u][q]);
+            }
           }
         }
       }
