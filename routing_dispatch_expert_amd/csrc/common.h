@@ -26,12 +26,9 @@ inline int row_waves_per_token(int64_t T) { return T >= 1024 ? 1 : (T >= 256 ? 2
 
 __device__ inline float bf16_to_f32(bf16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
-// fp32 -> bf16, round to nearest even (NaN stays NaN).
+// fp32 -> bf16, round to nearest even (NaN stays NaN): one v_cvt_pk_bf16_f32.
 __device__ inline bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
 // 16-byte store marked non-temporal: rows streamed out once (bucket scatter,

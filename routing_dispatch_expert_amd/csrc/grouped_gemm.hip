@@ -36,6 +36,12 @@ __device__ inline int owner_expert(const int32_t* __restrict__ mtile_off, int E,
 
 __device__ inline float silu(float g) { return g / (1.0f + expf(-g)); }
 
+// silu for results rounded to bf16 next: hardware 2^x and reciprocal (each
+// within about 1 ulp of fp32), far below the 2^-9 of the bf16 rounding.
+__device__ inline float silu_bf16(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+}
+
 // ---------------------------------------------------------------------------
 // bf16 matrix-core GEMM, one BM x BN block of A B^T per work-group of 4 waves
 // (2 x 2). Each wave owns a (BM/2) x (BN/2) block as TM x TN tiles of
@@ -279,7 +285,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BM >= 25
 #pragma unroll
         for (int j = 0; j < TN / 2; ++j) {
           const int64_t col = n0 + wn * (BN / 4) + j * 32 + lr;
-          if (col < N) oute[row * N + col] = f32_to_bf16(silu(acc[i][j][q]) * acc[i][j + TN / 2][q]);
+          if (col < N) oute[row * N + col] = f32_to_bf16(silu_bf16(acc[i][j][q]) * acc[i][j + TN / 2][q]);
         }
       } else {
 #pragma unroll
@@ -455,27 +461,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   stage(T_{}, As0, Bs0, As1, Bs1, k);
   stage(F_{}, As1, Bs1, As0, Bs0, k + 1);
 
+  // Epilogue through LDS: the stage buffers are free now. Each wave converts
+  // its 128-row result to bf16 into a 32 KiB buffer of its own (rows padded by
+  // 16 bytes so the two half-waves, four rows apart, write different banks),
+  // then stores whole 16-byte row chunks, so every global store is coalesced.
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();  // every wave is done with the stage buffers
+  constexpr int OC = SWIGLU ? BN / 4 : BN / 2;  // output columns per wave (64 or 128)
+  constexpr int RS = OC * 2 + 16;               // LDS row stride, bytes
+  constexpr int HR = SWIGLU ? 128 : 64;         // rows staged per pass (fits 32 KiB)
+  constexpr int CPR = OC / 8;                   // 16-byte chunks per row
+  static_assert(HR * RS <= BM * CH * 16, "staging fits one stage buffer");
+  char* eb = reinterpret_cast<char*>(wave == 0 ? As0 : wave == 1 ? As1 : wave == 2 ? Bs0 : Bs1);
   bf16_t* oute = out + static_cast<int64_t>(e) * C * N;
+  const int row0 = m0 + wm * (BM / 2);
+  const int64_t col0 = n0 + wn * OC;
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  for (int pass = 0; pass < (BM / 2) / HR; ++pass) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int row = m0 + wm * (BM / 2) + i * 32 + 8 * (q >> 2) + 4 * lk + (q & 3);
-      if (row >= rows) continue;
-      if (SWIGLU) {
+    for (int ii = 0; ii < HR / 32; ++ii) {
+      const int i = pass * (HR / 32) + ii;
 #pragma unroll
-        for (int j = 0; j < TN / 2; ++j) {
-          const int64_t col = n0 + wn * (BN / 4) + j * 32 + lr;
-          if (col < N) oute[row * N + col] = f32_to_bf16(silu(acc[i][j][q]) * acc[i][j + TN / 2][q]);
-        }
-      } else {
+      for (int q = 0; q < 16; ++q) {
+        const int r = ii * 32 + 8 * (q >> 2) + 4 * lk + (q & 3);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int64_t col = n0 + wn * (BN / 2) + j * 32 + lr;
-          if (col < N) oute[row * N + col] = f32_to_bf16(acc[i][j][q]);
+        for (int j = 0; j < OC / 32; ++j) {
+          const float v = SWIGLU ? silu_bf16(acc[i][j][q]) * acc[i][j + TN / 2][q] : acc[i][j][q];
+          *reinterpret_cast<bf16_t*>(eb + r * RS + (j * 32 + lr) * 2) = f32_to_bf16(v);
         }
       }
     }
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+#pragma unroll
+    for (int c = lane; c < HR * CPR; c += 64) {
+      const int r = c / CPR, ch = c % CPR;
+      const int grow = row0 + pass * HR + r;
+      const int64_t gcol = col0 + ch * 8;
+      const uint4 v = *reinterpret_cast<const uint4*>(eb + r * RS + ch * 16);
+      if (grow < rows && gcol < N) *reinterpret_cast<uint4*>(oute + grow * N + gcol) = v;
+    }
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // reads done before reuse
   }
 }
 
@@ -548,7 +573,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_skinny_kernel(
   for (int r = 0; r < 4; ++r) {
     const int row = m0 + 4 * (lane >> 4) + r;
     if (row < rows)
-      oute[row * N + col] = f32_to_bf16(SWIGLU ? silu(acc0[r]) * acc1[r] : acc0[r]);
+      oute[row * N + col] = f32_to_bf16(SWIGLU ? silu_bf16(acc0[r]) * acc1[r] : acc0[r]);
   }
 }
 
