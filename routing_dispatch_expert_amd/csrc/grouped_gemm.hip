@@ -102,6 +102,53 @@ __device__ inline uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 // Scheduling hints: instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
 
+// Epilogue of one wave's (32 TM) x (32 TN) accumulator block (v_mfma 32x32
+// layout: element q of lane l is row 8 (q / 4) + 4 (l / 32) + q % 4, column
+// l % 32 of its tile), staged through `cap` bytes of LDS that no other wave
+// touches: the results are rounded to bf16 into padded rows (16 extra bytes,
+// so the two half-waves, four rows apart, write different banks), then whole
+// 16-byte row chunks are stored, so every global store is coalesced. With
+// SWIGLU the tiles j < TN/2 hold gate and j + TN/2 the matching up values, and
+// silu(gate) * up is stored. Rows >= rows and columns >= N are not written
+// (N % 8 == 0).
+template <int TM, int TN, bool SWIGLU, int CAP>
+__device__ inline void store_wave_tile(const f32x16 (&acc)[TM][TN], char* eb, bf16_t* __restrict__ out,
+                                       int row0, int rows, int64_t col0, int64_t N, int lane) {
+  constexpr int WR = TM * 32;                        // rows of the wave's block
+  constexpr int OC = SWIGLU ? TN * 16 : TN * 32;     // output columns of the wave's block
+  constexpr int RS = OC * 2 + 16;                    // LDS row stride, bytes
+  constexpr int HR = WR * RS <= CAP ? WR : WR / 2;   // rows staged per pass
+  constexpr int CPR = OC / 8;                        // 16-byte chunks per row
+  static_assert(HR * RS <= CAP, "staging rows fit the LDS slice");
+  const int lr = lane & 31, lk = lane >> 5;
+#pragma unroll
+  for (int pass = 0; pass < WR / HR; ++pass) {
+#pragma unroll
+    for (int ii = 0; ii < HR / 32; ++ii) {
+      const int i = pass * (HR / 32) + ii;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int r = ii * 32 + 8 * (q >> 2) + 4 * lk + (q & 3);
+#pragma unroll
+        for (int j = 0; j < OC / 32; ++j) {
+          const float v = SWIGLU ? silu_bf16(acc[i][j][q]) * acc[i][j + TN / 2][q] : acc[i][j][q];
+          *reinterpret_cast<bf16_t*>(eb + r * RS + (j * 32 + lr) * 2) = f32_to_bf16(v);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0): rows staged
+#pragma unroll
+    for (int c = lane; c < HR * CPR; c += 64) {
+      const int r = c / CPR, ch = c % CPR;
+      const int grow = row0 + pass * HR + r;
+      const int64_t gcol = col0 + ch * 8;
+      const uint4 v = *reinterpret_cast<const uint4*>(eb + r * RS + ch * 16);
+      if (grow < rows && gcol < N) *reinterpret_cast<uint4*>(out + grow * N + gcol) = v;
+    }
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // reads done before reuse
+  }
+}
+
 template <int BM, int BN, bool SWIGLU>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BM >= 256 ? 1 : 2))) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
@@ -274,28 +321,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BM >= 25
   if (kt + 1 < nk) stage(kt++, true, false);
   stage(kt, false, false);
 
-  bf16_t* oute = out + static_cast<int64_t>(e) * C * N;
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int row = m0 + wm * (BM / 2) + i * 32 + 8 * (q >> 2) + 4 * lk + (q & 3);
-      if (row >= rows) continue;
-      if (SWIGLU) {
-#pragma unroll
-        for (int j = 0; j < TN / 2; ++j) {
-          const int64_t col = n0 + wn * (BN / 4) + j * 32 + lr;
-          if (col < N) oute[row * N + col] = f32_to_bf16(silu_bf16(acc[i][j][q]) * acc[i][j + TN / 2][q]);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int64_t col = n0 + wn * (BN / 2) + j * 32 + lr;
-          if (col < N) oute[row * N + col] = f32_to_bf16(acc[i][j][q]);
-        }
-      }
-    }
-  }
+  // the stage buffers are free: one per wave for the epilogue
+  __syncthreads();
+  char* eb = reinterpret_cast<char*>(wave == 0 ? As[0] : wave == 1 ? As[1] : wave == 2 ? Bs[0] : Bs[1]);
+  store_wave_tile<TM, TN, SWIGLU, (BM < BN ? BM : BN) * 8 * 16>(
+      acc, eb, out + static_cast<int64_t>(e) * C * N, m0 + wm * (BM / 2), rows,
+      n0 + wn * (SWIGLU ? BN / 4 : BN / 2), N, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -461,47 +492,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   stage(T_{}, As0, Bs0, As1, Bs1, k);
   stage(F_{}, As1, Bs1, As0, Bs0, k + 1);
 
-  // Epilogue through LDS: the stage buffers are free now. Each wave converts
-  // its 128-row result to bf16 into a 32 KiB buffer of its own (rows padded by
-  // 16 bytes so the two half-waves, four rows apart, write different banks),
-  // then stores whole 16-byte row chunks, so every global store is coalesced.
+  // the stage buffers are free: one per wave for the epilogue
   wait_vm_lgkm0<0>();
-  __builtin_amdgcn_s_barrier();  // every wave is done with the stage buffers
-  constexpr int OC = SWIGLU ? BN / 4 : BN / 2;  // output columns per wave (64 or 128)
-  constexpr int RS = OC * 2 + 16;               // LDS row stride, bytes
-  constexpr int HR = SWIGLU ? 128 : 64;         // rows staged per pass (fits 32 KiB)
-  constexpr int CPR = OC / 8;                   // 16-byte chunks per row
-  static_assert(HR * RS <= BM * CH * 16, "staging fits one stage buffer");
+  __builtin_amdgcn_s_barrier();
   char* eb = reinterpret_cast<char*>(wave == 0 ? As0 : wave == 1 ? As1 : wave == 2 ? Bs0 : Bs1);
-  bf16_t* oute = out + static_cast<int64_t>(e) * C * N;
-  const int row0 = m0 + wm * (BM / 2);
-  const int64_t col0 = n0 + wn * OC;
-#pragma unroll
-  for (int pass = 0; pass < (BM / 2) / HR; ++pass) {
-#pragma unroll
-    for (int ii = 0; ii < HR / 32; ++ii) {
-      const int i = pass * (HR / 32) + ii;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int r = ii * 32 + 8 * (q >> 2) + 4 * lk + (q & 3);
-#pragma unroll
-        for (int j = 0; j < OC / 32; ++j) {
-          const float v = SWIGLU ? silu_bf16(acc[i][j][q]) * acc[i][j + TN / 2][q] : acc[i][j][q];
-          *reinterpret_cast<bf16_t*>(eb + r * RS + (j * 32 + lr) * 2) = f32_to_bf16(v);
-        }
-      }
-    }
-    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
-#pragma unroll
-    for (int c = lane; c < HR * CPR; c += 64) {
-      const int r = c / CPR, ch = c % CPR;
-      const int grow = row0 + pass * HR + r;
-      const int64_t gcol = col0 + ch * 8;
-      const uint4 v = *reinterpret_cast<const uint4*>(eb + r * RS + ch * 16);
-      if (grow < rows && gcol < N) *reinterpret_cast<uint4*>(oute + grow * N + gcol) = v;
-    }
-    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // reads done before reuse
-  }
+  store_wave_tile<TM, TN, SWIGLU, BM * CH * 16>(acc, eb, out + static_cast<int64_t>(e) * C * N,
+                                                 m0 + wm * (BM / 2), rows, n0 + wn * (SWIGLU ? BN / 4 : BN / 2),
+                                                 N, lane);
 }
 
 // ---------------------------------------------------------------------------
