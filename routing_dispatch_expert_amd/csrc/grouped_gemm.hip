@@ -542,12 +542,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_skinny_kernel(
   int64_t ks = 0;
   for (; ks + U <= nk; ks += U) {
     bf16x8 a[U], b0[U], b1[U];
+    // one matrix at a time: consecutive loads of a lane fall in the same
+    // 128-byte lines (4 lanes x 16 bytes per step of 32), so each weight line
+    // is requested by back-to-back loads
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      b0[u] = *reinterpret_cast<const bf16x8*>(b0p + (ks + u) * 32);
-      if (SWIGLU) b1[u] = *reinterpret_cast<const bf16x8*>(b1p + (ks + u) * 32);
-      a[u] = a_in ? *reinterpret_cast<const bf16x8*>(ap + (ks + u) * 32) : bf16x8{};
+    for (int u = 0; u < U; ++u) b0[u] = *reinterpret_cast<const bf16x8*>(b0p + (ks + u) * 32);
+    if (SWIGLU) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) b1[u] = *reinterpret_cast<const bf16x8*>(b1p + (ks + u) * 32);
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) a[u] = a_in ? *reinterpret_cast<const bf16x8*>(ap + (ks + u) * 32) : bf16x8{};
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b0[u], acc0, 0, 0, 0);

@@ -96,6 +96,7 @@ __global__ __launch_bounds__(1024) void scan_finalize_kernel(
     int32_t* __restrict__ send, int64_t* __restrict__ totals, int bm, int32_t* __restrict__ mtile_off) {
   __shared__ int part[16][65];
   __shared__ int kept_s[4096];
+  __shared__ int send_s[4096];  // kept rows per rank (P <= E)
   __shared__ int sh[17];
   __shared__ unsigned long long ksum;
   const int ex = threadIdx.x & 63;
@@ -103,7 +104,9 @@ __global__ __launch_bounds__(1024) void scan_finalize_kernel(
   const int64_t chunk = ceil_div(nt, 16);
   const int64_t b0 = min(nt, ly * chunk);
   const int64_t b1 = min(nt, b0 + chunk);
+  const int per = E / P;
   if (threadIdx.x == 0) ksum = 0;
+  for (int p = threadIdx.x; p < P; p += blockDim.x) send_s[p] = 0;  // ordered by the first barrier below
   for (int eb = 0; eb < E; eb += 64) {
     const int e = eb + ex;
     int sum = 0;
@@ -124,22 +127,17 @@ __global__ __launch_bounds__(1024) void scan_finalize_kernel(
         const int kv = static_cast<int>(min<int64_t>(run, C));
         kept[e] = kv;
         kept_s[e] = kv;
-        atomicAdd(&ksum, static_cast<unsigned long long>(kv));  // integer sum: order-free
+        atomicAdd(&ksum, static_cast<unsigned long long>(kv));  // integer sums: order-free
+        atomicAdd(&send_s[e / per], kv);
       }
     }
     __syncthreads();
   }
-  const int per = E / P;
   if (send)
-    for (int p = threadIdx.x; p < P; p += blockDim.x) {
-      int sp = 0;
-      for (int e = p * per; e < (p + 1) * per; ++e) sp += kept_s[e];
-      send[p] = sp;
-    }
+    for (int p = threadIdx.x; p < P; p += blockDim.x) send[p] = send_s[p];
   if (totals && threadIdx.x == 0) {
     const int64_t n_kept = static_cast<int64_t>(ksum);
-    int64_t rank0 = 0;
-    for (int e = 0; e < per; ++e) rank0 += kept_s[e];
+    const int64_t rank0 = send_s[0];
     totals[0] = T * k - n_kept;
     totals[1] = 0;  // fully dropped tokens: accumulated by the slot kernel
     totals[2] = static_cast<int64_t>(E) * C - n_kept;
