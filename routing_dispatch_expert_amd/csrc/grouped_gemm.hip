@@ -104,19 +104,23 @@ constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, 
 
 // Epilogue of one wave's (32 TM) x (32 TN) accumulator block (v_mfma 32x32
 // layout: element q of lane l is row 8 (q / 4) + 4 (l / 32) + q % 4, column
-// l % 32 of its tile), staged through `cap` bytes of LDS that no other wave
-// touches: the results are rounded to bf16 into padded rows (16 extra bytes,
-// so the two half-waves, four rows apart, write different banks), then whole
-// 16-byte row chunks are stored, so every global store is coalesced. With
+// l % 32 of its tile), staged through CAP bytes of LDS that no other wave
+// touches: the results are rounded to bf16 into rows padded by 16 bytes (or,
+// without PAD, swizzled) so the two half-waves, four rows apart, write
+// different banks; then whole 16-byte row chunks are stored, so every global
+// store is coalesced. With
 // SWIGLU the tiles j < TN/2 hold gate and j + TN/2 the matching up values, and
 // silu(gate) * up is stored. Rows >= rows and columns >= N are not written
 // (N % 8 == 0).
-template <int TM, int TN, bool SWIGLU, int CAP>
+template <int TM, int TN, bool SWIGLU, int CAP, bool PAD = true>
 __device__ inline void store_wave_tile(const f32x16 (&acc)[TM][TN], char* eb, bf16_t* __restrict__ out,
                                        int row0, int rows, int64_t col0, int64_t N, int lane) {
   constexpr int WR = TM * 32;                        // rows of the wave's block
   constexpr int OC = SWIGLU ? TN * 16 : TN * 32;     // output columns of the wave's block
-  constexpr int RS = OC * 2 + 16;                    // LDS row stride, bytes
+  constexpr int RS = OC * 2 + (PAD ? 16 : 0);        // LDS row stride, bytes
+  // without padding, rows with bit 2 of the row index set keep their 64-byte
+  // halves swapped, which separates the half-waves just as well
+  auto at = [&](int r, int byte) { return r * RS + (PAD ? byte : (byte ^ (((r >> 2) & 1) << 6))); };
   constexpr int HR = WR * RS <= CAP ? WR : WR / 2;   // rows staged per pass
   constexpr int CPR = OC / 8;                        // 16-byte chunks per row
   static_assert(HR * RS <= CAP, "staging rows fit the LDS slice");
@@ -132,7 +136,7 @@ __device__ inline void store_wave_tile(const f32x16 (&acc)[TM][TN], char* eb, bf
 #pragma unroll
         for (int j = 0; j < OC / 32; ++j) {
           const float v = SWIGLU ? silu_bf16(acc[i][j][q]) * acc[i][j + TN / 2][q] : acc[i][j][q];
-          *reinterpret_cast<bf16_t*>(eb + r * RS + (j * 32 + lr) * 2) = f32_to_bf16(v);
+          *reinterpret_cast<bf16_t*>(eb + at(r, (j * 32 + lr) * 2)) = f32_to_bf16(v);
         }
       }
     }
@@ -142,7 +146,7 @@ __device__ inline void store_wave_tile(const f32x16 (&acc)[TM][TN], char* eb, bf
       const int r = c / CPR, ch = c % CPR;
       const int grow = row0 + pass * HR + r;
       const int64_t gcol = col0 + ch * 8;
-      const uint4 v = *reinterpret_cast<const uint4*>(eb + r * RS + ch * 16);
+      const uint4 v = *reinterpret_cast<const uint4*>(eb + at(r, ch * 16));
       if (grow < rows && gcol < N) *reinterpret_cast<uint4*>(out + grow * N + gcol) = v;
     }
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // reads done before reuse
@@ -502,6 +506,155 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ---------------------------------------------------------------------------
+// 128 x 256 variant for two work-groups per CU: K in 32-wide stages (64-byte
+// LDS rows) through two slots, 48 KiB in all, so a second work-group's matrix
+// work covers this one's barriers, DMA waits and epilogue. 4 waves (2 x 2) of
+// 64 x 128, each as 2 x 4 v_mfma_f32_32x32x16_bf16 tiles. One DMA instruction
+// of a wave fills 16 rows (lane L: row L / 4, position L % 4); chunk c of row
+// r sits at position c ^ ((r / 4) % 4), so the 16 lanes of a fragment read
+// (16 consecutive rows) hit distinct banks. Needs K % 64 == 0.
+// ---------------------------------------------------------------------------
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_dma_m128_kernel(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
+    bf16_t* __restrict__ out, const int32_t* __restrict__ kept, const int32_t* __restrict__ mtile_off,
+    int E, int64_t C, int64_t K, int64_t N, int nt_count) {
+  constexpr int BM = 128, BN = 256, BK = 32, TM = 2, TN = 4;
+  constexpr int CH = BK / 8;                    // 16-byte chunks per LDS row
+  constexpr int BNO = SWIGLU ? BN / 2 : BN;
+  constexpr int A_PW = BM / 16 / 4;             // 16-row DMA blocks per wave: A (2), B (4)
+  constexpr int B_PW = BN / 16 / 4;
+  constexpr int NMFMA = TM * TN, NFRAG = TM + TN;
+  __shared__ uint4 As0[BM * CH], As1[BM * CH];
+  __shared__ uint4 Bs0[BN * CH], Bs1[BN * CH];
+
+  int e, m0, nt;
+  if (!tile_of_block<BM>(mtile_off, E, nt_count, &e, &m0, &nt)) return;
+  e = __builtin_amdgcn_readfirstlane(e);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  const int rows = __builtin_amdgcn_readfirstlane(kept[e]);
+  const int64_t n0 = static_cast<int64_t>(nt) * BNO;
+  const int64_t nk = K / BK;  // even, at least 2
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const auto ra_src = buffer_rsrc(A + static_cast<int64_t>(e) * C * K, static_cast<uint32_t>(C * K * 2));
+  // B rows 0..127 of a SwiGLU block are gate rows, 128..255 up rows: waves 0-1
+  // load the first half, waves 2-3 the second
+  const bf16_t* bbase = (SWIGLU && wave >= 2) ? B1 : B0;
+  const auto rb_src = buffer_rsrc(bbase + static_cast<int64_t>(e) * N * K, static_cast<uint32_t>(N * K * 2));
+  uint32_t a_voff[A_PW], b_voff[B_PW];
+#pragma unroll
+  for (int i = 0; i < A_PW; ++i) {
+    const int row = (wave * A_PW + i) * 16 + (lane >> 2);
+    const int ch = (lane & 3) ^ ((row >> 2) & 3);  // the chunk stored at position lane % 4
+    a_voff[i] = static_cast<uint32_t>((m0 + row) * K * 2 + ch * 16);  // rows past C read as zero
+  }
+#pragma unroll
+  for (int i = 0; i < B_PW; ++i) {
+    const int row = (wave * B_PW + i) * 16 + (lane >> 2);
+    const int ch = (lane & 3) ^ ((row >> 2) & 3);
+    const int64_t bn = n0 + (SWIGLU ? (row % (BN / 2)) : row);
+    b_voff[i] = bn < N ? static_cast<uint32_t>(bn * K * 2 + ch * 16) : 0x80000000u;
+  }
+  auto dma = [&](uint4* as, uint4* bs, int64_t ks) {  // ks: stage number
+    const uint32_t soff = static_cast<uint32_t>(ks * BK * 2);
+#pragma unroll
+    for (int i = 0; i < A_PW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_src, MOE_LDS(as + (wave * A_PW + i) * 16 * CH), 16, a_voff[i],
+                                               soff, 0, 0);
+#pragma unroll
+    for (int i = 0; i < B_PW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_src, MOE_LDS(bs + (wave * B_PW + i) * 16 * CH), 16, b_voff[i],
+                                               soff, 0, 0);
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lk = lane >> 5;
+  int a_row[TM], b_row[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) a_row[i] = (wm * (BM / 2) + i * 32 + lr) * CH;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int br = SWIGLU ? ((j < TN / 2) ? (wn * (BN / 4) + j * 32) : (BN / 2 + wn * (BN / 4) + (j - TN / 2) * 32))
+                          : (wn * (BN / 2) + j * 32);
+    b_row[j] = (br + lr) * CH;
+  }
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  bf16x8 fa[2][TM], fb[2][TN];
+  const int rsw = (lr >> 2) & 3;
+  auto fload = [&](const uint4* as, const uint4* bs, int ks, int slot) {
+    const int pc = (ks * 2 + lk) ^ rsw;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[slot][i] = *reinterpret_cast<const bf16x8*>(&as[a_row[i] + pc]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[slot][j] = *reinterpret_cast<const bf16x8*>(&bs[b_row[j] + pc]);
+  };
+  auto mfmas = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+  };
+  auto interleave = [&]() {  // 8 matrix ops with the 6 fragment reads between them
+#pragma unroll
+    for (int g = 0; g < NFRAG; ++g) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA - NFRAG, 0);
+  };
+  // Stage k in (as, bs); stage k + 1 goes to (an, bn_) unless this is the last.
+  auto stage = [&](auto has_next, const uint4* as, const uint4* bs, uint4* an, uint4* bn_, int64_t k) {
+    if constexpr (decltype(has_next)::value) dma(an, bn_, k + 1);
+    fload(as, bs, 1, 1);
+    mfmas(0);
+    interleave();
+    if constexpr (decltype(has_next)::value) {
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm_lgkm0<0>();            // own DMA of stage k + 1 landed, reads of stage k done ...
+      __builtin_amdgcn_s_barrier();  // ... and everyone else's
+      __builtin_amdgcn_sched_barrier(0);
+      fload(an, bn_, 0, 0);
+    }
+    mfmas(1);
+    interleave();
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+
+  dma(As0, Bs0, 0);
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  fload(As0, Bs0, 0, 0);
+  int64_t k = 0;
+  for (; k + 2 < nk; k += 2) {
+    stage(T_{}, As0, Bs0, As1, Bs1, k);
+    stage(T_{}, As1, Bs1, As0, Bs0, k + 1);
+  }
+  stage(T_{}, As0, Bs0, As1, Bs1, k);
+  stage(F_{}, As1, Bs1, As0, Bs0, k + 1);
+
+  // the stage buffers are free: an 8 KiB half of a B slot per wave for the epilogue
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  char* eb = reinterpret_cast<char*>(wave < 2 ? Bs0 : Bs1) + (wave & 1) * (BN * CH * 8);
+  store_wave_tile<TM, TN, SWIGLU, BN * CH * 8, false>(acc, eb, out + static_cast<int64_t>(e) * C * N,
+                                                       m0 + wm * (BM / 2), rows,
+                                                       n0 + wn * (SWIGLU ? BN / 4 : BN / 2), N, lane);
+}
+
+// ---------------------------------------------------------------------------
 // Few rows per expert (decode): the run is a stream of each touched expert's
 // weights, each element used by at most 16 rows. A work-group takes one
 // expert's rows (16 at most) and 64 output columns; each wave owns 16 columns
@@ -664,7 +817,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 // Block shape of the bf16 kernel: 256 x 256 once experts hold enough rows to
 // fill it, else 128 x 128.
-constexpr int kBigTileMinC = 512;
+#ifndef MOE_BIG_TILE_MIN_C
+#define MOE_BIG_TILE_MIN_C 512
+#endif
+constexpr int kBigTileMinC = MOE_BIG_TILE_MIN_C;
 
 // Row tiles of the skinny kernel when every expert holds this few rows.
 constexpr int kSkinnyMaxC = kSkinnyRows;
@@ -698,12 +854,17 @@ hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out,
   const auto* pb0 = static_cast<const bf16_t*>(b0);
   const auto* pb1 = static_cast<const bf16_t*>(b1);
   auto* po = static_cast<bf16_t*>(out);
-  if (BM == 256 && BN == 256 && K % 128 == 0)
+  if constexpr (BM == 128 && BN == 256) {
+    if (K % 64) return hipErrorInvalidValue;  // callers pick this tile only for K % 64 == 0
+    gemm_bf16_dma_m128_kernel<SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
+        pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt));
+  } else if (BM == 256 && BN == 256 && K % 128 == 0) {
     gemm_bf16_dma_kernel<SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
         pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt));
-  else
+  } else {
     gemm_bf16_kernel<BM, BN, SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
         pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt));
+  }
   return hipGetLastError();
 }
 
@@ -718,6 +879,8 @@ hipError_t launch_gemm_gate_up(const void* buckets, const int32_t* kept, const i
       return launch_skinny<true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, s);
     if (grouped_gemm_bm(true, C) == 256)
       return launch_bf16<256, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, s);
+    if (d % 64 == 0)
+      return launch_bf16<128, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, s);
     return launch_bf16<128, 128, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, s);
   }
   const unsigned mtiles = static_cast<unsigned>(E * ceil_div(C, 64));
@@ -736,6 +899,8 @@ hipError_t launch_gemm_down(const void* h, const int32_t* kept, const int32_t* m
       return launch_skinny<false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, s);
     if (grouped_gemm_bm(true, C) == 256)
       return launch_bf16<256, 256, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, s);
+    if (d_ff % 64 == 0)
+      return launch_bf16<128, 256, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, s);
     return launch_bf16<128, 128, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, s);
   }
   const unsigned mtiles = static_cast<unsigned>(E * ceil_div(C, 64));
