@@ -64,10 +64,9 @@ hipError_t launch_tile_hist(const int32_t* idx, int64_t T, int k, int E, int32_t
 // for row tiles of `bm` rows.
 hipError_t launch_scan(const int32_t* tile_cnt, int64_t nt, int E, int64_t C, int P,
                        int64_t row_bytes, int k, int64_t T, int32_t* tile_off, int32_t* routed,
-                       int32_t* kept, int32_t* send, int64_t* totals, int bm, int tail_rows,
-                       int32_t* mtile_off, int32_t* src, hipStream_t s);
-hipError_t launch_mtile_map(const int32_t* kept, int E, int bm, int tail_rows, int32_t* mtile_off,
-                            hipStream_t s);
+                       int32_t* kept, int32_t* send, int64_t* totals, int bm, int32_t* mtile_off,
+                       int32_t* src, hipStream_t s);
+hipError_t launch_mtile_map(const int32_t* kept, int E, int bm, int32_t* mtile_off, hipStream_t s);
 hipError_t launch_slots(const int32_t* idx, const int32_t* tile_off, int64_t T, int k, int E,
                         int64_t C, int32_t* slot, int32_t* src, int64_t* totals, hipStream_t s);
 hipError_t launch_scatter_rows(const void* x, const int32_t* idx, const int32_t* slot, int64_t T,
@@ -77,11 +76,6 @@ hipError_t launch_scatter_rows(const void* x, const int32_t* idx, const int32_t*
 // Row-tile height the grouped GEMM uses for these sizes (the mtile map must
 // be built for the same value).
 int grouped_gemm_bm(bool bf16, int64_t C);
-// Rows of the tail tiles (0: none). With 256-row tiles an expert whose last
-// tile would hold at most this many rows gets a 128-row tail tile in a second
-// map instead: the tile map is then [E + 1] main offsets followed by [E + 1]
-// tail offsets.
-int grouped_gemm_tail_rows(bool bf16, int64_t C, int64_t d, int64_t d_ff);
 // GEMM 1: h = silu(X Wg^T) * (X Wu^T) on rows < kept.
 hipError_t launch_gemm_gate_up(const void* buckets, const int32_t* kept, const int32_t* mtile_off,
                                const void* wg, const void* wu, int E, int64_t C, int64_t d,

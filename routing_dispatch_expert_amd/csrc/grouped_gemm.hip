@@ -512,15 +512,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // 64 x 128, each as 2 x 4 v_mfma_f32_32x32x16_bf16 tiles. One DMA instruction
 // of a wave fills 16 rows (lane L: row L / 4, position L % 4); chunk c of row
 // r sits at position c ^ ((r / 4) % 4), so the 16 lanes of a fragment read
-// (16 consecutive rows) hit distinct banks. Needs K % 64 == 0. With tail_of
-// (256) it runs the tail tiles of the 256-row kernel: one per expert, rows
-// from the last multiple of 256 below kept.
+// (16 consecutive rows) hit distinct banks. Needs K % 64 == 0.
 // ---------------------------------------------------------------------------
 template <bool SWIGLU>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_dma_m128_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     bf16_t* __restrict__ out, const int32_t* __restrict__ kept, const int32_t* __restrict__ mtile_off,
-    int E, int64_t C, int64_t K, int64_t N, int nt_count, int tail_of) {
+    int E, int64_t C, int64_t K, int64_t N, int nt_count) {
   constexpr int BM = 128, BN = 256, BK = 32, TM = 2, TN = 4;
   constexpr int CH = BK / 8;                    // 16-byte chunks per LDS row
   constexpr int BNO = SWIGLU ? BN / 2 : BN;
@@ -536,7 +534,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   m0 = __builtin_amdgcn_readfirstlane(m0);
   nt = __builtin_amdgcn_readfirstlane(nt);
   const int rows = __builtin_amdgcn_readfirstlane(kept[e]);
-  if (tail_of) m0 += rows / tail_of * tail_of;  // tail tile: the rows after the expert's whole tail_of-row tiles
   const int64_t n0 = static_cast<int64_t>(nt) * BNO;
   const int64_t nk = K / BK;  // even, at least 2
 
@@ -834,10 +831,6 @@ int grouped_gemm_bm(bool bf16, int64_t C) {
   return C >= kBigTileMinC ? 256 : 128;
 }
 
-int grouped_gemm_tail_rows(bool bf16, int64_t C, int64_t d, int64_t d_ff) {
-  return grouped_gemm_bm(bf16, C) == 256 && d % 64 == 0 && d_ff % 64 == 0 ? 128 : 0;
-}
-
 namespace {
 
 template <bool SWIGLU>
@@ -864,7 +857,7 @@ hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out,
   if constexpr (BM == 128 && BN == 256) {
     if (K % 64) return hipErrorInvalidValue;  // callers pick this tile only for K % 64 == 0
     gemm_bf16_dma_m128_kernel<SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
-        pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), 0);
+        pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt));
   } else if (BM == 256 && BN == 256 && K % 128 == 0) {
     gemm_bf16_dma_kernel<SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
         pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt));
@@ -872,18 +865,6 @@ hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out,
     gemm_bf16_kernel<BM, BN, SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
         pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt));
   }
-  return hipGetLastError();
-}
-
-// Tail tiles of the 256-row kernel (at most one per expert), 128 x 256 each.
-template <bool SWIGLU>
-hipError_t launch_tail(const void* a, const void* b0, const void* b1, void* out, const int32_t* kept,
-                       const int32_t* tail_off, int E, int64_t C, int64_t K, int64_t N, hipStream_t s) {
-  const int64_t nt = ceil_div(N, SWIGLU ? 128 : 256);
-  const int64_t blocks = ceil_div(E * nt, 8) * 8;
-  gemm_bf16_dma_m128_kernel<SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
-      static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0), static_cast<const bf16_t*>(b1),
-      static_cast<bf16_t*>(out), kept, tail_off, E, C, K, N, static_cast<int>(nt), 256);
   return hipGetLastError();
 }
 
@@ -896,11 +877,8 @@ hipError_t launch_gemm_gate_up(const void* buckets, const int32_t* kept, const i
   if (bf16) {
     if (grouped_gemm_bm(true, C) == kSkinnyRows && d % 32 == 0)
       return launch_skinny<true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, s);
-    if (grouped_gemm_bm(true, C) == 256) {
-      const hipError_t err = launch_bf16<256, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, s);
-      if (err != hipSuccess || !grouped_gemm_tail_rows(true, C, d, d_ff)) return err;
-      return launch_tail<true>(buckets, wg, wu, h, kept, mtile_off + E + 1, E, C, d, d_ff, s);
-    }
+    if (grouped_gemm_bm(true, C) == 256)
+      return launch_bf16<256, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, s);
     if (d % 64 == 0)
       return launch_bf16<128, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, s);
     return launch_bf16<128, 128, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, s);
@@ -919,11 +897,8 @@ hipError_t launch_gemm_down(const void* h, const int32_t* kept, const int32_t* m
   if (bf16) {
     if (grouped_gemm_bm(true, C) == kSkinnyRows && d_ff % 32 == 0)
       return launch_skinny<false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, s);
-    if (grouped_gemm_bm(true, C) == 256) {
-      const hipError_t err = launch_bf16<256, 256, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, s);
-      if (err != hipSuccess || !grouped_gemm_tail_rows(true, C, d, d_ff)) return err;
-      return launch_tail<false>(h, wd, nullptr, y, kept, mtile_off + E + 1, E, C, d_ff, d, s);
-    }
+    if (grouped_gemm_bm(true, C) == 256)
+      return launch_bf16<256, 256, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, s);
     if (d_ff % 64 == 0)
       return launch_bf16<128, 256, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, s);
     return launch_bf16<128, 128, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, s);

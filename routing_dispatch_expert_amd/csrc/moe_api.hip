@@ -158,7 +158,7 @@ LayerPlan plan_layer(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E, in
   p.kept = c.take<int32_t>(E);
   p.send = c.take<int32_t>(P);
   p.totals = c.take<int64_t>(MOE_NUM_TOTALS);
-  p.mtile = c.take<int32_t>(2 * (static_cast<size_t>(E) + 1));  // main and tail row-tile maps
+  p.mtile = c.take<int32_t>(static_cast<size_t>(E) + 1);
   p.src = c.take<int32_t>(static_cast<size_t>(E) * C);
   p.buckets = c.take<char>(static_cast<size_t>(E) * C * d * eb);
   p.h = c.take<char>(static_cast<size_t>(E) * C * d_ff * eb);
@@ -271,7 +271,7 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SLOTS, false, s), "event");
   if (!fused_hist) MOE_HIP_TRY(moe::launch_tile_hist(idx, T, k, E, p.tile_cnt, s), "tile histogram");
   MOE_HIP_TRY(moe::launch_scan(p.tile_cnt, nt, E, C, P, d * eb, k, T, p.tile_off, routed, kept, send,
-                               totals, bm, moe::grouped_gemm_tail_rows(bf16, C, d, d_ff), p.mtile, src, s),
+                               totals, bm, p.mtile, src, s),
               "scan");
   MOE_HIP_TRY(moe::launch_slots(idx, p.tile_off, T, k, E, C, slot, src, totals, s), "slots");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SLOTS, true, s), "event");
@@ -379,7 +379,7 @@ int moe_permute(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, in
   const int64_t eb = elem_bytes(dtype);
   MOE_HIP_TRY(moe::launch_tile_hist(topk_idx, T, k, E, tile_cnt, s), "tile histogram");
   MOE_HIP_TRY(moe::launch_scan(tile_cnt, nt, E, C, P, d * eb, k, T, tile_off, routed_count, kept_count,
-                               send_count, totals, 0, 0, nullptr, src, s),
+                               send_count, totals, 0, nullptr, src, s),
               "scan");
   MOE_HIP_TRY(moe::launch_slots(topk_idx, tile_off, T, k, E, C, slot, src, totals, s), "slots");
   MOE_HIP_TRY(moe::launch_scatter_rows(x, topk_idx, slot, T, k, C, d * eb, buckets, s), "scatter");
@@ -388,7 +388,7 @@ int moe_permute(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, in
 
 int moe_grouped_gemm_workspace_size(int32_t E, int64_t C, size_t* bytes) {
   if (!bytes || E < 1 || C < 1) return fail(MOE_ERR_INVALID_ARG, "need bytes, E >= 1, C >= 1");
-  *bytes = align_up(2 * (static_cast<size_t>(E) + 1) * sizeof(int32_t));  // main and tail row-tile maps
+  *bytes = align_up((static_cast<size_t>(E) + 1) * sizeof(int32_t));
   return MOE_OK;
 }
 
@@ -412,9 +412,7 @@ int moe_grouped_gemm(const void* buckets, const int32_t* kept_count, const void*
   auto s = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == MOE_DTYPE_BF16;
   auto* mtile = static_cast<int32_t*>(workspace);
-  MOE_HIP_TRY(moe::launch_mtile_map(kept_count, E, moe::grouped_gemm_bm(bf16, C),
-                                     moe::grouped_gemm_tail_rows(bf16, C, d, d_ff), mtile, s),
-              "tile map");
+  MOE_HIP_TRY(moe::launch_mtile_map(kept_count, E, moe::grouped_gemm_bm(bf16, C), mtile, s), "tile map");
   MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept_count, mtile, W_gate, W_up, E, C, d, d_ff, bf16, h, s),
               "grouped gemm (gate, up)");
   MOE_HIP_TRY(moe::launch_gemm_down(h, kept_count, mtile, W_down, E, C, d, d_ff, bf16, y, s),

@@ -67,23 +67,14 @@ __device__ int block_exclusive_scan_1024(int v, int* total, int* sh /* >= 17 int
 
 // mtile_off[e] = sum over e' < e of ceil(kept[e'] / bm); mtile_off[E] = total.
 // Block of 1024 threads, 4 experts per thread (E <= 4096).
-// Row-tile map: mtile_off[e] = row tiles of experts before e (tiles of bm
-// rows), mtile_off[E] = all of them. With tail_rows, an expert whose last
-// tile would hold at most tail_rows rows leaves it out and gets one tail tile
-// instead, counted in a second map at mtile_off + E + 1.
-__device__ void mtile_prefix(const int* kept_s, int E, int bm, int tail_rows, int32_t* mtile_off, int* sh) {
-  int v[4], tv[4];
-  int local = 0, tlocal = 0;
+__device__ void mtile_prefix(const int* kept_s, int E, int bm, int32_t* mtile_off, int* sh) {
+  int v[4];
+  int local = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = threadIdx.x * 4 + q;
-    const int kv = e < E ? kept_s[e] : 0;
-    const int rem = kv % bm;
-    const bool tail = tail_rows > 0 && rem > 0 && rem <= tail_rows;
-    v[q] = tail ? kv / bm : (kv + bm - 1) / bm;
-    tv[q] = tail ? 1 : 0;
+    v[q] = e < E ? (kept_s[e] + bm - 1) / bm : 0;
     local += v[q];
-    tlocal += tv[q];
   }
   int total;
   int run = block_exclusive_scan_1024(local, &total, sh);
@@ -94,18 +85,6 @@ __device__ void mtile_prefix(const int* kept_s, int E, int bm, int tail_rows, in
     run += v[q];
   }
   if (threadIdx.x == 0) mtile_off[E] = total;
-  if (tail_rows > 0) {
-    int ttotal;
-    int trun = block_exclusive_scan_1024(tlocal, &ttotal, sh);
-    int32_t* tail_off = mtile_off + E + 1;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = threadIdx.x * 4 + q;
-      if (e < E) tail_off[e] = trun;
-      trun += tv[q];
-    }
-    if (threadIdx.x == 0) tail_off[E] = ttotal;
-  }
 }
 
 // Exclusive scan over tiles per expert, then counts, totals, send counts and
@@ -114,8 +93,7 @@ __device__ void mtile_prefix(const int* kept_s, int E, int bm, int tail_rows, in
 __global__ __launch_bounds__(1024) void scan_finalize_kernel(
     const int32_t* __restrict__ tile_cnt, int64_t nt, int E, int64_t C, int P, int64_t row_bytes, int k,
     int64_t T, int32_t* __restrict__ tile_off, int32_t* __restrict__ routed, int32_t* __restrict__ kept,
-    int32_t* __restrict__ send, int64_t* __restrict__ totals, int bm, int tail_rows,
-    int32_t* __restrict__ mtile_off) {
+    int32_t* __restrict__ send, int64_t* __restrict__ totals, int bm, int32_t* __restrict__ mtile_off) {
   __shared__ int part[16][65];
   __shared__ int kept_s[4096];
   __shared__ int send_s[4096];  // kept rows per rank (P <= E)
@@ -165,16 +143,16 @@ __global__ __launch_bounds__(1024) void scan_finalize_kernel(
     totals[2] = static_cast<int64_t>(E) * C - n_kept;
     totals[3] = (n_kept - rank0) * row_bytes;
   }
-  if (mtile_off) mtile_prefix(kept_s, E, bm, tail_rows, mtile_off, sh);
+  if (mtile_off) mtile_prefix(kept_s, E, bm, mtile_off, sh);
 }
 
 __global__ __launch_bounds__(1024) void mtile_map_kernel(const int32_t* __restrict__ kept, int E,
-                                                         int bm, int tail_rows, int32_t* __restrict__ mtile_off) {
+                                                         int bm, int32_t* __restrict__ mtile_off) {
   __shared__ int kept_s[4096];
   __shared__ int sh[17];
   for (int e = threadIdx.x; e < E; e += blockDim.x) kept_s[e] = kept[e];
   __syncthreads();
-  mtile_prefix(kept_s, E, bm, tail_rows, mtile_off, sh);
+  mtile_prefix(kept_s, E, bm, mtile_off, sh);
 }
 
 // src[e][s] = -1 on padding rows s >= kept[e] (kept rows come from the slot kernel).
@@ -302,10 +280,10 @@ hipError_t launch_tile_hist(const int32_t* idx, int64_t T, int k, int E, int32_t
 
 hipError_t launch_scan(const int32_t* tile_cnt, int64_t nt, int E, int64_t C, int P,
                        int64_t row_bytes, int k, int64_t T, int32_t* tile_off, int32_t* routed,
-                       int32_t* kept, int32_t* send, int64_t* totals, int bm, int tail_rows,
-                       int32_t* mtile_off, int32_t* src, hipStream_t s) {
+                       int32_t* kept, int32_t* send, int64_t* totals, int bm, int32_t* mtile_off,
+                       int32_t* src, hipStream_t s) {
   scan_finalize_kernel<<<dim3(1), dim3(1024), 0, s>>>(tile_cnt, nt, E, C, P, row_bytes, k, T, tile_off, routed,
-                                                      kept, send, totals, bm, tail_rows, mtile_off);
+                                                      kept, send, totals, bm, mtile_off);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !src) return err;
   const unsigned gx = static_cast<unsigned>(std::min<int64_t>(ceil_div(C, 256), 64));
@@ -313,9 +291,8 @@ hipError_t launch_scan(const int32_t* tile_cnt, int64_t nt, int E, int64_t C, in
   return hipGetLastError();
 }
 
-hipError_t launch_mtile_map(const int32_t* kept, int E, int bm, int tail_rows, int32_t* mtile_off,
-                            hipStream_t s) {
-  mtile_map_kernel<<<dim3(1), dim3(1024), 0, s>>>(kept, E, bm, tail_rows, mtile_off);
+hipError_t launch_mtile_map(const int32_t* kept, int E, int bm, int32_t* mtile_off, hipStream_t s) {
+  mtile_map_kernel<<<dim3(1), dim3(1024), 0, s>>>(kept, E, bm, mtile_off);
   return hipGetLastError();
 }
 
