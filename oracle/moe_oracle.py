@@ -17,7 +17,8 @@ What is computed, in the pages' own order (sources are cited per function):
   5. each expert's SwiGLU MLP on the copies it keeps;
   6. the combine: the inverse permutation, gate-weighted and summed onto the
      residual, with fully dropped tokens passed through unchanged;
-  7. routing statistics.
+  7. routing statistics;
+  8. the backward pass: the gradients of the layer's inputs and weights.
 
 All floating point here is fp64 (numpy), from the exact values of the inputs;
 results are rounded once to the precision the path fixes (fp32 for logits and
@@ -45,7 +46,7 @@ __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "f64_to_f32", "encode", "silu",
     "decode", "capacity", "router_logits", "topk_experts", "rank_limited_experts", "gate_weights",
     "assign_slots", "dispatch_buckets", "send_counts", "expert_hidden", "expert_mlp",
-    "combine", "routing_stats", "dispatch_bytes", "layer_forward",
+    "combine", "routing_stats", "dispatch_bytes", "layer_forward", "layer_backward",
 ]
 
 
@@ -83,11 +84,14 @@ def f64_to_bf16_bits(v: np.ndarray) -> np.ndarray:
 
 
 def decode(a: np.ndarray, dtype: str) -> np.ndarray:
-    """Inputs as float64: bf16 arrays arrive as raw 16-bit patterns."""
+    """Inputs as float64: bf16 arrays arrive as raw 16-bit patterns. "f64" is
+    the unrounded form used for finite-difference checks of the gradients."""
     if dtype == "bf16":
         return bf16_bits_to_f64(a)
     if dtype == "f32":
         return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == "f64":
+        return np.asarray(a, dtype=np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -95,6 +99,8 @@ def encode(v64: np.ndarray, dtype: str) -> np.ndarray:
     """Round float64 results once to the layer's dtype (bf16 as bit patterns)."""
     if dtype == "bf16":
         return f64_to_bf16_bits(v64)
+    if dtype == "f64":
+        return np.asarray(v64, dtype=np.float64)
     return f64_to_f32(v64)
 
 
@@ -130,7 +136,8 @@ def topk_experts(logits32: np.ndarray, k: int) -> np.ndarray:
     the pages; the reading taken: order by score descending, then expert index
     ascending, so the lowest index wins a tie. +0.0 and -0.0 compare equal.
     """
-    l = np.asarray(logits32, dtype=np.float32) + np.float32(0.0)  # -0.0 -> +0.0
+    l = np.asarray(logits32)
+    l = l + l.dtype.type(0.0)  # -0.0 -> +0.0 (fp32 scores; fp64 ones in the unrounded mode)
     T, E = l.shape
     if not 1 <= k <= E:
         raise ValueError("need 1 <= k <= E")
@@ -154,7 +161,8 @@ def rank_limited_experts(logits32: np.ndarray, k: int, P: int, M: int) -> np.nda
     k experts are then the best of the allowed ranks' experts, ordered as in
     topk_experts. M = 0 or M >= P is no limit. Needs M * (E/P) >= k.
     """
-    l = np.asarray(logits32, dtype=np.float32) + np.float32(0.0)
+    l = np.asarray(logits32)
+    l = l + l.dtype.type(0.0)
     T, E = l.shape
     if M == 0 or M >= P:
         return topk_experts(l, k)
@@ -164,7 +172,7 @@ def rank_limited_experts(logits32: np.ndarray, k: int, P: int, M: int) -> np.nda
     best_ranks = np.argsort(-rank_score, axis=1, kind="stable")[:, :M]
     allowed = np.zeros((T, P), dtype=bool)
     np.put_along_axis(allowed, best_ranks, True, axis=1)
-    masked = np.where(np.repeat(allowed, E // P, axis=1), l, np.float32(-np.inf))
+    masked = np.where(np.repeat(allowed, E // P, axis=1), l, l.dtype.type(-np.inf))
     order = np.argsort(-masked, axis=1, kind="stable")
     return order[:, :k].astype(np.int32)
 
@@ -353,7 +361,7 @@ def routing_stats(slot: np.ndarray, routed: np.ndarray, kept: np.ndarray, C: int
 # ---------------------------------------------------------------------------
 
 def layer_forward(x, wr, expert_weights, T, d, d_ff, E, k, cf, dtype, P=1, bias=None,
-                  tokens=None, max_ranks=0):
+                  tokens=None, max_ranks=0, exact=False):
     """The layer as the plain per-token definition, steps 1 to 7 above.
 
     x [T, d] and wr [E, d] are the inputs (bf16 as bit patterns, or fp32).
@@ -363,6 +371,8 @@ def layer_forward(x, wr, expert_weights, T, d, d_ff, E, k, cf, dtype, P=1, bias=
     output only for `tokens` (all when None), since each output row depends
     only on its own token once the slots are known. max_ranks > 0 limits each
     token's experts to that many of the P ranks (rank_limited_experts).
+    exact=True keeps the scores and gates in fp64 (no fp32 rounding): the
+    smooth function that finite differences of the gradients need.
 
     Returns a dict: logits, idx, w, C, slot, src, routed, kept, stats,
     tokens, out64 (fp64, unrounded), out (rounded once to dtype; a token with
@@ -370,12 +380,21 @@ def layer_forward(x, wr, expert_weights, T, d, d_ff, E, k, cf, dtype, P=1, bias=
     """
     x = np.asarray(x)
     x64 = decode(x, dtype)
-    logits = router_logits(x64, decode(wr, dtype), bias)
-    idx = rank_limited_experts(logits, k, P, max_ranks)
-    w = gate_weights(logits, idx)
+    if exact:
+        logits = x64 @ decode(wr, dtype).T
+        if bias is not None:
+            logits = logits + np.asarray(bias, dtype=np.float64)[None, :]
+        idx = rank_limited_experts(logits, k, P, max_ranks)
+        lsel = np.take_along_axis(logits, idx, axis=1)
+        z = np.exp(lsel - lsel[:, :1])
+        w = z / z.sum(axis=1, keepdims=True)
+    else:
+        logits = router_logits(x64, decode(wr, dtype), bias)
+        idx = rank_limited_experts(logits, k, P, max_ranks)
+        w = gate_weights(logits, idx)
     C = capacity(T, E, k, cf)
     slot, src, routed, kept = assign_slots(idx, E, C)
-    eb = 2 if dtype == "bf16" else 4
+    eb = {"bf16": 2, "f32": 4, "f64": 8}[dtype]
     stats = routing_stats(slot, routed, kept, C, P, d, eb)
 
     tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
@@ -392,3 +411,67 @@ def layer_forward(x, wr, expert_weights, T, d, d_ff, E, k, cf, dtype, P=1, bias=
     return {"logits": logits, "idx": idx, "w": w, "C": C, "slot": slot, "src": src,
             "routed": routed, "kept": kept, "stats": stats, "tokens": tok,
             "out64": out64, "out": out}
+
+
+# ---------------------------------------------------------------------------
+# 8. the backward pass
+# ---------------------------------------------------------------------------
+
+def layer_backward(x, wr, expert_weights, dout, T, d, d_ff, E, k, cf, dtype, P=1, bias=None,
+                   max_ranks=0, exact=False):
+    """Gradients of the layer, given dout = dLoss/dout [T, d] in the layer dtype.
+
+    [EP-A2A] "The bandwidth bill": the backward pass repeats the dispatch and
+    combine (two more all-to-alls per layer), i.e. it runs the same routing
+    in reverse. The pages give no formulas; the reading taken is the chain
+    rule through the forward above, with the top-k choice and the capacity
+    drops held fixed (they are piecewise constant):
+
+      combine:   dw[t, j] = <dout[t], y[t, j]> for a kept copy, 0 if dropped;
+                 dy[t, j] = w[t, j] * dout[t]; dx[t] starts at dout[t]
+      gates:     dl[t, j] = w[t, j] * (dw[t, j] - sum_i w[t, i] dw[t, i])
+      router:    dx += dl Wr[idx]; dWr[e] = sum_t dl[t, e] x[t]; db = sum_t dl[t]
+      experts:   dh = dy Wd; dWd = dy^T h; dg = dh u silu'(g); du = dh silu(g);
+                 dWg = dg^T X; dWu = du^T X; dx[t] += dg Wg + du Wu
+                 with silu'(g) = s (1 + g (1 - s)), s = sigmoid(g)
+
+    Every sum is fp64 over the copies each expert kept. Returns a dict: dx,
+    dwr [E, d], db [E], dwg, dwu [E, d_ff, d], dwd [E, d, d_ff] (all fp64),
+    dw and dl [T, k], and the routing (idx, w, slot).
+    """
+    fwd = layer_forward(x, wr, expert_weights, T, d, d_ff, E, k, cf, dtype, P=P, bias=bias,
+                        tokens=np.arange(0), max_ranks=max_ranks, exact=exact)
+    idx, w, slot = fwd["idx"], np.asarray(fwd["w"], dtype=np.float64), fwd["slot"]
+    x64 = decode(np.asarray(x), dtype)
+    g_out = decode(np.asarray(dout), dtype)
+    dx = g_out.copy()
+    dw = np.zeros((T, k))
+    dwg = np.zeros((E, d_ff, d))
+    dwu = np.zeros((E, d_ff, d))
+    dwd = np.zeros((E, d, d_ff))
+    for e in range(E):
+        rows, js = np.nonzero((idx == e) & (slot >= 0))
+        if rows.size == 0:
+            continue
+        wg, wu, wd = (decode(a, dtype) for a in expert_weights(e))
+        X = x64[rows]
+        gpre = X @ wg.T
+        upre = X @ wu.T
+        sg = 1.0 / (1.0 + np.exp(-gpre))
+        h = gpre * sg * upre
+        y = h @ wd.T
+        dw[rows, js] = np.sum(g_out[rows] * y, axis=1)
+        dy = w[rows, js][:, None] * g_out[rows]
+        dh = dy @ wd
+        dwd[e] = dy.T @ h
+        dg = dh * upre * sg * (1.0 + gpre * (1.0 - sg))
+        du = dh * gpre * sg
+        dwg[e] = dg.T @ X
+        dwu[e] = du.T @ X
+        np.add.at(dx, rows, dg @ wg + du @ wu)
+    dl = w * (dw - np.sum(w * dw, axis=1, keepdims=True))
+    dl_full = np.zeros((T, E))
+    np.put_along_axis(dl_full, idx, dl, axis=1)
+    dx += dl_full @ decode(np.asarray(wr), dtype)
+    return {"dx": dx, "dwr": dl_full.T @ x64, "db": dl_full.sum(axis=0), "dwg": dwg, "dwu": dwu,
+            "dwd": dwd, "dw": dw, "dl": dl, "idx": idx, "w": w, "slot": slot}
