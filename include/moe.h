@@ -121,6 +121,30 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
                       int32_t P, int32_t max_ranks, moe_dtype_t dtype, void* out,
                       moe_stats_t* stats, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward pass of the layer ([EP-A2A] "The bandwidth bill": the backward
+ * runs the dispatch and the combine again, in reverse; "All-to-all: the
+ * distributed transpose": the combine is the gate-weighted inverse of the
+ * dispatch). Given the forward's inputs (as for moe_layer_forward) and
+ * dout = dLoss/dout [T, d] (dtype), writes
+ *   dx [T, d] dtype; dW_router [E, d] dtype; d_bias [E] fp32 (may be NULL);
+ *   dW_gate, dW_up [E, d_ff, d] and dW_down [E, d, d_ff] dtype,
+ * the chain rule through the forward with the top-k choice and the capacity
+ * drops held fixed: a dropped copy passes no gradient to its expert, but its
+ * gate still does through the softmax; a fully dropped token gets dx = dout.
+ * Routing, capacity and the expert activations are recomputed from the
+ * inputs (no forward state is kept). Sums run in fp32 in a fixed order, so
+ * results are deterministic. dx must not overlap x or dout. Gradients are
+ * written, not accumulated. workspace: moe_backward_workspace_size() bytes,
+ * 256-byte aligned. Errors as moe_layer_forward. */
+int moe_backward_workspace_size(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k, float cf,
+                                int32_t P, moe_dtype_t dtype, size_t* bytes);
+int moe_layer_backward(const void* x, const void* W_router, const float* router_bias,
+                       const void* W_gate, const void* W_up, const void* W_down, const void* dout,
+                       int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k, float cf, int32_t P,
+                       int32_t max_ranks, moe_dtype_t dtype, void* dx, void* dW_router,
+                       float* d_bias, void* dW_gate, void* dW_up, void* dW_down, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* Router stage ([EP-inferensys] gating-network entry): logits on the matrix
  * cores, then top-k (with the rank limit P, max_ranks) and gates as in moe_route. logits_out [T, E] fp32 may be
  * NULL; otherwise it receives the scores (bias included). The scores are

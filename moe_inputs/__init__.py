@@ -40,7 +40,7 @@ GAP = 1e-3          # minimum adjacent gap among a token's top k+1 scores
 MAX_ATTEMPTS = 10000
 
 # stream ids of the tensors
-_X, _WR, _WG, _WU, _WD = 1, 2, 3, 4, 5
+_X, _WR, _WG, _WU, _WD, _DOUT = 1, 2, 3, 4, 5, 6
 
 
 def _rng(*key: int) -> np.random.Generator:
@@ -152,6 +152,11 @@ class Workload:
                 self.x[t] = _draw((self.d,), self.x_std, self.dtype, self.seed, _X, int(t), attempt)
             self.resampled += bad.size
             bad = bad[self._near_tied(bad)]
+
+    # ---- upstream gradient ------------------------------------------------
+    def grad_out(self, seed: int = 0) -> np.ndarray:
+        """dLoss/dout [T, d] for backward checks: N(0, 1) in the layer dtype."""
+        return _draw((self.T, self.d), 1.0, self.dtype, self.seed, _DOUT, seed)
 
     # ---- expert weights ---------------------------------------------------
     @property

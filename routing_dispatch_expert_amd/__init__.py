@@ -22,8 +22,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 TOTALS = ("dropped", "fully_dropped_tokens", "padded_rows", "offrank_bytes")
 
-EXPORTS = ("moe_capacity", "moe_workspace_size", "moe_layer_forward", "moe_router_workspace_size",
-           "moe_router", "moe_route",
+EXPORTS = ("moe_capacity", "moe_workspace_size", "moe_layer_forward", "moe_backward_workspace_size",
+           "moe_layer_backward", "moe_router_workspace_size", "moe_router", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_grouped_gemm_workspace_size",
            "moe_grouped_gemm", "moe_combine", "moe_set_stage_events", "moe_status_string", "moe_last_error")
 STAGES = ("router", "route", "slots", "scatter", "gate_up", "down", "combine")
@@ -49,6 +49,9 @@ _SIGS = {
     "moe_workspace_size": [_I64, _I64, _I64, _I32, _I32, _F32, _I32, ctypes.c_int, _P],
     "moe_layer_forward": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _F32, _I32, _I32, ctypes.c_int,
                           _P, ctypes.POINTER(moe_stats_t), _P, _SZ, _P],
+    "moe_backward_workspace_size": [_I64, _I64, _I64, _I32, _I32, _F32, _I32, ctypes.c_int, _P],
+    "moe_layer_backward": [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _F32, _I32, _I32, ctypes.c_int,
+                           _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "moe_router_workspace_size": [_I64, _I64, _I32, ctypes.c_int, _P],
     "moe_router": [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, ctypes.c_int, _P, _P, _P, _P, _SZ, _P],
     "moe_route": [_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P],
@@ -159,6 +162,23 @@ def moe_layer_forward(x, W_router, router_bias, W_gate, W_up, W_down, T, d, d_ff
            "moe_layer_forward")
 
 
+def moe_backward_workspace_size(T, d, d_ff, E, k, cf, P, dtype) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_backward_workspace_size(T, d, d_ff, E, k, cf, P, _dtype(dtype), ctypes.byref(n)),
+           "moe_backward_workspace_size")
+    return n.value
+
+
+def moe_layer_backward(x, W_router, router_bias, W_gate, W_up, W_down, dout, T, d, d_ff, E, k, cf, P, max_ranks,
+                       dtype, dx, dW_router, d_bias, dW_gate, dW_up, dW_down, workspace, workspace_bytes,
+                       stream=None):
+    _check(lib().moe_layer_backward(_ptr(x), _ptr(W_router), _ptr(router_bias), _ptr(W_gate), _ptr(W_up),
+                                    _ptr(W_down), _ptr(dout), T, d, d_ff, E, k, cf, P, max_ranks, _dtype(dtype),
+                                    _ptr(dx), _ptr(dW_router), _ptr(d_bias), _ptr(dW_gate), _ptr(dW_up),
+                                    _ptr(dW_down), _ptr(workspace), workspace_bytes, _stream(stream)),
+           "moe_layer_backward")
+
+
 def moe_router_workspace_size(T, d, E, dtype) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().moe_router_workspace_size(T, d, E, _dtype(dtype), ctypes.byref(n)), "moe_router_workspace_size")
@@ -267,5 +287,33 @@ def forward(x, W_router, W_gate, W_up, W_down, k, cf, P=1, router_bias=None, str
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     moe_layer_forward(x, W_router, router_bias, W_gate, W_up, W_down, T, d, d_ff, E, k, cf, P, max_ranks, dt,
                       res["out"], res, workspace, nbytes, stream)
+    res["workspace"] = workspace
+    return res
+
+
+def backward(x, W_router, W_gate, W_up, W_down, dout, k, cf, P=1, router_bias=None, stream=None, max_ranks=0,
+             workspace=None):
+    """Gradients of the layer for dout on torch device tensors; returns a dict
+    dx, dW_router, d_bias (fp32, when router_bias is given), dW_gate, dW_up,
+    dW_down, workspace."""
+    import torch
+    T, d = x.shape
+    E = W_router.shape[0]
+    d_ff = W_gate.shape[1]
+    dt = x.dtype
+    for t, n, s in ((x, "x", (T, d)), (dout, "dout", (T, d)), (W_router, "W_router", (E, d)),
+                    (W_gate, "W_gate", (E, d_ff, d)), (W_up, "W_up", (E, d_ff, d)), (W_down, "W_down", (E, d, d_ff))):
+        _require(t, n, dt, s)
+    if router_bias is not None:
+        _require(router_bias, "router_bias", torch.float32, (E,))
+    res = {"dx": torch.empty_like(x), "dW_router": torch.empty_like(W_router), "dW_gate": torch.empty_like(W_gate),
+           "dW_up": torch.empty_like(W_up), "dW_down": torch.empty_like(W_down),
+           "d_bias": None if router_bias is None else torch.empty(E, dtype=torch.float32, device=x.device)}
+    nbytes = moe_backward_workspace_size(T, d, d_ff, E, k, cf, P, dt)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    moe_layer_backward(x, W_router, router_bias, W_gate, W_up, W_down, dout, T, d, d_ff, E, k, cf, P, max_ranks, dt,
+                       res["dx"], res["dW_router"], res["d_bias"], res["dW_gate"], res["dW_up"], res["dW_down"],
+                       workspace, nbytes, stream)
     res["workspace"] = workspace
     return res

@@ -19,7 +19,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_hip.so")
 ARCH = "gfx950"
 
-SOURCES = ["moe_api.hip", "router.hip", "permute.hip", "grouped_gemm.hip", "combine.hip"]
+SOURCES = ["moe_api.hip", "router.hip", "permute.hip", "grouped_gemm.hip", "combine.hip", "backward.hip"]
 
 
 def hipcc() -> str:

@@ -1,0 +1,363 @@
+// Backward pass of the MoE layer (gfx950): the row kernels and transposes
+// around the grouped GEMMs.
+//
+// Sources: "Expert Parallelism & All-to-All" (neelmishra.github.io), "The
+// bandwidth bill" - the backward pass runs the dispatch and the combine again,
+// in reverse; "All-to-all: the distributed transpose" - the combine is the
+// exact inverse permutation, weighted by the gates. The gradients are the
+// chain rule through the forward, with the top-k choice and the capacity
+// drops held fixed (both are piecewise constant):
+//
+//   combine:  dw[t,j] = <dout[t], y[e,s]> (kept copy (t,j) at expert e, row s),
+//             dy[e,s] = w[t,j] dout[t]; a dropped copy has dw = 0
+//   gates:    dl[t,j] = w[t,j] (dw[t,j] - sum_i w[t,i] dw[t,i])
+//   experts:  h = silu(g) u; dg = dh u silu'(g), du = dh silu(g),
+//             silu'(g) = s (1 + g (1 - s)), s = sigmoid(g)
+//   dispatch: dx[t] = dout[t] + sum_j [kept] dX[e,s] + sum_j dl[t,j] Wr[e]
+//   router:   dWr[e] = sum_t dl[t,e] x[t]; db[e] = sum_t dl[t,e]
+//
+// Every sum is fp32 in a fixed order; each result is rounded once.
+#include <algorithm>
+
+#include "common.h"
+
+namespace moe {
+namespace {
+
+// 16-byte words: 8 bf16 or 4 fp32 values.
+template <bool BF16>
+struct Word {
+  static constexpr int N = BF16 ? 8 : 4;
+  __device__ static void load(const uint4& v, float (&f)[N]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (BF16) {
+        f[2 * q] = __uint_as_float(w[q] << 16);
+        f[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+      } else {
+        f[q] = __uint_as_float(w[q]);
+      }
+    }
+  }
+  __device__ static uint4 store(const float (&f)[N]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (BF16)
+        w[q] = static_cast<uint32_t>(f32_to_bf16(f[2 * q])) | (static_cast<uint32_t>(f32_to_bf16(f[2 * q + 1])) << 16);
+      else
+        w[q] = __float_as_uint(f[q]);
+    }
+    return uint4{w[0], w[1], w[2], w[3]};
+  }
+};
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Tiled transpose through LDS: dst[b][c][col_off + r] = src[b][r][c] for
+// r < valid[b] (all R rows when valid is NULL), and 0 for the other r < Rp;
+// src rows are src_ld elements apart, dst rows dst_ld.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ src, T* __restrict__ dst, int64_t R,
+                                                        int64_t Cc, int64_t src_ld, int64_t dst_ld, int64_t col_off,
+                                                        int64_t Rp, const int32_t* __restrict__ valid,
+                                                        int64_t src_bstride, int64_t dst_bstride) {
+  __shared__ T tile[64][65];
+  const int64_t b = blockIdx.z;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64, c0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int64_t nv = valid ? min(static_cast<int64_t>(valid[b]), R) : R;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const T* s = src + b * src_bstride;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < nv && c < Cc) ? s[r * src_ld + c] : T(0);
+  }
+  __syncthreads();
+  T* d = dst + b * dst_bstride;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (c < Cc && r < Rp) d[c * dst_ld + col_off + r] = tile[tx][i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// SwiGLU on the kept rows of [E][C][F]: forward h = silu(g) u; backward
+// dgu[.][0:F] = dh u silu'(g), dgu[.][F:2F] = dh silu(g). One block per row.
+// ---------------------------------------------------------------------------
+__device__ inline float sigmoidf_(float g) { return 1.0f / (1.0f + expf(-g)); }
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void swiglu_fwd_kernel(const uint4* __restrict__ g, const uint4* __restrict__ u,
+                                                         uint4* __restrict__ h, const int32_t* __restrict__ kept,
+                                                         int64_t C, int64_t VF) {
+  const int64_t row = blockIdx.x;
+  if (row % C >= kept[row / C]) return;
+  using W = Word<BF16>;
+  for (int64_t v = threadIdx.x; v < VF; v += blockDim.x) {
+    float gf[W::N], uf[W::N], hf[W::N];
+    W::load(g[row * VF + v], gf);
+    W::load(u[row * VF + v], uf);
+#pragma unroll
+    for (int q = 0; q < W::N; ++q) hf[q] = gf[q] * sigmoidf_(gf[q]) * uf[q];
+    h[row * VF + v] = W::store(hf);
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint4* __restrict__ dh, const uint4* __restrict__ g,
+                                                         const uint4* __restrict__ u, uint4* __restrict__ dgu,
+                                                         const int32_t* __restrict__ kept, int64_t C, int64_t VF) {
+  const int64_t row = blockIdx.x;
+  if (row % C >= kept[row / C]) return;
+  using W = Word<BF16>;
+  for (int64_t v = threadIdx.x; v < VF; v += blockDim.x) {
+    float df[W::N], gf[W::N], uf[W::N], dgf[W::N], duf[W::N];
+    W::load(dh[row * VF + v], df);
+    W::load(g[row * VF + v], gf);
+    W::load(u[row * VF + v], uf);
+#pragma unroll
+    for (int q = 0; q < W::N; ++q) {
+      const float s = sigmoidf_(gf[q]);
+      dgf[q] = df[q] * uf[q] * s * (1.0f + gf[q] * (1.0f - s));
+      duf[q] = df[q] * gf[q] * s;
+    }
+    dgu[row * 2 * VF + v] = W::store(dgf);
+    dgu[row * 2 * VF + VF + v] = W::store(duf);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine backward, one wave per token: for each kept copy j (ascending) the
+// dot product dw_j = <dout, y_j> (per-lane partials in word order, then a
+// fixed butterfly) and dy_j = w_j dout; then the gate gradients dl.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restrict__ dout, const uint4* __restrict__ y,
+                                                          const int32_t* __restrict__ idx, const float* __restrict__ w,
+                                                          const int32_t* __restrict__ slot, int64_t T, int k, int64_t C,
+                                                          int64_t V, uint4* __restrict__ dy, float* __restrict__ dl) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole waves only; no barriers below
+  using W = Word<BF16>;
+  const uint4* drow = dout + t * V;
+  float my_dw = 0.f;  // lane j keeps dw of copy j
+  for (int j = 0; j < k; ++j) {
+    const int sl = __builtin_amdgcn_readfirstlane(slot[t * k + j]);
+    float part = 0.f;
+    if (sl >= 0) {
+      const int64_t base = (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(idx[t * k + j])) * C + sl) * V;
+      const float wj = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(w[t * k + j])));
+      for (int64_t v = lane; v < V; v += 64) {
+        float df[W::N], yf[W::N], of[W::N];
+        W::load(drow[v], df);
+        W::load(y[base + v], yf);
+#pragma unroll
+        for (int q = 0; q < W::N; ++q) {
+          part = fmaf(df[q], yf[q], part);
+          of[q] = wj * df[q];
+        }
+        dy[base + v] = W::store(of);
+      }
+    }
+    const float dw = wave_sum(part);  // the same value in every lane; 0 for a dropped copy
+    if (lane == j) my_dw = dw;
+  }
+  const float wl = lane < k ? w[t * k + lane] : 0.f;
+  const float ssum = wave_sum(wl * my_dw);  // sum_i w_i dw_i
+  if (lane < k) dl[t * k + lane] = wl * (my_dw - ssum);
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch backward, one wave per token: dx = dout + sum_j [kept] dX[e_j, s_j]
+// + sum_j dl_j Wr[e_j], j ascending in each sum, fp32, rounded once.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(256) void gather_dx_kernel(const uint4* __restrict__ dout, const uint4* __restrict__ dX,
+                                                        const uint4* __restrict__ wr, const int32_t* __restrict__ idx,
+                                                        const float* __restrict__ dl, const int32_t* __restrict__ slot,
+                                                        int64_t T, int k, int64_t C, int64_t V, uint4* __restrict__ dx) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
+  using W = Word<BF16>;
+  for (int64_t v = lane; v < V; v += 64) {
+    float acc[W::N], f[W::N];
+    W::load(dout[t * V + v], acc);
+    for (int j = 0; j < k; ++j) {
+      const int sl = __builtin_amdgcn_readfirstlane(slot[t * k + j]);
+      if (sl < 0) continue;
+      const int64_t e = __builtin_amdgcn_readfirstlane(idx[t * k + j]);
+      W::load(dX[(e * C + sl) * V + v], f);
+#pragma unroll
+      for (int q = 0; q < W::N; ++q) acc[q] += f[q];
+    }
+    for (int j = 0; j < k; ++j) {
+      const int64_t e = __builtin_amdgcn_readfirstlane(idx[t * k + j]);
+      const float c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(dl[t * k + j])));
+      W::load(wr[e * V + v], f);
+#pragma unroll
+      for (int q = 0; q < W::N; ++q) acc[q] = fmaf(c, f[q], acc[q]);
+    }
+    dx[t * V + v] = W::store(acc);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Router weight gradient: dWr[e][i] = sum_t sum_j [idx[t,j] = e] dl[t,j] x[t][i]
+// (t, then j ascending), and db[e] the same without x. A block takes 16
+// experts x 256 columns; its accumulators live in LDS, one column per thread.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(256) void router_wgrad_kernel(const void* __restrict__ x, const int32_t* __restrict__ idx,
+                                                           const float* __restrict__ dl, int64_t T, int k, int E,
+                                                           int64_t d, void* __restrict__ dwr, float* __restrict__ db) {
+  constexpr int EB = 16;
+  __shared__ float acc[EB][256];
+  __shared__ float dbs[EB];
+  const int tid = threadIdx.x;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + tid;
+  const int e0 = blockIdx.y * EB;
+#pragma unroll
+  for (int q = 0; q < EB; ++q) acc[q][tid] = 0.f;
+  if (tid < EB) dbs[tid] = 0.f;
+  __syncthreads();
+  for (int64_t t = 0; t < T; ++t) {
+    for (int j = 0; j < k; ++j) {
+      const int q = __builtin_amdgcn_readfirstlane(idx[t * k + j]) - e0;
+      if (q < 0 || q >= EB) continue;  // uniform across the block
+      const float c = dl[t * k + j];
+      if (i < d) {
+        const float xv = BF16 ? bf16_to_f32(static_cast<const bf16_t*>(x)[t * d + i])
+                              : static_cast<const float*>(x)[t * d + i];
+        acc[q][tid] = fmaf(c, xv, acc[q][tid]);
+      }
+      if (tid == 0 && blockIdx.x == 0) dbs[q] += c;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < EB; ++q) {
+    const int e = e0 + q;
+    if (e >= E || i >= d) continue;
+    if (BF16)
+      static_cast<bf16_t*>(dwr)[static_cast<int64_t>(e) * d + i] = f32_to_bf16(acc[q][tid]);
+    else
+      static_cast<float*>(dwr)[static_cast<int64_t>(e) * d + i] = acc[q][tid];
+  }
+  if (db && blockIdx.x == 0 && tid < EB && e0 + tid < E) db[e0 + tid] = dbs[tid];
+}
+
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = v;
+}
+
+}  // namespace
+
+hipError_t launch_transpose(const void* src, void* dst, int64_t batch, int64_t R, int64_t Cc, int64_t src_ld,
+                            int64_t dst_ld, int64_t col_off, int64_t Rp, const int32_t* valid, int64_t src_bstride,
+                            int64_t dst_bstride, bool bf16, hipStream_t s) {
+  if (batch == 0 || Cc == 0 || Rp == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(ceil_div(Cc, 64)), static_cast<unsigned>(ceil_div(Rp, 64)),
+                  static_cast<unsigned>(batch));
+  if (bf16)
+    transpose_kernel<uint16_t><<<grid, dim3(256), 0, s>>>(static_cast<const uint16_t*>(src),
+                                                          static_cast<uint16_t*>(dst), R, Cc, src_ld, dst_ld,
+                                                          col_off, Rp, valid, src_bstride, dst_bstride);
+  else
+    transpose_kernel<uint32_t><<<grid, dim3(256), 0, s>>>(static_cast<const uint32_t*>(src),
+                                                          static_cast<uint32_t*>(dst), R, Cc, src_ld, dst_ld,
+                                                          col_off, Rp, valid, src_bstride, dst_bstride);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_fwd(const void* g, const void* u, void* h, const int32_t* kept, int E, int64_t C,
+                             int64_t F, bool bf16, hipStream_t s) {
+  if (E * C == 0) return hipSuccess;
+  const int64_t VF = F * (bf16 ? 2 : 4) / 16;
+  const dim3 grid(static_cast<unsigned>(E * C));
+  if (bf16)
+    swiglu_fwd_kernel<true><<<grid, dim3(256), 0, s>>>(static_cast<const uint4*>(g), static_cast<const uint4*>(u),
+                                                       static_cast<uint4*>(h), kept, C, VF);
+  else
+    swiglu_fwd_kernel<false><<<grid, dim3(256), 0, s>>>(static_cast<const uint4*>(g), static_cast<const uint4*>(u),
+                                                        static_cast<uint4*>(h), kept, C, VF);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const void* dh, const void* g, const void* u, void* dgu, const int32_t* kept, int E,
+                             int64_t C, int64_t F, bool bf16, hipStream_t s) {
+  if (E * C == 0) return hipSuccess;
+  const int64_t VF = F * (bf16 ? 2 : 4) / 16;
+  const dim3 grid(static_cast<unsigned>(E * C));
+  const auto* a = static_cast<const uint4*>(dh);
+  const auto* b = static_cast<const uint4*>(g);
+  const auto* c = static_cast<const uint4*>(u);
+  auto* o = static_cast<uint4*>(dgu);
+  if (bf16)
+    swiglu_bwd_kernel<true><<<grid, dim3(256), 0, s>>>(a, b, c, o, kept, C, VF);
+  else
+    swiglu_bwd_kernel<false><<<grid, dim3(256), 0, s>>>(a, b, c, o, kept, C, VF);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(const void* dout, const void* y, const int32_t* idx, const float* w,
+                              const int32_t* slot, int64_t T, int64_t d, int k, int64_t C, bool bf16, void* dy,
+                              float* dl, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (k > 32) return hipErrorInvalidValue;
+  const int64_t V = d * (bf16 ? 2 : 4) / 16;
+  const dim3 grid(static_cast<unsigned>(ceil_div(T, 4)));
+  const auto* a = static_cast<const uint4*>(dout);
+  const auto* b = static_cast<const uint4*>(y);
+  auto* o = static_cast<uint4*>(dy);
+  if (bf16)
+    combine_bwd_kernel<true><<<grid, dim3(256), 0, s>>>(a, b, idx, w, slot, T, k, C, V, o, dl);
+  else
+    combine_bwd_kernel<false><<<grid, dim3(256), 0, s>>>(a, b, idx, w, slot, T, k, C, V, o, dl);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_dx(const void* dout, const void* dX, const void* wr, const int32_t* idx, const float* dl,
+                            const int32_t* slot, int64_t T, int64_t d, int k, int64_t C, bool bf16, void* dx,
+                            hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int64_t V = d * (bf16 ? 2 : 4) / 16;
+  const dim3 grid(static_cast<unsigned>(ceil_div(T, 4)));
+  const auto* a = static_cast<const uint4*>(dout);
+  const auto* b = static_cast<const uint4*>(dX);
+  const auto* c = static_cast<const uint4*>(wr);
+  auto* o = static_cast<uint4*>(dx);
+  if (bf16)
+    gather_dx_kernel<true><<<grid, dim3(256), 0, s>>>(a, b, c, idx, dl, slot, T, k, C, V, o);
+  else
+    gather_dx_kernel<false><<<grid, dim3(256), 0, s>>>(a, b, c, idx, dl, slot, T, k, C, V, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_wgrad(const void* x, const int32_t* idx, const float* dl, int64_t T, int k, int E,
+                               int64_t d, bool bf16, void* dwr, float* db, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(ceil_div(d, 256)), static_cast<unsigned>(ceil_div(E, 16)));
+  if (bf16)
+    router_wgrad_kernel<true><<<grid, dim3(256), 0, s>>>(x, idx, dl, T, k, E, d, dwr, db);
+  else
+    router_wgrad_kernel<false><<<grid, dim3(256), 0, s>>>(x, idx, dl, T, k, E, d, dwr, db);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  fill_i32_kernel<<<dim3(static_cast<unsigned>(std::min<int64_t>(ceil_div(n, 256), 1024))), dim3(256), 0, s>>>(p, n, v);
+  return hipGetLastError();
+}
+
+}  // namespace moe

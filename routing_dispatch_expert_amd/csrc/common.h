@@ -85,6 +85,30 @@ hipError_t launch_gemm_down(const void* h, const int32_t* kept, const int32_t* m
                             const void* wd, int E, int64_t C, int64_t d, int64_t d_ff, bool bf16,
                             void* y, hipStream_t s);
 
+// ---- backward (backward.hip) ----
+// dst[b][c][col_off + r] = src[b][r][c] for r < valid[b] (or R), 0 for r < Rp.
+hipError_t launch_transpose(const void* src, void* dst, int64_t batch, int64_t R, int64_t Cc, int64_t src_ld,
+                            int64_t dst_ld, int64_t col_off, int64_t Rp, const int32_t* valid, int64_t src_bstride,
+                            int64_t dst_bstride, bool bf16, hipStream_t s);
+// h = silu(g) u on kept rows of [E][C][F].
+hipError_t launch_swiglu_fwd(const void* g, const void* u, void* h, const int32_t* kept, int E, int64_t C,
+                             int64_t F, bool bf16, hipStream_t s);
+// dgu [E][C][2F] = [dh u silu'(g) | dh silu(g)] on kept rows.
+hipError_t launch_swiglu_bwd(const void* dh, const void* g, const void* u, void* dgu, const int32_t* kept, int E,
+                             int64_t C, int64_t F, bool bf16, hipStream_t s);
+// dy rows of kept copies = w dout; dl [T][k] = gate gradients.
+hipError_t launch_combine_bwd(const void* dout, const void* y, const int32_t* idx, const float* w,
+                              const int32_t* slot, int64_t T, int64_t d, int k, int64_t C, bool bf16, void* dy,
+                              float* dl, hipStream_t s);
+// dx = dout + sum_j [kept] dX[e_j, s_j] + sum_j dl_j Wr[e_j].
+hipError_t launch_gather_dx(const void* dout, const void* dX, const void* wr, const int32_t* idx, const float* dl,
+                            const int32_t* slot, int64_t T, int64_t d, int k, int64_t C, bool bf16, void* dx,
+                            hipStream_t s);
+// dWr [E][d] (dtype) and db [E] fp32 (may be NULL) from dl and x.
+hipError_t launch_router_wgrad(const void* x, const int32_t* idx, const float* dl, int64_t T, int k, int E,
+                               int64_t d, bool bf16, void* dwr, float* db, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+
 // ---- combine (combine.hip) ----
 hipError_t launch_combine(const void* x, const void* y, const int32_t* idx, const float* w,
                           const int32_t* slot, int64_t T, int64_t d, int k, int64_t C, bool bf16,

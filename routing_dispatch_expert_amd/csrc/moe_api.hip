@@ -167,6 +167,49 @@ LayerPlan plan_layer(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E, in
   return p;
 }
 
+// Backward workspace: the forward plan (routing, buckets X, h, y) plus the
+// recomputed g and u, the gradient rows and the transposed operands of the
+// gradient GEMMs. Kp = C rounded up to 64: the row count the weight gradients
+// contract over (rows past kept are zero in the transposed copies).
+struct BackPlan {
+  LayerPlan f;
+  void *g, *u, *dy, *dh, *dgu, *dX, *WdT, *WguT, *dyT, *hT, *dgT, *duT, *XT;
+  float* dl;
+  int32_t *kfull_d, *kfull_f, *mtile_d, *mtile_f;
+  int64_t Kp;
+  size_t bytes;
+};
+
+BackPlan plan_backward(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k, int64_t C, int32_t P,
+                       int eb) {
+  BackPlan b;
+  b.f = plan_layer(ws, T, d, d_ff, E, k, C, P, eb);
+  Carver c(ws ? static_cast<char*>(ws) + b.f.bytes : nullptr);
+  const size_t EC = static_cast<size_t>(E) * C;
+  b.Kp = moe::ceil_div(C, 64) * 64;
+  const size_t EKp = static_cast<size_t>(E) * b.Kp;
+  b.g = c.take<char>(EC * d_ff * eb);
+  b.u = c.take<char>(EC * d_ff * eb);
+  b.dl = c.take<float>(static_cast<size_t>(T) * k);
+  b.dy = c.take<char>(EC * d * eb);
+  b.dh = c.take<char>(EC * d_ff * eb);
+  b.dgu = c.take<char>(EC * 2 * d_ff * eb);
+  b.dX = c.take<char>(EC * d * eb);
+  b.WdT = c.take<char>(static_cast<size_t>(E) * d_ff * d * eb);
+  b.WguT = c.take<char>(static_cast<size_t>(E) * d * 2 * d_ff * eb);
+  b.dyT = c.take<char>(EKp * d * eb);
+  b.hT = c.take<char>(EKp * d_ff * eb);
+  b.dgT = c.take<char>(EKp * d_ff * eb);
+  b.duT = c.take<char>(EKp * d_ff * eb);
+  b.XT = c.take<char>(EKp * d * eb);
+  b.kfull_d = c.take<int32_t>(E);
+  b.kfull_f = c.take<int32_t>(E);
+  b.mtile_d = c.take<int32_t>(static_cast<size_t>(E) + 1);
+  b.mtile_f = c.take<int32_t>(static_cast<size_t>(E) + 1);
+  b.bytes = b.f.bytes + align_up(c.off);
+  return b;
+}
+
 template <class T>
 T* pick(T* user, T* fallback) {
   return user ? user : fallback;
@@ -289,6 +332,114 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
   MOE_HIP_TRY(stage_mark(MOE_STAGE_COMBINE, false, s), "event");
   MOE_HIP_TRY(moe::launch_combine(x, p.y, idx, w, slot, T, d, k, C, bf16, out, s), "combine");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_COMBINE, true, s), "event");
+  return MOE_OK;
+}
+
+int moe_backward_workspace_size(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k, float cf, int32_t P,
+                                moe_dtype_t dtype, size_t* bytes) {
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  int64_t C;
+  const int st = check_layer_shape(T, d, d_ff, E, k, cf, P, dtype, &C);
+  if (st != MOE_OK) return st;
+  *bytes = plan_backward(nullptr, T, d, d_ff, E, k, C, P, elem_bytes(dtype)).bytes;
+  return MOE_OK;
+}
+
+int moe_layer_backward(const void* x, const void* W_router, const float* router_bias, const void* W_gate,
+                       const void* W_up, const void* W_down, const void* dout, int64_t T, int64_t d, int64_t d_ff,
+                       int32_t E, int32_t k, float cf, int32_t P, int32_t max_ranks, moe_dtype_t dtype, void* dx,
+                       void* dW_router, float* d_bias, void* dW_gate, void* dW_up, void* dW_down,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int64_t C;
+  int st = check_layer_shape(T, d, d_ff, E, k, cf, P, dtype, &C);
+  if (st != MOE_OK) return st;
+  if ((st = check_rank_limit(E, k, P, max_ranks)) != MOE_OK) return st;
+  if (!x || !W_router || !W_gate || !W_up || !W_down || !dout || !dx || !dW_router || !dW_gate || !dW_up ||
+      !dW_down)
+    return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
+  const int eb = elem_bytes(dtype);
+  const size_t row_bytes = static_cast<size_t>(T * d * eb);
+  if (overlaps(dx, row_bytes, x, row_bytes) || overlaps(dx, row_bytes, dout, row_bytes))
+    return fail(MOE_ERR_INVALID_ARG, "dx overlaps x or dout");
+  const int64_t Kp = moe::ceil_div(C, 64) * 64;
+  // the gradient GEMMs: rows d or d_ff contracting over Kp rows, and 2 d_ff
+  if ((st = check_expert_extent(d, Kp, d_ff)) != MOE_OK || (st = check_expert_extent(d_ff, Kp, d)) != MOE_OK ||
+      (st = check_expert_extent(C, d, 2 * d_ff)) != MOE_OK)
+    return st;
+  if (T == 0) return MOE_OK;
+  const BackPlan need = plan_backward(nullptr, T, d, d_ff, E, k, C, P, eb);
+  if (!workspace || workspace_bytes < need.bytes || reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need.bytes);
+  BackPlan b = plan_backward(workspace, T, d, d_ff, E, k, C, P, eb);
+  const LayerPlan& p = b.f;
+  const bool bf16 = dtype == MOE_DTYPE_BF16;
+  auto s = static_cast<hipStream_t>(stream);
+  const int64_t nt = moe::ceil_div(T, moe::kTileTokens);
+  const int bm = moe::grouped_gemm_bm(bf16, C);
+  const int64_t F = d_ff;
+
+  // 1. the forward again: routing, buckets X, g, u, h, y
+  const int splits = moe::router_splits(T, d, E, bf16);
+  const bool fused_hist = moe::route_builds_histogram(k);
+  MOE_HIP_TRY(moe::launch_router_logits(x, W_router, T, d, E, bf16, splits, p.logits, s), "router logits");
+  MOE_HIP_TRY(moe::launch_route(p.logits, splits, router_bias, T, E, k, nullptr, p.idx, p.w,
+                                fused_hist ? p.tile_cnt : nullptr, P, max_ranks, s),
+              "route");
+  if (!fused_hist) MOE_HIP_TRY(moe::launch_tile_hist(p.idx, T, k, E, p.tile_cnt, s), "tile histogram");
+  MOE_HIP_TRY(moe::launch_scan(p.tile_cnt, nt, E, C, P, d * eb, k, T, p.tile_off, p.routed, p.kept, p.send,
+                               p.totals, bm, p.mtile, nullptr, s),
+              "scan");
+  MOE_HIP_TRY(moe::launch_slots(p.idx, p.tile_off, T, k, E, C, p.slot, nullptr, p.totals, s), "slots");
+  MOE_HIP_TRY(moe::launch_scatter_rows(x, p.idx, p.slot, T, k, C, d * eb, p.buckets, s), "scatter");
+  // g = X Wg^T and u = X Wu^T (the plain row-tile GEMM: N = d_ff, K = d)
+  MOE_HIP_TRY(moe::launch_gemm_down(p.buckets, p.kept, p.mtile, W_gate, E, C, F, d, bf16, b.g, s), "gemm g");
+  MOE_HIP_TRY(moe::launch_gemm_down(p.buckets, p.kept, p.mtile, W_up, E, C, F, d, bf16, b.u, s), "gemm u");
+  MOE_HIP_TRY(moe::launch_swiglu_fwd(b.g, b.u, p.h, p.kept, E, C, F, bf16, s), "swiglu");
+  MOE_HIP_TRY(moe::launch_gemm_down(p.h, p.kept, p.mtile, W_down, E, C, d, F, bf16, p.y, s), "gemm y");
+
+  // 2. combine backward: dy = w dout on kept rows, dl = gate gradients
+  MOE_HIP_TRY(moe::launch_combine_bwd(dout, p.y, p.idx, p.w, p.slot, T, d, k, C, bf16, b.dy, b.dl, s),
+              "combine backward");
+  // 3. dh = dy Wd (B = Wd^T, [E][d_ff][d]); dg, du
+  MOE_HIP_TRY(moe::launch_transpose(W_down, b.WdT, E, d, F, F, d, 0, d, nullptr, d * F, F * d, bf16, s),
+              "transpose W_down");
+  MOE_HIP_TRY(moe::launch_gemm_down(b.dy, p.kept, p.mtile, b.WdT, E, C, F, d, bf16, b.dh, s), "gemm dh");
+  MOE_HIP_TRY(moe::launch_swiglu_bwd(b.dh, b.g, b.u, b.dgu, p.kept, E, C, F, bf16, s), "swiglu backward");
+  // 4. dX = [dg | du] [Wg ; Wu] (B = [Wg^T | Wu^T], [E][d][2 d_ff])
+  MOE_HIP_TRY(moe::launch_transpose(W_gate, b.WguT, E, F, d, d, 2 * F, 0, F, nullptr, F * d, d * 2 * F, bf16, s),
+              "transpose W_gate");
+  MOE_HIP_TRY(moe::launch_transpose(W_up, b.WguT, E, F, d, d, 2 * F, F, F, nullptr, F * d, d * 2 * F, bf16, s),
+              "transpose W_up");
+  MOE_HIP_TRY(moe::launch_gemm_down(b.dgu, p.kept, p.mtile, b.WguT, E, C, d, 2 * F, bf16, b.dX, s), "gemm dX");
+  // 5. router gradients, then dx = dout + the expert paths + the router path
+  MOE_HIP_TRY(moe::launch_router_wgrad(x, p.idx, b.dl, T, k, E, d, bf16, dW_router, d_bias, s), "router wgrad");
+  MOE_HIP_TRY(moe::launch_gather_dx(dout, b.dX, W_router, p.idx, b.dl, p.slot, T, d, k, C, bf16, dx, s),
+              "gather dx");
+  // 6. weight gradients over each expert's kept rows: dWd = dy^T h, dWg = dg^T X,
+  //    dWu = du^T X, as row-tile GEMMs of the transposed operands (M = d or
+  //    d_ff rows for every expert, K = Kp)
+  MOE_HIP_TRY(moe::launch_transpose(b.dy, b.dyT, E, C, d, d, b.Kp, 0, b.Kp, p.kept, C * d, d * b.Kp, bf16, s),
+              "transpose dy");
+  MOE_HIP_TRY(moe::launch_transpose(p.h, b.hT, E, C, F, F, b.Kp, 0, b.Kp, p.kept, C * F, F * b.Kp, bf16, s),
+              "transpose h");
+  MOE_HIP_TRY(moe::launch_transpose(b.dgu, b.dgT, E, C, F, 2 * F, b.Kp, 0, b.Kp, p.kept, C * 2 * F, F * b.Kp, bf16,
+                                    s),
+              "transpose dg");
+  MOE_HIP_TRY(moe::launch_transpose(static_cast<char*>(b.dgu) + F * eb, b.duT, E, C, F, 2 * F, b.Kp, 0, b.Kp,
+                                    p.kept, C * 2 * F, F * b.Kp, bf16, s),
+              "transpose du");
+  MOE_HIP_TRY(moe::launch_transpose(p.buckets, b.XT, E, C, d, d, b.Kp, 0, b.Kp, p.kept, C * d, d * b.Kp, bf16, s),
+              "transpose X");
+  MOE_HIP_TRY(moe::launch_fill_i32(b.kfull_d, E, static_cast<int32_t>(d), s), "fill");
+  MOE_HIP_TRY(moe::launch_fill_i32(b.kfull_f, E, static_cast<int32_t>(F), s), "fill");
+  MOE_HIP_TRY(moe::launch_mtile_map(b.kfull_d, E, moe::grouped_gemm_bm(bf16, d), b.mtile_d, s), "tile map");
+  MOE_HIP_TRY(moe::launch_mtile_map(b.kfull_f, E, moe::grouped_gemm_bm(bf16, F), b.mtile_f, s), "tile map");
+  MOE_HIP_TRY(moe::launch_gemm_down(b.dyT, b.kfull_d, b.mtile_d, b.hT, E, d, F, b.Kp, bf16, dW_down, s),
+              "gemm dW_down");
+  MOE_HIP_TRY(moe::launch_gemm_down(b.dgT, b.kfull_f, b.mtile_f, b.XT, E, F, d, b.Kp, bf16, dW_gate, s),
+              "gemm dW_gate");
+  MOE_HIP_TRY(moe::launch_gemm_down(b.duT, b.kfull_f, b.mtile_f, b.XT, E, F, d, b.Kp, bf16, dW_up, s),
+              "gemm dW_up");
   return MOE_OK;
 }
 
