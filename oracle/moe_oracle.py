@@ -47,6 +47,7 @@ __all__ = [
     "decode", "capacity", "router_logits", "topk_experts", "rank_limited_experts", "gate_weights",
     "assign_slots", "dispatch_buckets", "send_counts", "expert_hidden", "expert_mlp",
     "combine", "routing_stats", "dispatch_bytes", "layer_forward", "layer_backward",
+    "layer_backward_sample",
 ]
 
 
@@ -475,3 +476,55 @@ def layer_backward(x, wr, expert_weights, dout, T, d, d_ff, E, k, cf, dtype, P=1
     dx += dl_full @ decode(np.asarray(wr), dtype)
     return {"dx": dx, "dwr": dl_full.T @ x64, "db": dl_full.sum(axis=0), "dwg": dwg, "dwu": dwu,
             "dwd": dwd, "dw": dw, "dl": dl, "idx": idx, "w": w, "slot": slot}
+
+
+def layer_backward_sample(x, wr, expert_weights, dout, T, d, d_ff, E, k, cf, dtype, P=1, bias=None,
+                          max_ranks=0, tokens=(), cols=()):
+    """Chosen outputs of layer_backward, each computed on its own (for layers
+    too large for the dense form): dx rows of `tokens`, and for each (e, f) in
+    `cols` the column dWd[e][:, f] and the rows dWg[e][f, :], dWu[e][f, :].
+    Same formulas and readings as layer_backward; routing is computed for all
+    T tokens. Experts are visited one at a time, so only one expert's weights
+    are held in fp64. Returns {"dx": {t: row}, "dwd": {(e, f): col},
+    "dwg": {...}, "dwu": {...}}.
+    """
+    fwd = layer_forward(x, wr, expert_weights, T, d, d_ff, E, k, cf, dtype, P=P, bias=bias,
+                        tokens=np.arange(0), max_ranks=max_ranks)
+    idx, w, slot = fwd["idx"], np.asarray(fwd["w"], dtype=np.float64), fwd["slot"]
+    x = np.asarray(x)
+    dout = np.asarray(dout)
+    tok = np.asarray(list(tokens), dtype=np.int64)
+    xt, gt = decode(x[tok], dtype), decode(dout[tok], dtype)
+    dw = np.zeros((tok.size, k))
+    dxe = np.zeros((tok.size, d))
+    sub_idx, sub_slot = idx[tok], slot[tok]
+    res = {"dx": {}, "dwd": {}, "dwg": {}, "dwu": {}}
+    for e in sorted(set(np.unique(sub_idx[sub_slot >= 0]).tolist()) | {int(c[0]) for c in cols}):
+        wg, wu, wd = (decode(a, dtype) for a in expert_weights(int(e)))
+        rows, js = np.nonzero((sub_idx == e) & (sub_slot >= 0))
+        if rows.size:
+            gpre, upre = xt[rows] @ wg.T, xt[rows] @ wu.T
+            sg = 1.0 / (1.0 + np.exp(-gpre))
+            y = (gpre * sg * upre) @ wd.T
+            dw[rows, js] = np.sum(gt[rows] * y, axis=1)
+            dh = (w[tok[rows], js][:, None] * gt[rows]) @ wd
+            dg = dh * upre * sg * (1.0 + gpre * (1.0 - sg))
+            du = dh * gpre * sg
+            np.add.at(dxe, rows, dg @ wg + du @ wu)
+        for ce, f in cols:
+            if ce != e:
+                continue
+            r2, j2 = np.nonzero((idx == e) & (slot >= 0))
+            X = decode(x[r2], dtype)
+            dy = w[r2, j2][:, None] * decode(dout[r2], dtype)
+            gcol, ucol = X @ wg[f], X @ wu[f]
+            s2 = 1.0 / (1.0 + np.exp(-gcol))
+            res["dwd"][(int(e), int(f))] = dy.T @ (gcol * s2 * ucol)
+            dh2 = dy @ wd[:, f]
+            res["dwg"][(int(e), int(f))] = (dh2 * ucol * s2 * (1.0 + gcol * (1.0 - s2))) @ X
+            res["dwu"][(int(e), int(f))] = (dh2 * gcol * s2) @ X
+    wr64 = decode(np.asarray(wr), dtype)
+    for n, t in enumerate(tok):
+        dl = w[t] * (dw[n] - np.sum(w[t] * dw[n]))
+        res["dx"][int(t)] = gt[n] + dxe[n] + dl @ wr64[idx[t]]
+    return res

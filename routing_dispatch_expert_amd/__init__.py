@@ -292,10 +292,10 @@ def forward(x, W_router, W_gate, W_up, W_down, k, cf, P=1, router_bias=None, str
 
 
 def backward(x, W_router, W_gate, W_up, W_down, dout, k, cf, P=1, router_bias=None, stream=None, max_ranks=0,
-             workspace=None):
+             workspace=None, want_d_bias=False):
     """Gradients of the layer for dout on torch device tensors; returns a dict
-    dx, dW_router, d_bias (fp32, when router_bias is given), dW_gate, dW_up,
-    dW_down, workspace."""
+    dx, dW_router, d_bias (fp32, when router_bias is given or want_d_bias),
+    dW_gate, dW_up, dW_down, workspace."""
     import torch
     T, d = x.shape
     E = W_router.shape[0]
@@ -308,7 +308,8 @@ def backward(x, W_router, W_gate, W_up, W_down, dout, k, cf, P=1, router_bias=No
         _require(router_bias, "router_bias", torch.float32, (E,))
     res = {"dx": torch.empty_like(x), "dW_router": torch.empty_like(W_router), "dW_gate": torch.empty_like(W_gate),
            "dW_up": torch.empty_like(W_up), "dW_down": torch.empty_like(W_down),
-           "d_bias": None if router_bias is None else torch.empty(E, dtype=torch.float32, device=x.device)}
+           "d_bias": (torch.empty(E, dtype=torch.float32, device=x.device)
+                      if router_bias is not None or want_d_bias else None)}
     nbytes = moe_backward_workspace_size(T, d, d_ff, E, k, cf, P, dt)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)

@@ -63,3 +63,71 @@ def test_backward_small_shapes_every_element(case):
     tol = 2e-2 if dt == "bf16" else 1e-4
     for key, v in errs.items():
         assert v <= tol, (key, v)
+
+
+# ---------------------------------------------------------- named workloads ---
+
+FULL = ["mixtral_prefill", "zipf_skew_drops", "deepseek_v3_decode"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_backward_named_workload_sampled(name):
+    from tests.gpu_util import DeviceWeights
+    wl = moe_inputs.workload(name)
+    dt = wl.dtype
+    say(f"backward workload {name}: T={wl.T} d={wl.d} E={wl.E} k={wl.k} d_ff={wl.d_ff}")
+    host, dev = DeviceWeights.get(wl)
+    dout = wl.grad_out(1)
+    b = None if wl.bias_vec is None else torch.from_numpy(wl.bias_vec).cuda()
+    r = moe.backward(to_dev(wl.x, dt), to_dev(wl.wr, dt), *dev, to_dev(dout, dt), wl.k, wl.cf, P=wl.P,
+                     router_bias=b, max_ranks=wl.max_ranks, want_d_bias=True)
+    torch.cuda.synchronize()
+    del r["workspace"]
+    torch.cuda.empty_cache()
+    route = oracle.layer_forward(wl.x, wl.wr, lambda e: (host[0][e], host[1][e], host[2][e]), wl.T, wl.d, wl.d_ff,
+                                 wl.E, wl.k, wl.cf, dt, P=wl.P, bias=wl.bias_vec, tokens=np.arange(0),
+                                 max_ranks=wl.max_ranks)
+    rng = np.random.default_rng(wl.seed + 17)
+    T = wl.T
+    tok = set(range(min(3, T))) | {T - 1} | set(rng.choice(T, size=min(8 if T > 64 else T, T), replace=False).tolist())
+    fully = np.nonzero(np.all(route["slot"] < 0, axis=1))[0]
+    if fully.size:
+        tok |= set(rng.choice(fully, size=min(3, fully.size), replace=False).tolist())
+    tok = sorted(tok)
+    kept = route["kept"]
+    touched = np.nonzero(kept > 0)[0]
+    experts = sorted({int(touched[np.argmax(kept[touched])]), int(touched[np.argmin(kept[touched])]),
+                      int(rng.choice(touched))})
+    cols = [(e, int(f)) for e in experts for f in rng.choice(wl.d_ff, size=2, replace=False)]
+    ref = oracle.layer_backward_sample(wl.x, wl.wr, lambda e: (host[0][e], host[1][e], host[2][e]), dout, wl.T,
+                                       wl.d, wl.d_ff, wl.E, wl.k, wl.cf, dt, P=wl.P, bias=wl.bias_vec,
+                                       max_ranks=wl.max_ranks, tokens=tok, cols=cols)
+    dx = bits_to_f64(to_host(r["dx"], dt), dt)
+    worst = 0.0
+    for t in tok:
+        e_ = _rel(dx[t], ref["dx"][t])
+        worst = max(worst, e_)
+        if np.all(route["slot"][t] < 0):  # fully dropped: dx = dout bit for bit
+            assert np.array_equal(to_host(r["dx"], dt)[t].view(np.uint8), np.asarray(dout[t]).view(np.uint8))
+    say(f"  dx over {len(tok)} tokens: max rel err {worst:.2e}")
+    assert worst <= 2e-2
+    # A weight-gradient row can be small because its dh is a near-cancelling sum
+    # over d: dy is stored in bf16, so dh carries an absolute error of about
+    # 2^-9 sqrt(sum_i (dy_i Wd_if)^2) whatever its size. Each sampled row is
+    # therefore measured against the largest magnitude among the sampled rows
+    # of the same gradient, not against its own.
+    for key, name_ in (("dwd", "dW_down"), ("dwg", "dW_gate"), ("dwu", "dW_up")):
+        scale = max(np.abs(ref[key][c]).max() for c in cols)
+        for (e, f) in cols:
+            g = r[name_][e, :, f] if key == "dwd" else r[name_][e, f, :]
+            err = np.abs(bits_to_f64(to_host(g, dt), dt) - ref[key][(e, f)]).max() / scale
+            assert err <= 2e-2, (key, e, f, err)
+    # properties of the gate gradients at any size: sum_j dl[t, j] = 0 for every
+    # token, so db and every column of dW_router sum to zero over the experts
+    db = r["d_bias"].cpu().numpy().astype(np.float64)
+    gwr = bits_to_f64(to_host(r["dW_router"], dt), dt)
+    assert abs(db.sum()) <= 1e-3 * np.abs(db).sum() + 1e-6
+    col = np.abs(gwr.sum(axis=0))
+    assert np.all(col <= 2 ** -7 * np.abs(gwr).sum(axis=0) + 1e-6)
+    if name == "deepseek_v3_decode":
+        DeviceWeights.clear()

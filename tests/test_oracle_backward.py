@@ -109,3 +109,24 @@ def test_gate_gradients_sum_to_zero_per_token():
     g = _backward(case, p, dout)
     assert np.allclose(g["dl"].sum(axis=1), 0.0, atol=1e-12)
     assert np.allclose(g["db"].sum(), 0.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("ci", [0, 1, 4])
+def test_sampled_backward_equals_the_dense_one(ci):
+    case = CASES[ci]
+    T, d, E, k, f, cf, P, M, _ = case
+    p, dout = _draw(case, 700 + ci)
+    g = _backward(case, p, dout)
+    ew = lambda e: (p["wg"][e], p["wu"][e], p["wd"][e])  # noqa: E731
+    cols = [(e, c) for e in range(E) for c in range(f)]
+    s = oracle.layer_backward_sample(p["x"], p["wr"], ew, dout, T, d, f, E, k, cf, "f64", P=P, bias=p["b"],
+                                     max_ranks=M, tokens=range(T), cols=cols)
+    # the dense form rounds its scores to fp32 only in the default mode: compare that mode
+    gd = oracle.layer_backward(p["x"], p["wr"], ew, dout, T, d, f, E, k, cf, "f64", P=P, bias=p["b"], max_ranks=M)
+    for t in range(T):
+        assert np.allclose(s["dx"][t], gd["dx"][t], rtol=1e-12, atol=1e-12)
+    for (e, c) in cols:
+        assert np.allclose(s["dwd"][(e, c)], gd["dwd"][e][:, c], rtol=1e-12, atol=1e-12)
+        assert np.allclose(s["dwg"][(e, c)], gd["dwg"][e][c], rtol=1e-12, atol=1e-12)
+        assert np.allclose(s["dwu"][(e, c)], gd["dwu"][e][c], rtol=1e-12, atol=1e-12)
+    assert np.allclose(g["dx"], gd["dx"], rtol=1e-4, atol=1e-4)  # exact vs fp32-rounded scores: close
