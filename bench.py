@@ -11,6 +11,10 @@ Prints one JSON line: routed tokens/s per layer (whole job), per-stage GPU
 times from HIP events recorded by the library around each stage, the
 roofline of the dominant kernel, and the CPU oracle timed on a bounded sample
 of the same workload.
+
+With --backward a step is one call of moe_layer_backward instead (the
+gradients of x, the router and the expert weights for a seeded dout), and the
+line reports backward tokens/s.
 """
 from __future__ import annotations
 
@@ -43,6 +47,7 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens whose output the oracle computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-stage event loop")
+    ap.add_argument("--backward", action="store_true", help="time moe_layer_backward instead of the forward")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first copy a buffer of this many MiB on the device (a reference kernel of known "
                          "traffic for hardware counters)")
@@ -102,6 +107,92 @@ def cpu_baseline(wl, host_w, sample: int):
                       f"{wl.T}), fp64 numpy, median of 3 runs: {dt:.1f} s each ({sum(times):.1f} s total)"}
 
 
+def run_backward(args, wl, moe, torch, np, dev, to_dev, host_w):
+    """One step = moe_layer_backward over the workload, inputs resident in HBM."""
+    x, wr = to_dev(wl.x), to_dev(wl.wr)
+    wg, wu, wd = (to_dev(a) for a in host_w)
+    dout = to_dev(wl.grad_out(1))
+    bias = None if wl.bias_vec is None else torch.from_numpy(wl.bias_vec).to(dev)
+    T, d, d_ff, E, k, cf, P = wl.T, wl.d, wl.d_ff, wl.E, wl.k, wl.cf, wl.P
+    outs = {"dx": torch.empty_like(x), "dW_router": torch.empty_like(wr), "dW_gate": torch.empty_like(wg),
+            "dW_up": torch.empty_like(wu), "dW_down": torch.empty_like(wd),
+            "d_bias": torch.empty(E, dtype=torch.float32, device=dev)}
+    ws_bytes = moe.moe_backward_workspace_size(T, d, d_ff, E, k, cf, P, wl.dtype)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.moe_layer_backward(x, wr, bias, wg, wu, wd, dout, T, d, d_ff, E, k, cf, P, wl.max_ranks, wl.dtype,
+                               outs["dx"], outs["dW_router"], outs["d_bias"], outs["dW_gate"], outs["dW_up"],
+                               outs["dW_down"], ws, ws_bytes, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1) / args.steps
+    print(f"[bench] backward: timed {args.steps} steps: {wall * 1e3 / args.steps:.3f} ms/step wall, "
+          f"{gpu_ms:.3f} ms/step GPU", file=sys.stderr, flush=True)
+    import oracle
+    r = oracle.layer_forward(wl.x, wl.wr, lambda e: (host_w[0][e], host_w[1][e], host_w[2][e]), T, d, d_ff, E, k,
+                             cf, wl.dtype, P=P, bias=wl.bias_vec, tokens=np.arange(0), max_ranks=wl.max_ranks)
+    n_kept = int(r["kept"].sum())
+    algo = 12 * n_kept * d * d_ff  # dh, dX (two), dWd, dWg, dWu: 2 N d d_ff flop each
+    done = algo + 6 * n_kept * d * d_ff  # plus the recomputed forward GEMMs
+    tf = algo / gpu_ms / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        S = min(args.cpu_sample, T, 1024)  # the fp64 backward costs about 3x the forward per token
+        sub = moe_inputs_sample(wl, S)
+        print(f"[bench] timing the CPU oracle backward on {S} tokens", file=sys.stderr, flush=True)
+        times = []
+        for _ in range(3):
+            t1 = time.perf_counter()
+            oracle.layer_backward(sub["x"], wl.wr, lambda e: (host_w[0][e], host_w[1][e], host_w[2][e]), sub["dout"],
+                                  S, d, d_ff, E, k, cf, wl.dtype, P=P, bias=wl.bias_vec, max_ranks=wl.max_ranks)
+            times.append(time.perf_counter() - t1)
+        dt = sorted(times)[1]
+        cpu = {"value": round(S / dt, 3), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+               "sample": f"backward of the first {S} of {T} tokens as a layer of their own (capacity for {S} "
+                         f"tokens), fp64 numpy, median of 3 runs: {dt:.1f} s each"}
+    line = {
+        "metric": "backward tokens/s per MoE layer (gradients of x, router and expert weights)",
+        "value": round(T * args.steps / wall, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded Gaussian inputs, upstream gradient and random-init weights of the named shape)",
+        "config": {"workload": wl.name, "T": T, "d": d, "E": E, "k": k, "d_ff": d_ff, "cf": cf, "P": P,
+                   "max_ranks": wl.max_ranks, "N_kept": n_kept},
+        "gpu_ms_per_step": round(gpu_ms, 4),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_TFLOPS[wl.dtype], "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_TFLOPS[wl.dtype], 4), "traffic": None,
+                     "kernel": "whole backward step (expert-gradient flops over step time)",
+                     "algo_flops_per_step": algo, "executed_gemm_flops_per_step": done},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def moe_inputs_sample(wl, S):
+    """The first S tokens (and their upstream gradient) as a layer input."""
+    return {"x": wl.x[:S], "dout": wl.grad_out(1)[:S]}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1]))
+    except Exception:  # pragma: no cover
+        return 1
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -128,6 +219,9 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     host_w = wl.all_expert_weights()
+    if args.backward:
+        run_backward(args, wl, moe, torch, np, dev, to_dev, host_w)
+        return
     x, wr = to_dev(wl.x), to_dev(wl.wr)
     wg, wu, wd = (to_dev(a) for a in host_w)
     bias = None if wl.bias_vec is None else torch.from_numpy(wl.bias_vec).to(dev)

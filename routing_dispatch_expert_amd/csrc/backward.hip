@@ -212,24 +212,30 @@ __global__ __launch_bounds__(256) void gather_dx_kernel(const uint4* __restrict_
 
 // ---------------------------------------------------------------------------
 // Router weight gradient: dWr[e][i] = sum_t sum_j [idx[t,j] = e] dl[t,j] x[t][i]
-// (t, then j ascending), and db[e] the same without x. A block takes 16
-// experts x 256 columns; its accumulators live in LDS, one column per thread.
+// and db[e] the same without x. Tokens are split into chunks (grid z): a
+// block takes 16 experts x 256 columns of one chunk, accumulates in LDS (one
+// column per thread, t then j ascending) and writes fp32 partials; a second
+// kernel sums the chunks in order and rounds once. Deterministic.
 // ---------------------------------------------------------------------------
 template <bool BF16>
-__global__ __launch_bounds__(256) void router_wgrad_kernel(const void* __restrict__ x, const int32_t* __restrict__ idx,
-                                                           const float* __restrict__ dl, int64_t T, int k, int E,
-                                                           int64_t d, void* __restrict__ dwr, float* __restrict__ db) {
+__global__ __launch_bounds__(256) void router_wgrad_part_kernel(const void* __restrict__ x,
+                                                                const int32_t* __restrict__ idx,
+                                                                const float* __restrict__ dl, int64_t T, int64_t tchunk,
+                                                                int k, int E, int64_t d, float* __restrict__ part,
+                                                                float* __restrict__ dbpart) {
   constexpr int EB = 16;
   __shared__ float acc[EB][256];
   __shared__ float dbs[EB];
   const int tid = threadIdx.x;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + tid;
   const int e0 = blockIdx.y * EB;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.z) * tchunk;
+  const int64_t t1 = min(T, t0 + tchunk);
 #pragma unroll
   for (int q = 0; q < EB; ++q) acc[q][tid] = 0.f;
   if (tid < EB) dbs[tid] = 0.f;
   __syncthreads();
-  for (int64_t t = 0; t < T; ++t) {
+  for (int64_t t = t0; t < t1; ++t) {
     for (int j = 0; j < k; ++j) {
       const int q = __builtin_amdgcn_readfirstlane(idx[t * k + j]) - e0;
       if (q < 0 || q >= EB) continue;  // uniform across the block
@@ -243,16 +249,36 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const void* __restric
     }
   }
   __syncthreads();
+  float* pz = part + static_cast<int64_t>(blockIdx.z) * E * d;
 #pragma unroll
   for (int q = 0; q < EB; ++q) {
     const int e = e0 + q;
-    if (e >= E || i >= d) continue;
-    if (BF16)
-      static_cast<bf16_t*>(dwr)[static_cast<int64_t>(e) * d + i] = f32_to_bf16(acc[q][tid]);
-    else
-      static_cast<float*>(dwr)[static_cast<int64_t>(e) * d + i] = acc[q][tid];
+    if (e < E && i < d) pz[static_cast<int64_t>(e) * d + i] = acc[q][tid];
   }
-  if (db && blockIdx.x == 0 && tid < EB && e0 + tid < E) db[e0 + tid] = dbs[tid];
+  if (blockIdx.x == 0 && tid < EB && e0 + tid < E) dbpart[static_cast<int64_t>(blockIdx.z) * E + e0 + tid] = dbs[tid];
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void router_wgrad_sum_kernel(const float* __restrict__ part,
+                                                               const float* __restrict__ dbpart, int nchunk, int E,
+                                                               int64_t d, void* __restrict__ dwr,
+                                                               float* __restrict__ db) {
+  const int64_t n = static_cast<int64_t>(E) * d;
+  for (int64_t o = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; o < n;
+       o += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    float s = 0.f;
+    for (int z = 0; z < nchunk; ++z) s += part[static_cast<int64_t>(z) * n + o];  // chunk order
+    if (BF16)
+      static_cast<bf16_t*>(dwr)[o] = f32_to_bf16(s);
+    else
+      static_cast<float*>(dwr)[o] = s;
+  }
+  if (db && blockIdx.x == 0)
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      float s = 0.f;
+      for (int z = 0; z < nchunk; ++z) s += dbpart[static_cast<int64_t>(z) * E + e];
+      db[e] = s;
+    }
 }
 
 __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
@@ -344,13 +370,31 @@ hipError_t launch_gather_dx(const void* dout, const void* dX, const void* wr, co
   return hipGetLastError();
 }
 
+int router_wgrad_chunks(int64_t T, int E, int64_t d) {
+  // about 2048 blocks, chunks of at least 64 tokens
+  const int64_t tiles = ceil_div(d, 256) * ceil_div(E, 16);
+  const int64_t by_work = ceil_div(2048, tiles);
+  return static_cast<int>(std::max<int64_t>(1, std::min(by_work, ceil_div(T, 64))));
+}
+
 hipError_t launch_router_wgrad(const void* x, const int32_t* idx, const float* dl, int64_t T, int k, int E,
-                               int64_t d, bool bf16, void* dwr, float* db, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(ceil_div(d, 256)), static_cast<unsigned>(ceil_div(E, 16)));
+                               int64_t d, bool bf16, float* part, void* dwr, float* db, hipStream_t s) {
+  const int nz = router_wgrad_chunks(T, E, d);
+  const int64_t tchunk = ceil_div(T, nz);
+  float* dbpart = part + static_cast<int64_t>(nz) * E * d;
+  const dim3 grid(static_cast<unsigned>(ceil_div(d, 256)), static_cast<unsigned>(ceil_div(E, 16)),
+                  static_cast<unsigned>(nz));
   if (bf16)
-    router_wgrad_kernel<true><<<grid, dim3(256), 0, s>>>(x, idx, dl, T, k, E, d, dwr, db);
+    router_wgrad_part_kernel<true><<<grid, dim3(256), 0, s>>>(x, idx, dl, T, tchunk, k, E, d, part, dbpart);
   else
-    router_wgrad_kernel<false><<<grid, dim3(256), 0, s>>>(x, idx, dl, T, k, E, d, dwr, db);
+    router_wgrad_part_kernel<false><<<grid, dim3(256), 0, s>>>(x, idx, dl, T, tchunk, k, E, d, part, dbpart);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const unsigned g2 = static_cast<unsigned>(std::min<int64_t>(ceil_div(static_cast<int64_t>(E) * d, 256), 4096));
+  if (bf16)
+    router_wgrad_sum_kernel<true><<<dim3(g2), dim3(256), 0, s>>>(part, dbpart, nz, E, d, dwr, db);
+  else
+    router_wgrad_sum_kernel<false><<<dim3(g2), dim3(256), 0, s>>>(part, dbpart, nz, E, d, dwr, db);
   return hipGetLastError();
 }
 

@@ -104,9 +104,11 @@ hipError_t launch_combine_bwd(const void* dout, const void* y, const int32_t* id
 hipError_t launch_gather_dx(const void* dout, const void* dX, const void* wr, const int32_t* idx, const float* dl,
                             const int32_t* slot, int64_t T, int64_t d, int k, int64_t C, bool bf16, void* dx,
                             hipStream_t s);
-// dWr [E][d] (dtype) and db [E] fp32 (may be NULL) from dl and x.
+// dWr [E][d] (dtype) and db [E] fp32 (may be NULL) from dl and x; part is fp32
+// scratch of router_wgrad_chunks() * E * (d + 1) floats.
+int router_wgrad_chunks(int64_t T, int E, int64_t d);
 hipError_t launch_router_wgrad(const void* x, const int32_t* idx, const float* dl, int64_t T, int k, int E,
-                               int64_t d, bool bf16, void* dwr, float* db, hipStream_t s);
+                               int64_t d, bool bf16, float* part, void* dwr, float* db, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 
 // ---- combine (combine.hip) ----

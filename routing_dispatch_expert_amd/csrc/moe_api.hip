@@ -174,7 +174,7 @@ LayerPlan plan_layer(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E, in
 struct BackPlan {
   LayerPlan f;
   void *g, *u, *dy, *dh, *dgu, *dX, *WdT, *WguT, *dyT, *hT, *dgT, *duT, *XT;
-  float* dl;
+  float *dl, *rpart;
   int32_t *kfull_d, *kfull_f, *mtile_d, *mtile_f;
   int64_t Kp;
   size_t bytes;
@@ -206,6 +206,7 @@ BackPlan plan_backward(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E, 
   b.kfull_f = c.take<int32_t>(E);
   b.mtile_d = c.take<int32_t>(static_cast<size_t>(E) + 1);
   b.mtile_f = c.take<int32_t>(static_cast<size_t>(E) + 1);
+  b.rpart = c.take<float>(static_cast<size_t>(moe::router_wgrad_chunks(T, E, d)) * E * (d + 1));
   b.bytes = b.f.bytes + align_up(c.off);
   return b;
 }
@@ -412,7 +413,8 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
               "transpose W_up");
   MOE_HIP_TRY(moe::launch_gemm_down(b.dgu, p.kept, p.mtile, b.WguT, E, C, d, 2 * F, bf16, b.dX, s), "gemm dX");
   // 5. router gradients, then dx = dout + the expert paths + the router path
-  MOE_HIP_TRY(moe::launch_router_wgrad(x, p.idx, b.dl, T, k, E, d, bf16, dW_router, d_bias, s), "router wgrad");
+  MOE_HIP_TRY(moe::launch_router_wgrad(x, p.idx, b.dl, T, k, E, d, bf16, b.rpart, dW_router, d_bias, s),
+              "router wgrad");
   MOE_HIP_TRY(moe::launch_gather_dx(dout, b.dX, W_router, p.idx, b.dl, p.slot, T, d, k, C, bf16, dx, s),
               "gather dx");
   // 6. weight gradients over each expert's kept rows: dWd = dy^T h, dWg = dg^T X,
