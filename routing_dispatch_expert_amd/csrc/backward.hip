@@ -371,9 +371,9 @@ hipError_t launch_gather_dx(const void* dout, const void* dX, const void* wr, co
 }
 
 int router_wgrad_chunks(int64_t T, int E, int64_t d) {
-  // about 2048 blocks, chunks of at least 64 tokens
+  // about 8192 blocks, chunks of at least 64 tokens
   const int64_t tiles = ceil_div(d, 256) * ceil_div(E, 16);
-  const int64_t by_work = ceil_div(2048, tiles);
+  const int64_t by_work = ceil_div(8192, tiles);
   return static_cast<int>(std::max<int64_t>(1, std::min(by_work, ceil_div(T, 64))));
 }
 
