@@ -47,7 +47,7 @@ __all__ = [
     "decode", "capacity", "router_logits", "topk_experts", "rank_limited_experts", "gate_weights",
     "assign_slots", "dispatch_buckets", "send_counts", "expert_hidden", "expert_mlp",
     "combine", "routing_stats", "dispatch_bytes", "layer_forward", "layer_backward",
-    "layer_backward_sample",
+    "layer_backward_sample", "replica_plan", "replica_layout", "assign_replica_slots",
 ]
 
 
@@ -358,11 +358,89 @@ def routing_stats(slot: np.ndarray, routed: np.ndarray, kept: np.ndarray, C: int
 
 
 # ---------------------------------------------------------------------------
+# hot-expert replication
+# ---------------------------------------------------------------------------
+
+def replica_plan(routed: np.ndarray, extra: int) -> np.ndarray:
+    """Replica counts: one per expert, plus `extra` more for the hot ones.
+
+    [EP-guide] section 4, "Expert Replication": popular experts are replicated
+    on several devices so their tokens can go to either copy, for better
+    balance and fewer drops at the cost of memory; [EP-vs-TP] names a load
+    balancer that re-places experts under skew. No policy is given. Reading
+    taken: each extra replica goes, one at a time, to the expert with the
+    highest load per replica, routed[e] / r[e] (compared exactly as integers),
+    the lowest index winning a tie.
+    """
+    routed = np.asarray(routed, dtype=np.int64)
+    r = np.ones(routed.size, dtype=np.int64)
+    for _ in range(int(extra)):
+        best = 0
+        for e in range(1, routed.size):
+            if routed[e] * r[best] > routed[best] * r[e]:
+                best = e
+        r[best] += 1
+    return r.astype(np.int32)
+
+
+def replica_layout(replicas: np.ndarray, P: int):
+    """Instances of the replicated experts: offsets [E+1] (instance i of
+    expert e is inst_off[e] + j for its replica j), expert_of[R] and
+    rank_of[R]. Reading taken for placement ([EP-guide] section 4 puts
+    replica 2 of expert 0 on the next device): replica j of expert e sits on
+    rank (home(e) + j) mod P, home(e) = e // (E/P) as for unreplicated experts.
+    """
+    r = np.asarray(replicas, dtype=np.int64)
+    E = r.size
+    if P < 1 or E % P or np.any(r < 1):
+        raise ValueError("need E % P == 0 and every replica count >= 1")
+    inst_off = np.concatenate(([0], np.cumsum(r)))
+    expert_of = np.repeat(np.arange(E), r)
+    j = np.arange(inst_off[-1]) - inst_off[expert_of]
+    rank_of = (expert_of // (E // P) + j) % P
+    return inst_off, expert_of, rank_of
+
+
+def assign_replica_slots(idx: np.ndarray, replicas: np.ndarray, C: int):
+    """Slots when expert e has r_e replicas of capacity C each.
+
+    Reading taken (the pages say only that an expert's tokens may go to either
+    replica): the copies of expert e, in the token order of assign_slots, are
+    dealt to its replicas in turn. Copy q (its rank among e's copies) goes to
+    replica q mod r_e at slot q div r_e, and is dropped iff that slot is >= C,
+    so the expert keeps min(routed, r_e C) copies and its replicas' loads
+    differ by at most one. Returns instance[T, k], slot[T, k] (-1 = dropped),
+    src[R*C], routed[E] and kept[R].
+    """
+    T, k = idx.shape
+    r = np.asarray(replicas, dtype=np.int64)
+    E = r.size
+    inst_off = np.concatenate(([0], np.cumsum(r)))
+    R = int(inst_off[-1])
+    flat = idx.reshape(-1).astype(np.int64)
+    n = flat.size
+    order = np.argsort(flat, kind="stable")
+    routed = np.bincount(flat, minlength=E).astype(np.int64)
+    start = np.concatenate(([0], np.cumsum(routed)[:-1]))
+    q = np.empty(n, dtype=np.int64)
+    q[order] = np.arange(n, dtype=np.int64) - start[flat[order]]
+    inst = inst_off[flat] + q % r[flat]
+    s = q // r[flat]
+    keep = s < C
+    slot = np.where(keep, s, -1).astype(np.int32).reshape(T, k)
+    src = np.full(R * C, -1, dtype=np.int32)
+    ids = np.nonzero(keep)[0]
+    src[inst[ids] * C + s[ids]] = ids.astype(np.int32)
+    kept = np.bincount(inst[keep], minlength=R).astype(np.int64)
+    return inst.astype(np.int32).reshape(T, k), slot, src, routed, kept
+
+
+# ---------------------------------------------------------------------------
 # the whole layer
 # ---------------------------------------------------------------------------
 
 def layer_forward(x, wr, expert_weights, T, d, d_ff, E, k, cf, dtype, P=1, bias=None,
-                  tokens=None, max_ranks=0, exact=False):
+                  tokens=None, max_ranks=0, exact=False, replicas=None):
     """The layer as the plain per-token definition, steps 1 to 7 above.
 
     x [T, d] and wr [E, d] are the inputs (bf16 as bit patterns, or fp32).
@@ -374,6 +452,9 @@ def layer_forward(x, wr, expert_weights, T, d, d_ff, E, k, cf, dtype, P=1, bias=
     token's experts to that many of the P ranks (rank_limited_experts).
     exact=True keeps the scores and gates in fp64 (no fp32 rounding): the
     smooth function that finite differences of the gradients need.
+    replicas [E] (replica counts, see replica_plan) spreads each expert's
+    copies over its replicas (assign_replica_slots); slot is then the row in
+    the copy's instance, and kept, src and send_count are per instance.
 
     Returns a dict: logits, idx, w, C, slot, src, routed, kept, stats,
     tokens, out64 (fp64, unrounded), out (rounded once to dtype; a token with
@@ -394,9 +475,19 @@ def layer_forward(x, wr, expert_weights, T, d, d_ff, E, k, cf, dtype, P=1, bias=
         idx = rank_limited_experts(logits, k, P, max_ranks)
         w = gate_weights(logits, idx)
     C = capacity(T, E, k, cf)
-    slot, src, routed, kept = assign_slots(idx, E, C)
     eb = {"bf16": 2, "f32": 4, "f64": 8}[dtype]
-    stats = routing_stats(slot, routed, kept, C, P, d, eb)
+    instance = None
+    if replicas is None:
+        slot, src, routed, kept = assign_slots(idx, E, C)
+        stats = routing_stats(slot, routed, kept, C, P, d, eb)
+    else:
+        instance, slot, src, routed, kept = assign_replica_slots(idx, replicas, C)
+        _, _, rank_of = replica_layout(replicas, P)
+        sc = np.bincount(rank_of, weights=kept, minlength=P).astype(np.int64)
+        n_kept = int(kept.sum())
+        stats = {"routed": routed, "kept": kept, "send_count": sc, "dropped": T * k - n_kept,
+                 "fully_dropped_tokens": int(np.all(slot < 0, axis=1).sum()),
+                 "padded_rows": kept.size * C - n_kept, "offrank_bytes": int(sc[1:].sum()) * d * eb}
 
     tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     y = np.zeros((tok.size, k, d), dtype=np.float64)
@@ -411,7 +502,7 @@ def layer_forward(x, wr, expert_weights, T, d, d_ff, E, k, cf, dtype, P=1, bias=
     out[passthru] = x[tok[passthru]]
     return {"logits": logits, "idx": idx, "w": w, "C": C, "slot": slot, "src": src,
             "routed": routed, "kept": kept, "stats": stats, "tokens": tok,
-            "out64": out64, "out": out}
+            "out64": out64, "out": out, "instance": instance}
 
 
 # ---------------------------------------------------------------------------

@@ -111,9 +111,10 @@ def mlp(xrow, wg, wu, wd):
     return [dot(r, h) for r in wd]
 
 
-def layer(x, wr, bias, wg, wu, wd, k, cf32, P=1, M=0):
+def layer(x, wr, bias, wg, wu, wd, k, cf32, P=1, M=0, caps=None):
     """x: T lists of d doubles; wr: E lists; wg/wu: E x d_ff x d; wd: E x d x d_ff.
-    M > 0 limits every token to experts of at most M of the P ranks.
+    M > 0 limits every token to experts of at most M of the P ranks. caps, if
+    given, is a capacity per expert (in units of C) instead of C for all.
 
     Returns dict with logits, idx, w, C, slot, src, routed, kept, out (doubles).
     """
@@ -134,10 +135,11 @@ def layer(x, wr, bias, wg, wu, wd, k, cf32, P=1, M=0):
             e = idx[t][j]
             s = fill[e]
             fill[e] += 1
-            if s < C:
+            if s < (C if caps is None else caps[e] * C):
                 slot[t][j] = s
-                src[e * C + s] = t * k + j
-    kept = [min(f, C) for f in fill]
+                if caps is None:
+                    src[e * C + s] = t * k + j
+    kept = [min(f, C if caps is None else caps[e] * C) for e, f in enumerate(fill)]
     out = []
     for t in range(T):
         row = list(x[t])

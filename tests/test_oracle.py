@@ -486,3 +486,81 @@ def test_generator_rank_limited_gap_conditioning():
     idx = oracle.rank_limited_experts(l.astype(np.float32), 4, 8, 2)
     chosen = np.take_along_axis(l, idx, axis=1)
     assert (chosen[:, :-1] - chosen[:, 1:]).min() > 1e-3 - 1e-6
+
+
+# ------------------------------------------------------ hot-expert replicas ---
+
+@pytest.mark.parametrize("case", range(8))
+def test_replicated_layer_matches_per_expert_capacity_bruteforce(case):
+    rng = np.random.default_rng(800 + case)
+    P = int(rng.choice([1, 2]))
+    E = P * int(rng.integers(1, 4))
+    k = int(rng.integers(1, min(2, E) + 1))
+    T, d, f = int(rng.integers(3, 10)), int(rng.integers(2, 5)), int(rng.integers(1, 4))
+    cf = float(rng.choice([0.25, 0.5, 1.0]))
+    dtype = "bf16" if case % 2 else "f32"
+    reps = rng.integers(1, 4, size=E).astype(np.int32)
+    wl = moe_inputs.custom(T=T, d=d, E=E, k=k, d_ff=f, cf=cf, dtype=dtype, seed=820 + case, wr_std=1.0,
+                           bias="hot0" if case % 3 == 0 else None, P=P)
+    r = oracle.layer_forward(wl.x, wl.wr, wl.expert, T, d, f, E, k, cf, dtype, P=P, bias=wl.bias_vec, replicas=reps)
+    ex = [wl.expert(e) for e in range(E)]
+    b = bf.layer(_as_lists(wl.x, dtype), _as_lists(wl.wr, dtype),
+                 None if wl.bias_vec is None else [float(v) for v in wl.bias_vec],
+                 [_as_lists(e[0], dtype) for e in ex], [_as_lists(e[1], dtype) for e in ex],
+                 [_as_lists(e[2], dtype) for e in ex], k, float(np.float32(cf)), caps=[int(v) for v in reps])
+    assert r["idx"].tolist() == b["idx"]
+    assert ((r["slot"] >= 0) == (np.array(b["slot"]) >= 0)).all()
+    assert np.allclose(r["out64"], np.array(b["out"]), rtol=1e-12, atol=1e-13)
+    # per expert: kept copies = min(routed, r C) over its replicas
+    inst_off, expert_of, _ = oracle.replica_layout(reps, P)
+    per_expert = np.bincount(expert_of, weights=r["kept"], minlength=E)
+    assert np.array_equal(per_expert, np.minimum(r["routed"], reps * r["C"]))
+
+
+def test_replica_slots_invariants_and_identity():
+    rng = np.random.default_rng(830)
+    T, E, k, C = 400, 6, 2, 30
+    idx = np.array([rng.permutation(E)[:k] for _ in range(T)], np.int32)
+    reps = np.array([3, 1, 2, 1, 4, 1], np.int32)
+    inst, slot, src, routed, kept = oracle.assign_replica_slots(idx, reps, C)
+    inst_off, expert_of, _ = oracle.replica_layout(reps, 1)
+    for e in range(E):
+        ks = kept[inst_off[e]:inst_off[e + 1]]
+        assert ks.sum() == min(routed[e], reps[e] * C)
+        if routed[e] < reps[e] * C:                  # unsaturated: loads differ by at most one
+            assert ks.max() - ks.min() <= 1
+    for i in range(inst_off[-1]):
+        rows = np.nonzero((inst == i) & (slot >= 0))
+        s_ = slot[rows]
+        assert sorted(s_.tolist()) == list(range(kept[i]))        # slots 0..kept-1
+        assert np.all(np.diff(s_[np.argsort(rows[0] * k + rows[1])]) > 0)   # increasing in token order
+        assert np.all(expert_of[i] == idx[rows])
+    # src inverts (instance, slot)
+    ids = src[src >= 0]
+    assert np.array_equal(inst.reshape(-1)[ids] * C + slot.reshape(-1)[ids], np.nonzero(src >= 0)[0])
+    # one replica each is the plain assignment
+    s1, src1, r1, k1 = oracle.assign_slots(idx, E, C)
+    i2, s2, src2, r2, k2 = oracle.assign_replica_slots(idx, np.ones(E, np.int32), C)
+    assert np.array_equal(s1, s2) and np.array_equal(src1, src2) and np.array_equal(k1, k2)
+    assert np.array_equal(i2, idx)
+
+
+def test_replica_plan_minimises_the_worst_load_per_replica():
+    from fractions import Fraction
+    rng = np.random.default_rng(840)
+    for _ in range(60):
+        E = int(rng.integers(1, 5))
+        extra = int(rng.integers(0, 6))
+        routed = rng.integers(0, 50, size=E)
+        plan = oracle.replica_plan(routed, extra)
+        assert plan.sum() == E + extra and np.all(plan >= 1)
+        worst = max(Fraction(int(a), int(b)) for a, b in zip(routed, plan))
+        best = None
+        for alloc in itertools.product(range(extra + 1), repeat=E):   # every way to hand out the extras
+            if sum(alloc) != extra:
+                continue
+            w = max(Fraction(int(a), 1 + c) for a, c in zip(routed, alloc))
+            best = w if best is None or w < best else best
+        assert worst == best
+    # ties go to the lower index
+    assert oracle.replica_plan(np.array([10, 10, 3]), 1).tolist() == [2, 1, 1]
