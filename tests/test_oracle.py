@@ -519,11 +519,12 @@ def test_replicated_layer_matches_per_expert_capacity_bruteforce(case):
 
 def test_replica_slots_invariants_and_identity():
     rng = np.random.default_rng(830)
-    T, E, k, C = 400, 6, 2, 30
+    T, E, k, C = 400, 6, 2, 60
     idx = np.array([rng.permutation(E)[:k] for _ in range(T)], np.int32)
     reps = np.array([3, 1, 2, 1, 4, 1], np.int32)
     inst, slot, src, routed, kept = oracle.assign_replica_slots(idx, reps, C)
     inst_off, expert_of, _ = oracle.replica_layout(reps, 1)
+    assert np.sum((routed < reps * C) & (reps > 1)) >= 2 and np.sum(routed > reps * C) >= 2  # both regimes
     for e in range(E):
         ks = kept[inst_off[e]:inst_off[e + 1]]
         assert ks.sum() == min(routed[e], reps[e] * C)
