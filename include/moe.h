@@ -87,6 +87,7 @@ typedef struct {
   int64_t* totals;       /* [MOE_NUM_TOTALS] */
   void* buckets;         /* [E, C, d] dtype; rank p's send buffer is experts
                             [p*E/P, (p+1)*E/P), a contiguous slice */
+  int32_t* instance;     /* [T, k] replica instance of each copy (replicated layer only) */
 } moe_stats_t;
 
 /* Expert capacity C = ceil(cf * k * T / E), evaluated in IEEE double as
@@ -144,6 +145,38 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
                        int32_t max_ranks, moe_dtype_t dtype, void* dx, void* dW_router,
                        float* d_bias, void* dW_gate, void* dW_up, void* dW_down, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/* Hot-expert replication ([EP-guide] section 4 "Expert Replication": a popular
+ * expert is replicated on several devices and its tokens may go to either
+ * copy, for better balance and fewer drops at the cost of memory; [EP-vs-TP]
+ * "Expert parallelism pays in all-to-all dispatch": a load balancer re-places
+ * experts under skew). The pages give no policy; the readings taken:
+ *  - moe_replica_plan (host only): r[e] = 1 for every expert, then each of
+ *    `extra` more replicas goes to the expert with the highest routed[e]/r[e]
+ *    (exact integer comparison, lowest index on a tie).
+ *  - moe_layer_forward_replicated: expert e has replicas[e] >= 1 instances of
+ *    capacity C each (C = moe_capacity of the unreplicated layer); instance i
+ *    = inst_off[e] + j for replica j, inst_off the exclusive prefix sum.
+ *    The copies of expert e, in stable token order, are dealt to its
+ *    replicas in turn: copy q goes to replica q mod r at slot q div r, and is
+ *    dropped iff that slot is >= C. Replica j of expert e sits on rank
+ *    (e / (E/P) + j) mod P for the send counts.
+ *  The output is that of the unreplicated layer in which expert e has
+ *  capacity replicas[e] * C. replicas is [E] int32 device memory summing to
+ *  R (E <= R <= 4096; results are unspecified otherwise, instances are
+ *  clamped to R - 1). stats: topk_idx, topk_w as before; slot = row in the
+ *  copy's instance; instance [T, k]; src [R, C]; routed_count [E];
+ *  kept_count [R]; send_count [P]; totals; buckets [R, C, d].
+ *  workspace: moe_replicated_workspace_size() bytes, 256-byte aligned. */
+int moe_replica_plan(const int32_t* routed_count, int32_t E, int32_t extra, int32_t* replicas);
+int moe_replicated_workspace_size(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k, float cf,
+                                  int32_t P, int32_t R, moe_dtype_t dtype, size_t* bytes);
+int moe_layer_forward_replicated(const void* x, const void* W_router, const float* router_bias,
+                                 const void* W_gate, const void* W_up, const void* W_down,
+                                 int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k, float cf,
+                                 int32_t P, int32_t max_ranks, const int32_t* replicas, int32_t R,
+                                 moe_dtype_t dtype, void* out, moe_stats_t* stats, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /* Router stage ([EP-inferensys] gating-network entry): logits on the matrix
  * cores, then top-k (with the rank limit P, max_ranks) and gates as in moe_route. logits_out [T, E] fp32 may be

@@ -23,7 +23,7 @@ MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 TOTALS = ("dropped", "fully_dropped_tokens", "padded_rows", "offrank_bytes")
 
 EXPORTS = ("moe_capacity", "moe_workspace_size", "moe_layer_forward", "moe_backward_workspace_size",
-           "moe_layer_backward", "moe_router_workspace_size", "moe_router", "moe_route",
+           "moe_layer_backward", "moe_replica_plan", "moe_replicated_workspace_size", "moe_layer_forward_replicated", "moe_router_workspace_size", "moe_router", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_grouped_gemm_workspace_size",
            "moe_grouped_gemm", "moe_combine", "moe_set_stage_events", "moe_status_string", "moe_last_error")
 STAGES = ("router", "route", "slots", "scatter", "gate_up", "down", "combine")
@@ -39,7 +39,7 @@ class moe_stats_t(ctypes.Structure):
     _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("slot", ctypes.c_void_p),
                 ("src", ctypes.c_void_p), ("routed_count", ctypes.c_void_p),
                 ("kept_count", ctypes.c_void_p), ("send_count", ctypes.c_void_p),
-                ("totals", ctypes.c_void_p), ("buckets", ctypes.c_void_p)]
+                ("totals", ctypes.c_void_p), ("buckets", ctypes.c_void_p), ("instance", ctypes.c_void_p)]
 
 
 _lib = None
@@ -52,6 +52,10 @@ _SIGS = {
     "moe_backward_workspace_size": [_I64, _I64, _I64, _I32, _I32, _F32, _I32, ctypes.c_int, _P],
     "moe_layer_backward": [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _F32, _I32, _I32, ctypes.c_int,
                            _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "moe_replica_plan": [_P, _I32, _I32, _P],
+    "moe_replicated_workspace_size": [_I64, _I64, _I64, _I32, _I32, _F32, _I32, _I32, ctypes.c_int, _P],
+    "moe_layer_forward_replicated": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _F32, _I32, _I32, _P,
+                                     _I32, ctypes.c_int, _P, ctypes.POINTER(moe_stats_t), _P, _SZ, _P],
     "moe_router_workspace_size": [_I64, _I64, _I32, ctypes.c_int, _P],
     "moe_router": [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, ctypes.c_int, _P, _P, _P, _P, _SZ, _P],
     "moe_route": [_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P],
@@ -177,6 +181,31 @@ def moe_layer_backward(x, W_router, router_bias, W_gate, W_up, W_down, dout, T, 
                                     _ptr(dx), _ptr(dW_router), _ptr(d_bias), _ptr(dW_gate), _ptr(dW_up),
                                     _ptr(dW_down), _ptr(workspace), workspace_bytes, _stream(stream)),
            "moe_layer_backward")
+
+
+def moe_replica_plan(routed_count, extra):
+    """Host-side replica counts (numpy int32 array of length E) from routed counts."""
+    import numpy as np
+    routed = np.ascontiguousarray(routed_count, dtype=np.int32)
+    out = np.empty_like(routed)
+    _check(lib().moe_replica_plan(routed.ctypes.data, routed.size, int(extra), out.ctypes.data), "moe_replica_plan")
+    return out
+
+
+def moe_replicated_workspace_size(T, d, d_ff, E, k, cf, P, R, dtype) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_replicated_workspace_size(T, d, d_ff, E, k, cf, P, R, _dtype(dtype), ctypes.byref(n)),
+           "moe_replicated_workspace_size")
+    return n.value
+
+
+def moe_layer_forward_replicated(x, W_router, router_bias, W_gate, W_up, W_down, T, d, d_ff, E, k, cf, P, max_ranks,
+                                 replicas, R, dtype, out, stats, workspace, workspace_bytes, stream=None):
+    _check(lib().moe_layer_forward_replicated(_ptr(x), _ptr(W_router), _ptr(router_bias), _ptr(W_gate), _ptr(W_up),
+                                              _ptr(W_down), T, d, d_ff, E, k, cf, P, max_ranks, _ptr(replicas), R,
+                                              _dtype(dtype), _ptr(out), _stats(stats), _ptr(workspace),
+                                              workspace_bytes, _stream(stream)),
+           "moe_layer_forward_replicated")
 
 
 def moe_router_workspace_size(T, d, E, dtype) -> int:
@@ -316,5 +345,38 @@ def backward(x, W_router, W_gate, W_up, W_down, dout, k, cf, P=1, router_bias=No
     moe_layer_backward(x, W_router, router_bias, W_gate, W_up, W_down, dout, T, d, d_ff, E, k, cf, P, max_ranks, dt,
                        res["dx"], res["dW_router"], res["d_bias"], res["dW_gate"], res["dW_up"], res["dW_down"],
                        workspace, nbytes, stream)
+    res["workspace"] = workspace
+    return res
+
+
+def forward_replicated(x, W_router, W_gate, W_up, W_down, k, cf, replicas, P=1, router_bias=None, stream=None,
+                       want_buckets=False, want_src=False, workspace=None, max_ranks=0):
+    """The layer with replicated experts; replicas is an int32 cuda tensor [E]
+    (each >= 1). Returns a dict like forward(), with per-instance kept_count,
+    src and buckets, and the instance of each copy."""
+    import torch
+    T, d = x.shape
+    E = W_router.shape[0]
+    d_ff = W_gate.shape[1]
+    dt = x.dtype
+    _require(replicas, "replicas", torch.int32, (E,))
+    R = int(replicas.sum().item())
+    C = moe_capacity(T, E, k, cf)
+    dev = x.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    res = {"C": C, "R": R, "out": torch.empty_like(x), "topk_idx": torch.empty((T, k), **i32),
+           "topk_w": torch.empty((T, k), dtype=torch.float32, device=dev), "slot": torch.empty((T, k), **i32),
+           "instance": torch.empty((T, k), **i32), "routed_count": torch.empty(E, **i32),
+           "kept_count": torch.empty(R, **i32), "send_count": torch.empty(P, **i32),
+           "totals": torch.empty(4, dtype=torch.int64, device=dev)}
+    if want_buckets:
+        res["buckets"] = torch.empty((R, C, d), dtype=dt, device=dev)
+    if want_src:
+        res["src"] = torch.empty((R, C), **i32)
+    nbytes = moe_replicated_workspace_size(T, d, d_ff, E, k, cf, P, R, dt)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    moe_layer_forward_replicated(x, W_router, router_bias, W_gate, W_up, W_down, T, d, d_ff, E, k, cf, P, max_ranks,
+                                 replicas, R, dt, res["out"], res, workspace, nbytes, stream)
     res["workspace"] = workspace
     return res

@@ -62,10 +62,17 @@ hipError_t launch_tile_hist(const int32_t* idx, int64_t T, int k, int E, int32_t
 // Exclusive scan of the tile histogram over tiles, per expert; then counts,
 // totals, send counts and (if mtile_off != nullptr) the GEMM row-tile prefix
 // for row tiles of `bm` rows.
+// place [E] (optional): rank of each bucket for the send counts (default e / (E/P)).
 hipError_t launch_scan(const int32_t* tile_cnt, int64_t nt, int E, int64_t C, int P,
                        int64_t row_bytes, int k, int64_t T, int32_t* tile_off, int32_t* routed,
                        int32_t* kept, int32_t* send, int64_t* totals, int bm, int32_t* mtile_off,
-                       int32_t* src, hipStream_t s);
+                       int32_t* src, hipStream_t s, const int32_t* place = nullptr);
+// Replicated experts: instance offsets [E+1], expert [R] and rank [R] of each
+// instance; then the instance of each copy from its rank among its expert's copies.
+hipError_t launch_replica_layout(const int32_t* replicas, int E, int R, int P, int32_t* inst_off, int32_t* wmap,
+                                 int32_t* place, hipStream_t s);
+hipError_t launch_instances(const int32_t* idx, const int32_t* qrank, const int32_t* replicas,
+                            const int32_t* inst_off, int64_t n, int R, int32_t* inst, hipStream_t s);
 hipError_t launch_mtile_map(const int32_t* kept, int E, int bm, int32_t* mtile_off, hipStream_t s);
 hipError_t launch_slots(const int32_t* idx, const int32_t* tile_off, int64_t T, int k, int E,
                         int64_t C, int32_t* slot, int32_t* src, int64_t* totals, hipStream_t s);
@@ -76,14 +83,15 @@ hipError_t launch_scatter_rows(const void* x, const int32_t* idx, const int32_t*
 // Row-tile height the grouped GEMM uses for these sizes (the mtile map must
 // be built for the same value).
 int grouped_gemm_bm(bool bf16, int64_t C);
-// GEMM 1: h = silu(X Wg^T) * (X Wu^T) on rows < kept.
+// GEMM 1: h = silu(X Wg^T) * (X Wu^T) on rows < kept. With wmap [E], bucket
+// e uses the weights of expert wmap[e] (replicated experts).
 hipError_t launch_gemm_gate_up(const void* buckets, const int32_t* kept, const int32_t* mtile_off,
                                const void* wg, const void* wu, int E, int64_t C, int64_t d,
-                               int64_t d_ff, bool bf16, void* h, hipStream_t s);
-// GEMM 2: y = h Wd^T on rows < kept.
+                               int64_t d_ff, bool bf16, void* h, hipStream_t s, const int32_t* wmap = nullptr);
+// GEMM 2: y = h Wd^T on rows < kept (wmap as above).
 hipError_t launch_gemm_down(const void* h, const int32_t* kept, const int32_t* mtile_off,
                             const void* wd, int E, int64_t C, int64_t d, int64_t d_ff, bool bf16,
-                            void* y, hipStream_t s);
+                            void* y, hipStream_t s, const int32_t* wmap = nullptr);
 
 // ---- backward (backward.hip) ----
 // dst[b][c][col_off + r] = src[b][r][c] for r < valid[b] (or R), 0 for r < Rp.

@@ -157,7 +157,7 @@ template <int BM, int BN, bool SWIGLU>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BM >= 256 ? 1 : 2))) void gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     bf16_t* __restrict__ out, const int32_t* __restrict__ kept, const int32_t* __restrict__ mtile_off,
-    int E, int64_t C, int64_t K, int64_t N, int nt_count) {
+    int E, int64_t C, int64_t K, int64_t N, int nt_count, const int32_t* __restrict__ wmap) {
   constexpr int BK = 64;
   constexpr int TM = BM / 64, TN = BN / 64;      // 32 x 32 tiles per wave
   constexpr int AL = BM * (BK / 8) / 256;        // 16-byte chunks per thread
@@ -187,8 +187,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BM >= 25
   const uint32_t a_bytes = static_cast<uint32_t>(C * K * 2);
   const uint32_t b_bytes = static_cast<uint32_t>(N * K * 2);
   const auto ra_src = buffer_rsrc(A + static_cast<int64_t>(e) * C * K, a_bytes);
-  const auto rb_src0 = buffer_rsrc(B0 + static_cast<int64_t>(e) * N * K, b_bytes);
-  const auto rb_src1 = buffer_rsrc((SWIGLU ? B1 : B0) + static_cast<int64_t>(e) * N * K, b_bytes);
+  const int we = wmap ? __builtin_amdgcn_readfirstlane(wmap[e]) : e;  // expert whose weights this row tile uses
+  const auto rb_src0 = buffer_rsrc(B0 + static_cast<int64_t>(we) * N * K, b_bytes);
+  const auto rb_src1 = buffer_rsrc((SWIGLU ? B1 : B0) + static_cast<int64_t>(we) * N * K, b_bytes);
   uint32_t a_off[AL], b_off[BL];
 #pragma unroll
   for (int r = 0; r < AL; ++r) a_off[r] = static_cast<uint32_t>((m0 + lrow + 32 * r) * K * 2 + lch * 16);
@@ -361,7 +362,7 @@ template <bool SWIGLU>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_dma_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     bf16_t* __restrict__ out, const int32_t* __restrict__ kept, const int32_t* __restrict__ mtile_off,
-    int E, int64_t C, int64_t K, int64_t N, int nt_count) {
+    int E, int64_t C, int64_t K, int64_t N, int nt_count, const int32_t* __restrict__ wmap) {
   constexpr int BM = 256, BN = 256, BK = 64, TM = 4, TN = 4;
   constexpr int CH = BK / 8;                    // 16-byte chunks per LDS row
   constexpr int BNO = SWIGLU ? BN / 2 : BN;
@@ -386,7 +387,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // B rows 0..127 of a SwiGLU block are gate rows, 128..255 up rows: waves 0-1
   // load the first half, waves 2-3 the second
   const bf16_t* bbase = (SWIGLU && wave >= 2) ? B1 : B0;
-  const auto rb_src = buffer_rsrc(bbase + static_cast<int64_t>(e) * N * K, static_cast<uint32_t>(N * K * 2));
+  const int we = wmap ? __builtin_amdgcn_readfirstlane(wmap[e]) : e;  // expert whose weights this row tile uses
+  const auto rb_src = buffer_rsrc(bbase + static_cast<int64_t>(we) * N * K, static_cast<uint32_t>(N * K * 2));
   uint32_t a_voff[PER_WAVE], b_voff[PER_WAVE];
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
@@ -518,7 +520,7 @@ template <bool SWIGLU>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_dma_m128_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     bf16_t* __restrict__ out, const int32_t* __restrict__ kept, const int32_t* __restrict__ mtile_off,
-    int E, int64_t C, int64_t K, int64_t N, int nt_count) {
+    int E, int64_t C, int64_t K, int64_t N, int nt_count, const int32_t* __restrict__ wmap) {
   constexpr int BM = 128, BN = 256, BK = 32, TM = 2, TN = 4;
   constexpr int CH = BK / 8;                    // 16-byte chunks per LDS row
   constexpr int BNO = SWIGLU ? BN / 2 : BN;
@@ -544,7 +546,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // B rows 0..127 of a SwiGLU block are gate rows, 128..255 up rows: waves 0-1
   // load the first half, waves 2-3 the second
   const bf16_t* bbase = (SWIGLU && wave >= 2) ? B1 : B0;
-  const auto rb_src = buffer_rsrc(bbase + static_cast<int64_t>(e) * N * K, static_cast<uint32_t>(N * K * 2));
+  const int we = wmap ? __builtin_amdgcn_readfirstlane(wmap[e]) : e;  // expert whose weights this row tile uses
+  const auto rb_src = buffer_rsrc(bbase + static_cast<int64_t>(we) * N * K, static_cast<uint32_t>(N * K * 2));
   uint32_t a_voff[A_PW], b_voff[B_PW];
 #pragma unroll
   for (int i = 0; i < A_PW; ++i) {
@@ -670,7 +673,7 @@ template <bool SWIGLU>
 __global__ __launch_bounds__(256) void gemm_bf16_skinny_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     bf16_t* __restrict__ out, const int32_t* __restrict__ kept, const int32_t* __restrict__ mtile_off,
-    int E, int64_t C, int64_t K, int64_t N, int nch) {
+    int E, int64_t C, int64_t K, int64_t N, int nch, const int32_t* __restrict__ wmap) {
   constexpr int U = 8;  // K steps in flight
   const int mt = blockIdx.x / nch;
   const int nc = blockIdx.x - mt * nch;
@@ -687,8 +690,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_skinny_kernel(
   const bool a_in = arow < rows;
   const bf16_t* ap = A + (static_cast<int64_t>(e) * C + (a_in ? arow : 0)) * K + kg;
   const int64_t bcol = min(col0 + (lane & 15), N - 1);
-  const bf16_t* b0p = B0 + (static_cast<int64_t>(e) * N + bcol) * K + kg;
-  const bf16_t* b1p = SWIGLU ? B1 + (static_cast<int64_t>(e) * N + bcol) * K + kg : nullptr;
+  const int64_t we = wmap ? __builtin_amdgcn_readfirstlane(wmap[e]) : e;
+  const bf16_t* b0p = B0 + (we * N + bcol) * K + kg;
+  const bf16_t* b1p = SWIGLU ? B1 + (we * N + bcol) * K + kg : nullptr;
 
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   const int64_t nk = K / 32;  // K is a multiple of 32 here
@@ -744,7 +748,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
                                                        float* __restrict__ out,
                                                        const int32_t* __restrict__ kept,
                                                        const int32_t* __restrict__ mtile_off,
-                                                       int E, int64_t C, int64_t K, int64_t N) {
+                                                       int E, int64_t C, int64_t K, int64_t N,
+                                                       const int32_t* __restrict__ wmap) {
   constexpr int BM = 64, BN = 64, BK = 16;
   constexpr int NB = SWIGLU ? 2 : 1;
   __shared__ float As[BK][BM + 4];
@@ -759,8 +764,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
   const float* Ae = A + static_cast<int64_t>(e) * C * K;
-  const float* Bp[2] = {B0 + static_cast<int64_t>(e) * N * K,
-                        SWIGLU ? B1 + static_cast<int64_t>(e) * N * K : nullptr};
+  const int64_t we = wmap ? wmap[e] : e;
+  const float* Bp[2] = {B0 + we * N * K, SWIGLU ? B1 + we * N * K : nullptr};
 
   float acc[NB][4][4];
 #pragma unroll
@@ -835,18 +840,20 @@ namespace {
 
 template <bool SWIGLU>
 hipError_t launch_skinny(const void* a, const void* b0, const void* b1, void* out, const int32_t* kept,
-                         const int32_t* mtile_off, int E, int64_t C, int64_t K, int64_t N, hipStream_t s) {
+                         const int32_t* mtile_off, int E, int64_t C, int64_t K, int64_t N, const int32_t* wmap,
+                         hipStream_t s) {
   const int64_t nch = ceil_div(N, 64);
   const int64_t blocks = E * ceil_div(C, kSkinnyRows) * nch;
   gemm_bf16_skinny_kernel<SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
       static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0), static_cast<const bf16_t*>(b1),
-      static_cast<bf16_t*>(out), kept, mtile_off, E, C, K, N, static_cast<int>(nch));
+      static_cast<bf16_t*>(out), kept, mtile_off, E, C, K, N, static_cast<int>(nch), wmap);
   return hipGetLastError();
 }
 
 template <int BM, int BN, bool SWIGLU>
 hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out, const int32_t* kept,
-                       const int32_t* mtile_off, int E, int64_t C, int64_t K, int64_t N, hipStream_t s) {
+                       const int32_t* mtile_off, int E, int64_t C, int64_t K, int64_t N, const int32_t* wmap,
+                       hipStream_t s) {
   const int64_t mt_max = E * ceil_div(C, BM);  // upper bound of live row tiles
   const int64_t nt = ceil_div(N, SWIGLU ? BN / 2 : BN);
   const int64_t blocks = ceil_div(mt_max * nt, 8) * 8;  // whole rounds over the 8 XCDs
@@ -857,13 +864,13 @@ hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out,
   if constexpr (BM == 128 && BN == 256) {
     if (K % 64) return hipErrorInvalidValue;  // callers pick this tile only for K % 64 == 0
     gemm_bf16_dma_m128_kernel<SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
-        pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt));
+        pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap);
   } else if (BM == 256 && BN == 256 && K % 128 == 0) {
     gemm_bf16_dma_kernel<SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
-        pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt));
+        pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap);
   } else {
     gemm_bf16_kernel<BM, BN, SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
-        pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt));
+        pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap);
   }
   return hipGetLastError();
 }
@@ -872,41 +879,41 @@ hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out,
 
 hipError_t launch_gemm_gate_up(const void* buckets, const int32_t* kept, const int32_t* mtile_off,
                                const void* wg, const void* wu, int E, int64_t C, int64_t d,
-                               int64_t d_ff, bool bf16, void* h, hipStream_t s) {
+                               int64_t d_ff, bool bf16, void* h, hipStream_t s, const int32_t* wmap) {
   if (E * C == 0) return hipSuccess;
   if (bf16) {
     if (grouped_gemm_bm(true, C) == kSkinnyRows && d % 32 == 0)
-      return launch_skinny<true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, s);
+      return launch_skinny<true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s);
     if (grouped_gemm_bm(true, C) == 256)
-      return launch_bf16<256, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, s);
+      return launch_bf16<256, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s);
     if (d % 64 == 0)
-      return launch_bf16<128, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, s);
-    return launch_bf16<128, 128, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, s);
+      return launch_bf16<128, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s);
+    return launch_bf16<128, 128, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s);
   }
   const unsigned mtiles = static_cast<unsigned>(E * ceil_div(C, 64));
   gemm_f32_kernel<true><<<dim3(mtiles, static_cast<unsigned>(ceil_div(d_ff, 64))), dim3(256), 0, s>>>(
       static_cast<const float*>(buckets), static_cast<const float*>(wg), static_cast<const float*>(wu),
-      static_cast<float*>(h), kept, mtile_off, E, C, d, d_ff);
+      static_cast<float*>(h), kept, mtile_off, E, C, d, d_ff, wmap);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_down(const void* h, const int32_t* kept, const int32_t* mtile_off,
                             const void* wd, int E, int64_t C, int64_t d, int64_t d_ff, bool bf16,
-                            void* y, hipStream_t s) {
+                            void* y, hipStream_t s, const int32_t* wmap) {
   if (E * C == 0) return hipSuccess;
   if (bf16) {
     if (grouped_gemm_bm(true, C) == kSkinnyRows && d_ff % 32 == 0)
-      return launch_skinny<false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, s);
+      return launch_skinny<false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, wmap, s);
     if (grouped_gemm_bm(true, C) == 256)
-      return launch_bf16<256, 256, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, s);
+      return launch_bf16<256, 256, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, wmap, s);
     if (d_ff % 64 == 0)
-      return launch_bf16<128, 256, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, s);
-    return launch_bf16<128, 128, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, s);
+      return launch_bf16<128, 256, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, wmap, s);
+    return launch_bf16<128, 128, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, wmap, s);
   }
   const unsigned mtiles = static_cast<unsigned>(E * ceil_div(C, 64));
   gemm_f32_kernel<false><<<dim3(mtiles, static_cast<unsigned>(ceil_div(d, 64))), dim3(256), 0, s>>>(
       static_cast<const float*>(h), static_cast<const float*>(wd), nullptr, static_cast<float*>(y), kept,
-      mtile_off, E, C, d_ff, d);
+      mtile_off, E, C, d_ff, d, wmap);
   return hipGetLastError();
 }
 

@@ -211,6 +211,59 @@ BackPlan plan_backward(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E, 
   return b;
 }
 
+// Instances of replicated experts: E <= R <= 4096 (the scan's LDS), R*C < 2^31.
+int check_replicas(int32_t E, int32_t R, int64_t C) {
+  if (R < E || R > kMaxE) return fail(MOE_ERR_INVALID_ARG, "R=%d must be in [E=%d, %d]", R, E, kMaxE);
+  if (static_cast<int64_t>(R) * C >= (int64_t{1} << 31)) return fail(MOE_ERR_UNSUPPORTED, "R*C must stay below 2^31");
+  return MOE_OK;
+}
+
+// Replicated-layer workspace: routing as in the plain layer, the token-order
+// rank of each copy within its expert, the instance maps, and the per-instance
+// arrays (counts, row-tile map, buckets, h, y) for R instances.
+struct ReplPlan {
+  float *logits, *w;
+  int32_t *idx, *qrank, *inst, *slot, *tile_cnt, *tile_off, *routed, *routed2, *kept1, *kept, *send, *send1,
+      *mtile, *inst_off, *wmap, *place;
+  int64_t *totals, *totals1;
+  void *buckets, *h, *y;
+  size_t bytes;
+};
+
+ReplPlan plan_replicated(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k, int64_t C, int32_t P,
+                         int32_t R, int eb) {
+  Carver c(ws);
+  ReplPlan p;
+  const int64_t nt = moe::ceil_div(T, moe::kTileTokens);
+  const int S = moe::router_splits(T, d, E, eb == 2);
+  const size_t Tk = static_cast<size_t>(T) * k;
+  p.logits = c.take<float>(static_cast<size_t>(S) * T * E);
+  p.idx = c.take<int32_t>(Tk);
+  p.w = c.take<float>(Tk);
+  p.qrank = c.take<int32_t>(Tk);
+  p.inst = c.take<int32_t>(Tk);
+  p.slot = c.take<int32_t>(Tk);
+  p.tile_cnt = c.take<int32_t>(static_cast<size_t>(nt) * R);
+  p.tile_off = c.take<int32_t>(static_cast<size_t>(nt) * R);
+  p.routed = c.take<int32_t>(E);
+  p.routed2 = c.take<int32_t>(R);
+  p.kept1 = c.take<int32_t>(E);
+  p.kept = c.take<int32_t>(R);
+  p.send = c.take<int32_t>(P);
+  p.send1 = c.take<int32_t>(P);
+  p.totals = c.take<int64_t>(MOE_NUM_TOTALS);
+  p.totals1 = c.take<int64_t>(MOE_NUM_TOTALS);
+  p.mtile = c.take<int32_t>(static_cast<size_t>(R) + 1);
+  p.inst_off = c.take<int32_t>(static_cast<size_t>(E) + 1);
+  p.wmap = c.take<int32_t>(R);
+  p.place = c.take<int32_t>(R);
+  p.buckets = c.take<char>(static_cast<size_t>(R) * C * d * eb);
+  p.h = c.take<char>(static_cast<size_t>(R) * C * d_ff * eb);
+  p.y = c.take<char>(static_cast<size_t>(R) * C * d * eb);
+  p.bytes = align_up(c.off);
+  return p;
+}
+
 template <class T>
 T* pick(T* user, T* fallback) {
   return user ? user : fallback;
@@ -442,6 +495,97 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
               "gemm dW_gate");
   MOE_HIP_TRY(moe::launch_gemm_down(b.duT, b.kfull_f, b.mtile_f, b.XT, E, F, d, b.Kp, bf16, dW_up, s),
               "gemm dW_up");
+  return MOE_OK;
+}
+
+int moe_replica_plan(const int32_t* routed_count, int32_t E, int32_t extra, int32_t* replicas) {
+  if (!routed_count || !replicas || E < 1 || extra < 0)
+    return fail(MOE_ERR_INVALID_ARG, "need routed_count, replicas, E >= 1, extra >= 0");
+  for (int e = 0; e < E; ++e) replicas[e] = 1;
+  for (int n = 0; n < extra; ++n) {  // the highest load per replica gets the next one
+    int best = 0;
+    for (int e = 1; e < E; ++e)
+      if (static_cast<int64_t>(routed_count[e]) * replicas[best] > static_cast<int64_t>(routed_count[best]) * replicas[e])
+        best = e;
+    ++replicas[best];
+  }
+  return MOE_OK;
+}
+
+int moe_replicated_workspace_size(int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k, float cf, int32_t P,
+                                  int32_t R, moe_dtype_t dtype, size_t* bytes) {
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  int64_t C;
+  int st = check_layer_shape(T, d, d_ff, E, k, cf, P, dtype, &C);
+  if (st != MOE_OK || (st = check_replicas(E, R, C)) != MOE_OK) return st;
+  *bytes = plan_replicated(nullptr, T, d, d_ff, E, k, C, P, R, elem_bytes(dtype)).bytes;
+  return MOE_OK;
+}
+
+int moe_layer_forward_replicated(const void* x, const void* W_router, const float* router_bias, const void* W_gate,
+                                 const void* W_up, const void* W_down, int64_t T, int64_t d, int64_t d_ff, int32_t E,
+                                 int32_t k, float cf, int32_t P, int32_t max_ranks, const int32_t* replicas,
+                                 int32_t R, moe_dtype_t dtype, void* out, moe_stats_t* stats, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  int64_t C;
+  int st = check_layer_shape(T, d, d_ff, E, k, cf, P, dtype, &C);
+  if (st != MOE_OK) return st;
+  if ((st = check_rank_limit(E, k, P, max_ranks)) != MOE_OK || (st = check_replicas(E, R, C)) != MOE_OK) return st;
+  if (!x || !W_router || !W_gate || !W_up || !W_down || !out || !replicas)
+    return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
+  const int eb = elem_bytes(dtype);
+  if (overlaps(x, static_cast<size_t>(T * d * eb), out, static_cast<size_t>(T * d * eb)))
+    return fail(MOE_ERR_INVALID_ARG, "out overlaps x");
+  if (T == 0) return MOE_OK;
+  const ReplPlan need = plan_replicated(nullptr, T, d, d_ff, E, k, C, P, R, eb);
+  if (!workspace || workspace_bytes < need.bytes || reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need.bytes);
+  ReplPlan p = plan_replicated(workspace, T, d, d_ff, E, k, C, P, R, eb);
+  moe_stats_t none;
+  std::memset(&none, 0, sizeof(none));
+  const moe_stats_t& S = stats ? *stats : none;
+  int32_t* idx = pick(S.topk_idx, p.idx);
+  float* w = pick(S.topk_w, p.w);
+  int32_t* slot = pick(S.slot, p.slot);
+  int32_t* inst = pick(S.instance, p.inst);
+  int32_t* routed = pick(S.routed_count, p.routed);
+  int32_t* kept = pick(S.kept_count, p.kept);
+  int32_t* send = pick(S.send_count, p.send);
+  int64_t* totals = pick(S.totals, p.totals);
+  void* buckets = pick(S.buckets, p.buckets);
+  int32_t* src = S.src;
+  const bool bf16 = dtype == MOE_DTYPE_BF16;
+  auto s = static_cast<hipStream_t>(stream);
+  const int64_t nt = moe::ceil_div(T, moe::kTileTokens);
+  const int bm = moe::grouped_gemm_bm(bf16, C);
+  const int64_t no_cap = T * k;  // a capacity nothing exceeds
+
+  // routing, then each copy's token-order rank among its expert's copies
+  const int splits = moe::router_splits(T, d, E, bf16);
+  const bool fused_hist = moe::route_builds_histogram(k);
+  MOE_HIP_TRY(moe::launch_router_logits(x, W_router, T, d, E, bf16, splits, p.logits, s), "router logits");
+  MOE_HIP_TRY(moe::launch_route(p.logits, splits, router_bias, T, E, k, nullptr, idx, w,
+                                fused_hist ? p.tile_cnt : nullptr, P, max_ranks, s),
+              "route");
+  if (!fused_hist) MOE_HIP_TRY(moe::launch_tile_hist(idx, T, k, E, p.tile_cnt, s), "tile histogram");
+  MOE_HIP_TRY(moe::launch_scan(p.tile_cnt, nt, E, no_cap, P, d * eb, k, T, p.tile_off, routed, p.kept1, p.send1,
+                               p.totals1, 0, nullptr, nullptr, s),
+              "scan (experts)");
+  MOE_HIP_TRY(moe::launch_slots(idx, p.tile_off, T, k, E, no_cap, p.qrank, nullptr, nullptr, s), "ranks");
+  // instances, then the capacity-bounded permutation over them
+  MOE_HIP_TRY(moe::launch_replica_layout(replicas, E, R, P, p.inst_off, p.wmap, p.place, s), "replica layout");
+  MOE_HIP_TRY(moe::launch_instances(idx, p.qrank, replicas, p.inst_off, T * k, R, inst, s), "instances");
+  MOE_HIP_TRY(moe::launch_tile_hist(inst, T, k, R, p.tile_cnt, s), "tile histogram (instances)");
+  MOE_HIP_TRY(moe::launch_scan(p.tile_cnt, nt, R, C, P, d * eb, k, T, p.tile_off, p.routed2, kept, send, totals,
+                               bm, p.mtile, src, s, p.place),
+              "scan (instances)");
+  MOE_HIP_TRY(moe::launch_slots(inst, p.tile_off, T, k, R, C, slot, src, totals, s), "slots");
+  MOE_HIP_TRY(moe::launch_scatter_rows(x, inst, slot, T, k, C, d * eb, buckets, s), "scatter");
+  MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, p.mtile, W_gate, W_up, R, C, d, d_ff, bf16, p.h, s, p.wmap),
+              "grouped gemm (gate, up)");
+  MOE_HIP_TRY(moe::launch_gemm_down(p.h, kept, p.mtile, W_down, R, C, d, d_ff, bf16, p.y, s, p.wmap),
+              "grouped gemm (down)");
+  MOE_HIP_TRY(moe::launch_combine(x, p.y, inst, w, slot, T, d, k, C, bf16, out, s), "combine");
   return MOE_OK;
 }
 

@@ -93,7 +93,8 @@ __device__ void mtile_prefix(const int* kept_s, int E, int bm, int32_t* mtile_of
 __global__ __launch_bounds__(1024) void scan_finalize_kernel(
     const int32_t* __restrict__ tile_cnt, int64_t nt, int E, int64_t C, int P, int64_t row_bytes, int k,
     int64_t T, int32_t* __restrict__ tile_off, int32_t* __restrict__ routed, int32_t* __restrict__ kept,
-    int32_t* __restrict__ send, int64_t* __restrict__ totals, int bm, int32_t* __restrict__ mtile_off) {
+    int32_t* __restrict__ send, int64_t* __restrict__ totals, int bm, int32_t* __restrict__ mtile_off,
+    const int32_t* __restrict__ place) {
   __shared__ int part[16][65];
   __shared__ int kept_s[4096];
   __shared__ int send_s[4096];  // kept rows per rank (P <= E)
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(1024) void scan_finalize_kernel(
         kept[e] = kv;
         kept_s[e] = kv;
         atomicAdd(&ksum, static_cast<unsigned long long>(kv));  // integer sums: order-free
-        atomicAdd(&send_s[e / per], kv);
+        atomicAdd(&send_s[place ? place[e] : e / per], kv);
       }
     }
     __syncthreads();
@@ -267,6 +268,58 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restri
   }
 }
 
+// Replica layout, one block: inst_off [E+1] = exclusive prefix of the replica
+// counts (each taken as at least 1), expert of each instance (wmap [R]) and its
+// rank (place [R]): replica j of expert e on rank (e / (E/P) + j) mod P.
+__global__ __launch_bounds__(1024) void replica_layout_kernel(const int32_t* __restrict__ replicas, int E, int R,
+                                                              int P, int32_t* __restrict__ inst_off,
+                                                              int32_t* __restrict__ wmap,
+                                                              int32_t* __restrict__ place) {
+  __shared__ int sh[17];
+  for (int i = threadIdx.x; i < R; i += blockDim.x) {  // instances no replica reaches: expert 0, rank 0
+    wmap[i] = 0;
+    place[i] = 0;
+  }
+  int v[4];
+  int local = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = threadIdx.x * 4 + q;
+    v[q] = e < E ? max(replicas[e], 1) : 0;
+    local += v[q];
+  }
+  int total;
+  int run = block_exclusive_scan_1024(local, &total, sh);
+  const int per = E / P;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = threadIdx.x * 4 + q;
+    if (e >= E) continue;
+    inst_off[e] = run;
+    for (int j = 0; j < v[q] && run + j < R; ++j) {
+      wmap[run + j] = e;
+      place[run + j] = (e / per + j) % P;
+    }
+    run += v[q];
+  }
+  if (threadIdx.x == 0) inst_off[E] = total;
+}
+
+// Instance of each copy: copy (t, j) of expert e with token-order rank q among
+// e's copies goes to instance inst_off[e] + q mod r (clamped below R).
+__global__ __launch_bounds__(256) void instance_kernel(const int32_t* __restrict__ idx,
+                                                       const int32_t* __restrict__ qrank,
+                                                       const int32_t* __restrict__ replicas,
+                                                       const int32_t* __restrict__ inst_off, int64_t n, int R,
+                                                       int32_t* __restrict__ inst) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int e = idx[i];
+    const int r = max(replicas[e], 1);
+    inst[i] = min(inst_off[e] + qrank[i] % r, R - 1);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_tile_hist(const int32_t* idx, int64_t T, int k, int E, int32_t* tile_cnt,
@@ -281,9 +334,9 @@ hipError_t launch_tile_hist(const int32_t* idx, int64_t T, int k, int E, int32_t
 hipError_t launch_scan(const int32_t* tile_cnt, int64_t nt, int E, int64_t C, int P,
                        int64_t row_bytes, int k, int64_t T, int32_t* tile_off, int32_t* routed,
                        int32_t* kept, int32_t* send, int64_t* totals, int bm, int32_t* mtile_off,
-                       int32_t* src, hipStream_t s) {
+                       int32_t* src, hipStream_t s, const int32_t* place) {
   scan_finalize_kernel<<<dim3(1), dim3(1024), 0, s>>>(tile_cnt, nt, E, C, P, row_bytes, k, T, tile_off, routed,
-                                                      kept, send, totals, bm, mtile_off);
+                                                      kept, send, totals, bm, mtile_off, place);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !src) return err;
   const unsigned gx = static_cast<unsigned>(std::min<int64_t>(ceil_div(C, 256), 64));
@@ -320,6 +373,20 @@ hipError_t launch_scatter_rows(const void* x, const int32_t* idx, const int32_t*
     scatter_rows_kernel<2><<<grid, dim3(256), 0, s>>>(xv, idx, slot, T, k, C, V, bv);
   else
     scatter_rows_kernel<4><<<grid, dim3(256), 0, s>>>(xv, idx, slot, T, k, C, V, bv);
+  return hipGetLastError();
+}
+
+hipError_t launch_replica_layout(const int32_t* replicas, int E, int R, int P, int32_t* inst_off, int32_t* wmap,
+                                 int32_t* place, hipStream_t s) {
+  replica_layout_kernel<<<dim3(1), dim3(1024), 0, s>>>(replicas, E, R, P, inst_off, wmap, place);
+  return hipGetLastError();
+}
+
+hipError_t launch_instances(const int32_t* idx, const int32_t* qrank, const int32_t* replicas,
+                            const int32_t* inst_off, int64_t n, int R, int32_t* inst, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  instance_kernel<<<dim3(static_cast<unsigned>(std::min<int64_t>(ceil_div(n, 256), 4096))), dim3(256), 0, s>>>(
+      idx, qrank, replicas, inst_off, n, R, inst);
   return hipGetLastError();
 }
 

@@ -5,8 +5,10 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
+import oracle
 import routing_dispatch_expert_amd as moe
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -138,3 +140,23 @@ def test_library_has_no_torch_dependency():
     out = subprocess.run(["ldd", moe.LIB_PATH], capture_output=True, text=True).stdout
     assert "torch" not in out and "python" not in out
     assert isinstance(moe.lib(), ctypes.CDLL)
+
+
+def test_replica_plan_matches_the_oracle():
+    rng = np.random.default_rng(41)
+    for _ in range(50):
+        E = int(rng.integers(1, 70))
+        routed = rng.integers(0, 5000, size=E).astype(np.int32)
+        extra = int(rng.integers(0, 40))
+        assert np.array_equal(moe.moe_replica_plan(routed, extra), oracle.replica_plan(routed, extra))
+
+
+@pytest.mark.parametrize("R", [7, 4097])
+def test_replicated_layer_rejects_bad_instance_counts(R):
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_layer_forward_replicated(FAKE, FAKE, None, FAKE, FAKE, FAKE, 64, 128, 256, 8, 2, 1.25, 1, 0, FAKE, R,
+                                         "bf16", FAKE * 2, None, FAKE * 3, 1 << 40)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError):
+        moe.moe_layer_forward_replicated(FAKE, FAKE, None, FAKE, FAKE, FAKE, 64, 128, 256, 8, 2, 1.25, 1, 0, None, 8,
+                                         "bf16", FAKE * 2, None, FAKE * 3, 1 << 40)
