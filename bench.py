@@ -12,6 +12,9 @@ times from HIP events recorded by the library around each stage, the
 roofline of the dominant kernel, and the CPU oracle timed on a bounded sample
 of the same workload.
 
+With --replicas EXTRA a step is one call of moe_layer_forward_replicated,
+with EXTRA replicas dealt to the most loaded experts of the same batch.
+
 With --backward a step is one call of moe_layer_backward instead (the
 gradients of x, the router and the expert weights for a seeded dout), and the
 line reports backward tokens/s.
@@ -48,22 +51,27 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-stage event loop")
     ap.add_argument("--backward", action="store_true", help="time moe_layer_backward instead of the forward")
+    ap.add_argument("--replicas", type=int, default=-1, metavar="EXTRA",
+                    help="time moe_layer_forward_replicated with EXTRA replicas dealt greedily to the most loaded "
+                         "experts (counts from one plain forward of the same batch)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first copy a buffer of this many MiB on the device (a reference kernel of known "
                          "traffic for hardware counters)")
     return ap.parse_args()
 
 
-def stage_work(wl, n_kept: int, touched: int):
+def stage_work(wl, n_kept: int, touched: int, buckets: int):
     """Algorithmic HBM bytes (and flops) of each stage for this run: kept rows
-    only, touched experts' weights only, every operand moved once."""
+    only, touched buckets' weights only (a replicated expert's weights once
+    per instance, as each instance would hold its own copy), every operand
+    moved once. buckets = E, or the instance count R when replicated."""
     T, d, f, E, k = wl.T, wl.d, wl.d_ff, wl.E, wl.k
     b = wl.elem_bytes
     nt = -(-T // 64)
     return {
         "router": dict(bytes=T * d * b + E * d * b + T * E * 4, flops=2 * T * d * E, bound="hbm"),
         "route": dict(bytes=T * E * 4 + T * k * 8, flops=0, bound="hbm"),
-        "slots": dict(bytes=3 * T * k * 4 + 4 * nt * E * 4, flops=0, bound="hbm"),
+        "slots": dict(bytes=3 * T * k * 4 + 4 * nt * buckets * 4, flops=0, bound="hbm"),
         "scatter": dict(bytes=(T + n_kept) * d * b + T * k * 8, flops=0, bound="hbm"),
         "gate_up": dict(bytes=touched * 2 * f * d * b + n_kept * (d + f) * b, flops=4 * n_kept * d * f,
                         bound="mfma"),
@@ -85,7 +93,7 @@ def read_traffic(gemm_src_sha: str):
     return float(m_b.group(1))
 
 
-def cpu_baseline(wl, host_w, sample: int):
+def cpu_baseline(wl, host_w, sample: int, replicas=None):
     import numpy as np
     import oracle
     try:
@@ -99,7 +107,7 @@ def cpu_baseline(wl, host_w, sample: int):
         t0 = time.perf_counter()
         oracle.layer_forward(wl.x, wl.wr, lambda e: (host_w[0][e], host_w[1][e], host_w[2][e]), wl.T, wl.d,
                              wl.d_ff, wl.E, wl.k, wl.cf, wl.dtype, P=wl.P, bias=wl.bias_vec, tokens=tokens,
-                             max_ranks=wl.max_ranks)
+                             max_ranks=wl.max_ranks, replicas=replicas)
         times.append(time.perf_counter() - t0)
     dt = sorted(times)[1]
     return {"value": round(tokens.size / dt, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
@@ -240,6 +248,26 @@ def main():
         moe.moe_layer_forward(x, wr, bias, wg, wu, wd, T, d, d_ff, E, k, cf, P, wl.max_ranks, wl.dtype, outs["out"],
                               outs, ws, ws_bytes, stream)
 
+    reps, repl_cfg = None, {}
+    if args.replicas >= 0:
+        step()
+        torch.cuda.synchronize()
+        base_dropped = int(outs["totals"][0].item())
+        reps = moe.moe_replica_plan(outs["routed_count"].cpu().numpy(), args.replicas)
+        R = int(reps.sum())
+        reps_dev = torch.from_numpy(reps).to(dev)
+        outs["kept_count"] = torch.empty(R, **i32)
+        outs["instance"] = torch.empty((T, k), **i32)
+        ws_bytes = moe.moe_replicated_workspace_size(T, d, d_ff, E, k, cf, P, R, wl.dtype)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        repl_cfg = {"replicas_extra": args.replicas, "instances": R, "replicated_experts": int((reps > 1).sum()),
+                    "max_replicas": int(reps.max()), "dropped_without_replicas": base_dropped}
+        print(f"[bench] replicated layer: {R} instances, replicas {reps.tolist()}", file=sys.stderr, flush=True)
+
+        def step():  # noqa: F811 (the replicated layer replaces the plain one)
+            moe.moe_layer_forward_replicated(x, wr, bias, wg, wu, wd, T, d, d_ff, E, k, cf, P, wl.max_ranks, reps_dev,
+                                             R, wl.dtype, outs["out"], outs, ws, ws_bytes, stream)
+
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -267,7 +295,7 @@ def main():
     kept = outs["kept_count"].cpu().numpy()
     n_kept, touched = int(kept.sum()), int((kept > 0).sum())
     totals = outs["totals"].cpu().numpy().tolist()
-    work = stage_work(wl, n_kept, touched)
+    work = stage_work(wl, n_kept, touched, int(kept.size))
 
     stages = {}
     if not args.no_profile:
@@ -315,16 +343,17 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on {min(args.cpu_sample, T)} tokens", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, host_w, args.cpu_sample)
+        cpu = cpu_baseline(wl, host_w, args.cpu_sample, reps)
 
+    metric = METRIC if reps is None else METRIC + " (hot experts replicated)"
     line = {
-        "metric": METRIC, "value": round(T * args.steps / wall, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": metric, "value": round(T * args.steps / wall, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic (seeded Gaussian inputs and random-init weights of the named shape)",
         "config": {"workload": wl.name, "T": T, "d": d, "E": E, "k": k, "d_ff": d_ff, "cf": cf, "P": P,
                    "max_ranks": wl.max_ranks, "C": C, "N_kept": n_kept, "touched_experts": touched,
-                   "dropped": totals[0]},
+                   "dropped": totals[0], **repl_cfg},
         "gpu_ms_per_step": round(gpu_ms, 4),
         "grouped_gemm_mfma_frac": None if not stages else round(
             (work["gate_up"]["flops"] + work["down"]["flops"]) /

@@ -239,7 +239,9 @@ int moe_combine(const void* x, const void* y, const int32_t* topk_idx, const flo
                 const int32_t* slot, int64_t T, int64_t d, int32_t E, int32_t k, int64_t C,
                 moe_dtype_t dtype, void* out, void* stream);
 
-/* Stages of moe_layer_forward, in launch order. */
+/* Stages of moe_layer_forward (and of moe_layer_forward_replicated, whose
+ * ROUTE stage also ranks each expert's copies and deals them to instances),
+ * in launch order. */
 enum {
   MOE_STAGE_ROUTER = 0,   /* scores on the matrix cores */
   MOE_STAGE_ROUTE = 1,    /* top-k and gates */
@@ -252,9 +254,10 @@ enum {
 };
 
 /* Profiling aid. With events set (2 * MOE_NUM_STAGES caller-created
- * hipEvent_t handles), moe_layer_forward on the calling thread records
- * events[2 i] on its stream just before stage i and events[2 i + 1] just
- * after, so the caller can read each stage's GPU time. events = NULL turns
+ * hipEvent_t handles), moe_layer_forward and moe_layer_forward_replicated
+ * on the calling thread record events[2 i] on their stream just before
+ * stage i and events[2 i + 1] just after, so the caller can read each
+ * stage's GPU time. events = NULL turns
  * this off (the default). Error: n_events != 2 * MOE_NUM_STAGES. */
 int moe_set_stage_events(void* const* events, int n_events);
 

@@ -563,7 +563,10 @@ int moe_layer_forward_replicated(const void* x, const void* W_router, const floa
   // routing, then each copy's token-order rank among its expert's copies
   const int splits = moe::router_splits(T, d, E, bf16);
   const bool fused_hist = moe::route_builds_histogram(k);
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTER, false, s), "event");
   MOE_HIP_TRY(moe::launch_router_logits(x, W_router, T, d, E, bf16, splits, p.logits, s), "router logits");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTER, true, s), "event");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTE, false, s), "event");
   MOE_HIP_TRY(moe::launch_route(p.logits, splits, router_bias, T, E, k, nullptr, idx, w,
                                 fused_hist ? p.tile_cnt : nullptr, P, max_ranks, s),
               "route");
@@ -575,17 +578,28 @@ int moe_layer_forward_replicated(const void* x, const void* W_router, const floa
   // instances, then the capacity-bounded permutation over them
   MOE_HIP_TRY(moe::launch_replica_layout(replicas, E, R, P, p.inst_off, p.wmap, p.place, s), "replica layout");
   MOE_HIP_TRY(moe::launch_instances(idx, p.qrank, replicas, p.inst_off, T * k, R, inst, s), "instances");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTE, true, s), "event");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_SLOTS, false, s), "event");
   MOE_HIP_TRY(moe::launch_tile_hist(inst, T, k, R, p.tile_cnt, s), "tile histogram (instances)");
   MOE_HIP_TRY(moe::launch_scan(p.tile_cnt, nt, R, C, P, d * eb, k, T, p.tile_off, p.routed2, kept, send, totals,
                                bm, p.mtile, src, s, p.place),
               "scan (instances)");
   MOE_HIP_TRY(moe::launch_slots(inst, p.tile_off, T, k, R, C, slot, src, totals, s), "slots");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_SLOTS, true, s), "event");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, false, s), "event");
   MOE_HIP_TRY(moe::launch_scatter_rows(x, inst, slot, T, k, C, d * eb, buckets, s), "scatter");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, true, s), "event");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, false, s), "event");
   MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, p.mtile, W_gate, W_up, R, C, d, d_ff, bf16, p.h, s, p.wmap),
               "grouped gemm (gate, up)");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, true, s), "event");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, false, s), "event");
   MOE_HIP_TRY(moe::launch_gemm_down(p.h, kept, p.mtile, W_down, R, C, d, d_ff, bf16, p.y, s, p.wmap),
               "grouped gemm (down)");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, true, s), "event");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_COMBINE, false, s), "event");
   MOE_HIP_TRY(moe::launch_combine(x, p.y, inst, w, slot, T, d, k, C, bf16, out, s), "combine");
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_COMBINE, true, s), "event");
   return MOE_OK;
 }
 
