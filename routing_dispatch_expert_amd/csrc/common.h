@@ -83,15 +83,27 @@ hipError_t launch_scatter_rows(const void* x, const int32_t* idx, const int32_t*
 // Row-tile height the grouped GEMM uses for these sizes (the mtile map must
 // be built for the same value).
 int grouped_gemm_bm(bool bf16, int64_t C);
+// Scratch that lets the 256 x 256 GEMM split the tiles of its last, partly
+// filled round over K: fp32 partial tiles of up to kSplitUnits work-groups and
+// one arrival counter per split tile (cleared by the launcher).
+constexpr int kSplitUnits = 256;
+struct SplitK {
+  float* part;    // [kSplitUnits][256 * 256]
+  int32_t* tick;  // [kSplitUnits]
+};
+size_t split_k_bytes();
+SplitK split_k_carve(void* base);  // base: 256-byte aligned, split_k_bytes() long
 // GEMM 1: h = silu(X Wg^T) * (X Wu^T) on rows < kept. With wmap [E], bucket
-// e uses the weights of expert wmap[e] (replicated experts).
+// e uses the weights of expert wmap[e] (replicated experts). With sk, a last
+// round that would leave most of the chip idle is split over K.
 hipError_t launch_gemm_gate_up(const void* buckets, const int32_t* kept, const int32_t* mtile_off,
                                const void* wg, const void* wu, int E, int64_t C, int64_t d,
-                               int64_t d_ff, bool bf16, void* h, hipStream_t s, const int32_t* wmap = nullptr);
-// GEMM 2: y = h Wd^T on rows < kept (wmap as above).
+                               int64_t d_ff, bool bf16, void* h, hipStream_t s, const int32_t* wmap = nullptr,
+                               const SplitK* sk = nullptr);
+// GEMM 2: y = h Wd^T on rows < kept (wmap and sk as above).
 hipError_t launch_gemm_down(const void* h, const int32_t* kept, const int32_t* mtile_off,
                             const void* wd, int E, int64_t C, int64_t d, int64_t d_ff, bool bf16,
-                            void* y, hipStream_t s, const int32_t* wmap = nullptr);
+                            void* y, hipStream_t s, const int32_t* wmap = nullptr, const SplitK* sk = nullptr);
 
 // ---- backward (backward.hip) ----
 // dst[b][c][col_off + r] = src[b][r][c] for r < valid[b] (or R), 0 for r < Rp.

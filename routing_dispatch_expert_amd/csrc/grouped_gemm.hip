@@ -14,6 +14,7 @@
 // padding rows beyond kept[e] cost no tiles: a work-group maps its row-tile id
 // to (expert, tile) by binary search over that prefix and exits when the id
 // is past the last live tile.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -66,15 +67,10 @@ __device__ inline float silu_bf16(float g) {
 // ---------------------------------------------------------------------------
 constexpr int kGroupN = 8;
 
+// Expert, first row and column tile of live tile `lid`.
 template <int BM>
-__device__ inline bool tile_of_block(const int32_t* __restrict__ mtile_off, int E, int nt_count,
-                                     int* e_out, int* m0_out, int* nt_out, int* lid_out = nullptr) {
-  const int64_t live = static_cast<int64_t>(mtile_off[E]) * nt_count;
-  const int64_t per_xcd = (live + 7) / 8;
-  const int64_t slot = blockIdx.x / 8;
-  if (slot >= per_xcd) return false;
-  const int64_t lid = (blockIdx.x % 8) * per_xcd + slot;
-  if (lid >= live) return false;
+__device__ inline void tile_coords(const int32_t* __restrict__ mtile_off, int E, int nt_count, int64_t lid,
+                                   int* e_out, int* m0_out, int* nt_out) {
   const int e = owner_expert(mtile_off, E, static_cast<int>(lid / nt_count));
   const int mte = mtile_off[e + 1] - mtile_off[e];
   const int64_t li = lid - static_cast<int64_t>(mtile_off[e]) * nt_count;
@@ -83,7 +79,72 @@ __device__ inline bool tile_of_block(const int32_t* __restrict__ mtile_off, int 
   *e_out = e;
   *m0_out = (r % mte) * BM;
   *nt_out = static_cast<int>(grp * kGroupN + r / mte);
-  if (lid_out) *lid_out = static_cast<int>(lid);
+}
+
+// Live tile of block b when the first n live tiles are spread over the XCDs
+// (block b runs on XCD b % 8 and takes tile (b % 8) * ceil(n / 8) + b / 8).
+__device__ inline int64_t xcd_tile(int64_t b, int64_t n) {
+  const int64_t per_xcd = (n + 7) / 8;
+  const int64_t slot = b / 8;
+  if (slot >= per_xcd) return -1;
+  const int64_t lid = (b % 8) * per_xcd + slot;
+  return lid < n ? lid : -1;
+}
+
+template <int BM>
+__device__ inline bool tile_of_block(const int32_t* __restrict__ mtile_off, int E, int nt_count,
+                                     int* e_out, int* m0_out, int* nt_out) {
+  const int64_t lid = xcd_tile(blockIdx.x, static_cast<int64_t>(mtile_off[E]) * nt_count);
+  if (lid < 0) return false;
+  tile_coords<BM>(mtile_off, E, nt_count, lid, e_out, m0_out, nt_out);
+  return true;
+}
+
+// Split-K of the last round. With G work-groups resident at once and L live
+// tiles, rem = L % G tiles would run alone in a last round. When G / rem >= 2
+// each of them is cut into s = min(G / rem, nk / 2, kMaxSplit) K ranges of
+// whole stage pairs, one block each (rem * s <= G blocks), after the L - rem
+// whole tiles. Block b then holds K stages [kb, ke) of split tile ti as its
+// chunk c of s; s = 1 means a whole tile.
+constexpr int kMaxSplit = 8;
+
+struct Work {
+  int e, m0, nt;
+  int64_t kb, ke;
+  int s, c, ti;
+};
+
+template <int BM>
+__device__ inline bool work_of_block(const int32_t* __restrict__ mtile_off, int E, int nt_count, int64_t nk,
+                                     int G, Work* w) {
+  const int64_t live = static_cast<int64_t>(mtile_off[E]) * nt_count;
+  int64_t rem = G > 0 ? live % G : 0;
+  int64_t s = rem > 0 ? G / rem : 1;
+  s = s < nk / 2 ? s : nk / 2;
+  s = s < kMaxSplit ? s : kMaxSplit;
+  if (s < 2) rem = 0, s = 1;
+  const int64_t whole = live - rem;
+  int64_t lid;
+  w->s = 1;
+  w->c = 0;
+  w->ti = 0;
+  w->kb = 0;
+  w->ke = nk;
+  if (blockIdx.x < whole) {
+    lid = xcd_tile(blockIdx.x, whole);
+    if (lid < 0) return false;
+  } else {
+    const int64_t u = blockIdx.x - whole;
+    if (u >= rem * s) return false;
+    w->s = static_cast<int>(s);
+    w->ti = static_cast<int>(u / s);
+    w->c = static_cast<int>(u % s);
+    lid = whole + w->ti;
+    const int64_t pairs = nk / 2;
+    w->kb = 2 * (w->c * pairs / s);
+    w->ke = 2 * ((w->c + 1) * pairs / s);
+  }
+  tile_coords<BM>(mtile_off, E, nt_count, lid, &w->e, &w->m0, &w->nt);
   return true;
 }
 
@@ -362,7 +423,8 @@ template <bool SWIGLU>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_dma_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     bf16_t* __restrict__ out, const int32_t* __restrict__ kept, const int32_t* __restrict__ mtile_off,
-    int E, int64_t C, int64_t K, int64_t N, int nt_count, const int32_t* __restrict__ wmap) {
+    int E, int64_t C, int64_t K, int64_t N, int nt_count, const int32_t* __restrict__ wmap,
+    float* __restrict__ part, int32_t* __restrict__ tick, int G) {
   constexpr int BM = 256, BN = 256, BK = 64, TM = 4, TN = 4;
   constexpr int CH = BK / 8;                    // 16-byte chunks per LDS row
   constexpr int BNO = SWIGLU ? BN / 2 : BN;
@@ -370,15 +432,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int NMFMA = TM * TN, NFRAG = TM + TN;
   __shared__ uint4 As0[BM * CH], As1[BM * CH];
   __shared__ uint4 Bs0[BN * CH], Bs1[BN * CH];
+  __shared__ int arrival;
 
-  int e, m0, nt;
-  if (!tile_of_block<BM>(mtile_off, E, nt_count, &e, &m0, &nt)) return;
-  e = __builtin_amdgcn_readfirstlane(e);
-  m0 = __builtin_amdgcn_readfirstlane(m0);
-  nt = __builtin_amdgcn_readfirstlane(nt);
+  Work wk;
+  if (!work_of_block<BM>(mtile_off, E, nt_count, K / BK, G, &wk)) return;
+  const int e = __builtin_amdgcn_readfirstlane(wk.e);
+  const int m0 = __builtin_amdgcn_readfirstlane(wk.m0);
+  const int nt = __builtin_amdgcn_readfirstlane(wk.nt);
+  const int split = __builtin_amdgcn_readfirstlane(wk.s);
+  const int chunk = __builtin_amdgcn_readfirstlane(wk.c);
+  const int ti = __builtin_amdgcn_readfirstlane(wk.ti);
+  const int64_t kb = __builtin_amdgcn_readfirstlane(static_cast<int>(wk.kb));  // stages [kb, ke): even, >= 2
+  const int64_t ke = __builtin_amdgcn_readfirstlane(static_cast<int>(wk.ke));
   const int rows = __builtin_amdgcn_readfirstlane(kept[e]);
   const int64_t n0 = static_cast<int64_t>(nt) * BNO;
-  const int64_t nk = K / BK;  // even, at least 2
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -486,17 +553,62 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   using T_ = std::true_type;
   using F_ = std::false_type;
 
-  dma(As0, Bs0, 0);
+  dma(As0, Bs0, kb);
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
   fload(As0, Bs0, 0, 0);
-  int64_t k = 0;
-  for (; k + 2 < nk; k += 2) {
+  int64_t k = kb;
+  for (; k + 2 < ke; k += 2) {
     stage(T_{}, As0, Bs0, As1, Bs1, k);
     stage(T_{}, As1, Bs1, As0, Bs0, k + 1);
   }
   stage(T_{}, As0, Bs0, As1, Bs1, k);
   stage(F_{}, As1, Bs1, As0, Bs0, k + 1);
+
+  if (split > 1) {
+    // Chunk of a split tile: publish the fp32 partial (thread t writes its
+    // 64 float4s at [g][t], coalesced), count the arrival; the last of the s
+    // blocks to arrive adds the s partials in chunk order (its own from
+    // registers), so the sum does not depend on which block came last.
+    constexpr int NG = TM * TN * 4;  // float4 groups per thread
+    float4* mine = reinterpret_cast<float4*>(part) + static_cast<int64_t>(ti * split + chunk) * NG * 256;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          mine[((i * TN + j) * 4 + q) * 256 + tid] =
+              float4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) arrival = atomicAdd(&tick[ti], 1);
+    __syncthreads();
+    if (arrival != split - 1) return;
+    __threadfence();
+    const float4* first = reinterpret_cast<const float4*>(part) + static_cast<int64_t>(ti * split) * NG * 256;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int g = (i * TN + j) * 4 + q;
+          const float4 own{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          float4 t = chunk == 0 ? own : first[g * 256 + tid];
+          for (int c = 1; c < split; ++c) {
+            const float4 v = c == chunk ? own : first[(static_cast<int64_t>(c) * NG + g) * 256 + tid];
+            t.x += v.x;
+            t.y += v.y;
+            t.z += v.z;
+            t.w += v.w;
+          }
+          acc[i][j][4 * q] = t.x;
+          acc[i][j][4 * q + 1] = t.y;
+          acc[i][j][4 * q + 2] = t.z;
+          acc[i][j][4 * q + 3] = t.w;
+        }
+  }
 
   // the stage buffers are free: one per wave for the epilogue
   wait_vm_lgkm0<0>();
@@ -830,6 +942,16 @@ constexpr int kBigTileMinC = MOE_BIG_TILE_MIN_C;
 // Row tiles of the skinny kernel when every expert holds this few rows.
 constexpr int kSkinnyMaxC = kSkinnyRows;
 
+size_t split_k_bytes() {
+  return static_cast<size_t>(kSplitUnits) * 256 * 256 * sizeof(float) + kSplitUnits * sizeof(int32_t);
+}
+
+SplitK split_k_carve(void* base) {
+  if (!base) return SplitK{nullptr, nullptr};
+  auto* p = static_cast<float*>(base);
+  return SplitK{p, reinterpret_cast<int32_t*>(p + static_cast<size_t>(kSplitUnits) * 256 * 256)};
+}
+
 int grouped_gemm_bm(bool bf16, int64_t C) {
   if (!bf16) return 64;
   if (C <= kSkinnyMaxC) return kSkinnyRows;
@@ -850,13 +972,27 @@ hipError_t launch_skinny(const void* a, const void* b0, const void* b1, void* ou
   return hipGetLastError();
 }
 
+// Work-groups of the 256 x 256 kernel resident at once (one per CU), rounded
+// down to whole rounds over the 8 XCDs; 0 if unknown (no split).
+int resident_groups() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = std::max(8, std::min(cus, kSplitUnits) / 8 * 8);
+  }
+  return cached[dev];
+}
+
 template <int BM, int BN, bool SWIGLU>
 hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out, const int32_t* kept,
                        const int32_t* mtile_off, int E, int64_t C, int64_t K, int64_t N, const int32_t* wmap,
-                       hipStream_t s) {
+                       hipStream_t s, const SplitK* sk = nullptr) {
   const int64_t mt_max = E * ceil_div(C, BM);  // upper bound of live row tiles
   const int64_t nt = ceil_div(N, SWIGLU ? BN / 2 : BN);
-  const int64_t blocks = ceil_div(mt_max * nt, 8) * 8;  // whole rounds over the 8 XCDs
+  int64_t blocks = ceil_div(mt_max * nt, 8) * 8;  // whole rounds over the 8 XCDs
   const auto* pa = static_cast<const bf16_t*>(a);
   const auto* pb0 = static_cast<const bf16_t*>(b0);
   const auto* pb1 = static_cast<const bf16_t*>(b1);
@@ -866,8 +1002,15 @@ hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out,
     gemm_bf16_dma_m128_kernel<SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
         pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap);
   } else if (BM == 256 && BN == 256 && K % 128 == 0) {
+    const int G = sk ? resident_groups() : 0;
+    if (G > 0) {
+      const hipError_t err = launch_fill_i32(sk->tick, G, 0, s);
+      if (err != hipSuccess) return err;
+      blocks += G;  // the split round: at most G blocks beyond the whole tiles
+    }
     gemm_bf16_dma_kernel<SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
-        pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap);
+        pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap, G > 0 ? sk->part : nullptr,
+        G > 0 ? sk->tick : nullptr, G);
   } else {
     gemm_bf16_kernel<BM, BN, SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
         pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap);
@@ -879,13 +1022,14 @@ hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out,
 
 hipError_t launch_gemm_gate_up(const void* buckets, const int32_t* kept, const int32_t* mtile_off,
                                const void* wg, const void* wu, int E, int64_t C, int64_t d,
-                               int64_t d_ff, bool bf16, void* h, hipStream_t s, const int32_t* wmap) {
+                               int64_t d_ff, bool bf16, void* h, hipStream_t s, const int32_t* wmap,
+                               const SplitK* sk) {
   if (E * C == 0) return hipSuccess;
   if (bf16) {
     if (grouped_gemm_bm(true, C) == kSkinnyRows && d % 32 == 0)
       return launch_skinny<true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s);
     if (grouped_gemm_bm(true, C) == 256)
-      return launch_bf16<256, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s);
+      return launch_bf16<256, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s, sk);
     if (d % 64 == 0)
       return launch_bf16<128, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s);
     return launch_bf16<128, 128, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s);
@@ -899,13 +1043,13 @@ hipError_t launch_gemm_gate_up(const void* buckets, const int32_t* kept, const i
 
 hipError_t launch_gemm_down(const void* h, const int32_t* kept, const int32_t* mtile_off,
                             const void* wd, int E, int64_t C, int64_t d, int64_t d_ff, bool bf16,
-                            void* y, hipStream_t s, const int32_t* wmap) {
+                            void* y, hipStream_t s, const int32_t* wmap, const SplitK* sk) {
   if (E * C == 0) return hipSuccess;
   if (bf16) {
     if (grouped_gemm_bm(true, C) == kSkinnyRows && d_ff % 32 == 0)
       return launch_skinny<false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, wmap, s);
     if (grouped_gemm_bm(true, C) == 256)
-      return launch_bf16<256, 256, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, wmap, s);
+      return launch_bf16<256, 256, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, wmap, s, sk);
     if (d_ff % 64 == 0)
       return launch_bf16<128, 256, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, wmap, s);
     return launch_bf16<128, 128, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, wmap, s);

@@ -139,6 +139,7 @@ struct LayerPlan {
   float* w;
   int64_t* totals;
   void *buckets, *h, *y;
+  moe::SplitK split;
   size_t bytes;
 };
 
@@ -163,6 +164,7 @@ LayerPlan plan_layer(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E, in
   p.buckets = c.take<char>(static_cast<size_t>(E) * C * d * eb);
   p.h = c.take<char>(static_cast<size_t>(E) * C * d_ff * eb);
   p.y = c.take<char>(static_cast<size_t>(E) * C * d * eb);
+  p.split = moe::split_k_carve(c.take<char>(moe::split_k_bytes()));
   p.bytes = align_up(c.off);
   return p;
 }
@@ -227,6 +229,7 @@ struct ReplPlan {
       *mtile, *inst_off, *wmap, *place;
   int64_t *totals, *totals1;
   void *buckets, *h, *y;
+  moe::SplitK split;
   size_t bytes;
 };
 
@@ -260,6 +263,7 @@ ReplPlan plan_replicated(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E
   p.buckets = c.take<char>(static_cast<size_t>(R) * C * d * eb);
   p.h = c.take<char>(static_cast<size_t>(R) * C * d_ff * eb);
   p.y = c.take<char>(static_cast<size_t>(R) * C * d * eb);
+  p.split = moe::split_k_carve(c.take<char>(moe::split_k_bytes()));
   p.bytes = align_up(c.off);
   return p;
 }
@@ -376,11 +380,12 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
   MOE_HIP_TRY(moe::launch_scatter_rows(x, idx, slot, T, k, C, d * eb, buckets, s), "scatter");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, false, s), "event");
-  MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, p.mtile, W_gate, W_up, E, C, d, d_ff, bf16, p.h, s),
+  MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, p.mtile, W_gate, W_up, E, C, d, d_ff, bf16, p.h, s, nullptr,
+                                       &p.split),
               "grouped gemm (gate, up)");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, false, s), "event");
-  MOE_HIP_TRY(moe::launch_gemm_down(p.h, kept, p.mtile, W_down, E, C, d, d_ff, bf16, p.y, s),
+  MOE_HIP_TRY(moe::launch_gemm_down(p.h, kept, p.mtile, W_down, E, C, d, d_ff, bf16, p.y, s, nullptr, &p.split),
               "grouped gemm (down)");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_COMBINE, false, s), "event");
@@ -446,10 +451,13 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   MOE_HIP_TRY(moe::launch_slots(p.idx, p.tile_off, T, k, E, C, p.slot, nullptr, p.totals, s), "slots");
   MOE_HIP_TRY(moe::launch_scatter_rows(x, p.idx, p.slot, T, k, C, d * eb, p.buckets, s), "scatter");
   // g = X Wg^T and u = X Wu^T (the plain row-tile GEMM: N = d_ff, K = d)
-  MOE_HIP_TRY(moe::launch_gemm_down(p.buckets, p.kept, p.mtile, W_gate, E, C, F, d, bf16, b.g, s), "gemm g");
-  MOE_HIP_TRY(moe::launch_gemm_down(p.buckets, p.kept, p.mtile, W_up, E, C, F, d, bf16, b.u, s), "gemm u");
+  const moe::SplitK* sk = &p.split;
+  MOE_HIP_TRY(moe::launch_gemm_down(p.buckets, p.kept, p.mtile, W_gate, E, C, F, d, bf16, b.g, s, nullptr, sk),
+              "gemm g");
+  MOE_HIP_TRY(moe::launch_gemm_down(p.buckets, p.kept, p.mtile, W_up, E, C, F, d, bf16, b.u, s, nullptr, sk),
+              "gemm u");
   MOE_HIP_TRY(moe::launch_swiglu_fwd(b.g, b.u, p.h, p.kept, E, C, F, bf16, s), "swiglu");
-  MOE_HIP_TRY(moe::launch_gemm_down(p.h, p.kept, p.mtile, W_down, E, C, d, F, bf16, p.y, s), "gemm y");
+  MOE_HIP_TRY(moe::launch_gemm_down(p.h, p.kept, p.mtile, W_down, E, C, d, F, bf16, p.y, s, nullptr, sk), "gemm y");
 
   // 2. combine backward: dy = w dout on kept rows, dl = gate gradients
   MOE_HIP_TRY(moe::launch_combine_bwd(dout, p.y, p.idx, p.w, p.slot, T, d, k, C, bf16, b.dy, b.dl, s),
@@ -457,14 +465,16 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   // 3. dh = dy Wd (B = Wd^T, [E][d_ff][d]); dg, du
   MOE_HIP_TRY(moe::launch_transpose(W_down, b.WdT, E, d, F, F, d, 0, d, nullptr, d * F, F * d, bf16, s),
               "transpose W_down");
-  MOE_HIP_TRY(moe::launch_gemm_down(b.dy, p.kept, p.mtile, b.WdT, E, C, F, d, bf16, b.dh, s), "gemm dh");
+  MOE_HIP_TRY(moe::launch_gemm_down(b.dy, p.kept, p.mtile, b.WdT, E, C, F, d, bf16, b.dh, s, nullptr, sk),
+              "gemm dh");
   MOE_HIP_TRY(moe::launch_swiglu_bwd(b.dh, b.g, b.u, b.dgu, p.kept, E, C, F, bf16, s), "swiglu backward");
   // 4. dX = [dg | du] [Wg ; Wu] (B = [Wg^T | Wu^T], [E][d][2 d_ff])
   MOE_HIP_TRY(moe::launch_transpose(W_gate, b.WguT, E, F, d, d, 2 * F, 0, F, nullptr, F * d, d * 2 * F, bf16, s),
               "transpose W_gate");
   MOE_HIP_TRY(moe::launch_transpose(W_up, b.WguT, E, F, d, d, 2 * F, F, F, nullptr, F * d, d * 2 * F, bf16, s),
               "transpose W_up");
-  MOE_HIP_TRY(moe::launch_gemm_down(b.dgu, p.kept, p.mtile, b.WguT, E, C, d, 2 * F, bf16, b.dX, s), "gemm dX");
+  MOE_HIP_TRY(moe::launch_gemm_down(b.dgu, p.kept, p.mtile, b.WguT, E, C, d, 2 * F, bf16, b.dX, s, nullptr, sk),
+              "gemm dX");
   // 5. router gradients, then dx = dout + the expert paths + the router path
   MOE_HIP_TRY(moe::launch_router_wgrad(x, p.idx, b.dl, T, k, E, d, bf16, b.rpart, dW_router, d_bias, s),
               "router wgrad");
@@ -489,11 +499,11 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   MOE_HIP_TRY(moe::launch_fill_i32(b.kfull_f, E, static_cast<int32_t>(F), s), "fill");
   MOE_HIP_TRY(moe::launch_mtile_map(b.kfull_d, E, moe::grouped_gemm_bm(bf16, d), b.mtile_d, s), "tile map");
   MOE_HIP_TRY(moe::launch_mtile_map(b.kfull_f, E, moe::grouped_gemm_bm(bf16, F), b.mtile_f, s), "tile map");
-  MOE_HIP_TRY(moe::launch_gemm_down(b.dyT, b.kfull_d, b.mtile_d, b.hT, E, d, F, b.Kp, bf16, dW_down, s),
+  MOE_HIP_TRY(moe::launch_gemm_down(b.dyT, b.kfull_d, b.mtile_d, b.hT, E, d, F, b.Kp, bf16, dW_down, s, nullptr, sk),
               "gemm dW_down");
-  MOE_HIP_TRY(moe::launch_gemm_down(b.dgT, b.kfull_f, b.mtile_f, b.XT, E, F, d, b.Kp, bf16, dW_gate, s),
+  MOE_HIP_TRY(moe::launch_gemm_down(b.dgT, b.kfull_f, b.mtile_f, b.XT, E, F, d, b.Kp, bf16, dW_gate, s, nullptr, sk),
               "gemm dW_gate");
-  MOE_HIP_TRY(moe::launch_gemm_down(b.duT, b.kfull_f, b.mtile_f, b.XT, E, F, d, b.Kp, bf16, dW_up, s),
+  MOE_HIP_TRY(moe::launch_gemm_down(b.duT, b.kfull_f, b.mtile_f, b.XT, E, F, d, b.Kp, bf16, dW_up, s, nullptr, sk),
               "gemm dW_up");
   return MOE_OK;
 }
@@ -590,11 +600,12 @@ int moe_layer_forward_replicated(const void* x, const void* W_router, const floa
   MOE_HIP_TRY(moe::launch_scatter_rows(x, inst, slot, T, k, C, d * eb, buckets, s), "scatter");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, false, s), "event");
-  MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, p.mtile, W_gate, W_up, R, C, d, d_ff, bf16, p.h, s, p.wmap),
+  MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, p.mtile, W_gate, W_up, R, C, d, d_ff, bf16, p.h, s, p.wmap,
+                                       &p.split),
               "grouped gemm (gate, up)");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, false, s), "event");
-  MOE_HIP_TRY(moe::launch_gemm_down(p.h, kept, p.mtile, W_down, R, C, d, d_ff, bf16, p.y, s, p.wmap),
+  MOE_HIP_TRY(moe::launch_gemm_down(p.h, kept, p.mtile, W_down, R, C, d, d_ff, bf16, p.y, s, p.wmap, &p.split),
               "grouped gemm (down)");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_COMBINE, false, s), "event");
@@ -699,7 +710,7 @@ int moe_permute(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, in
 
 int moe_grouped_gemm_workspace_size(int32_t E, int64_t C, size_t* bytes) {
   if (!bytes || E < 1 || C < 1) return fail(MOE_ERR_INVALID_ARG, "need bytes, E >= 1, C >= 1");
-  *bytes = align_up((static_cast<size_t>(E) + 1) * sizeof(int32_t));
+  *bytes = align_up((static_cast<size_t>(E) + 1) * sizeof(int32_t)) + align_up(moe::split_k_bytes());
   return MOE_OK;
 }
 
@@ -723,10 +734,13 @@ int moe_grouped_gemm(const void* buckets, const int32_t* kept_count, const void*
   auto s = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == MOE_DTYPE_BF16;
   auto* mtile = static_cast<int32_t*>(workspace);
+  const moe::SplitK sk = moe::split_k_carve(static_cast<char*>(workspace) +
+                                            align_up((static_cast<size_t>(E) + 1) * sizeof(int32_t)));
   MOE_HIP_TRY(moe::launch_mtile_map(kept_count, E, moe::grouped_gemm_bm(bf16, C), mtile, s), "tile map");
-  MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept_count, mtile, W_gate, W_up, E, C, d, d_ff, bf16, h, s),
+  MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept_count, mtile, W_gate, W_up, E, C, d, d_ff, bf16, h, s, nullptr,
+                                       &sk),
               "grouped gemm (gate, up)");
-  MOE_HIP_TRY(moe::launch_gemm_down(h, kept_count, mtile, W_down, E, C, d, d_ff, bf16, y, s),
+  MOE_HIP_TRY(moe::launch_gemm_down(h, kept_count, mtile, W_down, E, C, d, d_ff, bf16, y, s, nullptr, &sk),
               "grouped gemm (down)");
   return MOE_OK;
 }

@@ -187,6 +187,9 @@ GEMM_CASES = [
     (3, 600, 256, 384, "bf16"), (2, 1100, 520, 264, "bf16"), (4, 512, 64, 1032, "bf16"),
     (3, 700, 384, 640, "bf16"), (2, 513, 128, 128, "bf16"), (5, 900, 1024, 256, "bf16"),
     (40, 12, 256, 96, "bf16"), (8, 16, 4096, 1024, "bf16"), (3, 3, 40, 24, "bf16"),
+    # 256 x 256 tiles with a last round split over K on a 256-CU part: whole
+    # tiles plus split ones in GEMM 1 (GEMM 2 all split), and the reverse
+    (4, 768, 256, 4352, "bf16"), (8, 768, 4096, 256, "bf16"),
 ]
 
 
