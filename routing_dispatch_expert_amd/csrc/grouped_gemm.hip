@@ -429,7 +429,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int CH = BK / 8;                    // 16-byte chunks per LDS row
   constexpr int BNO = SWIGLU ? BN / 2 : BN;
   constexpr int PER_WAVE = BM / 8 / 4;          // 8-row DMA blocks per wave and operand
-  constexpr int NMFMA = TM * TN, NFRAG = TM + TN;
   __shared__ uint4 As0[BM * CH], As1[BM * CH];
   __shared__ uint4 Bs0[BN * CH], Bs1[BN * CH];
   __shared__ int arrival;
@@ -450,7 +449,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const auto ra_src = buffer_rsrc(A + static_cast<int64_t>(e) * C * K, static_cast<uint32_t>(C * K * 2));
+  // rows past kept (padding) read as zero without a memory access
+  const auto ra_src = buffer_rsrc(A + static_cast<int64_t>(e) * C * K,
+                                  static_cast<uint32_t>(min(static_cast<int64_t>(rows), C) * K * 2));
   // B rows 0..127 of a SwiGLU block are gate rows, 128..255 up rows: waves 0-1
   // load the first half, waves 2-3 the second
   const bf16_t* bbase = (SWIGLU && wave >= 2) ? B1 : B0;
@@ -461,7 +462,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int i = 0; i < PER_WAVE; ++i) {
     const int row = (wave * PER_WAVE + i) * 8 + (lane >> 3);
     const int ch = (lane & 7) ^ ((row >> 1) & 7);  // the chunk stored at position lane % 8
-    a_voff[i] = static_cast<uint32_t>((m0 + row) * K * 2 + ch * 16);  // rows past C read as zero
+    a_voff[i] = static_cast<uint32_t>((m0 + row) * K * 2 + ch * 16);  // rows past kept read as zero
     const int64_t bn = n0 + (SWIGLU ? (row % (BN / 2)) : row);
     b_voff[i] = bn < N ? static_cast<uint32_t>(bn * K * 2 + ch * 16) : 0x80000000u;
   }
@@ -496,74 +497,88 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-  bf16x8 fa[2][TM], fb[2][TN];
+  // A wave whose rows lie partly past the tile's kept rows multiplies only
+  // its first TA of TM 32-row blocks (rows past kept are never stored); it
+  // still issues its share of every stage's loads and takes every barrier.
+  const int live_rows = rows - m0 - wm * (BM / 2);
+  const int ta = __builtin_amdgcn_readfirstlane(live_rows <= 0 ? 0 : min(TM, (live_rows + 31) / 32));
   const int rsw = (lr >> 1) & 7;
-  auto fload = [&](const uint4* as, const uint4* bs, int ks, int slot) {
-    const int pc = (ks * 2 + lk) ^ rsw;
+  auto kloop = [&](auto ta_c) {
+    constexpr int TA = decltype(ta_c)::value;
+    constexpr int NMFMA = TA * TN, NFRAG = TA > 0 ? TA + TN : 1;
+    bf16x8 fa[2][TM], fb[2][TN];
+    auto fload = [&](const uint4* as, const uint4* bs, int ks, int slot) {
+      if constexpr (TA > 0) {
+        const int pc = (ks * 2 + lk) ^ rsw;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) fa[slot][i] = *reinterpret_cast<const bf16x8*>(&as[a_row[i] + pc]);
+        for (int i = 0; i < TA; ++i) fa[slot][i] = *reinterpret_cast<const bf16x8*>(&as[a_row[i] + pc]);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) fb[slot][j] = *reinterpret_cast<const bf16x8*>(&bs[b_row[j] + pc]);
-  };
-  auto mfmas = [&](int slot) {
+        for (int j = 0; j < TN; ++j) fb[slot][j] = *reinterpret_cast<const bf16x8*>(&bs[b_row[j] + pc]);
+      }
+    };
+    auto mfmas = [&](int slot) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TA; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
-  };
-  // Stage k in (as, bs); stage k + 1 goes to (an, bn_) unless this is the last.
-  auto stage = [&](auto has_next, const uint4* as, const uint4* bs, uint4* an, uint4* bn_, int64_t k) {
-    if constexpr (decltype(has_next)::value) dma(an, bn_, k + 1);
-    fload(as, bs, 1, 1);
-    mfmas(0);
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+    };
+    // interleave the next fragments' LDS reads with this step's matrix work
+    auto interleave = [&](bool reads_first) {
+      if constexpr (TA == TM) {
 #pragma unroll
-    for (int g = 0; g < NFRAG; ++g) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA / NFRAG, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-    fload(as, bs, 2, 0);
-    mfmas(1);
-#pragma unroll
-    for (int g = 0; g < NFRAG; ++g) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA / NFRAG, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-    fload(as, bs, 3, 1);
-    mfmas(0);
-#pragma unroll
-    for (int g = 0; g < NFRAG; ++g) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA / NFRAG, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-    if constexpr (decltype(has_next)::value) {
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vm_lgkm0<0>();            // own DMA of stage k + 1 landed, reads of stage k done ...
-      __builtin_amdgcn_s_barrier();  // ... and everyone else's
-      __builtin_amdgcn_sched_barrier(0);
-      fload(an, bn_, 0, 0);
-    }
-    mfmas(1);
-#pragma unroll
-    for (int g = 0; g < NFRAG; ++g) {
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA / NFRAG, 0);
-    }
-  };
-  using T_ = std::true_type;
-  using F_ = std::false_type;
+        for (int g = 0; g < NFRAG; ++g) {
+          if (reads_first) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA / NFRAG, 0);
+          if (!reads_first) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+      }
+    };
+    // Stage k in (as, bs); stage k + 1 goes to (an, bn_) unless this is the last.
+    auto stage = [&](auto has_next, const uint4* as, const uint4* bs, uint4* an, uint4* bn_, int64_t k) {
+      if constexpr (decltype(has_next)::value) dma(an, bn_, k + 1);
+      fload(as, bs, 1, 1);
+      mfmas(0);
+      interleave(false);
+      fload(as, bs, 2, 0);
+      mfmas(1);
+      interleave(false);
+      fload(as, bs, 3, 1);
+      mfmas(0);
+      interleave(false);
+      if constexpr (decltype(has_next)::value) {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm_lgkm0<0>();            // own DMA of stage k + 1 landed, reads of stage k done ...
+        __builtin_amdgcn_s_barrier();  // ... and everyone else's
+        __builtin_amdgcn_sched_barrier(0);
+        fload(an, bn_, 0, 0);
+      }
+      mfmas(1);
+      interleave(true);
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
 
-  dma(As0, Bs0, kb);
-  wait_vm_lgkm0<0>();
-  __builtin_amdgcn_s_barrier();
-  fload(As0, Bs0, 0, 0);
-  int64_t k = kb;
-  for (; k + 2 < ke; k += 2) {
+    dma(As0, Bs0, kb);
+    wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    fload(As0, Bs0, 0, 0);
+    int64_t k = kb;
+    for (; k + 2 < ke; k += 2) {
+      stage(T_{}, As0, Bs0, As1, Bs1, k);
+      stage(T_{}, As1, Bs1, As0, Bs0, k + 1);
+    }
     stage(T_{}, As0, Bs0, As1, Bs1, k);
-    stage(T_{}, As1, Bs1, As0, Bs0, k + 1);
-  }
-  stage(T_{}, As0, Bs0, As1, Bs1, k);
-  stage(F_{}, As1, Bs1, As0, Bs0, k + 1);
+    stage(F_{}, As1, Bs1, As0, Bs0, k + 1);
+  };
+  if (ta > 2)
+    kloop(std::integral_constant<int, TM>{});
+  else if (ta == 2)
+    kloop(std::integral_constant<int, 2>{});
+  else if (ta == 1)
+    kloop(std::integral_constant<int, 1>{});
+  else
+    kloop(std::integral_constant<int, 0>{});
 
   if (split > 1) {
     // Chunk of a split tile: publish the fp32 partial (thread t writes its
@@ -654,7 +669,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const auto ra_src = buffer_rsrc(A + static_cast<int64_t>(e) * C * K, static_cast<uint32_t>(C * K * 2));
+  // rows past kept (padding) read as zero without a memory access
+  const auto ra_src = buffer_rsrc(A + static_cast<int64_t>(e) * C * K,
+                                  static_cast<uint32_t>(min(static_cast<int64_t>(rows), C) * K * 2));
   // B rows 0..127 of a SwiGLU block are gate rows, 128..255 up rows: waves 0-1
   // load the first half, waves 2-3 the second
   const bf16_t* bbase = (SWIGLU && wave >= 2) ? B1 : B0;
@@ -665,7 +682,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int i = 0; i < A_PW; ++i) {
     const int row = (wave * A_PW + i) * 16 + (lane >> 2);
     const int ch = (lane & 3) ^ ((row >> 2) & 3);  // the chunk stored at position lane % 4
-    a_voff[i] = static_cast<uint32_t>((m0 + row) * K * 2 + ch * 16);  // rows past C read as zero
+    a_voff[i] = static_cast<uint32_t>((m0 + row) * K * 2 + ch * 16);  // rows past kept read as zero
   }
 #pragma unroll
   for (int i = 0; i < B_PW; ++i) {
