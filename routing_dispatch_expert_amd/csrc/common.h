@@ -83,6 +83,8 @@ hipError_t launch_scatter_rows(const void* x, const int32_t* idx, const int32_t*
 // Row-tile height the grouped GEMM uses for these sizes (the mtile map must
 // be built for the same value).
 int grouped_gemm_bm(bool bf16, int64_t C);
+// The same for GEMM 1 (gate/up), whose long K favours taller tiles sooner.
+int grouped_gemm_bm_gate_up(bool bf16, int64_t C);
 // Scratch that lets the 256 x 256 GEMM split the tiles of its last, partly
 // filled round over K: fp32 partial tiles of up to kSplitUnits work-groups and
 // one arrival counter per split tile (cleared by the launcher).

@@ -955,6 +955,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 #define MOE_BIG_TILE_MIN_C 512
 #endif
 constexpr int kBigTileMinC = MOE_BIG_TILE_MIN_C;
+#ifndef MOE_BIG_TILE_MIN_C_GATE_UP
+#define MOE_BIG_TILE_MIN_C_GATE_UP 256
+#endif
+constexpr int kBigTileMinCGateUp = MOE_BIG_TILE_MIN_C_GATE_UP;
 
 // Row tiles of the skinny kernel when every expert holds this few rows.
 constexpr int kSkinnyMaxC = kSkinnyRows;
@@ -973,6 +977,15 @@ int grouped_gemm_bm(bool bf16, int64_t C) {
   if (!bf16) return 64;
   if (C <= kSkinnyMaxC) return kSkinnyRows;
   return C >= kBigTileMinC ? 256 : 128;
+}
+
+// GEMM 1 reads each weight tile once per row tile: from 256 rows of capacity
+// on, one 256-row tile per expert (its padding rows cost no matrix work and no
+// loads) beats two 128-row tiles that each stream the weights.
+int grouped_gemm_bm_gate_up(bool bf16, int64_t C) {
+  if (!bf16) return 64;
+  if (C <= kSkinnyMaxC) return kSkinnyRows;
+  return C >= kBigTileMinCGateUp ? 256 : 128;
 }
 
 namespace {
@@ -1043,9 +1056,9 @@ hipError_t launch_gemm_gate_up(const void* buckets, const int32_t* kept, const i
                                const SplitK* sk) {
   if (E * C == 0) return hipSuccess;
   if (bf16) {
-    if (grouped_gemm_bm(true, C) == kSkinnyRows && d % 32 == 0)
+    if (grouped_gemm_bm_gate_up(true, C) == kSkinnyRows && d % 32 == 0)
       return launch_skinny<true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s);
-    if (grouped_gemm_bm(true, C) == 256)
+    if (grouped_gemm_bm_gate_up(true, C) == 256)
       return launch_bf16<256, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s, sk);
     if (d % 64 == 0)
       return launch_bf16<128, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s);

@@ -135,7 +135,7 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 
 struct LayerPlan {
   float* logits;
-  int32_t *idx, *slot, *tile_cnt, *tile_off, *routed, *kept, *send, *mtile, *src;
+  int32_t *idx, *slot, *tile_cnt, *tile_off, *routed, *kept, *send, *mtile, *mtile_gu, *src;
   float* w;
   int64_t* totals;
   void *buckets, *h, *y;
@@ -160,6 +160,7 @@ LayerPlan plan_layer(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E, in
   p.send = c.take<int32_t>(P);
   p.totals = c.take<int64_t>(MOE_NUM_TOTALS);
   p.mtile = c.take<int32_t>(static_cast<size_t>(E) + 1);
+  p.mtile_gu = c.take<int32_t>(static_cast<size_t>(E) + 1);
   p.src = c.take<int32_t>(static_cast<size_t>(E) * C);
   p.buckets = c.take<char>(static_cast<size_t>(E) * C * d * eb);
   p.h = c.take<char>(static_cast<size_t>(E) * C * d_ff * eb);
@@ -226,7 +227,7 @@ int check_replicas(int32_t E, int32_t R, int64_t C) {
 struct ReplPlan {
   float *logits, *w;
   int32_t *idx, *qrank, *inst, *slot, *tile_cnt, *tile_off, *routed, *routed2, *kept1, *kept, *send, *send1,
-      *mtile, *inst_off, *wmap, *place;
+      *mtile, *mtile_gu, *inst_off, *wmap, *place;
   int64_t *totals, *totals1;
   void *buckets, *h, *y;
   moe::SplitK split;
@@ -257,6 +258,7 @@ ReplPlan plan_replicated(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E
   p.totals = c.take<int64_t>(MOE_NUM_TOTALS);
   p.totals1 = c.take<int64_t>(MOE_NUM_TOTALS);
   p.mtile = c.take<int32_t>(static_cast<size_t>(R) + 1);
+  p.mtile_gu = c.take<int32_t>(static_cast<size_t>(R) + 1);
   p.inst_off = c.take<int32_t>(static_cast<size_t>(E) + 1);
   p.wmap = c.take<int32_t>(R);
   p.place = c.take<int32_t>(R);
@@ -380,8 +382,10 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
   MOE_HIP_TRY(moe::launch_scatter_rows(x, idx, slot, T, k, C, d * eb, buckets, s), "scatter");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, false, s), "event");
-  MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, p.mtile, W_gate, W_up, E, C, d, d_ff, bf16, p.h, s, nullptr,
-                                       &p.split),
+  const int bm_gu = moe::grouped_gemm_bm_gate_up(bf16, C);
+  if (bm_gu != bm) MOE_HIP_TRY(moe::launch_mtile_map(kept, E, bm_gu, p.mtile_gu, s), "tile map (gate, up)");
+  MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, bm_gu != bm ? p.mtile_gu : p.mtile, W_gate, W_up, E, C, d, d_ff,
+                                       bf16, p.h, s, nullptr, &p.split),
               "grouped gemm (gate, up)");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, false, s), "event");
@@ -600,8 +604,10 @@ int moe_layer_forward_replicated(const void* x, const void* W_router, const floa
   MOE_HIP_TRY(moe::launch_scatter_rows(x, inst, slot, T, k, C, d * eb, buckets, s), "scatter");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, false, s), "event");
-  MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, p.mtile, W_gate, W_up, R, C, d, d_ff, bf16, p.h, s, p.wmap,
-                                       &p.split),
+  const int bm_gu = moe::grouped_gemm_bm_gate_up(bf16, C);
+  if (bm_gu != bm) MOE_HIP_TRY(moe::launch_mtile_map(kept, R, bm_gu, p.mtile_gu, s), "tile map (gate, up)");
+  MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, bm_gu != bm ? p.mtile_gu : p.mtile, W_gate, W_up, R, C, d, d_ff,
+                                       bf16, p.h, s, p.wmap, &p.split),
               "grouped gemm (gate, up)");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, false, s), "event");
@@ -710,7 +716,7 @@ int moe_permute(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, in
 
 int moe_grouped_gemm_workspace_size(int32_t E, int64_t C, size_t* bytes) {
   if (!bytes || E < 1 || C < 1) return fail(MOE_ERR_INVALID_ARG, "need bytes, E >= 1, C >= 1");
-  *bytes = align_up((static_cast<size_t>(E) + 1) * sizeof(int32_t)) + align_up(moe::split_k_bytes());
+  *bytes = 2 * align_up((static_cast<size_t>(E) + 1) * sizeof(int32_t)) + align_up(moe::split_k_bytes());
   return MOE_OK;
 }
 
@@ -733,12 +739,14 @@ int moe_grouped_gemm(const void* buckets, const int32_t* kept_count, const void*
     return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
   auto s = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == MOE_DTYPE_BF16;
+  const size_t map_bytes = align_up((static_cast<size_t>(E) + 1) * sizeof(int32_t));
   auto* mtile = static_cast<int32_t*>(workspace);
-  const moe::SplitK sk = moe::split_k_carve(static_cast<char*>(workspace) +
-                                            align_up((static_cast<size_t>(E) + 1) * sizeof(int32_t)));
+  auto* mtile_gu = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + map_bytes);
+  const moe::SplitK sk = moe::split_k_carve(static_cast<char*>(workspace) + 2 * map_bytes);
   MOE_HIP_TRY(moe::launch_mtile_map(kept_count, E, moe::grouped_gemm_bm(bf16, C), mtile, s), "tile map");
-  MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept_count, mtile, W_gate, W_up, E, C, d, d_ff, bf16, h, s, nullptr,
-                                       &sk),
+  MOE_HIP_TRY(moe::launch_mtile_map(kept_count, E, moe::grouped_gemm_bm_gate_up(bf16, C), mtile_gu, s), "tile map");
+  MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept_count, mtile_gu, W_gate, W_up, E, C, d, d_ff, bf16, h, s,
+                                       nullptr, &sk),
               "grouped gemm (gate, up)");
   MOE_HIP_TRY(moe::launch_gemm_down(h, kept_count, mtile, W_down, E, C, d, d_ff, bf16, y, s, nullptr, &sk),
               "grouped gemm (down)");
