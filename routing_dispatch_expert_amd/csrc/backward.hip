@@ -87,6 +87,49 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ sr
   }
 }
 
+// The same for 2-byte elements in 16-byte words: a 64 x 64 tile comes in as
+// row chunks of 8 elements and leaves as chunks of 8 consecutive source rows
+// of one column. In LDS, chunk ch of row r sits at position ch ^ (r / 8 % 8),
+// so the 16 lanes that read one column for 8 row groups hit distinct banks.
+// Needs Cc, src_ld, dst_ld, col_off, Rp and both batch strides multiples of 8
+// and 16-byte aligned bases.
+__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                          int64_t R, int64_t Cc, int64_t src_ld, int64_t dst_ld,
+                                                          int64_t col_off, int64_t Rp,
+                                                          const int32_t* __restrict__ valid, int64_t src_bstride,
+                                                          int64_t dst_bstride) {
+  __shared__ uint4 tile[64 * 8];
+  const int64_t b = blockIdx.z;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64, c0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int64_t nv = valid ? min(static_cast<int64_t>(valid[b]), R) : R;
+  const int t = threadIdx.x;
+  const uint16_t* s = src + b * src_bstride;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = t / 8 + 32 * i, ch = t % 8;
+    const int64_t gr = r0 + r, gc = c0 + ch * 8;
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (gr < nv && gc < Cc) v = *reinterpret_cast<const uint4*>(s + gr * src_ld + gc);
+    tile[r * 8 + (ch ^ ((r >> 3) & 7))] = v;
+  }
+  __syncthreads();
+  const auto* t16 = reinterpret_cast<const uint16_t*>(tile);
+  uint16_t* d = dst + b * dst_bstride;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = t / 8 + 32 * i, r8 = t % 8;
+    const int64_t gc = c0 + c, gr = r0 + r8 * 8;
+    if (gc >= Cc || gr >= Rp) continue;
+    const int pos = ((c >> 3) ^ r8) * 8 + (c & 7);  // element c of rows r8 * 8 .. r8 * 8 + 7
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = static_cast<uint32_t>(t16[(r8 * 8 + 2 * q) * 64 + pos]) |
+             (static_cast<uint32_t>(t16[(r8 * 8 + 2 * q + 1) * 64 + pos]) << 16);
+    *reinterpret_cast<uint4*>(d + gc * dst_ld + col_off + gr) = uint4{w[0], w[1], w[2], w[3]};
+  }
+}
+
 // ---------------------------------------------------------------------------
 // SwiGLU on the kept rows of [E][C][F]: forward h = silu(g) u; backward
 // dgu[.][0:F] = dh u silu'(g), dgu[.][F:2F] = dh silu(g). One block per row.
@@ -295,7 +338,13 @@ hipError_t launch_transpose(const void* src, void* dst, int64_t batch, int64_t R
   if (batch == 0 || Cc == 0 || Rp == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(ceil_div(Cc, 64)), static_cast<unsigned>(ceil_div(Rp, 64)),
                   static_cast<unsigned>(batch));
-  if (bf16)
+  const bool words = Cc % 8 == 0 && src_ld % 8 == 0 && dst_ld % 8 == 0 && col_off % 8 == 0 && Rp % 8 == 0 &&
+                     src_bstride % 8 == 0 && dst_bstride % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(dst) % 16 == 0;
+  if (bf16 && words)
+    transpose16_kernel<<<grid, dim3(256), 0, s>>>(static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), R,
+                                                  Cc, src_ld, dst_ld, col_off, Rp, valid, src_bstride, dst_bstride);
+  else if (bf16)
     transpose_kernel<uint16_t><<<grid, dim3(256), 0, s>>>(static_cast<const uint16_t*>(src),
                                                           static_cast<uint16_t*>(dst), R, Cc, src_ld, dst_ld,
                                                           col_off, Rp, valid, src_bstride, dst_bstride);
