@@ -301,6 +301,66 @@ __global__ __launch_bounds__(256) void router_wgrad_part_kernel(const void* __re
   if (blockIdx.x == 0 && tid < EB && e0 + tid < E) dbpart[static_cast<int64_t>(blockIdx.z) * E + e0 + tid] = dbs[tid];
 }
 
+// The same with every expert in one block, for kWgradWideMinE <= E <=
+// kWgradWideMaxE (with fewer experts the 16-expert blocks above waste little
+// of their scan over the copies and keep more blocks in flight): a block
+// takes 64 columns of one token chunk and holds acc[E][64] in LDS; wave w
+// owns the experts e with e % 4 == w, so each accumulator has one writer,
+// which adds in token order. A token's k copies are read once by lanes 0..k-1
+// and broadcast; its 64 x values are read once per wave.
+constexpr int kWgradWideMinE = 64, kWgradWideMaxE = 512;
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void router_wgrad_wide_kernel(const void* __restrict__ x,
+                                                                const int32_t* __restrict__ idx,
+                                                                const float* __restrict__ dl, int64_t T, int64_t tchunk,
+                                                                int k, int E, int64_t d, float* __restrict__ part,
+                                                                float* __restrict__ dbpart) {
+  extern __shared__ float wacc[];  // [E][64], then db [E]
+  float* dbs = wacc + static_cast<int64_t>(E) * 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.z) * tchunk;
+  const int64_t t1 = min(T, t0 + tchunk);
+  const bool want_db = blockIdx.x == 0;
+  for (int q = tid; q < E * 64; q += 256) wacc[q] = 0.f;
+  for (int q = tid; q < E; q += 256) dbs[q] = 0.f;
+  __syncthreads();
+  constexpr int U = 8;  // tokens whose loads are in flight together
+  for (int64_t tb = t0; tb < t1; tb += U) {
+    int e_l[U];
+    float c_l[U], xv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t t = tb + u;
+      const bool ok = t < t1;
+      e_l[u] = ok && lane < k ? idx[t * k + lane] : 0;
+      c_l[u] = ok && lane < k ? dl[t * k + lane] : 0.f;
+      xv[u] = ok && i < d ? (BF16 ? bf16_to_f32(static_cast<const bf16_t*>(x)[t * d + i])
+                                  : static_cast<const float*>(x)[t * d + i])
+                          : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (tb + u >= t1) break;
+      for (int j = 0; j < k; ++j) {
+        const int e = __builtin_amdgcn_readlane(e_l[u], j);
+        if ((e & 3) != wave) continue;  // uniform across the wave
+        const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c_l[u]), j));
+        wacc[e * 64 + lane] = fmaf(c, xv[u], wacc[e * 64 + lane]);
+        if (want_db && lane == 0) dbs[e] += c;
+      }
+    }
+  }
+  __syncthreads();
+  float* pz = part + static_cast<int64_t>(blockIdx.z) * E * d;
+  for (int e = wave; e < E; e += 4)
+    if (i < d) pz[static_cast<int64_t>(e) * d + i] = wacc[e * 64 + lane];
+  if (want_db)
+    for (int e = tid; e < E; e += 256) dbpart[static_cast<int64_t>(blockIdx.z) * E + e] = dbs[e];
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void router_wgrad_sum_kernel(const float* __restrict__ part,
                                                                const float* __restrict__ dbpart, int nchunk, int E,
@@ -420,9 +480,11 @@ hipError_t launch_gather_dx(const void* dout, const void* dX, const void* wr, co
 }
 
 int router_wgrad_chunks(int64_t T, int E, int64_t d) {
-  // about 8192 blocks, chunks of at least 64 tokens
-  const int64_t tiles = ceil_div(d, 256) * ceil_div(E, 16);
-  const int64_t by_work = ceil_div(8192, tiles);
+  // wide kernel: about 2048 blocks of 64 columns; else about 8192 blocks of
+  // 16 experts x 256 columns; chunks of at least 64 tokens
+  const bool wide = E >= kWgradWideMinE && E <= kWgradWideMaxE;
+  const int64_t tiles = wide ? ceil_div(d, 64) : ceil_div(d, 256) * ceil_div(E, 16);
+  const int64_t by_work = ceil_div(wide ? 2048 : 8192, tiles);
   return static_cast<int>(std::max<int64_t>(1, std::min(by_work, ceil_div(T, 64))));
 }
 
@@ -431,12 +493,21 @@ hipError_t launch_router_wgrad(const void* x, const int32_t* idx, const float* d
   const int nz = router_wgrad_chunks(T, E, d);
   const int64_t tchunk = ceil_div(T, nz);
   float* dbpart = part + static_cast<int64_t>(nz) * E * d;
-  const dim3 grid(static_cast<unsigned>(ceil_div(d, 256)), static_cast<unsigned>(ceil_div(E, 16)),
-                  static_cast<unsigned>(nz));
-  if (bf16)
-    router_wgrad_part_kernel<true><<<grid, dim3(256), 0, s>>>(x, idx, dl, T, tchunk, k, E, d, part, dbpart);
-  else
-    router_wgrad_part_kernel<false><<<grid, dim3(256), 0, s>>>(x, idx, dl, T, tchunk, k, E, d, part, dbpart);
+  if (E >= kWgradWideMinE && E <= kWgradWideMaxE) {
+    const dim3 grid(static_cast<unsigned>(ceil_div(d, 64)), 1, static_cast<unsigned>(nz));
+    const size_t lds = static_cast<size_t>(E) * 65 * sizeof(float);
+    if (bf16)
+      router_wgrad_wide_kernel<true><<<grid, dim3(256), lds, s>>>(x, idx, dl, T, tchunk, k, E, d, part, dbpart);
+    else
+      router_wgrad_wide_kernel<false><<<grid, dim3(256), lds, s>>>(x, idx, dl, T, tchunk, k, E, d, part, dbpart);
+  } else {
+    const dim3 grid(static_cast<unsigned>(ceil_div(d, 256)), static_cast<unsigned>(ceil_div(E, 16)),
+                    static_cast<unsigned>(nz));
+    if (bf16)
+      router_wgrad_part_kernel<true><<<grid, dim3(256), 0, s>>>(x, idx, dl, T, tchunk, k, E, d, part, dbpart);
+    else
+      router_wgrad_part_kernel<false><<<grid, dim3(256), 0, s>>>(x, idx, dl, T, tchunk, k, E, d, part, dbpart);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const unsigned g2 = static_cast<unsigned>(std::min<int64_t>(ceil_div(static_cast<int64_t>(E) * d, 256), 4096));

@@ -102,10 +102,12 @@ hipError_t launch_gemm_gate_up(const void* buckets, const int32_t* kept, const i
                                const void* wg, const void* wu, int E, int64_t C, int64_t d,
                                int64_t d_ff, bool bf16, void* h, hipStream_t s, const int32_t* wmap = nullptr,
                                const SplitK* sk = nullptr);
-// GEMM 2: y = h Wd^T on rows < kept (wmap and sk as above).
+// GEMM 2: y = h Wd^T on rows < kept (wmap and sk as above). bm, if not 0,
+// overrides the bf16 row-tile height (128 or 256; mtile_off built for it).
 hipError_t launch_gemm_down(const void* h, const int32_t* kept, const int32_t* mtile_off,
                             const void* wd, int E, int64_t C, int64_t d, int64_t d_ff, bool bf16,
-                            void* y, hipStream_t s, const int32_t* wmap = nullptr, const SplitK* sk = nullptr);
+                            void* y, hipStream_t s, const int32_t* wmap = nullptr, const SplitK* sk = nullptr,
+                            int bm = 0);
 
 // ---- backward (backward.hip) ----
 // dst[b][c][col_off + r] = src[b][r][c] for r < valid[b] (or R), 0 for r < Rp.

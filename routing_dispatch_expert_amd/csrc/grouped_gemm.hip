@@ -1073,12 +1073,13 @@ hipError_t launch_gemm_gate_up(const void* buckets, const int32_t* kept, const i
 
 hipError_t launch_gemm_down(const void* h, const int32_t* kept, const int32_t* mtile_off,
                             const void* wd, int E, int64_t C, int64_t d, int64_t d_ff, bool bf16,
-                            void* y, hipStream_t s, const int32_t* wmap, const SplitK* sk) {
+                            void* y, hipStream_t s, const int32_t* wmap, const SplitK* sk, int bm) {
   if (E * C == 0) return hipSuccess;
   if (bf16) {
-    if (grouped_gemm_bm(true, C) == kSkinnyRows && d_ff % 32 == 0)
+    const int tile = bm ? bm : grouped_gemm_bm(true, C);
+    if (tile == kSkinnyRows && d_ff % 32 == 0)
       return launch_skinny<false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, wmap, s);
-    if (grouped_gemm_bm(true, C) == 256)
+    if (tile == 256)
       return launch_bf16<256, 256, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, wmap, s, sk);
     if (d_ff % 64 == 0)
       return launch_bf16<128, 256, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, wmap, s);

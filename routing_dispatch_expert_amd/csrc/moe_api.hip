@@ -454,11 +454,21 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
               "scan");
   MOE_HIP_TRY(moe::launch_slots(p.idx, p.tile_off, T, k, E, C, p.slot, nullptr, p.totals, s), "slots");
   MOE_HIP_TRY(moe::launch_scatter_rows(x, p.idx, p.slot, T, k, C, d * eb, p.buckets, s), "scatter");
-  // g = X Wg^T and u = X Wu^T (the plain row-tile GEMM: N = d_ff, K = d)
+  // g = X Wg^T and u = X Wu^T (the plain row-tile GEMM: N = d_ff, K = d). GEMMs
+  // that contract over d take the row-tile height of GEMM 1 (bm_d, map mtile_d_rows).
   const moe::SplitK* sk = &p.split;
-  MOE_HIP_TRY(moe::launch_gemm_down(p.buckets, p.kept, p.mtile, W_gate, E, C, F, d, bf16, b.g, s, nullptr, sk),
+  const int bm_d = moe::grouped_gemm_bm_gate_up(bf16, C);
+  int32_t* mtile_d_rows = p.mtile;
+  if (bm_d != bm) {
+    MOE_HIP_TRY(moe::launch_mtile_map(p.kept, E, bm_d, p.mtile_gu, s), "tile map");
+    mtile_d_rows = p.mtile_gu;
+  }
+  const int bmo_d = bf16 ? bm_d : 0;
+  MOE_HIP_TRY(moe::launch_gemm_down(p.buckets, p.kept, mtile_d_rows, W_gate, E, C, F, d, bf16, b.g, s, nullptr, sk,
+                                    bmo_d),
               "gemm g");
-  MOE_HIP_TRY(moe::launch_gemm_down(p.buckets, p.kept, p.mtile, W_up, E, C, F, d, bf16, b.u, s, nullptr, sk),
+  MOE_HIP_TRY(moe::launch_gemm_down(p.buckets, p.kept, mtile_d_rows, W_up, E, C, F, d, bf16, b.u, s, nullptr, sk,
+                                    bmo_d),
               "gemm u");
   MOE_HIP_TRY(moe::launch_swiglu_fwd(b.g, b.u, p.h, p.kept, E, C, F, bf16, s), "swiglu");
   MOE_HIP_TRY(moe::launch_gemm_down(p.h, p.kept, p.mtile, W_down, E, C, d, F, bf16, p.y, s, nullptr, sk), "gemm y");
@@ -469,7 +479,8 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   // 3. dh = dy Wd (B = Wd^T, [E][d_ff][d]); dg, du
   MOE_HIP_TRY(moe::launch_transpose(W_down, b.WdT, E, d, F, F, d, 0, d, nullptr, d * F, F * d, bf16, s),
               "transpose W_down");
-  MOE_HIP_TRY(moe::launch_gemm_down(b.dy, p.kept, p.mtile, b.WdT, E, C, F, d, bf16, b.dh, s, nullptr, sk),
+  MOE_HIP_TRY(moe::launch_gemm_down(b.dy, p.kept, mtile_d_rows, b.WdT, E, C, F, d, bf16, b.dh, s, nullptr, sk,
+                                    bmo_d),
               "gemm dh");
   MOE_HIP_TRY(moe::launch_swiglu_bwd(b.dh, b.g, b.u, b.dgu, p.kept, E, C, F, bf16, s), "swiglu backward");
   // 4. dX = [dg | du] [Wg ; Wu] (B = [Wg^T | Wu^T], [E][d][2 d_ff])
@@ -501,13 +512,24 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
               "transpose X");
   MOE_HIP_TRY(moe::launch_fill_i32(b.kfull_d, E, static_cast<int32_t>(d), s), "fill");
   MOE_HIP_TRY(moe::launch_fill_i32(b.kfull_f, E, static_cast<int32_t>(F), s), "fill");
-  MOE_HIP_TRY(moe::launch_mtile_map(b.kfull_d, E, moe::grouped_gemm_bm(bf16, d), b.mtile_d, s), "tile map");
-  MOE_HIP_TRY(moe::launch_mtile_map(b.kfull_f, E, moe::grouped_gemm_bm(bf16, F), b.mtile_f, s), "tile map");
-  MOE_HIP_TRY(moe::launch_gemm_down(b.dyT, b.kfull_d, b.mtile_d, b.hT, E, d, F, b.Kp, bf16, dW_down, s, nullptr, sk),
+  // A short contraction (Kp not a multiple of 128) leaves these GEMMs bound by
+  // writing the gradients: 128-row tiles, two work-groups per CU, let one
+  // group's stores overlap the other's matrix work.
+  auto wgrad_bm = [&](int64_t rows) {
+    const int dflt = moe::grouped_gemm_bm(bf16, rows);
+    return bf16 && b.Kp % 128 != 0 && dflt >= 128 ? 128 : dflt;
+  };
+  const int bm_wd = wgrad_bm(d), bm_wf = wgrad_bm(F);
+  MOE_HIP_TRY(moe::launch_mtile_map(b.kfull_d, E, bm_wd, b.mtile_d, s), "tile map");
+  MOE_HIP_TRY(moe::launch_mtile_map(b.kfull_f, E, bm_wf, b.mtile_f, s), "tile map");
+  MOE_HIP_TRY(moe::launch_gemm_down(b.dyT, b.kfull_d, b.mtile_d, b.hT, E, d, F, b.Kp, bf16, dW_down, s, nullptr, sk,
+                                    bf16 ? bm_wd : 0),
               "gemm dW_down");
-  MOE_HIP_TRY(moe::launch_gemm_down(b.dgT, b.kfull_f, b.mtile_f, b.XT, E, F, d, b.Kp, bf16, dW_gate, s, nullptr, sk),
+  MOE_HIP_TRY(moe::launch_gemm_down(b.dgT, b.kfull_f, b.mtile_f, b.XT, E, F, d, b.Kp, bf16, dW_gate, s, nullptr, sk,
+                                    bf16 ? bm_wf : 0),
               "gemm dW_gate");
-  MOE_HIP_TRY(moe::launch_gemm_down(b.duT, b.kfull_f, b.mtile_f, b.XT, E, F, d, b.Kp, bf16, dW_up, s, nullptr, sk),
+  MOE_HIP_TRY(moe::launch_gemm_down(b.duT, b.kfull_f, b.mtile_f, b.XT, E, F, d, b.Kp, bf16, dW_up, s, nullptr, sk,
+                                    bf16 ? bm_wf : 0),
               "gemm dW_up");
   return MOE_OK;
 }
