@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens whose output the oracle computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-stage event loop")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="in the per-stage loop, read this many MiB before each step so that L2 and the "
+                         "Infinity Cache hold nothing of the layer's data (0: no flush)")
     ap.add_argument("--backward", action="store_true", help="time moe_layer_backward instead of the forward")
     ap.add_argument("--replicas", type=int, default=-1, metavar="EXTRA",
                     help="time moe_layer_forward_replicated with EXTRA replicas dealt greedily to the most loaded "
@@ -73,11 +76,17 @@ def stage_work(wl, n_kept: int, touched: int, buckets: int):
         "route": dict(bytes=T * E * 4 + T * k * 8, flops=0, bound="hbm"),
         "slots": dict(bytes=3 * T * k * 4 + 4 * nt * buckets * 4, flops=0, bound="hbm"),
         "scatter": dict(bytes=(T + n_kept) * d * b + T * k * 8, flops=0, bound="hbm"),
-        "gate_up": dict(bytes=touched * 2 * f * d * b + n_kept * (d + f) * b, flops=4 * n_kept * d * f,
-                        bound="mfma"),
-        "down": dict(bytes=touched * f * d * b + n_kept * (f + d) * b, flops=2 * n_kept * d * f, bound="mfma"),
+        "gate_up": gemm_work(touched * 2 * f * d * b + n_kept * (d + f) * b, 4 * n_kept * d * f, wl.dtype),
+        "down": gemm_work(touched * f * d * b + n_kept * (f + d) * b, 2 * n_kept * d * f, wl.dtype),
         "combine": dict(bytes=(n_kept + 2 * T) * d * b + T * k * 12, flops=0, bound="hbm"),
     }
+
+
+def gemm_work(nbytes: int, flops: int, dtype: str):
+    """A GEMM stage is bound by the matrix cores when its arithmetic intensity
+    is above the ridge point (peak flop/s over peak HBM bytes/s), else by HBM."""
+    ridge = PEAK_TFLOPS[dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    return dict(bytes=nbytes, flops=flops, bound="mfma" if flops >= ridge * nbytes else "hbm")
 
 
 def read_traffic(gemm_src_sha: str):
@@ -111,6 +120,7 @@ def cpu_baseline(wl, host_w, sample: int, replicas=None):
         times.append(time.perf_counter() - t0)
     dt = sorted(times)[1]
     return {"value": round(tokens.size / dt, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "host": host_cpu(),
             "sample": f"layer outputs of the first {tokens.size} of {wl.T} tokens (routing and slots of all "
                       f"{wl.T}), fp64 numpy, median of 3 runs: {dt:.1f} s each ({sum(times):.1f} s total)"}
 
@@ -168,6 +178,7 @@ def run_backward(args, wl, moe, torch, np, dev, to_dev, host_w):
             times.append(time.perf_counter() - t1)
         dt = sorted(times)[1]
         cpu = {"value": round(S / dt, 3), "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+               "host": host_cpu(),
                "sample": f"backward of the first {S} of {T} tokens as a layer of their own (capacity for {S} "
                          f"tokens), fp64 numpy, median of 3 runs: {dt:.1f} s each"}
     line = {
@@ -191,6 +202,20 @@ def run_backward(args, wl, moe, torch, np, dev, to_dev, host_w):
 def moe_inputs_sample(wl, S):
     """The first S tokens (and their upstream gradient) as a layer input."""
     return {"x": wl.x[:S], "dout": wl.grad_out(1)[:S]}
+
+
+def host_cpu():
+    """The host's CPU model and logical CPU count, for the oracle's timing."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "logical_cpus": os.cpu_count()}
 
 
 def blas_threads():
@@ -305,13 +330,20 @@ def main():
         torch.cuda.synchronize()
         moe.moe_set_stage_events([e.cuda_event for e in evs])
         acc = np.zeros(len(moe.STAGES))
+        layer_ms = []
+        # a read, not a write: evicting dirty lines would add write-back traffic to the next step
+        flush = torch.ones((args.flush_mib << 20) // 8, dtype=torch.int64, device=dev) if args.flush_mib else None
         try:
-            for _ in range(args.steps):
+            for n in range(args.steps):
+                if flush is not None:
+                    flush.sum()
                 step()
                 torch.cuda.synchronize()
                 acc += [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(len(moe.STAGES))]
+                layer_ms.append(evs[0].elapsed_time(evs[-1]))
         finally:
             moe.moe_set_stage_events(None)
+        del flush
         for i, name in enumerate(moe.STAGES):
             ms = acc[i] / args.steps
             w = work[name]
@@ -340,6 +372,11 @@ def main():
                         "frac": s["hbm_frac"], "traffic": traffic, "kernel": dom,
                         "algo_bytes_per_launch": int(w["bytes"]), "avg_launch_ms": s["ms"]}
 
+    layer_cold = None
+    if stages:
+        layer_cold = round(float(np.median(layer_ms)), 5)
+        print(f"[bench] layer (first to last kernel, after a {args.flush_mib} MiB read): median {layer_cold} ms",
+              file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on {min(args.cpu_sample, T)} tokens", file=sys.stderr, flush=True)
@@ -355,6 +392,11 @@ def main():
                    "max_ranks": wl.max_ranks, "C": C, "N_kept": n_kept, "touched_experts": touched,
                    "dropped": totals[0], **repl_cfg},
         "gpu_ms_per_step": round(gpu_ms, 4),
+        "assignments_per_s": round(T * k * args.steps / wall, 1),
+        "layer_ms_cold_median": layer_cold,
+        "stage_timing": None if not stages else (
+            f"HIP events around each stage, mean of {args.steps} steps, each after a {args.flush_mib} MiB read "
+            "that leaves none of the layer's data in L2 or the Infinity Cache"),
         "grouped_gemm_mfma_frac": None if not stages else round(
             (work["gate_up"]["flops"] + work["down"]["flops"]) /
             ((stages["gate_up"]["ms"] + stages["down"]["ms"]) * 1e9) / PEAK_TFLOPS[wl.dtype], 4),
