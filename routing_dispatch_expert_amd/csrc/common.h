@@ -109,6 +109,14 @@ hipError_t launch_gemm_down(const void* h, const int32_t* kept, const int32_t* m
                             void* y, hipStream_t s, const int32_t* wmap = nullptr, const SplitK* sk = nullptr,
                             int bm = 0);
 
+// out = A [B0; B1] on rows < kept with B K-major: B0 [E][K0][N] holds K rows
+// 0 .. K0 - 1 and B1 [E][K - K0][N] the rest (NULL when K0 == K). bf16,
+// 256-row tiles (mtile_off built for 256); needs K % 128 == 0, K0 % 64 == 0
+// and N % 8 == 0, else hipErrorInvalidValue.
+hipError_t launch_gemm_kmajor_b(const void* a, const int32_t* kept, const int32_t* mtile_off, const void* b0,
+                                const void* b1, int64_t K0, int E, int64_t C, int64_t K, int64_t N, void* out,
+                                hipStream_t s, const SplitK* sk = nullptr);
+
 // ---- backward (backward.hip) ----
 // dst[b][c][col_off + r] = src[b][r][c] for r < valid[b] (or R), 0 for r < Rp.
 hipError_t launch_transpose(const void* src, void* dst, int64_t batch, int64_t R, int64_t Cc, int64_t src_ld,

@@ -410,6 +410,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BM >= 25
 // apart and the only waits on the DMA are the explicit ones below.
 // ---------------------------------------------------------------------------
 #define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+#define MOE_LDS_V4I16(p) ((__attribute__((address_space(3))) v4i16*)(p))
 
 // s_waitcnt encodings (gfx9 family): vmcnt in bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8; a field at its maximum does not wait.
@@ -419,12 +422,21 @@ __device__ inline void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
 }
 
-template <bool SWIGLU>
+// With BT the B operand is stored K-major, [K][N] with N contiguous (B0 holds
+// rows k < K0 and B1, if not NULL, rows K0 .. K - 1; K0 % 64 == 0). A stage of
+// B is then 64 K rows x 256 columns in LDS, 16-byte chunk c of row k at
+// position c ^ (4 (k % 4)), and each wave reads its fragments with
+// ds_read_b64_tr_b16, which hands lane i of a 16-lane group element i % 4 of
+// the piece that lane 4 q + i / 4 points at, as its element q: two such reads
+// give a lane the eight consecutive K values of one column that the matrix
+// core wants.
+template <bool SWIGLU, bool BT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_dma_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     bf16_t* __restrict__ out, const int32_t* __restrict__ kept, const int32_t* __restrict__ mtile_off,
     int E, int64_t C, int64_t K, int64_t N, int nt_count, const int32_t* __restrict__ wmap,
-    float* __restrict__ part, int32_t* __restrict__ tick, int G) {
+    float* __restrict__ part, int32_t* __restrict__ tick, int G, int64_t K0 = 0) {
+  static_assert(!(SWIGLU && BT), "the K-major B operand serves the plain GEMM only");
   constexpr int BM = 256, BN = 256, BK = 64, TM = 4, TN = 4;
   constexpr int CH = BK / 8;                    // 16-byte chunks per LDS row
   constexpr int BNO = SWIGLU ? BN / 2 : BN;
@@ -456,15 +468,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // load the first half, waves 2-3 the second
   const bf16_t* bbase = (SWIGLU && wave >= 2) ? B1 : B0;
   const int we = wmap ? __builtin_amdgcn_readfirstlane(wmap[e]) : e;  // expert whose weights this row tile uses
-  const auto rb_src = buffer_rsrc(bbase + static_cast<int64_t>(we) * N * K, static_cast<uint32_t>(N * K * 2));
+  const int64_t kb0 = BT ? K0 : K;  // K rows held by B0
+  const auto rb_src = buffer_rsrc(bbase + static_cast<int64_t>(we) * N * kb0, static_cast<uint32_t>(N * kb0 * 2));
+  const auto rb_src1 = buffer_rsrc(BT && B1 ? B1 + static_cast<int64_t>(we) * N * (K - K0) : B0,
+                                   BT && B1 ? static_cast<uint32_t>(N * (K - K0) * 2) : 0u);
   uint32_t a_voff[PER_WAVE], b_voff[PER_WAVE];
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
     const int row = (wave * PER_WAVE + i) * 8 + (lane >> 3);
     const int ch = (lane & 7) ^ ((row >> 1) & 7);  // the chunk stored at position lane % 8
     a_voff[i] = static_cast<uint32_t>((m0 + row) * K * 2 + ch * 16);  // rows past kept read as zero
-    const int64_t bn = n0 + (SWIGLU ? (row % (BN / 2)) : row);
-    b_voff[i] = bn < N ? static_cast<uint32_t>(bn * K * 2 + ch * 16) : 0x80000000u;
+    if constexpr (BT) {
+      // one instruction fills K rows 2 u and 2 u + 1 of the stage (u = wave * 8 + i), 32 positions each
+      const int kr = (wave * PER_WAVE + i) * 2 + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (kr & 3));  // the chunk stored at position lane % 32
+      const int64_t bn = n0 + c * 8;
+      b_voff[i] = bn < N ? static_cast<uint32_t>((kr * N + bn) * 2) : 0x80000000u;
+    } else {
+      const int64_t bn = n0 + (SWIGLU ? (row % (BN / 2)) : row);
+      b_voff[i] = bn < N ? static_cast<uint32_t>(bn * K * 2 + ch * 16) : 0x80000000u;
+    }
   }
   auto dma = [&](uint4* as, uint4* bs, int64_t ks) {  // ks: stage number
     const uint32_t soff = static_cast<uint32_t>(ks * BK * 2);
@@ -472,10 +495,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int i = 0; i < PER_WAVE; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_src, MOE_LDS(as + (wave * PER_WAVE + i) * 8 * CH), 16,
                                                a_voff[i], soff, 0, 0);
+    if constexpr (BT) {
+      const bool second = ks * BK >= K0;  // uniform: K0 is a multiple of the stage depth
+      const auto rb = second ? rb_src1 : rb_src;
+      const uint32_t bsoff = static_cast<uint32_t>((second ? ks * BK - K0 : ks * BK) * N * 2);
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_src, MOE_LDS(bs + (wave * PER_WAVE + i) * 8 * CH), 16,
-                                               b_voff[i], soff, 0, 0);
+      for (int i = 0; i < PER_WAVE; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MOE_LDS(bs + (wave * PER_WAVE + i) * 8 * CH), 16, b_voff[i],
+                                                 bsoff, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_src, MOE_LDS(bs + (wave * PER_WAVE + i) * 8 * CH), 16,
+                                                 b_voff[i], soff, 0, 0);
+    }
   };
 
   const int wm = wave >> 1, wn = wave & 1;
@@ -488,6 +521,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int br = SWIGLU ? ((j < TN / 2) ? (wn * (BN / 4) + j * 32) : (BN / 2 + wn * (BN / 4) + (j - TN / 2) * 32))
                           : (wn * (BN / 2) + j * 32);
     b_row[j] = (br + lr) * CH;
+  }
+  // K-major B: byte offset, within a stage, of this lane's first 8-byte piece
+  // of fragment j (sub-step 0, K values 0..3 of its column group)
+  int bt_off[TN];
+  if constexpr (BT) {
+    const int g = lane >> 4, jj = lane & 15;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int nl = wn * (BN / 2) + j * 32 + 16 * (g & 1) + 4 * (jj & 3);
+      const int kr = 8 * (g >> 1) + (jj >> 2);
+      bt_off[j] = kr * (BN * 2) + (((nl >> 3) ^ (4 * (jj >> 2))) * 16) + (nl & 7) * 2;
+    }
   }
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -505,15 +550,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int rsw = (lr >> 1) & 7;
   auto kloop = [&](auto ta_c) {
     constexpr int TA = decltype(ta_c)::value;
-    constexpr int NMFMA = TA * TN, NFRAG = TA > 0 ? TA + TN : 1;
+    constexpr int NMFMA = TA * TN, NFRAG = TA > 0 ? TA + (BT ? 2 : 1) * TN : 1;
     bf16x8 fa[2][TM], fb[2][TN];
     auto fload = [&](const uint4* as, const uint4* bs, int ks, int slot) {
       if constexpr (TA > 0) {
         const int pc = (ks * 2 + lk) ^ rsw;
 #pragma unroll
         for (int i = 0; i < TA; ++i) fa[slot][i] = *reinterpret_cast<const bf16x8*>(&as[a_row[i] + pc]);
+        if constexpr (BT) {
+          const char* base = reinterpret_cast<const char*>(bs) + ks * 16 * (BN * 2);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) fb[slot][j] = *reinterpret_cast<const bf16x8*>(&bs[b_row[j] + pc]);
+          for (int j = 0; j < TN; ++j) {
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS_V4I16(base + bt_off[j]));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS_V4I16(base + bt_off[j] + 4 * BN * 2));
+            const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            fb[slot][j] = __builtin_bit_cast(bf16x8, both);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) fb[slot][j] = *reinterpret_cast<const bf16x8*>(&bs[b_row[j] + pc]);
+        }
       }
     };
     auto mfmas = [&](int slot) {
@@ -1049,6 +1105,27 @@ hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out,
 }
 
 }  // namespace
+
+hipError_t launch_gemm_kmajor_b(const void* a, const int32_t* kept, const int32_t* mtile_off, const void* b0,
+                                const void* b1, int64_t K0, int E, int64_t C, int64_t K, int64_t N, void* out,
+                                hipStream_t s, const SplitK* sk) {
+  if (E * C == 0) return hipSuccess;
+  if (K % 128 || K0 % 64 || K0 <= 0 || K0 > K || (K0 < K && !b1) || N % 8) return hipErrorInvalidValue;
+  const int64_t mt_max = E * ceil_div(C, 256);
+  const int64_t nt = ceil_div(N, 256);
+  int64_t blocks = ceil_div(mt_max * nt, 8) * 8;
+  const int G = sk ? resident_groups() : 0;
+  if (G > 0) {
+    const hipError_t err = launch_fill_i32(sk->tick, G, 0, s);
+    if (err != hipSuccess) return err;
+    blocks += G;
+  }
+  gemm_bf16_dma_kernel<false, true><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
+      static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0), static_cast<const bf16_t*>(b1),
+      static_cast<bf16_t*>(out), kept, mtile_off, E, C, K, N, static_cast<int>(nt), nullptr,
+      G > 0 ? sk->part : nullptr, G > 0 ? sk->tick : nullptr, G, K0);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_gate_up(const void* buckets, const int32_t* kept, const int32_t* mtile_off,
                                const void* wg, const void* wu, int E, int64_t C, int64_t d,

@@ -174,6 +174,13 @@ LayerPlan plan_layer(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E, in
 // recomputed g and u, the gradient rows and the transposed operands of the
 // gradient GEMMs. Kp = C rounded up to 64: the row count the weight gradients
 // contract over (rows past kept are zero in the transposed copies).
+// The gradient GEMMs through the weights (dh = dy Wd, dX = [dg | du] [Wg ; Wu])
+// read the weights K-major where the 256-row LDS-DMA kernel can: then no
+// transposed weight copies are made.
+bool backward_kmajor(bool bf16, int64_t C, int64_t d, int64_t F) {
+  return bf16 && moe::grouped_gemm_bm_gate_up(bf16, C) == 256 && d % 128 == 0 && F % 64 == 0;
+}
+
 struct BackPlan {
   LayerPlan f;
   void *g, *u, *dy, *dh, *dgu, *dX, *WdT, *WguT, *dyT, *hT, *dgT, *duT, *XT;
@@ -198,8 +205,9 @@ BackPlan plan_backward(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E, 
   b.dh = c.take<char>(EC * d_ff * eb);
   b.dgu = c.take<char>(EC * 2 * d_ff * eb);
   b.dX = c.take<char>(EC * d * eb);
-  b.WdT = c.take<char>(static_cast<size_t>(E) * d_ff * d * eb);
-  b.WguT = c.take<char>(static_cast<size_t>(E) * d * 2 * d_ff * eb);
+  const bool kmajor = backward_kmajor(eb == 2, C, d, d_ff);
+  b.WdT = c.take<char>(kmajor ? 0 : static_cast<size_t>(E) * d_ff * d * eb);
+  b.WguT = c.take<char>(kmajor ? 0 : static_cast<size_t>(E) * d * 2 * d_ff * eb);
   b.dyT = c.take<char>(EKp * d * eb);
   b.hT = c.take<char>(EKp * d_ff * eb);
   b.dgT = c.take<char>(EKp * d_ff * eb);
@@ -476,20 +484,29 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   // 2. combine backward: dy = w dout on kept rows, dl = gate gradients
   MOE_HIP_TRY(moe::launch_combine_bwd(dout, p.y, p.idx, p.w, p.slot, T, d, k, C, bf16, b.dy, b.dl, s),
               "combine backward");
-  // 3. dh = dy Wd (B = Wd^T, [E][d_ff][d]); dg, du
-  MOE_HIP_TRY(moe::launch_transpose(W_down, b.WdT, E, d, F, F, d, 0, d, nullptr, d * F, F * d, bf16, s),
-              "transpose W_down");
-  MOE_HIP_TRY(moe::launch_gemm_down(b.dy, p.kept, mtile_d_rows, b.WdT, E, C, F, d, bf16, b.dh, s, nullptr, sk,
-                                    bmo_d),
-              "gemm dh");
-  MOE_HIP_TRY(moe::launch_swiglu_bwd(b.dh, b.g, b.u, b.dgu, p.kept, E, C, F, bf16, s), "swiglu backward");
-  // 4. dX = [dg | du] [Wg ; Wu] (B = [Wg^T | Wu^T], [E][d][2 d_ff])
-  MOE_HIP_TRY(moe::launch_transpose(W_gate, b.WguT, E, F, d, d, 2 * F, 0, F, nullptr, F * d, d * 2 * F, bf16, s),
-              "transpose W_gate");
-  MOE_HIP_TRY(moe::launch_transpose(W_up, b.WguT, E, F, d, d, 2 * F, F, F, nullptr, F * d, d * 2 * F, bf16, s),
-              "transpose W_up");
-  MOE_HIP_TRY(moe::launch_gemm_down(b.dgu, p.kept, p.mtile, b.WguT, E, C, d, 2 * F, bf16, b.dX, s, nullptr, sk),
-              "gemm dX");
+  // 3. dh = dy Wd; dg, du. 4. dX = [dg | du] [Wg ; Wu]. Either straight from the
+  //    weights (K-major B: Wd is [d][d_ff] = [K][N], Wg and Wu are [d_ff][d]),
+  //    or through transposed copies (B = Wd^T [E][d_ff][d], [Wg^T | Wu^T] [E][d][2 d_ff]).
+  if (backward_kmajor(bf16, C, d, F)) {  // then bm_d == 256 and mtile_d_rows is its map
+    MOE_HIP_TRY(moe::launch_gemm_kmajor_b(b.dy, p.kept, mtile_d_rows, W_down, nullptr, d, E, C, d, F, b.dh, s, sk),
+                "gemm dh");
+    MOE_HIP_TRY(moe::launch_swiglu_bwd(b.dh, b.g, b.u, b.dgu, p.kept, E, C, F, bf16, s), "swiglu backward");
+    MOE_HIP_TRY(moe::launch_gemm_kmajor_b(b.dgu, p.kept, mtile_d_rows, W_gate, W_up, F, E, C, 2 * F, d, b.dX, s, sk),
+                "gemm dX");
+  } else {
+    MOE_HIP_TRY(moe::launch_transpose(W_down, b.WdT, E, d, F, F, d, 0, d, nullptr, d * F, F * d, bf16, s),
+                "transpose W_down");
+    MOE_HIP_TRY(moe::launch_gemm_down(b.dy, p.kept, mtile_d_rows, b.WdT, E, C, F, d, bf16, b.dh, s, nullptr, sk,
+                                      bmo_d),
+                "gemm dh");
+    MOE_HIP_TRY(moe::launch_swiglu_bwd(b.dh, b.g, b.u, b.dgu, p.kept, E, C, F, bf16, s), "swiglu backward");
+    MOE_HIP_TRY(moe::launch_transpose(W_gate, b.WguT, E, F, d, d, 2 * F, 0, F, nullptr, F * d, d * 2 * F, bf16, s),
+                "transpose W_gate");
+    MOE_HIP_TRY(moe::launch_transpose(W_up, b.WguT, E, F, d, d, 2 * F, F, F, nullptr, F * d, d * 2 * F, bf16, s),
+                "transpose W_up");
+    MOE_HIP_TRY(moe::launch_gemm_down(b.dgu, p.kept, p.mtile, b.WguT, E, C, d, 2 * F, bf16, b.dX, s, nullptr, sk),
+                "gemm dX");
+  }
   // 5. router gradients, then dx = dout + the expert paths + the router path
   MOE_HIP_TRY(moe::launch_router_wgrad(x, p.idx, b.dl, T, k, E, d, bf16, b.rpart, dW_router, d_bias, s),
               "router wgrad");

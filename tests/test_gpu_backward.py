@@ -30,6 +30,7 @@ BACK_CASES = [
     dict(T=64, d=128, E=8, k=2, d_ff=256, cf=1.25, dtype="f32", x_std=1 / np.sqrt(128), wr_std=1 / np.sqrt(128)),
     dict(T=16, d=256, E=32, k=4, d_ff=128, cf=2.0),                                    # decode-sized buckets
     dict(T=2048, d=256, E=4, k=2, d_ff=512, cf=1.25),                                  # 256-row tiles
+    dict(T=1024, d=384, E=4, k=2, d_ff=192, cf=1.0),   # K-major weights, column tiles past N, stacked K
     dict(T=40, d=64, E=1, k=1, d_ff=64, cf=1.0),                                       # one expert: dense
     # 64 or more experts: the router weight gradient holds every expert in one block
     dict(T=200, d=136, E=64, k=6, d_ff=40, cf=2.0, bias="zipf1.2"),
