@@ -15,6 +15,7 @@
 // to (expert, tile) by binary search over that prefix and exits when the id
 // is past the last live tile.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -1061,15 +1062,17 @@ hipError_t launch_skinny(const void* a, const void* b0, const void* b1, void* ou
 // Work-groups of the 256 x 256 kernel resident at once (one per CU), rounded
 // down to whole rounds over the 8 XCDs; 0 if unknown (no split).
 int resident_groups() {
-  static int cached[64];
+  static std::atomic<int> cached[64];  // per device; 0 = not yet asked
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
+  int g = cached[dev].load(std::memory_order_relaxed);
+  if (g == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cached[dev] = std::max(8, std::min(cus, kSplitUnits) / 8 * 8);
+    g = std::max(8, std::min(cus, kSplitUnits) / 8 * 8);
+    cached[dev].store(g, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return g;
 }
 
 template <int BM, int BN, bool SWIGLU>
