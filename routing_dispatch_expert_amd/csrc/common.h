@@ -42,6 +42,9 @@ __device__ inline void store_stream(uint4* p, uint4 v) {
 // ---- router (router.hip) ----
 // Number of d-slices S the scores are split into (partials part[S][T][E]).
 int router_splits(int64_t T, int64_t d, int E, bool bf16);
+// Router scores as S partial slices part[S][T][E] over d (the route kernel
+// adds them in slice order). With many experts they run on the grouped GEMM
+// kernel.
 hipError_t launch_router_logits(const void* x, const void* wr, int64_t T, int64_t d, int E, bool bf16,
                                 int S, float* part, hipStream_t s);
 // Sums the S partials (slice order) and the bias, writes logits_out if given,
@@ -109,6 +112,12 @@ hipError_t launch_gemm_down(const void* h, const int32_t* kept, const int32_t* m
                             void* y, hipStream_t s, const int32_t* wmap = nullptr, const SplitK* sk = nullptr,
                             int bm = 0);
 
+// out [slices][M][N] fp32: slice c = A [M][K] B [N][K]^T over the c-th of
+// `slices` equal K ranges (whole 128-wide pairs of stages), bf16 operands, one
+// group of 256-row tiles. Needs K % 128 == 0, N % 8 == 0 and
+// 1 <= slices <= K / 128, else hipErrorInvalidValue.
+hipError_t launch_gemm_rows_f32(const void* a, const void* b, int64_t M, int64_t K, int64_t N, int slices,
+                                float* out, hipStream_t s);
 // out = A [B0; B1] on rows < kept with B K-major: B0 [E][K0][N] holds K rows
 // 0 .. K0 - 1 and B1 [E][K - K0][N] the rest (NULL when K0 == K). bf16,
 // 256-row tiles (mtile_off built for 256); needs K % 128 == 0, K0 % 64 == 0

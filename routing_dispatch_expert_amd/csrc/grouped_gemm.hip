@@ -68,13 +68,14 @@ __device__ inline float silu_bf16(float g) {
 // ---------------------------------------------------------------------------
 constexpr int kGroupN = 8;
 
-// Expert, first row and column tile of live tile `lid`.
+// Expert, first row and column tile of live tile `lid`. Without a row-tile
+// map there is one group of ceil(C / BM) row tiles.
 template <int BM>
 __device__ inline void tile_coords(const int32_t* __restrict__ mtile_off, int E, int nt_count, int64_t lid,
-                                   int* e_out, int* m0_out, int* nt_out) {
-  const int e = owner_expert(mtile_off, E, static_cast<int>(lid / nt_count));
-  const int mte = mtile_off[e + 1] - mtile_off[e];
-  const int64_t li = lid - static_cast<int64_t>(mtile_off[e]) * nt_count;
+                                   int* e_out, int* m0_out, int* nt_out, int64_t C = 0) {
+  const int e = mtile_off ? owner_expert(mtile_off, E, static_cast<int>(lid / nt_count)) : 0;
+  const int mte = mtile_off ? mtile_off[e + 1] - mtile_off[e] : static_cast<int>((C + BM - 1) / BM);
+  const int64_t li = lid - (mtile_off ? static_cast<int64_t>(mtile_off[e]) * nt_count : 0);
   const int64_t grp = li / (static_cast<int64_t>(mte) * kGroupN);
   const int r = static_cast<int>(li - grp * mte * kGroupN);
   *e_out = e;
@@ -115,10 +116,24 @@ struct Work {
   int s, c, ti;
 };
 
+// With slices > 1 instead (and G = 0), block b takes K range b % slices of
+// live tile b / slices, and the caller keeps the slices' results apart.
 template <int BM>
 __device__ inline bool work_of_block(const int32_t* __restrict__ mtile_off, int E, int nt_count, int64_t nk,
-                                     int G, Work* w) {
-  const int64_t live = static_cast<int64_t>(mtile_off[E]) * nt_count;
+                                     int G, Work* w, int64_t C = 0, int slices = 1) {
+  const int64_t live = (mtile_off ? static_cast<int64_t>(mtile_off[E]) : (C + BM - 1) / BM) * nt_count;
+  if (slices > 1) {
+    const int64_t lid = blockIdx.x / slices;
+    if (lid >= live) return false;
+    w->s = 1;
+    w->ti = 0;
+    w->c = static_cast<int>(blockIdx.x % slices);
+    const int64_t pairs = nk / 2;
+    w->kb = 2 * (w->c * pairs / slices);
+    w->ke = 2 * ((w->c + 1) * pairs / slices);
+    tile_coords<BM>(mtile_off, E, nt_count, lid, &w->e, &w->m0, &w->nt, C);
+    return true;
+  }
   int64_t rem = G > 0 ? live % G : 0;
   int64_t s = rem > 0 ? G / rem : 1;
   s = s < nk / 2 ? s : nk / 2;
@@ -145,7 +160,7 @@ __device__ inline bool work_of_block(const int32_t* __restrict__ mtile_off, int 
     w->kb = 2 * (w->c * pairs / s);
     w->ke = 2 * ((w->c + 1) * pairs / s);
   }
-  tile_coords<BM>(mtile_off, E, nt_count, lid, &w->e, &w->m0, &w->nt);
+  tile_coords<BM>(mtile_off, E, nt_count, lid, &w->e, &w->m0, &w->nt, C);
   return true;
 }
 
@@ -431,13 +446,17 @@ __device__ inline void wait_vm_lgkm0() {
 // the piece that lane 4 q + i / 4 points at, as its element q: two such reads
 // give a lane the eight consecutive K values of one column that the matrix
 // core wants.
-template <bool SWIGLU, bool BT = false>
+// With F32OUT the output is fp32 (out points at floats) and stored straight
+// from the accumulators; kept and mtile_off may then be NULL: one group of C
+// rows, all kept.
+template <bool SWIGLU, bool BT = false, bool F32OUT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_dma_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     bf16_t* __restrict__ out, const int32_t* __restrict__ kept, const int32_t* __restrict__ mtile_off,
     int E, int64_t C, int64_t K, int64_t N, int nt_count, const int32_t* __restrict__ wmap,
-    float* __restrict__ part, int32_t* __restrict__ tick, int G, int64_t K0 = 0) {
+    float* __restrict__ part, int32_t* __restrict__ tick, int G, int64_t K0 = 0, int slices = 1) {
   static_assert(!(SWIGLU && BT), "the K-major B operand serves the plain GEMM only");
+  static_assert(!(F32OUT && (SWIGLU || BT)), "fp32 output serves the plain GEMM only");
   constexpr int BM = 256, BN = 256, BK = 64, TM = 4, TN = 4;
   constexpr int CH = BK / 8;                    // 16-byte chunks per LDS row
   constexpr int BNO = SWIGLU ? BN / 2 : BN;
@@ -447,7 +466,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __shared__ int arrival;
 
   Work wk;
-  if (!work_of_block<BM>(mtile_off, E, nt_count, K / BK, G, &wk)) return;
+  if (!work_of_block<BM>(mtile_off, E, nt_count, K / BK, G, &wk, C, slices)) return;
   const int e = __builtin_amdgcn_readfirstlane(wk.e);
   const int m0 = __builtin_amdgcn_readfirstlane(wk.m0);
   const int nt = __builtin_amdgcn_readfirstlane(wk.nt);
@@ -456,7 +475,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int ti = __builtin_amdgcn_readfirstlane(wk.ti);
   const int64_t kb = __builtin_amdgcn_readfirstlane(static_cast<int>(wk.kb));  // stages [kb, ke): even, >= 2
   const int64_t ke = __builtin_amdgcn_readfirstlane(static_cast<int>(wk.ke));
-  const int rows = __builtin_amdgcn_readfirstlane(kept[e]);
+  const int rows = __builtin_amdgcn_readfirstlane(kept ? kept[e] : static_cast<int>(C));
   const int64_t n0 = static_cast<int64_t>(nt) * BNO;
 
   const int tid = threadIdx.x;
@@ -640,8 +659,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (split > 1) {
     // Chunk of a split tile: publish the fp32 partial (thread t writes its
     // 64 float4s at [g][t], coalesced), count the arrival; the last of the s
-    // blocks to arrive adds the s partials in chunk order (its own from
-    // registers), so the sum does not depend on which block came last.
+    // blocks to arrive adds the s partials in chunk order, so the sum does
+    // not depend on which block came last.
     constexpr int NG = TM * TN * 4;  // float4 groups per thread
     float4* mine = reinterpret_cast<float4*>(part) + static_cast<int64_t>(ti * split + chunk) * NG * 256;
 #pragma unroll
@@ -658,7 +677,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __syncthreads();
     if (arrival != split - 1) return;
     __threadfence();
-    const float4* first = reinterpret_cast<const float4*>(part) + static_cast<int64_t>(ti * split) * NG * 256;
+    // every partial, this block's own included, is read back in chunk order;
+    // a group's s loads are in flight together (a load-add chain would wait
+    // out the memory latency once per load)
+    const float4* first =
+        reinterpret_cast<const float4*>(part) + static_cast<int64_t>(ti * split) * NG * 256 + tid;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -666,15 +689,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int g = (i * TN + j) * 4 + q;
-          const float4 own{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          float4 t = chunk == 0 ? own : first[g * 256 + tid];
-          for (int c = 1; c < split; ++c) {
-            const float4 v = c == chunk ? own : first[(static_cast<int64_t>(c) * NG + g) * 256 + tid];
-            t.x += v.x;
-            t.y += v.y;
-            t.z += v.z;
-            t.w += v.w;
-          }
+          float4 v[kMaxSplit];
+#pragma unroll
+          for (int c = 0; c < kMaxSplit; ++c)
+            if (c < split) v[c] = first[(static_cast<int64_t>(c) * NG + g) * 256];
+          float4 t = v[0];
+#pragma unroll
+          for (int c = 1; c < kMaxSplit; ++c)
+            if (c < split) {
+              t.x += v[c].x;
+              t.y += v[c].y;
+              t.z += v[c].z;
+              t.w += v[c].w;
+            }
           acc[i][j][4 * q] = t.x;
           acc[i][j][4 * q + 1] = t.y;
           acc[i][j][4 * q + 2] = t.z;
@@ -682,6 +709,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
   }
 
+  if constexpr (F32OUT) {  // lanes 0-31 and 32-63 each store 32 consecutive floats of one row
+    // with K slices, slice c of [slices][C][N]
+    float* o = reinterpret_cast<float*>(out) + static_cast<int64_t>(e) * C * N +
+               (slices > 1 ? static_cast<int64_t>(chunk) * C * N : 0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int r = m0 + wm * (BM / 2) + i * 32 + 8 * (q >> 2) + 4 * lk + (q & 3);
+          const int64_t c = n0 + wn * (BN / 2) + j * 32 + lr;
+          if (r < rows && c < N) o[r * N + c] = acc[i][j][q];
+        }
+    return;
+  }
   // the stage buffers are free: one per wave for the epilogue
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
@@ -1108,6 +1151,18 @@ hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out,
 }
 
 }  // namespace
+
+hipError_t launch_gemm_rows_f32(const void* a, const void* b, int64_t M, int64_t K, int64_t N, int slices,
+                                float* out, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (K % 128 || N % 8 || slices < 1 || slices > K / 128) return hipErrorInvalidValue;
+  const int64_t nt = ceil_div(N, 256);
+  const int64_t blocks = ceil_div(M, 256) * nt * slices;
+  gemm_bf16_dma_kernel<false, false, true><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
+      static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b), nullptr, reinterpret_cast<bf16_t*>(out),
+      nullptr, nullptr, 1, M, K, N, static_cast<int>(nt), nullptr, nullptr, nullptr, 0, 0, slices);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_kmajor_b(const void* a, const int32_t* kept, const int32_t* mtile_off, const void* b0,
                                 const void* b1, int64_t K0, int E, int64_t C, int64_t K, int64_t N, void* out,

@@ -349,8 +349,21 @@ hipError_t route_dispatch(const RouteArgs& a, hipStream_t s) {
 
 }  // namespace
 
+// With many experts the score GEMM is a real one (T x E x d): it runs on the
+// grouped GEMM's 256 x 256 LDS-DMA tiles with fp32 output, so each tile of
+// router weights is read once per 256 tokens, not once per 16. (With fewer
+// than 128 experts most of a 256-wide tile would be padding.)
+static bool router_on_gemm(int64_t T, int64_t d, int E, bool bf16) {
+  return bf16 && E >= 128 && E % 8 == 0 && T >= 256 && d % 128 == 0;
+}
+
 int router_splits(int64_t T, int64_t d, int E, bool bf16) {
   if (!bf16 || T == 0) return 1;
+  if (router_on_gemm(T, d, E, bf16)) {  // d-slices so that about 256 tiles run at once
+    const int64_t tiles = ceil_div(T, 256) * ceil_div(E, 256);
+    return static_cast<int>(std::max<int64_t>(
+        1, std::min({ceil_div(256, tiles), d / 128, int64_t{kMaxRouterSplits}})));
+  }
   const int nt = E <= 16 ? 1 : (E <= 32 ? 2 : 4);
   const int64_t items = ceil_div(T, 16) * ceil_div(E, 16 * nt);
   const int64_t by_work = ceil_div(2048, items);        // aim at >= 2048 waves
@@ -361,6 +374,7 @@ int router_splits(int64_t T, int64_t d, int E, bool bf16) {
 hipError_t launch_router_logits(const void* x, const void* wr, int64_t T, int64_t d, int E, bool bf16,
                                 int S, float* part, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  if (router_on_gemm(T, d, E, bf16)) return launch_gemm_rows_f32(x, wr, T, d, E, S, part, s);
   if (!bf16) {
     const int64_t n = T * E;
     router_logits_f32<<<dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, s>>>(

@@ -81,6 +81,8 @@ ROUTER_CASES = [
     (300, 256, 8, 2, "bf16", None), (200, 1024, 64, 6, "bf16", "zipf1.2"), (130, 520, 256, 8, "bf16", None),
     (100, 128, 8, 2, "f32", None), (65, 72, 20, 3, "bf16", None), (1, 4096, 8, 2, "bf16", None),
     (64, 7168, 256, 8, "bf16", None), (40, 2048, 64, 20, "bf16", "zipf1.2"), (4100, 4096, 8, 2, "bf16", None),
+    # 128 or more experts and 256 or more tokens: scores on the grouped GEMM kernel (fp32 slices over d)
+    (1000, 1024, 128, 6, "bf16", "zipf1.2"), (600, 7168, 256, 8, "bf16", None), (2304, 2048, 128, 4, "bf16", None),
 ]
 # rank-limited: (T, d, E, k, dtype, bias, P, M, logits wanted); without logits_out
 # and with several d-slices or a bias the summed scores go back over slice 0
