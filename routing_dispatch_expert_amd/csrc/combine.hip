@@ -17,18 +17,18 @@ namespace moe {
 namespace {
 
 // One wave per token (WPT waves for short batches); lanes walk the row in
-// 16-byte words (8 bf16 or 4 fp32 values), U words per lane at a time. The
+// 16-byte words (8 bf16 or 4 fp32 values), U words per lane at a time, read
+// with the non-temporal hint (every word is read once). The
 // token's copies are taken JB at a time: their slots, experts and gates are
 // wave-uniform scalar loads, the words of every kept copy of the batch are in
 // flight before any arithmetic, and the sum runs in ascending j.
-template <bool BF16, int WPT>
+template <bool BF16, int WPT, int U>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ x,
                                                       const uint4* __restrict__ y,
                                                       const int32_t* __restrict__ idx,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ slot, int64_t T, int k,
                                                       int64_t C, int64_t V, uint4* __restrict__ out) {
-  constexpr int U = 4;
   constexpr int JB = 2;                  // copies whose words are in flight together
   constexpr int NE = BF16 ? 8 : 4;
   constexpr int LANES = 64 * WPT;        // threads sharing one token
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t v = v0 + LANES * u;
-      if (v < V) xv[u] = xr[v];
+      if (v < V) xv[u] = load_stream(&xr[v]);
     }
     if (!any) {  // every copy dropped: the row passes through bit for bit
 #pragma unroll
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int64_t v = v0 + LANES * u;
-          if (v < V) yv[jb][u] = src[jb][v];
+          if (v < V) yv[jb][u] = load_stream(&src[jb][v]);
         }
       }
 #pragma unroll
@@ -138,8 +138,10 @@ hipError_t launch_combine(const void* x, const void* y, const int32_t* idx, cons
   const auto* xv = static_cast<const uint4*>(x);
   const auto* yv = static_cast<const uint4*>(y);
   auto* ov = static_cast<uint4*>(out);
-#define MOE_COMBINE(B, W) combine_kernel<B, W><<<grid, dim3(256), 0, s>>>(xv, yv, idx, w, slot, T, k, C, V, ov)
-  if (bf16) {
+#define MOE_COMBINE(B, W) combine_kernel<B, W, 4><<<grid, dim3(256), 0, s>>>(xv, yv, idx, w, slot, T, k, C, V, ov)
+  if (bf16 && wpt == 1 && V >= 768) {  // long rows (d >= 6144): 8 words per lane in flight
+    combine_kernel<true, 1, 8><<<grid, dim3(256), 0, s>>>(xv, yv, idx, w, slot, T, k, C, V, ov);
+  } else if (bf16) {
     if (wpt == 1) MOE_COMBINE(true, 1); else if (wpt == 2) MOE_COMBINE(true, 2); else MOE_COMBINE(true, 4);
   } else {
     if (wpt == 1) MOE_COMBINE(false, 1); else if (wpt == 2) MOE_COMBINE(false, 2); else MOE_COMBINE(false, 4);

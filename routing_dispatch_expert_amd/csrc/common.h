@@ -39,6 +39,14 @@ __device__ inline void store_stream(uint4* p, uint4 v) {
   __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
 }
 
+// A 16-byte load with the non-temporal hint (data read once, not to be kept
+// in the caches).
+__device__ inline uint4 load_stream(const uint4* p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return uint4{w[0], w[1], w[2], w[3]};
+}
+
 // ---- router (router.hip) ----
 // Number of d-slices S the scores are split into (partials part[S][T][E]).
 int router_splits(int64_t T, int64_t d, int E, bool bf16);

@@ -244,7 +244,8 @@ def test_grouped_gemm_rows_below_kept(E, C, d, d_ff, dtype):
 # ------------------------------------------------------------------ combine ---
 
 COMBINE_CASES = [(500, 64, 8, 2, 1.0, "bf16"), (300, 40, 16, 4, 0.5, "bf16"), (64, 128, 8, 2, 1.25, "f32"),
-                 (200, 8, 4, 4, 0.25, "bf16"), (1, 16, 2, 1, 1.0, "f32")]
+                 (200, 8, 4, 4, 0.25, "bf16"), (1, 16, 2, 1, 1.0, "f32"),
+                 (1100, 6208, 8, 3, 0.5, "bf16")]   # long rows: 8 words per lane, a ragged last pass
 
 
 @pytest.mark.parametrize("T,d,E,k,cf,dtype", COMBINE_CASES)
