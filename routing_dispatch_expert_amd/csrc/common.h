@@ -126,6 +126,13 @@ hipError_t launch_gemm_down(const void* h, const int32_t* kept, const int32_t* m
 // 1 <= slices <= K / 128, else hipErrorInvalidValue.
 hipError_t launch_gemm_rows_f32(const void* a, const void* b, int64_t M, int64_t K, int64_t N, int slices,
                                 float* out, hipStream_t s);
+// Weight gradients: out[e] [M][N] = A_e^T B_e over the kk[e] rows of group e,
+// both operands K-major: A_e element (k, m) at a + e a_es + k lda + aoff + m,
+// B_e element (k, n) at b + e b_es + k N + n. bf16; every group writes its
+// whole M x N block (zero when kk[e] is 0). Needs M, N, lda and aoff
+// multiples of 8 and aoff + M <= lda, else hipErrorInvalidValue.
+hipError_t launch_gemm_tn(const void* a, int64_t lda, int64_t a_es, int64_t aoff, const void* b, int64_t b_es,
+                          const int32_t* kk, int E, int64_t M, int64_t N, void* out, hipStream_t s);
 // out = A [B0; B1] on rows < kept with B K-major: B0 [E][K0][N] holds K rows
 // 0 .. K0 - 1 and B1 [E][K - K0][N] the rest (NULL when K0 == K). bf16,
 // 256-row tiles (mtile_off built for 256); needs K % 128 == 0, K0 % 64 == 0

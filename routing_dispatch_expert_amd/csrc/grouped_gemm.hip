@@ -69,13 +69,16 @@ __device__ inline float silu_bf16(float g) {
 constexpr int kGroupN = 8;
 
 // Expert, first row and column tile of live tile `lid`. Without a row-tile
-// map there is one group of ceil(C / BM) row tiles.
+// map every one of the E groups has ceil(C / BM) row tiles.
 template <int BM>
 __device__ inline void tile_coords(const int32_t* __restrict__ mtile_off, int E, int nt_count, int64_t lid,
                                    int* e_out, int* m0_out, int* nt_out, int64_t C = 0) {
-  const int e = mtile_off ? owner_expert(mtile_off, E, static_cast<int>(lid / nt_count)) : 0;
-  const int mte = mtile_off ? mtile_off[e + 1] - mtile_off[e] : static_cast<int>((C + BM - 1) / BM);
-  const int64_t li = lid - (mtile_off ? static_cast<int64_t>(mtile_off[e]) * nt_count : 0);
+  const int mt_all = static_cast<int>((C + BM - 1) / BM);
+  const int e = mtile_off ? owner_expert(mtile_off, E, static_cast<int>(lid / nt_count))
+                          : static_cast<int>(lid / (static_cast<int64_t>(mt_all) * nt_count));
+  const int mte = mtile_off ? mtile_off[e + 1] - mtile_off[e] : mt_all;
+  const int64_t li = lid - (mtile_off ? static_cast<int64_t>(mtile_off[e]) * nt_count
+                                      : static_cast<int64_t>(e) * mt_all * nt_count);
   const int64_t grp = li / (static_cast<int64_t>(mte) * kGroupN);
   const int r = static_cast<int>(li - grp * mte * kGroupN);
   *e_out = e;
@@ -121,7 +124,7 @@ struct Work {
 template <int BM>
 __device__ inline bool work_of_block(const int32_t* __restrict__ mtile_off, int E, int nt_count, int64_t nk,
                                      int G, Work* w, int64_t C = 0, int slices = 1) {
-  const int64_t live = (mtile_off ? static_cast<int64_t>(mtile_off[E]) : (C + BM - 1) / BM) * nt_count;
+  const int64_t live = (mtile_off ? static_cast<int64_t>(mtile_off[E]) : E * ((C + BM - 1) / BM)) * nt_count;
   if (slices > 1) {
     const int64_t lid = blockIdx.x / slices;
     if (lid >= live) return false;
@@ -427,7 +430,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BM >= 25
 // ---------------------------------------------------------------------------
 #define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef short v8i16 __attribute__((ext_vector_type(8)));
 #define MOE_LDS_V4I16(p) ((__attribute__((address_space(3))) v4i16*)(p))
 
 // s_waitcnt encodings (gfx9 family): vmcnt in bits 3:0 and 15:14, expcnt 6:4,
@@ -449,14 +451,23 @@ __device__ inline void wait_vm_lgkm0() {
 // With F32OUT the output is fp32 (out points at floats) and stored straight
 // from the accumulators; kept and mtile_off may then be NULL: one group of C
 // rows, all kept.
-template <bool SWIGLU, bool BT = false, bool F32OUT = false>
+// With AT as well (weight gradients, out[e] = A_e^T B_e over each expert's
+// kept rows), A is K-major too: element (k, m) of group e at
+// A + e a_es + k lda + aoff + m, B's at B0 + e b_es + k N + n; group e
+// contracts over kk[e] rows (rounded up to whole 128-row stage pairs, the
+// rows past kk[e] reading as zero), every group has C (= M) output rows, and
+// kept and mtile_off are NULL.
+template <bool SWIGLU, bool BT = false, bool F32OUT = false, bool AT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_dma_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     bf16_t* __restrict__ out, const int32_t* __restrict__ kept, const int32_t* __restrict__ mtile_off,
     int E, int64_t C, int64_t K, int64_t N, int nt_count, const int32_t* __restrict__ wmap,
-    float* __restrict__ part, int32_t* __restrict__ tick, int G, int64_t K0 = 0, int slices = 1) {
+    float* __restrict__ part, int32_t* __restrict__ tick, int G, int64_t K0 = 0, int slices = 1,
+    const int32_t* __restrict__ kk = nullptr, int64_t lda = 0, int64_t a_es = 0, int64_t aoff = 0,
+    int64_t b_es = 0) {
   static_assert(!(SWIGLU && BT), "the K-major B operand serves the plain GEMM only");
   static_assert(!(F32OUT && (SWIGLU || BT)), "fp32 output serves the plain GEMM only");
+  static_assert(!AT || (BT && !F32OUT), "a K-major A comes with a K-major B");
   constexpr int BM = 256, BN = 256, BK = 64, TM = 4, TN = 4;
   constexpr int CH = BK / 8;                    // 16-byte chunks per LDS row
   constexpr int BNO = SWIGLU ? BN / 2 : BN;
@@ -473,23 +484,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int split = __builtin_amdgcn_readfirstlane(wk.s);
   const int chunk = __builtin_amdgcn_readfirstlane(wk.c);
   const int ti = __builtin_amdgcn_readfirstlane(wk.ti);
-  const int64_t kb = __builtin_amdgcn_readfirstlane(static_cast<int>(wk.kb));  // stages [kb, ke): even, >= 2
-  const int64_t ke = __builtin_amdgcn_readfirstlane(static_cast<int>(wk.ke));
+  const int kr_e = AT ? __builtin_amdgcn_readfirstlane(kk[e]) : 0;  // rows this group contracts over
+  const int64_t kb = __builtin_amdgcn_readfirstlane(static_cast<int>(wk.kb));  // stages [kb, ke): even
+  const int64_t ke = AT ? 2 * ((kr_e + 2 * BK - 1) / (2 * BK))
+                        : __builtin_amdgcn_readfirstlane(static_cast<int>(wk.ke));
   const int rows = __builtin_amdgcn_readfirstlane(kept ? kept[e] : static_cast<int>(C));
   const int64_t n0 = static_cast<int64_t>(nt) * BNO;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // rows past kept (padding) read as zero without a memory access
-  const auto ra_src = buffer_rsrc(A + static_cast<int64_t>(e) * C * K,
-                                  static_cast<uint32_t>(min(static_cast<int64_t>(rows), C) * K * 2));
+  // rows past kept (padding) read as zero without a memory access; with AT,
+  // K rows past kk[e]
+  const auto ra_src = AT ? buffer_rsrc(A + static_cast<int64_t>(e) * a_es, static_cast<uint32_t>(kr_e * lda * 2))
+                         : buffer_rsrc(A + static_cast<int64_t>(e) * C * K,
+                                       static_cast<uint32_t>(min(static_cast<int64_t>(rows), C) * K * 2));
   // B rows 0..127 of a SwiGLU block are gate rows, 128..255 up rows: waves 0-1
   // load the first half, waves 2-3 the second
   const bf16_t* bbase = (SWIGLU && wave >= 2) ? B1 : B0;
   const int we = wmap ? __builtin_amdgcn_readfirstlane(wmap[e]) : e;  // expert whose weights this row tile uses
   const int64_t kb0 = BT ? K0 : K;  // K rows held by B0
-  const auto rb_src = buffer_rsrc(bbase + static_cast<int64_t>(we) * N * kb0, static_cast<uint32_t>(N * kb0 * 2));
+  const auto rb_src = AT ? buffer_rsrc(B0 + static_cast<int64_t>(e) * b_es, static_cast<uint32_t>(kr_e * N * 2))
+                         : buffer_rsrc(bbase + static_cast<int64_t>(we) * N * kb0,
+                                       static_cast<uint32_t>(N * kb0 * 2));
   const auto rb_src1 = buffer_rsrc(BT && B1 ? B1 + static_cast<int64_t>(we) * N * (K - K0) : B0,
                                    BT && B1 ? static_cast<uint32_t>(N * (K - K0) * 2) : 0u);
   uint32_t a_voff[PER_WAVE], b_voff[PER_WAVE];
@@ -497,7 +514,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int i = 0; i < PER_WAVE; ++i) {
     const int row = (wave * PER_WAVE + i) * 8 + (lane >> 3);
     const int ch = (lane & 7) ^ ((row >> 1) & 7);  // the chunk stored at position lane % 8
-    a_voff[i] = static_cast<uint32_t>((m0 + row) * K * 2 + ch * 16);  // rows past kept read as zero
+    if constexpr (AT) {  // as B below: K rows 2 u and 2 u + 1 of the stage, 32 positions each
+      const int kr = (wave * PER_WAVE + i) * 2 + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (kr & 3));
+      const int64_t am = m0 + c * 8;
+      a_voff[i] = am < C ? static_cast<uint32_t>((kr * lda + aoff + am) * 2) : 0x80000000u;
+    } else {
+      a_voff[i] = static_cast<uint32_t>((m0 + row) * K * 2 + ch * 16);  // rows past kept read as zero
+    }
     if constexpr (BT) {
       // one instruction fills K rows 2 u and 2 u + 1 of the stage (u = wave * 8 + i), 32 positions each
       const int kr = (wave * PER_WAVE + i) * 2 + (lane >> 5);
@@ -511,12 +535,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   auto dma = [&](uint4* as, uint4* bs, int64_t ks) {  // ks: stage number
     const uint32_t soff = static_cast<uint32_t>(ks * BK * 2);
+    const uint32_t asoff = AT ? static_cast<uint32_t>(ks * BK * lda * 2) : soff;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_src, MOE_LDS(as + (wave * PER_WAVE + i) * 8 * CH), 16,
-                                               a_voff[i], soff, 0, 0);
+                                               a_voff[i], asoff, 0, 0);
     if constexpr (BT) {
-      const bool second = ks * BK >= K0;  // uniform: K0 is a multiple of the stage depth
+      const bool second = !AT && ks * BK >= K0;  // uniform: K0 is a multiple of the stage depth
       const auto rb = second ? rb_src1 : rb_src;
       const uint32_t bsoff = static_cast<uint32_t>((second ? ks * BK - K0 : ks * BK) * N * 2);
 #pragma unroll
@@ -544,14 +569,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   // K-major B: byte offset, within a stage, of this lane's first 8-byte piece
   // of fragment j (sub-step 0, K values 0..3 of its column group)
-  int bt_off[TN];
+  int bt_off[TN], at_off[TM];
   if constexpr (BT) {
     const int g = lane >> 4, jj = lane & 15;
+    const int kr = 8 * (g >> 1) + (jj >> 2);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int nl = wn * (BN / 2) + j * 32 + 16 * (g & 1) + 4 * (jj & 3);
-      const int kr = 8 * (g >> 1) + (jj >> 2);
       bt_off[j] = kr * (BN * 2) + (((nl >> 3) ^ (4 * (jj >> 2))) * 16) + (nl & 7) * 2;
+    }
+    if constexpr (AT) {  // the same for the 32-row blocks of A (BM == BN)
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int ml = wm * (BM / 2) + i * 32 + 16 * (g & 1) + 4 * (jj & 3);
+        at_off[i] = kr * (BM * 2) + (((ml >> 3) ^ (4 * (jj >> 2))) * 16) + (ml & 7) * 2;
+      }
     }
   }
   f32x16 acc[TM][TN];
@@ -570,22 +602,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int rsw = (lr >> 1) & 7;
   auto kloop = [&](auto ta_c) {
     constexpr int TA = decltype(ta_c)::value;
-    constexpr int NMFMA = TA * TN, NFRAG = TA > 0 ? TA + (BT ? 2 : 1) * TN : 1;
+    constexpr int NMFMA = TA * TN, NFRAG = TA > 0 ? (AT ? 2 : 1) * TA + (BT ? 2 : 1) * TN : 1;
     bf16x8 fa[2][TM], fb[2][TN];
+    auto tr_pair = [](const char* p) {  // 8 consecutive K values of one column of a K-major stage
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS_V4I16(p));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS_V4I16(p + 4 * BN * 2));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
     auto fload = [&](const uint4* as, const uint4* bs, int ks, int slot) {
       if constexpr (TA > 0) {
         const int pc = (ks * 2 + lk) ^ rsw;
+        if constexpr (AT) {
+          const char* abase = reinterpret_cast<const char*>(as) + ks * 16 * (BM * 2);
 #pragma unroll
-        for (int i = 0; i < TA; ++i) fa[slot][i] = *reinterpret_cast<const bf16x8*>(&as[a_row[i] + pc]);
+          for (int i = 0; i < TA; ++i) fa[slot][i] = tr_pair(abase + at_off[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < TA; ++i) fa[slot][i] = *reinterpret_cast<const bf16x8*>(&as[a_row[i] + pc]);
+        }
         if constexpr (BT) {
           const char* base = reinterpret_cast<const char*>(bs) + ks * 16 * (BN * 2);
 #pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS_V4I16(base + bt_off[j]));
-            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MOE_LDS_V4I16(base + bt_off[j] + 4 * BN * 2));
-            const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            fb[slot][j] = __builtin_bit_cast(bf16x8, both);
-          }
+          for (int j = 0; j < TN; ++j) fb[slot][j] = tr_pair(base + bt_off[j]);
         } else {
 #pragma unroll
           for (int j = 0; j < TN; ++j) fb[slot][j] = *reinterpret_cast<const bf16x8*>(&bs[b_row[j] + pc]);
@@ -647,14 +685,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     stage(T_{}, As0, Bs0, As1, Bs1, k);
     stage(F_{}, As1, Bs1, As0, Bs0, k + 1);
   };
-  if (ta > 2)
-    kloop(std::integral_constant<int, TM>{});
-  else if (ta == 2)
-    kloop(std::integral_constant<int, 2>{});
-  else if (ta == 1)
-    kloop(std::integral_constant<int, 1>{});
-  else
-    kloop(std::integral_constant<int, 0>{});
+  if (ke > kb) {  // with AT a group that kept no row contracts over nothing: its block is zero
+    if (ta > 2)
+      kloop(std::integral_constant<int, TM>{});
+    else if (ta == 2)
+      kloop(std::integral_constant<int, 2>{});
+    else if (ta == 1)
+      kloop(std::integral_constant<int, 1>{});
+    else
+      kloop(std::integral_constant<int, 0>{});
+  }
 
   if (split > 1) {
     // Chunk of a split tile: publish the fp32 partial (thread t writes its
@@ -1161,6 +1201,18 @@ hipError_t launch_gemm_rows_f32(const void* a, const void* b, int64_t M, int64_t
   gemm_bf16_dma_kernel<false, false, true><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
       static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b), nullptr, reinterpret_cast<bf16_t*>(out),
       nullptr, nullptr, 1, M, K, N, static_cast<int>(nt), nullptr, nullptr, nullptr, 0, 0, slices);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_tn(const void* a, int64_t lda, int64_t a_es, int64_t aoff, const void* b, int64_t b_es,
+                          const int32_t* kk, int E, int64_t M, int64_t N, void* out, hipStream_t s) {
+  if (E == 0 || M == 0 || N == 0) return hipSuccess;
+  if (M % 8 || N % 8 || lda % 8 || aoff % 8 || aoff + M > lda) return hipErrorInvalidValue;
+  const int64_t nt = ceil_div(N, 256);
+  const int64_t blocks = ceil_div(E * ceil_div(M, 256) * nt, 8) * 8;
+  gemm_bf16_dma_kernel<false, true, false, true><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
+      static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b), nullptr, static_cast<bf16_t*>(out), nullptr,
+      nullptr, E, M, 0, N, static_cast<int>(nt), nullptr, nullptr, nullptr, 0, 0, 1, kk, lda, a_es, aoff, b_es);
   return hipGetLastError();
 }
 

@@ -208,11 +208,14 @@ BackPlan plan_backward(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E, 
   const bool kmajor = backward_kmajor(eb == 2, C, d, d_ff);
   b.WdT = c.take<char>(kmajor ? 0 : static_cast<size_t>(E) * d_ff * d * eb);
   b.WguT = c.take<char>(kmajor ? 0 : static_cast<size_t>(E) * d * 2 * d_ff * eb);
-  b.dyT = c.take<char>(EKp * d * eb);
-  b.hT = c.take<char>(EKp * d_ff * eb);
-  b.dgT = c.take<char>(EKp * d_ff * eb);
-  b.duT = c.take<char>(EKp * d_ff * eb);
-  b.XT = c.take<char>(EKp * d * eb);
+  // bf16 weight gradients read the buckets K-major in place; fp32 contracts
+  // over transposed copies
+  const size_t tk = eb == 2 ? 0 : EKp;
+  b.dyT = c.take<char>(tk * d * eb);
+  b.hT = c.take<char>(tk * d_ff * eb);
+  b.dgT = c.take<char>(tk * d_ff * eb);
+  b.duT = c.take<char>(tk * d_ff * eb);
+  b.XT = c.take<char>(tk * d * eb);
   b.kfull_d = c.take<int32_t>(E);
   b.kfull_f = c.take<int32_t>(E);
   b.mtile_d = c.take<int32_t>(static_cast<size_t>(E) + 1);
@@ -513,8 +516,18 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   MOE_HIP_TRY(moe::launch_gather_dx(dout, b.dX, W_router, p.idx, b.dl, p.slot, T, d, k, C, bf16, dx, s),
               "gather dx");
   // 6. weight gradients over each expert's kept rows: dWd = dy^T h, dWg = dg^T X,
-  //    dWu = du^T X, as row-tile GEMMs of the transposed operands (M = d or
-  //    d_ff rows for every expert, K = Kp)
+  //    dWu = du^T X. bf16: both operands read K-major straight from the
+  //    buckets, each expert contracting over its own kept rows.
+  if (bf16) {
+    MOE_HIP_TRY(moe::launch_gemm_tn(b.dy, d, C * d, 0, p.h, C * F, p.kept, E, d, F, dW_down, s), "gemm dW_down");
+    MOE_HIP_TRY(moe::launch_gemm_tn(b.dgu, 2 * F, C * 2 * F, 0, p.buckets, C * d, p.kept, E, F, d, dW_gate, s),
+                "gemm dW_gate");
+    MOE_HIP_TRY(moe::launch_gemm_tn(b.dgu, 2 * F, C * 2 * F, F, p.buckets, C * d, p.kept, E, F, d, dW_up, s),
+                "gemm dW_up");
+    return MOE_OK;
+  }
+  //    fp32: row-tile GEMMs of the transposed operands (M = d or d_ff rows
+  //    for every expert, K = Kp)
   MOE_HIP_TRY(moe::launch_transpose(b.dy, b.dyT, E, C, d, d, b.Kp, 0, b.Kp, p.kept, C * d, d * b.Kp, bf16, s),
               "transpose dy");
   MOE_HIP_TRY(moe::launch_transpose(p.h, b.hT, E, C, F, F, b.Kp, 0, b.Kp, p.kept, C * F, F * b.Kp, bf16, s),
@@ -529,24 +542,13 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
               "transpose X");
   MOE_HIP_TRY(moe::launch_fill_i32(b.kfull_d, E, static_cast<int32_t>(d), s), "fill");
   MOE_HIP_TRY(moe::launch_fill_i32(b.kfull_f, E, static_cast<int32_t>(F), s), "fill");
-  // A short contraction (Kp not a multiple of 128) leaves these GEMMs bound by
-  // writing the gradients: 128-row tiles, two work-groups per CU, let one
-  // group's stores overlap the other's matrix work.
-  auto wgrad_bm = [&](int64_t rows) {
-    const int dflt = moe::grouped_gemm_bm(bf16, rows);
-    return bf16 && b.Kp % 128 != 0 && dflt >= 128 ? 128 : dflt;
-  };
-  const int bm_wd = wgrad_bm(d), bm_wf = wgrad_bm(F);
-  MOE_HIP_TRY(moe::launch_mtile_map(b.kfull_d, E, bm_wd, b.mtile_d, s), "tile map");
-  MOE_HIP_TRY(moe::launch_mtile_map(b.kfull_f, E, bm_wf, b.mtile_f, s), "tile map");
-  MOE_HIP_TRY(moe::launch_gemm_down(b.dyT, b.kfull_d, b.mtile_d, b.hT, E, d, F, b.Kp, bf16, dW_down, s, nullptr, sk,
-                                    bf16 ? bm_wd : 0),
+  MOE_HIP_TRY(moe::launch_mtile_map(b.kfull_d, E, moe::grouped_gemm_bm(bf16, d), b.mtile_d, s), "tile map");
+  MOE_HIP_TRY(moe::launch_mtile_map(b.kfull_f, E, moe::grouped_gemm_bm(bf16, F), b.mtile_f, s), "tile map");
+  MOE_HIP_TRY(moe::launch_gemm_down(b.dyT, b.kfull_d, b.mtile_d, b.hT, E, d, F, b.Kp, bf16, dW_down, s),
               "gemm dW_down");
-  MOE_HIP_TRY(moe::launch_gemm_down(b.dgT, b.kfull_f, b.mtile_f, b.XT, E, F, d, b.Kp, bf16, dW_gate, s, nullptr, sk,
-                                    bf16 ? bm_wf : 0),
+  MOE_HIP_TRY(moe::launch_gemm_down(b.dgT, b.kfull_f, b.mtile_f, b.XT, E, F, d, b.Kp, bf16, dW_gate, s),
               "gemm dW_gate");
-  MOE_HIP_TRY(moe::launch_gemm_down(b.duT, b.kfull_f, b.mtile_f, b.XT, E, F, d, b.Kp, bf16, dW_up, s, nullptr, sk,
-                                    bf16 ? bm_wf : 0),
+  MOE_HIP_TRY(moe::launch_gemm_down(b.duT, b.kfull_f, b.mtile_f, b.XT, E, F, d, b.Kp, bf16, dW_up, s),
               "gemm dW_up");
   return MOE_OK;
 }
