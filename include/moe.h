@@ -26,6 +26,8 @@
  *  - Every array argument is a caller-owned, contiguous, row-major DEVICE
  *    pointer unless stated otherwise. The library never allocates, frees or
  *    keeps memory between calls; scratch memory is the caller's `workspace`.
+ *    Two calls whose work may overlap on the device (different streams) need
+ *    separate workspaces; calls ordered on one stream may share one.
  *  - bf16 arrays hold IEEE bfloat16 bit patterns; fp32 arrays hold IEEE binary32.
  *    `dtype` selects the element type of x, weights, buckets, h, y and out;
  *    logits, gates are always fp32, indices and counts int32, totals int64.
