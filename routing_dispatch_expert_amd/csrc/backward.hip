@@ -177,11 +177,11 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint4* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Combine backward, one wave per token: for each kept copy j (ascending) the
-// dot product dw_j = <dout, y_j> (per-lane partials in word order, then a
-// fixed butterfly) and dy_j = w_j dout; then the gate gradients dl.
+// Combine backward, one wave per token: dy_j = w_j dout for each kept copy j
+// and, with DOT, the dot product dw_j = <dout, y_j> (per-lane partials in
+// word order, then a fixed butterfly) and the gate gradients dl.
 // ---------------------------------------------------------------------------
-template <bool BF16>
+template <bool BF16, bool DOT = true>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restrict__ dout, const uint4* __restrict__ y,
                                                           const int32_t* __restrict__ idx, const float* __restrict__ w,
                                                           const int32_t* __restrict__ slot, int64_t T, int k, int64_t C,
@@ -201,21 +201,60 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
       for (int64_t v = lane; v < V; v += 64) {
         float df[W::N], yf[W::N], of[W::N];
         W::load(drow[v], df);
-        W::load(y[base + v], yf);
+        if (DOT) W::load(y[base + v], yf);
 #pragma unroll
         for (int q = 0; q < W::N; ++q) {
-          part = fmaf(df[q], yf[q], part);
+          if (DOT) part = fmaf(df[q], yf[q], part);
           of[q] = wj * df[q];
         }
         dy[base + v] = W::store(of);
       }
     }
+    if (!DOT) continue;
     const float dw = wave_sum(part);  // the same value in every lane; 0 for a dropped copy
     if (lane == j) my_dw = dw;
   }
+  if (!DOT) return;
   const float wl = lane < k ? w[t * k + lane] : 0.f;
   const float ssum = wave_sum(wl * my_dw);  // sum_i w_i dw_i
   if (lane < k) dl[t * k + lane] = wl * (my_dw - ssum);
+}
+
+// ---------------------------------------------------------------------------
+// Gate gradients from the expert side, one wave per token. For a kept copy j,
+// dh_j = w_j dout Wd is its hidden gradient and h_j its activation, so
+// q_j = <dh_j, h_j> = w_j <dout, h_j Wd^T> = w_j dw_j; a dropped copy has
+// q_j = 0. Then dl_j = w_j (dw_j - sum_i w_i dw_i) = q_j - w_j sum_i q_i.
+// Each q_j is per-lane partials in word order, then a fixed butterfly.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(256) void gate_grad_kernel(const uint4* __restrict__ dh, const uint4* __restrict__ h,
+                                                        const int32_t* __restrict__ idx, const float* __restrict__ w,
+                                                        const int32_t* __restrict__ slot, int64_t T, int k, int64_t C,
+                                                        int64_t VF, float* __restrict__ dl) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole waves only; no barriers below
+  using W = Word<BF16>;
+  float my_q = 0.f;  // lane j keeps q of copy j
+  for (int j = 0; j < k; ++j) {
+    const int sl = __builtin_amdgcn_readfirstlane(slot[t * k + j]);
+    if (sl < 0) continue;  // q_j = 0
+    const int64_t base = (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(idx[t * k + j])) * C + sl) * VF;
+    float part = 0.f;
+    for (int64_t v = lane; v < VF; v += 64) {
+      float gf[W::N], hf[W::N];
+      W::load(dh[base + v], gf);
+      W::load(h[base + v], hf);
+#pragma unroll
+      for (int q = 0; q < W::N; ++q) part = fmaf(gf[q], hf[q], part);
+    }
+    const float q = wave_sum(part);
+    if (lane == j) my_q = q;
+  }
+  const float wl = lane < k ? w[t * k + lane] : 0.f;
+  const float qsum = wave_sum(my_q);  // lanes >= k hold 0
+  if (lane < k) dl[t * k + lane] = my_q - wl * qsum;
 }
 
 // ---------------------------------------------------------------------------
@@ -455,10 +494,29 @@ hipError_t launch_combine_bwd(const void* dout, const void* y, const int32_t* id
   const auto* a = static_cast<const uint4*>(dout);
   const auto* b = static_cast<const uint4*>(y);
   auto* o = static_cast<uint4*>(dy);
-  if (bf16)
+  if (bf16 && y)
     combine_bwd_kernel<true><<<grid, dim3(256), 0, s>>>(a, b, idx, w, slot, T, k, C, V, o, dl);
-  else
+  else if (bf16)
+    combine_bwd_kernel<true, false><<<grid, dim3(256), 0, s>>>(a, b, idx, w, slot, T, k, C, V, o, dl);
+  else if (y)
     combine_bwd_kernel<false><<<grid, dim3(256), 0, s>>>(a, b, idx, w, slot, T, k, C, V, o, dl);
+  else
+    combine_bwd_kernel<false, false><<<grid, dim3(256), 0, s>>>(a, b, idx, w, slot, T, k, C, V, o, dl);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_grad(const void* dh, const void* h, const int32_t* idx, const float* w, const int32_t* slot,
+                            int64_t T, int64_t F, int k, int64_t C, bool bf16, float* dl, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (k > 32) return hipErrorInvalidValue;
+  const int64_t VF = F * (bf16 ? 2 : 4) / 16;
+  const dim3 grid(static_cast<unsigned>(ceil_div(T, 4)));
+  const auto* a = static_cast<const uint4*>(dh);
+  const auto* b = static_cast<const uint4*>(h);
+  if (bf16)
+    gate_grad_kernel<true><<<grid, dim3(256), 0, s>>>(a, b, idx, w, slot, T, k, C, VF, dl);
+  else
+    gate_grad_kernel<false><<<grid, dim3(256), 0, s>>>(a, b, idx, w, slot, T, k, C, VF, dl);
   return hipGetLastError();
 }
 

@@ -152,10 +152,15 @@ hipError_t launch_swiglu_fwd(const void* g, const void* u, void* h, const int32_
 // dgu [E][C][2F] = [dh u silu'(g) | dh silu(g)] on kept rows.
 hipError_t launch_swiglu_bwd(const void* dh, const void* g, const void* u, void* dgu, const int32_t* kept, int E,
                              int64_t C, int64_t F, bool bf16, hipStream_t s);
-// dy rows of kept copies = w dout; dl [T][k] = gate gradients.
+// dy rows of kept copies = w dout; with y (the expert outputs) also dl [T][k],
+// the gate gradients (y NULL: dl untouched).
 hipError_t launch_combine_bwd(const void* dout, const void* y, const int32_t* idx, const float* w,
                               const int32_t* slot, int64_t T, int64_t d, int k, int64_t C, bool bf16, void* dy,
                               float* dl, hipStream_t s);
+// dl [T][k], the gate gradients, from the hidden gradients dh = dy Wd and
+// activations h of the kept copies ([E][C][F] each).
+hipError_t launch_gate_grad(const void* dh, const void* h, const int32_t* idx, const float* w, const int32_t* slot,
+                            int64_t T, int64_t F, int k, int64_t C, bool bf16, float* dl, hipStream_t s);
 // dx = dout + sum_j [kept] dX[e_j, s_j] + sum_j dl_j Wr[e_j].
 hipError_t launch_gather_dx(const void* dout, const void* dX, const void* wr, const int32_t* idx, const float* dl,
                             const int32_t* slot, int64_t T, int64_t d, int k, int64_t C, bool bf16, void* dx,

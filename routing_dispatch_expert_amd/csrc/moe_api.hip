@@ -452,7 +452,8 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   const int bm = moe::grouped_gemm_bm(bf16, C);
   const int64_t F = d_ff;
 
-  // 1. the forward again: routing, buckets X, g, u, h, y
+  // 1. the forward again: routing, buckets X, g, u, h (y is not needed: the
+  //    gate gradients come from dh and h, step 4)
   const int splits = moe::router_splits(T, d, E, bf16);
   const bool fused_hist = moe::route_builds_histogram(k);
   MOE_HIP_TRY(moe::launch_router_logits(x, W_router, T, d, E, bf16, splits, p.logits, s), "router logits");
@@ -482,10 +483,9 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
                                     bmo_d),
               "gemm u");
   MOE_HIP_TRY(moe::launch_swiglu_fwd(b.g, b.u, p.h, p.kept, E, C, F, bf16, s), "swiglu");
-  MOE_HIP_TRY(moe::launch_gemm_down(p.h, p.kept, p.mtile, W_down, E, C, d, F, bf16, p.y, s, nullptr, sk), "gemm y");
 
-  // 2. combine backward: dy = w dout on kept rows, dl = gate gradients
-  MOE_HIP_TRY(moe::launch_combine_bwd(dout, p.y, p.idx, p.w, p.slot, T, d, k, C, bf16, b.dy, b.dl, s),
+  // 2. combine backward: dy = w dout on kept rows
+  MOE_HIP_TRY(moe::launch_combine_bwd(dout, nullptr, p.idx, p.w, p.slot, T, d, k, C, bf16, b.dy, nullptr, s),
               "combine backward");
   // 3. dh = dy Wd; dg, du. 4. dX = [dg | du] [Wg ; Wu]. Either straight from the
   //    weights (K-major B: Wd is [d][d_ff] = [K][N], Wg and Wu are [d_ff][d]),
@@ -510,6 +510,8 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
     MOE_HIP_TRY(moe::launch_gemm_down(b.dgu, p.kept, p.mtile, b.WguT, E, C, d, 2 * F, bf16, b.dX, s, nullptr, sk),
                 "gemm dX");
   }
+  //    the gate gradients: q_j = <dh_j, h_j> = w_j <dout, y_j>, dl_j = q_j - w_j sum_i q_i
+  MOE_HIP_TRY(moe::launch_gate_grad(b.dh, p.h, p.idx, p.w, p.slot, T, F, k, C, bf16, b.dl, s), "gate gradients");
   // 5. router gradients, then dx = dout + the expert paths + the router path
   MOE_HIP_TRY(moe::launch_router_wgrad(x, p.idx, b.dl, T, k, E, d, bf16, b.rpart, dW_router, d_bias, s),
               "router wgrad");
