@@ -163,7 +163,7 @@ def run_backward(args, wl, moe, torch, np, dev, to_dev, host_w):
                              cf, wl.dtype, P=P, bias=wl.bias_vec, tokens=np.arange(0), max_ranks=wl.max_ranks)
     n_kept = int(r["kept"].sum())
     algo = 12 * n_kept * d * d_ff  # dh, dX (two), dWd, dWg, dWu: 2 N d d_ff flop each
-    done = algo + 6 * n_kept * d * d_ff  # plus the recomputed forward GEMMs
+    done = algo + 4 * n_kept * d * d_ff  # plus the recomputed g and u
     tf = algo / gpu_ms / 1e9
     cpu = None
     if not args.no_cpu_baseline:
