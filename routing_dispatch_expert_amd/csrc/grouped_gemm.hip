@@ -422,9 +422,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BM >= 25
 // ---------------------------------------------------------------------------
 // bf16 matrix-core GEMM with the operands brought into LDS by the buffer
 // unit itself (buffer_load_dwordx4 ... lds), bypassing registers. 256 x 256
-// block, 4 waves (2 x 2) of 128 x 128, each as 4 x 4 v_mfma_f32_32x32x16_bf16
-// tiles; K in 64-wide stages (every row a whole 128-byte line) through two
-// LDS slots: stage k + 1 streams in while stage k feeds the matrix cores.
+// block of NW waves: with 4, one per SIMD, 2 x 2 waves of 128 x 128 (4 x 4
+// v_mfma_f32_32x32x16_bf16 tiles); with 8, two per SIMD, 2 x 4 waves of
+// 128 x 64 (4 x 2 tiles), so while one wave of a SIMD waits at a barrier or
+// on its DMA the other's matrix work keeps the SIMD busy (the block tile, and
+// with it the LDS and L2 traffic per flop, stays that of 256 x 256). K in
+// 64-wide stages (every row a whole 128-byte line) through two LDS slots:
+// stage k + 1 streams in while stage k feeds the matrix cores.
 // Needs K % 128 == 0.
 // LDS rows are 64 elements (eight 16-byte chunks); chunk c of row r sits at
 // c ^ ((r / 2) % 8), so 16 lanes reading 16 consecutive rows hit 16 distinct
@@ -462,8 +466,8 @@ __device__ inline void wait_vm_lgkm0() {
 // contracts over kk[e] rows (rounded up to whole 128-row stage pairs, the
 // rows past kk[e] reading as zero), every group has C (= M) output rows, and
 // kept and mtile_off are NULL.
-template <bool SWIGLU, bool BT = false, bool F32OUT = false, bool AT = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_dma_kernel(
+template <bool SWIGLU, bool BT = false, bool F32OUT = false, bool AT = false, int NW = 4>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void gemm_bf16_dma_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     bf16_t* __restrict__ out, const int32_t* __restrict__ kept, const int32_t* __restrict__ mtile_off,
     int E, int64_t C, int64_t K, int64_t N, int nt_count, const int32_t* __restrict__ wmap,
@@ -473,10 +477,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   static_assert(!(SWIGLU && BT), "the K-major B operand serves the plain GEMM only");
   static_assert(!(F32OUT && (SWIGLU || BT)), "fp32 output serves the plain GEMM only");
   static_assert(!AT || (BT && !F32OUT), "a K-major A comes with a K-major B");
-  constexpr int BM = 256, BN = 256, BK = 64, TM = 4, TN = 4;
+  static_assert(NW == 4 || (NW == 8 && !BT && !F32OUT), "8 waves serve the row-major GEMMs with bf16 output");
+  // NW = 4: one wave per SIMD, 2 x 2 waves of 128 x 128. NW = 8: two waves per
+  // SIMD, 2 x 4 waves of 128 x 64, so one wave's matrix work covers the other's
+  // barrier and DMA waits.
+  constexpr int BM = 256, BN = 256, BK = 64, TM = 4, TN = NW == 4 ? 4 : 2;
+  constexpr int WNC = NW / 2;                   // waves along N
+  constexpr int NTHR = NW * 64;
   constexpr int CH = BK / 8;                    // 16-byte chunks per LDS row
   constexpr int BNO = SWIGLU ? BN / 2 : BN;
-  constexpr int PER_WAVE = BM / 8 / 4;          // 8-row DMA blocks per wave and operand
+  constexpr int PER_WAVE = BM / 8 / NW;         // 8-row DMA blocks per wave and operand
   __shared__ uint4 As0[BM * CH], As1[BM * CH];
   __shared__ uint4 Bs0[BN * CH], Bs1[BN * CH];
   __shared__ int arrival;
@@ -504,9 +514,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const auto ra_src = AT ? buffer_rsrc(A + static_cast<int64_t>(e) * a_es, static_cast<uint32_t>(kr_e * lda * 2))
                          : buffer_rsrc(A + static_cast<int64_t>(e) * C * K,
                                        static_cast<uint32_t>(min(static_cast<int64_t>(rows), C) * K * 2));
-  // B rows 0..127 of a SwiGLU block are gate rows, 128..255 up rows: waves 0-1
-  // load the first half, waves 2-3 the second
-  const bf16_t* bbase = (SWIGLU && wave >= 2) ? B1 : B0;
+  // B rows 0..127 of a SwiGLU block are gate rows, 128..255 up rows: the first
+  // half of the waves load the first half
+  const bf16_t* bbase = (SWIGLU && wave >= NW / 2) ? B1 : B0;
   const int we = wmap ? __builtin_amdgcn_readfirstlane(wmap[e]) : e;  // expert whose weights this row tile uses
   const int64_t kb0 = BT ? K0 : K;  // K rows held by B0
   const auto rb_src = AT ? buffer_rsrc(B0 + static_cast<int64_t>(e) * b_es, static_cast<uint32_t>(kr_e * N * 2))
@@ -514,7 +524,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                        static_cast<uint32_t>(N * kb0 * 2));
   const auto rb_src1 = buffer_rsrc(BT && B1 ? B1 + static_cast<int64_t>(we) * N * (K - K0) : B0,
                                    BT && B1 ? static_cast<uint32_t>(N * (K - K0) * 2) : 0u);
-  uint32_t a_voff[PER_WAVE], b_voff[PER_WAVE];
+  // sized for 4 waves (a size that depends on NW makes the host pass drop the kernel)
+  uint32_t a_voff[BM / 8 / 4], b_voff[BM / 8 / 4];
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
     const int row = (wave * PER_WAVE + i) * 8 + (lane >> 3);
@@ -561,15 +572,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   };
 
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WNC, wn = wave % WNC;
   const int lr = lane & 31, lk = lane >> 5;
   int a_row[TM], b_row[TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i) a_row[i] = (wm * (BM / 2) + i * 32 + lr) * CH;
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    const int br = SWIGLU ? ((j < TN / 2) ? (wn * (BN / 4) + j * 32) : (BN / 2 + wn * (BN / 4) + (j - TN / 2) * 32))
-                          : (wn * (BN / 2) + j * 32);
+    const int br = SWIGLU ? ((j < TN / 2) ? (wn * (TN / 2 * 32) + j * 32)
+                                          : (BN / 2 + wn * (TN / 2 * 32) + (j - TN / 2) * 32))
+                          : (wn * (TN * 32) + j * 32);
     b_row[j] = (br + lr) * CH;
   }
   // K-major B: byte offset, within a stage, of this lane's first 8-byte piece
@@ -707,14 +719,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // blocks to arrive adds the s partials in chunk order, so the sum does
     // not depend on which block came last.
     constexpr int NG = TM * TN * 4;  // float4 groups per thread
-    float4* mine = reinterpret_cast<float4*>(part) + static_cast<int64_t>(ti * split + chunk) * NG * 256;
+    float4* mine = reinterpret_cast<float4*>(part) + static_cast<int64_t>(ti * split + chunk) * NG * NTHR;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          mine[((i * TN + j) * 4 + q) * 256 + tid] =
+          mine[((i * TN + j) * 4 + q) * NTHR + tid] =
               float4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
     __threadfence();
     __syncthreads();
@@ -726,7 +738,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // a group's s loads are in flight together (a load-add chain would wait
     // out the memory latency once per load)
     const float4* first =
-        reinterpret_cast<const float4*>(part) + static_cast<int64_t>(ti * split) * NG * 256 + tid;
+        reinterpret_cast<const float4*>(part) + static_cast<int64_t>(ti * split) * NG * NTHR + tid;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -737,7 +749,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           float4 v[kMaxSplit];
 #pragma unroll
           for (int c = 0; c < kMaxSplit; ++c)
-            if (c < split) v[c] = first[(static_cast<int64_t>(c) * NG + g) * 256];
+            if (c < split) v[c] = first[(static_cast<int64_t>(c) * NG + g) * NTHR];
           float4 t = v[0];
 #pragma unroll
           for (int c = 1; c < kMaxSplit; ++c)
@@ -770,15 +782,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
     return;
   }
-  // the stage buffers are free: one per wave for the epilogue
+  // the stage buffers are free: one per wave for the epilogue (half of one with 8 waves)
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
-  char* eb = reinterpret_cast<char*>(wave == 0 ? As0 : wave == 1 ? As1 : wave == 2 ? Bs0 : Bs1);
+  const int sb = wave / (NW / 4);
+  char* eb = reinterpret_cast<char*>(sb == 0 ? As0 : sb == 1 ? As1 : sb == 2 ? Bs0 : Bs1) +
+             (wave % (NW / 4)) * (BM * CH * 16 / (NW / 4));
   // K-major (BT) instantiations run only in the backward pass, where non-temporal stores
   // measured 0.2-2% faster end to end; the forward GEMMs measured faster with plain stores
-  store_wave_tile<TM, TN, SWIGLU, BM * CH * 16, true, BT>(acc, eb, out + static_cast<int64_t>(e) * C * N,
-                                                 m0 + wm * (BM / 2), rows, n0 + wn * (SWIGLU ? BN / 4 : BN / 2),
-                                                 N, lane);
+  store_wave_tile<TM, TN, SWIGLU, BM * CH * 16 / (NW / 4), true, BT>(
+      acc, eb, out + static_cast<int64_t>(e) * C * N, m0 + wm * (BM / 2), rows,
+      n0 + wn * (SWIGLU ? TN * 16 : TN * 32), N, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1165,6 +1179,12 @@ int resident_groups() {
   return g;
 }
 
+// Waves per work-group of the 256 x 256 kernel on the row-major GEMMs.
+#ifndef MOE_DMA_WAVES
+#define MOE_DMA_WAVES 8
+#endif
+constexpr int kDmaWaves = MOE_DMA_WAVES;
+
 template <int BM, int BN, bool SWIGLU>
 hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out, const int32_t* kept,
                        const int32_t* mtile_off, int E, int64_t C, int64_t K, int64_t N, const int32_t* wmap,
@@ -1180,14 +1200,20 @@ hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out,
     if (K % 64) return hipErrorInvalidValue;  // callers pick this tile only for K % 64 == 0
     gemm_bf16_dma_m128_kernel<SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
         pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap);
-  } else if (BM == 256 && BN == 256 && K % 128 == 0) {
+  } else if constexpr (BM == 256 && BN == 256) {
+    if (K % 128) {
+      gemm_bf16_kernel<BM, BN, SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
+          pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap);
+      return hipGetLastError();
+    }
     const int G = sk ? resident_groups() : 0;
     if (G > 0) {
       const hipError_t err = launch_fill_i32(sk->tick, G, 0, s);
       if (err != hipSuccess) return err;
       blocks += G;  // the split round: at most G blocks beyond the whole tiles
     }
-    gemm_bf16_dma_kernel<SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
+    gemm_bf16_dma_kernel<SWIGLU, false, false, false, kDmaWaves>
+        <<<dim3(static_cast<unsigned>(blocks)), dim3(kDmaWaves * 64), 0, s>>>(
         pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap, G > 0 ? sk->part : nullptr,
         G > 0 ? sk->tick : nullptr, G);
   } else {
