@@ -477,7 +477,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   static_assert(!(SWIGLU && BT), "the K-major B operand serves the plain GEMM only");
   static_assert(!(F32OUT && (SWIGLU || BT)), "fp32 output serves the plain GEMM only");
   static_assert(!AT || (BT && !F32OUT), "a K-major A comes with a K-major B");
-  static_assert(NW == 4 || (NW == 8 && !BT && !F32OUT), "8 waves serve the row-major GEMMs with bf16 output");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   // NW = 4: one wave per SIMD, 2 x 2 waves of 128 x 128. NW = 8: two waves per
   // SIMD, 2 x 4 waves of 128 x 64, so one wave's matrix work covers the other's
   // barrier and DMA waits.
@@ -592,7 +592,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     const int kr = 8 * (g >> 1) + (jj >> 2);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int nl = wn * (BN / 2) + j * 32 + 16 * (g & 1) + 4 * (jj & 3);
+      const int nl = wn * (TN * 32) + j * 32 + 16 * (g & 1) + 4 * (jj & 3);
       bt_off[j] = kr * (BN * 2) + (((nl >> 3) ^ (4 * (jj >> 2))) * 16) + (nl & 7) * 2;
     }
     if constexpr (AT) {  // the same for the 32-row blocks of A (BM == BN)
@@ -777,7 +777,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int r = m0 + wm * (BM / 2) + i * 32 + 8 * (q >> 2) + 4 * lk + (q & 3);
-          const int64_t c = n0 + wn * (BN / 2) + j * 32 + lr;
+          const int64_t c = n0 + wn * (TN * 32) + j * 32 + lr;
           if (r < rows && c < N) o[r * N + c] = acc[i][j][q];
         }
     return;
@@ -1179,11 +1179,25 @@ int resident_groups() {
   return g;
 }
 
-// Waves per work-group of the 256 x 256 kernel on the row-major GEMMs.
+// Waves per work-group of the 256 x 256 kernel: row-major GEMMs, fp32-output
+// row GEMM (router scores), K-major B (backward dh, dX), K-major A and B
+// (weight gradients).
 #ifndef MOE_DMA_WAVES
 #define MOE_DMA_WAVES 8
 #endif
+#ifndef MOE_ROWS_F32_WAVES
+#define MOE_ROWS_F32_WAVES 8
+#endif
+#ifndef MOE_KMAJOR_WAVES
+#define MOE_KMAJOR_WAVES 8
+#endif
+#ifndef MOE_TN_WAVES
+#define MOE_TN_WAVES 8
+#endif
 constexpr int kDmaWaves = MOE_DMA_WAVES;
+constexpr int kRowsF32Waves = MOE_ROWS_F32_WAVES;
+constexpr int kKmajorWaves = MOE_KMAJOR_WAVES;
+constexpr int kTnWaves = MOE_TN_WAVES;
 
 template <int BM, int BN, bool SWIGLU>
 hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out, const int32_t* kept,
@@ -1231,7 +1245,8 @@ hipError_t launch_gemm_rows_f32(const void* a, const void* b, int64_t M, int64_t
   if (K % 128 || N % 8 || slices < 1 || slices > K / 128) return hipErrorInvalidValue;
   const int64_t nt = ceil_div(N, 256);
   const int64_t blocks = ceil_div(M, 256) * nt * slices;
-  gemm_bf16_dma_kernel<false, false, true><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
+  gemm_bf16_dma_kernel<false, false, true, false, kRowsF32Waves>
+      <<<dim3(static_cast<unsigned>(blocks)), dim3(kRowsF32Waves * 64), 0, s>>>(
       static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b), nullptr, reinterpret_cast<bf16_t*>(out),
       nullptr, nullptr, 1, M, K, N, static_cast<int>(nt), nullptr, nullptr, nullptr, 0, 0, slices);
   return hipGetLastError();
@@ -1243,7 +1258,8 @@ hipError_t launch_gemm_tn(const void* a, int64_t lda, int64_t a_es, int64_t aoff
   if (M % 8 || N % 8 || lda % 8 || aoff % 8 || aoff + M > lda) return hipErrorInvalidValue;
   const int64_t nt = ceil_div(N, 256);
   const int64_t blocks = ceil_div(E * ceil_div(M, 256) * nt, 8) * 8;
-  gemm_bf16_dma_kernel<false, true, false, true><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
+  gemm_bf16_dma_kernel<false, true, false, true, kTnWaves>
+      <<<dim3(static_cast<unsigned>(blocks)), dim3(kTnWaves * 64), 0, s>>>(
       static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b), nullptr, static_cast<bf16_t*>(out), nullptr,
       nullptr, E, M, 0, N, static_cast<int>(nt), nullptr, nullptr, nullptr, 0, 0, 1, kk, lda, a_es, aoff, b_es);
   return hipGetLastError();
@@ -1263,7 +1279,8 @@ hipError_t launch_gemm_kmajor_b(const void* a, const int32_t* kept, const int32_
     if (err != hipSuccess) return err;
     blocks += G;
   }
-  gemm_bf16_dma_kernel<false, true><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
+  gemm_bf16_dma_kernel<false, true, false, false, kKmajorWaves>
+      <<<dim3(static_cast<unsigned>(blocks)), dim3(kKmajorWaves * 64), 0, s>>>(
       static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0), static_cast<const bf16_t*>(b1),
       static_cast<bf16_t*>(out), kept, mtile_off, E, C, K, N, static_cast<int>(nt), nullptr,
       G > 0 ? sk->part : nullptr, G > 0 ? sk->tick : nullptr, G, K0);
