@@ -94,14 +94,20 @@ hipError_t launch_scatter_rows(const void* x, const int32_t* idx, const int32_t*
 // Row-tile height the grouped GEMM uses for these sizes (the mtile map must
 // be built for the same value).
 int grouped_gemm_bm(bool bf16, int64_t C);
-// The same for GEMM 1 (gate/up), whose long K favours taller tiles sooner.
-int grouped_gemm_bm_gate_up(bool bf16, int64_t C);
-// Scratch that lets the 256 x 256 GEMM split the tiles of its last, partly
-// filled round over K: fp32 partial tiles of up to kSplitUnits work-groups and
-// one arrival counter per split tile (cleared by the launcher).
+// The same for GEMM 1 (gate/up, contraction length K = d), whose long K
+// favours taller tiles sooner.
+int grouped_gemm_bm_gate_up(bool bf16, int64_t C, int64_t K);
+// Row-tile height of the backward GEMMs that contract over d (the g and u
+// recompute, dh, dX): GEMM 1's choice without the 320-row tile.
+int grouped_gemm_bm_contract_d(bool bf16, int64_t C);
+// Scratch that lets the 256-column LDS-DMA GEMM split the tiles of its last,
+// partly filled round over K: fp32 partial tiles (up to 320 x 256) of up to
+// kSplitUnits work-groups and one arrival counter per split tile (cleared by
+// the launcher).
 constexpr int kSplitUnits = 256;
+constexpr int kSplitTileElems = 320 * 256;
 struct SplitK {
-  float* part;    // [kSplitUnits][256 * 256]
+  float* part;    // [kSplitUnits][kSplitTileElems]
   int32_t* tick;  // [kSplitUnits]
 };
 size_t split_k_bytes();

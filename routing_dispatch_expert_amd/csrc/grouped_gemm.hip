@@ -192,6 +192,12 @@ constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, 
 // SWIGLU the tiles j < TN/2 hold gate and j + TN/2 the matching up values, and
 // silu(gate) * up is stored. Rows >= rows and columns >= N are not written
 // (N % 8 == 0). NT marks the stores non-temporal (results nothing reads soon).
+constexpr int staged_rows(int wr, int rs, int cap) {
+  for (int h = wr; h >= 32; h -= 32)
+    if (wr % h == 0 && h * rs <= cap) return h;
+  return 0;
+}
+
 template <int TM, int TN, bool SWIGLU, int CAP, bool PAD = true, bool NT = false>
 __device__ inline void store_wave_tile(const f32x16 (&acc)[TM][TN], char* eb, bf16_t* __restrict__ out,
                                        int row0, int rows, int64_t col0, int64_t N, int lane) {
@@ -201,9 +207,9 @@ __device__ inline void store_wave_tile(const f32x16 (&acc)[TM][TN], char* eb, bf
   // without padding, rows with bit 2 of the row index set keep their 64-byte
   // halves swapped, which separates the half-waves just as well
   auto at = [&](int r, int byte) { return r * RS + (PAD ? byte : (byte ^ (((r >> 2) & 1) << 6))); };
-  constexpr int HR = WR * RS <= CAP ? WR : WR / 2;   // rows staged per pass
+  constexpr int HR = staged_rows(WR, RS, CAP);       // rows staged per pass
   constexpr int CPR = OC / 8;                        // 16-byte chunks per row
-  static_assert(HR * RS <= CAP, "staging rows fit the LDS slice");
+  static_assert(HR > 0 && HR * RS <= CAP, "staging rows fit the LDS slice");
   const int lr = lane & 31, lk = lane >> 5;
 #pragma unroll
   for (int pass = 0; pass < WR / HR; ++pass) {
@@ -466,7 +472,7 @@ __device__ inline void wait_vm_lgkm0() {
 // contracts over kk[e] rows (rounded up to whole 128-row stage pairs, the
 // rows past kk[e] reading as zero), every group has C (= M) output rows, and
 // kept and mtile_off are NULL.
-template <bool SWIGLU, bool BT = false, bool F32OUT = false, bool AT = false, int NW = 4>
+template <bool SWIGLU, bool BT = false, bool F32OUT = false, bool AT = false, int NW = 4, int TM_ = 4>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void gemm_bf16_dma_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     bf16_t* __restrict__ out, const int32_t* __restrict__ kept, const int32_t* __restrict__ mtile_off,
@@ -478,15 +484,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   static_assert(!(F32OUT && (SWIGLU || BT)), "fp32 output serves the plain GEMM only");
   static_assert(!AT || (BT && !F32OUT), "a K-major A comes with a K-major B");
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(TM_ == 4 || (TM_ == 5 && NW == 8 && !BT && !AT && !F32OUT), "320-row blocks: 8 waves, row-major");
   // NW = 4: one wave per SIMD, 2 x 2 waves of 128 x 128. NW = 8: two waves per
-  // SIMD, 2 x 4 waves of 128 x 64, so one wave's matrix work covers the other's
-  // barrier and DMA waits.
-  constexpr int BM = 256, BN = 256, BK = 64, TM = 4, TN = NW == 4 ? 4 : 2;
+  // SIMD, 2 x 4 waves of (32 TM) x 64, so one wave's matrix work covers the
+  // other's barrier and DMA waits. TM = 5 makes the block 320 rows tall.
+  constexpr int TM = TM_, BM = 64 * TM, BN = 256, BK = 64, TN = NW == 4 ? 4 : 2;
   constexpr int WNC = NW / 2;                   // waves along N
   constexpr int NTHR = NW * 64;
   constexpr int CH = BK / 8;                    // 16-byte chunks per LDS row
   constexpr int BNO = SWIGLU ? BN / 2 : BN;
-  constexpr int PER_WAVE = BM / 8 / NW;         // 8-row DMA blocks per wave and operand
+  constexpr int PWA = BM / 8 / NW, PWB = BN / 8 / NW;  // 8-row DMA blocks per wave: A, B
   __shared__ uint4 As0[BM * CH], As1[BM * CH];
   __shared__ uint4 Bs0[BN * CH], Bs1[BN * CH];
   __shared__ int arrival;
@@ -524,23 +531,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
                                        static_cast<uint32_t>(N * kb0 * 2));
   const auto rb_src1 = buffer_rsrc(BT && B1 ? B1 + static_cast<int64_t>(we) * N * (K - K0) : B0,
                                    BT && B1 ? static_cast<uint32_t>(N * (K - K0) * 2) : 0u);
-  // sized for 4 waves (a size that depends on NW makes the host pass drop the kernel)
-  uint32_t a_voff[BM / 8 / 4], b_voff[BM / 8 / 4];
+  // fixed sizes (a size that depends on the template parameters makes the host
+  // pass drop the kernel); PWA, PWB <= 8
+  uint32_t a_voff[8], b_voff[8];
 #pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int row = (wave * PER_WAVE + i) * 8 + (lane >> 3);
+  for (int i = 0; i < PWA; ++i) {
+    const int row = (wave * PWA + i) * 8 + (lane >> 3);
     const int ch = (lane & 7) ^ ((row >> 1) & 7);  // the chunk stored at position lane % 8
     if constexpr (AT) {  // as B below: K rows 2 u and 2 u + 1 of the stage, 32 positions each
-      const int kr = (wave * PER_WAVE + i) * 2 + (lane >> 5);
+      const int kr = (wave * PWA + i) * 2 + (lane >> 5);
       const int c = (lane & 31) ^ (4 * (kr & 3));
       const int64_t am = m0 + c * 8;
       a_voff[i] = am < C ? static_cast<uint32_t>((kr * lda + aoff + am) * 2) : 0x80000000u;
     } else {
       a_voff[i] = static_cast<uint32_t>((m0 + row) * K * 2 + ch * 16);  // rows past kept read as zero
     }
+  }
+#pragma unroll
+  for (int i = 0; i < PWB; ++i) {
+    const int row = (wave * PWB + i) * 8 + (lane >> 3);
+    const int ch = (lane & 7) ^ ((row >> 1) & 7);
     if constexpr (BT) {
-      // one instruction fills K rows 2 u and 2 u + 1 of the stage (u = wave * 8 + i), 32 positions each
-      const int kr = (wave * PER_WAVE + i) * 2 + (lane >> 5);
+      // one instruction fills K rows 2 u and 2 u + 1 of the stage (u = wave * PWB + i), 32 positions each
+      const int kr = (wave * PWB + i) * 2 + (lane >> 5);
       const int c = (lane & 31) ^ (4 * (kr & 3));  // the chunk stored at position lane % 32
       const int64_t bn = n0 + c * 8;
       b_voff[i] = bn < N ? static_cast<uint32_t>((kr * N + bn) * 2) : 0x80000000u;
@@ -553,21 +566,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     const uint32_t soff = static_cast<uint32_t>(ks * BK * 2);
     const uint32_t asoff = AT ? static_cast<uint32_t>(ks * BK * lda * 2) : soff;
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_src, MOE_LDS(as + (wave * PER_WAVE + i) * 8 * CH), 16,
+    for (int i = 0; i < PWA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_src, MOE_LDS(as + (wave * PWA + i) * 8 * CH), 16,
                                                a_voff[i], asoff, 0, 0);
     if constexpr (BT) {
       const bool second = !AT && ks * BK >= K0;  // uniform: K0 is a multiple of the stage depth
       const auto rb = second ? rb_src1 : rb_src;
       const uint32_t bsoff = static_cast<uint32_t>((second ? ks * BK - K0 : ks * BK) * N * 2);
 #pragma unroll
-      for (int i = 0; i < PER_WAVE; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MOE_LDS(bs + (wave * PER_WAVE + i) * 8 * CH), 16, b_voff[i],
+      for (int i = 0; i < PWB; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, MOE_LDS(bs + (wave * PWB + i) * 8 * CH), 16, b_voff[i],
                                                  bsoff, 0, 0);
     } else {
 #pragma unroll
-      for (int i = 0; i < PER_WAVE; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_src, MOE_LDS(bs + (wave * PER_WAVE + i) * 8 * CH), 16,
+      for (int i = 0; i < PWB; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb_src, MOE_LDS(bs + (wave * PWB + i) * 8 * CH), 16,
                                                  b_voff[i], soff, 0, 0);
     }
   };
@@ -703,8 +716,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     stage(F_{}, As1, Bs1, As0, Bs0, k + 1);
   };
   if (ke > kb) {  // with AT a group that kept no row contracts over nothing: its block is zero
-    if (ta > 2)
+    if (ta >= TM || (TM == 4 && ta == 3))
       kloop(std::integral_constant<int, TM>{});
+    else if (TM == 5 && ta == 4)
+      kloop(std::integral_constant<int, TM == 5 ? 4 : TM>{});
+    else if (TM == 5 && ta == 3)
+      kloop(std::integral_constant<int, TM == 5 ? 3 : TM>{});
     else if (ta == 2)
       kloop(std::integral_constant<int, 2>{});
     else if (ta == 1)
@@ -786,11 +803,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
   const int sb = wave / (NW / 4);
-  char* eb = reinterpret_cast<char*>(sb == 0 ? As0 : sb == 1 ? As1 : sb == 2 ? Bs0 : Bs1) +
-             (wave % (NW / 4)) * (BM * CH * 16 / (NW / 4));
+  constexpr int EB = BN * CH * 16 / (NW / 4);  // bytes per wave (A slots are at least as large)
+  char* eb = reinterpret_cast<char*>(sb == 0 ? As0 : sb == 1 ? As1 : sb == 2 ? Bs0 : Bs1) + (wave % (NW / 4)) * EB;
   // K-major (BT) instantiations run only in the backward pass, where non-temporal stores
   // measured 0.2-2% faster end to end; the forward GEMMs measured faster with plain stores
-  store_wave_tile<TM, TN, SWIGLU, BM * CH * 16 / (NW / 4), true, BT>(
+  store_wave_tile<TM, TN, SWIGLU, EB, true, BT>(
       acc, eb, out + static_cast<int64_t>(e) * C * N, m0 + wm * (BM / 2), rows,
       n0 + wn * (SWIGLU ? TN * 16 : TN * 32), N, lane);
 }
@@ -1125,13 +1142,13 @@ constexpr int kBigTileMinCGateUp = MOE_BIG_TILE_MIN_C_GATE_UP;
 constexpr int kSkinnyMaxC = kSkinnyRows;
 
 size_t split_k_bytes() {
-  return static_cast<size_t>(kSplitUnits) * 256 * 256 * sizeof(float) + kSplitUnits * sizeof(int32_t);
+  return static_cast<size_t>(kSplitUnits) * kSplitTileElems * sizeof(float) + kSplitUnits * sizeof(int32_t);
 }
 
 SplitK split_k_carve(void* base) {
   if (!base) return SplitK{nullptr, nullptr};
   auto* p = static_cast<float*>(base);
-  return SplitK{p, reinterpret_cast<int32_t*>(p + static_cast<size_t>(kSplitUnits) * 256 * 256)};
+  return SplitK{p, reinterpret_cast<int32_t*>(p + static_cast<size_t>(kSplitUnits) * kSplitTileElems)};
 }
 
 int grouped_gemm_bm(bool bf16, int64_t C) {
@@ -1143,10 +1160,21 @@ int grouped_gemm_bm(bool bf16, int64_t C) {
 // GEMM 1 reads each weight tile once per row tile: from 256 rows of capacity
 // on, one 256-row tile per expert (its padding rows cost no matrix work and no
 // loads) beats two 128-row tiles that each stream the weights.
-int grouped_gemm_bm_gate_up(bool bf16, int64_t C) {
+int grouped_gemm_bm_contract_d(bool bf16, int64_t C) {
   if (!bf16) return 64;
   if (C <= kSkinnyMaxC) return kSkinnyRows;
   return C >= kBigTileMinCGateUp ? 256 : 128;
+}
+
+// With 256 < C <= 320 a 256-row tile would leave most experts a second, nearly
+// empty tile that streams the same weights again; one 320-row tile covers
+// every expert (needs K % 128 == 0, as the 256-row tile does).
+#ifndef MOE_TALL_TILE
+#define MOE_TALL_TILE 1
+#endif
+int grouped_gemm_bm_gate_up(bool bf16, int64_t C, int64_t K) {
+  if (MOE_TALL_TILE && bf16 && C > 256 && C <= 320 && K % 128 == 0) return 320;
+  return grouped_gemm_bm_contract_d(bf16, C);
 }
 
 namespace {
@@ -1210,7 +1238,18 @@ hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out,
   const auto* pb0 = static_cast<const bf16_t*>(b0);
   const auto* pb1 = static_cast<const bf16_t*>(b1);
   auto* po = static_cast<bf16_t*>(out);
-  if constexpr (BM == 128 && BN == 256) {
+  if constexpr (BM == 320 && BN == 256) {
+    if (K % 128) return hipErrorInvalidValue;  // callers pick this tile only for K % 128 == 0
+    const int G = sk ? resident_groups() : 0;
+    if (G > 0) {
+      const hipError_t err = launch_fill_i32(sk->tick, G, 0, s);
+      if (err != hipSuccess) return err;
+      blocks += G;
+    }
+    gemm_bf16_dma_kernel<SWIGLU, false, false, false, 8, 5><<<dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s>>>(
+        pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap, G > 0 ? sk->part : nullptr,
+        G > 0 ? sk->tick : nullptr, G);
+  } else if constexpr (BM == 128 && BN == 256) {
     if (K % 64) return hipErrorInvalidValue;  // callers pick this tile only for K % 64 == 0
     gemm_bf16_dma_m128_kernel<SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
         pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap);
@@ -1293,9 +1332,12 @@ hipError_t launch_gemm_gate_up(const void* buckets, const int32_t* kept, const i
                                const SplitK* sk) {
   if (E * C == 0) return hipSuccess;
   if (bf16) {
-    if (grouped_gemm_bm_gate_up(true, C) == kSkinnyRows && d % 32 == 0)
+    const int bm = grouped_gemm_bm_gate_up(true, C, d);
+    if (bm == kSkinnyRows && d % 32 == 0)
       return launch_skinny<true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s);
-    if (grouped_gemm_bm_gate_up(true, C) == 256)
+    if (bm == 320)
+      return launch_bf16<320, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s, sk);
+    if (bm == 256)
       return launch_bf16<256, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s, sk);
     if (d % 64 == 0)
       return launch_bf16<128, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s);

@@ -178,7 +178,7 @@ LayerPlan plan_layer(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E, in
 // read the weights K-major where the 256-row LDS-DMA kernel can: then no
 // transposed weight copies are made.
 bool backward_kmajor(bool bf16, int64_t C, int64_t d, int64_t F) {
-  return bf16 && moe::grouped_gemm_bm_gate_up(bf16, C) == 256 && d % 128 == 0 && F % 64 == 0;
+  return bf16 && moe::grouped_gemm_bm_contract_d(bf16, C) == 256 && d % 128 == 0 && F % 64 == 0;
 }
 
 struct BackPlan {
@@ -393,7 +393,7 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
   MOE_HIP_TRY(moe::launch_scatter_rows(x, idx, slot, T, k, C, d * eb, buckets, s), "scatter");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, false, s), "event");
-  const int bm_gu = moe::grouped_gemm_bm_gate_up(bf16, C);
+  const int bm_gu = moe::grouped_gemm_bm_gate_up(bf16, C, d);
   if (bm_gu != bm) MOE_HIP_TRY(moe::launch_mtile_map(kept, E, bm_gu, p.mtile_gu, s), "tile map (gate, up)");
   MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, bm_gu != bm ? p.mtile_gu : p.mtile, W_gate, W_up, E, C, d, d_ff,
                                        bf16, p.h, s, nullptr, &p.split),
@@ -469,7 +469,7 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   // g = X Wg^T and u = X Wu^T (the plain row-tile GEMM: N = d_ff, K = d). GEMMs
   // that contract over d take the row-tile height of GEMM 1 (bm_d, map mtile_d_rows).
   const moe::SplitK* sk = &p.split;
-  const int bm_d = moe::grouped_gemm_bm_gate_up(bf16, C);
+  const int bm_d = moe::grouped_gemm_bm_contract_d(bf16, C);
   int32_t* mtile_d_rows = p.mtile;
   if (bm_d != bm) {
     MOE_HIP_TRY(moe::launch_mtile_map(p.kept, E, bm_d, p.mtile_gu, s), "tile map");
@@ -647,7 +647,7 @@ int moe_layer_forward_replicated(const void* x, const void* W_router, const floa
   MOE_HIP_TRY(moe::launch_scatter_rows(x, inst, slot, T, k, C, d * eb, buckets, s), "scatter");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, false, s), "event");
-  const int bm_gu = moe::grouped_gemm_bm_gate_up(bf16, C);
+  const int bm_gu = moe::grouped_gemm_bm_gate_up(bf16, C, d);
   if (bm_gu != bm) MOE_HIP_TRY(moe::launch_mtile_map(kept, R, bm_gu, p.mtile_gu, s), "tile map (gate, up)");
   MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, bm_gu != bm ? p.mtile_gu : p.mtile, W_gate, W_up, R, C, d, d_ff,
                                        bf16, p.h, s, p.wmap, &p.split),
@@ -787,7 +787,7 @@ int moe_grouped_gemm(const void* buckets, const int32_t* kept_count, const void*
   auto* mtile_gu = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + map_bytes);
   const moe::SplitK sk = moe::split_k_carve(static_cast<char*>(workspace) + 2 * map_bytes);
   MOE_HIP_TRY(moe::launch_mtile_map(kept_count, E, moe::grouped_gemm_bm(bf16, C), mtile, s), "tile map");
-  MOE_HIP_TRY(moe::launch_mtile_map(kept_count, E, moe::grouped_gemm_bm_gate_up(bf16, C), mtile_gu, s), "tile map");
+  MOE_HIP_TRY(moe::launch_mtile_map(kept_count, E, moe::grouped_gemm_bm_gate_up(bf16, C, d), mtile_gu, s), "tile map");
   MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept_count, mtile_gu, W_gate, W_up, E, C, d, d_ff, bf16, h, s,
                                        nullptr, &sk),
               "grouped gemm (gate, up)");

@@ -88,6 +88,7 @@ SMALL = [
     dict(T=40, d=64, E=1, k=1, d_ff=64, cf=1.0),
     dict(T=500, d=64, E=4, k=1, d_ff=64, cf=0.1, bias="hot0"),
     dict(T=200, d=72, E=64, k=6, d_ff=40, cf=2.0),
+    dict(T=1200, d=256, E=32, k=8, d_ff=192, cf=1.0),   # C = 300: 320-row tiles in GEMM 1
     # rank-limited routing: each token's experts on at most max_ranks of the P ranks
     dict(T=300, d=256, E=32, k=4, d_ff=96, cf=1.0, P=8, max_ranks=2),
     dict(T=130, d=1024, E=64, k=6, d_ff=72, cf=1.25, P=8, max_ranks=1, bias="zipf1.2"),

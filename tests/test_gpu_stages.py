@@ -192,6 +192,9 @@ GEMM_CASES = [
     # 256 x 256 tiles with a last round split over K on a 256-CU part: whole
     # tiles plus split ones in GEMM 1 (GEMM 2 all split), and the reverse
     (4, 768, 256, 4352, "bf16"), (8, 768, 4096, 256, "bf16"),
+    # 256 < C <= 320: one 320-row tile per expert in GEMM 1 (row blocks of 32
+    # past kept skipped per wave), with 2-, 8- and 3-way splits of the last round
+    (6, 300, 256, 320, "bf16"), (4, 320, 1024, 256, "bf16"), (3, 257, 384, 192, "bf16"),
 ]
 
 
