@@ -108,9 +108,9 @@ __device__ inline bool tile_of_block(const int32_t* __restrict__ mtile_off, int 
 // Split-K of the last round. With G work-groups resident at once and L live
 // tiles, rem = L % G tiles would run alone in a last round. When G / rem >= 2
 // each of them is cut into s = min(G / rem, nk / 2, kMaxSplit) K ranges of
-// whole stage pairs, one block each (rem * s <= G blocks), after the L - rem
-// whole tiles. Block b then holds K stages [kb, ke) of split tile ti as its
-// chunk c of s; s = 1 means a whole tile.
+// whole stage pairs, one block each (rem * s <= G blocks), after the blocks of
+// the L - rem whole tiles. Block b then holds K stages [kb, ke) of split tile
+// ti as its chunk c of s; s = 1 means a whole tile.
 constexpr int kMaxSplit = 8;
 
 struct Work {
@@ -143,17 +143,20 @@ __device__ inline bool work_of_block(const int32_t* __restrict__ mtile_off, int 
   s = s < kMaxSplit ? s : kMaxSplit;
   if (s < 2) rem = 0, s = 1;
   const int64_t whole = live - rem;
+  // xcd_tile hands the whole tiles to the first ceil(whole / 8) * 8 blocks
+  // (some of them idle); the split blocks come after those
+  const int64_t whole_blocks = (whole + 7) / 8 * 8;
   int64_t lid;
   w->s = 1;
   w->c = 0;
   w->ti = 0;
   w->kb = 0;
   w->ke = nk;
-  if (blockIdx.x < whole) {
+  if (blockIdx.x < whole_blocks) {
     lid = xcd_tile(blockIdx.x, whole);
     if (lid < 0) return false;
   } else {
-    const int64_t u = blockIdx.x - whole;
+    const int64_t u = blockIdx.x - whole_blocks;
     if (u >= rem * s) return false;
     w->s = static_cast<int>(s);
     w->ti = static_cast<int>(u / s);

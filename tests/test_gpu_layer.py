@@ -88,7 +88,7 @@ SMALL = [
     dict(T=40, d=64, E=1, k=1, d_ff=64, cf=1.0),
     dict(T=500, d=64, E=4, k=1, d_ff=64, cf=0.1, bias="hot0"),
     dict(T=200, d=72, E=64, k=6, d_ff=40, cf=2.0),
-    dict(T=1200, d=256, E=32, k=8, d_ff=192, cf=1.0),   # C = 300: 320-row tiles in GEMM 1
+    dict(T=1200, d=256, E=32, k=8, d_ff=256, cf=1.0),   # C = 300: 320-row tiles in both GEMMs
     # rank-limited routing: each token's experts on at most max_ranks of the P ranks
     dict(T=300, d=256, E=32, k=4, d_ff=96, cf=1.0, P=8, max_ranks=2),
     dict(T=130, d=1024, E=64, k=6, d_ff=72, cf=1.25, P=8, max_ranks=1, bias="zipf1.2"),
@@ -139,6 +139,48 @@ def _sample_tokens(wl, ref_slot, n_rand, seed):
     return np.array(sorted(picks))
 
 
+def check_expert_gemms_full(wl, r, host, dev):
+    """The stage GEMMs at the workload's full size, on the layer's own buckets
+    and kept counts (so with the same tile lists and split rounds as the
+    layer): every kept row of h and y is written, no padding row is, and
+    sampled rows (first, last and one more of 8 experts) match the oracle."""
+    E, C, d, F = wl.E, r["C"], wl.d, wl.d_ff
+    kept_dev = r["kept_count"]
+    kept = kept_dev.cpu().numpy()
+    bf = wl.dtype == "bf16"
+
+    def sentinel(shape):
+        if bf:
+            return torch.full(shape, 0x1234, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        return torch.full(shape, 777.0, dtype=torch.float32, device="cuda")
+
+    h, y = sentinel((E, C, F)), sentinel((E, C, d))
+    ws_n = moe.moe_grouped_gemm_workspace_size(E, C)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    moe.moe_grouped_gemm(r["buckets"], kept_dev, *dev, E, C, d, F, wl.dtype, h, y, ws, ws_n)
+    torch.cuda.synchronize()
+    live = torch.arange(C, device="cuda")[None, :] < kept_dev[:, None].long()
+    for name, t in (("h", h), ("y", y)):
+        is_sent = (t.view(torch.int16) == 0x1234) if bf else (t == 777.0)
+        assert not is_sent.any(-1)[live].any().item(), f"{name}: a kept row left (partly) unwritten"
+        assert is_sent.all(-1)[~live].all().item(), f"{name}: a padding row written"
+    rng = np.random.default_rng(wl.seed + 5)
+    experts = set(rng.choice(E, size=min(7, E), replace=False).tolist()) | {int(np.argmax(kept))}
+    tol_h, tol_y = (4e-3, 1e-2) if bf else (1e-5, 1e-5)
+    for e in sorted(experts):
+        n = int(kept[e])
+        if n == 0:
+            continue
+        rows = sorted({0, n - 1, int(rng.integers(0, n))})
+        X = bits_to_f64(to_host(r["buckets"][e, rows], wl.dtype), wl.dtype)
+        wg, wu, wd = (oracle.decode(a[e], wl.dtype) for a in host)
+        got_h = bits_to_f64(to_host(h[e, rows], wl.dtype), wl.dtype)
+        got_y = bits_to_f64(to_host(y[e, rows], wl.dtype), wl.dtype)
+        assert row_rel_err(got_h, oracle.expert_hidden(X, wg, wu)).max() <= tol_h, f"h rows {rows} of expert {e}"
+        assert row_rel_err(got_y, oracle.expert_mlp(X, wg, wu, wd)).max() <= tol_y, f"y rows {rows} of expert {e}"
+    say(f"  expert GEMMs at full size: all {int(kept.sum())} kept rows written; rows of {len(experts)} experts match")
+
+
 WORKLOAD_SAMPLES = {"tiny_f32": None, "mixtral_prefill": 16, "deepseek_v3_prefill": 2,
                     "deepseek_v3_node_limited": 2, "deepseek_v3_decode": 6, "zipf_skew_drops": 16}
 
@@ -163,6 +205,7 @@ def test_named_workload(name):
     rng = np.random.default_rng(3)
     check_buckets(wl, r, ref, sorted(set(rng.choice(wl.E, size=min(8, wl.E), replace=False).tolist())))
     check_out(wl, r, ref)
+    check_expert_gemms_full(wl, r, host, dev)
     if wl.max_ranks:
         ranks = r["topk_idx"].cpu().numpy() // (wl.E // wl.P)
         assert max(len(set(row)) for row in ranks.tolist()) <= wl.max_ranks

@@ -192,9 +192,14 @@ GEMM_CASES = [
     # 256 x 256 tiles with a last round split over K on a 256-CU part: whole
     # tiles plus split ones in GEMM 1 (GEMM 2 all split), and the reverse
     (4, 768, 256, 4352, "bf16"), (8, 768, 4096, 256, "bf16"),
-    # 256 < C <= 320: one 320-row tile per expert in GEMM 1 (row blocks of 32
-    # past kept skipped per wave), with 2-, 8- and 3-way splits of the last round
+    # 256 < C <= 320: one 320-row tile per expert (row blocks of 32 past kept
+    # skipped per wave) in GEMM 1, and in GEMM 2 where d_ff % 128 == 0; 2-, 8-
+    # and 3-way splits of the last round, one stage pair (no split), N < 256
     (6, 300, 256, 320, "bf16"), (4, 320, 1024, 256, "bf16"), (3, 257, 384, 192, "bf16"),
+    (5, 290, 128, 384, "bf16"),
+    # more than 8 whole tiles, not a multiple of 8, no split (one stage pair):
+    # every XCD slot of the tile spread must still run
+    (3, 600, 128, 640, "bf16"),
 ]
 
 
