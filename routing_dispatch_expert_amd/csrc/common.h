@@ -97,6 +97,8 @@ int grouped_gemm_bm(bool bf16, int64_t C);
 // The same for GEMM 1 (gate/up, contraction length K = d), whose long K
 // favours taller tiles sooner.
 int grouped_gemm_bm_gate_up(bool bf16, int64_t C, int64_t K);
+// The same for GEMM 2 (down, K = d_ff) in the forward pass.
+int grouped_gemm_bm_down(bool bf16, int64_t C, int64_t K);
 // Row-tile height of the backward GEMMs that contract over d (the g and u
 // recompute, dh, dX): GEMM 1's choice without the 320-row tile.
 int grouped_gemm_bm_contract_d(bool bf16, int64_t C);

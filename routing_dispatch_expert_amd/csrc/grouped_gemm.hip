@@ -1180,6 +1180,14 @@ int grouped_gemm_bm_gate_up(bool bf16, int64_t C, int64_t K) {
   return grouped_gemm_bm_contract_d(bf16, C);
 }
 
+#ifndef MOE_TALL_DOWN
+#define MOE_TALL_DOWN 1
+#endif
+int grouped_gemm_bm_down(bool bf16, int64_t C, int64_t K) {
+  if (MOE_TALL_DOWN && bf16 && C > 256 && C <= 320 && K % 128 == 0) return 320;
+  return grouped_gemm_bm(bf16, C);
+}
+
 namespace {
 
 template <bool SWIGLU>
@@ -1361,6 +1369,8 @@ hipError_t launch_gemm_down(const void* h, const int32_t* kept, const int32_t* m
     const int tile = bm ? bm : grouped_gemm_bm(true, C);
     if (tile == kSkinnyRows && d_ff % 32 == 0)
       return launch_skinny<false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, wmap, s);
+    if (tile == 320)
+      return launch_bf16<320, 256, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, wmap, s, sk);
     if (tile == 256)
       return launch_bf16<256, 256, false>(h, wd, nullptr, y, kept, mtile_off, E, C, d_ff, d, wmap, s, sk);
     if (d_ff % 64 == 0)

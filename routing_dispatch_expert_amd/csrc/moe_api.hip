@@ -370,7 +370,7 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
   const bool bf16 = dtype == MOE_DTYPE_BF16;
   auto s = static_cast<hipStream_t>(stream);
   const int64_t nt = moe::ceil_div(T, moe::kTileTokens);
-  const int bm = moe::grouped_gemm_bm(bf16, C);
+  const int bm = moe::grouped_gemm_bm_down(bf16, C, d_ff);
 
   const int splits = moe::router_splits(T, d, E, bf16);
   const bool fused_hist = moe::route_builds_histogram(k);
@@ -400,7 +400,7 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
               "grouped gemm (gate, up)");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, false, s), "event");
-  MOE_HIP_TRY(moe::launch_gemm_down(p.h, kept, p.mtile, W_down, E, C, d, d_ff, bf16, p.y, s, nullptr, &p.split),
+  MOE_HIP_TRY(moe::launch_gemm_down(p.h, kept, p.mtile, W_down, E, C, d, d_ff, bf16, p.y, s, nullptr, &p.split, bm),
               "grouped gemm (down)");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_COMBINE, false, s), "event");
@@ -614,7 +614,7 @@ int moe_layer_forward_replicated(const void* x, const void* W_router, const floa
   const bool bf16 = dtype == MOE_DTYPE_BF16;
   auto s = static_cast<hipStream_t>(stream);
   const int64_t nt = moe::ceil_div(T, moe::kTileTokens);
-  const int bm = moe::grouped_gemm_bm(bf16, C);
+  const int bm = moe::grouped_gemm_bm_down(bf16, C, d_ff);
   const int64_t no_cap = T * k;  // a capacity nothing exceeds
 
   // routing, then each copy's token-order rank among its expert's copies
@@ -654,7 +654,7 @@ int moe_layer_forward_replicated(const void* x, const void* W_router, const floa
               "grouped gemm (gate, up)");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, false, s), "event");
-  MOE_HIP_TRY(moe::launch_gemm_down(p.h, kept, p.mtile, W_down, R, C, d, d_ff, bf16, p.y, s, p.wmap, &p.split),
+  MOE_HIP_TRY(moe::launch_gemm_down(p.h, kept, p.mtile, W_down, R, C, d, d_ff, bf16, p.y, s, p.wmap, &p.split, bm),
               "grouped gemm (down)");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_COMBINE, false, s), "event");
@@ -786,12 +786,13 @@ int moe_grouped_gemm(const void* buckets, const int32_t* kept_count, const void*
   auto* mtile = static_cast<int32_t*>(workspace);
   auto* mtile_gu = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + map_bytes);
   const moe::SplitK sk = moe::split_k_carve(static_cast<char*>(workspace) + 2 * map_bytes);
-  MOE_HIP_TRY(moe::launch_mtile_map(kept_count, E, moe::grouped_gemm_bm(bf16, C), mtile, s), "tile map");
+  const int bm = moe::grouped_gemm_bm_down(bf16, C, d_ff);
+  MOE_HIP_TRY(moe::launch_mtile_map(kept_count, E, bm, mtile, s), "tile map");
   MOE_HIP_TRY(moe::launch_mtile_map(kept_count, E, moe::grouped_gemm_bm_gate_up(bf16, C, d), mtile_gu, s), "tile map");
   MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept_count, mtile_gu, W_gate, W_up, E, C, d, d_ff, bf16, h, s,
                                        nullptr, &sk),
               "grouped gemm (gate, up)");
-  MOE_HIP_TRY(moe::launch_gemm_down(h, kept_count, mtile, W_down, E, C, d, d_ff, bf16, y, s, nullptr, &sk),
+  MOE_HIP_TRY(moe::launch_gemm_down(h, kept_count, mtile, W_down, E, C, d, d_ff, bf16, y, s, nullptr, &sk, bm),
               "grouped gemm (down)");
   return MOE_OK;
 }
