@@ -99,9 +99,6 @@ int grouped_gemm_bm(bool bf16, int64_t C);
 int grouped_gemm_bm_gate_up(bool bf16, int64_t C, int64_t K);
 // The same for GEMM 2 (down, K = d_ff) in the forward pass.
 int grouped_gemm_bm_down(bool bf16, int64_t C, int64_t K);
-// Row-tile height of the backward GEMMs that contract over d (the g and u
-// recompute, dh, dX): GEMM 1's choice without the 320-row tile.
-int grouped_gemm_bm_contract_d(bool bf16, int64_t C);
 // Scratch that lets the 256-column LDS-DMA GEMM split the tiles of its last,
 // partly filled round over K: fp32 partial tiles (up to 320 x 256) of up to
 // kSplitUnits work-groups and one arrival counter per split tile (cleared by
@@ -143,11 +140,11 @@ hipError_t launch_gemm_tn(const void* a, int64_t lda, int64_t a_es, int64_t aoff
                           const int32_t* kk, int E, int64_t M, int64_t N, void* out, hipStream_t s);
 // out = A [B0; B1] on rows < kept with B K-major: B0 [E][K0][N] holds K rows
 // 0 .. K0 - 1 and B1 [E][K - K0][N] the rest (NULL when K0 == K). bf16,
-// 256-row tiles (mtile_off built for 256); needs K % 128 == 0, K0 % 64 == 0
-// and N % 8 == 0, else hipErrorInvalidValue.
+// bm-row tiles, bm 256 or 320 (mtile_off built for bm); needs K % 128 == 0,
+// K0 % 64 == 0 and N % 8 == 0, else hipErrorInvalidValue.
 hipError_t launch_gemm_kmajor_b(const void* a, const int32_t* kept, const int32_t* mtile_off, const void* b0,
                                 const void* b1, int64_t K0, int E, int64_t C, int64_t K, int64_t N, void* out,
-                                hipStream_t s, const SplitK* sk = nullptr);
+                                hipStream_t s, const SplitK* sk = nullptr, int bm = 256);
 
 // ---- backward (backward.hip) ----
 // dst[b][c][col_off + r] = src[b][r][c] for r < valid[b] (or R), 0 for r < Rp.

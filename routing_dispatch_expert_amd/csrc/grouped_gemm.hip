@@ -487,7 +487,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   static_assert(!(F32OUT && (SWIGLU || BT)), "fp32 output serves the plain GEMM only");
   static_assert(!AT || (BT && !F32OUT), "a K-major A comes with a K-major B");
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
-  static_assert(TM_ == 4 || (TM_ == 5 && NW == 8 && !BT && !AT && !F32OUT), "320-row blocks: 8 waves, row-major");
+  static_assert(TM_ == 4 || (TM_ == 5 && NW == 8 && !AT && !F32OUT), "320-row blocks: 8 waves, row-major A");
   // NW = 4: one wave per SIMD, 2 x 2 waves of 128 x 128. NW = 8: two waves per
   // SIMD, 2 x 4 waves of (32 TM) x 64, so one wave's matrix work covers the
   // other's barrier and DMA waits. TM = 5 makes the block 320 rows tall.
@@ -1162,29 +1162,20 @@ int grouped_gemm_bm(bool bf16, int64_t C) {
 
 // GEMM 1 reads each weight tile once per row tile: from 256 rows of capacity
 // on, one 256-row tile per expert (its padding rows cost no matrix work and no
-// loads) beats two 128-row tiles that each stream the weights.
-int grouped_gemm_bm_contract_d(bool bf16, int64_t C) {
+// loads) beats two 128-row tiles that each stream the weights. With
+// 256 < C <= 320 a 256-row tile would leave most experts a second, nearly
+// empty tile that streams the same weights again; one 320-row tile covers
+// every expert (needs K % 128 == 0, as the 256-row tile does).
+int grouped_gemm_bm_gate_up(bool bf16, int64_t C, int64_t K) {
   if (!bf16) return 64;
   if (C <= kSkinnyMaxC) return kSkinnyRows;
+  if (C > 256 && C <= 320 && K % 128 == 0) return 320;
   return C >= kBigTileMinCGateUp ? 256 : 128;
 }
 
-// With 256 < C <= 320 a 256-row tile would leave most experts a second, nearly
-// empty tile that streams the same weights again; one 320-row tile covers
-// every expert (needs K % 128 == 0, as the 256-row tile does).
-#ifndef MOE_TALL_TILE
-#define MOE_TALL_TILE 1
-#endif
-int grouped_gemm_bm_gate_up(bool bf16, int64_t C, int64_t K) {
-  if (MOE_TALL_TILE && bf16 && C > 256 && C <= 320 && K % 128 == 0) return 320;
-  return grouped_gemm_bm_contract_d(bf16, C);
-}
-
-#ifndef MOE_TALL_DOWN
-#define MOE_TALL_DOWN 1
-#endif
+// GEMM 2 in the forward pass: the same 320-row tile where it applies.
 int grouped_gemm_bm_down(bool bf16, int64_t C, int64_t K) {
-  if (MOE_TALL_DOWN && bf16 && C > 256 && C <= 320 && K % 128 == 0) return 320;
+  if (bf16 && C > 256 && C <= 320 && K % 128 == 0) return 320;
   return grouped_gemm_bm(bf16, C);
 }
 
@@ -1317,10 +1308,11 @@ hipError_t launch_gemm_tn(const void* a, int64_t lda, int64_t a_es, int64_t aoff
 
 hipError_t launch_gemm_kmajor_b(const void* a, const int32_t* kept, const int32_t* mtile_off, const void* b0,
                                 const void* b1, int64_t K0, int E, int64_t C, int64_t K, int64_t N, void* out,
-                                hipStream_t s, const SplitK* sk) {
+                                hipStream_t s, const SplitK* sk, int bm) {
   if (E * C == 0) return hipSuccess;
-  if (K % 128 || K0 % 64 || K0 <= 0 || K0 > K || (K0 < K && !b1) || N % 8) return hipErrorInvalidValue;
-  const int64_t mt_max = E * ceil_div(C, 256);
+  if (K % 128 || K0 % 64 || K0 <= 0 || K0 > K || (K0 < K && !b1) || N % 8 || (bm != 256 && bm != 320))
+    return hipErrorInvalidValue;
+  const int64_t mt_max = E * ceil_div(C, bm);
   const int64_t nt = ceil_div(N, 256);
   int64_t blocks = ceil_div(mt_max * nt, 8) * 8;
   const int G = sk ? resident_groups() : 0;
@@ -1329,11 +1321,19 @@ hipError_t launch_gemm_kmajor_b(const void* a, const int32_t* kept, const int32_
     if (err != hipSuccess) return err;
     blocks += G;
   }
-  gemm_bf16_dma_kernel<false, true, false, false, kKmajorWaves>
-      <<<dim3(static_cast<unsigned>(blocks)), dim3(kKmajorWaves * 64), 0, s>>>(
-      static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b0), static_cast<const bf16_t*>(b1),
-      static_cast<bf16_t*>(out), kept, mtile_off, E, C, K, N, static_cast<int>(nt), nullptr,
-      G > 0 ? sk->part : nullptr, G > 0 ? sk->tick : nullptr, G, K0);
+  const auto* pa = static_cast<const bf16_t*>(a);
+  const auto* pb0 = static_cast<const bf16_t*>(b0);
+  const auto* pb1 = static_cast<const bf16_t*>(b1);
+  auto* po = static_cast<bf16_t*>(out);
+  float* part = G > 0 ? sk->part : nullptr;
+  int32_t* tick = G > 0 ? sk->tick : nullptr;
+  if (bm == 320)
+    gemm_bf16_dma_kernel<false, true, false, false, 8, 5><<<dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s>>>(
+        pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), nullptr, part, tick, G, K0);
+  else
+    gemm_bf16_dma_kernel<false, true, false, false, kKmajorWaves>
+        <<<dim3(static_cast<unsigned>(blocks)), dim3(kKmajorWaves * 64), 0, s>>>(
+        pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), nullptr, part, tick, G, K0);
   return hipGetLastError();
 }
 

@@ -178,7 +178,8 @@ LayerPlan plan_layer(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E, in
 // read the weights K-major where the 256-row LDS-DMA kernel can: then no
 // transposed weight copies are made.
 bool backward_kmajor(bool bf16, int64_t C, int64_t d, int64_t F) {
-  return bf16 && moe::grouped_gemm_bm_contract_d(bf16, C) == 256 && d % 128 == 0 && F % 64 == 0;
+  const int bm = moe::grouped_gemm_bm_gate_up(bf16, C, d);
+  return bf16 && (bm == 256 || bm == 320) && d % 128 == 0 && F % 64 == 0;
 }
 
 struct BackPlan {
@@ -469,7 +470,7 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   // g = X Wg^T and u = X Wu^T (the plain row-tile GEMM: N = d_ff, K = d). GEMMs
   // that contract over d take the row-tile height of GEMM 1 (bm_d, map mtile_d_rows).
   const moe::SplitK* sk = &p.split;
-  const int bm_d = moe::grouped_gemm_bm_contract_d(bf16, C);
+  const int bm_d = moe::grouped_gemm_bm_gate_up(bf16, C, d);
   int32_t* mtile_d_rows = p.mtile;
   if (bm_d != bm) {
     MOE_HIP_TRY(moe::launch_mtile_map(p.kept, E, bm_d, p.mtile_gu, s), "tile map");
@@ -490,11 +491,13 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   // 3. dh = dy Wd; dg, du. 4. dX = [dg | du] [Wg ; Wu]. Either straight from the
   //    weights (K-major B: Wd is [d][d_ff] = [K][N], Wg and Wu are [d_ff][d]),
   //    or through transposed copies (B = Wd^T [E][d_ff][d], [Wg^T | Wu^T] [E][d][2 d_ff]).
-  if (backward_kmajor(bf16, C, d, F)) {  // then bm_d == 256 and mtile_d_rows is its map
-    MOE_HIP_TRY(moe::launch_gemm_kmajor_b(b.dy, p.kept, mtile_d_rows, W_down, nullptr, d, E, C, d, F, b.dh, s, sk),
+  if (backward_kmajor(bf16, C, d, F)) {  // then bm_d is 256 or 320 and mtile_d_rows is its map
+    MOE_HIP_TRY(moe::launch_gemm_kmajor_b(b.dy, p.kept, mtile_d_rows, W_down, nullptr, d, E, C, d, F, b.dh, s, sk,
+                                          bm_d),
                 "gemm dh");
     MOE_HIP_TRY(moe::launch_swiglu_bwd(b.dh, b.g, b.u, b.dgu, p.kept, E, C, F, bf16, s), "swiglu backward");
-    MOE_HIP_TRY(moe::launch_gemm_kmajor_b(b.dgu, p.kept, mtile_d_rows, W_gate, W_up, F, E, C, 2 * F, d, b.dX, s, sk),
+    MOE_HIP_TRY(moe::launch_gemm_kmajor_b(b.dgu, p.kept, mtile_d_rows, W_gate, W_up, F, E, C, 2 * F, d, b.dX, s, sk,
+                                          bm_d),
                 "gemm dX");
   } else {
     MOE_HIP_TRY(moe::launch_transpose(W_down, b.WdT, E, d, F, F, d, 0, d, nullptr, d * F, F * d, bf16, s),
