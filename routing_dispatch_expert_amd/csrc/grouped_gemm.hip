@@ -17,6 +17,7 @@
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 
@@ -184,6 +185,21 @@ __device__ inline uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 
 // Scheduling hints: instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
+
+// One k-step's schedule: NR groups, each one LDS read and its share of the NM
+// matrix instructions (shares differ by at most one), the read first or last.
+template <int C, bool READS_FIRST>
+__device__ inline void interleave_group() {
+  if constexpr (READS_FIRST) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  if constexpr (C > 0) __builtin_amdgcn_sched_group_barrier(kSchedMfma, C, 0);
+  if constexpr (!READS_FIRST) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+}
+
+template <int NM, int NR, bool READS_FIRST, int... G>
+__device__ inline void interleave_groups(std::integer_sequence<int, G...>) {
+  (interleave_group<(NM * (G + 1)) / NR - (NM * G) / NR, READS_FIRST>(), ...);
+}
+
 
 // Epilogue of one wave's (32 TM) x (32 TN) accumulator block (v_mfma 32x32
 // layout: element q of lane l is row 8 (q / 4) + 4 (l / 32) + q % 4, column
@@ -671,28 +687,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
     };
     // interleave the next fragments' LDS reads with this step's matrix work
-    auto interleave = [&](bool reads_first) {
-      if constexpr (TA == TM) {
-#pragma unroll
-        for (int g = 0; g < NFRAG; ++g) {
-          if (reads_first) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMFMA / NFRAG, 0);
-          if (!reads_first) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-        }
-      }
+    auto interleave = [&](auto reads_first) {
+      if constexpr (TA == TM)
+        interleave_groups<NMFMA, NFRAG, decltype(reads_first)::value>(std::make_integer_sequence<int, NFRAG>{});
     };
     // Stage k in (as, bs); stage k + 1 goes to (an, bn_) unless this is the last.
     auto stage = [&](auto has_next, const uint4* as, const uint4* bs, uint4* an, uint4* bn_, int64_t k) {
       if constexpr (decltype(has_next)::value) dma(an, bn_, k + 1);
       fload(as, bs, 1, 1);
       mfmas(0);
-      interleave(false);
+      interleave(std::false_type{});
       fload(as, bs, 2, 0);
       mfmas(1);
-      interleave(false);
+      interleave(std::false_type{});
       fload(as, bs, 3, 1);
       mfmas(0);
-      interleave(false);
+      interleave(std::false_type{});
       if constexpr (decltype(has_next)::value) {
         __builtin_amdgcn_sched_barrier(0);
         wait_vm_lgkm0<0>();            // own DMA of stage k + 1 landed, reads of stage k done ...
@@ -701,7 +711,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         fload(an, bn_, 0, 0);
       }
       mfmas(1);
-      interleave(true);
+      interleave(std::true_type{});
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
