@@ -94,11 +94,12 @@ hipError_t launch_scatter_rows(const void* x, const int32_t* idx, const int32_t*
 // Row-tile height the grouped GEMM uses for these sizes (the mtile map must
 // be built for the same value).
 int grouped_gemm_bm(bool bf16, int64_t C);
-// The same for GEMM 1 (gate/up, contraction length K = d), whose long K
-// favours taller tiles sooner.
+// The same for GEMM 1 (gate/up, contraction length K = d) and GEMM 2 (down,
+// K = d_ff) in the forward pass, and for the backward GEMMs that contract
+// over d.
 int grouped_gemm_bm_gate_up(bool bf16, int64_t C, int64_t K);
-// The same for GEMM 2 (down, K = d_ff) in the forward pass.
 int grouped_gemm_bm_down(bool bf16, int64_t C, int64_t K);
+int grouped_gemm_bm_contract_d(bool bf16, int64_t C, int64_t K);
 // Scratch that lets the 256-column LDS-DMA GEMM split the tiles of its last,
 // partly filled round over K: fp32 partial tiles (up to 320 x 256) of up to
 // kSplitUnits work-groups and one arrival counter per split tile (cleared by

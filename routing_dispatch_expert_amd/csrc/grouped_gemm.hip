@@ -1181,22 +1181,35 @@ int grouped_gemm_bm(bool bf16, int64_t C) {
   return C >= kBigTileMinC ? 256 : 128;
 }
 
-// GEMM 1 reads each weight tile once per row tile: from 256 rows of capacity
-// on, one 256-row tile per expert (its padding rows cost no matrix work and no
-// loads) beats two 128-row tiles that each stream the weights. With
-// 256 < C <= 320 a 256-row tile would leave most experts a second, nearly
-// empty tile that streams the same weights again; one 320-row tile covers
-// every expert (needs K % 128 == 0, as the 256-row tile does).
-int grouped_gemm_bm_gate_up(bool bf16, int64_t C, int64_t K) {
+// The backward GEMMs that contract over d (g and u recomputed, dh, dX). Each
+// weight tile streams once per row tile: from 256 rows of capacity on, one
+// 256-row tile per expert (its padding rows cost no matrix work and no loads)
+// beats two 128-row tiles that each stream the weights. With 256 < C <= 320 a
+// 256-row tile would leave most experts a second, nearly empty tile that
+// streams the same weights again; one 320-row tile covers every expert (needs
+// K % 128 == 0, as the 256-row tile does).
+int grouped_gemm_bm_contract_d(bool bf16, int64_t C, int64_t K) {
   if (!bf16) return 64;
   if (C <= kSkinnyMaxC) return kSkinnyRows;
   if (C > 256 && C <= 320 && K % 128 == 0) return 320;
   return C >= kBigTileMinCGateUp ? 256 : 128;
 }
 
-// GEMM 2 in the forward pass: the same 320-row tile where it applies.
+// GEMM 1 in the forward pass takes 320-row tiles for every C > 256 (K % 128
+// == 0): at Mixtral's 1280 four of them fit exactly, and the nearly empty
+// fifth 256-row tile of an expert just over 1024 rows is gone (gate/up
+// 1.77 -> 1.72 ms; the skewed workload's 0.416 -> 0.403 ms).
+int grouped_gemm_bm_gate_up(bool bf16, int64_t C, int64_t K) {
+  if (bf16 && C > 256 && K % 128 == 0) return 320;
+  return grouped_gemm_bm_contract_d(bf16, C, K);
+}
+
+// GEMM 2 in the forward pass: 320-row tiles for 256 < C <= 320 as above, and
+// for larger C when K >= 4096 (Mixtral's down GEMM 1.05 -> 0.89 ms: 512
+// tiles, two whole rounds, instead of 576). With short K they lost (the
+// skewed workload's K = 1408: 0.227 -> 0.361 ms).
 int grouped_gemm_bm_down(bool bf16, int64_t C, int64_t K) {
-  if (bf16 && C > 256 && C <= 320 && K % 128 == 0) return 320;
+  if (bf16 && C > 256 && K % 128 == 0 && (C <= 320 || K >= 4096)) return 320;
   return grouped_gemm_bm(bf16, C);
 }
 

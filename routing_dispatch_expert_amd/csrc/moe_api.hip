@@ -178,7 +178,7 @@ LayerPlan plan_layer(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E, in
 // read the weights K-major where the 256-row LDS-DMA kernel can: then no
 // transposed weight copies are made.
 bool backward_kmajor(bool bf16, int64_t C, int64_t d, int64_t F) {
-  const int bm = moe::grouped_gemm_bm_gate_up(bf16, C, d);
+  const int bm = moe::grouped_gemm_bm_contract_d(bf16, C, d);
   return bf16 && (bm == 256 || bm == 320) && d % 128 == 0 && F % 64 == 0;
 }
 
@@ -470,7 +470,7 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   // g = X Wg^T and u = X Wu^T (the plain row-tile GEMM: N = d_ff, K = d). GEMMs
   // that contract over d take the row-tile height of GEMM 1 (bm_d, map mtile_d_rows).
   const moe::SplitK* sk = &p.split;
-  const int bm_d = moe::grouped_gemm_bm_gate_up(bf16, C, d);
+  const int bm_d = moe::grouped_gemm_bm_contract_d(bf16, C, d);
   int32_t* mtile_d_rows = p.mtile;
   if (bm_d != bm) {
     MOE_HIP_TRY(moe::launch_mtile_map(p.kept, E, bm_d, p.mtile_gu, s), "tile map");
