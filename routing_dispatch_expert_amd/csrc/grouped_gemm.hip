@@ -1197,14 +1197,11 @@ int grouped_gemm_bm_contract_d(bool bf16, int64_t C, int64_t K) {
   return C >= kBigTileMinCGateUp ? 256 : 128;
 }
 
-// GEMM 1 in the forward pass takes 320-row tiles for every C > 256 (K % 128
-// == 0): at Mixtral's 1280 four of them fit exactly, and the nearly empty
-// fifth 256-row tile of an expert just over 1024 rows is gone (gate/up
-// 1.77 -> 1.72 ms; the skewed workload's 0.416 -> 0.403 ms).
-int grouped_gemm_bm_gate_up(bool bf16, int64_t C, int64_t K) {
-  if (bf16 && C > 256 && K % 128 == 0) return 320;
-  return grouped_gemm_bm_contract_d(bf16, C, K);
-}
+// GEMM 1 in the forward pass: the same rule. At Mixtral's C = 1280 four
+// 320-row tiles fit exactly, and the nearly empty fifth 256-row tile of an
+// expert just over 1024 rows is gone (gate/up 1.77 -> 1.72 ms). At K = 2048
+// the skewed workload gained 3% from them but its replicated layout lost 15%.
+int grouped_gemm_bm_gate_up(bool bf16, int64_t C, int64_t K) { return grouped_gemm_bm_contract_d(bf16, C, K); }
 
 // GEMM 2 in the forward pass: 320-row tiles for 256 < C <= 320 as above, and
 // for larger C when K >= 4096 (Mixtral's down GEMM 1.05 -> 0.89 ms: 512
