@@ -400,16 +400,112 @@ __global__ __launch_bounds__(256) void router_wgrad_wide_kernel(const void* __re
     for (int e = tid; e < E; e += 256) dbpart[static_cast<int64_t>(blockIdx.z) * E + e] = dbs[e];
 }
 
+// Per expert, its routed copies in token order (lists from the slots pass):
+// block (x, e, z) takes copies [cc z, cc z + cc) of expert e, 8 columns per
+// lane (2048 per block, d % 8 == 0), and writes its fp32 partial sum of
+// dl * x in copy order, plus (x == 0) the sum of dl, as partial row
+// route_off[e] / cc + e + z. Those rows never overlap between experts (an
+// expert with r copies has ceil(r / cc) chunks, at most one more than the
+// whole chunks its copies span), so floor(T k / cc) + E + 1 rows suffice.
+// Blocks past an expert's copies write nothing; the sum kernel reads only the
+// chunks that exist.
+__device__ inline int64_t wgrad_chunk_row(const int32_t* route_off, int e, int cc) {
+  return static_cast<int64_t>(route_off[e]) / cc + e;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void router_wgrad_gather_kernel(
+    const void* __restrict__ x, const int32_t* __restrict__ lcopy, const int32_t* __restrict__ ltok,
+    const int32_t* __restrict__ route_off, const int32_t* __restrict__ routed, const float* __restrict__ dl,
+    int cc, int64_t d, float* __restrict__ part, float* __restrict__ dbpart) {
+  const int e = blockIdx.y, z = blockIdx.z;
+  const int n = __builtin_amdgcn_readfirstlane(routed[e]);
+  const int r0 = z * cc;
+  if (r0 >= n) return;
+  const int r1 = min(n, r0 + cc);
+  const int64_t off = __builtin_amdgcn_readfirstlane(route_off[e]);
+  const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+  const bool live = c0 < d;
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  float dbs = 0.f;
+  constexpr int U = 8;  // copies whose loads are in flight together
+  for (int r = r0; r < r1; r += U) {
+    float cf[U], xv[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = r + u < r1;  // uniform
+      const int ci = ok ? __builtin_amdgcn_readfirstlane(lcopy[off + r + u]) : 0;
+      const int64_t t = ok ? __builtin_amdgcn_readfirstlane(ltok[off + r + u]) : 0;
+      cf[u] = ok ? dl[ci] : 0.f;
+      if (ok && live) {
+        if constexpr (BF16) {
+          const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(x) + t * d + c0);
+          const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            xv[u][2 * q] = __uint_as_float(ww[q] << 16);
+            xv[u][2 * q + 1] = __uint_as_float(ww[q] & 0xffff0000u);
+          }
+        } else {
+          const float4* px = reinterpret_cast<const float4*>(static_cast<const float*>(x) + t * d + c0);
+          const float4 a = px[0], b = px[1];
+          xv[u][0] = a.x, xv[u][1] = a.y, xv[u][2] = a.z, xv[u][3] = a.w;
+          xv[u][4] = b.x, xv[u][5] = b.y, xv[u][6] = b.z, xv[u][7] = b.w;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) xv[u][q] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (r + u >= r1) break;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = fmaf(cf[u], xv[u][q], acc[q]);
+      dbs += cf[u];
+    }
+  }
+  const int64_t row = wgrad_chunk_row(route_off, e, cc) + z;
+  float* pz = part + row * d;
+  if (live) {
+    reinterpret_cast<float4*>(pz + c0)[0] = float4{acc[0], acc[1], acc[2], acc[3]};
+    reinterpret_cast<float4*>(pz + c0)[1] = float4{acc[4], acc[5], acc[6], acc[7]};
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) dbpart[row] = dbs;
+}
+
+// Sums the chunk partials in chunk order: partial z of (e, i) at
+// part[z][e][i] (nchunk chunks), or with routed (the gather layout, chunks of
+// cc copies) at row route_off[e] / cc + e + z, ceil(routed[e] / cc) of them.
 template <bool BF16>
 __global__ __launch_bounds__(256) void router_wgrad_sum_kernel(const float* __restrict__ part,
                                                                const float* __restrict__ dbpart, int nchunk, int E,
                                                                int64_t d, void* __restrict__ dwr,
-                                                               float* __restrict__ db) {
+                                                               float* __restrict__ db,
+                                                               const int32_t* __restrict__ routed,
+                                                               const int32_t* __restrict__ route_off, int cc) {
   const int64_t n = static_cast<int64_t>(E) * d;
+  // (first row, row stride, count) of the partials of expert e, in rows of d (or 1 for db)
+  auto at = [&](int e, int64_t width, int64_t& first, int64_t& stride) {
+    if (routed) {
+      first = wgrad_chunk_row(route_off, e, cc) * width;
+      stride = width;
+      return (routed[e] + cc - 1) / cc;
+    }
+    first = static_cast<int64_t>(e) * width;
+    stride = static_cast<int64_t>(E) * width;
+    return nchunk;
+  };
   for (int64_t o = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; o < n;
        o += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     float s = 0.f;
-    for (int z = 0; z < nchunk; ++z) s += part[static_cast<int64_t>(z) * n + o];  // chunk order
+    const int e = static_cast<int>(o / d);
+    int64_t first, stride;
+    const int nz = at(e, d, first, stride);
+    const int64_t i = o - static_cast<int64_t>(e) * d;
+    for (int z = 0; z < nz; ++z) s += part[first + z * stride + i];  // chunk order
     if (BF16)
       static_cast<bf16_t*>(dwr)[o] = f32_to_bf16(s);
     else
@@ -418,7 +514,9 @@ __global__ __launch_bounds__(256) void router_wgrad_sum_kernel(const float* __re
   if (db && blockIdx.x == 0)
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
       float s = 0.f;
-      for (int z = 0; z < nchunk; ++z) s += dbpart[static_cast<int64_t>(z) * E + e];
+      int64_t first, stride;
+      const int nz = at(e, 1, first, stride);
+      for (int z = 0; z < nz; ++z) s += dbpart[first + z * stride];
       db[e] = s;
     }
 }
@@ -537,6 +635,27 @@ hipError_t launch_gather_dx(const void* dout, const void* dX, const void* wr, co
   return hipGetLastError();
 }
 
+namespace {
+bool wgrad_gather(int E, int64_t d) { return E >= kWgradWideMinE && d % 8 == 0; }
+
+// Copies per chunk of the gather kernel: a power of two in [64, 512] that
+// makes about 1024 or more chunk blocks of 2048 columns.
+int wgrad_copy_chunk(int64_t T, int k, int64_t d) {
+  const int64_t want = T * k * ceil_div(d, 2048) / 1024;
+  int cc = 64;
+  while (cc < 512 && cc * 2 <= want) cc *= 2;
+  return cc;
+}
+}  // namespace
+
+size_t router_wgrad_scratch_floats(int64_t T, int k, int E, int64_t d) {
+  if (wgrad_gather(E, d)) {
+    const int64_t rows = T * k / wgrad_copy_chunk(T, k, d) + E + 1;
+    return static_cast<size_t>(rows) * (d + 1);
+  }
+  return static_cast<size_t>(router_wgrad_chunks(T, E, d)) * E * (d + 1);
+}
+
 int router_wgrad_chunks(int64_t T, int E, int64_t d) {
   // wide kernel: about 2048 blocks of 64 columns; else about 8192 blocks of
   // 16 experts x 256 columns; chunks of at least 64 tokens
@@ -547,11 +666,27 @@ int router_wgrad_chunks(int64_t T, int E, int64_t d) {
 }
 
 hipError_t launch_router_wgrad(const void* x, const int32_t* idx, const float* dl, int64_t T, int k, int E,
-                               int64_t d, bool bf16, float* part, void* dwr, float* db, hipStream_t s) {
-  const int nz = router_wgrad_chunks(T, E, d);
+                               int64_t d, bool bf16, float* part, void* dwr, float* db, hipStream_t s,
+                               const int32_t* routed, const int32_t* route_off, const int32_t* lcopy,
+                               const int32_t* ltok) {
+  const bool gather = wgrad_gather(E, d);
+  if (gather && !(routed && route_off && lcopy && ltok)) return hipErrorInvalidValue;
+  const int cc = gather ? wgrad_copy_chunk(T, k, d) : 0;
+  // gather: chunk rows (T k / cc + E + 1) of d partials, then as many db partials
+  const int nz = gather ? static_cast<int>(ceil_div(T, cc)) : router_wgrad_chunks(T, E, d);
   const int64_t tchunk = ceil_div(T, nz);
-  float* dbpart = part + static_cast<int64_t>(nz) * E * d;
-  if (E >= kWgradWideMinE && E <= kWgradWideMaxE) {
+  float* dbpart = part + (gather ? (T * k / cc + E + 1) * d : static_cast<int64_t>(nz) * E * d);
+  if (gather) {
+    if (T > 0) {
+      const dim3 grid(static_cast<unsigned>(ceil_div(d, 2048)), static_cast<unsigned>(E), static_cast<unsigned>(nz));
+      if (bf16)
+        router_wgrad_gather_kernel<true><<<grid, dim3(256), 0, s>>>(x, lcopy, ltok, route_off, routed, dl, cc, d,
+                                                                    part, dbpart);
+      else
+        router_wgrad_gather_kernel<false><<<grid, dim3(256), 0, s>>>(x, lcopy, ltok, route_off, routed, dl, cc, d,
+                                                                     part, dbpart);
+    }
+  } else if (E >= kWgradWideMinE && E <= kWgradWideMaxE) {
     const dim3 grid(static_cast<unsigned>(ceil_div(d, 64)), 1, static_cast<unsigned>(nz));
     const size_t lds = static_cast<size_t>(E) * 65 * sizeof(float);
     if (bf16)
@@ -569,10 +704,12 @@ hipError_t launch_router_wgrad(const void* x, const int32_t* idx, const float* d
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const unsigned g2 = static_cast<unsigned>(std::min<int64_t>(ceil_div(static_cast<int64_t>(E) * d, 256), 4096));
+  const int32_t* rt = gather ? routed : nullptr;
   if (bf16)
-    router_wgrad_sum_kernel<true><<<dim3(g2), dim3(256), 0, s>>>(part, dbpart, nz, E, d, dwr, db);
+    router_wgrad_sum_kernel<true><<<dim3(g2), dim3(256), 0, s>>>(part, dbpart, nz, E, d, dwr, db, rt, route_off, cc);
   else
-    router_wgrad_sum_kernel<false><<<dim3(g2), dim3(256), 0, s>>>(part, dbpart, nz, E, d, dwr, db);
+    router_wgrad_sum_kernel<false><<<dim3(g2), dim3(256), 0, s>>>(part, dbpart, nz, E, d, dwr, db, rt, route_off,
+                                                                  cc);
   return hipGetLastError();
 }
 

@@ -85,8 +85,14 @@ hipError_t launch_replica_layout(const int32_t* replicas, int E, int R, int P, i
 hipError_t launch_instances(const int32_t* idx, const int32_t* qrank, const int32_t* replicas,
                             const int32_t* inst_off, int64_t n, int R, int32_t* inst, hipStream_t s);
 hipError_t launch_mtile_map(const int32_t* kept, int E, int bm, int32_t* mtile_off, hipStream_t s);
+// With route_off ([E + 1], the exclusive scan of the routed counts), lcopy and
+// ltok ([T * k]) list every routed copy per expert in token order: entry
+// route_off[e] + r is copy r of expert e (flat index t * k + j, and t).
 hipError_t launch_slots(const int32_t* idx, const int32_t* tile_off, int64_t T, int k, int E,
-                        int64_t C, int32_t* slot, int32_t* src, int64_t* totals, hipStream_t s);
+                        int64_t C, int32_t* slot, int32_t* src, int64_t* totals, hipStream_t s,
+                        const int32_t* route_off = nullptr, int32_t* lcopy = nullptr, int32_t* ltok = nullptr);
+// out[i] = sum of in[0 .. i) for i <= n (one work-group).
+hipError_t launch_exclusive_scan(const int32_t* in, int n, int32_t* out, hipStream_t s);
 hipError_t launch_scatter_rows(const void* x, const int32_t* idx, const int32_t* slot, int64_t T,
                                int k, int64_t C, int64_t row_bytes, void* buckets, hipStream_t s);
 
@@ -172,10 +178,15 @@ hipError_t launch_gather_dx(const void* dout, const void* dX, const void* wr, co
                             const int32_t* slot, int64_t T, int64_t d, int k, int64_t C, bool bf16, void* dx,
                             hipStream_t s);
 // dWr [E][d] (dtype) and db [E] fp32 (may be NULL) from dl and x; part is fp32
-// scratch of router_wgrad_chunks() * E * (d + 1) floats.
+// scratch of router_wgrad_scratch_floats() floats. With the routed-copy
+// lists of launch_slots (route_off, lcopy, ltok, routed counts), 64 or more
+// experts and d % 8 == 0, each expert gathers its own copies' rows instead.
 int router_wgrad_chunks(int64_t T, int E, int64_t d);
+size_t router_wgrad_scratch_floats(int64_t T, int k, int E, int64_t d);
 hipError_t launch_router_wgrad(const void* x, const int32_t* idx, const float* dl, int64_t T, int k, int E,
-                               int64_t d, bool bf16, float* part, void* dwr, float* db, hipStream_t s);
+                               int64_t d, bool bf16, float* part, void* dwr, float* db, hipStream_t s,
+                               const int32_t* routed = nullptr, const int32_t* route_off = nullptr,
+                               const int32_t* lcopy = nullptr, const int32_t* ltok = nullptr);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 
 // ---- combine (combine.hip) ----

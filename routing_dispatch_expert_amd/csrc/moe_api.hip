@@ -187,6 +187,7 @@ struct BackPlan {
   void *g, *u, *dy, *dh, *dgu, *dX, *WdT, *WguT, *dyT, *hT, *dgT, *duT, *XT;
   float *dl, *rpart;
   int32_t *kfull_d, *kfull_f, *mtile_d, *mtile_f;
+  int32_t *route_off, *lcopy, *ltok;  // routed copies listed per expert (router weight gradient)
   int64_t Kp;
   size_t bytes;
 };
@@ -221,7 +222,10 @@ BackPlan plan_backward(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E, 
   b.kfull_f = c.take<int32_t>(E);
   b.mtile_d = c.take<int32_t>(static_cast<size_t>(E) + 1);
   b.mtile_f = c.take<int32_t>(static_cast<size_t>(E) + 1);
-  b.rpart = c.take<float>(static_cast<size_t>(moe::router_wgrad_chunks(T, E, d)) * E * (d + 1));
+  b.rpart = c.take<float>(moe::router_wgrad_scratch_floats(T, k, E, d));
+  b.route_off = c.take<int32_t>(static_cast<size_t>(E) + 1);
+  b.lcopy = c.take<int32_t>(static_cast<size_t>(T) * k);
+  b.ltok = c.take<int32_t>(static_cast<size_t>(T) * k);
   b.bytes = b.f.bytes + align_up(c.off);
   return b;
 }
@@ -465,7 +469,10 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   MOE_HIP_TRY(moe::launch_scan(p.tile_cnt, nt, E, C, P, d * eb, k, T, p.tile_off, p.routed, p.kept, p.send,
                                p.totals, bm, p.mtile, nullptr, s),
               "scan");
-  MOE_HIP_TRY(moe::launch_slots(p.idx, p.tile_off, T, k, E, C, p.slot, nullptr, p.totals, s), "slots");
+  MOE_HIP_TRY(moe::launch_exclusive_scan(p.routed, E, b.route_off, s), "routed offsets");
+  MOE_HIP_TRY(moe::launch_slots(p.idx, p.tile_off, T, k, E, C, p.slot, nullptr, p.totals, s, b.route_off, b.lcopy,
+                                b.ltok),
+              "slots");
   MOE_HIP_TRY(moe::launch_scatter_rows(x, p.idx, p.slot, T, k, C, d * eb, p.buckets, s), "scatter");
   // g = X Wg^T and u = X Wu^T (the plain row-tile GEMM: N = d_ff, K = d). GEMMs
   // that contract over d take the row-tile height of GEMM 1 (bm_d, map mtile_d_rows).
@@ -516,7 +523,8 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   //    the gate gradients: q_j = <dh_j, h_j> = w_j <dout, y_j>, dl_j = q_j - w_j sum_i q_i
   MOE_HIP_TRY(moe::launch_gate_grad(b.dh, p.h, p.idx, p.w, p.slot, T, F, k, C, bf16, b.dl, s), "gate gradients");
   // 5. router gradients, then dx = dout + the expert paths + the router path
-  MOE_HIP_TRY(moe::launch_router_wgrad(x, p.idx, b.dl, T, k, E, d, bf16, b.rpart, dW_router, d_bias, s),
+  MOE_HIP_TRY(moe::launch_router_wgrad(x, p.idx, b.dl, T, k, E, d, bf16, b.rpart, dW_router, d_bias, s, p.routed,
+                                       b.route_off, b.lcopy, b.ltok),
               "router wgrad");
   MOE_HIP_TRY(moe::launch_gather_dx(dout, b.dX, W_router, p.idx, b.dl, p.slot, T, d, k, C, bf16, dx, s),
               "gather dx");

@@ -170,12 +170,18 @@ __global__ __launch_bounds__(256) void src_padding_kernel(const int32_t* __restr
 // flattened order; lanes with the same expert form a group found by ballots
 // over the expert-id bits; a lane's rank is the number of group lanes below
 // it. The group's highest lane advances the expert's running count.
+// With route_off (the exclusive scan of the routed counts), every routed copy,
+// kept or dropped, is also listed per expert in token order: entry
+// route_off[e] + rank holds the copy's flat index (lcopy) and token (ltok).
 __global__ __launch_bounds__(64) void slots_kernel(const int32_t* __restrict__ idx,
                                                    const int32_t* __restrict__ tile_off,
                                                    int64_t T, int k, int E, int64_t C,
                                                    int32_t* __restrict__ slot,
                                                    int32_t* __restrict__ src,
-                                                   int64_t* __restrict__ totals) {
+                                                   int64_t* __restrict__ totals,
+                                                   const int32_t* __restrict__ route_off,
+                                                   int32_t* __restrict__ lcopy,
+                                                   int32_t* __restrict__ ltok) {
   extern __shared__ int sm[];
   int* cnt = sm;          // [E]
   int* sbuf = sm + E;     // [64 * k]
@@ -218,6 +224,11 @@ __global__ __launch_bounds__(64) void slots_kernel(const int32_t* __restrict__ i
       slot[t0 * k + i] = sl;
       sbuf[i] = sl;
       if (src && sl >= 0) src[static_cast<int64_t>(e) * C + s] = static_cast<int32_t>(t0 * k + i);
+      if (route_off) {
+        const int64_t at = static_cast<int64_t>(route_off[e]) + s;
+        lcopy[at] = static_cast<int32_t>(t0 * k + i);
+        ltok[at] = static_cast<int32_t>(t0 + i / k);
+      }
     }
   }
   __syncthreads();
@@ -350,12 +361,48 @@ hipError_t launch_mtile_map(const int32_t* kept, int E, int bm, int32_t* mtile_o
 }
 
 hipError_t launch_slots(const int32_t* idx, const int32_t* tile_off, int64_t T, int k, int E,
-                        int64_t C, int32_t* slot, int32_t* src, int64_t* totals, hipStream_t s) {
+                        int64_t C, int32_t* slot, int32_t* src, int64_t* totals, hipStream_t s,
+                        const int32_t* route_off, int32_t* lcopy, int32_t* ltok) {
   const int64_t nt = ceil_div(T, kTileTokens);
   if (nt == 0) return hipSuccess;
+  if (route_off && (!lcopy || !ltok)) return hipErrorInvalidValue;
   const size_t shm = (static_cast<size_t>(E) + static_cast<size_t>(kTileTokens) * k) * sizeof(int);
   slots_kernel<<<dim3(static_cast<unsigned>(nt)), dim3(64), shm, s>>>(idx, tile_off, T, k, E, C,
-                                                                     slot, src, totals);
+                                                                     slot, src, totals, route_off, lcopy, ltok);
+  return hipGetLastError();
+}
+
+namespace {
+// Exclusive scan of n int32 counts by one block: thread t sums a contiguous
+// run, the run totals are scanned in LDS, then each run is written out.
+__global__ __launch_bounds__(1024) void exclusive_scan_kernel(const int32_t* __restrict__ in, int n,
+                                                              int32_t* __restrict__ out) {
+  __shared__ int32_t tot[1024];
+  const int t = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  const int a = min(n, t * per), b = min(n, a + per);
+  int32_t sum = 0;
+  for (int i = a; i < b; ++i) sum += in[i];
+  tot[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
+    const int32_t v = t >= off ? tot[t - off] : 0;
+    __syncthreads();
+    tot[t] += v;
+    __syncthreads();
+  }
+  int32_t run = tot[t] - sum;
+  for (int i = a; i < b; ++i) {
+    out[i] = run;
+    run += in[i];
+  }
+  if (t == 1023) out[n] = tot[1023];
+}
+}  // namespace
+
+hipError_t launch_exclusive_scan(const int32_t* in, int n, int32_t* out, hipStream_t s) {
+  if (n < 0) return hipErrorInvalidValue;
+  exclusive_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(in, n, out);
   return hipGetLastError();
 }
 
