@@ -68,6 +68,9 @@ __device__ inline float silu_bf16(float g) {
 // tiles (B) in its L2.
 // ---------------------------------------------------------------------------
 constexpr int kGroupN = 8;
+#ifndef MOE_PERSIST_AT
+#define MOE_PERSIST_AT 1
+#endif
 
 // Expert, first row and column tile of live tile `lid`. Without a row-tile
 // map every one of the E groups has ceil(C / BM) row tiles.
@@ -124,14 +127,15 @@ struct Work {
 // live tile b / slices, and the caller keeps the slices' results apart.
 template <int BM>
 __device__ inline bool work_of_block(const int32_t* __restrict__ mtile_off, int E, int nt_count, int64_t nk,
-                                     int G, Work* w, int64_t C = 0, int slices = 1) {
+                                     int G, Work* w, int64_t C = 0, int slices = 1, int64_t bid = -1) {
+  if (bid < 0) bid = blockIdx.x;
   const int64_t live = (mtile_off ? static_cast<int64_t>(mtile_off[E]) : E * ((C + BM - 1) / BM)) * nt_count;
   if (slices > 1) {
-    const int64_t lid = blockIdx.x / slices;
+    const int64_t lid = bid / slices;
     if (lid >= live) return false;
     w->s = 1;
     w->ti = 0;
-    w->c = static_cast<int>(blockIdx.x % slices);
+    w->c = static_cast<int>(bid % slices);
     const int64_t pairs = nk / 2;
     w->kb = 2 * (w->c * pairs / slices);
     w->ke = 2 * ((w->c + 1) * pairs / slices);
@@ -153,11 +157,11 @@ __device__ inline bool work_of_block(const int32_t* __restrict__ mtile_off, int 
   w->ti = 0;
   w->kb = 0;
   w->ke = nk;
-  if (blockIdx.x < whole_blocks) {
-    lid = xcd_tile(blockIdx.x, whole);
+  if (bid < whole_blocks) {
+    lid = xcd_tile(bid, whole);
     if (lid < 0) return false;
   } else {
-    const int64_t u = blockIdx.x - whole_blocks;
+    const int64_t u = bid - whole_blocks;
     if (u >= rem * s) return false;
     w->s = static_cast<int>(s);
     w->ti = static_cast<int>(u / s);
@@ -517,8 +521,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   __shared__ uint4 Bs0[BN * CH], Bs1[BN * CH];
   __shared__ int arrival;
 
+  // With AT (no split round) the launch may hold fewer blocks than tiles: each
+  // block then takes tile ids bid, bid + gridDim.x, ... (one XCD's, in order)
+  // until its XCD's tiles run out.
+  constexpr bool PERSIST = AT && MOE_PERSIST_AT;
+  for (int64_t bid = blockIdx.x;; bid += gridDim.x) {
   Work wk;
-  if (!work_of_block<BM>(mtile_off, E, nt_count, K / BK, G, &wk, C, slices)) return;
+  if (!work_of_block<BM>(mtile_off, E, nt_count, K / BK, G, &wk, C, slices, bid)) return;
   const int e = __builtin_amdgcn_readfirstlane(wk.e);
   const int m0 = __builtin_amdgcn_readfirstlane(wk.m0);
   const int nt = __builtin_amdgcn_readfirstlane(wk.nt);
@@ -834,6 +843,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   store_wave_tile<TM, TN, SWIGLU, EB, true, BT>(
       acc, eb, out + static_cast<int64_t>(e) * C * N, m0 + wm * (BM / 2), rows,
       n0 + wn * (SWIGLU ? TN * 16 : TN * 32), N, lane);
+  if constexpr (!PERSIST) return;
+  __syncthreads();  // every wave's staging reads are done before the next tile's DMA
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1331,7 +1343,11 @@ hipError_t launch_gemm_tn(const void* a, int64_t lda, int64_t a_es, int64_t aoff
   if (E == 0 || M == 0 || N == 0) return hipSuccess;
   if (M % 8 || N % 8 || lda % 8 || aoff % 8 || aoff + M > lda) return hipErrorInvalidValue;
   const int64_t nt = ceil_div(N, 256);
-  const int64_t blocks = ceil_div(E * ceil_div(M, 256) * nt, 8) * 8;
+  int64_t blocks = ceil_div(E * ceil_div(M, 256) * nt, 8) * 8;
+  if (MOE_PERSIST_AT) {  // one resident block per CU walks its XCD's tiles
+    const int g = resident_groups();
+    if (g > 0) blocks = std::min<int64_t>(blocks, g);
+  }
   gemm_bf16_dma_kernel<false, true, false, true, kTnWaves>
       <<<dim3(static_cast<unsigned>(blocks)), dim3(kTnWaves * 64), 0, s>>>(
       static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b), nullptr, static_cast<bf16_t*>(out), nullptr,
