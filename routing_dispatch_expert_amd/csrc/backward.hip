@@ -191,6 +191,36 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
   if (t >= T) return;  // whole waves only; no barriers below
   using W = Word<BF16>;
   const uint4* drow = dout + t * V;
+  if constexpr (!DOT) {
+    // dout is read once: U words per lane at a time, then written scaled to
+    // every kept copy (non-temporal: nothing here reads them again)
+    constexpr int U = 4;
+    for (int64_t v0 = 0; v0 < V; v0 += 64 * U) {
+      float df[U][W::N];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t v = v0 + u * 64 + lane;
+        if (v < V) W::load(load_stream(drow + v), df[u]);
+      }
+      for (int j = 0; j < k; ++j) {
+        const int sl = __builtin_amdgcn_readfirstlane(slot[t * k + j]);
+        if (sl < 0) continue;
+        const int64_t base = (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(idx[t * k + j])) * C + sl) * V;
+        const float wj = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(w[t * k + j])));
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t v = v0 + u * 64 + lane;
+          if (v < V) {
+            float of[W::N];
+#pragma unroll
+            for (int q = 0; q < W::N; ++q) of[q] = wj * df[u][q];
+            store_stream(dy + base + v, W::store(of));
+          }
+        }
+      }
+    }
+    return;
+  }
   float my_dw = 0.f;  // lane j keeps dw of copy j
   for (int j = 0; j < k; ++j) {
     const int sl = __builtin_amdgcn_readfirstlane(slot[t * k + j]);
@@ -270,25 +300,55 @@ __global__ __launch_bounds__(256) void gather_dx_kernel(const uint4* __restrict_
   if (t >= T) return;
   const int lane = threadIdx.x & 63;
   using W = Word<BF16>;
-  for (int64_t v = lane; v < V; v += 64) {
-    float acc[W::N], f[W::N];
-    W::load(dout[t * V + v], acc);
+  // U words per lane at a time; dout and the dX rows are read once
+  // (non-temporal), the router rows are shared by many tokens (cached)
+  constexpr int U = 4;
+  for (int64_t v0 = 0; v0 < V; v0 += 64 * U) {
+    float acc[U][W::N];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * 64 + lane;
+      if (v < V) W::load(load_stream(dout + t * V + v), acc[u]);
+    }
     for (int j = 0; j < k; ++j) {
       const int sl = __builtin_amdgcn_readfirstlane(slot[t * k + j]);
       if (sl < 0) continue;
       const int64_t e = __builtin_amdgcn_readfirstlane(idx[t * k + j]);
-      W::load(dX[(e * C + sl) * V + v], f);
+      uint4 g[U];
 #pragma unroll
-      for (int q = 0; q < W::N; ++q) acc[q] += f[q];
+      for (int u = 0; u < U; ++u) {
+        const int64_t v = v0 + u * 64 + lane;
+        if (v < V) g[u] = load_stream(dX + (e * C + sl) * V + v);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (v0 + u * 64 + lane < V) {
+          float f[W::N];
+          W::load(g[u], f);
+#pragma unroll
+          for (int q = 0; q < W::N; ++q) acc[u][q] += f[q];
+        }
+      }
     }
     for (int j = 0; j < k; ++j) {
       const int64_t e = __builtin_amdgcn_readfirstlane(idx[t * k + j]);
       const float c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(dl[t * k + j])));
-      W::load(wr[e * V + v], f);
 #pragma unroll
-      for (int q = 0; q < W::N; ++q) acc[q] = fmaf(c, f[q], acc[q]);
+      for (int u = 0; u < U; ++u) {
+        const int64_t v = v0 + u * 64 + lane;
+        if (v < V) {
+          float f[W::N];
+          W::load(wr[e * V + v], f);
+#pragma unroll
+          for (int q = 0; q < W::N; ++q) acc[u][q] = fmaf(c, f[q], acc[u][q]);
+        }
+      }
     }
-    dx[t * V + v] = W::store(acc);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * 64 + lane;
+      if (v < V) store_stream(dx + t * V + v, W::store(acc[u]));
+    }
   }
 }
 
