@@ -37,6 +37,9 @@ BACK_CASES = [
     dict(T=100, d=64, E=96, k=4, d_ff=64, cf=1.0, dtype="f32", x_std=0.125, wr_std=0.125),
     dict(T=1200, d=256, E=32, k=8, d_ff=192, cf=1.0),  # C = 300: 320-row tiles for the GEMMs over d
     dict(T=1100, d=4096, E=4, k=2, d_ff=256, cf=1.25),  # C = 688, d >= 4096: 320-row tiles over d too
+    # more than 1024 experts: the routed-count scan gives each thread several
+    # experts; most experts get no copy
+    dict(T=300, d=64, E=1500, k=4, d_ff=64, cf=2.0),
 ]
 
 
