@@ -495,7 +495,8 @@ __device__ inline void wait_vm_lgkm0() {
 // contracts over kk[e] rows (rounded up to whole 128-row stage pairs, the
 // rows past kk[e] reading as zero), every group has C (= M) output rows, and
 // kept and mtile_off are NULL.
-template <bool SWIGLU, bool BT = false, bool F32OUT = false, bool AT = false, int NW = 4, int TM_ = 4>
+template <bool SWIGLU, bool BT = false, bool F32OUT = false, bool AT = false, int NW = 4, int TM_ = 4,
+          bool EARLY = true>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void gemm_bf16_dma_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
     bf16_t* __restrict__ out, const int32_t* __restrict__ kept, const int32_t* __restrict__ mtile_off,
@@ -706,9 +707,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
       if constexpr (TA == TM)
         interleave_groups<NMFMA, NFRAG, decltype(reads_first)::value>(std::make_integer_sequence<int, NFRAG>{});
     };
-    // Stage k in (as, bs); stage k + 1 goes to (an, bn_) unless this is the last.
-    auto stage = [&](auto has_next, const uint4* as, const uint4* bs, uint4* an, uint4* bn_, int64_t k) {
-      if constexpr (decltype(has_next)::value) dma(an, bn_, k + 1);
+    // Stage k is in (as, bs). With EARLY, stage k + 1 is already on its way
+    // into (an, bn_); once every wave has read its last fragments of stage k
+    // and stage k + 1 has landed (one barrier), stage k + 2 is requested into
+    // (as, bs) at once, a sub-step before the matrix work of stage k ends, so
+    // each stage's loads have a stage and a quarter of matrix work to arrive.
+    // Without EARLY, stage k + 1 is requested as stage k starts (one stage).
+    auto stage = [&](auto has_next, auto has_next2, uint4* as, uint4* bs, uint4* an, uint4* bn_, int64_t k) {
+      if constexpr (!EARLY && decltype(has_next)::value) dma(an, bn_, k + 1);
       if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);  // the matrix run goes first
       fload(as, bs, 1, 1);
       mfmas(0);
@@ -728,6 +734,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         wait_vm_lgkm0<0>();            // own DMA of stage k + 1 landed, reads of stage k done ...
         __builtin_amdgcn_s_barrier();  // ... and everyone else's
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (EARLY && decltype(has_next2)::value) dma(as, bs, k + 2);
         fload(an, bn_, 0, 0);
       }
       mfmas(1);
@@ -739,14 +746,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     dma(As0, Bs0, kb);
     wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
+    if constexpr (EARLY) dma(As1, Bs1, kb + 1);  // ke - kb is even and positive
     fload(As0, Bs0, 0, 0);
     int64_t k = kb;
-    for (; k + 2 < ke; k += 2) {
-      stage(T_{}, As0, Bs0, As1, Bs1, k);
-      stage(T_{}, As1, Bs1, As0, Bs0, k + 1);
+    for (; k + 2 < ke; k += 2) {  // then k + 3 < ke as well
+      stage(T_{}, T_{}, As0, Bs0, As1, Bs1, k);
+      stage(T_{}, T_{}, As1, Bs1, As0, Bs0, k + 1);
     }
-    stage(T_{}, As0, Bs0, As1, Bs1, k);
-    stage(F_{}, As1, Bs1, As0, Bs0, k + 1);
+    stage(T_{}, F_{}, As0, Bs0, As1, Bs1, k);
+    stage(F_{}, F_{}, As1, Bs1, As0, Bs0, k + 1);
   };
   if (ke > kb) {  // with AT a group that kept no row contracts over nothing: its block is zero
     if (ta >= TM || (TM == 4 && ta == 3))
@@ -1293,9 +1301,18 @@ hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out,
       if (err != hipSuccess) return err;
       blocks += G;
     }
-    gemm_bf16_dma_kernel<SWIGLU, false, false, false, 8, 5><<<dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s>>>(
-        pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap, G > 0 ? sk->part : nullptr,
-        G > 0 ? sk->tick : nullptr, G);
+    // Each stage's loads are requested a sub-step early, except for SwiGLU
+    // over experts of 64 or more column tiles: there (d_ff = 14336, K = 4096)
+    // the early request measured 2% slower, against 1-4% faster elsewhere.
+    if (SWIGLU && nt >= 64)
+      gemm_bf16_dma_kernel<SWIGLU, false, false, false, 8, 5, false>
+          <<<dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s>>>(
+          pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap, G > 0 ? sk->part : nullptr,
+          G > 0 ? sk->tick : nullptr, G);
+    else
+      gemm_bf16_dma_kernel<SWIGLU, false, false, false, 8, 5><<<dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s>>>(
+          pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap, G > 0 ? sk->part : nullptr,
+          G > 0 ? sk->tick : nullptr, G);
   } else if constexpr (BM == 128 && BN == 256) {
     if (K % 64) return hipErrorInvalidValue;  // callers pick this tile only for K % 64 == 0
     gemm_bf16_dma_m128_kernel<SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
