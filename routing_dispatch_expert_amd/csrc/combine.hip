@@ -44,6 +44,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
   }
   const uint4* xr = x + t * V;
   uint4* orow = out + t * V;
+  // taken while every lane is active: lanes past the row's end leave the loop below
   const uint64_t kept = __ballot(s_l >= 0);
   // row of kept copy j (a wave-uniform lane index) and its gate
   auto copy_row = [&](int j, float& wj) {

@@ -19,10 +19,6 @@ constexpr int kTileTokens = 64;
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Waves that share one token's row in the row-moving kernels (scatter,
-// combine): 1 when there are many tokens, up to 4 (a whole 256-thread block)
-// when there are few, so short batches still keep enough loads in flight.
-inline int row_waves_per_token(int64_t T) { return T >= 1024 ? 1 : (T >= 256 ? 2 : 4); }
 
 __device__ inline float bf16_to_f32(bf16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 

@@ -241,38 +241,45 @@ __global__ __launch_bounds__(64) void slots_kernel(const int32_t* __restrict__ i
   }
 }
 
-// Row scatter: one wave per token moves its row (16-byte words, U per lane in
-// flight) to each kept destination bucket row; the row is read once and
-// written k' <= k times with streaming stores. The token's slots are
-// wave-uniform scalar loads.
-template <int WPT>
+// Row scatter: one 256-thread block per token moves its row (16-byte words,
+// U per lane, so a row of up to 256*U words takes one pass) to each kept
+// destination bucket row; the row is read once and written k' <= k times with
+// streaming stores. Lane j of each wave loads copy j's slot and expert (k <=
+// 32) while the row's words are on their way, and a ballot over the slots
+// gives the kept copies.
+template <int U>
 __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restrict__ x,
                                                            const int32_t* __restrict__ idx,
                                                            const int32_t* __restrict__ slot, int64_t T,
                                                            int k, int64_t C, int64_t V,
                                                            uint4* __restrict__ buckets) {
-  constexpr int U = 4;
-  constexpr int LANES = 64 * WPT;  // threads sharing one token
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * (4 / WPT) + threadIdx.x / LANES;
+  const int64_t t = blockIdx.x;
   if (t >= T) return;
-  const int lane = threadIdx.x % LANES;
-  const int32_t* st = slot + t * k;
-  const int32_t* it = idx + t * k;
+  const int lane = threadIdx.x;
+  const int wl = threadIdx.x % 64;
+  int s_l = -1, e_l = 0;
+  if (wl < k) {
+    s_l = slot[t * k + wl];
+    e_l = idx[t * k + wl];
+  }
   const uint4* xr = x + t * V;
-  for (int64_t v0 = lane; v0 < V; v0 += LANES * U) {
+  // taken while every lane is active: lanes past the row's end leave the loop below
+  const uint64_t kept = __ballot(s_l >= 0);
+  for (int64_t v0 = lane; v0 < V; v0 += 256 * U) {
     uint4 val[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t v = v0 + LANES * u;
+      const int64_t v = v0 + 256 * u;
       if (v < V) val[u] = xr[v];
     }
-    for (int j = 0; j < k; ++j) {
-      const int sl = __builtin_amdgcn_readfirstlane(st[j]);
-      if (sl < 0) continue;
-      uint4* dst = buckets + (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(it[j])) * C + sl) * V;
+    for (uint64_t m = kept; m; m &= m - 1) {
+      const int j = __builtin_ctzll(m);
+      const int e = __builtin_amdgcn_readlane(e_l, j);
+      const int sl = __builtin_amdgcn_readlane(s_l, j);
+      uint4* dst = buckets + (static_cast<int64_t>(e) * C + sl) * V;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t v = v0 + LANES * u;
+        const int64_t v = v0 + 256 * u;
         if (v < V) store_stream(&dst[v], val[u]);
       }
     }
@@ -411,15 +418,18 @@ hipError_t launch_scatter_rows(const void* x, const int32_t* idx, const int32_t*
   if (T == 0) return hipSuccess;
   const auto* xv = static_cast<const uint4*>(x);
   auto* bv = static_cast<uint4*>(buckets);
+  if (k > 32) return hipErrorInvalidValue;  // one lane per copy, k <= 32 lanes of a wave
   const int64_t V = row_bytes / 16;
-  const int wpt = row_waves_per_token(T);
-  const dim3 grid(static_cast<unsigned>(ceil_div(T, 4 / wpt)));
-  if (wpt == 1)
+  const dim3 grid(static_cast<unsigned>(T));
+  // words per lane: the smallest of 1, 2, 4 that covers the row in one pass, else 8
+  if (V <= 256)
     scatter_rows_kernel<1><<<grid, dim3(256), 0, s>>>(xv, idx, slot, T, k, C, V, bv);
-  else if (wpt == 2)
+  else if (V <= 512)
     scatter_rows_kernel<2><<<grid, dim3(256), 0, s>>>(xv, idx, slot, T, k, C, V, bv);
-  else
+  else if (V <= 1024)
     scatter_rows_kernel<4><<<grid, dim3(256), 0, s>>>(xv, idx, slot, T, k, C, V, bv);
+  else
+    scatter_rows_kernel<8><<<grid, dim3(256), 0, s>>>(xv, idx, slot, T, k, C, V, bv);
   return hipGetLastError();
 }
 

@@ -140,6 +140,9 @@ PERMUTE_CASES = [
     (300, 256, 8, 1.25, 8, 16, "bf16", False), (65, 4, 2, 0.3, 2, 8, "f32", True),
     (64, 8, 2, 1.25, 1, 128, "f32", False), (1, 3, 2, 1.0, 1, 8, "bf16", False),
     (129, 1, 1, 2.0, 1, 8, "bf16", False), (5000, 32, 4, 0.5, 8, 24, "bf16", True),
+    (40, 8, 2, 1.0, 2, 20480, "bf16", False),   # 2560 words a row: two passes of 8 words per lane
+    (30, 4, 2, 1.0, 1, 8200, "f32", True),      # 2050 words a row: a second pass of 2 words
+    (100, 64, 32, 0.5, 4, 64, "bf16", True),    # k = 32: every metadata lane of a wave, many drops
 ]
 
 
@@ -253,7 +256,11 @@ def test_grouped_gemm_rows_below_kept(E, C, d, d_ff, dtype):
 
 COMBINE_CASES = [(500, 64, 8, 2, 1.0, "bf16"), (300, 40, 16, 4, 0.5, "bf16"), (64, 128, 8, 2, 1.25, "f32"),
                  (200, 8, 4, 4, 0.25, "bf16"), (1, 16, 2, 1, 1.0, "f32"),
-                 (1100, 6208, 8, 3, 0.5, "bf16")]   # long rows: 8 words per lane, a ragged last pass
+                 (1100, 6208, 8, 3, 0.5, "bf16"),   # one pass of 4 words per lane, the last ragged
+                 (40, 20480, 8, 2, 1.0, "bf16"),    # 2560 words a row: two passes of 8 words per lane
+                 (30, 8200, 4, 2, 1.0, "f32"),      # 2050 words a row: a second pass of 2 words
+                 (100, 64, 64, 32, 0.5, "bf16"),    # k = 32: every metadata lane of a wave, many drops
+                 (50, 24, 32, 32, 1.0, "f32")]      # k = E = 32
 
 
 @pytest.mark.parametrize("T,d,E,k,cf,dtype", COMBINE_CASES)
