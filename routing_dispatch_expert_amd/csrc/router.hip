@@ -20,8 +20,9 @@ namespace {
 constexpr int kMaxRouterSplits = 8;  // d-slices of the router scores (partials summed in order)
 
 // ---------------------------------------------------------------------------
-// Scores on the matrix cores. Each wave is one work item: 16 tokens x (16*NT)
-// experts over one of S slices of d, with v_mfma_f32_16x16x32_bf16; it writes
+// Scores on the matrix cores. Each wave is one work item: 16 MT tokens x
+// (16 NT) experts over one of S slices of d, with v_mfma_f32_16x16x32_bf16;
+// each router-weight fragment it loads serves its MT token tiles. It writes
 // fp32 partial sums part[s][t][e]. The route kernel adds the S partials in
 // slice order (a fixed order: the result does not depend on scheduling), so
 // few tokens still spread over many waves. Both operands come straight from
@@ -29,69 +30,90 @@ constexpr int kMaxRouterSplits = 8;  // d-slices of the router scores (partials 
 // Lane l of an A/B operand holds row (l % 16), K elements 8*(l/16) .. +8;
 // the accumulator of lane l holds rows 4*(l/16) + r, column l % 16.
 // ---------------------------------------------------------------------------
-template <int NT>
+template <int NT, int MT>
 __global__ __launch_bounds__(256) void router_logits_bf16(const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ wr, int64_t T,
                                                           int64_t d, int E, int S, int64_t kper,
                                                           float* __restrict__ part) {
+  constexpr int U = MT == 1 ? 4 : 2;  // k-steps whose loads are in flight together
   const int lane = threadIdx.x & 63;
-  const int64_t tt = ceil_div(T, 16);
+  const int64_t tt = ceil_div(T, 16 * MT);
   const int64_t ec = ceil_div(E, 16 * NT);
   const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (item >= tt * ec * S) return;
-  const int64_t t0 = (item % tt) * 16;
+  const int64_t t0 = (item % tt) * 16 * MT;
   const int e0 = static_cast<int>((item / tt) % ec) * 16 * NT;
   const int s = static_cast<int>(item / (tt * ec));
   const int64_t k_lo = s * kper, k_hi = min(d, k_lo + kper);
   const int kg = (lane >> 4) * 8;
-  const int64_t trow = min(t0 + (lane & 15), T - 1);  // rows past T are computed, not stored
-  const bf16_t* xp = x + trow * d + kg;
+  const bf16_t* xp[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int64_t trow = min(t0 + 16 * m + (lane & 15), T - 1);  // rows past T are computed, not stored
+    xp[m] = x + trow * d + kg;
+  }
   const bf16_t* wp[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const int e = min(e0 + 16 * j + (lane & 15), E - 1);
     wp[j] = wr + static_cast<int64_t>(e) * d + kg;
   }
-  f32x4 acc[NT];
+  f32x4 acc[MT][NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   int64_t k0 = k_lo;
-  for (; k0 + 4 * 32 <= k_hi; k0 += 4 * 32) {  // four steps in flight
-    bf16x8 a[4], b[4][NT];
+  for (; k0 + U * 32 <= k_hi; k0 += U * 32) {
+    bf16x8 a[U][MT], b[U][NT];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      a[u] = *reinterpret_cast<const bf16x8*>(xp + k0 + 32 * u);
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) a[u][m] = *reinterpret_cast<const bf16x8*>(xp[m] + k0 + 32 * u);
 #pragma unroll
       for (int j = 0; j < NT; ++j) b[u][j] = *reinterpret_cast<const bf16x8*>(wp[j] + k0 + 32 * u);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int j = 0; j < NT; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][j], acc[j], 0, 0, 0);
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][m], b[u][j], acc[m][j], 0, 0, 0);
   }
   for (; k0 < k_hi; k0 += 32) {
     const bool in = k0 + kg < k_hi;  // d is a multiple of 8: whole 8-element groups
-    bf16x8 a = {};
-    if (in) a = *reinterpret_cast<const bf16x8*>(xp + k0);
+    bf16x8 a[MT], b[NT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      a[m] = bf16x8{};
+      if (in) a[m] = *reinterpret_cast<const bf16x8*>(xp[m] + k0);
+    }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      bf16x8 b = {};
-      if (in) b = *reinterpret_cast<const bf16x8*>(wp[j] + k0);
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+      b[j] = bf16x8{};
+      if (in) b[j] = *reinterpret_cast<const bf16x8*>(wp[j] + k0);
     }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], b[j], acc[m][j], 0, 0, 0);
   }
   float* ps = part + static_cast<int64_t>(s) * T * E;
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const int e = e0 + 16 * j + (lane & 15);
-    if (e >= E) continue;
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t t = t0 + 4 * (lane >> 4) + r;
-      if (t < T) ps[t * E + e] = acc[j][r];
+    for (int j = 0; j < NT; ++j) {
+      const int e = e0 + 16 * j + (lane & 15);
+      if (e >= E) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = t0 + 16 * m + 4 * (lane >> 4) + r;
+        if (t < T) ps[t * E + e] = acc[m][j][r];
+      }
     }
-  }
 }
 
 // fp32 scores: one thread per (token, expert), plain fused multiply-adds.
@@ -357,6 +379,18 @@ static bool router_on_gemm(int64_t T, int64_t d, int E, bool bf16) {
   return bf16 && E >= 128 && E % 8 == 0 && T >= 256 && d % 128 == 0;
 }
 
+// Token tiles of 16 per wave of the score kernel: the largest of 4 and 2 that
+// still gives 1024 waves with the most d-slices allowed, else 1. Each router
+// weight fragment a wave loads then serves that many tiles (measured on
+// T = 16384, E = 64: 43 -> 26 us; T = 4096, E = 8: 10.7 -> 10.0 us).
+static int router_tile_tokens(int64_t T, int64_t d, int E) {
+  const int nt = E <= 16 ? 1 : (E <= 32 ? 2 : 4);
+  const int64_t s_max = std::max<int64_t>(1, std::min<int64_t>(d / 256, kMaxRouterSplits));
+  for (int mt : {4, 2})
+    if (ceil_div(T, 16 * mt) * ceil_div(E, 16 * nt) * s_max >= 1024) return mt;
+  return 1;
+}
+
 int router_splits(int64_t T, int64_t d, int E, bool bf16) {
   if (!bf16 || T == 0) return 1;
   if (router_on_gemm(T, d, E, bf16)) {  // d-slices so that about 256 tiles run at once
@@ -365,9 +399,10 @@ int router_splits(int64_t T, int64_t d, int E, bool bf16) {
         1, std::min({ceil_div(256, tiles), d / 128, int64_t{kMaxRouterSplits}})));
   }
   const int nt = E <= 16 ? 1 : (E <= 32 ? 2 : 4);
-  const int64_t items = ceil_div(T, 16) * ceil_div(E, 16 * nt);
-  const int64_t by_work = ceil_div(2048, items);        // aim at >= 2048 waves
-  const int64_t by_len = std::max<int64_t>(1, d / 256);  // at least 256 of d per slice
+  const int mt = router_tile_tokens(T, d, E);
+  const int64_t items = ceil_div(T, 16 * mt) * ceil_div(E, 16 * nt);
+  const int64_t by_work = ceil_div(mt == 1 ? 2048 : 1024, items);  // aim at >= 2048 (1024) waves
+  const int64_t by_len = std::max<int64_t>(1, d / 256);              // at least 256 of d per slice
   return static_cast<int>(std::max<int64_t>(1, std::min({by_work, by_len, int64_t{kMaxRouterSplits}})));
 }
 
@@ -382,17 +417,29 @@ hipError_t launch_router_logits(const void* x, const void* wr, int64_t T, int64_
     return hipGetLastError();
   }
   const int nt = E <= 16 ? 1 : (E <= 32 ? 2 : 4);
+  const int mt = router_tile_tokens(T, d, E);
   const int64_t kper = ceil_div(ceil_div(d, S), 32) * 32;
-  const int64_t items = ceil_div(T, 16) * ceil_div(E, 16 * nt) * S;
+  const int64_t items = ceil_div(T, 16 * mt) * ceil_div(E, 16 * nt) * S;
   const dim3 grid(static_cast<unsigned>(ceil_div(items, 4)));
   const auto* xb = static_cast<const bf16_t*>(x);
   const auto* wb = static_cast<const bf16_t*>(wr);
-  if (nt == 1)
-    router_logits_bf16<1><<<grid, dim3(256), 0, s>>>(xb, wb, T, d, E, S, kper, part);
-  else if (nt == 2)
-    router_logits_bf16<2><<<grid, dim3(256), 0, s>>>(xb, wb, T, d, E, S, kper, part);
-  else
-    router_logits_bf16<4><<<grid, dim3(256), 0, s>>>(xb, wb, T, d, E, S, kper, part);
+#define MOE_SCORES(N, M) router_logits_bf16<N, M><<<grid, dim3(256), 0, s>>>(xb, wb, T, d, E, S, kper, part)
+#define MOE_SCORES_M(N)                    \
+  if (mt == 4)                             \
+    MOE_SCORES(N, 4);                      \
+  else if (mt == 2)                        \
+    MOE_SCORES(N, 2);                      \
+  else                                     \
+    MOE_SCORES(N, 1)
+  if (nt == 1) {
+    MOE_SCORES_M(1);
+  } else if (nt == 2) {
+    MOE_SCORES_M(2);
+  } else {
+    MOE_SCORES_M(4);
+  }
+#undef MOE_SCORES_M
+#undef MOE_SCORES
   return hipGetLastError();
 }
 

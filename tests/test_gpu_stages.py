@@ -80,7 +80,9 @@ def test_route_given_logits_is_exact(T, E, k, kind, P, M):
 ROUTER_CASES = [
     (300, 256, 8, 2, "bf16", None), (200, 1024, 64, 6, "bf16", "zipf1.2"), (130, 520, 256, 8, "bf16", None),
     (100, 128, 8, 2, "f32", None), (65, 72, 20, 3, "bf16", None), (1, 4096, 8, 2, "bf16", None),
-    (64, 7168, 256, 8, "bf16", None), (40, 2048, 64, 20, "bf16", "zipf1.2"), (4100, 4096, 8, 2, "bf16", None),
+    (64, 7168, 256, 8, "bf16", None), (40, 2048, 64, 20, "bf16", "zipf1.2"),
+    # score waves of 2 and 4 token tiles of 16, each with a ragged last tile
+    (4100, 4096, 8, 2, "bf16", None), (8200, 2048, 64, 6, "bf16", "zipf1.2"),
     # 128 or more experts and 256 or more tokens: scores on the grouped GEMM kernel (fp32 slices over d)
     (1000, 1024, 128, 6, "bf16", "zipf1.2"), (600, 7168, 256, 8, "bf16", None), (2304, 2048, 128, 4, "bf16", None),
 ]
