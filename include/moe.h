@@ -148,11 +148,12 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
                        float* d_bias, void* dW_gate, void* dW_up, void* dW_down, void* workspace,
                        size_t workspace_bytes, void* stream);
 
-/* Hot-expert replication ([EP-guide] section 4 "Expert Replication": a popular
- * expert is replicated on several devices and its tokens may go to either
- * copy, for better balance and fewer drops at the cost of memory; [EP-vs-TP]
- * "Expert parallelism pays in all-to-all dispatch": a load balancer re-places
- * experts under skew). The pages give no policy; the readings taken:
+/* Hot-expert replication ([EP-guide] section 6 "Optimizations", "Expert
+ * Replication": a popular expert is replicated on several devices and its
+ * tokens may go to either copy, for better balance and fewer drops at the
+ * cost of memory; [EP-vs-TP] "Expert parallelism pays in all-to-all
+ * dispatch": a load balancer re-places experts under skew). The pages give
+ * no policy; the readings taken:
  *  - moe_replica_plan (host only): r[e] = 1 for every expert, then each of
  *    `extra` more replicas goes to the expert with the highest routed[e]/r[e]
  *    (exact integer comparison, lowest index on a tie).

@@ -364,9 +364,9 @@ def routing_stats(slot: np.ndarray, routed: np.ndarray, kept: np.ndarray, C: int
 def replica_plan(routed: np.ndarray, extra: int) -> np.ndarray:
     """Replica counts: one per expert, plus `extra` more for the hot ones.
 
-    [EP-guide] section 4, "Expert Replication": popular experts are replicated
-    on several devices so their tokens can go to either copy, for better
-    balance and fewer drops at the cost of memory; [EP-vs-TP] names a load
+    [EP-guide] section 6 "Optimizations", "Expert Replication": popular experts
+    are replicated on several devices so their tokens can go to either copy,
+    for better balance and fewer drops at the cost of memory; [EP-vs-TP] names a load
     balancer that re-places experts under skew. No policy is given. Reading
     taken: each extra replica goes, one at a time, to the expert with the
     highest load per replica, routed[e] / r[e] (compared exactly as integers),
@@ -386,9 +386,10 @@ def replica_plan(routed: np.ndarray, extra: int) -> np.ndarray:
 def replica_layout(replicas: np.ndarray, P: int):
     """Instances of the replicated experts: offsets [E+1] (instance i of
     expert e is inst_off[e] + j for its replica j), expert_of[R] and
-    rank_of[R]. Reading taken for placement ([EP-guide] section 4 puts
-    replica 2 of expert 0 on the next device): replica j of expert e sits on
-    rank (home(e) + j) mod P, home(e) = e // (E/P) as for unreplicated experts.
+    rank_of[R]. Reading taken for placement ([EP-guide] section 6
+    "Optimizations", "Expert Replication", puts replica 2 of expert 0 on the
+    next device): replica j of expert e sits on rank (home(e) + j) mod P,
+    home(e) = e // (E/P) as for unreplicated experts.
     """
     r = np.asarray(replicas, dtype=np.int64)
     E = r.size

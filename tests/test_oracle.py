@@ -565,3 +565,86 @@ def test_replica_plan_minimises_the_worst_load_per_replica():
         assert worst == best
     # ties go to the lower index
     assert oracle.replica_plan(np.array([10, 10, 3]), 1).tolist() == [2, 1, 1]
+
+
+# --------------------------------------------------- where replicas live ---
+
+def _ring_placement(replicas, P):
+    """Placement walked one replica at a time: every expert's first replica on
+    its home rank (the contiguous owner of E/P whole experts), each further
+    replica on the rank after the previous one, wrapping after rank P - 1.
+    Returns [(expert, replica j, rank)] in instance order."""
+    E = len(replicas)
+    out = []
+    for e in range(E):
+        rank = 0
+        while (rank + 1) * (E // P) <= e:   # home: the rank whose slice holds e
+            rank += 1
+        for j in range(int(replicas[e])):
+            out.append((e, j, rank))
+            rank = rank + 1 if rank + 1 < P else 0
+    return out
+
+
+def check_replica_placement(layout):
+    """Every pin of the placement reading, for a function with replica_layout's
+    signature; raises AssertionError on the first violation."""
+    g = golden("replica_placement.json")
+    inst_off, expert_of, rank_of = layout(np.array(g["replicas"], np.int32), g["P"])
+    for p in g["placement"]:    # the page's two-GPU example, replica numbers 1-based
+        i = inst_off[p["expert"]] + p["replica"] - 1
+        assert expert_of[i] == p["expert"] and rank_of[i] == p["gpu"], p
+    rng = np.random.default_rng(850)
+    for P in (2, 4, 8):
+        for trial in range(12):
+            E = P * int(rng.integers(1, 5))
+            reps = rng.integers(1, 2 * P + 2, size=E).astype(np.int32)
+            reps[rng.integers(0, E)] = 1
+            inst_off, expert_of, rank_of = layout(reps, P)
+            R = int(reps.sum())
+            assert inst_off.tolist() == np.concatenate(([0], np.cumsum(reps))).tolist()
+            assert len(rank_of) == R and np.all((rank_of >= 0) & (rank_of < P))
+            walk = _ring_placement(reps, P)
+            assert [w[0] for w in walk] == list(expert_of)
+            assert [w[2] for w in walk] == list(rank_of), (P, reps.tolist())
+            for e in range(E):
+                ranks = rank_of[inst_off[e]:inst_off[e + 1]]
+                assert ranks[0] == e // (E // P)                     # replica 0 on the home rank
+                if reps[e] <= P:                                       # spread: one replica per rank
+                    assert len(set(ranks.tolist())) == reps[e]
+                else:                                                  # every rank, as evenly as possible
+                    cnt = np.bincount(ranks, minlength=P)
+                    assert cnt.max() - cnt.min() <= 1
+            # send counts over the instances' ranks add up to every kept row
+            kept = rng.integers(0, 50, size=R)
+            sc = np.bincount(rank_of, weights=kept, minlength=P)
+            assert sc.sum() == kept.sum()
+            # with one replica each the placement is the plain contiguous ownership
+            _, _, r1 = layout(np.ones(E, np.int32), P)
+            assert np.array_equal(r1, np.arange(E) // (E // P))
+
+
+def test_replica_placement_pins():
+    check_replica_placement(oracle.replica_layout)
+
+
+def _mutant(rank_fn):
+    def layout(replicas, P):
+        inst_off, expert_of, _ = oracle.replica_layout(replicas, P)
+        E = len(replicas)
+        j = np.arange(inst_off[-1]) - inst_off[expert_of]
+        return inst_off, expert_of, rank_fn(expert_of, j, E, P)
+    return layout
+
+
+@pytest.mark.parametrize("name,rank_fn", [
+    ("previous device", lambda e, j, E, P: (e // (E // P) - j) % P),
+    ("no spreading", lambda e, j, E, P: e // (E // P) + 0 * j),
+    ("round-robin home", lambda e, j, E, P: (e + j) % P),
+    ("no wrap", lambda e, j, E, P: e // (E // P) + j),
+    ("home skipped", lambda e, j, E, P: (e // (E // P) + 1 + j) % P),
+    ("stride two", lambda e, j, E, P: (e // (E // P) + 2 * j) % P),
+])
+def test_replica_placement_pins_catch_planted_mistakes(name, rank_fn):
+    with pytest.raises(AssertionError):
+        check_replica_placement(_mutant(rank_fn))
