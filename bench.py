@@ -4,8 +4,10 @@
 One step is one call of moe_layer_forward (router, top-k and gates, slots,
 bucket scatter, grouped SwiGLU GEMMs, combine) over one batch of tokens, with
 inputs and weights already resident in HBM. Default workload: the
-Mixtral-shaped prefill layer (T=4096 tokens, d=4096, E=8 experts, top-2,
-d_ff=14336, cf=1.25, bf16), synthetic seeded inputs.
+DeepSeek-V3-shaped prefill layer (T=8192 tokens, d=7168, E=256 experts, top-8,
+d_ff=2048, cf=1.25, bf16, buckets laid out as P=8 send buffers), synthetic
+seeded inputs; --workload names another (mixtral_prefill, zipf_skew_drops,
+deepseek_v3_decode, deepseek_v3_node_limited, tiny_f32).
 
 Prints one JSON line: routed tokens/s per layer (whole job), per-stage GPU
 times from HIP events recorded by the library around each stage, the
@@ -18,6 +20,11 @@ with EXTRA replicas dealt to the most loaded experts of the same batch.
 With --backward a step is one call of moe_layer_backward instead (the
 gradients of x, the router and the expert weights for a seeded dout), and the
 line reports backward tokens/s.
+
+With --counters-summary no GPU work is done: the rocprofv3 counter CSVs of
+the profiling passes (PROFILE_PASSES, each a run of this script under
+rocprofv3 --pmc) are summarised per kernel, in the text format of the
+profiles/*_counters.txt files that the roofline's `traffic` is read from.
 """
 from __future__ import annotations
 
@@ -37,8 +44,23 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 METRIC = "routed tokens/s per MoE layer; grouped-GEMM % MFMA peak; permute % HBM BW"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_mixtral_prefill_traffic.txt")
-GEMM_SOURCE = os.path.join(ROOT, "routing_dispatch_expert_amd", "csrc", "grouped_gemm.hip")
+DEFAULT_WORKLOAD = "deepseek_v3_prefill"
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "routing_dispatch_expert_amd", "csrc")
+# the sources a kernel's counters depend on (the summary is stale once they change)
+STAGE_SOURCES = {"gate_up": ["grouped_gemm.hip", "common.h"], "down": ["grouped_gemm.hip", "common.h"],
+                 "scatter": ["permute.hip", "common.h"], "combine": ["combine.hip", "common.h"]}
+# tokens whose layer output the CPU oracle computes for the baseline (all when absent)
+CPU_SAMPLE = {"deepseek_v3_prefill": 512, "deepseek_v3_node_limited": 512}
+# rocprofv3 counter passes, one run each: name, counters (within one pass's
+# hardware limits: FETCH_SIZE takes 3 TCC counters, WRITE_SIZE 2)
+PROFILE_PASSES = [("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE"),
+                  ("mfma", "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE"),
+                  ("l2", "TCC_HIT_sum TCC_MISS_sum")]
+PROFILE_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc {counters} --output-format csv "
+               "-d $OUT/{workload}/{name} -o run -- python $REPO/bench.py --workload {workload} --steps 2 --warmup 1 "
+               "--no-cpu-baseline --no-profile --device-weights --copy-probe-mib 1024")
+COPY_PROBE_KIB = 1024 * 1024
 
 
 def parse():
@@ -46,8 +68,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixtral_prefill")
-    ap.add_argument("--cpu-sample", type=int, default=4096, help="tokens whose output the oracle computes")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-sample", type=int, default=None,
+                    help="tokens whose output the oracle computes (default: all, or 512 on the DeepSeek-V3 "
+                         "prefill shapes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-stage event loop")
     ap.add_argument("--flush-mib", type=int, default=512,
@@ -60,6 +84,13 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first copy a buffer of this many MiB on the device (a reference kernel of known "
                          "traffic for hardware counters)")
+    ap.add_argument("--device-weights", action="store_true",
+                    help="draw the expert weights on the device (torch's seeded generator, the same laws) "
+                         "instead of on the host: for counter passes, whose figures do not depend on the "
+                         "weights' values; implies --no-cpu-baseline")
+    ap.add_argument("--counters-summary", metavar="DIR",
+                    help="summarise the counter passes of --workload found under DIR/<workload>/<pass> and "
+                         "print the summary (no GPU work)")
     return ap.parse_args()
 
 
@@ -89,17 +120,133 @@ def gemm_work(nbytes: int, flops: int, dtype: str):
     return dict(bytes=nbytes, flops=flops, bound="mfma" if flops >= ridge * nbytes else "hbm")
 
 
-def read_traffic(gemm_src_sha: str):
-    """HBM bytes per launch of the gate/up GEMM from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def sources_sha(stage: str) -> str:
+    """sha256 over the kernel sources a stage's counters depend on."""
+    h = hashlib.sha256()
+    for name in STAGE_SOURCES[stage]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counters_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"moe_layer_{workload}_counters.txt")
+
+
+def read_traffic(workload: str, stage: str):
+    """HBM bytes per launch of a stage's kernel from the committed rocprofv3
+    counter summary of this workload, if it was taken on the current kernel
+    sources (else None)."""
+    path = counters_file(workload)
+    if not os.path.exists(path):
         return None
-    txt = open(TRAFFIC_FILE).read()
-    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", txt)
-    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not (m_sha and m_b) or m_sha.group(1) != gemm_src_sha:
+    txt = open(path).read()
+    m_sha = re.search(rf"^{stage}_sources_sha256:\s*([0-9a-f]+)", txt, re.M)
+    m_b = re.search(rf"^{stage}_hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
+    if not (m_sha and m_b) or m_sha.group(1) != sources_sha(stage):
         return None
     return float(m_b.group(1))
+
+
+def short_kernel_name(name: str) -> str:
+    """'void moe::(anonymous namespace)::k<a, b>(args...)' -> 'k<a, b>'."""
+    n = name.strip().strip('"')
+    if n.startswith("void "):
+        n = n[5:]
+    depth, cut = 0, len(n)
+    for i, ch in enumerate(n):       # drop the argument list (the first '(' outside template brackets)
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0 and not n.startswith("(anonymous", i):
+            cut = i
+            break
+    n = n[:cut]
+    return re.sub(r"^(?:[\w]+::|\(anonymous namespace\)::)+", "", n)
+
+
+def stage_of_kernel(short: str):
+    """The layer stage a forward kernel belongs to (None for the others)."""
+    m = re.match(r"(gemm_\w+?)<(\w+)(?:, (\w+))?(?:, (\w+))?", short)
+    if m:
+        if m.group(2) == "true":
+            return "gate_up"
+        if m.group(1) == "gemm_bf16_dma_kernel" and m.group(4) == "true":
+            return "router"                          # fp32-output score GEMM
+        return "down"
+    for prefix, stage in (("router_logits", "router"), ("route_kernel", "route"), ("scatter_rows", "scatter"),
+                          ("combine_kernel", "combine"), ("slots", "slots"), ("scan_finalize", "slots"),
+                          ("tile_hist", "slots"), ("perm", "slots")):
+        if short.startswith(prefix):
+            return stage
+    return None
+
+
+def read_counter_csv(folder: str):
+    """{short kernel name: {counter: [value per dispatch]}} from the
+    *counter_collection.csv files rocprofv3 wrote under folder."""
+    import csv
+    import glob
+    out = {}
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {folder}")
+    for path in files:
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                k = short_kernel_name(row["Kernel_Name"])
+                out.setdefault(k, {}).setdefault(row["Counter_Name"], {}).setdefault(
+                    row.get("Dispatch_Id") or row.get("Correlation_Id"), 0.0)
+                out[k][row["Counter_Name"]][row.get("Dispatch_Id") or row.get("Correlation_Id")] += \
+                    float(row["Counter_Value"])
+    return {k: {c: list(v.values()) for c, v in cs.items()} for k, cs in out.items()}
+
+
+def counters_summary(root: str, workload: str) -> str:
+    """Text summary of the counter passes of one workload (see PROFILE_PASSES)."""
+    import numpy as np
+    passes = {name: read_counter_csv(os.path.join(root, workload, name)) for name, _ in PROFILE_PASSES}
+    copy = next(k for k in passes["fetch"] if "copyBuffer" in k)
+    f_fac = COPY_PROBE_KIB / np.mean(passes["fetch"][copy]["FETCH_SIZE"])
+    w_fac = COPY_PROBE_KIB / np.mean(passes["write"][copy]["WRITE_SIZE"])
+    lines = [f"rocprofv3 hardware counters of the MoE layer forward, workload {workload} (MI355X)", "",
+             "Commands (from the repository root as $REPO, any output folder $OUT; one pass per run):"]
+    for name, counters in PROFILE_PASSES:
+        lines.append("  " + PROFILE_CMD.format(counters=counters, workload=workload, name=name))
+    lines.append(f"  python $REPO/bench.py --workload {workload} --counters-summary $OUT")
+    lines += ["", "HBM bytes: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by what each reads for the "
+              f"reference copy kernel ({copy}, 1 GiB read + 1 GiB written):",
+              f"  FETCH_SIZE factor {f_fac:.5f}, WRITE_SIZE factor {w_fac:.5f}",
+              "MFMA: SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 = executed bf16 matrix flops; SQ_VALU_MFMA_BUSY_CYCLES "
+              "over GRBM_GUI_ACTIVE x 1024 SIMDs = matrix-core busy fraction; GRBM_GUI_ACTIVE = GPU clock cycles "
+              "of the dispatch. L2 hit rate = TCC_HIT / (TCC_HIT + TCC_MISS).", "",
+              "Per dispatch (mean over the dispatches of the run):"]
+    hdr = (f"{'kernel':62s} {'stage':8s} {'FETCH KiB':>11s} {'WRITE KiB':>11s} {'HBM bytes':>11s} "
+           f"{'MFMA flop':>11s} {'MFMA busy':>9s} {'cycles':>10s} {'L2 hit':>7s}")
+    lines.append(hdr)
+    per_stage = {}
+    for k in passes["fetch"]:
+        def mean(p, c):
+            v = passes[p].get(k, {}).get(c)
+            return float(np.mean(v)) if v else float("nan")
+        fk, wk = mean("fetch", "FETCH_SIZE"), mean("write", "WRITE_SIZE")
+        hbm = (fk * f_fac + wk * w_fac) * 1024
+        mops, busy, gui = mean("mfma", "SQ_INSTS_VALU_MFMA_MOPS_BF16"), mean("mfma", "SQ_VALU_MFMA_BUSY_CYCLES"), \
+            mean("mfma", "GRBM_GUI_ACTIVE")
+        hit, miss = mean("l2", "TCC_HIT_sum"), mean("l2", "TCC_MISS_sum")
+        st = stage_of_kernel(k)
+        lines.append(f"{k[:62]:62s} {st or '-':8s} {fk:11.1f} {wk:11.1f} {hbm:11.4e} {mops * 512:11.4e} "
+                     f"{busy / (gui * 1024) if gui > 0 else float('nan'):9.3f} {gui:10.0f} "
+                     f"{hit / (hit + miss) if hit + miss > 0 else float('nan'):7.3f}")
+        if st:
+            per_stage.setdefault(st, []).append(hbm)
+    lines.append("")
+    for st in ("gate_up", "down", "scatter", "combine"):
+        if st in per_stage:
+            lines.append(f"{st}_hbm_bytes_per_launch: {sum(per_stage[st]):.6e}")
+            lines.append(f"{st}_sources_sha256: {sources_sha(st)}")
+    return "\n".join(lines) + "\n"
 
 
 def cpu_baseline(wl, host_w, sample: int, replicas=None):
@@ -112,17 +259,21 @@ def cpu_baseline(wl, host_w, sample: int, replicas=None):
         cores = 1
     tokens = np.arange(min(sample, wl.T))
     times = []
-    for _ in range(3):  # median of three runs
+    while len(times) < 3:    # median of three runs, or one run when a run takes over 10 s
         t0 = time.perf_counter()
         oracle.layer_forward(wl.x, wl.wr, lambda e: (host_w[0][e], host_w[1][e], host_w[2][e]), wl.T, wl.d,
                              wl.d_ff, wl.E, wl.k, wl.cf, wl.dtype, P=wl.P, bias=wl.bias_vec, tokens=tokens,
                              max_ranks=wl.max_ranks, replicas=replicas)
         times.append(time.perf_counter() - t0)
-    dt = sorted(times)[1]
+        if times[0] > 10.0:
+            break
+    dt = sorted(times)[len(times) // 2]
+    runs = "median of 3 runs" if len(times) == 3 else "one run"
     return {"value": round(tokens.size / dt, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "host": host_cpu(),
             "sample": f"layer outputs of the first {tokens.size} of {wl.T} tokens (routing and slots of all "
-                      f"{wl.T}), fp64 numpy, median of 3 runs: {dt:.1f} s each ({sum(times):.1f} s total)"}
+                      f"{wl.T}; every touched expert's weights decoded), fp64 numpy, {runs}: {dt:.1f} s each "
+                      f"({sum(times):.1f} s total)"}
 
 
 def run_backward(args, wl, moe, torch, np, dev, to_dev, host_w):
@@ -226,8 +377,27 @@ def blas_threads():
         return 1
 
 
+def device_expert_weights(wl, torch, dev):
+    """Expert weights drawn on the device with torch's generator, seeded from
+    the workload's weight seed: N(0, 1/sqrt(fan_in)) rounded to the layer
+    dtype, the laws of the host-drawn weights (not their bits)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(1000003 * (wl.weight_seed + 1))
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    out = []
+    for shape, fan_in in (((wl.E, wl.d_ff, wl.d), wl.d), ((wl.E, wl.d_ff, wl.d), wl.d), ((wl.E, wl.d, wl.d_ff), wl.d_ff)):
+        w = torch.empty(shape, dtype=dt, device=dev)
+        for e in range(wl.E):   # one expert at a time: no fp32 copy of the whole tensor
+            w[e] = (torch.randn(shape[1:], generator=g, device=dev) * (fan_in ** -0.5)).to(dt)
+        out.append(w)
+    return tuple(out)
+
+
 def main():
     args = parse()
+    if args.counters_summary:
+        sys.stdout.write(counters_summary(args.counters_summary, args.workload))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the layer here has no multi-GPU path (asked for --gpus "
               f"{args.gpus})", file=sys.stderr)
@@ -251,12 +421,19 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    host_w = wl.all_expert_weights()
-    if args.backward:
-        run_backward(args, wl, moe, torch, np, dev, to_dev, host_w)
-        return
+    if args.device_weights:
+        if args.backward or args.replicas >= 0:
+            sys.exit("--device-weights serves the plain forward's counter passes only")
+        args.no_cpu_baseline = True
+        host_w = None
+        wg, wu, wd = device_expert_weights(wl, torch, dev)
+    else:
+        host_w = wl.all_expert_weights()
+        if args.backward:
+            run_backward(args, wl, moe, torch, np, dev, to_dev, host_w)
+            return
+        wg, wu, wd = (to_dev(a) for a in host_w)
     x, wr = to_dev(wl.x), to_dev(wl.wr)
-    wg, wu, wd = (to_dev(a) for a in host_w)
     bias = None if wl.bias_vec is None else torch.from_numpy(wl.bias_vec).to(dev)
     T, d, d_ff, E, k, cf, P = wl.T, wl.d, wl.d_ff, wl.E, wl.k, wl.cf, wl.P
     C = moe.moe_capacity(T, E, k, cf)
@@ -361,8 +538,7 @@ def main():
     if stages:
         dom = max(stages, key=lambda n: stages[n]["ms"])
         w, s = work[dom], stages[dom]
-        sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
-        traffic = read_traffic(sha) if (dom == "gate_up" and wl.name == "mixtral_prefill") else None
+        traffic = read_traffic(wl.name, dom) if (dom in STAGE_SOURCES and reps is None) else None
         if w["bound"] == "mfma":
             roofline = {"bound": "mfma", "achieved": s["TFLOP_per_s"], "peak": PEAK_TFLOPS[wl.dtype],
                         "unit": "TFLOP/s", "frac": s["mfma_frac"], "traffic": traffic, "kernel": dom,
@@ -379,8 +555,9 @@ def main():
               file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
-        print(f"[bench] timing the CPU oracle on {min(args.cpu_sample, T)} tokens", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, host_w, args.cpu_sample, reps)
+        sample = args.cpu_sample if args.cpu_sample is not None else CPU_SAMPLE.get(wl.name, T)
+        print(f"[bench] timing the CPU oracle on {min(sample, T)} tokens", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, host_w, sample, reps)
 
     metric = METRIC if reps is None else METRIC + " (hot experts replicated)"
     line = {
@@ -400,7 +577,12 @@ def main():
         "grouped_gemm_mfma_frac": None if not stages else round(
             (work["gate_up"]["flops"] + work["down"]["flops"]) /
             ((stages["gate_up"]["ms"] + stages["down"]["ms"]) * 1e9) / PEAK_TFLOPS[wl.dtype], 4),
-        "permute_hbm_frac": None if not stages else stages["scatter"]["hbm_frac"],
+        # the permutation (scan, capacity, slots and drop mask, scatter) over its
+        # whole span; the scatter kernel alone beside it
+        "permute_hbm_frac": None if not stages else round(
+            (work["slots"]["bytes"] + work["scatter"]["bytes"]) /
+            ((stages["slots"]["ms"] + stages["scatter"]["ms"]) * 1e6) / PEAK_HBM_GBS, 4),
+        "scatter_hbm_frac": None if not stages else stages["scatter"]["hbm_frac"],
         "combine_hbm_frac": None if not stages else stages["combine"]["hbm_frac"],
         "stages": stages, "roofline": roofline, "cpu_baseline": cpu,
     }

@@ -212,6 +212,8 @@ int moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t P, i
  * routed/kept counts, slot [T, k], src [E, C], buckets [E, C, d] (kept rows
  * only; padding rows are not written), send_count [P] and totals. C is given
  * (normally moe_capacity()). Any of src, send_count, totals may be NULL.
+ * A topk_idx entry outside [0, E) is dropped (slot -1, counted in no
+ * expert), so no index given by a caller reaches outside the buckets.
  * workspace: moe_permute_workspace_size() bytes. */
 int moe_permute_workspace_size(int64_t T, int32_t E, size_t* bytes);
 int moe_permute(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, int32_t E,
@@ -227,6 +229,11 @@ int moe_permute(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, in
  *   y[e, s] = h[e, s] W_down[e]^T
  * Rows >= kept_count[e] are neither read for results nor written. bf16 runs
  * on the matrix cores with fp32 accumulation, h and y rounded to bf16.
+ * kept_count [E] int32 device memory; each count is taken clamped to [0, C]
+ * (a count above C processes the C rows of the bucket, a negative one none),
+ * so the call never reads or writes outside buckets [E, C, d], h [E, C, d_ff]
+ * and y [E, C, d]. Weights are [E, d_ff, d] (W_gate, W_up) and [E, d, d_ff]
+ * (W_down). Errors as for the layer, plus E * C >= 2^31 (MOE_ERR_UNSUPPORTED).
  * workspace: moe_grouped_gemm_workspace_size() bytes. */
 int moe_grouped_gemm_workspace_size(int32_t E, int64_t C, size_t* bytes);
 int moe_grouped_gemm(const void* buckets, const int32_t* kept_count, const void* W_gate,
@@ -237,7 +244,10 @@ int moe_grouped_gemm(const void* buckets, const int32_t* kept_count, const void*
 /* Combine stage ([EP-A2A] "All-to-all: the distributed transpose"):
  *   out[t] = x[t] + sum_j [slot[t,j] >= 0] topk_w[t,j] * y[topk_idx[t,j], slot[t,j]]
  * summed in fp32 over j ascending and rounded once; tokens with every slot -1
- * are copied bit for bit ([EP-inferensys] capacity entry). y is [E, C, d]. */
+ * are copied bit for bit ([EP-inferensys] capacity entry). y is [E, C, d].
+ * A copy counts as kept only when 0 <= slot[t,j] < C and 0 <= topk_idx[t,j]
+ * < E; any other copy is treated as dropped, so no index reaches outside y.
+ * x, out [T, d]; topk_idx, slot [T, k] int32; topk_w [T, k] fp32. */
 int moe_combine(const void* x, const void* y, const int32_t* topk_idx, const float* topk_w,
                 const int32_t* slot, int64_t T, int64_t d, int32_t E, int32_t k, int64_t C,
                 moe_dtype_t dtype, void* out, void* stream);

@@ -8,8 +8,9 @@
 // entry - a dropped token passes through the layer unchanged.
 //
 // out[t] = x[t] + sum_j [slot[t,j] >= 0] w[t,j] * y[idx[t,j], slot[t,j]]
-// The sum over j (ascending) is taken in fp32 with fused multiply-adds, added
-// to x in fp32 and rounded once. A token with no kept copy is copied bit for
+// A copy counts as kept only when 0 <= slot < C and 0 <= idx < E, so no
+// index given by a caller reaches outside y. The sum over j (ascending) is
+// taken in fp32 with fused multiply-adds, added to x in fp32 and rounded once. A token with no kept copy is copied bit for
 // bit (x + 0 would turn -0.0 into +0.0).
 #include "common.h"
 
@@ -29,7 +30,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
                                                       const int32_t* __restrict__ idx,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ slot, int64_t T, int k,
-                                                      int64_t C, int64_t V, uint4* __restrict__ out) {
+                                                      int E, int64_t C, int64_t V, uint4* __restrict__ out) {
   constexpr int NE = BF16 ? 8 : 4;
   const int64_t t = blockIdx.x;
   if (t >= T) return;
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
   const uint4* xr = x + t * V;
   uint4* orow = out + t * V;
   // taken while every lane is active: lanes past the row's end leave the loop below
-  const uint64_t kept = __ballot(s_l >= 0);
+  const uint64_t kept = __ballot(s_l >= 0 && s_l < C && e_l >= 0 && e_l < E);
   // row of kept copy j (a wave-uniform lane index) and its gate
   auto copy_row = [&](int j, float& wj) {
     const int e = __builtin_amdgcn_readlane(e_l, j);
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
 }  // namespace
 
 hipError_t launch_combine(const void* x, const void* y, const int32_t* idx, const float* w,
-                          const int32_t* slot, int64_t T, int64_t d, int k, int64_t C, bool bf16,
+                          const int32_t* slot, int64_t T, int64_t d, int k, int E, int64_t C, bool bf16,
                           void* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (k > 32) return hipErrorInvalidValue;  // one lane per copy, k <= 32 lanes of a wave
@@ -149,7 +150,7 @@ hipError_t launch_combine(const void* x, const void* y, const int32_t* idx, cons
   auto* ov = static_cast<uint4*>(out);
   // words per lane: the smallest of 1, 2, 4 that covers the row in one pass, else 8
   const int U = V <= 256 ? 1 : (V <= 512 ? 2 : (V <= 1024 ? 4 : 8));
-#define MOE_COMBINE(B, UU) combine_kernel<B, UU><<<grid, dim3(256), 0, s>>>(xv, yv, idx, w, slot, T, k, C, V, ov)
+#define MOE_COMBINE(B, UU) combine_kernel<B, UU><<<grid, dim3(256), 0, s>>>(xv, yv, idx, w, slot, T, k, E, C, V, ov)
 #define MOE_COMBINE_U(B)                       \
   switch (U) {                                 \
     case 1: MOE_COMBINE(B, 1); break;          \

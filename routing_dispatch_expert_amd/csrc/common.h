@@ -80,7 +80,8 @@ hipError_t launch_replica_layout(const int32_t* replicas, int E, int R, int P, i
                                  int32_t* place, hipStream_t s);
 hipError_t launch_instances(const int32_t* idx, const int32_t* qrank, const int32_t* replicas,
                             const int32_t* inst_off, int64_t n, int R, int32_t* inst, hipStream_t s);
-hipError_t launch_mtile_map(const int32_t* kept, int E, int bm, int32_t* mtile_off, hipStream_t s);
+// Row-tile prefix of bm-row tiles over the counts kept[e] clamped to [0, C].
+hipError_t launch_mtile_map(const int32_t* kept, int E, int64_t C, int bm, int32_t* mtile_off, hipStream_t s);
 // With route_off ([E + 1], the exclusive scan of the routed counts), lcopy and
 // ltok ([T * k]) list every routed copy per expert in token order: entry
 // route_off[e] + r is copy r of expert e (flat index t * k + j, and t).
@@ -186,8 +187,9 @@ hipError_t launch_router_wgrad(const void* x, const int32_t* idx, const float* d
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 
 // ---- combine (combine.hip) ----
+// A copy is kept when 0 <= slot < C and 0 <= idx < E (E buckets in y).
 hipError_t launch_combine(const void* x, const void* y, const int32_t* idx, const float* w,
-                          const int32_t* slot, int64_t T, int64_t d, int k, int64_t C, bool bf16,
+                          const int32_t* slot, int64_t T, int64_t d, int k, int E, int64_t C, bool bf16,
                           void* out, hipStream_t s);
 
 }  // namespace moe

@@ -37,6 +37,12 @@ __device__ inline int owner_expert(const int32_t* __restrict__ mtile_off, int E,
   return lo;
 }
 
+// Rows of bucket e that hold data: kept[e] clamped to [0, C], so a count
+// beyond the capacity never reaches past the bucket.
+__device__ inline int bucket_rows(const int32_t* __restrict__ kept, int e, int64_t C) {
+  return static_cast<int>(min(max(static_cast<int64_t>(kept[e]), int64_t{0}), C));
+}
+
 __device__ inline float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // silu for results rounded to bf16 next: hardware 2^x and reciprocal (each
@@ -68,9 +74,9 @@ __device__ inline float silu_bf16(float g) {
 // tiles (B) in its L2.
 // ---------------------------------------------------------------------------
 constexpr int kGroupN = 8;
-#ifndef MOE_PERSIST_AT
-#define MOE_PERSIST_AT 1
-#endif
+// Weight-gradient launches (K-major A and B) keep one resident block per CU
+// that walks its XCD's tiles in turn.
+constexpr bool kPersistAt = true;
 
 // Expert, first row and column tile of live tile `lid`. Without a row-tile
 // map every one of the E groups has ceil(C / BM) row tiles.
@@ -288,7 +294,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BM >= 25
   e = __builtin_amdgcn_readfirstlane(e);
   m0 = __builtin_amdgcn_readfirstlane(m0);
   nt = __builtin_amdgcn_readfirstlane(nt);
-  const int rows = __builtin_amdgcn_readfirstlane(kept[e]);
+  const int rows = __builtin_amdgcn_readfirstlane(bucket_rows(kept, e, C));
   const int64_t n0 = static_cast<int64_t>(nt) * BNO;
 
   // Global operands through raw buffer loads: one 32-bit offset per chunk,
@@ -525,7 +531,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // With AT (no split round) the launch may hold fewer blocks than tiles: each
   // block then takes tile ids bid, bid + gridDim.x, ... (one XCD's, in order)
   // until its XCD's tiles run out.
-  constexpr bool PERSIST = AT && MOE_PERSIST_AT;
+  constexpr bool PERSIST = AT && kPersistAt;
   for (int64_t bid = blockIdx.x;; bid += gridDim.x) {
   Work wk;
   if (!work_of_block<BM>(mtile_off, E, nt_count, K / BK, G, &wk, C, slices, bid)) return;
@@ -539,7 +545,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int64_t kb = __builtin_amdgcn_readfirstlane(static_cast<int>(wk.kb));  // stages [kb, ke): even
   const int64_t ke = AT ? 2 * ((kr_e + 2 * BK - 1) / (2 * BK))
                         : __builtin_amdgcn_readfirstlane(static_cast<int>(wk.ke));
-  const int rows = __builtin_amdgcn_readfirstlane(kept ? kept[e] : static_cast<int>(C));
+  const int rows = __builtin_amdgcn_readfirstlane(kept ? bucket_rows(kept, e, C) : static_cast<int>(C));
   const int64_t n0 = static_cast<int64_t>(nt) * BNO;
 
   const int tid = threadIdx.x;
@@ -884,7 +890,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   e = __builtin_amdgcn_readfirstlane(e);
   m0 = __builtin_amdgcn_readfirstlane(m0);
   nt = __builtin_amdgcn_readfirstlane(nt);
-  const int rows = __builtin_amdgcn_readfirstlane(kept[e]);
+  const int rows = __builtin_amdgcn_readfirstlane(bucket_rows(kept, e, C));
   const int64_t n0 = static_cast<int64_t>(nt) * BNO;
   const int64_t nk = K / BK;  // even, at least 2
 
@@ -1031,7 +1037,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_skinny_kernel(
   if (mt >= mtile_off[E]) return;
   const int e = __builtin_amdgcn_readfirstlane(owner_expert(mtile_off, E, mt));
   const int m0 = __builtin_amdgcn_readfirstlane((mt - mtile_off[e]) * kSkinnyRows);
-  const int rows = __builtin_amdgcn_readfirstlane(kept[e]);
+  const int rows = __builtin_amdgcn_readfirstlane(bucket_rows(kept, e, C));
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t col0 = static_cast<int64_t>(nc) * 64 + wave * 16;
@@ -1110,7 +1116,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   if (mt >= mtile_off[E]) return;
   const int e = owner_expert(mtile_off, E, mt);
   const int m0 = (mt - mtile_off[e]) * BM;
-  const int rows = kept[e];
+  const int rows = bucket_rows(kept, e, C);
   const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
@@ -1173,14 +1179,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 // Block shape of the bf16 kernel: 256 x 256 once experts hold enough rows to
 // fill it, else 128 x 128.
-#ifndef MOE_BIG_TILE_MIN_C
-#define MOE_BIG_TILE_MIN_C 512
-#endif
-constexpr int kBigTileMinC = MOE_BIG_TILE_MIN_C;
-#ifndef MOE_BIG_TILE_MIN_C_GATE_UP
-#define MOE_BIG_TILE_MIN_C_GATE_UP 256
-#endif
-constexpr int kBigTileMinCGateUp = MOE_BIG_TILE_MIN_C_GATE_UP;
+constexpr int kBigTileMinC = 512;
+constexpr int kBigTileMinCGateUp = 256;
 
 // Row tiles of the skinny kernel when every expert holds this few rows.
 constexpr int kSkinnyMaxC = kSkinnyRows;
@@ -1265,22 +1265,10 @@ int resident_groups() {
 // Waves per work-group of the 256 x 256 kernel: row-major GEMMs, fp32-output
 // row GEMM (router scores), K-major B (backward dh, dX), K-major A and B
 // (weight gradients).
-#ifndef MOE_DMA_WAVES
-#define MOE_DMA_WAVES 8
-#endif
-#ifndef MOE_ROWS_F32_WAVES
-#define MOE_ROWS_F32_WAVES 8
-#endif
-#ifndef MOE_KMAJOR_WAVES
-#define MOE_KMAJOR_WAVES 8
-#endif
-#ifndef MOE_TN_WAVES
-#define MOE_TN_WAVES 8
-#endif
-constexpr int kDmaWaves = MOE_DMA_WAVES;
-constexpr int kRowsF32Waves = MOE_ROWS_F32_WAVES;
-constexpr int kKmajorWaves = MOE_KMAJOR_WAVES;
-constexpr int kTnWaves = MOE_TN_WAVES;
+constexpr int kDmaWaves = 8;
+constexpr int kRowsF32Waves = 8;
+constexpr int kKmajorWaves = 8;
+constexpr int kTnWaves = 8;
 
 template <int BM, int BN, bool SWIGLU>
 hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out, const int32_t* kept,
@@ -1361,7 +1349,7 @@ hipError_t launch_gemm_tn(const void* a, int64_t lda, int64_t a_es, int64_t aoff
   if (M % 8 || N % 8 || lda % 8 || aoff % 8 || aoff + M > lda) return hipErrorInvalidValue;
   const int64_t nt = ceil_div(N, 256);
   int64_t blocks = ceil_div(E * ceil_div(M, 256) * nt, 8) * 8;
-  if (MOE_PERSIST_AT) {  // one resident block per CU walks its XCD's tiles
+  if (kPersistAt) {  // one resident block per CU walks its XCD's tiles
     const int g = resident_groups();
     if (g > 0) blocks = std::min<int64_t>(blocks, g);
   }

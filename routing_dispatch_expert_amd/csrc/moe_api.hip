@@ -399,7 +399,7 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, false, s), "event");
   const int bm_gu = moe::grouped_gemm_bm_gate_up(bf16, C, d);
-  if (bm_gu != bm) MOE_HIP_TRY(moe::launch_mtile_map(kept, E, bm_gu, p.mtile_gu, s), "tile map (gate, up)");
+  if (bm_gu != bm) MOE_HIP_TRY(moe::launch_mtile_map(kept, E, C, bm_gu, p.mtile_gu, s), "tile map (gate, up)");
   MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, bm_gu != bm ? p.mtile_gu : p.mtile, W_gate, W_up, E, C, d, d_ff,
                                        bf16, p.h, s, nullptr, &p.split),
               "grouped gemm (gate, up)");
@@ -409,7 +409,7 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
               "grouped gemm (down)");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_COMBINE, false, s), "event");
-  MOE_HIP_TRY(moe::launch_combine(x, p.y, idx, w, slot, T, d, k, C, bf16, out, s), "combine");
+  MOE_HIP_TRY(moe::launch_combine(x, p.y, idx, w, slot, T, d, k, E, C, bf16, out, s), "combine");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_COMBINE, true, s), "event");
   return MOE_OK;
 }
@@ -480,7 +480,7 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   const int bm_d = moe::grouped_gemm_bm_contract_d(bf16, C, d);
   int32_t* mtile_d_rows = p.mtile;
   if (bm_d != bm) {
-    MOE_HIP_TRY(moe::launch_mtile_map(p.kept, E, bm_d, p.mtile_gu, s), "tile map");
+    MOE_HIP_TRY(moe::launch_mtile_map(p.kept, E, C, bm_d, p.mtile_gu, s), "tile map");
     mtile_d_rows = p.mtile_gu;
   }
   const int bmo_d = bf16 ? bm_d : 0;
@@ -555,8 +555,8 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
               "transpose X");
   MOE_HIP_TRY(moe::launch_fill_i32(b.kfull_d, E, static_cast<int32_t>(d), s), "fill");
   MOE_HIP_TRY(moe::launch_fill_i32(b.kfull_f, E, static_cast<int32_t>(F), s), "fill");
-  MOE_HIP_TRY(moe::launch_mtile_map(b.kfull_d, E, moe::grouped_gemm_bm(bf16, d), b.mtile_d, s), "tile map");
-  MOE_HIP_TRY(moe::launch_mtile_map(b.kfull_f, E, moe::grouped_gemm_bm(bf16, F), b.mtile_f, s), "tile map");
+  MOE_HIP_TRY(moe::launch_mtile_map(b.kfull_d, E, d, moe::grouped_gemm_bm(bf16, d), b.mtile_d, s), "tile map");
+  MOE_HIP_TRY(moe::launch_mtile_map(b.kfull_f, E, F, moe::grouped_gemm_bm(bf16, F), b.mtile_f, s), "tile map");
   MOE_HIP_TRY(moe::launch_gemm_down(b.dyT, b.kfull_d, b.mtile_d, b.hT, E, d, F, b.Kp, bf16, dW_down, s),
               "gemm dW_down");
   MOE_HIP_TRY(moe::launch_gemm_down(b.dgT, b.kfull_f, b.mtile_f, b.XT, E, F, d, b.Kp, bf16, dW_gate, s),
@@ -659,7 +659,7 @@ int moe_layer_forward_replicated(const void* x, const void* W_router, const floa
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, false, s), "event");
   const int bm_gu = moe::grouped_gemm_bm_gate_up(bf16, C, d);
-  if (bm_gu != bm) MOE_HIP_TRY(moe::launch_mtile_map(kept, R, bm_gu, p.mtile_gu, s), "tile map (gate, up)");
+  if (bm_gu != bm) MOE_HIP_TRY(moe::launch_mtile_map(kept, R, C, bm_gu, p.mtile_gu, s), "tile map (gate, up)");
   MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, bm_gu != bm ? p.mtile_gu : p.mtile, W_gate, W_up, R, C, d, d_ff,
                                        bf16, p.h, s, p.wmap, &p.split),
               "grouped gemm (gate, up)");
@@ -669,7 +669,7 @@ int moe_layer_forward_replicated(const void* x, const void* W_router, const floa
               "grouped gemm (down)");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_COMBINE, false, s), "event");
-  MOE_HIP_TRY(moe::launch_combine(x, p.y, inst, w, slot, T, d, k, C, bf16, out, s), "combine");
+  MOE_HIP_TRY(moe::launch_combine(x, p.y, inst, w, slot, T, d, k, R, C, bf16, out, s), "combine");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_COMBINE, true, s), "event");
   return MOE_OK;
 }
@@ -798,8 +798,8 @@ int moe_grouped_gemm(const void* buckets, const int32_t* kept_count, const void*
   auto* mtile_gu = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + map_bytes);
   const moe::SplitK sk = moe::split_k_carve(static_cast<char*>(workspace) + 2 * map_bytes);
   const int bm = moe::grouped_gemm_bm_down(bf16, C, d_ff);
-  MOE_HIP_TRY(moe::launch_mtile_map(kept_count, E, bm, mtile, s), "tile map");
-  MOE_HIP_TRY(moe::launch_mtile_map(kept_count, E, moe::grouped_gemm_bm_gate_up(bf16, C, d), mtile_gu, s), "tile map");
+  MOE_HIP_TRY(moe::launch_mtile_map(kept_count, E, C, bm, mtile, s), "tile map");
+  MOE_HIP_TRY(moe::launch_mtile_map(kept_count, E, C, moe::grouped_gemm_bm_gate_up(bf16, C, d), mtile_gu, s), "tile map");
   MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept_count, mtile_gu, W_gate, W_up, E, C, d, d_ff, bf16, h, s,
                                        nullptr, &sk),
               "grouped gemm (gate, up)");
@@ -822,7 +822,7 @@ int moe_combine(const void* x, const void* y, const int32_t* topk_idx, const flo
   const size_t row = static_cast<size_t>(d) * elem_bytes(dtype);
   if (overlaps(x, T * row, out, T * row)) return fail(MOE_ERR_INVALID_ARG, "out overlaps x");
   if (T == 0) return MOE_OK;
-  MOE_HIP_TRY(moe::launch_combine(x, y, topk_idx, topk_w, slot, T, d, k, C, dtype == MOE_DTYPE_BF16, out,
+  MOE_HIP_TRY(moe::launch_combine(x, y, topk_idx, topk_w, slot, T, d, k, E, C, dtype == MOE_DTYPE_BF16, out,
                                   static_cast<hipStream_t>(stream)),
               "combine");
   return MOE_OK;

@@ -22,7 +22,7 @@ namespace moe {
 namespace {
 
 // Per-tile expert histogram: tile_cnt[b][e] = copies of expert e among tokens
-// [64 b, 64 b + 64).
+// [64 b, 64 b + 64). Entries outside [0, E) are counted nowhere (dropped).
 __global__ __launch_bounds__(256) void tile_hist_kernel(const int32_t* __restrict__ idx,
                                                         int64_t T, int k, int E,
                                                         int32_t* __restrict__ tile_cnt) {
@@ -32,7 +32,10 @@ __global__ __launch_bounds__(256) void tile_hist_kernel(const int32_t* __restric
   const int n = static_cast<int>(min<int64_t>(kTileTokens, T - t0)) * k;
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
-  for (int i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&hist[idx[t0 * k + i]], 1);
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int e = idx[t0 * k + i];
+    if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&hist[e], 1);
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) tile_cnt[b * E + e] = hist[e];
 }
@@ -147,11 +150,14 @@ __global__ __launch_bounds__(1024) void scan_finalize_kernel(
   if (mtile_off) mtile_prefix(kept_s, E, bm, mtile_off, sh);
 }
 
-__global__ __launch_bounds__(1024) void mtile_map_kernel(const int32_t* __restrict__ kept, int E,
+// Row-tile map from counts given by the caller: each count is clamped to
+// [0, C] first, so no tile starts past an expert's bucket.
+__global__ __launch_bounds__(1024) void mtile_map_kernel(const int32_t* __restrict__ kept, int E, int64_t C,
                                                          int bm, int32_t* __restrict__ mtile_off) {
   __shared__ int kept_s[4096];
   __shared__ int sh[17];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) kept_s[e] = kept[e];
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    kept_s[e] = static_cast<int>(min(max(static_cast<int64_t>(kept[e]), int64_t{0}), C));
   __syncthreads();
   mtile_prefix(kept_s, E, bm, mtile_off, sh);
 }
@@ -206,8 +212,9 @@ __global__ __launch_bounds__(64) void slots_kernel(const int32_t* __restrict__ i
     const int base = c * 64;
     if (base >= ncp) break;
     const int i = base + lane;
-    const bool active = i < ncp;
-    const int e = ev[c];
+    const bool valid = static_cast<unsigned>(ev[c]) < static_cast<unsigned>(E);  // else dropped
+    const bool active = i < ncp && valid;
+    const int e = valid ? ev[c] : 0;
     unsigned long long mask = __ballot(active);
     for (int bit = 0; bit < nbits; ++bit) {
       const bool set = (e >> bit) & 1;
@@ -219,6 +226,10 @@ __global__ __launch_bounds__(64) void slots_kernel(const int32_t* __restrict__ i
     __syncthreads();
     if (active && (63 - __clzll(mask)) == lane) cnt[e] = s + 1;
     __syncthreads();
+    if (i < ncp && !valid) {
+      slot[t0 * k + i] = -1;
+      sbuf[i] = -1;
+    }
     if (active) {
       const int sl = s < C ? s : -1;
       slot[t0 * k + i] = sl;
@@ -362,8 +373,8 @@ hipError_t launch_scan(const int32_t* tile_cnt, int64_t nt, int E, int64_t C, in
   return hipGetLastError();
 }
 
-hipError_t launch_mtile_map(const int32_t* kept, int E, int bm, int32_t* mtile_off, hipStream_t s) {
-  mtile_map_kernel<<<dim3(1), dim3(1024), 0, s>>>(kept, E, bm, mtile_off);
+hipError_t launch_mtile_map(const int32_t* kept, int E, int64_t C, int bm, int32_t* mtile_off, hipStream_t s) {
+  mtile_map_kernel<<<dim3(1), dim3(1024), 0, s>>>(kept, E, C, bm, mtile_off);
   return hipGetLastError();
 }
 

@@ -375,8 +375,10 @@ hipError_t route_dispatch(const RouteArgs& a, hipStream_t s) {
 // grouped GEMM's 256 x 256 LDS-DMA tiles with fp32 output, so each tile of
 // router weights is read once per 256 tokens, not once per 16. (With fewer
 // than 128 experts most of a 256-wide tile would be padding.)
+// The GEMM kernel addresses x as one buffer of 32-bit byte offsets, so x must
+// stay below 2^31 bytes there; larger batches keep the wave kernel.
 static bool router_on_gemm(int64_t T, int64_t d, int E, bool bf16) {
-  return bf16 && E >= 128 && E % 8 == 0 && T >= 256 && d % 128 == 0;
+  return bf16 && E >= 128 && E % 8 == 0 && T >= 256 && d % 128 == 0 && T * d * 2 < (int64_t{1} << 31);
 }
 
 // Token tiles of 16 per wave of the score kernel: the largest of 4 and 2 that

@@ -89,3 +89,34 @@ def logits_tolerance(x64: np.ndarray, wr64: np.ndarray, bias) -> np.ndarray:
     if bias is not None:
         tol = tol + 2 * U * (mag + np.abs(np.asarray(bias, np.float64))[None, :])
     return tol + 1e-30
+
+
+GUARD_WORDS = 4096   # canary elements after each guarded output
+
+
+class Guarded:
+    """Device outputs followed by canary regions: each array is the head of a
+    larger buffer whose tail holds a fixed pattern, so a write past the end of
+    an output shows up as a changed tail."""
+
+    def __init__(self):
+        self._tails = []
+
+    def empty(self, shape, dtype, name):
+        n = int(np.prod(shape)) if len(shape) else 1
+        buf = torch.empty(n + GUARD_WORDS, dtype=dtype, device="cuda")
+        if dtype in (torch.int32, torch.int64):
+            buf.fill_(-0x5A5A5A5)
+        elif dtype == torch.bfloat16:
+            buf.view(torch.int16).fill_(0x5A5A)
+        else:
+            buf.fill_(-1234.5)
+        tail = buf[n:]
+        self._tails.append((name, tail, tail.clone()))
+        return buf[:n].view(shape)
+
+    def check(self):
+        for name, tail, want in self._tails:
+            a = tail.view(torch.int16) if tail.dtype == torch.bfloat16 else tail
+            b = want.view(torch.int16) if want.dtype == torch.bfloat16 else want
+            assert torch.equal(a, b), f"{name}: written past its end"

@@ -2,7 +2,10 @@
 
 Every gradient is compared element by element on small shapes that cover each
 GEMM path (256- and 128-row tiles, the register-staged and decode kernels,
-fp32), capacity drops, a router bias and a rank limit.
+fp32), capacity drops, a router bias and a rank limit: dx per token (and its
+part beyond dout), the three expert-weight gradients per expert block, the
+router-weight gradient over the whole tensor. The named workloads are checked
+on sampled tokens and on sampled rows of the expert-weight gradients.
 """
 import numpy as np
 import pytest
@@ -10,7 +13,7 @@ import pytest
 import moe_inputs
 import oracle
 import routing_dispatch_expert_amd as moe
-from tests.gpu_util import bits_to_f64, gpu_available, say, to_dev, to_host
+from tests.gpu_util import bits_to_f64, gpu_available, row_rel_err, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -48,6 +51,29 @@ def _rel(got, ref):
     return float(np.abs(got - ref).max() / (den if den > 0 else 1.0))
 
 
+def _block_err(got, ref):
+    """Per expert block (first axis): max|got - ref| / max|ref| within the block,
+    the worst block returned. A block whose reference is exactly zero (an
+    expert that kept no row) must come back exactly zero."""
+    g, r = got.reshape(got.shape[0], -1), ref.reshape(ref.shape[0], -1)
+    den, err = np.abs(r).max(1), np.abs(g - r).max(1)
+    zero = den == 0
+    assert np.all(err[zero] == 0), "a gradient block of an expert with no kept row is not zero"
+    return float((err[~zero] / den[~zero]).max()) if np.any(~zero) else 0.0
+
+
+def _dx_err(got, ref, dout64, dtype):
+    """Per token: max|got - ref| / max|ref|, and the same for the layer's own
+    part of dx (dx - dout) measured against that part, with a floor of
+    2^-8 max|dx_t| (dx is rounded once to the output type, at most 2^-9 of
+    |dx| for bf16, plus the fp32 sums before it)."""
+    whole = row_rel_err(got, ref)
+    floor = (2.0 ** -8 if dtype == "bf16" else 2.0 ** -22) * np.abs(ref).max(1)
+    part_ref = np.abs(ref - dout64).max(1)
+    part = np.abs((got - dout64) - (ref - dout64)).max(1) / np.maximum(part_ref, floor)
+    return float(whole.max()), float(part.max())
+
+
 @pytest.mark.parametrize("case", range(len(BACK_CASES)))
 def test_backward_small_shapes_every_element(case):
     cfg = dict(BACK_CASES[case])
@@ -65,7 +91,11 @@ def test_backward_small_shapes_every_element(case):
     torch.cuda.synchronize()
     got = {key: bits_to_f64(to_host(r[name], dt), dt) for key, name in
            (("dx", "dx"), ("dwr", "dW_router"), ("dwg", "dW_gate"), ("dwu", "dW_up"), ("dwd", "dW_down"))}
-    errs = {key: _rel(got[key], ref[key]) for key in got}
+    errs = {}
+    errs["dx"], errs["dx-dout"] = _dx_err(got["dx"], ref["dx"], bits_to_f64(dout, dt), dt)
+    for key in ("dwg", "dwu", "dwd"):
+        errs[key] = _block_err(got[key], ref[key])   # per expert
+    errs["dwr"] = _rel(got["dwr"], ref["dwr"])
     if b is not None:
         errs["db"] = _rel(r["d_bias"].cpu().numpy().astype(np.float64), ref["db"])
     say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))

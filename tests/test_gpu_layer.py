@@ -2,8 +2,11 @@
 
 Small shapes are compared on every output element; the named workloads at
 their full sizes are compared bit for bit on all routing outputs (indices,
-counts, slots, drop masks, inverse map, statistics, send-buffer rows) and on
-the layer output of sampled tokens, which the oracle computes one by one.
+counts, slots, drop masks, inverse map, statistics, every expert's
+send-buffer rows) and on the layer output of every token (1024 tokens of the
+two DeepSeek-V3-shaped prefill batches), plus every kept row of both expert
+GEMMs (32 experts on the DeepSeek-V3 prefill shapes). Every output array is
+followed by a canary region that must come back unchanged.
 Layer output metric: per token max|got - ref| / max|ref|, at most 2e-2 for
 bf16 and 1e-4 for fp32.
 """
@@ -13,7 +16,8 @@ import pytest
 import moe_inputs
 import oracle
 import routing_dispatch_expert_amd as moe
-from tests.gpu_util import DeviceWeights, bits_to_f64, gpu_available, row_rel_err, say, to_dev, to_host
+from tests.gpu_util import (DeviceWeights, Guarded, bits_to_f64, gpu_available, row_rel_err, say, to_dev,
+                            to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,10 +33,26 @@ def _gpu():
 
 
 def run_layer(wl, wg, wu, wd, want_buckets=True):
+    """moe_layer_forward with every output (and the buckets) in guarded buffers."""
+    T, d, E, k, P = wl.T, wl.d, wl.E, wl.k, wl.P
+    x = to_dev(wl.x, wl.dtype)
+    C = moe.moe_capacity(T, E, k, wl.cf)
+    g = Guarded()
+    tdt = x.dtype
+    r = {"C": C, "out": g.empty((T, d), tdt, "out"), "topk_idx": g.empty((T, k), torch.int32, "topk_idx"),
+         "topk_w": g.empty((T, k), torch.float32, "topk_w"), "slot": g.empty((T, k), torch.int32, "slot"),
+         "src": g.empty((E, C), torch.int32, "src"), "routed_count": g.empty((E,), torch.int32, "routed"),
+         "kept_count": g.empty((E,), torch.int32, "kept"), "send_count": g.empty((P,), torch.int32, "send"),
+         "totals": g.empty((4,), torch.int64, "totals")}
+    if want_buckets:
+        r["buckets"] = g.empty((E, C, d), tdt, "buckets")
     b = None if wl.bias_vec is None else torch.from_numpy(wl.bias_vec).cuda()
-    r = moe.forward(to_dev(wl.x, wl.dtype), to_dev(wl.wr, wl.dtype), wg, wu, wd, wl.k, wl.cf, P=wl.P,
-                    router_bias=b, want_buckets=want_buckets, want_src=True, max_ranks=wl.max_ranks)
+    n = moe.moe_workspace_size(T, d, wl.d_ff, E, k, wl.cf, P, wl.dtype)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+    moe.moe_layer_forward(x, to_dev(wl.wr, wl.dtype), b, wg, wu, wd, T, d, wl.d_ff, E, k, wl.cf, P, wl.max_ranks,
+                          wl.dtype, r["out"], r, ws, n)
     torch.cuda.synchronize()
+    g.check()
     return r
 
 
@@ -54,12 +74,16 @@ def check_routing(wl, r, ref):
     assert np.all(np.abs(w - ref["w"]) <= 2e-4 * ref["w"] + 1e-7), "topk_w"
 
 
-def check_buckets(wl, r, ref, experts):
+def check_buckets(wl, r, ref, experts=None):
+    """Kept bucket rows are bit copies of their tokens' rows (every expert
+    unless a subset is given)."""
     got = to_host(r["buckets"], wl.dtype)
-    k = wl.k
+    C, k = ref["C"], wl.k
+    src = ref["src"].reshape(-1, C)
+    experts = range(wl.E) if experts is None else experts
     for e in experts:
         n = ref["kept"][e]
-        rows = ref["src"][e * ref["C"]: e * ref["C"] + n] // k
+        rows = src[e, :n] // k
         assert np.array_equal(got[e, :n].view(np.uint8), wl.x[rows].view(np.uint8)), f"bucket rows of expert {e}"
 
 
@@ -139,53 +163,74 @@ def _sample_tokens(wl, ref_slot, n_rand, seed):
     return np.array(sorted(picks))
 
 
-def check_expert_gemms_full(wl, r, host, dev):
+def check_expert_gemms_full(wl, r, host, dev, n_experts=None):
     """The stage GEMMs at the workload's full size, on the layer's own buckets
     and kept counts (so with the same tile lists and split rounds as the
-    layer): every kept row of h and y is written, no padding row is, and
-    sampled rows (first, last and one more of 8 experts) match the oracle."""
+    layer): every kept row of h and y is written, no padding row is, nothing
+    past either array is, and every kept row of every expert (of n_experts
+    experts, the fullest and emptiest touched ones among them, when given)
+    matches the oracle."""
     E, C, d, F = wl.E, r["C"], wl.d, wl.d_ff
     kept_dev = r["kept_count"]
     kept = kept_dev.cpu().numpy()
     bf = wl.dtype == "bf16"
+    g = Guarded()
 
-    def sentinel(shape):
+    def sentinel(shape, name):
+        t = g.empty(shape, torch.bfloat16 if bf else torch.float32, name)
         if bf:
-            return torch.full(shape, 0x1234, dtype=torch.int16, device="cuda").view(torch.bfloat16)
-        return torch.full(shape, 777.0, dtype=torch.float32, device="cuda")
+            t.view(torch.int16).fill_(0x1234)
+        else:
+            t.fill_(777.0)
+        return t
 
-    h, y = sentinel((E, C, F)), sentinel((E, C, d))
+    h, y = sentinel((E, C, F), "h"), sentinel((E, C, d), "y")
     ws_n = moe.moe_grouped_gemm_workspace_size(E, C)
     ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
     moe.moe_grouped_gemm(r["buckets"], kept_dev, *dev, E, C, d, F, wl.dtype, h, y, ws, ws_n)
     torch.cuda.synchronize()
+    g.check()
     live = torch.arange(C, device="cuda")[None, :] < kept_dev[:, None].long()
     for name, t in (("h", h), ("y", y)):
         is_sent = (t.view(torch.int16) == 0x1234) if bf else (t == 777.0)
         assert not is_sent.any(-1)[live].any().item(), f"{name}: a kept row left (partly) unwritten"
         assert is_sent.all(-1)[~live].all().item(), f"{name}: a padding row written"
-    rng = np.random.default_rng(wl.seed + 5)
-    experts = set(rng.choice(E, size=min(7, E), replace=False).tolist()) | {int(np.argmax(kept))}
+    touched = np.nonzero(kept > 0)[0]
+    if n_experts is None or n_experts >= touched.size:
+        experts = touched.tolist()
+    else:
+        rng = np.random.default_rng(wl.seed + 5)
+        pick = {int(touched[np.argmax(kept[touched])]), int(touched[np.argmin(kept[touched])])}
+        rest = [int(e) for e in touched if int(e) not in pick]
+        pick |= set(rng.choice(rest, size=n_experts - len(pick), replace=False).tolist())
+        experts = sorted(pick)
     tol_h, tol_y = (4e-3, 1e-2) if bf else (1e-5, 1e-5)
-    for e in sorted(experts):
+    src = r["src"].cpu().numpy()
+    worst_h = worst_y = 0.0
+    n_rows = 0
+    for e in experts:
         n = int(kept[e])
-        if n == 0:
-            continue
-        rows = sorted({0, n - 1, int(rng.integers(0, n))})
-        X = bits_to_f64(to_host(r["buckets"][e, rows], wl.dtype), wl.dtype)
+        X = oracle.decode(wl.x[src[e, :n] // wl.k], wl.dtype)    # the tokens' rows, bit-checked in the buckets
         wg, wu, wd = (oracle.decode(a[e], wl.dtype) for a in host)
-        got_h = bits_to_f64(to_host(h[e, rows], wl.dtype), wl.dtype)
-        got_y = bits_to_f64(to_host(y[e, rows], wl.dtype), wl.dtype)
-        assert row_rel_err(got_h, oracle.expert_hidden(X, wg, wu)).max() <= tol_h, f"h rows {rows} of expert {e}"
-        assert row_rel_err(got_y, oracle.expert_mlp(X, wg, wu, wd)).max() <= tol_y, f"y rows {rows} of expert {e}"
-    say(f"  expert GEMMs at full size: all {int(kept.sum())} kept rows written; rows of {len(experts)} experts match")
+        got_h = bits_to_f64(to_host(h[e, :n], wl.dtype), wl.dtype)
+        got_y = bits_to_f64(to_host(y[e, :n], wl.dtype), wl.dtype)
+        eh = row_rel_err(got_h, oracle.expert_hidden(X, wg, wu)).max()
+        ey = row_rel_err(got_y, oracle.expert_mlp(X, wg, wu, wd)).max()
+        assert eh <= tol_h, f"h of expert {e}: {eh}"
+        assert ey <= tol_y, f"y of expert {e}: {ey}"
+        worst_h, worst_y, n_rows = max(worst_h, eh), max(worst_y, ey), n_rows + n
+    say(f"  expert GEMMs at full size: all {int(kept.sum())} kept rows written; {n_rows} rows of "
+        f"{len(experts)} experts match (h {worst_h:.2e}, y {worst_y:.2e})")
 
 
-WORKLOAD_SAMPLES = {"tiny_f32": None, "mixtral_prefill": 16, "deepseek_v3_prefill": 2,
-                    "deepseek_v3_node_limited": 2, "deepseek_v3_decode": 6, "zipf_skew_drops": 16}
+# tokens whose layer output the oracle computes (None: all of them), and the
+# experts whose GEMM rows it computes in full (None: every touched expert)
+WORKLOAD_TOKENS = {"tiny_f32": None, "mixtral_prefill": None, "deepseek_v3_prefill": 1024,
+                   "deepseek_v3_node_limited": 1024, "deepseek_v3_decode": None, "zipf_skew_drops": None}
+WORKLOAD_GEMM_EXPERTS = {"deepseek_v3_prefill": 32, "deepseek_v3_node_limited": 32}
 
 
-@pytest.mark.parametrize("name", list(WORKLOAD_SAMPLES))
+@pytest.mark.parametrize("name", list(WORKLOAD_TOKENS))
 def test_named_workload(name):
     wl = moe_inputs.workload(name)
     say(f"workload {name}: T={wl.T} d={wl.d} E={wl.E} k={wl.k} d_ff={wl.d_ff} cf={wl.cf} P={wl.P} "
@@ -196,16 +241,15 @@ def test_named_workload(name):
     ref_route = oracle.layer_forward(wl.x, wl.wr, lambda e: (host[0][e], host[1][e], host[2][e]), wl.T, wl.d,
                                      wl.d_ff, wl.E, wl.k, wl.cf, wl.dtype, P=wl.P, bias=wl.bias_vec,
                                      tokens=np.arange(0), max_ranks=wl.max_ranks)
-    n = WORKLOAD_SAMPLES[name]
+    n = WORKLOAD_TOKENS[name]
     tokens = None if n is None else _sample_tokens(wl, ref_route["slot"], n, seed=wl.seed)
     ref = oracle.layer_forward(wl.x, wl.wr, lambda e: (host[0][e], host[1][e], host[2][e]), wl.T, wl.d, wl.d_ff,
                                wl.E, wl.k, wl.cf, wl.dtype, P=wl.P, bias=wl.bias_vec, tokens=tokens,
                                max_ranks=wl.max_ranks)
     check_routing(wl, r, ref)
-    rng = np.random.default_rng(3)
-    check_buckets(wl, r, ref, sorted(set(rng.choice(wl.E, size=min(8, wl.E), replace=False).tolist())))
+    check_buckets(wl, r, ref)
     check_out(wl, r, ref)
-    check_expert_gemms_full(wl, r, host, dev)
+    check_expert_gemms_full(wl, r, host, dev, WORKLOAD_GEMM_EXPERTS.get(name))
     if wl.max_ranks:
         ranks = r["topk_idx"].cpu().numpy() // (wl.E // wl.P)
         assert max(len(set(row)) for row in ranks.tolist()) <= wl.max_ranks

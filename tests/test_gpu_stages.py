@@ -10,7 +10,8 @@ import pytest
 import moe_inputs
 import oracle
 import routing_dispatch_expert_amd as moe
-from tests.gpu_util import U, bits_to_f64, gpu_available, logits_tolerance, row_rel_err, say, to_dev, to_host
+from tests.gpu_util import (U, Guarded, bits_to_f64, gpu_available, logits_tolerance, row_rel_err, say, to_dev,
+                            to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -163,13 +164,17 @@ def test_permute_is_exact(T, E, k, cf, P, d, dtype, skew):
     eb = 2 if dtype == "bf16" else 4
     sentinel = 0x7F7F if dtype == "bf16" else np.float32(-12345.5)
     buckets = to_dev(np.full((E, C, d), sentinel, dtype=np.uint16 if dtype == "bf16" else np.float32), dtype)
-    slot, src, routed, kept, send = _i32(T, k), _i32(E, C), _i32(E), _i32(E), _i32(P)
-    totals = torch.empty(4, dtype=torch.int64, device="cuda")
+    g = Guarded()
+    slot, src = g.empty((T, k), torch.int32, "slot"), g.empty((E, C), torch.int32, "src")
+    routed, kept, send = g.empty((E,), torch.int32, "routed"), g.empty((E,), torch.int32, "kept"), \
+        g.empty((P,), torch.int32, "send")
+    totals = g.empty((4,), torch.int64, "totals")
     ws_n = moe.moe_permute_workspace_size(T, E)
     ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
     moe.moe_permute(to_dev(x, dtype), torch.from_numpy(idx).cuda(), T, d, E, k, C, P, dtype, buckets, slot,
                     src, routed, kept, send, totals, ws, ws_n)
     torch.cuda.synchronize()
+    g.check()
     assert np.array_equal(slot.cpu().numpy(), slot_r)
     assert np.array_equal(src.cpu().numpy().reshape(-1), src_r)
     assert np.array_equal(routed.cpu().numpy(), routed_r)
@@ -205,6 +210,9 @@ GEMM_CASES = [
     # more than 8 whole tiles, not a multiple of 8, no split (one stage pair):
     # every XCD slot of the tile spread must still run
     (3, 600, 128, 640, "bf16"),
+    # SwiGLU over 64 or more column tiles (d_ff >= 8192) on 320-row tiles: the
+    # instantiation that requests each stage at the start of the one before
+    (2, 300, 256, 8192, "bf16"),
 ]
 
 
@@ -308,3 +316,140 @@ def test_zero_tokens_is_a_no_op():
     moe.moe_combine(out, out, _i32(1), _f32(1), _i32(1), 0, 4, 8, 2, 1, "f32", out)
     torch.cuda.synchronize()
     assert torch.all(out == 3.0)
+
+
+# ------------------------------------------------- indices given by a caller ---
+
+def test_grouped_gemm_clamps_counts_to_the_capacity():
+    """kept counts above C process the C rows of the bucket, negative ones none;
+    nothing is written past h or y."""
+    E, C, d, F = 4, 300, 256, 384
+    kept = np.array([C + 77, -5, 130, 1 << 30], np.int32)
+    eff = np.clip(kept, 0, C)
+    wl = moe_inputs.custom(T=E * C, d=d, E=E, k=1, d_ff=F, cf=1.0, seed=61, reject=False)
+    X = wl.x.reshape(E, C, d)
+    wg, wu, wd = wl.all_expert_weights()
+    g = Guarded()
+    h = g.empty((E, C, F), torch.bfloat16, "h")
+    y = g.empty((E, C, d), torch.bfloat16, "y")
+    h.view(torch.int16).fill_(0x1234)
+    y.view(torch.int16).fill_(0x1234)
+    ws_n = moe.moe_grouped_gemm_workspace_size(E, C)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    moe.moe_grouped_gemm(to_dev(X, "bf16"), torch.from_numpy(kept).cuda(), to_dev(wg, "bf16"), to_dev(wu, "bf16"),
+                         to_dev(wd, "bf16"), E, C, d, F, "bf16", h, y, ws, ws_n)
+    torch.cuda.synchronize()
+    g.check()
+    hg, yg = to_host(h, "bf16"), to_host(y, "bf16")
+    for e in range(E):
+        n = int(eff[e])
+        if n:
+            Xe = bits_to_f64(X[e, :n], "bf16")
+            wge, wue, wde = (oracle.decode(a[e], "bf16") for a in (wg, wu, wd))
+            assert row_rel_err(bits_to_f64(hg[e, :n], "bf16"), oracle.expert_hidden(Xe, wge, wue)).max() <= 4e-3
+            assert row_rel_err(bits_to_f64(yg[e, :n], "bf16"), oracle.expert_mlp(Xe, wge, wue, wde)).max() <= 1e-2
+        assert np.all(hg[e, n:] == 0x1234) and np.all(yg[e, n:] == 0x1234), f"rows past {n} of expert {e}"
+
+
+def test_combine_treats_out_of_range_copies_as_dropped():
+    T, d, E, k, C = 300, 64, 8, 3, 60
+    rng = np.random.default_rng(71)
+    idx = _random_routes(rng, T, E, k, skew=False)
+    w = rng.random((T, k)).astype(np.float32)
+    slot, _, _, _ = oracle.assign_slots(idx, E, C)
+    bad_idx, bad_slot = idx.copy(), slot.copy()
+    bad_idx[5, 0], bad_idx[6, 1], bad_slot[7, 2], bad_slot[8, 0] = E, -3, C, C + 1000
+    bad_idx[9, :], bad_slot[10, :] = E + 1, C            # whole tokens: passed through
+    eff = np.where((bad_idx >= 0) & (bad_idx < E) & (bad_slot < C), bad_slot, -1)
+    wl = moe_inputs.custom(T=T, d=d, E=E, k=k, d_ff=8, cf=1.0, seed=72, reject=False)
+    ybits = moe_inputs.custom(T=E * C, d=d, E=E, k=k, d_ff=8, cf=1.0, seed=73, reject=False).x.reshape(E, C, d)
+    y64, x64 = bits_to_f64(ybits, "bf16"), bits_to_f64(wl.x, "bf16")
+    ycop = np.zeros((T, k, d))
+    for t, j in zip(*np.nonzero(eff >= 0)):
+        ycop[t, j] = y64[idx[t, j], eff[t, j]]
+    ref = oracle.combine(x64, ycop, w, eff)
+    g = Guarded()
+    out = g.empty((T, d), torch.bfloat16, "out")
+    moe.moe_combine(to_dev(wl.x, "bf16"), to_dev(ybits, "bf16"), torch.from_numpy(bad_idx).cuda(),
+                    torch.from_numpy(w).cuda(), torch.from_numpy(bad_slot).cuda(), T, d, E, k, C, "bf16", out)
+    torch.cuda.synchronize()
+    g.check()
+    got = to_host(out, "bf16")
+    dropped = np.all(eff < 0, axis=1)
+    assert dropped[9] and dropped[10]
+    assert np.array_equal(got[dropped].view(np.uint8), wl.x[dropped].view(np.uint8))
+    mag = np.abs(x64) + np.einsum("tj,tjd->td", np.where(eff >= 0, w, 0.0), np.abs(ycop))
+    tol = 2.0 ** -8 * np.abs(ref) + (k + 2) * U * mag + 1e-30
+    assert np.all(np.abs(bits_to_f64(got, "bf16") - ref)[~dropped] <= tol[~dropped])
+
+
+def test_permute_drops_out_of_range_experts():
+    """An expert index outside [0, E) is dropped (slot -1) and counted in no
+    expert: the result equals the permutation of the remaining copies, which
+    the oracle gives when those copies go to one extra expert that keeps
+    none of them."""
+    T, E, k, P, d = 500, 16, 4, 4, 64
+    rng = np.random.default_rng(81)
+    idx = _random_routes(rng, T, E, k, skew=True)
+    C = oracle.capacity(T, E, k, 1.0)
+    bad = idx.copy()
+    bad[3, 1], bad[100, 0], bad[101, 3] = E, -1, 1 << 20
+    bad[200, :] = E + 2                                      # a whole token
+    inval = (bad < 0) | (bad >= E)
+    as_extra = np.where(inval, E, bad).astype(np.int32)     # the remaining copies keep their order
+    slot_e, src_e, routed_e, kept_e = oracle.assign_slots(as_extra, E + 1, C)
+    slot_r = np.where(inval, -1, slot_e)
+    routed_r, kept_r = routed_e[:E], kept_e[:E]
+    src_r = src_e[:E * C]
+    st = oracle.routing_stats(slot_r, routed_r, kept_r, C, P, d, 2)
+    x = moe_inputs.custom(T=T, d=d, E=E, k=k, d_ff=8, cf=1.0, seed=82, reject=False).x
+    b_ref = oracle.dispatch_buckets(x, np.where(inval, 0, bad), slot_r, E, C)
+    g = Guarded()
+    buckets = g.empty((E, C, d), torch.bfloat16, "buckets")
+    slot, src = g.empty((T, k), torch.int32, "slot"), g.empty((E, C), torch.int32, "src")
+    routed, kept = g.empty((E,), torch.int32, "routed"), g.empty((E,), torch.int32, "kept")
+    send, totals = g.empty((P,), torch.int32, "send"), g.empty((4,), torch.int64, "totals")
+    ws_n = moe.moe_permute_workspace_size(T, E)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    moe.moe_permute(to_dev(x, "bf16"), torch.from_numpy(bad).cuda(), T, d, E, k, C, P, "bf16", buckets, slot, src,
+                    routed, kept, send, totals, ws, ws_n)
+    torch.cuda.synchronize()
+    g.check()
+    assert np.array_equal(slot.cpu().numpy(), slot_r)
+    assert np.array_equal(src.cpu().numpy().reshape(-1), src_r)
+    assert np.array_equal(routed.cpu().numpy(), routed_r)
+    assert np.array_equal(kept.cpu().numpy(), kept_r)
+    assert np.array_equal(send.cpu().numpy(), st["send_count"])
+    assert totals.cpu().numpy().tolist() == [st["dropped"], st["fully_dropped_tokens"], st["padded_rows"],
+                                             st["offrank_bytes"]]
+    got = to_host(buckets, "bf16")
+    for e in range(E):
+        assert np.array_equal(got[e, :kept_r[e]], b_ref[e, :kept_r[e]]), f"expert {e}"
+
+
+def test_router_scores_past_2gib_of_tokens():
+    """x of more than 2^31 bytes (DeepSeek-V3 width and expert count): the
+    scores are right for rows on both sides of that byte offset. x repeats a
+    seeded 4096-token batch, so every row's reference is its base row's."""
+    Tb, d, E, k = 4096, 7168, 256, 8
+    reps = 40                                   # 163840 tokens, 2.35e9 bytes of x
+    T = Tb * reps
+    assert T * d * 2 >= 1 << 31
+    wl = moe_inputs.custom(T=Tb, d=d, E=E, k=k, d_ff=8, cf=1.0, seed=91)
+    x64, wr64 = oracle.decode(wl.x, "bf16"), oracle.decode(wl.wr, "bf16")
+    l_ref = oracle.router_logits(x64, wr64, None)
+    idx_ref = oracle.topk_experts(l_ref, k)
+    x = to_dev(wl.x, "bf16").repeat(reps, 1)
+    logits, idx, w = _f32(T, E), _i32(T, k), _f32(T, k)
+    ws_n = moe.moe_router_workspace_size(T, d, E, "bf16")
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    moe.moe_router(x, to_dev(wl.wr, "bf16"), None, T, d, E, k, 1, 0, "bf16", idx, w, logits, ws, ws_n)
+    torch.cuda.synchronize()
+    del x
+    assert np.array_equal(idx.cpu().numpy(), np.tile(idx_ref, (reps, 1)))
+    tol = logits_tolerance(x64, wr64, None)
+    first_past = -(-(1 << 31) // (d * 2))       # first row that starts past 2^31 bytes
+    for t0 in (0, first_past - 2, T - Tb):
+        rows = np.arange(t0, t0 + Tb) % T
+        err = np.abs(logits[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64) - l_ref[rows % Tb])
+        assert np.all(err <= tol[rows % Tb]), (t0, float(np.max(err / tol[rows % Tb])))
