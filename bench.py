@@ -55,7 +55,8 @@ CPU_SAMPLE = {"deepseek_v3_prefill": 512, "deepseek_v3_node_limited": 512}
 # rocprofv3 counter passes, one run each: name, counters (within one pass's
 # hardware limits: FETCH_SIZE takes 3 TCC counters, WRITE_SIZE 2)
 PROFILE_PASSES = [("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE"),
-                  ("mfma", "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE"),
+                  ("mfma", "MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_WAVE_CYCLES SQ_WAIT_INST_ANY "
+                           "SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS"),
                   ("l2", "TCC_HIT_sum TCC_MISS_sum")]
 PROFILE_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc {counters} --output-format csv "
                "-d $OUT/{workload}/{name} -o run -- python $REPO/bench.py --workload {workload} --steps 2 --warmup 1 "
@@ -218,12 +219,14 @@ def counters_summary(root: str, workload: str) -> str:
     lines += ["", "HBM bytes: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by what each reads for the "
               f"reference copy kernel ({copy}, 1 GiB read + 1 GiB written):",
               f"  FETCH_SIZE factor {f_fac:.5f}, WRITE_SIZE factor {w_fac:.5f}",
-              "MFMA: SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 = executed bf16 matrix flops; SQ_VALU_MFMA_BUSY_CYCLES "
-              "over GRBM_GUI_ACTIVE x 1024 SIMDs = matrix-core busy fraction; GRBM_GUI_ACTIVE = GPU clock cycles "
-              "of the dispatch. L2 hit rate = TCC_HIT / (TCC_HIT + TCC_MISS).", "",
+              "MFMA: SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 = executed bf16 matrix flops; MfmaUtil = matrix-core "
+              "busy cycles summed over the 1024 SIMDs over (GRBM_GUI_ACTIVE x 1024), in %; wait = "
+              "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (share of wave time waiting to issue); LDS bank = "
+              "SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS (conflict cycles per LDS-active quad-cycle); "
+              "L2 hit = TCC_HIT / (TCC_HIT + TCC_MISS).", "",
               "Per dispatch (mean over the dispatches of the run):"]
     hdr = (f"{'kernel':62s} {'stage':8s} {'FETCH KiB':>11s} {'WRITE KiB':>11s} {'HBM bytes':>11s} "
-           f"{'MFMA flop':>11s} {'MFMA busy':>9s} {'cycles':>10s} {'L2 hit':>7s}")
+           f"{'MFMA flop':>11s} {'MfmaUtil':>8s} {'wait':>6s} {'LDS bank':>8s} {'L2 hit':>7s}")
     lines.append(hdr)
     per_stage = {}
     for k in passes["fetch"]:
@@ -232,12 +235,13 @@ def counters_summary(root: str, workload: str) -> str:
             return float(np.mean(v)) if v else float("nan")
         fk, wk = mean("fetch", "FETCH_SIZE"), mean("write", "WRITE_SIZE")
         hbm = (fk * f_fac + wk * w_fac) * 1024
-        mops, busy, gui = mean("mfma", "SQ_INSTS_VALU_MFMA_MOPS_BF16"), mean("mfma", "SQ_VALU_MFMA_BUSY_CYCLES"), \
-            mean("mfma", "GRBM_GUI_ACTIVE")
+        mops, util = mean("mfma", "SQ_INSTS_VALU_MFMA_MOPS_BF16"), mean("mfma", "MfmaUtil")
+        wait = mean("mfma", "SQ_WAIT_INST_ANY") / mean("mfma", "SQ_WAVE_CYCLES")
+        bank = mean("mfma", "SQ_LDS_BANK_CONFLICT") / mean("mfma", "SQ_ACTIVE_INST_LDS")
         hit, miss = mean("l2", "TCC_HIT_sum"), mean("l2", "TCC_MISS_sum")
         st = stage_of_kernel(k)
         lines.append(f"{k[:62]:62s} {st or '-':8s} {fk:11.1f} {wk:11.1f} {hbm:11.4e} {mops * 512:11.4e} "
-                     f"{busy / (gui * 1024) if gui > 0 else float('nan'):9.3f} {gui:10.0f} "
+                     f"{util:8.2f} {wait:6.3f} {bank:8.4f} "
                      f"{hit / (hit + miss) if hit + miss > 0 else float('nan'):7.3f}")
         if st:
             per_stage.setdefault(st, []).append(hbm)
