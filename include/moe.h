@@ -222,6 +222,21 @@ int moe_permute(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, in
                 int32_t* send_count, int64_t* totals, void* workspace, size_t workspace_bytes,
                 void* stream);
 
+/* moe_permute without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). Same arguments, results and errors as moe_permute; its
+ * scratch (what moe_permute_workspace_size() gives, at most 16 MiB) is a
+ * static buffer inside the library, one per GPU, held until the process
+ * ends. Larger T x E are rejected with MOE_ERR_UNSUPPORTED before any work is
+ * enqueued. The call allocates nothing. Every call on one GPU uses that GPU's
+ * buffer: calls whose work may overlap on the device (different streams, or
+ * different host threads without ordering) race and give unspecified
+ * results; calls ordered on one stream are safe. */
+int moe_permute_static(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, int32_t E,
+                       int32_t k, int64_t C, int32_t P, moe_dtype_t dtype, void* buckets,
+                       int32_t* slot, int32_t* src, int32_t* routed_count, int32_t* kept_count,
+                       int32_t* send_count, int64_t* totals, void* stream);
+
 /* Expert stage ([EP-guide] section 1, three matrices per expert; [EP-A2A]
  * "Tensor parallelism for experts", gate/up/down): for every expert e and
  * bucket row s < kept_count[e]:

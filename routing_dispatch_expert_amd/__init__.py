@@ -24,7 +24,7 @@ TOTALS = ("dropped", "fully_dropped_tokens", "padded_rows", "offrank_bytes")
 
 EXPORTS = ("moe_capacity", "moe_workspace_size", "moe_layer_forward", "moe_backward_workspace_size",
            "moe_layer_backward", "moe_replica_plan", "moe_replicated_workspace_size", "moe_layer_forward_replicated", "moe_router_workspace_size", "moe_router", "moe_route",
-           "moe_permute_workspace_size", "moe_permute", "moe_grouped_gemm_workspace_size",
+           "moe_permute_workspace_size", "moe_permute", "moe_permute_static", "moe_grouped_gemm_workspace_size",
            "moe_grouped_gemm", "moe_combine", "moe_set_stage_events", "moe_status_string", "moe_last_error")
 STAGES = ("router", "route", "slots", "scatter", "gate_up", "down", "combine")
 
@@ -62,6 +62,8 @@ _SIGS = {
     "moe_permute_workspace_size": [_I64, _I32, _P],
     "moe_permute": [_P, _P, _I64, _I64, _I32, _I32, _I64, _I32, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P,
                     _P, _SZ, _P],
+    "moe_permute_static": [_P, _P, _I64, _I64, _I32, _I32, _I64, _I32, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P,
+                           _P],
     "moe_grouped_gemm_workspace_size": [_I32, _I64, _P],
     "moe_grouped_gemm": [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P, _SZ, _P],
     "moe_combine": [_P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I64, ctypes.c_int, _P, _P],
@@ -238,6 +240,13 @@ def moe_permute(x, topk_idx, T, d, E, k, C, P, dtype, buckets, slot, src, routed
                              _ptr(slot), _ptr(src), _ptr(routed_count), _ptr(kept_count),
                              _ptr(send_count), _ptr(totals), _ptr(workspace), workspace_bytes,
                              _stream(stream)), "moe_permute")
+
+
+def moe_permute_static(x, topk_idx, T, d, E, k, C, P, dtype, buckets, slot, src, routed_count, kept_count,
+                       send_count, totals, stream=None):
+    _check(lib().moe_permute_static(_ptr(x), _ptr(topk_idx), T, d, E, k, C, P, _dtype(dtype), _ptr(buckets),
+                                    _ptr(slot), _ptr(src), _ptr(routed_count), _ptr(kept_count),
+                                    _ptr(send_count), _ptr(totals), _stream(stream)), "moe_permute_static")
 
 
 def moe_grouped_gemm_workspace_size(E, C) -> int:

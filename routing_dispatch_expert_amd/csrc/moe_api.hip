@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "common.h"
 
@@ -289,6 +290,69 @@ ReplPlan plan_replicated(void* ws, int64_t T, int64_t d, int64_t d_ff, int32_t E
 template <class T>
 T* pick(T* user, T* fallback) {
   return user ? user : fallback;
+}
+
+// Argument checks of the permutation entry points: on the host, before any
+// HIP call.
+int check_permute(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, int32_t E, int32_t k, int64_t C,
+                  int32_t P, moe_dtype_t dtype, const void* buckets, const int32_t* slot,
+                  const int32_t* routed_count, const int32_t* kept_count) {
+  if (!valid_dtype(dtype)) return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (T < 0 || d < 1 || E < 1 || k < 1 || k > E || C < 1)
+    return fail(MOE_ERR_INVALID_ARG, "need T >= 0, d >= 1, 1 <= k <= E, C >= 1");
+  if (P < 1 || E % P) return fail(MOE_ERR_INVALID_ARG, "P=%d must be >= 1 and divide E=%d", P, E);
+  int st = check_width(d, dtype, "d");
+  if (st != MOE_OK) return st;
+  if (E > kMaxE || k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "E or k too large");
+  if (T * k >= (int64_t{1} << 31) || E * C >= (int64_t{1} << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T*k and E*C must stay below 2^31");
+  if (!x || !topk_idx || !buckets || !slot || !routed_count || !kept_count)
+    return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
+  return MOE_OK;
+}
+
+// The permutation's launches over `scratch`, device memory of
+// moe_permute_workspace_size() bytes, 256-byte aligned.
+int run_permute(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, int32_t E, int32_t k, int64_t C,
+                int32_t P, moe_dtype_t dtype, void* buckets, int32_t* slot, int32_t* src, int32_t* routed_count,
+                int32_t* kept_count, int32_t* send_count, int64_t* totals, void* scratch, hipStream_t s) {
+  const int64_t nt = moe::ceil_div(T, moe::kTileTokens);
+  Carver c(scratch);
+  int32_t* tile_cnt = c.take<int32_t>(static_cast<size_t>(nt) * E);
+  int32_t* tile_off = c.take<int32_t>(static_cast<size_t>(nt) * E);
+  const int64_t eb = elem_bytes(dtype);
+  MOE_HIP_TRY(moe::launch_tile_hist(topk_idx, T, k, E, tile_cnt, s), "tile histogram");
+  MOE_HIP_TRY(moe::launch_scan(tile_cnt, nt, E, C, P, d * eb, k, T, tile_off, routed_count, kept_count,
+                               send_count, totals, 0, nullptr, src, s),
+              "scan");
+  MOE_HIP_TRY(moe::launch_slots(topk_idx, tile_off, T, k, E, C, slot, src, totals, s), "slots");
+  MOE_HIP_TRY(moe::launch_scatter_rows(x, topk_idx, slot, T, k, C, d * eb, buckets, s), "scatter");
+  return MOE_OK;
+}
+
+// Scratch of moe_permute_static, for callers that cannot allocate: one copy
+// per GPU (each device's module holds its own), kept until the process ends.
+// Host code never uses the array's name as an address: static_scratch()
+// asks the runtime for this device's copy once and keeps the pointer.
+constexpr size_t kStaticScratchBytes = size_t{16} << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(void** out) {
+  int dev = -1;
+  MOE_HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    MOE_HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 }  // namespace
@@ -737,35 +801,31 @@ int moe_permute(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, in
                 int64_t C, int32_t P, moe_dtype_t dtype, void* buckets, int32_t* slot, int32_t* src,
                 int32_t* routed_count, int32_t* kept_count, int32_t* send_count, int64_t* totals,
                 void* workspace, size_t workspace_bytes, void* stream) {
-  if (!valid_dtype(dtype)) return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", dtype);
-  if (T < 0 || d < 1 || E < 1 || k < 1 || k > E || C < 1)
-    return fail(MOE_ERR_INVALID_ARG, "need T >= 0, d >= 1, 1 <= k <= E, C >= 1");
-  if (P < 1 || E % P) return fail(MOE_ERR_INVALID_ARG, "P=%d must be >= 1 and divide E=%d", P, E);
-  int st = check_width(d, dtype, "d");
-  if (st != MOE_OK) return st;
-  if (E > kMaxE || k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "E or k too large");
-  if (T * k >= (int64_t{1} << 31) || E * C >= (int64_t{1} << 31))
-    return fail(MOE_ERR_UNSUPPORTED, "T*k and E*C must stay below 2^31");
-  if (!x || !topk_idx || !buckets || !slot || !routed_count || !kept_count)
-    return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
-  if (T == 0) return MOE_OK;
+  int st = check_permute(x, topk_idx, T, d, E, k, C, P, dtype, buckets, slot, routed_count, kept_count);
+  if (st != MOE_OK || T == 0) return st;
   size_t need;
   moe_permute_workspace_size(T, E, &need);
   if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % kAlign)
     return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned", need);
-  const int64_t nt = moe::ceil_div(T, moe::kTileTokens);
-  Carver c(workspace);
-  int32_t* tile_cnt = c.take<int32_t>(static_cast<size_t>(nt) * E);
-  int32_t* tile_off = c.take<int32_t>(static_cast<size_t>(nt) * E);
-  auto s = static_cast<hipStream_t>(stream);
-  const int64_t eb = elem_bytes(dtype);
-  MOE_HIP_TRY(moe::launch_tile_hist(topk_idx, T, k, E, tile_cnt, s), "tile histogram");
-  MOE_HIP_TRY(moe::launch_scan(tile_cnt, nt, E, C, P, d * eb, k, T, tile_off, routed_count, kept_count,
-                               send_count, totals, 0, nullptr, src, s),
-              "scan");
-  MOE_HIP_TRY(moe::launch_slots(topk_idx, tile_off, T, k, E, C, slot, src, totals, s), "slots");
-  MOE_HIP_TRY(moe::launch_scatter_rows(x, topk_idx, slot, T, k, C, d * eb, buckets, s), "scatter");
-  return MOE_OK;
+  return run_permute(x, topk_idx, T, d, E, k, C, P, dtype, buckets, slot, src, routed_count, kept_count, send_count,
+                     totals, workspace, static_cast<hipStream_t>(stream));
+}
+
+int moe_permute_static(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, int32_t E, int32_t k,
+                       int64_t C, int32_t P, moe_dtype_t dtype, void* buckets, int32_t* slot, int32_t* src,
+                       int32_t* routed_count, int32_t* kept_count, int32_t* send_count, int64_t* totals,
+                       void* stream) {
+  int st = check_permute(x, topk_idx, T, d, E, k, C, P, dtype, buckets, slot, routed_count, kept_count);
+  if (st != MOE_OK || T == 0) return st;
+  size_t need;
+  moe_permute_workspace_size(T, E, &need);
+  if (need > kStaticScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED, "T=%lld, E=%d need %zu bytes of scratch, more than the %zu of the static buffer",
+                static_cast<long long>(T), E, need, kStaticScratchBytes);
+  void* scr = nullptr;
+  if ((st = static_scratch(&scr)) != MOE_OK) return st;
+  return run_permute(x, topk_idx, T, d, E, k, C, P, dtype, buckets, slot, src, routed_count, kept_count, send_count,
+                     totals, scr, static_cast<hipStream_t>(stream));
 }
 
 int moe_grouped_gemm_workspace_size(int32_t E, int64_t C, size_t* bytes) {

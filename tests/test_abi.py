@@ -106,6 +106,7 @@ def test_zero_tokens_returns_ok_without_launching():
     moe.moe_router(FAKE, FAKE, None, 0, 128, 8, 2, 1, 0, "bf16", FAKE, FAKE, None, None, 0)
     assert moe.moe_router_workspace_size(64, 7168, 256, "bf16") >= 64 * 256 * 4
     moe.moe_permute(FAKE, FAKE, 0, 128, 8, 2, 20, 1, "bf16", FAKE, FAKE, None, FAKE, FAKE, None, None, None, 0)
+    moe.moe_permute_static(FAKE, FAKE, 0, 128, 8, 2, 20, 1, "bf16", FAKE, FAKE, None, FAKE, FAKE, None, None)
     moe.moe_combine(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 128, 8, 2, 20, "bf16", FAKE * 2)
 
 
@@ -124,6 +125,9 @@ def test_zero_tokens_returns_ok_without_launching():
                             FAKE * 3, 1 << 30),
     lambda: moe.moe_permute(FAKE, FAKE, 4, 128, 8, 2, 4, 1, "bf16", FAKE, FAKE, None, FAKE, FAKE, None, None,
                             None, 0),
+    lambda: moe.moe_permute_static(FAKE, FAKE, 4, 128, 8, 2, 0, 1, "bf16", FAKE, FAKE, None, FAKE, FAKE, None, None),
+    lambda: moe.moe_permute_static(FAKE, FAKE, 4, 128, 8, 2, 4, 3, "bf16", FAKE, FAKE, None, FAKE, FAKE, None, None),
+    lambda: moe.moe_permute_static(FAKE, None, 4, 128, 8, 2, 4, 1, "bf16", FAKE, FAKE, None, FAKE, FAKE, None, None),
     lambda: moe.moe_grouped_gemm(FAKE, FAKE, FAKE, FAKE, None, 8, 20, 128, 256, "bf16", FAKE, FAKE, FAKE * 3, 1 << 30),
     lambda: moe.moe_grouped_gemm(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 20, 128, 256, "bf16", FAKE, FAKE, None, 0),
     lambda: moe.moe_combine(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 128, 8, 2, 20, "bf16", FAKE),
@@ -160,3 +164,13 @@ def test_replicated_layer_rejects_bad_instance_counts(R):
     with pytest.raises(moe.MoeError):
         moe.moe_layer_forward_replicated(FAKE, FAKE, None, FAKE, FAKE, FAKE, 64, 128, 256, 8, 2, 1.25, 1, 0, None, 8,
                                          "bf16", FAKE * 2, None, FAKE * 3, 1 << 40)
+
+
+def test_static_permute_rejects_sizes_beyond_its_buffer_before_any_gpu_call():
+    # 65536 tokens x 4096 experts need 2 x 1024 x 4096 x 4 bytes of scratch (32 MiB)
+    assert moe.moe_permute_workspace_size(65536, 4096) > 16 << 20
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_permute_static(FAKE, FAKE, 65536, 128, 4096, 1, 16, 1, "bf16", FAKE, FAKE, None, FAKE, FAKE, None,
+                               None)
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+    assert "static buffer" in moe.moe_last_error()
