@@ -83,8 +83,8 @@ def parse():
                     help="time moe_layer_forward_replicated with EXTRA replicas dealt greedily to the most loaded "
                          "experts (counts from one plain forward of the same batch)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="first copy a buffer of this many MiB on the device (a reference kernel of known "
-                         "traffic for hardware counters)")
+                    help="first run a reference kernel of known traffic for hardware counters: read a buffer "
+                         "of this many MiB and write its bitwise complement to another")
     ap.add_argument("--device-weights", action="store_true",
                     help="draw the expert weights on the device (torch's seeded generator, the same laws) "
                          "instead of on the host: for counter passes, whose figures do not depend on the "
@@ -208,7 +208,10 @@ def counters_summary(root: str, workload: str) -> str:
     """Text summary of the counter passes of one workload (see PROFILE_PASSES)."""
     import numpy as np
     passes = {name: read_counter_csv(os.path.join(root, workload, name)) for name, _ in PROFILE_PASSES}
-    copy = next(k for k in passes["fetch"] if "copyBuffer" in k)
+    probes = [k for k in passes["fetch"] if "bitwise_not" in k]
+    if not probes:
+        raise RuntimeError("no reference kernel (bitwise_not of the 1 GiB probe) in the fetch pass")
+    copy = probes[0]
     f_fac = COPY_PROBE_KIB / np.mean(passes["fetch"][copy]["FETCH_SIZE"])
     w_fac = COPY_PROBE_KIB / np.mean(passes["write"][copy]["WRITE_SIZE"])
     lines = [f"rocprofv3 hardware counters of the MoE layer forward, workload {workload} (MI355X)", "",
@@ -217,7 +220,7 @@ def counters_summary(root: str, workload: str) -> str:
         lines.append("  " + PROFILE_CMD.format(counters=counters, workload=workload, name=name))
     lines.append(f"  python $REPO/bench.py --workload {workload} --counters-summary $OUT")
     lines += ["", "HBM bytes: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by what each reads for the "
-              f"reference copy kernel ({copy}, 1 GiB read + 1 GiB written):",
+              f"reference kernel ({copy[:60]}..., 1 GiB read + 1 GiB written):",
               f"  FETCH_SIZE factor {f_fac:.5f}, WRITE_SIZE factor {w_fac:.5f}",
               "MFMA: SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 = executed bf16 matrix flops; MfmaUtil = matrix-core "
               "busy cycles summed over the 1024 SIMDs over (GRBM_GUI_ACTIVE x 1024), in %; wait = "
@@ -391,8 +394,10 @@ def device_expert_weights(wl, torch, dev):
     out = []
     for shape, fan_in in (((wl.E, wl.d_ff, wl.d), wl.d), ((wl.E, wl.d_ff, wl.d), wl.d), ((wl.E, wl.d, wl.d_ff), wl.d_ff)):
         w = torch.empty(shape, dtype=dt, device=dev)
-        for e in range(wl.E):   # one expert at a time: no fp32 copy of the whole tensor
-            w[e] = (torch.randn(shape[1:], generator=g, device=dev) * (fan_in ** -0.5)).to(dt)
+        per = max(1, (1 << 28) // (shape[1] * shape[2]))   # experts per draw: at most 1 GiB of fp32
+        for e in range(0, wl.E, per):
+            n = min(per, wl.E - e)
+            w[e:e + n] = (torch.randn((n,) + shape[1:], generator=g, device=dev) * (fan_in ** -0.5)).to(dt)
         out.append(w)
     return tuple(out)
 
@@ -477,7 +482,7 @@ def main():
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.bitwise_not(src, out=dst)   # one elementwise kernel: reads and writes every byte once
         torch.cuda.synchronize()
         del src, dst
 

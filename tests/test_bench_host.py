@@ -14,7 +14,9 @@ GATE_UP = ("void moe::(anonymous namespace)::gemm_bf16_dma_kernel<true, false, f
            "(unsigned short const*, unsigned short const*, int, long)")
 DOWN = "void moe::(anonymous namespace)::gemm_bf16_dma_kernel<false, false, false, false, 8, 5, true>(int)"
 SCORES = "void moe::(anonymous namespace)::gemm_bf16_dma_kernel<false, false, true, false, 8, 4, true>(int)"
-COPY = "__amd_rocclr_copyBuffer"
+COPY = ("void at::native::vectorized_elementwise_kernel<16, at::native::bitwise_not_kernel_cuda(at::TensorIteratorBase&)"
+        "::{lambda(unsigned char)#1}, std::array<char*, 2ul> >(int, at::native::bitwise_not_kernel_cuda(at::TensorIteratorBase&)"
+        "::{lambda(unsigned char)#1}, std::array<char*, 2ul>)")
 
 
 def test_short_names_and_stages():
@@ -26,7 +28,8 @@ def test_short_names_and_stages():
     assert bench.stage_of_kernel("gemm_bf16_skinny_kernel<false>") == "down"
     assert bench.stage_of_kernel("scatter_rows_kernel<4>") == "scatter"
     assert bench.stage_of_kernel("combine_kernel<true, 4>") == "combine"
-    assert bench.stage_of_kernel(COPY) is None
+    assert bench.stage_of_kernel(bench.short_kernel_name(COPY)) is None
+    assert "bitwise_not" in bench.short_kernel_name(COPY)
 
 
 def _write_pass(folder, rows):
