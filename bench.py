@@ -238,9 +238,11 @@ def counters_summary(root: str, workload: str) -> str:
             return float(np.mean(v)) if v else float("nan")
         fk, wk = mean("fetch", "FETCH_SIZE"), mean("write", "WRITE_SIZE")
         hbm = (fk * f_fac + wk * w_fac) * 1024
+        def ratio(a, b):
+            return a / b if b > 0 else float("nan")
         mops, util = mean("mfma", "SQ_INSTS_VALU_MFMA_MOPS_BF16"), mean("mfma", "MfmaUtil")
-        wait = mean("mfma", "SQ_WAIT_INST_ANY") / mean("mfma", "SQ_WAVE_CYCLES")
-        bank = mean("mfma", "SQ_LDS_BANK_CONFLICT") / mean("mfma", "SQ_ACTIVE_INST_LDS")
+        wait = ratio(mean("mfma", "SQ_WAIT_INST_ANY"), mean("mfma", "SQ_WAVE_CYCLES"))
+        bank = ratio(mean("mfma", "SQ_LDS_BANK_CONFLICT"), mean("mfma", "SQ_ACTIVE_INST_LDS"))
         hit, miss = mean("l2", "TCC_HIT_sum"), mean("l2", "TCC_MISS_sum")
         st = stage_of_kernel(k)
         lines.append(f"{k[:62]:62s} {st or '-':8s} {fk:11.1f} {wk:11.1f} {hbm:11.4e} {mops * 512:11.4e} "
