@@ -56,7 +56,7 @@ CPU_SAMPLE = {"deepseek_v3_prefill": 512, "deepseek_v3_node_limited": 512}
 # hardware limits: FETCH_SIZE takes 3 TCC counters, WRITE_SIZE 2)
 PROFILE_PASSES = [("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE"),
                   ("mfma", "MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_WAVE_CYCLES SQ_WAIT_INST_ANY "
-                           "SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS"),
+                           "SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS GRBM_GUI_ACTIVE"),
                   ("l2", "TCC_HIT_sum TCC_MISS_sum")]
 PROFILE_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc {counters} --output-format csv "
                "-d $OUT/{workload}/{name} -o run -- python $REPO/bench.py --workload {workload} --steps 2 --warmup 1 "
@@ -197,10 +197,14 @@ def read_counter_csv(folder: str):
         with open(path, newline="") as f:
             for row in csv.DictReader(f):
                 k = short_kernel_name(row["Kernel_Name"])
-                out.setdefault(k, {}).setdefault(row["Counter_Name"], {}).setdefault(
-                    row.get("Dispatch_Id") or row.get("Correlation_Id"), 0.0)
-                out[k][row["Counter_Name"]][row.get("Dispatch_Id") or row.get("Correlation_Id")] += \
-                    float(row["Counter_Value"])
+                disp = row.get("Dispatch_Id") or row.get("Correlation_Id")
+                cs = out.setdefault(k, {})
+                cs.setdefault(row["Counter_Name"], {}).setdefault(disp, 0.0)
+                cs[row["Counter_Name"]][disp] += float(row["Counter_Value"])
+                try:   # the dispatch's duration (ns), as the profiled run timed it
+                    cs.setdefault("duration_ns", {})[disp] = float(int(row["End_Timestamp"]) - int(row["Start_Timestamp"]))
+                except (KeyError, ValueError):
+                    pass
     return {k: {c: list(v.values()) for c, v in cs.items()} for k, cs in out.items()}
 
 
@@ -226,10 +230,11 @@ def counters_summary(root: str, workload: str) -> str:
               "busy cycles summed over the 1024 SIMDs over (GRBM_GUI_ACTIVE x 1024), in %; wait = "
               "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (share of wave time waiting to issue); LDS bank = "
               "SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS (conflict cycles per LDS-active quad-cycle); "
-              "L2 hit = TCC_HIT / (TCC_HIT + TCC_MISS).", "",
+              "GHz = GRBM_GUI_ACTIVE (summed over the 8 XCDs) / 8 / the profiled dispatch's duration, the "
+              "clock the dispatch ran at; L2 hit = TCC_HIT / (TCC_HIT + TCC_MISS).", "",
               "Per dispatch (mean over the dispatches of the run):"]
     hdr = (f"{'kernel':62s} {'stage':8s} {'FETCH KiB':>11s} {'WRITE KiB':>11s} {'HBM bytes':>11s} "
-           f"{'MFMA flop':>11s} {'MfmaUtil':>8s} {'wait':>6s} {'LDS bank':>8s} {'L2 hit':>7s}")
+           f"{'MFMA flop':>11s} {'MfmaUtil':>8s} {'wait':>6s} {'LDS bank':>8s} {'GHz':>5s} {'L2 hit':>7s}")
     lines.append(hdr)
     per_stage = {}
     for k in passes["fetch"]:
@@ -243,10 +248,11 @@ def counters_summary(root: str, workload: str) -> str:
         mops, util = mean("mfma", "SQ_INSTS_VALU_MFMA_MOPS_BF16"), mean("mfma", "MfmaUtil")
         wait = ratio(mean("mfma", "SQ_WAIT_INST_ANY"), mean("mfma", "SQ_WAVE_CYCLES"))
         bank = ratio(mean("mfma", "SQ_LDS_BANK_CONFLICT"), mean("mfma", "SQ_ACTIVE_INST_LDS"))
+        ghz = ratio(mean("mfma", "GRBM_GUI_ACTIVE") / 8, mean("mfma", "duration_ns"))
         hit, miss = mean("l2", "TCC_HIT_sum"), mean("l2", "TCC_MISS_sum")
         st = stage_of_kernel(k)
         lines.append(f"{k[:62]:62s} {st or '-':8s} {fk:11.1f} {wk:11.1f} {hbm:11.4e} {mops * 512:11.4e} "
-                     f"{util:8.2f} {wait:6.3f} {bank:8.4f} "
+                     f"{util:8.2f} {wait:6.3f} {bank:8.4f} {ghz:5.2f} "
                      f"{hit / (hit + miss) if hit + miss > 0 else float('nan'):7.3f}")
         if st:
             per_stage.setdefault(st, []).append(hbm)

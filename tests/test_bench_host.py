@@ -59,6 +59,7 @@ def test_counter_summary_scales_by_the_copy_kernel(tmp_path):
     assert "FETCH_SIZE factor 2.00000" in txt and "WRITE_SIZE factor 1.00000" in txt
     line = next(l for l in txt.splitlines() if l.startswith("gemm_bf16_dma_kernel<true"))
     assert "gate_up" in line and "2.0726e+06" in line and "1.0240e+03" in line and "0.750" in line and "0.500" in line
+    assert line.split()[-2] == "nan"      # no GRBM_GUI_ACTIVE in this synthetic pass
     # gate/up: (1000 x 2 + 24) KiB
     assert f"gate_up_hbm_bytes_per_launch: {2024 * 1024:.6e}" in txt
     assert f"gate_up_sources_sha256: {bench.sources_sha('gate_up')}" in txt
