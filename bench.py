@@ -541,12 +541,14 @@ def main():
         for i, name in enumerate(moe.STAGES):
             ms = acc[i] / args.steps
             w = work[name]
+            # a stage with no kernels in it gets no rate
+            timed = ms > 1e-3
             s = {"ms": round(ms, 5), "algo_bytes": int(w["bytes"]),
-                 "GB_per_s": round(w["bytes"] / ms / 1e6, 1) if ms > 0 else None,
-                 "hbm_frac": round(w["bytes"] / ms / 1e6 / PEAK_HBM_GBS, 4) if ms > 0 else None}
+                 "GB_per_s": round(w["bytes"] / ms / 1e6, 1) if timed else None,
+                 "hbm_frac": round(w["bytes"] / ms / 1e6 / PEAK_HBM_GBS, 4) if timed else None}
             if w["flops"]:
-                s["TFLOP_per_s"] = round(w["flops"] / ms / 1e9, 1) if ms > 0 else None
-                s["mfma_frac"] = round(w["flops"] / ms / 1e9 / PEAK_TFLOPS[wl.dtype], 4) if ms > 0 else None
+                s["TFLOP_per_s"] = round(w["flops"] / ms / 1e9, 1) if timed else None
+                s["mfma_frac"] = round(w["flops"] / ms / 1e9 / PEAK_TFLOPS[wl.dtype], 4) if timed else None
             stages[name] = s
             print(f"[bench] stage {name:8s} {ms:8.4f} ms  " + " ".join(f"{a}={b}" for a, b in s.items()
                                                                        if a != "ms"), file=sys.stderr, flush=True)

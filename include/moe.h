@@ -273,7 +273,8 @@ int moe_combine(const void* x, const void* y, const int32_t* topk_idx, const flo
 enum {
   MOE_STAGE_ROUTER = 0,   /* scores on the matrix cores */
   MOE_STAGE_ROUTE = 1,    /* top-k and gates */
-  MOE_STAGE_SLOTS = 2,    /* tile histogram, scan, capacity, counts, slots */
+  MOE_STAGE_SLOTS = 2,    /* scan over token tiles, capacity, counts, GEMM tile maps, slots and drop
+                             mask (and the tile histogram when top-k did not build it) */
   MOE_STAGE_SCATTER = 3,  /* row copies into the buckets */
   MOE_STAGE_GATE_UP = 4,  /* grouped GEMM 1 with the SwiGLU product */
   MOE_STAGE_DOWN = 5,     /* grouped GEMM 2 */

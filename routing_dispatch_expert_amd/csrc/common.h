@@ -43,6 +43,43 @@ __device__ inline uint4 load_stream(const uint4* p) {
   return uint4{w[0], w[1], w[2], w[3]};
 }
 
+// Block barrier for data exchanged through LDS only: it orders the block's
+// LDS accesses across it, while global stores and loads still in flight stay
+// in flight (no wait on the vector memory counter, unlike __syncthreads).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Ranks of one tile's copies, by one wave (64 lanes; LDS reads and writes of
+// one wave stay in program order). ecp [ncp]: expert of each copy in
+// flattened token order (-1: dropped); cnt [E]: zero on entry, the tile's
+// histogram on exit. rank[i] (if given) = the number of copies before i in the
+// tile with the same expert, -1 for a dropped copy. Copies are taken 64 at a
+// time; lanes with the same expert form a group found by ballots over the
+// expert-id bits, and a lane's rank within the round is the number of group
+// lanes below it.
+__device__ inline void rank_tile(const int* ecp, int ncp, int E, int* cnt, int32_t* rank) {
+  const int lane = threadIdx.x & 63;
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int c0 = 0; c0 < ncp; c0 += 64) {
+    const int i = c0 + lane;
+    const int e = i < ncp ? ecp[i] : -1;
+    const bool active = e >= 0;
+    unsigned long long mask = __ballot(active);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = (e >> bit) & 1;
+      const unsigned long long m = __ballot(active && set);
+      mask &= set ? m : ~m;
+    }
+    const int r = active ? cnt[e] + __popcll(mask & below) : -1;
+    if (active && 63 - __clzll(mask) == lane) cnt[e] = r + 1;
+    if (rank && i < ncp) rank[i] = r;
+  }
+}
+
 // ---- router (router.hip) ----
 // Number of d-slices S the scores are split into (partials part[S][T][E]).
 int router_splits(int64_t T, int64_t d, int E, bool bf16);
@@ -59,21 +96,33 @@ hipError_t launch_router_logits(const void* x, const void* wr, int64_t T, int64_
 // then written over slice 0 of part.
 bool route_builds_histogram(int k);
 bool route_rank_limited(int P, int M);
+// With tile_cnt, also the ranks of each tile's copies (rank [T, k], optional;
+// rank_tile).
 hipError_t launch_route(const float* part, int S, const float* bias, int64_t T, int E, int k,
                         float* logits_out, int32_t* idx, float* w, int32_t* tile_cnt, int P, int M,
-                        hipStream_t s);
+                        hipStream_t s, int32_t* rank = nullptr);
 
 // ---- permutation (permute.hip) ----
+// With rank, also the ranks of each tile's copies (rank_tile).
 hipError_t launch_tile_hist(const int32_t* idx, int64_t T, int k, int E, int32_t* tile_cnt,
-                            hipStream_t s);
+                            hipStream_t s, int32_t* rank = nullptr);
 // Exclusive scan of the tile histogram over tiles, per expert; then counts,
 // totals, send counts and (if mtile_off != nullptr) the GEMM row-tile prefix
-// for row tiles of `bm` rows.
+// for row tiles of `bm` rows (and a second map for bm1 rows when mtile1 is
+// given). 1 <= P <= E <= 4096.
 // place [E] (optional): rank of each bucket for the send counts (default e / (E/P)).
 hipError_t launch_scan(const int32_t* tile_cnt, int64_t nt, int E, int64_t C, int P,
                        int64_t row_bytes, int k, int64_t T, int32_t* tile_off, int32_t* routed,
                        int32_t* kept, int32_t* send, int64_t* totals, int bm, int32_t* mtile_off,
-                       int32_t* src, hipStream_t s, const int32_t* place = nullptr);
+                       int32_t* src, hipStream_t s, const int32_t* place = nullptr, int bm1 = 0,
+                       int32_t* mtile1 = nullptr);
+// Slots from the scan and the in-tile ranks: slot [T, k] holds each copy's
+// rank within its tile on entry (route or tile histogram) and its slot (-1:
+// dropped) on exit; slot = tile_off + rank, kept below C. Also src (optional;
+// kept rows only: the scan writes the padding) and totals[1] += tokens with no
+// kept copy (optional; the scan zeroed it). Experts outside [0, E) are dropped.
+hipError_t launch_slots_from_ranks(const int32_t* idx, int32_t* slot, const int32_t* tile_off, int64_t T, int k,
+                                  int E, int64_t C, int32_t* src, int64_t* totals, hipStream_t s);
 // Replicated experts: instance offsets [E+1], expert [R] and rank [R] of each
 // instance; then the instance of each copy from its rank among its expert's copies.
 hipError_t launch_replica_layout(const int32_t* replicas, int E, int R, int P, int32_t* inst_off, int32_t* wmap,

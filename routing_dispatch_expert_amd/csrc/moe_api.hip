@@ -320,13 +320,14 @@ int run_permute(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, in
   Carver c(scratch);
   int32_t* tile_cnt = c.take<int32_t>(static_cast<size_t>(nt) * E);
   int32_t* tile_off = c.take<int32_t>(static_cast<size_t>(nt) * E);
-  const int64_t eb = elem_bytes(dtype);
-  MOE_HIP_TRY(moe::launch_tile_hist(topk_idx, T, k, E, tile_cnt, s), "tile histogram");
-  MOE_HIP_TRY(moe::launch_scan(tile_cnt, nt, E, C, P, d * eb, k, T, tile_off, routed_count, kept_count,
-                               send_count, totals, 0, nullptr, src, s),
+  const int64_t row = d * elem_bytes(dtype);
+  // ranks within each tile go to slot, then the slots (tile offset + rank) replace them
+  MOE_HIP_TRY(moe::launch_tile_hist(topk_idx, T, k, E, tile_cnt, s, slot), "tile histogram");
+  MOE_HIP_TRY(moe::launch_scan(tile_cnt, nt, E, C, P, row, k, T, tile_off, routed_count, kept_count, send_count,
+                               totals, 0, nullptr, src, s),
               "scan");
-  MOE_HIP_TRY(moe::launch_slots(topk_idx, tile_off, T, k, E, C, slot, src, totals, s), "slots");
-  MOE_HIP_TRY(moe::launch_scatter_rows(x, topk_idx, slot, T, k, C, d * eb, buckets, s), "scatter");
+  MOE_HIP_TRY(moe::launch_slots_from_ranks(topk_idx, slot, tile_off, T, k, E, C, src, totals, s), "slots");
+  MOE_HIP_TRY(moe::launch_scatter_rows(x, topk_idx, slot, T, k, C, row, buckets, s), "scatter");
   return MOE_OK;
 }
 
@@ -438,32 +439,34 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
   int32_t* src = S.src;  // only built when asked for
   const bool bf16 = dtype == MOE_DTYPE_BF16;
   auto s = static_cast<hipStream_t>(stream);
-  const int64_t nt = moe::ceil_div(T, moe::kTileTokens);
   const int bm = moe::grouped_gemm_bm_down(bf16, C, d_ff);
 
   const int splits = moe::router_splits(T, d, E, bf16);
-  const bool fused_hist = moe::route_builds_histogram(k);
   MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTER, false, s), "event");
   MOE_HIP_TRY(moe::launch_router_logits(x, W_router, T, d, E, bf16, splits, p.logits, s), "router logits");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTER, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTE, false, s), "event");
+  const bool fused_hist = moe::route_builds_histogram(k);
+  const int64_t nt = moe::ceil_div(T, moe::kTileTokens);
+  // the tile histogram comes with each copy's rank within its tile, kept in slot
   MOE_HIP_TRY(moe::launch_route(p.logits, splits, router_bias, T, E, k, nullptr, idx, w,
-                                fused_hist ? p.tile_cnt : nullptr, P, max_ranks, s),
+                                fused_hist ? p.tile_cnt : nullptr, P, max_ranks, s, fused_hist ? slot : nullptr),
               "route");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTE, true, s), "event");
+  // the scan also writes the counts, totals and both GEMMs' row-tile maps;
+  // slots are the tile offsets plus the ranks
+  const int bm_gu = moe::grouped_gemm_bm_gate_up(bf16, C, d);
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SLOTS, false, s), "event");
-  if (!fused_hist) MOE_HIP_TRY(moe::launch_tile_hist(idx, T, k, E, p.tile_cnt, s), "tile histogram");
-  MOE_HIP_TRY(moe::launch_scan(p.tile_cnt, nt, E, C, P, d * eb, k, T, p.tile_off, routed, kept, send,
-                               totals, bm, p.mtile, src, s),
+  if (!fused_hist) MOE_HIP_TRY(moe::launch_tile_hist(idx, T, k, E, p.tile_cnt, s, slot), "tile histogram");
+  MOE_HIP_TRY(moe::launch_scan(p.tile_cnt, nt, E, C, P, d * eb, k, T, p.tile_off, routed, kept, send, totals, bm,
+                               p.mtile, src, s, nullptr, bm_gu, bm_gu != bm ? p.mtile_gu : nullptr),
               "scan");
-  MOE_HIP_TRY(moe::launch_slots(idx, p.tile_off, T, k, E, C, slot, src, totals, s), "slots");
+  MOE_HIP_TRY(moe::launch_slots_from_ranks(idx, slot, p.tile_off, T, k, E, C, src, totals, s), "slots");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SLOTS, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, false, s), "event");
   MOE_HIP_TRY(moe::launch_scatter_rows(x, idx, slot, T, k, C, d * eb, buckets, s), "scatter");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, false, s), "event");
-  const int bm_gu = moe::grouped_gemm_bm_gate_up(bf16, C, d);
-  if (bm_gu != bm) MOE_HIP_TRY(moe::launch_mtile_map(kept, E, C, bm_gu, p.mtile_gu, s), "tile map (gate, up)");
   MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, bm_gu != bm ? p.mtile_gu : p.mtile, W_gate, W_up, E, C, d, d_ff,
                                        bf16, p.h, s, nullptr, &p.split),
               "grouped gemm (gate, up)");

@@ -21,22 +21,28 @@
 namespace moe {
 namespace {
 
-// Per-tile expert histogram: tile_cnt[b][e] = copies of expert e among tokens
-// [64 b, 64 b + 64). Entries outside [0, E) are counted nowhere (dropped).
+// Per-tile expert histogram and ranks: tile_cnt[b][e] = copies of expert e
+// among tokens [64 b, 64 b + 64), and rank [T, k] (optional) of each copy
+// within its tile (rank_tile). Entries outside [0, E) are counted nowhere and
+// ranked -1 (dropped).
 __global__ __launch_bounds__(256) void tile_hist_kernel(const int32_t* __restrict__ idx,
                                                         int64_t T, int k, int E,
-                                                        int32_t* __restrict__ tile_cnt) {
-  extern __shared__ int hist[];
+                                                        int32_t* __restrict__ tile_cnt,
+                                                        int32_t* __restrict__ rank) {
+  extern __shared__ int sm[];
+  int* hist = sm;        // [E]
+  int* ecp = sm + E;     // [64 k]
   const int64_t b = blockIdx.x;
   const int64_t t0 = b * kTileTokens;
   const int n = static_cast<int>(min<int64_t>(kTileTokens, T - t0)) * k;
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
-  __syncthreads();
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     const int e = idx[t0 * k + i];
-    if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&hist[e], 1);
+    ecp[i] = static_cast<unsigned>(e) < static_cast<unsigned>(E) ? e : -1;
   }
-  __syncthreads();
+  lds_barrier();
+  if (threadIdx.x < 64) rank_tile(ecp, n, E, hist, rank ? rank + t0 * k : nullptr);
+  lds_barrier();
   for (int e = threadIdx.x; e < E; e += blockDim.x) tile_cnt[b * E + e] = hist[e];
 }
 
@@ -51,7 +57,7 @@ __device__ int block_exclusive_scan_1024(int v, int* total, int* sh /* >= 17 int
     if (lane >= off) incl += o;
   }
   if (lane == 63) sh[wave] = incl;
-  __syncthreads();
+  lds_barrier();
   if (threadIdx.x == 0) {
     int run = 0;
     for (int w = 0; w < 16; ++w) {
@@ -61,10 +67,10 @@ __device__ int block_exclusive_scan_1024(int v, int* total, int* sh /* >= 17 int
     }
     sh[16] = run;
   }
-  __syncthreads();
+  lds_barrier();
   const int out = sh[wave] + incl - v;
   *total = sh[16];
-  __syncthreads();
+  lds_barrier();
   return out;
 }
 
@@ -90,64 +96,121 @@ __device__ void mtile_prefix(const int* kept_s, int E, int bm, int32_t* mtile_of
   if (threadIdx.x == 0) mtile_off[E] = total;
 }
 
-// Exclusive scan over tiles per expert, then counts, totals, send counts and
-// the GEMM row-tile map; one block of 1024 threads. The scan takes 64 experts
-// at a time with 16 lanes each; lane ly owns a contiguous run of tiles.
-__global__ __launch_bounds__(1024) void scan_finalize_kernel(
-    const int32_t* __restrict__ tile_cnt, int64_t nt, int E, int64_t C, int P, int64_t row_bytes, int k,
-    int64_t T, int32_t* __restrict__ tile_off, int32_t* __restrict__ routed, int32_t* __restrict__ kept,
-    int32_t* __restrict__ send, int64_t* __restrict__ totals, int bm, int32_t* __restrict__ mtile_off,
-    const int32_t* __restrict__ place) {
-  __shared__ int part[16][65];
-  __shared__ int kept_s[4096];
-  __shared__ int send_s[4096];  // kept rows per rank (P <= E)
+// Per-rank send counts, totals and the GEMM row-tile maps from the kept
+// counts in LDS (one block of 1024 threads). kpre [E + 1] and send_s [P] are
+// LDS scratch. The send counts are differences of the kept prefix (rank p
+// holds experts [p E/P, (p+1) E/P)), or LDS sums over `place` when given.
+struct ScanTail {
+  int64_t C, row_bytes, T;
+  int E, P, k;
+  int32_t* send;
+  int64_t* totals;
+  int bm0, bm1;
+  int32_t *mtile0, *mtile1;
+  const int32_t* place;
+};
+
+__device__ void scan_tail(const ScanTail& a, const int* kept_s, int* kpre, int* send_s, int* sh) {
+  const int tid = threadIdx.x;
+  int v[4];
+  int local = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    v[q] = e < a.E ? kept_s[e] : 0;
+    local += v[q];
+  }
+  int n_kept;  // at most T k copies: fits an int like the copy indices
+  int run = block_exclusive_scan_1024(local, &n_kept, sh);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    if (e < a.E) kpre[e] = run;
+    run += v[q];
+  }
+  if (tid == 0) kpre[a.E] = n_kept;
+  if (a.place)
+    for (int p = tid; p < a.P; p += blockDim.x) send_s[p] = 0;
+  lds_barrier();
+  const int per = a.E / a.P;
+  if (a.place) {
+    for (int e = tid; e < a.E; e += blockDim.x) atomicAdd(&send_s[a.place[e]], kept_s[e]);  // order-free
+    lds_barrier();
+  }
+  if (a.send)
+    for (int p = tid; p < a.P; p += blockDim.x)
+      a.send[p] = a.place ? send_s[p] : kpre[(p + 1) * per] - kpre[p * per];
+  if (a.totals && tid == 0) {
+    const int send0 = a.place ? send_s[0] : kpre[per];
+    a.totals[0] = a.T * a.k - n_kept;
+    a.totals[1] = 0;  // fully dropped tokens: added by the slot kernel that follows
+    a.totals[2] = static_cast<int64_t>(a.E) * a.C - n_kept;
+    a.totals[3] = static_cast<int64_t>(n_kept - send0) * a.row_bytes;
+  }
+  if (a.mtile0) mtile_prefix(kept_s, a.E, a.bm0, a.mtile0, sh);
+  if (a.mtile1) mtile_prefix(kept_s, a.E, a.bm1, a.mtile1, sh);
+}
+
+// The scan, one block of 1024 threads: per expert, the exclusive prefix over
+// tiles of its tile counts (tile_off), then the routed and kept counts and
+// the tail. Experts are taken EB at a time (EB = 64 .. 1024, a power of two
+// covering E where it can), 1024 / EB lanes per expert; lane ly sums a
+// contiguous run of tiles, the runs are scanned in LDS, and each lane writes
+// its run's offsets. Loads go out eight at a time.
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ tile_cnt, int64_t nt,
+                                                    int32_t* __restrict__ tile_off, int32_t* __restrict__ routed,
+                                                    int32_t* __restrict__ kept, ScanTail tail) {
+  extern __shared__ int sm[];
+  const int E = tail.E;
+  int* kept_s = sm;              // [E]
+  int* kpre = sm + E;            // [E + 1]
+  int* send_s = kpre + E + 1;    // [P]
+  __shared__ int part[1024];
   __shared__ int sh[17];
-  __shared__ unsigned long long ksum;
-  const int ex = threadIdx.x & 63;
-  const int ly = threadIdx.x >> 6;
-  const int64_t chunk = ceil_div(nt, 16);
+  const int EB = E <= 64 ? 64 : (E <= 128 ? 128 : (E <= 256 ? 256 : (E <= 512 ? 512 : 1024)));
+  const int LY = 1024 / EB;
+  const int tid = threadIdx.x, ex = tid % EB, ly = tid / EB;
+  const int64_t chunk = ceil_div(nt, LY);
   const int64_t b0 = min(nt, ly * chunk);
   const int64_t b1 = min(nt, b0 + chunk);
-  const int per = E / P;
-  if (threadIdx.x == 0) ksum = 0;
-  for (int p = threadIdx.x; p < P; p += blockDim.x) send_s[p] = 0;  // ordered by the first barrier below
-  for (int eb = 0; eb < E; eb += 64) {
-    const int e = eb + ex;
+  constexpr int B = 8;
+  for (int base = 0; base < E; base += EB) {
+    const int e = base + ex;
     int sum = 0;
     if (e < E)
-      for (int64_t b = b0; b < b1; ++b) sum += tile_cnt[b * E + e];
-    part[ly][ex] = sum;
-    __syncthreads();
-    int run = 0;
-    for (int l = 0; l < ly; ++l) run += part[l][ex];
-    if (e < E) {
-      for (int64_t b = b0; b < b1; ++b) {
-        const int v = tile_cnt[b * E + e];
-        tile_off[b * E + e] = run;
-        run += v;
+      for (int64_t b = b0; b < b1; b += B) {
+        int v[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) v[j] = b + j < b1 ? tile_cnt[(b + j) * E + e] : 0;
+#pragma unroll
+        for (int j = 0; j < B; ++j) sum += v[j];
       }
-      if (ly == 15) {
+    part[tid] = sum;
+    lds_barrier();
+    int run = 0;
+    for (int l = 0; l < ly; ++l) run += part[l * EB + ex];
+    if (e < E) {
+      for (int64_t b = b0; b < b1; b += B) {
+        int v[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) v[j] = b + j < b1 ? tile_cnt[(b + j) * E + e] : 0;
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+          if (b + j < b1) {
+            tile_off[(b + j) * E + e] = run;
+            run += v[j];
+          }
+      }
+      if (ly == LY - 1) {
+        const int kv = static_cast<int>(min<int64_t>(run, tail.C));
         routed[e] = run;
-        const int kv = static_cast<int>(min<int64_t>(run, C));
         kept[e] = kv;
         kept_s[e] = kv;
-        atomicAdd(&ksum, static_cast<unsigned long long>(kv));  // integer sums: order-free
-        atomicAdd(&send_s[place ? place[e] : e / per], kv);
       }
     }
-    __syncthreads();
+    lds_barrier();  // part is taken again
   }
-  if (send)
-    for (int p = threadIdx.x; p < P; p += blockDim.x) send[p] = send_s[p];
-  if (totals && threadIdx.x == 0) {
-    const int64_t n_kept = static_cast<int64_t>(ksum);
-    const int64_t rank0 = send_s[0];
-    totals[0] = T * k - n_kept;
-    totals[1] = 0;  // fully dropped tokens: accumulated by the slot kernel
-    totals[2] = static_cast<int64_t>(E) * C - n_kept;
-    totals[3] = (n_kept - rank0) * row_bytes;
-  }
-  if (mtile_off) mtile_prefix(kept_s, E, bm, mtile_off, sh);
+  scan_tail(tail, kept_s, kpre, send_s, sh);
 }
 
 // Row-tile map from counts given by the caller: each count is clamped to
@@ -252,6 +315,49 @@ __global__ __launch_bounds__(64) void slots_kernel(const int32_t* __restrict__ i
   }
 }
 
+// Slots from the scan and the in-tile ranks. A block of 256 threads takes
+// floor(256 / k) whole tokens, one thread per copy: slot = tile_off[tile][e]
+// + rank, kept when below C (rank -1 or an expert outside [0, E): dropped).
+// slot holds the ranks on entry and the slots on exit (each thread reads its
+// entry, then writes it). Also src (kept rows) and, per block, one addition
+// of its tokens with no kept copy to totals[1].
+__global__ __launch_bounds__(256) void slots_from_ranks_kernel(const int32_t* __restrict__ idx,
+                                                               int32_t* __restrict__ slot,
+                                                               const int32_t* __restrict__ tile_off, int64_t T,
+                                                               int k, int E, int64_t C, int32_t* __restrict__ src,
+                                                               int64_t* __restrict__ totals) {
+  __shared__ int any[256];
+  const int tb = 256 / k;
+  const int tid = threadIdx.x;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tb;
+  const int n = static_cast<int>(min<int64_t>(tb, T - t0));
+  if (tid < tb) any[tid] = 0;
+  lds_barrier();
+  if (tid < n * k) {
+    const int64_t i = t0 * k + tid;
+    const int e = idx[i];
+    const int r = slot[i];
+    int sl = -1;
+    if (static_cast<unsigned>(e) < static_cast<unsigned>(E) && r >= 0) {
+      const int64_t v = tile_off[((t0 + tid / k) / kTileTokens) * E + e] + static_cast<int64_t>(r);
+      if (v < C) sl = static_cast<int>(v);
+    }
+    slot[i] = sl;
+    if (sl >= 0) {
+      any[tid / k] = 1;  // every writer stores the same value
+      if (src) src[static_cast<int64_t>(e) * C + sl] = static_cast<int32_t>(i);
+    }
+  }
+  lds_barrier();
+  if (totals && tid < 64) {
+    int c = 0;
+    for (int j = tid; j < n; j += 64) c += any[j] == 0 ? 1 : 0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
+    if (tid == 0 && c) atomicAdd(reinterpret_cast<unsigned long long*>(&totals[1]), static_cast<unsigned long long>(c));
+  }
+}
+
 // Row scatter: one 256-thread block per token moves its row (16-byte words,
 // U per lane, so a row of up to 256*U words takes one pass) to each kept
 // destination bucket row; the row is read once and written k' <= k times with
@@ -352,24 +458,36 @@ __global__ __launch_bounds__(256) void instance_kernel(const int32_t* __restrict
 }  // namespace
 
 hipError_t launch_tile_hist(const int32_t* idx, int64_t T, int k, int E, int32_t* tile_cnt,
-                            hipStream_t s) {
+                            hipStream_t s, int32_t* rank) {
   const int64_t nt = ceil_div(T, kTileTokens);
   if (nt == 0) return hipSuccess;
-  tile_hist_kernel<<<dim3(static_cast<unsigned>(nt)), dim3(256), E * sizeof(int), s>>>(idx, T, k, E,
-                                                                                     tile_cnt);
+  const size_t shm = (static_cast<size_t>(E) + static_cast<size_t>(kTileTokens) * k) * sizeof(int);
+  tile_hist_kernel<<<dim3(static_cast<unsigned>(nt)), dim3(256), shm, s>>>(idx, T, k, E, tile_cnt, rank);
   return hipGetLastError();
 }
 
 hipError_t launch_scan(const int32_t* tile_cnt, int64_t nt, int E, int64_t C, int P,
                        int64_t row_bytes, int k, int64_t T, int32_t* tile_off, int32_t* routed,
                        int32_t* kept, int32_t* send, int64_t* totals, int bm, int32_t* mtile_off,
-                       int32_t* src, hipStream_t s, const int32_t* place) {
-  scan_finalize_kernel<<<dim3(1), dim3(1024), 0, s>>>(tile_cnt, nt, E, C, P, row_bytes, k, T, tile_off, routed,
-                                                      kept, send, totals, bm, mtile_off, place);
+                       int32_t* src, hipStream_t s, const int32_t* place, int bm1, int32_t* mtile1) {
+  if (E > 4096 || P < 1 || P > E) return hipErrorInvalidValue;
+  const ScanTail tail{C, row_bytes, T, E, P, k, send, totals, bm, bm1, mtile_off, mtile1, place};
+  const size_t shm = (2 * static_cast<size_t>(E) + 1 + P) * sizeof(int);
+  scan_kernel<<<dim3(1), dim3(1024), shm, s>>>(tile_cnt, nt, tile_off, routed, kept, tail);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !src) return err;
   const unsigned gx = static_cast<unsigned>(std::min<int64_t>(ceil_div(C, 256), 64));
   src_padding_kernel<<<dim3(gx, static_cast<unsigned>(E)), dim3(256), 0, s>>>(kept, C, E, src);
+  return hipGetLastError();
+}
+
+hipError_t launch_slots_from_ranks(const int32_t* idx, int32_t* slot, const int32_t* tile_off, int64_t T, int k,
+                                  int E, int64_t C, int32_t* src, int64_t* totals, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (k < 1 || k > 256) return hipErrorInvalidValue;
+  const int tb = 256 / k;
+  slots_from_ranks_kernel<<<dim3(static_cast<unsigned>(ceil_div(T, tb))), dim3(256), 0, s>>>(idx, slot, tile_off, T,
+                                                                                             k, E, C, src, totals);
   return hipGetLastError();
 }
 

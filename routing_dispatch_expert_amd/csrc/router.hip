@@ -17,7 +17,8 @@
 namespace moe {
 namespace {
 
-constexpr int kMaxRouterSplits = 8;  // d-slices of the router scores (partials summed in order)
+constexpr int kMaxRouterSplits = 16;  // d-slices of the router scores (partials summed in order)
+constexpr int kTiledSplits = 8;       // at most this many when a wave takes 2 or 4 token tiles
 
 // ---------------------------------------------------------------------------
 // Scores on the matrix cores. Each wave is one work item: 16 MT tokens x
@@ -183,12 +184,13 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* part, int S, c
                                                      int64_t T, int E, int k, float* logits_out,
                                                      int32_t* __restrict__ idx, float* __restrict__ w,
                                                      int32_t* __restrict__ tile_cnt, int P, int M,
-                                                     float* lsum, const float* lsrc) {
+                                                     float* lsum, const float* lsrc, int32_t* __restrict__ rank) {
   constexpr int kTokensPerBlock = 1024 / L;
   static_assert(!HIST || kTokensPerBlock == kTileTokens, "one block per histogram tile");
   extern __shared__ int smem[];
   int* hist = smem;                                                            // [E] when HIST
   uint32_t* rbest = reinterpret_cast<uint32_t*>(smem + (HIST ? E : 0));        // [tokens][P] when LIMIT
+  int* ecp = smem + (HIST ? E : 0) + (LIMIT ? kTokensPerBlock * P : 0);        // [tokens][k] when HIST
   const int g = threadIdx.x % L;
   const int tok = threadIdx.x / L;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + tok;
@@ -217,19 +219,21 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* part, int S, c
         const int e = eb + q * L;
         vv[q] = e < E ? part[t * E + e] : 0.f;
       }
-      float pv[kMaxRouterSplits - 1][G];  // all slices' loads in flight at once
+      for (int s0 = 1; s0 < S; s0 += 8) {
+        float pv[8][G];  // eight slices' loads in flight at once
 #pragma unroll
-      for (int s = 1; s < kMaxRouterSplits; ++s)
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int q = 0; q < G; ++q) {
-          const int e = eb + q * L;
-          pv[s - 1][q] = (s < S && e < E) ? part[s * TE + t * E + e] : 0.f;
-        }
+          for (int q = 0; q < G; ++q) {
+            const int e = eb + q * L;
+            pv[j][q] = (s0 + j < S && e < E) ? part[(s0 + j) * TE + t * E + e] : 0.f;
+          }
 #pragma unroll
-      for (int s = 1; s < kMaxRouterSplits; ++s)  // slice order
+        for (int j = 0; j < 8; ++j)  // slice order
 #pragma unroll
-        for (int q = 0; q < G; ++q)
-          if (s < S) vv[q] += pv[s - 1][q];
+          for (int q = 0; q < G; ++q)
+            if (s0 + j < S) vv[q] += pv[j][q];
+      }
 #pragma unroll
       for (int q = 0; q < G; ++q) {
         const int e = eb + q * L;
@@ -324,10 +328,14 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* part, int S, c
   if (valid && g < k) {
     idx[t * k + g] = sel_e;
     w[t * k + g] = static_cast<float>(z / sum);
-    if (HIST) atomicAdd(&hist[sel_e], 1);  // integer counts: order-free
   }
-  if (HIST) {
-    __syncthreads();
+  if (HIST) {  // the tile's histogram and the ranks of its copies
+    if (g < k) ecp[tok * k + g] = sel_e;
+    lds_barrier();
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock;
+    if (threadIdx.x < 64)
+      rank_tile(ecp, static_cast<int>(min<int64_t>(kTokensPerBlock, T - t0)) * k, E, hist, rank ? rank + t0 * k : nullptr);
+    lds_barrier();
     for (int e = threadIdx.x; e < E; e += blockDim.x) tile_cnt[static_cast<int64_t>(blockIdx.x) * E + e] = hist[e];
   }
 }
@@ -345,14 +353,15 @@ struct RouteArgs {
   int P, M;
   float* lsum;
   const float* lsrc;
+  int32_t* rank;
 };
 
 template <int L, int KMAX, bool HIST, bool LIMIT>
 hipError_t route_launch(const RouteArgs& a, hipStream_t s) {
   const int64_t tpb = 1024 / L;
-  const size_t lds = (HIST ? a.E * sizeof(int) : 0) + (LIMIT ? tpb * a.P * sizeof(uint32_t) : 0);
+  const size_t lds = (HIST ? (a.E + tpb * a.k) * sizeof(int) : 0) + (LIMIT ? tpb * a.P * sizeof(uint32_t) : 0);
   route_kernel<L, KMAX, HIST, LIMIT><<<dim3(static_cast<unsigned>(ceil_div(a.T, tpb))), dim3(1024), lds, s>>>(
-      a.part, a.S, a.bias, a.T, a.E, a.k, a.logits_out, a.idx, a.w, a.tile_cnt, a.P, a.M, a.lsum, a.lsrc);
+      a.part, a.S, a.bias, a.T, a.E, a.k, a.logits_out, a.idx, a.w, a.tile_cnt, a.P, a.M, a.lsum, a.lsrc, a.rank);
   return hipGetLastError();
 }
 
@@ -387,7 +396,7 @@ static bool router_on_gemm(int64_t T, int64_t d, int E, bool bf16) {
 // T = 16384, E = 64: 43 -> 26 us; T = 4096, E = 8: 10.7 -> 10.0 us).
 static int router_tile_tokens(int64_t T, int64_t d, int E) {
   const int nt = E <= 16 ? 1 : (E <= 32 ? 2 : 4);
-  const int64_t s_max = std::max<int64_t>(1, std::min<int64_t>(d / 256, kMaxRouterSplits));
+  const int64_t s_max = std::max<int64_t>(1, std::min<int64_t>(d / 256, kTiledSplits));
   for (int mt : {4, 2})
     if (ceil_div(T, 16 * mt) * ceil_div(E, 16 * nt) * s_max >= 1024) return mt;
   return 1;
@@ -405,7 +414,8 @@ int router_splits(int64_t T, int64_t d, int E, bool bf16) {
   const int64_t items = ceil_div(T, 16 * mt) * ceil_div(E, 16 * nt);
   const int64_t by_work = ceil_div(mt == 1 ? 2048 : 1024, items);  // aim at >= 2048 (1024) waves
   const int64_t by_len = std::max<int64_t>(1, d / 256);              // at least 256 of d per slice
-  return static_cast<int>(std::max<int64_t>(1, std::min({by_work, by_len, int64_t{kMaxRouterSplits}})));
+  const int64_t cap = mt == 1 ? kMaxRouterSplits : kTiledSplits;   // few tokens: more slices
+  return static_cast<int>(std::max<int64_t>(1, std::min({by_work, by_len, cap})));
 }
 
 hipError_t launch_router_logits(const void* x, const void* wr, int64_t T, int64_t d, int E, bool bf16,
@@ -451,10 +461,10 @@ bool route_rank_limited(int P, int M) { return M > 0 && M < P; }
 
 hipError_t launch_route(const float* part, int S, const float* bias, int64_t T, int E, int k,
                         float* logits_out, int32_t* idx, float* w, int32_t* tile_cnt, int P, int M,
-                        hipStream_t s) {
+                        hipStream_t s, int32_t* rank) {
   if (T == 0) return hipSuccess;
   if (tile_cnt && !route_builds_histogram(k)) return hipErrorInvalidValue;
-  RouteArgs a{part, S, bias, T, E, k, logits_out, idx, w, tile_cnt, P, M, nullptr, nullptr};
+  RouteArgs a{part, S, bias, T, E, k, logits_out, idx, w, tile_cnt, P, M, nullptr, nullptr, rank};
   if (!route_rank_limited(P, M)) return route_dispatch<false>(a, s);
   if (P > kMaxLimitRanks || E % P || static_cast<int64_t>(M) * (E / P) < k) return hipErrorInvalidValue;
   // Where pass 3 finds the summed scores: logits_out when asked for, the single
