@@ -156,7 +156,8 @@ __device__ void scan_tail(const ScanTail& a, const int* kept_s, int* kpre, int* 
 // the tail. Experts are taken EB at a time (EB = 64 .. 1024, a power of two
 // covering E where it can), 1024 / EB lanes per expert; lane ly sums a
 // contiguous run of tiles, the runs are scanned in LDS, and each lane writes
-// its run's offsets. Loads go out eight at a time.
+// its run's offsets. The first 16 counts of a run are loaded at once and stay
+// in registers between the two passes; the rest go out eight at a time.
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ tile_cnt, int64_t nt,
                                                     int32_t* __restrict__ tile_off, int32_t* __restrict__ routed,
                                                     int32_t* __restrict__ kept, ScanTail tail) {
@@ -170,27 +171,41 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   const int EB = E <= 64 ? 64 : (E <= 128 ? 128 : (E <= 256 ? 256 : (E <= 512 ? 512 : 1024)));
   const int LY = 1024 / EB;
   const int tid = threadIdx.x, ex = tid % EB, ly = tid / EB;
-  const int64_t chunk = ceil_div(nt, LY);
-  const int64_t b0 = min(nt, ly * chunk);
-  const int64_t b1 = min(nt, b0 + chunk);
-  constexpr int B = 8;
+  const int ntt = static_cast<int>(nt);  // nt E < 2^31 (checked by the launcher)
+  const int chunk = (ntt + LY - 1) / LY;
+  const int b0 = min(ntt, ly * chunk);
+  const int b1 = min(ntt, b0 + chunk);
+  constexpr int B = 8, F = 16;  // loads per batch; counts kept in registers
   for (int base = 0; base < E; base += EB) {
     const int e = base + ex;
+    int first[F];
     int sum = 0;
-    if (e < E)
-      for (int64_t b = b0; b < b1; b += B) {
+    if (e < E) {
+#pragma unroll
+      for (int j = 0; j < F; ++j) {
+        first[j] = b0 + j < b1 ? tile_cnt[(b0 + j) * E + e] : 0;
+        sum += first[j];
+      }
+      for (int b = b0 + F; b < b1; b += B) {
         int v[B];
 #pragma unroll
         for (int j = 0; j < B; ++j) v[j] = b + j < b1 ? tile_cnt[(b + j) * E + e] : 0;
 #pragma unroll
         for (int j = 0; j < B; ++j) sum += v[j];
       }
+    }
     part[tid] = sum;
     lds_barrier();
     int run = 0;
     for (int l = 0; l < ly; ++l) run += part[l * EB + ex];
     if (e < E) {
-      for (int64_t b = b0; b < b1; b += B) {
+#pragma unroll
+      for (int j = 0; j < F; ++j)
+        if (b0 + j < b1) {
+          tile_off[(b0 + j) * E + e] = run;
+          run += first[j];
+        }
+      for (int b = b0 + F; b < b1; b += B) {
         int v[B];
 #pragma unroll
         for (int j = 0; j < B; ++j) v[j] = b + j < b1 ? tile_cnt[(b + j) * E + e] : 0;
@@ -470,7 +485,7 @@ hipError_t launch_scan(const int32_t* tile_cnt, int64_t nt, int E, int64_t C, in
                        int64_t row_bytes, int k, int64_t T, int32_t* tile_off, int32_t* routed,
                        int32_t* kept, int32_t* send, int64_t* totals, int bm, int32_t* mtile_off,
                        int32_t* src, hipStream_t s, const int32_t* place, int bm1, int32_t* mtile1) {
-  if (E > 4096 || P < 1 || P > E) return hipErrorInvalidValue;
+  if (E > 4096 || P < 1 || P > E || nt * E >= (int64_t{1} << 31)) return hipErrorInvalidValue;
   const ScanTail tail{C, row_bytes, T, E, P, k, send, totals, bm, bm1, mtile_off, mtile1, place};
   const size_t shm = (2 * static_cast<size_t>(E) + 1 + P) * sizeof(int);
   scan_kernel<<<dim3(1), dim3(1024), shm, s>>>(tile_cnt, nt, tile_off, routed, kept, tail);
