@@ -179,6 +179,55 @@ __device__ inline void insert_sorted(float (&lv)[KMAX], int (&li)[KMAX], float v
   }
 }
 
+// Ranks of one tile's copies by all the block's waves: wave w takes copies
+// [64 w, 64 w + 64) (every wave of the block must call it). Within its 64
+// copies a lane's rank is the number of lanes below it with the same expert
+// (groups found by ballots over the expert-id bits) and the group's highest
+// lane stores the group size as the chunk's count of that expert; after a
+// barrier the counts become exclusive prefixes over the chunks, per expert,
+// and a copy's rank is its rank in its chunk plus the count of its expert in
+// the earlier chunks. Same result as rank_tile. cc: LDS scratch of
+// ceil(ncp / 64) E ints; cnt [E] gets the tile's histogram.
+constexpr int kRankChunkInts = 8192;
+__device__ void rank_tile_waves(const int* ecp, int ncp, int E, int* cnt, int* cc, int32_t* rank) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nch = (ncp + 63) / 64;  // at most the block's waves: ncp <= 64 k, k <= 16
+  for (int i = threadIdx.x; i < nch * E; i += blockDim.x) cc[i] = 0;
+  lds_barrier();
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int my_e = -1, my_r = 0;  // this lane's copy in chunk `wave` (nch <= 16 = waves of the block)
+  if (wave < nch) {
+    const int i = wave * 64 + lane;
+    const int e = i < ncp ? ecp[i] : -1;
+    const bool active = e >= 0;
+    unsigned long long mask = __ballot(active);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = (e >> bit) & 1;
+      const unsigned long long m = __ballot(active && set);
+      mask &= set ? m : ~m;
+    }
+    if (active) {
+      my_e = e;
+      my_r = __popcll(mask & below);
+      if (63 - __clzll(mask) == lane) cc[wave * E + e] = __popcll(mask);
+    }
+  }
+  lds_barrier();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int w = 0; w < nch; ++w) {
+      const int c = cc[w * E + e];
+      cc[w * E + e] = run;
+      run += c;
+    }
+    cnt[e] = run;
+  }
+  lds_barrier();
+  if (rank && wave < nch && wave * 64 + lane < ncp)
+    rank[wave * 64 + lane] = my_e >= 0 ? my_r + cc[wave * E + my_e] : -1;
+}
+
 template <int L, int KMAX, bool HIST, bool LIMIT>
 __global__ __launch_bounds__(1024) void route_kernel(const float* part, int S, const float* __restrict__ bias,
                                                      int64_t T, int E, int k, float* logits_out,
@@ -333,9 +382,14 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* part, int S, c
     if (g < k) ecp[tok * k + g] = sel_e;
     lds_barrier();
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock;
-    if (threadIdx.x < 64)
-      rank_tile(ecp, static_cast<int>(min<int64_t>(kTokensPerBlock, T - t0)) * k, E, hist, rank ? rank + t0 * k : nullptr);
-    lds_barrier();
+    const int ncp = static_cast<int>(min<int64_t>(kTokensPerBlock, T - t0)) * k;
+    int32_t* rk = rank ? rank + t0 * k : nullptr;
+    if (k * E <= kRankChunkInts) {
+      rank_tile_waves(ecp, ncp, E, hist, ecp + kTokensPerBlock * k, rk);
+    } else {
+      if (threadIdx.x < 64) rank_tile(ecp, ncp, E, hist, rk);
+      lds_barrier();
+    }
     for (int e = threadIdx.x; e < E; e += blockDim.x) tile_cnt[static_cast<int64_t>(blockIdx.x) * E + e] = hist[e];
   }
 }
@@ -359,7 +413,9 @@ struct RouteArgs {
 template <int L, int KMAX, bool HIST, bool LIMIT>
 hipError_t route_launch(const RouteArgs& a, hipStream_t s) {
   const int64_t tpb = 1024 / L;
-  const size_t lds = (HIST ? (a.E + tpb * a.k) * sizeof(int) : 0) + (LIMIT ? tpb * a.P * sizeof(uint32_t) : 0);
+  // HIST: histogram [E], the tile's experts [64 k] and, for the ranking by all waves, its chunk counts [k E]
+  const size_t lds = (HIST ? (a.E + tpb * a.k + (a.k * a.E <= kRankChunkInts ? a.k * a.E : 0)) * sizeof(int) : 0) +
+                     (LIMIT ? tpb * a.P * sizeof(uint32_t) : 0);
   route_kernel<L, KMAX, HIST, LIMIT><<<dim3(static_cast<unsigned>(ceil_div(a.T, tpb))), dim3(1024), lds, s>>>(
       a.part, a.S, a.bias, a.T, a.E, a.k, a.logits_out, a.idx, a.w, a.tile_cnt, a.P, a.M, a.lsum, a.lsrc, a.rank);
   return hipGetLastError();
