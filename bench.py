@@ -177,8 +177,8 @@ def stage_of_kernel(short: str):
             return "router"                          # fp32-output score GEMM
         return "down"
     for prefix, stage in (("router_logits", "router"), ("route_kernel", "route"), ("scatter_rows", "scatter"),
-                          ("combine_kernel", "combine"), ("slots", "slots"), ("scan_finalize", "slots"),
-                          ("tile_hist", "slots"), ("perm", "slots")):
+                          ("combine_kernel", "combine"), ("slots", "slots"), ("scan_kernel", "slots"),
+                          ("tile_hist", "slots")):
         if short.startswith(prefix):
             return stage
     return None
