@@ -118,6 +118,10 @@ SMALL = [
     dict(T=130, d=1024, E=64, k=6, d_ff=72, cf=1.25, P=8, max_ranks=1, bias="zipf1.2"),
     dict(T=64, d=128, E=8, k=2, d_ff=64, cf=1.25, P=4, max_ranks=1, dtype="f32", x_std=1 / np.sqrt(128),
          wr_std=1 / np.sqrt(128)),
+    # k E > 8192: the route kernel ranks each tile's copies with one wave instead of all sixteen
+    dict(T=150, d=64, E=1024, k=16, d_ff=32, cf=2.0, P=4),
+    # the most experts: the scan takes them 1024 at a time; k E = 8192 ranks with all waves
+    dict(T=100, d=64, E=4096, k=2, d_ff=32, cf=4.0, P=8),
 ]
 
 

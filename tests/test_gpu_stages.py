@@ -146,6 +146,9 @@ PERMUTE_CASES = [
     (40, 8, 2, 1.0, 2, 20480, "bf16", False),   # 2560 words a row: two passes of 8 words per lane
     (30, 4, 2, 1.0, 1, 8200, "f32", True),      # 2050 words a row: a second pass of 2 words
     (100, 64, 32, 0.5, 4, 64, "bf16", True),    # k = 32: every metadata lane of a wave, many drops
+    (70000, 8, 2, 1.25, 2, 8, "bf16", False),    # 1094 tiles: 69 per scan lane, past the 16 held in registers
+    (3000, 4096, 4, 1.0, 8, 8, "bf16", True),    # the most experts: the scan takes them 1024 at a time
+    (2000, 1000, 5, 1.5, 4, 8, "bf16", False),   # 1000 experts: a 1024-wide pass with idle lanes
 ]
 
 
