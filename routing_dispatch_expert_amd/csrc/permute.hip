@@ -46,7 +46,9 @@ __global__ __launch_bounds__(256) void tile_hist_kernel(const int32_t* __restric
   for (int e = threadIdx.x; e < E; e += blockDim.x) tile_cnt[b * E + e] = hist[e];
 }
 
-// Exclusive scan of one int per thread over a block of 1024 threads.
+// Exclusive scan of one int per thread over a block of 1024 threads. Its
+// barriers order LDS only: global stores issued before it may still be in
+// flight after it.
 __device__ int block_exclusive_scan_1024(int v, int* total, int* sh /* >= 17 ints */) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -430,6 +432,7 @@ __global__ __launch_bounds__(1024) void replica_layout_kernel(const int32_t* __r
     wmap[i] = 0;
     place[i] = 0;
   }
+  __syncthreads();  // these stores complete before other threads overwrite them (the scan's barriers order LDS only)
   int v[4];
   int local = 0;
 #pragma unroll
