@@ -80,6 +80,58 @@ __device__ inline void rank_tile(const int* ecp, int ncp, int E, int* cnt, int32
   }
 }
 
+// Ranks of one tile's copies by all the block's waves: wave w takes copies
+// [64 w, 64 w + 64) (every wave of the block must call it). Within its 64
+// copies a lane's rank is the number of lanes below it with the same expert
+// (groups found by ballots over the expert-id bits) and the group's highest
+// lane stores the group size as the chunk's count of that expert; after a
+// barrier the counts become exclusive prefixes over the chunks, per expert,
+// and a copy's rank is its rank in its chunk plus the count of its expert in
+// the earlier chunks. Same result as rank_tile. cc: LDS scratch of
+// ceil(ncp / 64) E ints (at most kRankChunkInts); cnt [E] gets the tile's
+// histogram; ceil(ncp / 64) must not exceed the block's waves.
+constexpr int kRankChunkInts = 8192;
+// Whether a 1024-thread block over one 64-token tile ranks with all its waves.
+__host__ __device__ inline bool tile_ranks_by_waves(int k, int E) { return k <= 16 && k * E <= kRankChunkInts; }
+__device__ inline void rank_tile_waves(const int* ecp, int ncp, int E, int* cnt, int* cc, int32_t* rank) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nch = (ncp + 63) / 64;  // at most the block's waves: ncp <= 64 k, k <= 16
+  for (int i = threadIdx.x; i < nch * E; i += blockDim.x) cc[i] = 0;
+  lds_barrier();
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int my_e = -1, my_r = 0;  // this lane's copy in chunk `wave` (nch <= 16 = waves of the block)
+  if (wave < nch) {
+    const int i = wave * 64 + lane;
+    const int e = i < ncp ? ecp[i] : -1;
+    const bool active = e >= 0;
+    unsigned long long mask = __ballot(active);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = (e >> bit) & 1;
+      const unsigned long long m = __ballot(active && set);
+      mask &= set ? m : ~m;
+    }
+    if (active) {
+      my_e = e;
+      my_r = __popcll(mask & below);
+      if (63 - __clzll(mask) == lane) cc[wave * E + e] = __popcll(mask);
+    }
+  }
+  lds_barrier();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int w = 0; w < nch; ++w) {
+      const int c = cc[w * E + e];
+      cc[w * E + e] = run;
+      run += c;
+    }
+    cnt[e] = run;
+  }
+  lds_barrier();
+  if (rank && wave < nch && wave * 64 + lane < ncp)
+    rank[wave * 64 + lane] = my_e >= 0 ? my_r + cc[wave * E + my_e] : -1;
+}
+
 // ---- router (router.hip) ----
 // Number of d-slices S the scores are split into (partials part[S][T][E]).
 int router_splits(int64_t T, int64_t d, int E, bool bf16);
@@ -90,11 +142,11 @@ hipError_t launch_router_logits(const void* x, const void* wr, int64_t T, int64_
                                 int S, float* part, hipStream_t s);
 // Sums the S partials (slice order) and the bias, writes logits_out if given,
 // then top-k and gates; with tile_cnt, also the per-64-token-tile histogram
-// (only when route_builds_histogram(k)). When route_rank_limited(P, M) the
+// (only when route_builds_histogram(k, E, T)). When route_rank_limited(P, M) the
 // choice is limited to experts of the M best of P ranks (P <= 64, E % P == 0,
 // M * E/P >= k); with S > 1 or a bias and no logits_out, the summed scores are
 // then written over slice 0 of part.
-bool route_builds_histogram(int k);
+bool route_builds_histogram(int k, int E, int64_t T);
 bool route_rank_limited(int P, int M);
 // With tile_cnt, also the ranks of each tile's copies (rank [T, k], optional;
 // rank_tile).

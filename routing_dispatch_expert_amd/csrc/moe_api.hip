@@ -446,7 +446,7 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
   MOE_HIP_TRY(moe::launch_router_logits(x, W_router, T, d, E, bf16, splits, p.logits, s), "router logits");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTER, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTE, false, s), "event");
-  const bool fused_hist = moe::route_builds_histogram(k);
+  const bool fused_hist = moe::route_builds_histogram(k, E, T);
   const int64_t nt = moe::ceil_div(T, moe::kTileTokens);
   // the tile histogram comes with each copy's rank within its tile, kept in slot
   MOE_HIP_TRY(moe::launch_route(p.logits, splits, router_bias, T, E, k, nullptr, idx, w,
@@ -527,7 +527,7 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   // 1. the forward again: routing, buckets X, g, u, h (y is not needed: the
   //    gate gradients come from dh and h, step 4)
   const int splits = moe::router_splits(T, d, E, bf16);
-  const bool fused_hist = moe::route_builds_histogram(k);
+  const bool fused_hist = moe::route_builds_histogram(k, E, T);
   MOE_HIP_TRY(moe::launch_router_logits(x, W_router, T, d, E, bf16, splits, p.logits, s), "router logits");
   MOE_HIP_TRY(moe::launch_route(p.logits, splits, router_bias, T, E, k, nullptr, p.idx, p.w,
                                 fused_hist ? p.tile_cnt : nullptr, P, max_ranks, s),
@@ -697,7 +697,7 @@ int moe_layer_forward_replicated(const void* x, const void* W_router, const floa
 
   // routing, then each copy's token-order rank among its expert's copies
   const int splits = moe::router_splits(T, d, E, bf16);
-  const bool fused_hist = moe::route_builds_histogram(k);
+  const bool fused_hist = moe::route_builds_histogram(k, E, T);
   MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTER, false, s), "event");
   MOE_HIP_TRY(moe::launch_router_logits(x, W_router, T, d, E, bf16, splits, p.logits, s), "router logits");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTER, true, s), "event");

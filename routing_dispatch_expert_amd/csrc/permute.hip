@@ -23,15 +23,18 @@ namespace {
 
 // Per-tile expert histogram and ranks: tile_cnt[b][e] = copies of expert e
 // among tokens [64 b, 64 b + 64), and rank [T, k] (optional) of each copy
-// within its tile (rank_tile). Entries outside [0, E) are counted nowhere and
-// ranked -1 (dropped).
-__global__ __launch_bounds__(256) void tile_hist_kernel(const int32_t* __restrict__ idx,
-                                                        int64_t T, int k, int E,
-                                                        int32_t* __restrict__ tile_cnt,
-                                                        int32_t* __restrict__ rank) {
+// within its tile. Entries outside [0, E) are counted nowhere and ranked -1
+// (dropped). One 1024-thread block per tile; all 16 waves rank the tile's
+// copies (rank_tile_waves) when its chunk counts fit LDS (k <= 16, k E <=
+// 8192), else one wave (rank_tile).
+__global__ __launch_bounds__(1024) void tile_hist_kernel(const int32_t* __restrict__ idx,
+                                                         int64_t T, int k, int E,
+                                                         int32_t* __restrict__ tile_cnt,
+                                                         int32_t* __restrict__ rank) {
   extern __shared__ int sm[];
-  int* hist = sm;        // [E]
-  int* ecp = sm + E;     // [64 k]
+  int* hist = sm;                        // [E]
+  int* ecp = sm + E;                     // [64 k]
+  int* cc = ecp + kTileTokens * k;       // [k E] for the all-wave ranking
   const int64_t b = blockIdx.x;
   const int64_t t0 = b * kTileTokens;
   const int n = static_cast<int>(min<int64_t>(kTileTokens, T - t0)) * k;
@@ -41,8 +44,13 @@ __global__ __launch_bounds__(256) void tile_hist_kernel(const int32_t* __restric
     ecp[i] = static_cast<unsigned>(e) < static_cast<unsigned>(E) ? e : -1;
   }
   lds_barrier();
-  if (threadIdx.x < 64) rank_tile(ecp, n, E, hist, rank ? rank + t0 * k : nullptr);
-  lds_barrier();
+  int32_t* rk = rank ? rank + t0 * k : nullptr;
+  if (tile_ranks_by_waves(k, E)) {
+    rank_tile_waves(ecp, n, E, hist, cc, rk);
+  } else {
+    if (threadIdx.x < 64) rank_tile(ecp, n, E, hist, rk);
+    lds_barrier();
+  }
   for (int e = threadIdx.x; e < E; e += blockDim.x) tile_cnt[b * E + e] = hist[e];
 }
 
@@ -479,8 +487,9 @@ hipError_t launch_tile_hist(const int32_t* idx, int64_t T, int k, int E, int32_t
                             hipStream_t s, int32_t* rank) {
   const int64_t nt = ceil_div(T, kTileTokens);
   if (nt == 0) return hipSuccess;
-  const size_t shm = (static_cast<size_t>(E) + static_cast<size_t>(kTileTokens) * k) * sizeof(int);
-  tile_hist_kernel<<<dim3(static_cast<unsigned>(nt)), dim3(256), shm, s>>>(idx, T, k, E, tile_cnt, rank);
+  const size_t shm = (static_cast<size_t>(E) + static_cast<size_t>(kTileTokens) * k +
+                     (tile_ranks_by_waves(k, E) ? static_cast<size_t>(k) * E : 0)) * sizeof(int);
+  tile_hist_kernel<<<dim3(static_cast<unsigned>(nt)), dim3(1024), shm, s>>>(idx, T, k, E, tile_cnt, rank);
   return hipGetLastError();
 }
 

@@ -19,6 +19,12 @@ namespace {
 
 constexpr int kMaxRouterSplits = 16;  // d-slices of the router scores (partials summed in order)
 constexpr int kTiledSplits = 8;       // at most this many when a wave takes 2 or 4 token tiles
+// With this many experts or more and fewer 64-token tiles than kWideRouteTiles
+// (decode-sized batches), top-k takes a whole wave per token (16 tokens a
+// block, four times the blocks of 16-lane groups) and the tile histogram and
+// ranks come from the tile kernel that follows: the DeepSeek-V3 decode route
+// 39 -> 16 + 5 us. With 128 tiles (DeepSeek-V3 prefill) it measured even.
+constexpr int kWideRouteE = 128, kWideRouteTiles = 64;
 
 // ---------------------------------------------------------------------------
 // Scores on the matrix cores. Each wave is one work item: 16 MT tokens x
@@ -179,55 +185,6 @@ __device__ inline void insert_sorted(float (&lv)[KMAX], int (&li)[KMAX], float v
   }
 }
 
-// Ranks of one tile's copies by all the block's waves: wave w takes copies
-// [64 w, 64 w + 64) (every wave of the block must call it). Within its 64
-// copies a lane's rank is the number of lanes below it with the same expert
-// (groups found by ballots over the expert-id bits) and the group's highest
-// lane stores the group size as the chunk's count of that expert; after a
-// barrier the counts become exclusive prefixes over the chunks, per expert,
-// and a copy's rank is its rank in its chunk plus the count of its expert in
-// the earlier chunks. Same result as rank_tile. cc: LDS scratch of
-// ceil(ncp / 64) E ints; cnt [E] gets the tile's histogram.
-constexpr int kRankChunkInts = 8192;
-__device__ void rank_tile_waves(const int* ecp, int ncp, int E, int* cnt, int* cc, int32_t* rank) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nch = (ncp + 63) / 64;  // at most the block's waves: ncp <= 64 k, k <= 16
-  for (int i = threadIdx.x; i < nch * E; i += blockDim.x) cc[i] = 0;
-  lds_barrier();
-  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
-  const unsigned long long below = (1ull << lane) - 1ull;
-  int my_e = -1, my_r = 0;  // this lane's copy in chunk `wave` (nch <= 16 = waves of the block)
-  if (wave < nch) {
-    const int i = wave * 64 + lane;
-    const int e = i < ncp ? ecp[i] : -1;
-    const bool active = e >= 0;
-    unsigned long long mask = __ballot(active);
-    for (int bit = 0; bit < nbits; ++bit) {
-      const bool set = (e >> bit) & 1;
-      const unsigned long long m = __ballot(active && set);
-      mask &= set ? m : ~m;
-    }
-    if (active) {
-      my_e = e;
-      my_r = __popcll(mask & below);
-      if (63 - __clzll(mask) == lane) cc[wave * E + e] = __popcll(mask);
-    }
-  }
-  lds_barrier();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int run = 0;
-    for (int w = 0; w < nch; ++w) {
-      const int c = cc[w * E + e];
-      cc[w * E + e] = run;
-      run += c;
-    }
-    cnt[e] = run;
-  }
-  lds_barrier();
-  if (rank && wave < nch && wave * 64 + lane < ncp)
-    rank[wave * 64 + lane] = my_e >= 0 ? my_r + cc[wave * E + my_e] : -1;
-}
-
 template <int L, int KMAX, bool HIST, bool LIMIT>
 __global__ __launch_bounds__(1024) void route_kernel(const float* part, int S, const float* __restrict__ bias,
                                                      int64_t T, int E, int k, float* logits_out,
@@ -384,7 +341,7 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* part, int S, c
     const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock;
     const int ncp = static_cast<int>(min<int64_t>(kTokensPerBlock, T - t0)) * k;
     int32_t* rk = rank ? rank + t0 * k : nullptr;
-    if (k * E <= kRankChunkInts) {
+    if (tile_ranks_by_waves(k, E)) {
       rank_tile_waves(ecp, ncp, E, hist, ecp + kTokensPerBlock * k, rk);
     } else {
       if (threadIdx.x < 64) rank_tile(ecp, ncp, E, hist, rk);
@@ -414,7 +371,7 @@ template <int L, int KMAX, bool HIST, bool LIMIT>
 hipError_t route_launch(const RouteArgs& a, hipStream_t s) {
   const int64_t tpb = 1024 / L;
   // HIST: histogram [E], the tile's experts [64 k] and, for the ranking by all waves, its chunk counts [k E]
-  const size_t lds = (HIST ? (a.E + tpb * a.k + (a.k * a.E <= kRankChunkInts ? a.k * a.E : 0)) * sizeof(int) : 0) +
+  const size_t lds = (HIST ? (a.E + tpb * a.k + (tile_ranks_by_waves(a.k, a.E) ? a.k * a.E : 0)) * sizeof(int) : 0) +
                      (LIMIT ? tpb * a.P * sizeof(uint32_t) : 0);
   route_kernel<L, KMAX, HIST, LIMIT><<<dim3(static_cast<unsigned>(ceil_div(a.T, tpb))), dim3(1024), lds, s>>>(
       a.part, a.S, a.bias, a.T, a.E, a.k, a.logits_out, a.idx, a.w, a.tile_cnt, a.P, a.M, a.lsum, a.lsrc, a.rank);
@@ -427,6 +384,11 @@ hipError_t route_dispatch(const RouteArgs& a, hipStream_t s) {
     if (a.k <= 2) return route_launch<16, 2, true, LIMIT>(a, s);
     if (a.k <= 8) return route_launch<16, 8, true, LIMIT>(a, s);
     return route_launch<16, 16, true, LIMIT>(a, s);
+  }
+  if (a.E >= kWideRouteE && a.k <= 16 && ceil_div(a.T, kTileTokens) < kWideRouteTiles) {  // a wave per token
+    if (a.k <= 2) return route_launch<64, 2, false, LIMIT>(a, s);
+    if (a.k <= 8) return route_launch<64, 8, false, LIMIT>(a, s);
+    return route_launch<64, 16, false, LIMIT>(a, s);
   }
   if (a.k <= 2) return route_launch<16, 2, false, LIMIT>(a, s);
   if (a.k <= 8) return route_launch<16, 8, false, LIMIT>(a, s);
@@ -511,7 +473,9 @@ hipError_t launch_router_logits(const void* x, const void* wr, int64_t T, int64_
   return hipGetLastError();
 }
 
-bool route_builds_histogram(int k) { return k <= 16; }
+bool route_builds_histogram(int k, int E, int64_t T) {
+  return k <= 16 && (E < kWideRouteE || ceil_div(T, kTileTokens) >= kWideRouteTiles);
+}
 
 bool route_rank_limited(int P, int M) { return M > 0 && M < P; }
 
@@ -519,7 +483,7 @@ hipError_t launch_route(const float* part, int S, const float* bias, int64_t T, 
                         float* logits_out, int32_t* idx, float* w, int32_t* tile_cnt, int P, int M,
                         hipStream_t s, int32_t* rank) {
   if (T == 0) return hipSuccess;
-  if (tile_cnt && !route_builds_histogram(k)) return hipErrorInvalidValue;
+  if (tile_cnt && !route_builds_histogram(k, E, T)) return hipErrorInvalidValue;
   RouteArgs a{part, S, bias, T, E, k, logits_out, idx, w, tile_cnt, P, M, nullptr, nullptr, rank};
   if (!route_rank_limited(P, M)) return route_dispatch<false>(a, s);
   if (P > kMaxLimitRanks || E % P || static_cast<int64_t>(M) * (E / P) < k) return hipErrorInvalidValue;
