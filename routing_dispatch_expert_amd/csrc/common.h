@@ -161,13 +161,14 @@ hipError_t launch_tile_hist(const int32_t* idx, int64_t T, int k, int E, int32_t
 // Exclusive scan of the tile histogram over tiles, per expert; then counts,
 // totals, send counts and (if mtile_off != nullptr) the GEMM row-tile prefix
 // for row tiles of `bm` rows (and a second map for bm1 rows when mtile1 is
-// given). 1 <= P <= E <= 4096.
+// given). 1 <= P <= E <= 4096. The scan block also zeroes clear[0 .. n_clear)
+// (optional: the grouped GEMMs' split-K arrival counters).
 // place [E] (optional): rank of each bucket for the send counts (default e / (E/P)).
 hipError_t launch_scan(const int32_t* tile_cnt, int64_t nt, int E, int64_t C, int P,
                        int64_t row_bytes, int k, int64_t T, int32_t* tile_off, int32_t* routed,
                        int32_t* kept, int32_t* send, int64_t* totals, int bm, int32_t* mtile_off,
                        int32_t* src, hipStream_t s, const int32_t* place = nullptr, int bm1 = 0,
-                       int32_t* mtile1 = nullptr);
+                       int32_t* mtile1 = nullptr, int32_t* clear = nullptr, int n_clear = 0);
 // Slots from the scan and the in-tile ranks: slot [T, k] holds each copy's
 // rank within its tile on entry (route or tile histogram) and its slot (-1:
 // dropped) on exit; slot = tile_off + rank, kept below C. Also src (optional;
@@ -212,7 +213,8 @@ constexpr int kSplitUnits = 256;
 constexpr int kSplitTileElems = 320 * 256;
 struct SplitK {
   float* part;    // [kSplitUnits][kSplitTileElems]
-  int32_t* tick;  // [kSplitUnits]
+  int32_t* tick;  // [kSplitUnits]; each split tile's last block sets its counter back to zero
+  bool zeroed = false;  // the counters are known to be zero (no clearing launch before the GEMM)
 };
 size_t split_k_bytes();
 SplitK split_k_carve(void* base);  // base: 256-byte aligned, split_k_bytes() long

@@ -797,6 +797,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     if (tid == 0) arrival = atomicAdd(&tick[ti], 1);
     __syncthreads();
     if (arrival != split - 1) return;
+    if (tid == 0) tick[ti] = 0;  // every arrival is in: the counter is ready for the next launch
     __threadfence();
     // every partial, this block's own included, is read back in chunk order;
     // a group's s loads are in flight together (a load-add chain would wait
@@ -1284,11 +1285,11 @@ hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out,
   if constexpr (BM == 320 && BN == 256) {
     if (K % 128) return hipErrorInvalidValue;  // callers pick this tile only for K % 128 == 0
     const int G = sk ? resident_groups() : 0;
-    if (G > 0) {
+    if (G > 0 && !sk->zeroed) {
       const hipError_t err = launch_fill_i32(sk->tick, G, 0, s);
       if (err != hipSuccess) return err;
-      blocks += G;
     }
+    if (G > 0) blocks += G;
     // Each stage's loads are requested a sub-step early, except for SwiGLU
     // over experts of 64 or more column tiles: there (d_ff = 14336, K = 4096)
     // the early request measured 2% slower, against 1-4% faster elsewhere.
@@ -1312,11 +1313,11 @@ hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out,
       return hipGetLastError();
     }
     const int G = sk ? resident_groups() : 0;
-    if (G > 0) {
+    if (G > 0 && !sk->zeroed) {
       const hipError_t err = launch_fill_i32(sk->tick, G, 0, s);
       if (err != hipSuccess) return err;
-      blocks += G;  // the split round: at most G blocks beyond the whole tiles
     }
+    if (G > 0) blocks += G;  // the split round: at most G blocks beyond the whole tiles
     gemm_bf16_dma_kernel<SWIGLU, false, false, false, kDmaWaves>
         <<<dim3(static_cast<unsigned>(blocks)), dim3(kDmaWaves * 64), 0, s>>>(
         pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap, G > 0 ? sk->part : nullptr,
@@ -1370,11 +1371,11 @@ hipError_t launch_gemm_kmajor_b(const void* a, const int32_t* kept, const int32_
   const int64_t nt = ceil_div(N, 256);
   int64_t blocks = ceil_div(mt_max * nt, 8) * 8;
   const int G = sk ? resident_groups() : 0;
-  if (G > 0) {
+  if (G > 0 && !sk->zeroed) {
     const hipError_t err = launch_fill_i32(sk->tick, G, 0, s);
     if (err != hipSuccess) return err;
-    blocks += G;
   }
+  if (G > 0) blocks += G;
   const auto* pa = static_cast<const bf16_t*>(a);
   const auto* pb0 = static_cast<const bf16_t*>(b0);
   const auto* pb1 = static_cast<const bf16_t*>(b1);

@@ -458,8 +458,13 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
   const int bm_gu = moe::grouped_gemm_bm_gate_up(bf16, C, d);
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SLOTS, false, s), "event");
   if (!fused_hist) MOE_HIP_TRY(moe::launch_tile_hist(idx, T, k, E, p.tile_cnt, s, slot), "tile histogram");
+  // the scan also clears the GEMMs' split-K arrival counters (each split tile's
+  // last block leaves its counter at zero again, so GEMM 2 needs no clearing)
+  moe::SplitK sk = p.split;
+  sk.zeroed = sk.tick != nullptr;
   MOE_HIP_TRY(moe::launch_scan(p.tile_cnt, nt, E, C, P, d * eb, k, T, p.tile_off, routed, kept, send, totals, bm,
-                               p.mtile, src, s, nullptr, bm_gu, bm_gu != bm ? p.mtile_gu : nullptr),
+                               p.mtile, src, s, nullptr, bm_gu, bm_gu != bm ? p.mtile_gu : nullptr, sk.tick,
+                               sk.tick ? moe::kSplitUnits : 0),
               "scan");
   MOE_HIP_TRY(moe::launch_slots_from_ranks(idx, slot, p.tile_off, T, k, E, C, src, totals, s), "slots");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SLOTS, true, s), "event");
@@ -468,11 +473,11 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, false, s), "event");
   MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, bm_gu != bm ? p.mtile_gu : p.mtile, W_gate, W_up, E, C, d, d_ff,
-                                       bf16, p.h, s, nullptr, &p.split),
+                                       bf16, p.h, s, nullptr, &sk),
               "grouped gemm (gate, up)");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, false, s), "event");
-  MOE_HIP_TRY(moe::launch_gemm_down(p.h, kept, p.mtile, W_down, E, C, d, d_ff, bf16, p.y, s, nullptr, &p.split, bm),
+  MOE_HIP_TRY(moe::launch_gemm_down(p.h, kept, p.mtile, W_down, E, C, d, d_ff, bf16, p.y, s, nullptr, &sk, bm),
               "grouped gemm (down)");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_COMBINE, false, s), "event");

@@ -118,6 +118,8 @@ struct ScanTail {
   int bm0, bm1;
   int32_t *mtile0, *mtile1;
   const int32_t* place;
+  int32_t* clear;  // zeroed when given: n_clear words
+  int n_clear;
 };
 
 __device__ void scan_tail(const ScanTail& a, const int* kept_s, int* kpre, int* send_s, int* sh) {
@@ -159,6 +161,8 @@ __device__ void scan_tail(const ScanTail& a, const int* kept_s, int* kpre, int* 
   }
   if (a.mtile0) mtile_prefix(kept_s, a.E, a.bm0, a.mtile0, sh);
   if (a.mtile1) mtile_prefix(kept_s, a.E, a.bm1, a.mtile1, sh);
+  if (a.clear)
+    for (int i = tid; i < a.n_clear; i += blockDim.x) a.clear[i] = 0;
 }
 
 // The scan, one block of 1024 threads: per expert, the exclusive prefix over
@@ -496,9 +500,10 @@ hipError_t launch_tile_hist(const int32_t* idx, int64_t T, int k, int E, int32_t
 hipError_t launch_scan(const int32_t* tile_cnt, int64_t nt, int E, int64_t C, int P,
                        int64_t row_bytes, int k, int64_t T, int32_t* tile_off, int32_t* routed,
                        int32_t* kept, int32_t* send, int64_t* totals, int bm, int32_t* mtile_off,
-                       int32_t* src, hipStream_t s, const int32_t* place, int bm1, int32_t* mtile1) {
-  if (E > 4096 || P < 1 || P > E || nt * E >= (int64_t{1} << 31)) return hipErrorInvalidValue;
-  const ScanTail tail{C, row_bytes, T, E, P, k, send, totals, bm, bm1, mtile_off, mtile1, place};
+                       int32_t* src, hipStream_t s, const int32_t* place, int bm1, int32_t* mtile1,
+                       int32_t* clear, int n_clear) {
+  if (E > 4096 || P < 1 || P > E || nt * E >= (int64_t{1} << 31) || n_clear < 0) return hipErrorInvalidValue;
+  const ScanTail tail{C, row_bytes, T, E, P, k, send, totals, bm, bm1, mtile_off, mtile1, place, clear, n_clear};
   const size_t shm = (2 * static_cast<size_t>(E) + 1 + P) * sizeof(int);
   scan_kernel<<<dim3(1), dim3(1024), shm, s>>>(tile_cnt, nt, tile_off, routed, kept, tail);
   hipError_t err = hipGetLastError();
