@@ -12,8 +12,10 @@
 // Slot of copy i = t*k + j of expert e: the number of earlier copies (in
 // flattened token order) of the same expert. It is found as
 //   tile offset (scan of per-tile counts over earlier tiles)
-// + rank inside the tile (wave ballots over the expert-id bits).
-// Positions never come from atomics; only the order-free per-tile counts do.
+// + rank inside the tile (wave ballots over the expert-id bits; computed with
+//   the tile histogram, by the route kernel or tile_hist_kernel).
+// Positions never come from atomics; the only atomics are order-free integer
+// sums (per-rank send counts over a replica placement, fully dropped tokens).
 #include <algorithm>
 
 #include "common.h"
