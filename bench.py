@@ -177,7 +177,7 @@ def stage_of_kernel(short: str):
             return "router"                          # fp32-output score GEMM
         return "down"
     for prefix, stage in (("router_logits", "router"), ("route_kernel", "route"), ("scatter_rows", "scatter"),
-                          ("combine_kernel", "combine"), ("slots", "slots"), ("scan_kernel", "slots"),
+                          ("slot_scatter", "scatter"), ("combine_kernel", "combine"), ("slots", "slots"), ("scan_kernel", "slots"),
                           ("tile_hist", "slots")):
         if short.startswith(prefix):
             return stage
@@ -533,7 +533,9 @@ def main():
                     flush.sum()
                 step()
                 torch.cuda.synchronize()
-                acc += [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(len(moe.STAGES))]
+                # a stage that launched nothing recorded no events: no time
+                acc += [evs[2 * i].elapsed_time(evs[2 * i + 1]) if moe.moe_stage_ran(i) else 0.0
+                        for i in range(len(moe.STAGES))]
                 layer_ms.append(evs[0].elapsed_time(evs[-1]))
         finally:
             moe.moe_set_stage_events(None)

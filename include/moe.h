@@ -275,7 +275,8 @@ enum {
   MOE_STAGE_ROUTE = 1,    /* top-k and gates */
   MOE_STAGE_SLOTS = 2,    /* scan over token tiles, capacity, counts, GEMM tile maps, slots and drop
                              mask (and the tile histogram when top-k did not build it) */
-  MOE_STAGE_SCATTER = 3,  /* row copies into the buckets */
+  MOE_STAGE_SCATTER = 3,  /* row copies into the buckets (with short tile histograms also the scan and
+                             slots: one kernel, the SLOTS stage then empty) */
   MOE_STAGE_GATE_UP = 4,  /* grouped GEMM 1 with the SwiGLU product */
   MOE_STAGE_DOWN = 5,     /* grouped GEMM 2 */
   MOE_STAGE_COMBINE = 6,  /* inverse permutation and weighted sum */
@@ -286,9 +287,15 @@ enum {
  * hipEvent_t handles), moe_layer_forward and moe_layer_forward_replicated
  * on the calling thread record events[2 i] on their stream just before
  * stage i and events[2 i + 1] just after, so the caller can read each
- * stage's GPU time. events = NULL turns
+ * stage's GPU time. A stage that launches no kernel in a call records
+ * neither of its events (their old times stay). events = NULL turns
  * this off (the default). Error: n_events != 2 * MOE_NUM_STAGES. */
 int moe_set_stage_events(void* const* events, int n_events);
+
+/* *ran = 1 if the calling thread's last layer call with stage events set
+ * recorded stage `stage`'s events, 0 if that stage launched nothing (or no
+ * such call was made). Errors: ran NULL, stage outside [0, MOE_NUM_STAGES). */
+int moe_stage_ran(int32_t stage, int32_t* ran);
 
 /* Static description of a status code. */
 const char* moe_status_string(int status);

@@ -25,7 +25,7 @@ TOTALS = ("dropped", "fully_dropped_tokens", "padded_rows", "offrank_bytes")
 EXPORTS = ("moe_capacity", "moe_workspace_size", "moe_layer_forward", "moe_backward_workspace_size",
            "moe_layer_backward", "moe_replica_plan", "moe_replicated_workspace_size", "moe_layer_forward_replicated", "moe_router_workspace_size", "moe_router", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_permute_static", "moe_grouped_gemm_workspace_size",
-           "moe_grouped_gemm", "moe_combine", "moe_set_stage_events", "moe_status_string", "moe_last_error")
+           "moe_grouped_gemm", "moe_combine", "moe_set_stage_events", "moe_stage_ran", "moe_status_string", "moe_last_error")
 STAGES = ("router", "route", "slots", "scatter", "gate_up", "down", "combine")
 
 
@@ -68,6 +68,7 @@ _SIGS = {
     "moe_grouped_gemm": [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P, _SZ, _P],
     "moe_combine": [_P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I64, ctypes.c_int, _P, _P],
     "moe_set_stage_events": [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int],
+    "moe_stage_ran": [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)],
 }
 
 
@@ -274,6 +275,13 @@ def moe_set_stage_events(events):
         return
     arr = (ctypes.c_void_p * len(events))(*events)
     _check(lib().moe_set_stage_events(arr, len(events)), "moe_set_stage_events")
+
+
+def moe_stage_ran(stage: int) -> bool:
+    """Whether the last layer call with stage events recorded this stage's events."""
+    ran = ctypes.c_int32(0)
+    _check(lib().moe_stage_ran(stage, ctypes.byref(ran)), "moe_stage_ran")
+    return bool(ran.value)
 
 
 # ----------------------------------------------------------------- convenience

@@ -149,15 +149,15 @@ hipError_t launch_router_logits(const void* x, const void* wr, int64_t T, int64_
 bool route_builds_histogram(int k, int E, int64_t T);
 bool route_rank_limited(int P, int M);
 // With tile_cnt, also the ranks of each tile's copies (rank [T, k], optional;
-// rank_tile).
+// rank_tile). *zero = 0 when given (a counter the next kernel adds to).
 hipError_t launch_route(const float* part, int S, const float* bias, int64_t T, int E, int k,
                         float* logits_out, int32_t* idx, float* w, int32_t* tile_cnt, int P, int M,
-                        hipStream_t s, int32_t* rank = nullptr);
+                        hipStream_t s, int32_t* rank = nullptr, int64_t* zero = nullptr);
 
 // ---- permutation (permute.hip) ----
-// With rank, also the ranks of each tile's copies (rank_tile).
+// With rank, also the ranks of each tile's copies (rank_tile); *zero = 0 when given.
 hipError_t launch_tile_hist(const int32_t* idx, int64_t T, int k, int E, int32_t* tile_cnt,
-                            hipStream_t s, int32_t* rank = nullptr);
+                            hipStream_t s, int32_t* rank = nullptr, int64_t* zero = nullptr);
 // Exclusive scan of the tile histogram over tiles, per expert; then counts,
 // totals, send counts and (if mtile_off != nullptr) the GEMM row-tile prefix
 // for row tiles of `bm` rows (and a second map for bm1 rows when mtile1 is
@@ -176,6 +176,18 @@ hipError_t launch_scan(const int32_t* tile_cnt, int64_t nt, int E, int64_t C, in
 // kept copy (optional; the scan zeroed it). Experts outside [0, E) are dropped.
 hipError_t launch_slots_from_ranks(const int32_t* idx, int32_t* slot, const int32_t* tile_off, int64_t T, int k,
                                   int E, int64_t C, int32_t* src, int64_t* totals, hipStream_t s);
+// The scan and the slots with the row scatter in one launch (block 0 scans
+// while the others place and copy rows), when slot_scatter_fits(T, k, E):
+// k <= 32, E <= 4096 and at most 256 tile counts ahead of any token's copies
+// (k (nt - 1) <= 256). Outputs as launch_scan (place: default) followed by
+// launch_slots_from_ranks and launch_scatter_rows; slot holds the ranks on
+// entry; totals[1] must be zero on entry (zero it in the histogram launch).
+bool slot_scatter_fits(int64_t T, int k, int E);
+hipError_t launch_slot_scatter(const int32_t* tile_cnt, int E, int64_t C, int P, int64_t row_bytes, int k,
+                               int64_t T, int32_t* tile_off, int32_t* routed, int32_t* kept, int32_t* send,
+                               int64_t* totals, int bm, int32_t* mtile_off, int bm1, int32_t* mtile1,
+                               int32_t* clear, int n_clear, const void* x, const int32_t* idx, int32_t* slot,
+                               int32_t* src, void* buckets, hipStream_t s);
 // Replicated experts: instance offsets [E+1], expert [R] and rank [R] of each
 // instance; then the instance of each copy from its rank among its expert's copies.
 hipError_t launch_replica_layout(const int32_t* replicas, int E, int R, int P, int32_t* inst_off, int32_t* wmap,

@@ -18,10 +18,14 @@ namespace {
 thread_local char g_err[512] = "";
 thread_local hipEvent_t g_stage_ev[2 * MOE_NUM_STAGES];
 thread_local bool g_stage_ev_on = false;
+thread_local bool g_stage_ran[MOE_NUM_STAGES] = {};
 
-// Records the start (end = false) or end event of a stage when profiling is on.
-hipError_t stage_mark(int stage, bool end, hipStream_t s) {
+// Records the start (end = false) or end event of a stage when profiling is
+// on; a stage that launches nothing (empty) records neither.
+hipError_t stage_mark(int stage, bool end, hipStream_t s, bool empty = false) {
   if (!g_stage_ev_on) return hipSuccess;
+  g_stage_ran[stage] = !empty;
+  if (empty) return hipSuccess;
   return hipEventRecord(g_stage_ev[2 * stage + (end ? 1 : 0)], s);
 }
 
@@ -322,7 +326,17 @@ int run_permute(const void* x, const int32_t* topk_idx, int64_t T, int64_t d, in
   int32_t* tile_off = c.take<int32_t>(static_cast<size_t>(nt) * E);
   const int64_t row = d * elem_bytes(dtype);
   // ranks within each tile go to slot, then the slots (tile offset + rank) replace them
-  MOE_HIP_TRY(moe::launch_tile_hist(topk_idx, T, k, E, tile_cnt, s, slot), "tile histogram");
+  // short tile histograms: the scan runs beside the slots and the row copies
+  const bool one_pass = moe::slot_scatter_fits(T, k, E);
+  MOE_HIP_TRY(moe::launch_tile_hist(topk_idx, T, k, E, tile_cnt, s, slot, one_pass && totals ? totals + 1 : nullptr),
+              "tile histogram");
+  if (one_pass) {
+    MOE_HIP_TRY(moe::launch_slot_scatter(tile_cnt, E, C, P, row, k, T, tile_off, routed_count, kept_count,
+                                         send_count, totals, 0, nullptr, 0, nullptr, nullptr, 0, x, topk_idx, slot,
+                                         src, buckets, s),
+                "slots and scatter");
+    return MOE_OK;
+  }
   MOE_HIP_TRY(moe::launch_scan(tile_cnt, nt, E, C, P, row, k, T, tile_off, routed_count, kept_count, send_count,
                                totals, 0, nullptr, src, s),
               "scan");
@@ -388,6 +402,13 @@ int moe_set_stage_events(void* const* events, int n_events) {
   return MOE_OK;
 }
 
+int moe_stage_ran(int32_t stage, int32_t* ran) {
+  if (!ran) return fail(MOE_ERR_INVALID_ARG, "ran is NULL");
+  if (stage < 0 || stage >= MOE_NUM_STAGES) return fail(MOE_ERR_INVALID_ARG, "no stage %d", stage);
+  *ran = g_stage_ran[stage] ? 1 : 0;
+  return MOE_OK;
+}
+
 int moe_capacity(int64_t T, int32_t E, int32_t k, float cf, int64_t* C_out) {
   if (!C_out) return fail(MOE_ERR_INVALID_ARG, "C_out is NULL");
   int64_t C;
@@ -448,28 +469,43 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
   MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTE, false, s), "event");
   const bool fused_hist = moe::route_builds_histogram(k, E, T);
   const int64_t nt = moe::ceil_div(T, moe::kTileTokens);
+  // short tile histograms: the scan runs beside the slots and the row copies,
+  // which count fully dropped tokens into totals[1], zeroed by the histogram's kernel
+  const bool one_pass = moe::slot_scatter_fits(T, k, E);
+  int64_t* zero_t1 = one_pass ? totals + 1 : nullptr;
   // the tile histogram comes with each copy's rank within its tile, kept in slot
   MOE_HIP_TRY(moe::launch_route(p.logits, splits, router_bias, T, E, k, nullptr, idx, w,
-                                fused_hist ? p.tile_cnt : nullptr, P, max_ranks, s, fused_hist ? slot : nullptr),
+                                fused_hist ? p.tile_cnt : nullptr, P, max_ranks, s, fused_hist ? slot : nullptr,
+                                fused_hist ? zero_t1 : nullptr),
               "route");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTE, true, s), "event");
   // the scan also writes the counts, totals and both GEMMs' row-tile maps;
   // slots are the tile offsets plus the ranks
   const int bm_gu = moe::grouped_gemm_bm_gate_up(bf16, C, d);
-  MOE_HIP_TRY(stage_mark(MOE_STAGE_SLOTS, false, s), "event");
-  if (!fused_hist) MOE_HIP_TRY(moe::launch_tile_hist(idx, T, k, E, p.tile_cnt, s, slot), "tile histogram");
+  int32_t* mtile_gu = bm_gu != bm ? p.mtile_gu : nullptr;
+  const bool slots_empty = fused_hist && one_pass;  // then the scatter's kernel does all of it
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_SLOTS, false, s, slots_empty), "event");
+  if (!fused_hist) MOE_HIP_TRY(moe::launch_tile_hist(idx, T, k, E, p.tile_cnt, s, slot, zero_t1), "tile histogram");
   // the scan also clears the GEMMs' split-K arrival counters (each split tile's
   // last block leaves its counter at zero again, so GEMM 2 needs no clearing)
   moe::SplitK sk = p.split;
   sk.zeroed = sk.tick != nullptr;
-  MOE_HIP_TRY(moe::launch_scan(p.tile_cnt, nt, E, C, P, d * eb, k, T, p.tile_off, routed, kept, send, totals, bm,
-                               p.mtile, src, s, nullptr, bm_gu, bm_gu != bm ? p.mtile_gu : nullptr, sk.tick,
-                               sk.tick ? moe::kSplitUnits : 0),
-              "scan");
-  MOE_HIP_TRY(moe::launch_slots_from_ranks(idx, slot, p.tile_off, T, k, E, C, src, totals, s), "slots");
-  MOE_HIP_TRY(stage_mark(MOE_STAGE_SLOTS, true, s), "event");
+  const int n_clear = sk.tick ? moe::kSplitUnits : 0;
+  if (!one_pass) {
+    MOE_HIP_TRY(moe::launch_scan(p.tile_cnt, nt, E, C, P, d * eb, k, T, p.tile_off, routed, kept, send, totals, bm,
+                                 p.mtile, src, s, nullptr, bm_gu, mtile_gu, sk.tick, n_clear),
+                "scan");
+    MOE_HIP_TRY(moe::launch_slots_from_ranks(idx, slot, p.tile_off, T, k, E, C, src, totals, s), "slots");
+  }
+  MOE_HIP_TRY(stage_mark(MOE_STAGE_SLOTS, true, s, slots_empty), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, false, s), "event");
-  MOE_HIP_TRY(moe::launch_scatter_rows(x, idx, slot, T, k, C, d * eb, buckets, s), "scatter");
+  if (one_pass)
+    MOE_HIP_TRY(moe::launch_slot_scatter(p.tile_cnt, E, C, P, d * eb, k, T, p.tile_off, routed, kept, send, totals,
+                                         bm, p.mtile, bm_gu, mtile_gu, sk.tick, n_clear, x, idx, slot, src, buckets,
+                                         s),
+                "slots and scatter");
+  else
+    MOE_HIP_TRY(moe::launch_scatter_rows(x, idx, slot, T, k, C, d * eb, buckets, s), "scatter");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, false, s), "event");
   MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, bm_gu != bm ? p.mtile_gu : p.mtile, W_gate, W_up, E, C, d, d_ff,

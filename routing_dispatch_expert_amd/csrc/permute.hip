@@ -25,15 +25,16 @@ namespace {
 
 // Per-tile expert histogram and ranks: tile_cnt[b][e] = copies of expert e
 // among tokens [64 b, 64 b + 64), and rank [T, k] (optional) of each copy
-// within its tile. Entries outside [0, E) are counted nowhere and ranked -1
+// within its tile; *zero = 0 when given. Entries outside [0, E) are counted nowhere and ranked -1
 // (dropped). One 1024-thread block per tile; all 16 waves rank the tile's
 // copies (rank_tile_waves) when its chunk counts fit LDS (k <= 16, k E <=
 // 8192), else one wave (rank_tile).
 __global__ __launch_bounds__(1024) void tile_hist_kernel(const int32_t* __restrict__ idx,
                                                          int64_t T, int k, int E,
                                                          int32_t* __restrict__ tile_cnt,
-                                                         int32_t* __restrict__ rank) {
+                                                         int32_t* __restrict__ rank, int64_t* zero) {
   extern __shared__ int sm[];
+  if (zero && blockIdx.x == 0 && threadIdx.x == 0) *zero = 0;
   int* hist = sm;                        // [E]
   int* ecp = sm + E;                     // [64 k]
   int* cc = ecp + kTileTokens * k;       // [k E] for the all-wave ranking
@@ -122,6 +123,7 @@ struct ScanTail {
   const int32_t* place;
   int32_t* clear;  // zeroed when given: n_clear words
   int n_clear;
+  bool leave_t1;   // totals[1] is zeroed before the scan and counted beside it
 };
 
 __device__ void scan_tail(const ScanTail& a, const int* kept_s, int* kpre, int* send_s, int* sh) {
@@ -157,7 +159,7 @@ __device__ void scan_tail(const ScanTail& a, const int* kept_s, int* kpre, int* 
   if (a.totals && tid == 0) {
     const int send0 = a.place ? send_s[0] : kpre[per];
     a.totals[0] = a.T * a.k - n_kept;
-    a.totals[1] = 0;  // fully dropped tokens: added by the slot kernel that follows
+    if (!a.leave_t1) a.totals[1] = 0;  // fully dropped tokens: added by the slot kernel that follows
     a.totals[2] = static_cast<int64_t>(a.E) * a.C - n_kept;
     a.totals[3] = static_cast<int64_t>(n_kept - send0) * a.row_bytes;
   }
@@ -172,12 +174,12 @@ __device__ void scan_tail(const ScanTail& a, const int* kept_s, int* kpre, int* 
 // the tail. Experts are taken EB at a time (EB = 64 .. 1024, a power of two
 // covering E where it can), 1024 / EB lanes per expert; lane ly sums a
 // contiguous run of tiles, the runs are scanned in LDS, and each lane writes
-// its run's offsets. The first 16 counts of a run are loaded at once and stay
+// its run's offsets. The first F counts of a run are loaded at once and stay
 // in registers between the two passes; the rest go out eight at a time.
-__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ tile_cnt, int64_t nt,
-                                                    int32_t* __restrict__ tile_off, int32_t* __restrict__ routed,
-                                                    int32_t* __restrict__ kept, ScanTail tail) {
-  extern __shared__ int sm[];
+template <int F>
+__device__ void scan_block(const int32_t* __restrict__ tile_cnt, int64_t nt, int32_t* __restrict__ tile_off,
+                           int32_t* __restrict__ routed, int32_t* __restrict__ kept, const ScanTail& tail,
+                           int* sm /* dynamic LDS: 2 E + 1 + P ints */) {
   const int E = tail.E;
   int* kept_s = sm;              // [E]
   int* kpre = sm + E;            // [E + 1]
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   const int chunk = (ntt + LY - 1) / LY;
   const int b0 = min(ntt, ly * chunk);
   const int b1 = min(ntt, b0 + chunk);
-  constexpr int B = 8, F = 16;  // loads per batch; counts kept in registers
+  constexpr int B = 8;  // loads per batch
   for (int base = 0; base < E; base += EB) {
     const int e = base + ex;
     int first[F];
@@ -242,6 +244,13 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
     lds_barrier();  // part is taken again
   }
   scan_tail(tail, kept_s, kpre, send_s, sh);
+}
+
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ tile_cnt, int64_t nt,
+                                                    int32_t* __restrict__ tile_off, int32_t* __restrict__ routed,
+                                                    int32_t* __restrict__ kept, ScanTail tail) {
+  extern __shared__ int sm[];
+  scan_block<16>(tile_cnt, nt, tile_off, routed, kept, tail, sm);
 }
 
 // Row-tile map from counts given by the caller: each count is clamped to
@@ -434,6 +443,154 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restri
   }
 }
 
+// Slots and row scatter in one launch, for layers with a short tile
+// histogram. Block 0 runs the scan (counts, totals but totals[1], tile maps,
+// cleared counters); every other block takes 1024 / H tokens, H threads
+// each, and a token's threads sum the histogram of the earlier tiles
+// themselves, so no block waits for the scan: slot = that sum for the copy's
+// expert + the copy's rank within its tile (held in slot on entry), kept
+// below C, exactly as tile_off + rank. With BYE (E a power of two <= 64,
+// E (nt - 1) <= 512) the threads add up every expert's column over the
+// earlier tiles, which are the first tl E words of the histogram (no load
+// waits for the copies' experts); otherwise each sums the counts of one copy's
+// expert (k (nt - 1) <= 256). The row words (U per lane) are loaded while the
+// counts are on their way; the copies then go out as in scatter_rows_kernel.
+// totals[1] must be zero on entry: each block adds its fully dropped tokens
+// once.
+template <int U, int H, bool BYE>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void slot_scatter_kernel(
+    const int32_t* __restrict__ tile_cnt, int64_t nt, int32_t* __restrict__ tile_off, int32_t* __restrict__ routed,
+    int32_t* __restrict__ kept, ScanTail tail, const uint4* __restrict__ x, const int32_t* __restrict__ idx,
+    int32_t* __restrict__ slot, int32_t* __restrict__ src, int64_t V, uint4* __restrict__ buckets) {
+  static_assert(H == 64 || H == 128 || H == 256, "one to four waves per token");
+  extern __shared__ int sm[];
+  if (blockIdx.x == 0) {
+    scan_block<4>(tile_cnt, nt, tile_off, routed, kept, tail, sm);  // short runs: few counts kept
+    return;
+  }
+  constexpr int KM = 32;                      // copies per token at most
+  constexpr int PW = BYE ? 64 : KM;           // prefix sums per token: experts or copies
+  constexpr int TB = 1024 / H;                // tokens per block
+  constexpr int PI = (BYE ? 512 : 256) / H;   // histogram counts per thread at most
+  __shared__ int psum[TB * PW], sls[TB * KM], es[TB * KM], fd[TB];
+  const int E = tail.E, k = tail.k;
+  const int64_t T = tail.T, C = tail.C;
+  const int q = threadIdx.x / H, u = threadIdx.x % H, wl = threadIdx.x & 63;
+  const bool first_wave = u < 64;  // of the token's H / 64
+  const int64_t t = (static_cast<int64_t>(blockIdx.x) - 1) * TB + q;
+  const bool live = t < T;
+  const int tl = static_cast<int>(t / kTileTokens);  // earlier tiles: 0 .. tl - 1
+  const int npre = live ? (BYE ? E : k) * tl : 0;
+  for (int j = u; j < (BYE ? E : k); j += H) psum[q * PW + j] = 0;
+  if (u == 0) fd[q] = 0;
+  // the copies' experts and ranks (first wave), the prefix operands, the row
+  int e0 = -1, r0 = -1;
+  if (live && first_wave && wl < k) {
+    e0 = idx[t * k + wl];
+    r0 = slot[t * k + wl];
+  }
+  int pj[PI], pe[PI], pv[PI];
+  const uint4* xr = x + t * V;
+  uint4 val[U];
+  if constexpr (BYE) {
+#pragma unroll
+    for (int i = 0; i < PI; ++i) {
+      const int c = u + i * H;
+      pv[i] = c < npre ? tile_cnt[c] : 0;  // tile c / E, expert c % E = u % E (E divides 64)
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PI; ++i) {
+      const int c = u + i * H;
+      pj[i] = 0;
+      pe[i] = -1;
+      if (c < npre) {
+        pj[i] = c / tl;
+        pe[i] = idx[t * k + pj[i]];
+      }
+    }
+  }
+  if (live) {
+#pragma unroll
+    for (int w = 0; w < U; ++w) {
+      const int64_t v = u + H * w;
+      if (v < V) val[w] = xr[v];
+    }
+  }
+  if constexpr (!BYE) {
+#pragma unroll
+    for (int i = 0; i < PI; ++i) {
+      pv[i] = 0;
+      if (static_cast<unsigned>(pe[i]) < static_cast<unsigned>(E))
+        pv[i] = tile_cnt[static_cast<int64_t>(u + i * H - pj[i] * tl) * E + pe[i]];
+    }
+  }
+  lds_barrier();  // psum is zero
+  if constexpr (BYE) {
+    // this lane's counts all belong to expert u % E; lanes E apart add up in
+    // the wave, whose first E lanes then add to LDS
+    int v = 0;
+#pragma unroll
+    for (int i = 0; i < PI; ++i) v += pv[i];
+    for (int off = E; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+    if (wl < E && v) atomicAdd(&psum[q * PW + wl], v);  // integer sums: any order
+  } else {
+#pragma unroll
+    for (int i = 0; i < PI; ++i)
+      if (pv[i]) atomicAdd(&psum[q * PW + pj[i]], pv[i]);  // integer sums: any order
+  }
+  lds_barrier();
+  int sl = -1;
+  if (live && first_wave && wl < k) {
+    if (static_cast<unsigned>(e0) < static_cast<unsigned>(E) && r0 >= 0) {
+      const int64_t v = psum[q * PW + (BYE ? e0 : wl)] + static_cast<int64_t>(r0);
+      if (v < C) sl = static_cast<int>(v);
+    }
+    slot[t * k + wl] = sl;  // this lane read the rank from the same word
+    if (sl >= 0 && src) src[static_cast<int64_t>(e0) * C + sl] = static_cast<int32_t>(t * k + wl);
+    sls[q * KM + wl] = sl;
+    es[q * KM + wl] = e0;
+  }
+  if (first_wave) {
+    const uint64_t any = __ballot(sl >= 0);
+    if (live && wl == 0 && any == 0) fd[q] = 1;
+  }
+  lds_barrier();
+  int s_l = -1, e_l = 0;
+  if (live && wl < k) {
+    s_l = sls[q * KM + wl];
+    e_l = es[q * KM + wl];
+  }
+  const uint64_t keep = __ballot(s_l >= 0);
+  if (threadIdx.x == 0 && tail.totals) {
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < TB; ++i) c += fd[i];
+    if (c) atomicAdd(reinterpret_cast<unsigned long long*>(&tail.totals[1]), static_cast<unsigned long long>(c));
+  }
+  if (!live) return;
+  for (int64_t v0 = u; v0 < V; v0 += H * U) {
+    if (v0 != u) {
+#pragma unroll
+      for (int w = 0; w < U; ++w) {
+        const int64_t v = v0 + H * w;
+        if (v < V) val[w] = xr[v];
+      }
+    }
+    for (uint64_t m = keep; m; m &= m - 1) {
+      const int j = __builtin_ctzll(m);
+      const int e = __builtin_amdgcn_readlane(e_l, j);
+      const int sj = __builtin_amdgcn_readlane(s_l, j);
+      uint4* dst = buckets + (static_cast<int64_t>(e) * C + sj) * V;
+#pragma unroll
+      for (int w = 0; w < U; ++w) {
+        const int64_t v = v0 + H * w;
+        if (v < V) store_stream(&dst[v], val[w]);
+      }
+    }
+  }
+}
+
 // Replica layout, one block: inst_off [E+1] = exclusive prefix of the replica
 // counts (each taken as at least 1), expert of each instance (wmap [R]) and its
 // rank (place [R]): replica j of expert e on rank (e / (E/P) + j) mod P.
@@ -490,12 +647,13 @@ __global__ __launch_bounds__(256) void instance_kernel(const int32_t* __restrict
 }  // namespace
 
 hipError_t launch_tile_hist(const int32_t* idx, int64_t T, int k, int E, int32_t* tile_cnt,
-                            hipStream_t s, int32_t* rank) {
+                            hipStream_t s, int32_t* rank, int64_t* zero) {
   const int64_t nt = ceil_div(T, kTileTokens);
   if (nt == 0) return hipSuccess;
   const size_t shm = (static_cast<size_t>(E) + static_cast<size_t>(kTileTokens) * k +
                      (tile_ranks_by_waves(k, E) ? static_cast<size_t>(k) * E : 0)) * sizeof(int);
-  tile_hist_kernel<<<dim3(static_cast<unsigned>(nt)), dim3(1024), shm, s>>>(idx, T, k, E, tile_cnt, rank);
+  tile_hist_kernel<<<dim3(static_cast<unsigned>(nt)), dim3(1024), shm, s>>>(idx, T, k, E, tile_cnt, rank,
+                                                                             zero);
   return hipGetLastError();
 }
 
@@ -593,6 +751,62 @@ hipError_t launch_scatter_rows(const void* x, const int32_t* idx, const int32_t*
     scatter_rows_kernel<4><<<grid, dim3(256), 0, s>>>(xv, idx, slot, T, k, C, V, bv);
   else
     scatter_rows_kernel<8><<<grid, dim3(256), 0, s>>>(xv, idx, slot, T, k, C, V, bv);
+  return hipGetLastError();
+}
+
+namespace {
+// the one-pass kernel sums every expert's column of the earlier tiles
+bool slot_scatter_by_expert(int64_t nt, int E) { return E <= 64 && (E & (E - 1)) == 0 && (nt - 1) * E <= 512; }
+}  // namespace
+
+bool slot_scatter_fits(int64_t T, int k, int E) {
+  const int64_t nt = ceil_div(T, kTileTokens);
+  return T > 0 && k <= 32 && E <= 4096 && ((nt - 1) * k <= 256 || slot_scatter_by_expert(nt, E));
+}
+
+hipError_t launch_slot_scatter(const int32_t* tile_cnt, int E, int64_t C, int P, int64_t row_bytes, int k,
+                               int64_t T, int32_t* tile_off, int32_t* routed, int32_t* kept, int32_t* send,
+                               int64_t* totals, int bm, int32_t* mtile_off, int bm1, int32_t* mtile1,
+                               int32_t* clear, int n_clear, const void* x, const int32_t* idx, int32_t* slot,
+                               int32_t* src, void* buckets, hipStream_t s) {
+  if (!slot_scatter_fits(T, k, E) || P < 1 || P > E || n_clear < 0) return hipErrorInvalidValue;
+  const int64_t nt = ceil_div(T, kTileTokens);
+  ScanTail tail{C, row_bytes, T, E, P, k, send, totals, bm, bm1, mtile_off, mtile1, nullptr, clear, n_clear};
+  tail.leave_t1 = true;
+  const size_t shm = (2 * static_cast<size_t>(E) + 1 + P) * sizeof(int);
+  const auto* xv = static_cast<const uint4*>(x);
+  auto* bv = static_cast<uint4*>(buckets);
+  const int64_t V = row_bytes / 16;
+  // threads per token: the fewest of 64, 128, 256 that cover the row with four
+  // words a lane (one word for rows of at most 64), 256 with eight beyond 1024
+  const bool bye = slot_scatter_by_expert(nt, E);
+  auto go = [&](auto u_c, auto h_c) {
+    constexpr int U = decltype(u_c)::value, H = decltype(h_c)::value;
+    const dim3 grid(static_cast<unsigned>(1 + ceil_div(T, 1024 / H)));
+    if (bye)
+      slot_scatter_kernel<U, H, true><<<grid, dim3(1024), shm, s>>>(tile_cnt, nt, tile_off, routed, kept, tail, xv,
+                                                                    idx, slot, src, V, bv);
+    else
+      slot_scatter_kernel<U, H, false><<<grid, dim3(1024), shm, s>>>(tile_cnt, nt, tile_off, routed, kept, tail, xv,
+                                                                     idx, slot, src, V, bv);
+  };
+  using I1 = std::integral_constant<int, 1>;
+  using I4 = std::integral_constant<int, 4>;
+  using I8 = std::integral_constant<int, 8>;
+  if (V <= 64)
+    go(I1{}, std::integral_constant<int, 64>{});
+  else if (V <= 256)
+    go(I4{}, std::integral_constant<int, 64>{});
+  else if (V <= 512)
+    go(I4{}, std::integral_constant<int, 128>{});
+  else if (V <= 1024)
+    go(I4{}, std::integral_constant<int, 256>{});
+  else
+    go(I8{}, std::integral_constant<int, 256>{});
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || !src) return err;
+  const unsigned gx = static_cast<unsigned>(std::min<int64_t>(ceil_div(C, 256), 64));
+  src_padding_kernel<<<dim3(gx, static_cast<unsigned>(E)), dim3(256), 0, s>>>(kept, C, E, src);
   return hipGetLastError();
 }
 

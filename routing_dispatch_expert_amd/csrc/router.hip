@@ -190,7 +190,8 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* part, int S, c
                                                      int64_t T, int E, int k, float* logits_out,
                                                      int32_t* __restrict__ idx, float* __restrict__ w,
                                                      int32_t* __restrict__ tile_cnt, int P, int M,
-                                                     float* lsum, const float* lsrc, int32_t* __restrict__ rank) {
+                                                     float* lsum, const float* lsrc, int32_t* __restrict__ rank,
+                                                     int64_t* zero) {
   constexpr int kTokensPerBlock = 1024 / L;
   static_assert(!HIST || kTokensPerBlock == kTileTokens, "one block per histogram tile");
   extern __shared__ int smem[];
@@ -201,6 +202,7 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* part, int S, c
   const int tok = threadIdx.x / L;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + tok;
   const bool valid = t < T;
+  if (zero && blockIdx.x == 0 && threadIdx.x == 0) *zero = 0;
   if (HIST)
     for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   if (LIMIT)
@@ -365,6 +367,7 @@ struct RouteArgs {
   float* lsum;
   const float* lsrc;
   int32_t* rank;
+  int64_t* zero;
 };
 
 template <int L, int KMAX, bool HIST, bool LIMIT>
@@ -374,7 +377,8 @@ hipError_t route_launch(const RouteArgs& a, hipStream_t s) {
   const size_t lds = (HIST ? (a.E + tpb * a.k + (tile_ranks_by_waves(a.k, a.E) ? a.k * a.E : 0)) * sizeof(int) : 0) +
                      (LIMIT ? tpb * a.P * sizeof(uint32_t) : 0);
   route_kernel<L, KMAX, HIST, LIMIT><<<dim3(static_cast<unsigned>(ceil_div(a.T, tpb))), dim3(1024), lds, s>>>(
-      a.part, a.S, a.bias, a.T, a.E, a.k, a.logits_out, a.idx, a.w, a.tile_cnt, a.P, a.M, a.lsum, a.lsrc, a.rank);
+      a.part, a.S, a.bias, a.T, a.E, a.k, a.logits_out, a.idx, a.w, a.tile_cnt, a.P, a.M, a.lsum, a.lsrc, a.rank,
+      a.zero);
   return hipGetLastError();
 }
 
@@ -481,10 +485,10 @@ bool route_rank_limited(int P, int M) { return M > 0 && M < P; }
 
 hipError_t launch_route(const float* part, int S, const float* bias, int64_t T, int E, int k,
                         float* logits_out, int32_t* idx, float* w, int32_t* tile_cnt, int P, int M,
-                        hipStream_t s, int32_t* rank) {
+                        hipStream_t s, int32_t* rank, int64_t* zero) {
   if (T == 0) return hipSuccess;
   if (tile_cnt && !route_builds_histogram(k, E, T)) return hipErrorInvalidValue;
-  RouteArgs a{part, S, bias, T, E, k, logits_out, idx, w, tile_cnt, P, M, nullptr, nullptr, rank};
+  RouteArgs a{part, S, bias, T, E, k, logits_out, idx, w, tile_cnt, P, M, nullptr, nullptr, rank, zero};
   if (!route_rank_limited(P, M)) return route_dispatch<false>(a, s);
   if (P > kMaxLimitRanks || E % P || static_cast<int64_t>(M) * (E / P) < k) return hipErrorInvalidValue;
   // Where pass 3 finds the summed scores: logits_out when asked for, the single

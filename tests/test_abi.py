@@ -35,6 +35,16 @@ def test_status_strings():
     assert moe.status_string(7) == "unknown status"
 
 
+def test_stage_ran_host_only():
+    # no layer call with events on this thread yet: nothing recorded
+    assert [moe.moe_stage_ran(i) for i in range(len(moe.STAGES))] == [False] * len(moe.STAGES)
+    for bad in (-1, len(moe.STAGES)):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_stage_ran(bad)
+        assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    assert moe.lib().moe_stage_ran(0, None) == moe.MOE_ERR_INVALID_ARG
+
+
 def test_capacity_host_only():
     assert [moe.moe_capacity(*a) for a in [(64, 8, 2, 1.25), (4096, 8, 2, 1.25), (8192, 256, 8, 1.25),
                                          (16384, 64, 6, 1.0), (64, 256, 8, 2.0)]] == [20, 1280, 320, 1536, 4]

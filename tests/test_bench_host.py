@@ -27,6 +27,7 @@ def test_short_names_and_stages():
     assert bench.stage_of_kernel("gemm_bf16_skinny_kernel<true>") == "gate_up"
     assert bench.stage_of_kernel("gemm_bf16_skinny_kernel<false>") == "down"
     assert bench.stage_of_kernel("scatter_rows_kernel<4>") == "scatter"
+    assert bench.stage_of_kernel("slot_scatter_kernel<2>") == "scatter"
     assert bench.stage_of_kernel("combine_kernel<true, 4>") == "combine"
     assert bench.stage_of_kernel("scan_kernel") == "slots"
     assert bench.stage_of_kernel("slots_from_ranks_kernel") == "slots"

@@ -152,6 +152,35 @@ def test_layer_is_deterministic():
                            b[key].view(torch.uint8) if b[key].dtype == torch.bfloat16 else b[key]), key
 
 
+@pytest.mark.parametrize("T,one_pass", [(2000, True), (9000, False)])
+def test_stage_events_change_nothing(T, one_pass):
+    # k (nt - 1) tile counts ahead of the last token: 4 * 31 = 124 (one kernel
+    # places and copies the rows, the slots stage is empty) or 4 * 140 = 560
+    wl = moe_inputs.custom(T=T, d=256, E=16, k=4, d_ff=256, cf=0.8, seed=78, P=4)
+    dw = tuple(to_dev(a, wl.dtype) for a in wl.all_expert_weights())
+    a = run_layer(wl, *dw)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(moe.STAGES))]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    moe.moe_set_stage_events([e.cuda_event for e in evs])
+    try:
+        b = run_layer(wl, *dw)
+        ran = [moe.moe_stage_ran(i) for i in range(len(moe.STAGES))]
+    finally:
+        moe.moe_set_stage_events(None)
+    want = [True] * len(moe.STAGES)
+    want[moe.STAGES.index("slots")] = not one_pass
+    assert ran == want
+    for i in range(len(moe.STAGES)):
+        if ran[i]:
+            assert evs[2 * i].elapsed_time(evs[2 * i + 1]) >= 0
+    for key in ("out", "topk_idx", "topk_w", "slot", "src", "routed_count", "kept_count", "send_count", "totals",
+                "buckets"):
+        assert torch.equal(a[key].view(torch.uint8) if a[key].dtype == torch.bfloat16 else a[key],
+                           b[key].view(torch.uint8) if b[key].dtype == torch.bfloat16 else b[key]), key
+
+
 # ---------------------------------------------------------- named workloads ---
 
 def _sample_tokens(wl, ref_slot, n_rand, seed):
