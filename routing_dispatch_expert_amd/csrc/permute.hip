@@ -443,21 +443,22 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restri
   }
 }
 
-// Slots and row scatter in one launch, for layers with a short tile
-// histogram. Block 0 runs the scan (counts, totals but totals[1], tile maps,
-// cleared counters); every other block takes 1024 / H tokens, H threads
-// each, and a token's threads sum the histogram of the earlier tiles
-// themselves, so no block waits for the scan: slot = that sum for the copy's
-// expert + the copy's rank within its tile (held in slot on entry), kept
-// below C, exactly as tile_off + rank. With BYE (E a power of two <= 64,
-// E (nt - 1) <= 512) the threads add up every expert's column over the
-// earlier tiles, which are the first tl E words of the histogram (no load
-// waits for the copies' experts); otherwise each sums the counts of one copy's
-// expert (k (nt - 1) <= 256). The row words (U per lane) are loaded while the
-// counts are on their way; the copies then go out as in scatter_rows_kernel.
-// totals[1] must be zero on entry: each block adds its fully dropped tokens
-// once.
-template <int U, int H, bool BYE>
+// Slots and row scatter in one launch, for layers whose earlier tiles'
+// counts are few enough for each block to add up. Block 0 runs the scan
+// (counts, totals but totals[1], tile maps, cleared split-K counters); every
+// other block takes 1024 / H tokens of one 64-token tile, H threads each, and
+// adds up the tile histogram over the earlier tiles itself, so no block waits
+// for the scan: slot = that sum for the copy's expert + the copy's rank within
+// its tile (held in slot on entry), kept below C, exactly as tile_off + rank.
+// With BP (E a power of two <= 1024, E (nt - 1) <= 65536) the whole block sums
+// every expert's column, the first tl E words of the histogram (thread i's
+// counts all belong to expert i % E, at most 64 of them, 16 loads in flight);
+// otherwise each token's threads sum the column of each copy's expert (k (nt
+// - 1) <= 256, one count per thread). The row words (U per lane) are loaded
+// first, while the counts are on their way; the copies then go out as in
+// scatter_rows_kernel. totals[1] must be zero on entry: each block adds its
+// fully dropped tokens once.
+template <int U, int H, bool BP>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void slot_scatter_kernel(
     const int32_t* __restrict__ tile_cnt, int64_t nt, int32_t* __restrict__ tile_off, int32_t* __restrict__ routed,
     int32_t* __restrict__ kept, ScanTail tail, const uint4* __restrict__ x, const int32_t* __restrict__ idx,
@@ -468,37 +469,58 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
     scan_block<4>(tile_cnt, nt, tile_off, routed, kept, tail, sm);  // short runs: few counts kept
     return;
   }
-  constexpr int KM = 32;                      // copies per token at most
-  constexpr int PW = BYE ? 64 : KM;           // prefix sums per token: experts or copies
-  constexpr int TB = 1024 / H;                // tokens per block
-  constexpr int PI = (BYE ? 512 : 256) / H;   // histogram counts per thread at most
-  __shared__ int psum[TB * PW], sls[TB * KM], es[TB * KM], fd[TB];
+  constexpr int KM = 32;          // copies per token at most
+  constexpr int TB = 1024 / H;    // tokens per block, all of one tile
+  constexpr int PI = 256 / H;     // per-copy counts per thread at most
+  __shared__ int psum[BP ? 1024 : TB * KM], sls[TB * KM], es[TB * KM], fd[TB];
   const int E = tail.E, k = tail.k;
   const int64_t T = tail.T, C = tail.C;
-  const int q = threadIdx.x / H, u = threadIdx.x % H, wl = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int q = tid / H, u = tid % H, wl = tid & 63;
   const bool first_wave = u < 64;  // of the token's H / 64
   const int64_t t = (static_cast<int64_t>(blockIdx.x) - 1) * TB + q;
   const bool live = t < T;
-  const int tl = static_cast<int>(t / kTileTokens);  // earlier tiles: 0 .. tl - 1
-  const int npre = live ? (BYE ? E : k) * tl : 0;
-  for (int j = u; j < (BYE ? E : k); j += H) psum[q * PW + j] = 0;
+  const int tl = static_cast<int>(t / kTileTokens);  // earlier tiles: 0 .. tl - 1 (one value per block)
+  if constexpr (BP) {
+    for (int e = tid; e < E; e += 1024) psum[e] = 0;
+  } else {
+    if (u < k) psum[q * KM + u] = 0;
+  }
   if (u == 0) fd[q] = 0;
-  // the copies' experts and ranks (first wave), the prefix operands, the row
+  // the copies' experts and ranks (first wave), the row, the prefix operands
   int e0 = -1, r0 = -1;
   if (live && first_wave && wl < k) {
     e0 = idx[t * k + wl];
     r0 = slot[t * k + wl];
   }
-  int pj[PI], pe[PI], pv[PI];
   const uint4* xr = x + t * V;
   uint4 val[U];
-  if constexpr (BYE) {
+  if (live) {
 #pragma unroll
-    for (int i = 0; i < PI; ++i) {
-      const int c = u + i * H;
-      pv[i] = c < npre ? tile_cnt[c] : 0;  // tile c / E, expert c % E = u % E (E divides 64)
+    for (int w = 0; w < U; ++w) {
+      const int64_t v = u + H * w;
+      if (v < V) val[w] = xr[v];
     }
+  }
+  if constexpr (BP) {
+    const int npre = E * tl;  // the block's first token is live
+    constexpr int B = 16;
+    int acc = 0;
+    for (int c0 = 0; c0 < npre; c0 += B * 1024) {
+      int v[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        const int c = c0 + i * 1024 + tid;
+        v[i] = c < npre ? tile_cnt[c] : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < B; ++i) acc += v[i];
+    }
+    lds_barrier();  // psum is zero
+    if (acc) atomicAdd(&psum[tid & (E - 1)], acc);  // integer sums: any order
   } else {
+    const int npre = live ? k * tl : 0;
+    int pj[PI], pe[PI], pv[PI];
 #pragma unroll
     for (int i = 0; i < PI; ++i) {
       const int c = u + i * H;
@@ -509,41 +531,22 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
         pe[i] = idx[t * k + pj[i]];
       }
     }
-  }
-  if (live) {
-#pragma unroll
-    for (int w = 0; w < U; ++w) {
-      const int64_t v = u + H * w;
-      if (v < V) val[w] = xr[v];
-    }
-  }
-  if constexpr (!BYE) {
 #pragma unroll
     for (int i = 0; i < PI; ++i) {
       pv[i] = 0;
       if (static_cast<unsigned>(pe[i]) < static_cast<unsigned>(E))
         pv[i] = tile_cnt[static_cast<int64_t>(u + i * H - pj[i] * tl) * E + pe[i]];
     }
-  }
-  lds_barrier();  // psum is zero
-  if constexpr (BYE) {
-    // this lane's counts all belong to expert u % E; lanes E apart add up in
-    // the wave, whose first E lanes then add to LDS
-    int v = 0;
-#pragma unroll
-    for (int i = 0; i < PI; ++i) v += pv[i];
-    for (int off = E; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
-    if (wl < E && v) atomicAdd(&psum[q * PW + wl], v);  // integer sums: any order
-  } else {
+    lds_barrier();  // psum is zero
 #pragma unroll
     for (int i = 0; i < PI; ++i)
-      if (pv[i]) atomicAdd(&psum[q * PW + pj[i]], pv[i]);  // integer sums: any order
+      if (pv[i]) atomicAdd(&psum[q * KM + pj[i]], pv[i]);  // integer sums: any order
   }
   lds_barrier();
   int sl = -1;
   if (live && first_wave && wl < k) {
     if (static_cast<unsigned>(e0) < static_cast<unsigned>(E) && r0 >= 0) {
-      const int64_t v = psum[q * PW + (BYE ? e0 : wl)] + static_cast<int64_t>(r0);
+      const int64_t v = psum[BP ? e0 : q * KM + wl] + static_cast<int64_t>(r0);
       if (v < C) sl = static_cast<int>(v);
     }
     slot[t * k + wl] = sl;  // this lane read the rank from the same word
@@ -755,13 +758,15 @@ hipError_t launch_scatter_rows(const void* x, const int32_t* idx, const int32_t*
 }
 
 namespace {
-// the one-pass kernel sums every expert's column of the earlier tiles
-bool slot_scatter_by_expert(int64_t nt, int E) { return E <= 64 && (E & (E - 1)) == 0 && (nt - 1) * E <= 512; }
+// each block of the one-pass kernel sums every expert's column of the earlier tiles
+bool slot_scatter_block_prefix(int64_t nt, int E) {
+  return E <= 1024 && (E & (E - 1)) == 0 && (nt - 1) * E <= 65536;
+}
 }  // namespace
 
 bool slot_scatter_fits(int64_t T, int k, int E) {
   const int64_t nt = ceil_div(T, kTileTokens);
-  return T > 0 && k <= 32 && E <= 4096 && ((nt - 1) * k <= 256 || slot_scatter_by_expert(nt, E));
+  return T > 0 && k <= 32 && E <= 4096 && ((nt - 1) * k <= 256 || slot_scatter_block_prefix(nt, E));
 }
 
 hipError_t launch_slot_scatter(const int32_t* tile_cnt, int E, int64_t C, int P, int64_t row_bytes, int k,
@@ -779,11 +784,11 @@ hipError_t launch_slot_scatter(const int32_t* tile_cnt, int E, int64_t C, int P,
   const int64_t V = row_bytes / 16;
   // threads per token: the fewest of 64, 128, 256 that cover the row with four
   // words a lane (one word for rows of at most 64), 256 with eight beyond 1024
-  const bool bye = slot_scatter_by_expert(nt, E);
+  const bool bp = slot_scatter_block_prefix(nt, E);
   auto go = [&](auto u_c, auto h_c) {
     constexpr int U = decltype(u_c)::value, H = decltype(h_c)::value;
     const dim3 grid(static_cast<unsigned>(1 + ceil_div(T, 1024 / H)));
-    if (bye)
+    if (bp)
       slot_scatter_kernel<U, H, true><<<grid, dim3(1024), shm, s>>>(tile_cnt, nt, tile_off, routed, kept, tail, xv,
                                                                     idx, slot, src, V, bv);
     else
