@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void router_logits_bf16(const bf16_t* __restri
                                                           const bf16_t* __restrict__ wr, int64_t T,
                                                           int64_t d, int E, int S, int64_t kper,
                                                           float* __restrict__ part) {
-  constexpr int U = MT == 1 ? 4 : 2;  // k-steps whose loads are in flight together
+  constexpr int U = MT <= 2 ? 4 : 2;  // k-steps whose loads are in flight together
   const int lane = threadIdx.x & 63;
   const int64_t tt = ceil_div(T, 16 * MT);
   const int64_t ec = ceil_div(E, 16 * NT);
@@ -81,6 +81,10 @@ __global__ __launch_bounds__(256) void router_logits_bf16(const bf16_t* __restri
 #pragma unroll
       for (int j = 0; j < NT; ++j) b[u][j] = *reinterpret_cast<const bf16x8*>(wp[j] + k0 + 32 * u);
     }
+    // every load of the group goes out before the first product (left to
+    // itself the scheduler interleaves them, keeping about two k-steps in
+    // flight: 12.0 -> 11.0 us on T = 4096, d = 4096, E = 8 with U = 4)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
