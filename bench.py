@@ -19,7 +19,10 @@ with EXTRA replicas dealt to the most loaded experts of the same batch.
 
 With --backward a step is one call of moe_layer_backward instead (the
 gradients of x, the router and the expert weights for a seeded dout), and the
-line reports backward tokens/s.
+line reports backward tokens/s. With --saved as well, a step is one call of
+moe_layer_backward_saved on the state of a forward that kept its
+activations; the line also gives that forward's time and that of the two
+together.
 
 With --counters-summary no GPU work is done: the rocprofv3 counter CSVs of
 the profiling passes (PROFILE_PASSES, each a run of this script under
@@ -79,6 +82,9 @@ def parse():
                     help="in the per-stage loop, read this many MiB before each step so that L2 and the "
                          "Infinity Cache hold nothing of the layer's data (0: no flush)")
     ap.add_argument("--backward", action="store_true", help="time moe_layer_backward instead of the forward")
+    ap.add_argument("--saved", action="store_true",
+                    help="with --backward: time moe_layer_backward_saved on the state of a forward that kept its "
+                         "activations, and that forward, and the two together")
     ap.add_argument("--replicas", type=int, default=-1, metavar="EXTRA",
                     help="time moe_layer_forward_replicated with EXTRA replicas dealt greedily to the most loaded "
                          "experts (counts from one plain forward of the same batch)")
@@ -304,11 +310,36 @@ def run_backward(args, wl, moe, torch, np, dev, to_dev, host_w):
     ws_bytes = moe.moe_backward_workspace_size(T, d, d_ff, E, k, cf, P, wl.dtype)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    kept_state = None
+    if args.saved:  # a forward that keeps its routing, buckets and activations
+        C = moe.moe_capacity(T, E, k, cf)
+        i32 = dict(dtype=torch.int32, device=dev)
+        kept_state = {"out": torch.empty_like(x), "topk_idx": torch.empty((T, k), **i32),
+                      "topk_w": torch.empty((T, k), dtype=torch.float32, device=dev),
+                      "slot": torch.empty((T, k), **i32), "routed_count": torch.empty(E, **i32),
+                      "kept_count": torch.empty(E, **i32), "send_count": torch.empty(P, **i32),
+                      "totals": torch.empty(4, dtype=torch.int64, device=dev),
+                      "buckets": torch.empty((E, C, d), dtype=x.dtype, device=dev)}
+        for name in ("g", "u", "h"):
+            kept_state[name] = torch.empty((E, C, d_ff), dtype=x.dtype, device=dev)
+        fws_bytes = moe.moe_workspace_size(T, d, d_ff, E, k, cf, P, wl.dtype)
+        fws = torch.empty(fws_bytes, dtype=torch.uint8, device=dev)
+
+        def forward_keep():
+            moe.moe_layer_forward(x, wr, bias, wg, wu, wd, T, d, d_ff, E, k, cf, P, wl.max_ranks, wl.dtype,
+                                  kept_state["out"], kept_state, fws, fws_bytes, stream)
+
+        forward_keep()
 
     def step():
-        moe.moe_layer_backward(x, wr, bias, wg, wu, wd, dout, T, d, d_ff, E, k, cf, P, wl.max_ranks, wl.dtype,
-                               outs["dx"], outs["dW_router"], outs["d_bias"], outs["dW_gate"], outs["dW_up"],
-                               outs["dW_down"], ws, ws_bytes, stream)
+        if kept_state is None:
+            moe.moe_layer_backward(x, wr, bias, wg, wu, wd, dout, T, d, d_ff, E, k, cf, P, wl.max_ranks, wl.dtype,
+                                   outs["dx"], outs["dW_router"], outs["d_bias"], outs["dW_gate"], outs["dW_up"],
+                                   outs["dW_down"], ws, ws_bytes, stream)
+        else:
+            moe.moe_layer_backward_saved(x, wr, bias, wg, wu, wd, dout, T, d, d_ff, E, k, cf, P, wl.max_ranks,
+                                         wl.dtype, kept_state, outs["dx"], outs["dW_router"], outs["d_bias"],
+                                         outs["dW_gate"], outs["dW_up"], outs["dW_down"], ws, ws_bytes, stream)
 
     for _ in range(args.warmup):
         step()
@@ -322,14 +353,28 @@ def run_backward(args, wl, moe, torch, np, dev, to_dev, host_w):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1) / args.steps
-    print(f"[bench] backward: timed {args.steps} steps: {wall * 1e3 / args.steps:.3f} ms/step wall, "
-          f"{gpu_ms:.3f} ms/step GPU", file=sys.stderr, flush=True)
+    print(f"[bench] backward{' from the kept state' if args.saved else ''}: timed {args.steps} steps: "
+          f"{wall * 1e3 / args.steps:.3f} ms/step wall, {gpu_ms:.3f} ms/step GPU", file=sys.stderr, flush=True)
+    keep_ms = train_ms = None
+    if args.saved:
+        def timed(fn):
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            for _ in range(args.steps):
+                fn()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t1) * 1e3 / args.steps
+
+        keep_ms = timed(forward_keep)
+        train_ms = timed(lambda: (forward_keep(), step()))
+        print(f"[bench] forward keeping its activations: {keep_ms:.3f} ms/step; with the backward from that "
+              f"state: {train_ms:.3f} ms/step", file=sys.stderr, flush=True)
     import oracle
     r = oracle.layer_forward(wl.x, wl.wr, lambda e: (host_w[0][e], host_w[1][e], host_w[2][e]), T, d, d_ff, E, k,
                              cf, wl.dtype, P=P, bias=wl.bias_vec, tokens=np.arange(0), max_ranks=wl.max_ranks)
     n_kept = int(r["kept"].sum())
     algo = 12 * n_kept * d * d_ff  # dh, dX (two), dWd, dWg, dWu: 2 N d d_ff flop each
-    done = algo + 4 * n_kept * d * d_ff  # plus the recomputed g and u
+    done = algo + (0 if args.saved else 4 * n_kept * d * d_ff)  # plus the recomputed g and u
     tf = algo / gpu_ms / 1e9
     cpu = None
     if not args.no_cpu_baseline:
@@ -348,7 +393,8 @@ def run_backward(args, wl, moe, torch, np, dev, to_dev, host_w):
                "sample": f"backward of the first {S} of {T} tokens as a layer of their own (capacity for {S} "
                          f"tokens), fp64 numpy, median of 3 runs: {dt:.1f} s each"}
     line = {
-        "metric": "backward tokens/s per MoE layer (gradients of x, router and expert weights)",
+        "metric": "backward tokens/s per MoE layer (gradients of x, router and expert weights)"
+                  + (" from the forward's kept state" if args.saved else ""),
         "value": round(T * args.steps / wall, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
@@ -356,6 +402,8 @@ def run_backward(args, wl, moe, torch, np, dev, to_dev, host_w):
         "config": {"workload": wl.name, "T": T, "d": d, "E": E, "k": k, "d_ff": d_ff, "cf": cf, "P": P,
                    "max_ranks": wl.max_ranks, "N_kept": n_kept},
         "gpu_ms_per_step": round(gpu_ms, 4),
+        "forward_keeping_state_ms": None if keep_ms is None else round(keep_ms, 4),
+        "forward_and_backward_ms": None if train_ms is None else round(train_ms, 4),
         "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_TFLOPS[wl.dtype], "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_TFLOPS[wl.dtype], 4), "traffic": None,
                      "kernel": "whole backward step (expert-gradient flops over step time)",
@@ -438,6 +486,8 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
+    if args.saved and not args.backward:
+        sys.exit("--saved goes with --backward")
     if args.device_weights:
         if args.backward or args.replicas >= 0:
             sys.exit("--device-weights serves the plain forward's counter passes only")

@@ -90,6 +90,16 @@ typedef struct {
   void* buckets;         /* [E, C, d] dtype; rank p's send buffer is experts
                             [p*E/P, (p+1)*E/P), a contiguous slice */
   int32_t* instance;     /* [T, k] replica instance of each copy (replicated layer only) */
+  /* The expert activations, kept for moe_layer_backward_saved (plain layer
+   * only; the replicated layer ignores them): g = X_e W_gate[e]^T, u = X_e
+   * W_up[e]^T and h = silu(g) * u, each [E, C, d_ff] dtype, rows < kept_count
+   * written (the others left as they were). Given all three, the layer
+   * computes g and u with two plain grouped GEMMs and h from their rounded
+   * values, as the backward does, instead of the one GEMM that yields h; else
+   * none of them is written. */
+  void* g;
+  void* u;
+  void* h;
 } moe_stats_t;
 
 /* Expert capacity C = ceil(cf * k * T / E), evaluated in IEEE double as
@@ -147,6 +157,20 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
                        int32_t max_ranks, moe_dtype_t dtype, void* dx, void* dW_router,
                        float* d_bias, void* dW_gate, void* dW_up, void* dW_down, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/* The backward pass from the forward's kept state: as moe_layer_backward,
+ * but the routing (topk_idx, topk_w), the buckets and the activations g, u, h
+ * come from `saved`, the stats of a moe_layer_forward call on the same inputs
+ * that kept them (all six pointers non-NULL), instead of being recomputed;
+ * the counts and slots are derived again from topk_idx. The results equal
+ * moe_layer_backward's bit for bit. Errors as moe_layer_backward, and a NULL
+ * saved array. */
+int moe_layer_backward_saved(const void* x, const void* W_router, const float* router_bias,
+                             const void* W_gate, const void* W_up, const void* W_down, const void* dout,
+                             int64_t T, int64_t d, int64_t d_ff, int32_t E, int32_t k, float cf, int32_t P,
+                             int32_t max_ranks, moe_dtype_t dtype, const moe_stats_t* saved, void* dx,
+                             void* dW_router, float* d_bias, void* dW_gate, void* dW_up, void* dW_down,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Hot-expert replication ([EP-guide] section 6 "Optimizations", "Expert
  * Replication": a popular expert is replicated on several devices and its

@@ -23,7 +23,7 @@ MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 TOTALS = ("dropped", "fully_dropped_tokens", "padded_rows", "offrank_bytes")
 
 EXPORTS = ("moe_capacity", "moe_workspace_size", "moe_layer_forward", "moe_backward_workspace_size",
-           "moe_layer_backward", "moe_replica_plan", "moe_replicated_workspace_size", "moe_layer_forward_replicated", "moe_router_workspace_size", "moe_router", "moe_route",
+           "moe_layer_backward", "moe_layer_backward_saved", "moe_replica_plan", "moe_replicated_workspace_size", "moe_layer_forward_replicated", "moe_router_workspace_size", "moe_router", "moe_route",
            "moe_permute_workspace_size", "moe_permute", "moe_permute_static", "moe_grouped_gemm_workspace_size",
            "moe_grouped_gemm", "moe_combine", "moe_set_stage_events", "moe_stage_ran", "moe_status_string", "moe_last_error")
 STAGES = ("router", "route", "slots", "scatter", "gate_up", "down", "combine")
@@ -39,7 +39,8 @@ class moe_stats_t(ctypes.Structure):
     _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("slot", ctypes.c_void_p),
                 ("src", ctypes.c_void_p), ("routed_count", ctypes.c_void_p),
                 ("kept_count", ctypes.c_void_p), ("send_count", ctypes.c_void_p),
-                ("totals", ctypes.c_void_p), ("buckets", ctypes.c_void_p), ("instance", ctypes.c_void_p)]
+                ("totals", ctypes.c_void_p), ("buckets", ctypes.c_void_p), ("instance", ctypes.c_void_p),
+                ("g", ctypes.c_void_p), ("u", ctypes.c_void_p), ("h", ctypes.c_void_p)]
 
 
 _lib = None
@@ -52,6 +53,8 @@ _SIGS = {
     "moe_backward_workspace_size": [_I64, _I64, _I64, _I32, _I32, _F32, _I32, ctypes.c_int, _P],
     "moe_layer_backward": [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _F32, _I32, _I32, ctypes.c_int,
                            _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "moe_layer_backward_saved": [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _F32, _I32, _I32,
+                                 ctypes.c_int, ctypes.POINTER(moe_stats_t), _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "moe_replica_plan": [_P, _I32, _I32, _P],
     "moe_replicated_workspace_size": [_I64, _I64, _I64, _I32, _I32, _F32, _I32, _I32, ctypes.c_int, _P],
     "moe_layer_forward_replicated": [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _F32, _I32, _I32, _P,
@@ -186,6 +189,18 @@ def moe_layer_backward(x, W_router, router_bias, W_gate, W_up, W_down, dout, T, 
            "moe_layer_backward")
 
 
+def moe_layer_backward_saved(x, W_router, router_bias, W_gate, W_up, W_down, dout, T, d, d_ff, E, k, cf, P,
+                             max_ranks, dtype, saved, dx, dW_router, d_bias, dW_gate, dW_up, dW_down, workspace,
+                             workspace_bytes, stream=None):
+    """saved: the stats dict of a moe_layer_forward call that kept g, u and h."""
+    _check(lib().moe_layer_backward_saved(_ptr(x), _ptr(W_router), _ptr(router_bias), _ptr(W_gate), _ptr(W_up),
+                                          _ptr(W_down), _ptr(dout), T, d, d_ff, E, k, cf, P, max_ranks,
+                                          _dtype(dtype), _stats(saved), _ptr(dx), _ptr(dW_router), _ptr(d_bias),
+                                          _ptr(dW_gate), _ptr(dW_up), _ptr(dW_down), _ptr(workspace),
+                                          workspace_bytes, _stream(stream)),
+           "moe_layer_backward_saved")
+
+
 def moe_replica_plan(routed_count, extra):
     """Host-side replica counts (numpy int32 array of length E) from routed counts."""
     import numpy as np
@@ -293,12 +308,14 @@ def _require(t, name, torch_dtype, shape):
 
 
 def forward(x, W_router, W_gate, W_up, W_down, k, cf, P=1, router_bias=None, stream=None,
-            want_buckets=False, want_src=False, workspace=None, max_ranks=0):
+            want_buckets=False, want_src=False, workspace=None, max_ranks=0, keep_activations=False):
     """Run the layer once on torch device tensors; returns a dict of outputs.
 
     x [T, d]; W_router [E, d]; W_gate, W_up [E, d_ff, d]; W_down [E, d, d_ff]
     (bf16 or fp32, all the same dtype); router_bias [E] fp32 or None;
     max_ranks > 0 limits each token's experts to that many of the P ranks.
+    keep_activations: also return the buckets and g, u, h [E, C, d_ff], the
+    state backward(..., saved=result) takes instead of recomputing it.
     """
     import torch
     T, d = x.shape
@@ -324,10 +341,13 @@ def forward(x, W_router, W_gate, W_up, W_down, k, cf, P=1, router_bias=None, str
         "send_count": torch.empty(P, **i32),
         "totals": torch.empty(4, dtype=torch.int64, device=dev),
     }
-    if want_buckets:
+    if want_buckets or keep_activations:
         res["buckets"] = torch.empty((E, C, d), dtype=dt, device=dev)
     if want_src:
         res["src"] = torch.empty((E, C), **i32)
+    if keep_activations:
+        for name in ("g", "u", "h"):
+            res[name] = torch.empty((E, C, d_ff), dtype=dt, device=dev)
     nbytes = moe_workspace_size(T, d, d_ff, E, k, cf, P, dt)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
@@ -338,10 +358,12 @@ def forward(x, W_router, W_gate, W_up, W_down, k, cf, P=1, router_bias=None, str
 
 
 def backward(x, W_router, W_gate, W_up, W_down, dout, k, cf, P=1, router_bias=None, stream=None, max_ranks=0,
-             workspace=None, want_d_bias=False):
+             workspace=None, want_d_bias=False, saved=None):
     """Gradients of the layer for dout on torch device tensors; returns a dict
     dx, dW_router, d_bias (fp32, when router_bias is given or want_d_bias),
-    dW_gate, dW_up, dW_down, workspace."""
+    dW_gate, dW_up, dW_down, workspace. saved: the result of
+    forward(..., keep_activations=True) on the same inputs, whose routing,
+    buckets and activations are then used instead of being recomputed."""
     import torch
     T, d = x.shape
     E = W_router.shape[0]
@@ -359,9 +381,14 @@ def backward(x, W_router, W_gate, W_up, W_down, dout, k, cf, P=1, router_bias=No
     nbytes = moe_backward_workspace_size(T, d, d_ff, E, k, cf, P, dt)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
-    moe_layer_backward(x, W_router, router_bias, W_gate, W_up, W_down, dout, T, d, d_ff, E, k, cf, P, max_ranks, dt,
-                       res["dx"], res["dW_router"], res["d_bias"], res["dW_gate"], res["dW_up"], res["dW_down"],
-                       workspace, nbytes, stream)
+    if saved is None:
+        moe_layer_backward(x, W_router, router_bias, W_gate, W_up, W_down, dout, T, d, d_ff, E, k, cf, P, max_ranks,
+                           dt, res["dx"], res["dW_router"], res["d_bias"], res["dW_gate"], res["dW_up"],
+                           res["dW_down"], workspace, nbytes, stream)
+    else:
+        moe_layer_backward_saved(x, W_router, router_bias, W_gate, W_up, W_down, dout, T, d, d_ff, E, k, cf, P,
+                                 max_ranks, dt, saved, res["dx"], res["dW_router"], res["d_bias"], res["dW_gate"],
+                                 res["dW_up"], res["dW_down"], workspace, nbytes, stream)
     res["workspace"] = workspace
     return res
 

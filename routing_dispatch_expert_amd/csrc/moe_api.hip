@@ -508,12 +508,26 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
     MOE_HIP_TRY(moe::launch_scatter_rows(x, idx, slot, T, k, C, d * eb, buckets, s), "scatter");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, false, s), "event");
-  MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, bm_gu != bm ? p.mtile_gu : p.mtile, W_gate, W_up, E, C, d, d_ff,
-                                       bf16, p.h, s, nullptr, &sk),
-              "grouped gemm (gate, up)");
+  int32_t* map_gu = bm_gu != bm ? p.mtile_gu : p.mtile;
+  void* h = p.h;
+  if (S.g && S.u && S.h) {
+    // g and u kept for the backward: the two plain GEMMs and the SwiGLU
+    // product of their rounded values, exactly as the backward recomputes them
+    h = S.h;
+    const int bmo = bf16 ? bm_gu : 0;
+    MOE_HIP_TRY(moe::launch_gemm_down(buckets, kept, map_gu, W_gate, E, C, d_ff, d, bf16, S.g, s, nullptr, &sk, bmo),
+                "grouped gemm (gate)");
+    MOE_HIP_TRY(moe::launch_gemm_down(buckets, kept, map_gu, W_up, E, C, d_ff, d, bf16, S.u, s, nullptr, &sk, bmo),
+                "grouped gemm (up)");
+    MOE_HIP_TRY(moe::launch_swiglu_fwd(S.g, S.u, h, kept, E, C, d_ff, bf16, s), "swiglu");
+  } else {
+    MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, map_gu, W_gate, W_up, E, C, d, d_ff, bf16, h, s, nullptr,
+                                         &sk),
+                "grouped gemm (gate, up)");
+  }
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, false, s), "event");
-  MOE_HIP_TRY(moe::launch_gemm_down(p.h, kept, p.mtile, W_down, E, C, d, d_ff, bf16, p.y, s, nullptr, &sk, bm),
+  MOE_HIP_TRY(moe::launch_gemm_down(h, kept, p.mtile, W_down, E, C, d, d_ff, bf16, p.y, s, nullptr, &sk, bm),
               "grouped gemm (down)");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_COMBINE, false, s), "event");
@@ -532,11 +546,15 @@ int moe_backward_workspace_size(int64_t T, int64_t d, int64_t d_ff, int32_t E, i
   return MOE_OK;
 }
 
-int moe_layer_backward(const void* x, const void* W_router, const float* router_bias, const void* W_gate,
-                       const void* W_up, const void* W_down, const void* dout, int64_t T, int64_t d, int64_t d_ff,
-                       int32_t E, int32_t k, float cf, int32_t P, int32_t max_ranks, moe_dtype_t dtype, void* dx,
-                       void* dW_router, float* d_bias, void* dW_gate, void* dW_up, void* dW_down,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// The backward; with `saved` (a kept forward state) the routing, buckets and
+// activations are taken from it instead of being recomputed.
+int layer_backward(const void* x, const void* W_router, const float* router_bias, const void* W_gate,
+                   const void* W_up, const void* W_down, const void* dout, int64_t T, int64_t d, int64_t d_ff,
+                   int32_t E, int32_t k, float cf, int32_t P, int32_t max_ranks, moe_dtype_t dtype,
+                   const moe_stats_t* saved, void* dx, void* dW_router, float* d_bias, void* dW_gate, void* dW_up,
+                   void* dW_down, void* workspace, size_t workspace_bytes, void* stream) {
   int64_t C;
   int st = check_layer_shape(T, d, d_ff, E, k, cf, P, dtype, &C);
   if (st != MOE_OK) return st;
@@ -544,6 +562,8 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   if (!x || !W_router || !W_gate || !W_up || !W_down || !dout || !dx || !dW_router || !dW_gate || !dW_up ||
       !dW_down)
     return fail(MOE_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (saved && (!saved->topk_idx || !saved->topk_w || !saved->buckets || !saved->g || !saved->u || !saved->h))
+    return fail(MOE_ERR_INVALID_ARG, "saved state needs topk_idx, topk_w, buckets, g, u and h");
   const int eb = elem_bytes(dtype);
   const size_t row_bytes = static_cast<size_t>(T * d * eb);
   if (overlaps(dx, row_bytes, x, row_bytes) || overlaps(dx, row_bytes, dout, row_bytes))
@@ -566,22 +586,31 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   const int64_t F = d_ff;
 
   // 1. the forward again: routing, buckets X, g, u, h (y is not needed: the
-  //    gate gradients come from dh and h, step 4)
+  //    gate gradients come from dh and h, step 4); with a kept state only the
+  //    counts, slots and per-expert copy lists, from its routing
+  int32_t* idx = saved ? saved->topk_idx : p.idx;
+  float* w = saved ? saved->topk_w : p.w;
+  void* X = saved ? saved->buckets : p.buckets;
+  void* g = saved ? saved->g : b.g;
+  void* u = saved ? saved->u : b.u;
+  void* h = saved ? saved->h : p.h;
   const int splits = moe::router_splits(T, d, E, bf16);
-  const bool fused_hist = moe::route_builds_histogram(k, E, T);
-  MOE_HIP_TRY(moe::launch_router_logits(x, W_router, T, d, E, bf16, splits, p.logits, s), "router logits");
-  MOE_HIP_TRY(moe::launch_route(p.logits, splits, router_bias, T, E, k, nullptr, p.idx, p.w,
-                                fused_hist ? p.tile_cnt : nullptr, P, max_ranks, s),
-              "route");
-  if (!fused_hist) MOE_HIP_TRY(moe::launch_tile_hist(p.idx, T, k, E, p.tile_cnt, s), "tile histogram");
+  const bool fused_hist = !saved && moe::route_builds_histogram(k, E, T);
+  if (!saved) {
+    MOE_HIP_TRY(moe::launch_router_logits(x, W_router, T, d, E, bf16, splits, p.logits, s), "router logits");
+    MOE_HIP_TRY(moe::launch_route(p.logits, splits, router_bias, T, E, k, nullptr, idx, w,
+                                  fused_hist ? p.tile_cnt : nullptr, P, max_ranks, s),
+                "route");
+  }
+  if (!fused_hist) MOE_HIP_TRY(moe::launch_tile_hist(idx, T, k, E, p.tile_cnt, s), "tile histogram");
   MOE_HIP_TRY(moe::launch_scan(p.tile_cnt, nt, E, C, P, d * eb, k, T, p.tile_off, p.routed, p.kept, p.send,
                                p.totals, bm, p.mtile, nullptr, s),
               "scan");
   MOE_HIP_TRY(moe::launch_exclusive_scan(p.routed, E, b.route_off, s), "routed offsets");
-  MOE_HIP_TRY(moe::launch_slots(p.idx, p.tile_off, T, k, E, C, p.slot, nullptr, p.totals, s, b.route_off, b.lcopy,
+  MOE_HIP_TRY(moe::launch_slots(idx, p.tile_off, T, k, E, C, p.slot, nullptr, p.totals, s, b.route_off, b.lcopy,
                                 b.ltok),
               "slots");
-  MOE_HIP_TRY(moe::launch_scatter_rows(x, p.idx, p.slot, T, k, C, d * eb, p.buckets, s), "scatter");
+  if (!saved) MOE_HIP_TRY(moe::launch_scatter_rows(x, idx, p.slot, T, k, C, d * eb, X, s), "scatter");
   // g = X Wg^T and u = X Wu^T (the plain row-tile GEMM: N = d_ff, K = d). GEMMs
   // that contract over d take the row-tile height of GEMM 1 (bm_d, map mtile_d_rows).
   const moe::SplitK* sk = &p.split;
@@ -592,16 +621,16 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
     mtile_d_rows = p.mtile_gu;
   }
   const int bmo_d = bf16 ? bm_d : 0;
-  MOE_HIP_TRY(moe::launch_gemm_down(p.buckets, p.kept, mtile_d_rows, W_gate, E, C, F, d, bf16, b.g, s, nullptr, sk,
-                                    bmo_d),
-              "gemm g");
-  MOE_HIP_TRY(moe::launch_gemm_down(p.buckets, p.kept, mtile_d_rows, W_up, E, C, F, d, bf16, b.u, s, nullptr, sk,
-                                    bmo_d),
-              "gemm u");
-  MOE_HIP_TRY(moe::launch_swiglu_fwd(b.g, b.u, p.h, p.kept, E, C, F, bf16, s), "swiglu");
+  if (!saved) {
+    MOE_HIP_TRY(moe::launch_gemm_down(X, p.kept, mtile_d_rows, W_gate, E, C, F, d, bf16, g, s, nullptr, sk, bmo_d),
+                "gemm g");
+    MOE_HIP_TRY(moe::launch_gemm_down(X, p.kept, mtile_d_rows, W_up, E, C, F, d, bf16, u, s, nullptr, sk, bmo_d),
+                "gemm u");
+    MOE_HIP_TRY(moe::launch_swiglu_fwd(g, u, h, p.kept, E, C, F, bf16, s), "swiglu");
+  }
 
   // 2. combine backward: dy = w dout on kept rows
-  MOE_HIP_TRY(moe::launch_combine_bwd(dout, nullptr, p.idx, p.w, p.slot, T, d, k, C, bf16, b.dy, nullptr, s),
+  MOE_HIP_TRY(moe::launch_combine_bwd(dout, nullptr, idx, w, p.slot, T, d, k, C, bf16, b.dy, nullptr, s),
               "combine backward");
   // 3. dh = dy Wd; dg, du. 4. dX = [dg | du] [Wg ; Wu]. Either straight from the
   //    weights (K-major B: Wd is [d][d_ff] = [K][N], Wg and Wu are [d_ff][d]),
@@ -610,7 +639,7 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
     MOE_HIP_TRY(moe::launch_gemm_kmajor_b(b.dy, p.kept, mtile_d_rows, W_down, nullptr, d, E, C, d, F, b.dh, s, sk,
                                           bm_d),
                 "gemm dh");
-    MOE_HIP_TRY(moe::launch_swiglu_bwd(b.dh, b.g, b.u, b.dgu, p.kept, E, C, F, bf16, s), "swiglu backward");
+    MOE_HIP_TRY(moe::launch_swiglu_bwd(b.dh, g, u, b.dgu, p.kept, E, C, F, bf16, s), "swiglu backward");
     MOE_HIP_TRY(moe::launch_gemm_kmajor_b(b.dgu, p.kept, mtile_d_rows, W_gate, W_up, F, E, C, 2 * F, d, b.dX, s, sk,
                                           bm_d),
                 "gemm dX");
@@ -620,7 +649,7 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
     MOE_HIP_TRY(moe::launch_gemm_down(b.dy, p.kept, mtile_d_rows, b.WdT, E, C, F, d, bf16, b.dh, s, nullptr, sk,
                                       bmo_d),
                 "gemm dh");
-    MOE_HIP_TRY(moe::launch_swiglu_bwd(b.dh, b.g, b.u, b.dgu, p.kept, E, C, F, bf16, s), "swiglu backward");
+    MOE_HIP_TRY(moe::launch_swiglu_bwd(b.dh, g, u, b.dgu, p.kept, E, C, F, bf16, s), "swiglu backward");
     MOE_HIP_TRY(moe::launch_transpose(W_gate, b.WguT, E, F, d, d, 2 * F, 0, F, nullptr, F * d, d * 2 * F, bf16, s),
                 "transpose W_gate");
     MOE_HIP_TRY(moe::launch_transpose(W_up, b.WguT, E, F, d, d, 2 * F, F, F, nullptr, F * d, d * 2 * F, bf16, s),
@@ -629,21 +658,21 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
                 "gemm dX");
   }
   //    the gate gradients: q_j = <dh_j, h_j> = w_j <dout, y_j>, dl_j = q_j - w_j sum_i q_i
-  MOE_HIP_TRY(moe::launch_gate_grad(b.dh, p.h, p.idx, p.w, p.slot, T, F, k, C, bf16, b.dl, s), "gate gradients");
+  MOE_HIP_TRY(moe::launch_gate_grad(b.dh, h, idx, w, p.slot, T, F, k, C, bf16, b.dl, s), "gate gradients");
   // 5. router gradients, then dx = dout + the expert paths + the router path
-  MOE_HIP_TRY(moe::launch_router_wgrad(x, p.idx, b.dl, T, k, E, d, bf16, b.rpart, dW_router, d_bias, s, p.routed,
+  MOE_HIP_TRY(moe::launch_router_wgrad(x, idx, b.dl, T, k, E, d, bf16, b.rpart, dW_router, d_bias, s, p.routed,
                                        b.route_off, b.lcopy, b.ltok),
               "router wgrad");
-  MOE_HIP_TRY(moe::launch_gather_dx(dout, b.dX, W_router, p.idx, b.dl, p.slot, T, d, k, C, bf16, dx, s),
+  MOE_HIP_TRY(moe::launch_gather_dx(dout, b.dX, W_router, idx, b.dl, p.slot, T, d, k, C, bf16, dx, s),
               "gather dx");
   // 6. weight gradients over each expert's kept rows: dWd = dy^T h, dWg = dg^T X,
   //    dWu = du^T X. bf16: both operands read K-major straight from the
   //    buckets, each expert contracting over its own kept rows.
   if (bf16) {
-    MOE_HIP_TRY(moe::launch_gemm_tn(b.dy, d, C * d, 0, p.h, C * F, p.kept, E, d, F, dW_down, s), "gemm dW_down");
-    MOE_HIP_TRY(moe::launch_gemm_tn(b.dgu, 2 * F, C * 2 * F, 0, p.buckets, C * d, p.kept, E, F, d, dW_gate, s),
+    MOE_HIP_TRY(moe::launch_gemm_tn(b.dy, d, C * d, 0, h, C * F, p.kept, E, d, F, dW_down, s), "gemm dW_down");
+    MOE_HIP_TRY(moe::launch_gemm_tn(b.dgu, 2 * F, C * 2 * F, 0, X, C * d, p.kept, E, F, d, dW_gate, s),
                 "gemm dW_gate");
-    MOE_HIP_TRY(moe::launch_gemm_tn(b.dgu, 2 * F, C * 2 * F, F, p.buckets, C * d, p.kept, E, F, d, dW_up, s),
+    MOE_HIP_TRY(moe::launch_gemm_tn(b.dgu, 2 * F, C * 2 * F, F, X, C * d, p.kept, E, F, d, dW_up, s),
                 "gemm dW_up");
     return MOE_OK;
   }
@@ -651,7 +680,7 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   //    for every expert, K = Kp)
   MOE_HIP_TRY(moe::launch_transpose(b.dy, b.dyT, E, C, d, d, b.Kp, 0, b.Kp, p.kept, C * d, d * b.Kp, bf16, s),
               "transpose dy");
-  MOE_HIP_TRY(moe::launch_transpose(p.h, b.hT, E, C, F, F, b.Kp, 0, b.Kp, p.kept, C * F, F * b.Kp, bf16, s),
+  MOE_HIP_TRY(moe::launch_transpose(h, b.hT, E, C, F, F, b.Kp, 0, b.Kp, p.kept, C * F, F * b.Kp, bf16, s),
               "transpose h");
   MOE_HIP_TRY(moe::launch_transpose(b.dgu, b.dgT, E, C, F, 2 * F, b.Kp, 0, b.Kp, p.kept, C * 2 * F, F * b.Kp, bf16,
                                     s),
@@ -659,7 +688,7 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   MOE_HIP_TRY(moe::launch_transpose(static_cast<char*>(b.dgu) + F * eb, b.duT, E, C, F, 2 * F, b.Kp, 0, b.Kp,
                                     p.kept, C * 2 * F, F * b.Kp, bf16, s),
               "transpose du");
-  MOE_HIP_TRY(moe::launch_transpose(p.buckets, b.XT, E, C, d, d, b.Kp, 0, b.Kp, p.kept, C * d, d * b.Kp, bf16, s),
+  MOE_HIP_TRY(moe::launch_transpose(X, b.XT, E, C, d, d, b.Kp, 0, b.Kp, p.kept, C * d, d * b.Kp, bf16, s),
               "transpose X");
   MOE_HIP_TRY(moe::launch_fill_i32(b.kfull_d, E, static_cast<int32_t>(d), s), "fill");
   MOE_HIP_TRY(moe::launch_fill_i32(b.kfull_f, E, static_cast<int32_t>(F), s), "fill");
@@ -672,6 +701,30 @@ int moe_layer_backward(const void* x, const void* W_router, const float* router_
   MOE_HIP_TRY(moe::launch_gemm_down(b.duT, b.kfull_f, b.mtile_f, b.XT, E, F, d, b.Kp, bf16, dW_up, s),
               "gemm dW_up");
   return MOE_OK;
+}
+
+}  // namespace
+
+int moe_layer_backward(const void* x, const void* W_router, const float* router_bias, const void* W_gate,
+                       const void* W_up, const void* W_down, const void* dout, int64_t T, int64_t d, int64_t d_ff,
+                       int32_t E, int32_t k, float cf, int32_t P, int32_t max_ranks, moe_dtype_t dtype, void* dx,
+                       void* dW_router, float* d_bias, void* dW_gate, void* dW_up, void* dW_down,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return layer_backward(x, W_router, router_bias, W_gate, W_up, W_down, dout, T, d, d_ff, E, k, cf, P, max_ranks,
+                        dtype, nullptr, dx, dW_router, d_bias, dW_gate, dW_up, dW_down, workspace, workspace_bytes,
+                        stream);
+}
+
+int moe_layer_backward_saved(const void* x, const void* W_router, const float* router_bias, const void* W_gate,
+                             const void* W_up, const void* W_down, const void* dout, int64_t T, int64_t d,
+                             int64_t d_ff, int32_t E, int32_t k, float cf, int32_t P, int32_t max_ranks,
+                             moe_dtype_t dtype, const moe_stats_t* saved, void* dx, void* dW_router, float* d_bias,
+                             void* dW_gate, void* dW_up, void* dW_down, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (!saved) return fail(MOE_ERR_INVALID_ARG, "saved is NULL");
+  return layer_backward(x, W_router, router_bias, W_gate, W_up, W_down, dout, T, d, d_ff, E, k, cf, P, max_ranks,
+                        dtype, saved, dx, dW_router, d_bias, dW_gate, dW_up, dW_down, workspace, workspace_bytes,
+                        stream);
 }
 
 int moe_replica_plan(const int32_t* routed_count, int32_t E, int32_t extra, int32_t* replicas) {

@@ -110,6 +110,21 @@ def test_layer_rejects_bad_arguments_before_any_gpu_call(kw, status):
     assert moe.moe_last_error()
 
 
+def _backward_saved(saved):
+    moe.moe_layer_backward_saved(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 64, 128, 256, 8, 2, 1.25, 1, 0, "bf16",
+                                 saved, FAKE * 2, FAKE * 3, None, FAKE * 4, FAKE * 5, FAKE * 6, FAKE * 7, 1 << 40)
+
+
+def test_saved_backward_needs_the_kept_state():
+    full = {name: FAKE for name in ("topk_idx", "topk_w", "buckets", "g", "u", "h")}
+    for missing in [None] + sorted(full):
+        saved = None if missing is None else {k: v for k, v in full.items() if k != missing}
+        with pytest.raises(moe.MoeError) as ei:
+            _backward_saved(saved)
+        assert ei.value.status == moe.MOE_ERR_INVALID_ARG, missing
+        assert moe.moe_last_error()
+
+
 def test_zero_tokens_returns_ok_without_launching():
     _layer(T=0, workspace=None, workspace_bytes=0)
     moe.moe_route(FAKE, 0, 8, 2, 1, 0, FAKE, FAKE)

@@ -92,6 +92,61 @@ def test_backward_small_shapes_every_element(case):
         assert v <= tol, (key, v)
 
 
+# ------------------------------------------------ backward from kept state ---
+
+# 128-, 256- and 320-row tiles, drops, a rank limit with a bias, fp32, decode-sized buckets
+SAVED_CASES = [0, 1, 2, 3, 4, 5, 10, 11]
+
+
+@pytest.mark.parametrize("case", SAVED_CASES)
+def test_backward_from_kept_forward_state(case):
+    """A forward that keeps g, u and h: its output still matches the oracle, its
+    g and u match the products of the bucket rows, and the backward that takes
+    that state gives exactly the gradients of the one that recomputes it."""
+    cfg = dict(BACK_CASES[case])
+    cfg.setdefault("dtype", "bf16")
+    wl = moe_inputs.custom(name=f"saved{case}", seed=2000 + case, **cfg)
+    say(f"backward from kept state {case}: {cfg}")
+    dt = wl.dtype
+    hw = wl.all_expert_weights()
+    x, wr = to_dev(wl.x, dt), to_dev(wl.wr, dt)
+    dw = tuple(to_dev(a, dt) for a in hw)
+    dout = to_dev(wl.grad_out(1), dt)
+    b = None if wl.bias_vec is None else torch.from_numpy(wl.bias_vec).cuda()
+    f = moe.forward(x, wr, *dw, wl.k, wl.cf, P=wl.P, router_bias=b, max_ranks=wl.max_ranks, keep_activations=True)
+    torch.cuda.synchronize()
+    ref = oracle.layer_forward(wl.x, wl.wr, lambda e: (hw[0][e], hw[1][e], hw[2][e]), wl.T, wl.d, wl.d_ff, wl.E,
+                               wl.k, wl.cf, dt, P=wl.P, bias=wl.bias_vec, max_ranks=wl.max_ranks)
+    assert np.array_equal(f["topk_idx"].cpu().numpy(), ref["idx"])
+    assert np.array_equal(f["slot"].cpu().numpy(), ref["slot"])
+    tok = ref["tokens"]
+    err = row_rel_err(bits_to_f64(to_host(f["out"], dt)[tok], dt), ref["out64"])
+    tol = 2e-2 if dt == "bf16" else 1e-4
+    assert err.max() <= tol, err.max()
+    kept = f["kept_count"].cpu().numpy()
+    X = bits_to_f64(to_host(f["buckets"], dt), dt)
+    g, u = (bits_to_f64(to_host(f[n], dt), dt) for n in ("g", "u"))
+    wg, wu = (bits_to_f64(a, dt) for a in hw[:2])
+    for e in range(wl.E):
+        n = int(kept[e])
+        if n == 0:
+            continue
+        for got, w in ((g, wg), (u, wu)):
+            assert row_rel_err(got[e, :n], X[e, :n] @ w[e].T).max() <= tol, e
+    # rows past kept are not part of the kept state: NaN there must not reach any gradient
+    for e in range(wl.E):
+        for name in ("g", "u", "h"):
+            f[name][e, int(kept[e]):] = float("nan")
+    r0 = moe.backward(x, wr, *dw, dout, wl.k, wl.cf, P=wl.P, router_bias=b, max_ranks=wl.max_ranks,
+                      want_d_bias=True)
+    r1 = moe.backward(x, wr, *dw, dout, wl.k, wl.cf, P=wl.P, router_bias=b, max_ranks=wl.max_ranks,
+                      want_d_bias=True, saved=f)
+    torch.cuda.synchronize()
+    for key in ("dx", "dW_router", "d_bias", "dW_gate", "dW_up", "dW_down"):
+        assert torch.equal(r0[key].view(torch.uint8) if r0[key].dtype == torch.bfloat16 else r0[key],
+                           r1[key].view(torch.uint8) if r1[key].dtype == torch.bfloat16 else r1[key]), key
+
+
 # ---------------------------------------------------------- named workloads ---
 
 FULL = ["mixtral_prefill", "zipf_skew_drops", "deepseek_v3_decode"]
