@@ -603,8 +603,13 @@ int layer_backward(const void* x, const void* W_router, const float* router_bias
                 "route");
   }
   if (!fused_hist) MOE_HIP_TRY(moe::launch_tile_hist(idx, T, k, E, p.tile_cnt, s), "tile histogram");
+  // the scan also clears the split-K arrival counters once; each split tile's
+  // last block leaves its counter at zero again for the next GEMM
+  moe::SplitK split = p.split;
+  split.zeroed = split.tick != nullptr;
   MOE_HIP_TRY(moe::launch_scan(p.tile_cnt, nt, E, C, P, d * eb, k, T, p.tile_off, p.routed, p.kept, p.send,
-                               p.totals, bm, p.mtile, nullptr, s),
+                               p.totals, bm, p.mtile, nullptr, s, nullptr, 0, nullptr, split.tick,
+                               split.tick ? moe::kSplitUnits : 0),
               "scan");
   MOE_HIP_TRY(moe::launch_exclusive_scan(p.routed, E, b.route_off, s), "routed offsets");
   MOE_HIP_TRY(moe::launch_slots(idx, p.tile_off, T, k, E, C, p.slot, nullptr, p.totals, s, b.route_off, b.lcopy,
@@ -613,7 +618,7 @@ int layer_backward(const void* x, const void* W_router, const float* router_bias
   if (!saved) MOE_HIP_TRY(moe::launch_scatter_rows(x, idx, p.slot, T, k, C, d * eb, X, s), "scatter");
   // g = X Wg^T and u = X Wu^T (the plain row-tile GEMM: N = d_ff, K = d). GEMMs
   // that contract over d take the row-tile height of GEMM 1 (bm_d, map mtile_d_rows).
-  const moe::SplitK* sk = &p.split;
+  const moe::SplitK* sk = &split;
   const int bm_d = moe::grouped_gemm_bm_contract_d(bf16, C, d);
   int32_t* mtile_d_rows = p.mtile;
   if (bm_d != bm) {
