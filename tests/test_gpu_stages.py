@@ -168,7 +168,28 @@ PERMUTE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("T,E,k,cf,P,d,dtype,skew", PERMUTE_CASES)
+def _random_permute_cases(n, seed=4242):
+    """Seeded shapes across the permutation's three launch plans (a block-wide
+    histogram sum, a per-token one, scan and slots apart), sized so the host
+    reference stays small."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        E = int(rng.choice([1, 2, 3, 5, 8, 12, 16, 24, 32, 48, 64, 100, 128, 256, 512, 1024, 1536]))
+        k = int(rng.integers(1, min(E, 32) + 1))
+        T = int(rng.integers(1, 12001))
+        cf = float(rng.choice([0.3, 0.6, 1.0, 1.25, 2.0]))
+        dtype = str(rng.choice(["bf16", "f32"]))
+        d = int(rng.choice([8, 24, 64, 200, 1000, 2048, 3000]))
+        P = int(rng.choice([p for p in (1, 2, 4, 8) if E % p == 0]))
+        C = -(-int(cf * k * T) // E) if E else 1
+        if T * k * d > 2e7 or E * max(C, 1) * d > 4e7:
+            continue
+        out.append((T, E, k, cf, P, d, dtype, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("T,E,k,cf,P,d,dtype,skew", PERMUTE_CASES + _random_permute_cases(24))
 def test_permute_is_exact(T, E, k, cf, P, d, dtype, skew):
     say(f"permute T={T} E={E} k={k} cf={cf} P={P} d={d} {dtype} skew={skew}")
     rng = np.random.default_rng(T + E + k)
