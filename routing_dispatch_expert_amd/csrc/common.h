@@ -232,11 +232,14 @@ size_t split_k_bytes();
 SplitK split_k_carve(void* base);  // base: 256-byte aligned, split_k_bytes() long
 // GEMM 1: h = silu(X Wg^T) * (X Wu^T) on rows < kept. With wmap [E], bucket
 // e uses the weights of expert wmap[e] (replicated experts). With sk, a last
-// round that would leave most of the chip idle is split over K.
+// round that would leave most of the chip idle is split over K. With g and u
+// (both or neither; only when gate_up_keeps_gu(bf16, C, d)) it also writes the
+// rounded g = X Wg^T and u = X Wu^T, [E, C, d_ff], rows < kept.
+bool gate_up_keeps_gu(bool bf16, int64_t C, int64_t d);
 hipError_t launch_gemm_gate_up(const void* buckets, const int32_t* kept, const int32_t* mtile_off,
                                const void* wg, const void* wu, int E, int64_t C, int64_t d,
                                int64_t d_ff, bool bf16, void* h, hipStream_t s, const int32_t* wmap = nullptr,
-                               const SplitK* sk = nullptr);
+                               const SplitK* sk = nullptr, void* g = nullptr, void* u = nullptr);
 // GEMM 2: y = h Wd^T on rows < kept (wmap and sk as above). bm, if not 0,
 // overrides the bf16 row-tile height (128 or 256; mtile_off built for it).
 hipError_t launch_gemm_down(const void* h, const int32_t* kept, const int32_t* mtile_off,

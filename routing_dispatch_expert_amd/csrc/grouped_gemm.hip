@@ -509,7 +509,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     int E, int64_t C, int64_t K, int64_t N, int nt_count, const int32_t* __restrict__ wmap,
     float* __restrict__ part, int32_t* __restrict__ tick, int G, int64_t K0 = 0, int slices = 1,
     const int32_t* __restrict__ kk = nullptr, int64_t lda = 0, int64_t a_es = 0, int64_t aoff = 0,
-    int64_t b_es = 0) {
+    int64_t b_es = 0, bf16_t* __restrict__ gout = nullptr, bf16_t* __restrict__ uout = nullptr) {
   static_assert(!(SWIGLU && BT), "the K-major B operand serves the plain GEMM only");
   static_assert(!(F32OUT && (SWIGLU || BT)), "fp32 output serves the plain GEMM only");
   static_assert(!AT || (BT && !F32OUT), "a K-major A comes with a K-major B");
@@ -858,6 +858,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   store_wave_tile<TM, TN, SWIGLU, EB, true, BT>(
       acc, eb, out + static_cast<int64_t>(e) * C * N, m0 + wm * (BM / 2), rows,
       n0 + wn * (SWIGLU ? TN * 16 : TN * 32), N, lane);
+  if constexpr (SWIGLU) {
+    // g and u themselves, rounded, when kept for the backward: the gate
+    // accumulators (column blocks 0 .. TN/2) and the up ones, at h's columns
+    if (gout) {
+      f32x16 half[TM][TN / 2];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN / 2; ++j) half[i][j] = acc[i][j];
+      store_wave_tile<TM, TN / 2, false, EB, true, false>(half, eb, gout + static_cast<int64_t>(e) * C * N,
+                                                          m0 + wm * (BM / 2), rows, n0 + wn * TN * 16, N, lane);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN / 2; ++j) half[i][j] = acc[i][j + TN / 2];
+      store_wave_tile<TM, TN / 2, false, EB, true, false>(half, eb, uout + static_cast<int64_t>(e) * C * N,
+                                                          m0 + wm * (BM / 2), rows, n0 + wn * TN * 16, N, lane);
+    }
+  }
   if constexpr (!PERSIST) return;
   __syncthreads();  // every wave's staging reads are done before the next tile's DMA
   }
@@ -1274,7 +1293,12 @@ constexpr int kTnWaves = 8;
 template <int BM, int BN, bool SWIGLU>
 hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out, const int32_t* kept,
                        const int32_t* mtile_off, int E, int64_t C, int64_t K, int64_t N, const int32_t* wmap,
-                       hipStream_t s, const SplitK* sk = nullptr) {
+                       hipStream_t s, const SplitK* sk = nullptr, void* gout = nullptr, void* uout = nullptr) {
+  // only the LDS-DMA kernel also writes the SwiGLU GEMM's g and u
+  if ((gout || uout) && !(SWIGLU && (BM == 320 || BM == 256) && BN == 256 && K % 128 == 0))
+    return hipErrorInvalidValue;
+  auto* pg = static_cast<bf16_t*>(gout);
+  auto* pu = static_cast<bf16_t*>(uout);
   const int64_t mt_max = E * ceil_div(C, BM);  // upper bound of live row tiles
   const int64_t nt = ceil_div(N, SWIGLU ? BN / 2 : BN);
   int64_t blocks = ceil_div(mt_max * nt, 8) * 8;  // whole rounds over the 8 XCDs
@@ -1297,11 +1321,11 @@ hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out,
       gemm_bf16_dma_kernel<SWIGLU, false, false, false, 8, 5, false>
           <<<dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s>>>(
           pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap, G > 0 ? sk->part : nullptr,
-          G > 0 ? sk->tick : nullptr, G);
+          G > 0 ? sk->tick : nullptr, G, 0, 1, nullptr, 0, 0, 0, 0, pg, pu);
     else
       gemm_bf16_dma_kernel<SWIGLU, false, false, false, 8, 5><<<dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s>>>(
           pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap, G > 0 ? sk->part : nullptr,
-          G > 0 ? sk->tick : nullptr, G);
+          G > 0 ? sk->tick : nullptr, G, 0, 1, nullptr, 0, 0, 0, 0, pg, pu);
   } else if constexpr (BM == 128 && BN == 256) {
     if (K % 64) return hipErrorInvalidValue;  // callers pick this tile only for K % 64 == 0
     gemm_bf16_dma_m128_kernel<SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
@@ -1321,7 +1345,7 @@ hipError_t launch_bf16(const void* a, const void* b0, const void* b1, void* out,
     gemm_bf16_dma_kernel<SWIGLU, false, false, false, kDmaWaves>
         <<<dim3(static_cast<unsigned>(blocks)), dim3(kDmaWaves * 64), 0, s>>>(
         pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap, G > 0 ? sk->part : nullptr,
-        G > 0 ? sk->tick : nullptr, G);
+        G > 0 ? sk->tick : nullptr, G, 0, 1, nullptr, 0, 0, 0, 0, pg, pu);
   } else {
     gemm_bf16_kernel<BM, BN, SWIGLU><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(
         pa, pb0, pb1, po, kept, mtile_off, E, C, K, N, static_cast<int>(nt), wmap);
@@ -1392,19 +1416,25 @@ hipError_t launch_gemm_kmajor_b(const void* a, const int32_t* kept, const int32_
   return hipGetLastError();
 }
 
+bool gate_up_keeps_gu(bool bf16, int64_t C, int64_t d) {
+  const int bm = grouped_gemm_bm_gate_up(bf16, C, d);
+  return bf16 && (bm == 320 || bm == 256) && d % 128 == 0;
+}
+
 hipError_t launch_gemm_gate_up(const void* buckets, const int32_t* kept, const int32_t* mtile_off,
                                const void* wg, const void* wu, int E, int64_t C, int64_t d,
                                int64_t d_ff, bool bf16, void* h, hipStream_t s, const int32_t* wmap,
-                               const SplitK* sk) {
+                               const SplitK* sk, void* g, void* u) {
+  if ((g || u) && !(g && u && gate_up_keeps_gu(bf16, C, d))) return hipErrorInvalidValue;
   if (E * C == 0) return hipSuccess;
   if (bf16) {
     const int bm = grouped_gemm_bm_gate_up(true, C, d);
     if (bm == kSkinnyRows && d % 32 == 0)
       return launch_skinny<true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s);
     if (bm == 320)
-      return launch_bf16<320, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s, sk);
+      return launch_bf16<320, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s, sk, g, u);
     if (bm == 256)
-      return launch_bf16<256, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s, sk);
+      return launch_bf16<256, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s, sk, g, u);
     if (d % 64 == 0)
       return launch_bf16<128, 256, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s);
     return launch_bf16<128, 128, true>(buckets, wg, wu, h, kept, mtile_off, E, C, d, d_ff, wmap, s);

@@ -510,10 +510,16 @@ int moe_layer_forward(const void* x, const void* W_router, const float* router_b
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, false, s), "event");
   int32_t* map_gu = bm_gu != bm ? p.mtile_gu : p.mtile;
   void* h = p.h;
-  if (S.g && S.u && S.h) {
-    // g and u kept for the backward: the two plain GEMMs and the SwiGLU
-    // product of their rounded values, exactly as the backward recomputes them
-    h = S.h;
+  const bool keep = S.g && S.u && S.h;
+  if (keep) h = S.h;
+  if (keep && moe::gate_up_keeps_gu(bf16, C, d)) {
+    // g and u kept for the backward: the same GEMM also writes them rounded
+    MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, map_gu, W_gate, W_up, E, C, d, d_ff, bf16, h, s, nullptr,
+                                         &sk, S.g, S.u),
+                "grouped gemm (gate, up)");
+  } else if (keep) {
+    // elsewhere the two plain GEMMs and the SwiGLU product of their rounded
+    // values, exactly as the backward recomputes them
     const int bmo = bf16 ? bm_gu : 0;
     MOE_HIP_TRY(moe::launch_gemm_down(buckets, kept, map_gu, W_gate, E, C, d_ff, d, bf16, S.g, s, nullptr, &sk, bmo),
                 "grouped gemm (gate)");
@@ -626,7 +632,11 @@ int layer_backward(const void* x, const void* W_router, const float* router_bias
     mtile_d_rows = p.mtile_gu;
   }
   const int bmo_d = bf16 ? bm_d : 0;
-  if (!saved) {
+  if (!saved && moe::gate_up_keeps_gu(bf16, C, d)) {  // GEMM 1 as the forward runs it, g and u kept
+    MOE_HIP_TRY(moe::launch_gemm_gate_up(X, p.kept, mtile_d_rows, W_gate, W_up, E, C, d, F, bf16, h, s, nullptr, sk,
+                                         g, u),
+                "gemm g, u");
+  } else if (!saved) {
     MOE_HIP_TRY(moe::launch_gemm_down(X, p.kept, mtile_d_rows, W_gate, E, C, F, d, bf16, g, s, nullptr, sk, bmo_d),
                 "gemm g");
     MOE_HIP_TRY(moe::launch_gemm_down(X, p.kept, mtile_d_rows, W_up, E, C, F, d, bf16, u, s, nullptr, sk, bmo_d),
