@@ -93,10 +93,11 @@ typedef struct {
   /* The expert activations, kept for moe_layer_backward_saved (plain layer
    * only; the replicated layer ignores them): g = X_e W_gate[e]^T, u = X_e
    * W_up[e]^T and h = silu(g) * u, each [E, C, d_ff] dtype, rows < kept_count
-   * written (the others left as they were). Given all three, the layer
-   * computes g and u with two plain grouped GEMMs and h from their rounded
-   * values, as the backward does, instead of the one GEMM that yields h; else
-   * none of them is written. */
+   * written (the others left as they were), all three or none. Where GEMM 1
+   * runs on 256- or 320-row tiles with d % 128 == 0 it writes the rounded g
+   * and u beside h, and the layer's output is unchanged; elsewhere g and u
+   * come from two plain grouped GEMMs and h from their rounded values, as
+   * the backward recomputes them. */
   void* g;
   void* u;
   void* h;
