@@ -171,21 +171,22 @@ __device__ inline uint32_t order_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Selects, not branches: written with an `if`, the swap compiled to a
+// masked branch per slot (the DeepSeek-V3 route kernel spent most of its
+// time there).
 template <int KMAX>
 __device__ inline void insert_sorted(float (&lv)[KMAX], int (&li)[KMAX], float v, int ei) {
   bool ins = false;
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
-    const bool take = ins || better(v, ei, lv[j], li[j]);
-    if (take) {
-      const float tv = lv[j];
-      const int te = li[j];
-      lv[j] = v;
-      li[j] = ei;
-      v = tv;
-      ei = te;
-    }
-    ins = ins || take;
+    const bool take = ins || better(v, ei, lv[j], li[j]);  // from here on every entry moves down one
+    const float tv = lv[j];
+    const int te = li[j];
+    lv[j] = take ? v : tv;
+    li[j] = take ? ei : te;
+    v = take ? tv : v;
+    ei = take ? te : ei;
+    ins = take;
   }
 }
 
@@ -321,15 +322,14 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* part, int S, c
       sel_v = bv;
       sel_e = be;
     }
-    if (li[0] == be) {  // the owner pops its head
+    const bool pop = li[0] == be;  // the owner pops its head
 #pragma unroll
-      for (int j = 0; j + 1 < KMAX; ++j) {
-        lv[j] = lv[j + 1];
-        li[j] = li[j + 1];
-      }
-      lv[KMAX - 1] = -INFINITY;
-      li[KMAX - 1] = INT_MAX;
+    for (int j = 0; j + 1 < KMAX; ++j) {
+      lv[j] = pop ? lv[j + 1] : lv[j];
+      li[j] = pop ? li[j + 1] : li[j];
     }
+    lv[KMAX - 1] = pop ? -INFINITY : lv[KMAX - 1];
+    li[KMAX - 1] = pop ? INT_MAX : li[KMAX - 1];
   }
 
   const double z = g < k ? exp(static_cast<double>(sel_v) - static_cast<double>(v0)) : 0.0;
