@@ -171,26 +171,38 @@ __device__ inline uint32_t order_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Selects, not branches: written with an `if`, the swap compiled to a
-// masked branch per slot (the DeepSeek-V3 route kernel spent most of its
-// time there).
-template <int KMAX>
+// SEL: selects instead of a masked branch per slot. With many scores a lane
+// (DeepSeek-V3 prefill: 16 of 256) the branches took most of the route
+// kernel's time (39 -> 30 us with selects); with few (4 a lane on the skewed
+// and decode shapes) the branches, mostly skipped, are cheaper (19.2 -> 20.4
+// us and 18.2 -> 20.6 us with selects). The route launch picks SEL from the
+// scores per lane.
+template <int KMAX, bool SEL>
 __device__ inline void insert_sorted(float (&lv)[KMAX], int (&li)[KMAX], float v, int ei) {
   bool ins = false;
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     const bool take = ins || better(v, ei, lv[j], li[j]);  // from here on every entry moves down one
-    const float tv = lv[j];
-    const int te = li[j];
-    lv[j] = take ? v : tv;
-    li[j] = take ? ei : te;
-    v = take ? tv : v;
-    ei = take ? te : ei;
+    if constexpr (SEL) {
+      const float tv = lv[j];
+      const int te = li[j];
+      lv[j] = take ? v : tv;
+      li[j] = take ? ei : te;
+      v = take ? tv : v;
+      ei = take ? te : ei;
+    } else if (take) {
+      const float tv = lv[j];
+      const int te = li[j];
+      lv[j] = v;
+      li[j] = ei;
+      v = tv;
+      ei = te;
+    }
     ins = take;
   }
 }
 
-template <int L, int KMAX, bool HIST, bool LIMIT>
+template <int L, int KMAX, bool HIST, bool LIMIT, bool SEL>
 __global__ __launch_bounds__(1024) void route_kernel(const float* part, int S, const float* __restrict__ bias,
                                                      int64_t T, int E, int k, float* logits_out,
                                                      int32_t* __restrict__ idx, float* __restrict__ w,
@@ -259,7 +271,7 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* part, int S, c
           if (lsum) lsum[t * E + e] = v;
           atomicMax(&rbest[tok * P + e / per], order_key(v));
         } else {
-          insert_sorted(lv, li, v, e);
+          insert_sorted<KMAX, SEL>(lv, li, v, e);
         }
       }
     }
@@ -297,7 +309,7 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* part, int S, c
         for (int q = 0; q < G; ++q) {
           const int e = eb + q * L;
           if (e >= E) break;
-          if ((allowed >> (e / per)) & 1u) insert_sorted(lv, li, vv[q] + 0.0f, e);
+          if ((allowed >> (e / per)) & 1u) insert_sorted<KMAX, SEL>(lv, li, vv[q] + 0.0f, e);
         }
       }
     }
@@ -323,13 +335,23 @@ __global__ __launch_bounds__(1024) void route_kernel(const float* part, int S, c
       sel_e = be;
     }
     const bool pop = li[0] == be;  // the owner pops its head
+    if constexpr (SEL) {
 #pragma unroll
-    for (int j = 0; j + 1 < KMAX; ++j) {
-      lv[j] = pop ? lv[j + 1] : lv[j];
-      li[j] = pop ? li[j + 1] : li[j];
+      for (int j = 0; j + 1 < KMAX; ++j) {
+        lv[j] = pop ? lv[j + 1] : lv[j];
+        li[j] = pop ? li[j + 1] : li[j];
+      }
+      lv[KMAX - 1] = pop ? -INFINITY : lv[KMAX - 1];
+      li[KMAX - 1] = pop ? INT_MAX : li[KMAX - 1];
+    } else if (pop) {
+#pragma unroll
+      for (int j = 0; j + 1 < KMAX; ++j) {
+        lv[j] = lv[j + 1];
+        li[j] = li[j + 1];
+      }
+      lv[KMAX - 1] = -INFINITY;
+      li[KMAX - 1] = INT_MAX;
     }
-    lv[KMAX - 1] = pop ? -INFINITY : lv[KMAX - 1];
-    li[KMAX - 1] = pop ? INT_MAX : li[KMAX - 1];
   }
 
   const double z = g < k ? exp(static_cast<double>(sel_v) - static_cast<double>(v0)) : 0.0;
@@ -376,13 +398,20 @@ struct RouteArgs {
 
 template <int L, int KMAX, bool HIST, bool LIMIT>
 hipError_t route_launch(const RouteArgs& a, hipStream_t s) {
+  const bool sel = a.E >= 8 * L;  // eight or more scores a lane: selects in the top-k insertion
   const int64_t tpb = 1024 / L;
   // HIST: histogram [E], the tile's experts [64 k] and, for the ranking by all waves, its chunk counts [k E]
   const size_t lds = (HIST ? (a.E + tpb * a.k + (tile_ranks_by_waves(a.k, a.E) ? a.k * a.E : 0)) * sizeof(int) : 0) +
                      (LIMIT ? tpb * a.P * sizeof(uint32_t) : 0);
-  route_kernel<L, KMAX, HIST, LIMIT><<<dim3(static_cast<unsigned>(ceil_div(a.T, tpb))), dim3(1024), lds, s>>>(
-      a.part, a.S, a.bias, a.T, a.E, a.k, a.logits_out, a.idx, a.w, a.tile_cnt, a.P, a.M, a.lsum, a.lsrc, a.rank,
-      a.zero);
+  const dim3 grid(static_cast<unsigned>(ceil_div(a.T, tpb)));
+  if (sel)
+    route_kernel<L, KMAX, HIST, LIMIT, true><<<grid, dim3(1024), lds, s>>>(
+        a.part, a.S, a.bias, a.T, a.E, a.k, a.logits_out, a.idx, a.w, a.tile_cnt, a.P, a.M, a.lsum, a.lsrc, a.rank,
+        a.zero);
+  else
+    route_kernel<L, KMAX, HIST, LIMIT, false><<<grid, dim3(1024), lds, s>>>(
+        a.part, a.S, a.bias, a.T, a.E, a.k, a.logits_out, a.idx, a.w, a.tile_cnt, a.P, a.M, a.lsum, a.lsrc, a.rank,
+        a.zero);
   return hipGetLastError();
 }
 
