@@ -178,16 +178,17 @@ hipError_t launch_slots_from_ranks(const int32_t* idx, int32_t* slot, const int3
                                   int E, int64_t C, int32_t* src, int64_t* totals, hipStream_t s);
 // The scan and the slots with the row scatter in one launch (block 0 scans
 // while the others place and copy rows), when slot_scatter_fits(T, k, E):
-// k <= 32, E <= 4096 and at most 256 tile counts ahead of any token's copies
-// (k (nt - 1) <= 256). Outputs as launch_scan (place: default) followed by
-// launch_slots_from_ranks and launch_scatter_rows; slot holds the ranks on
-// entry; totals[1] must be zero on entry (zero it in the histogram launch).
+// k <= 32, E <= 4096 and few enough earlier-tile counts to add up in each
+// block (E (nt - 1) <= 65536, or k (nt - 1) <= 256 per token). Outputs as
+// launch_scan followed by launch_slots_from_ranks and launch_scatter_rows;
+// slot holds the ranks on entry; totals[1] must be zero on entry (zero it in
+// the histogram launch).
 bool slot_scatter_fits(int64_t T, int k, int E);
 hipError_t launch_slot_scatter(const int32_t* tile_cnt, int E, int64_t C, int P, int64_t row_bytes, int k,
                                int64_t T, int32_t* tile_off, int32_t* routed, int32_t* kept, int32_t* send,
                                int64_t* totals, int bm, int32_t* mtile_off, int bm1, int32_t* mtile1,
                                int32_t* clear, int n_clear, const void* x, const int32_t* idx, int32_t* slot,
-                               int32_t* src, void* buckets, hipStream_t s);
+                               int32_t* src, void* buckets, hipStream_t s, const int32_t* place = nullptr);
 // Replicated experts: instance offsets [E+1], expert [R] and rank [R] of each
 // instance; then the instance of each copy from its rank among its expert's copies.
 hipError_t launch_replica_layout(const int32_t* replicas, int E, int R, int P, int32_t* inst_off, int32_t* wmap,

@@ -824,14 +824,26 @@ int moe_layer_forward_replicated(const void* x, const void* W_router, const floa
   MOE_HIP_TRY(moe::launch_instances(idx, p.qrank, replicas, p.inst_off, T * k, R, inst, s), "instances");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTE, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SLOTS, false, s), "event");
-  MOE_HIP_TRY(moe::launch_tile_hist(inst, T, k, R, p.tile_cnt, s), "tile histogram (instances)");
-  MOE_HIP_TRY(moe::launch_scan(p.tile_cnt, nt, R, C, P, d * eb, k, T, p.tile_off, p.routed2, kept, send, totals,
-                               bm, p.mtile, src, s, p.place),
-              "scan (instances)");
-  MOE_HIP_TRY(moe::launch_slots(inst, p.tile_off, T, k, R, C, slot, src, totals, s), "slots");
+  // the instances' slots: as in the plain layer, in one pass with the row
+  // copies where the tile histogram is short enough
+  const bool one_pass = moe::slot_scatter_fits(T, k, R);
+  MOE_HIP_TRY(moe::launch_tile_hist(inst, T, k, R, p.tile_cnt, s, one_pass ? slot : nullptr,
+                                    one_pass ? totals + 1 : nullptr),
+              "tile histogram (instances)");
+  if (!one_pass) {
+    MOE_HIP_TRY(moe::launch_scan(p.tile_cnt, nt, R, C, P, d * eb, k, T, p.tile_off, p.routed2, kept, send, totals,
+                                 bm, p.mtile, src, s, p.place),
+                "scan (instances)");
+    MOE_HIP_TRY(moe::launch_slots(inst, p.tile_off, T, k, R, C, slot, src, totals, s), "slots");
+  }
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SLOTS, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, false, s), "event");
-  MOE_HIP_TRY(moe::launch_scatter_rows(x, inst, slot, T, k, C, d * eb, buckets, s), "scatter");
+  if (one_pass)
+    MOE_HIP_TRY(moe::launch_slot_scatter(p.tile_cnt, R, C, P, d * eb, k, T, p.tile_off, p.routed2, kept, send, totals,
+                                         bm, p.mtile, 0, nullptr, nullptr, 0, x, inst, slot, src, buckets, s, p.place),
+                "slots and scatter (instances)");
+  else
+    MOE_HIP_TRY(moe::launch_scatter_rows(x, inst, slot, T, k, C, d * eb, buckets, s), "scatter");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, false, s), "event");
   const int bm_gu = moe::grouped_gemm_bm_gate_up(bf16, C, d);

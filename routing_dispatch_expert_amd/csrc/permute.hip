@@ -450,11 +450,10 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4* __restri
 // adds up the tile histogram over the earlier tiles itself, so no block waits
 // for the scan: slot = that sum for the copy's expert + the copy's rank within
 // its tile (held in slot on entry), kept below C, exactly as tile_off + rank.
-// With BP (E a power of two <= 1024, E (nt - 1) <= 65536) the whole block sums
-// every expert's column, the first tl E words of the histogram (thread i's
-// counts all belong to expert i % E, at most 64 of them, 16 loads in flight);
-// otherwise each token's threads sum the column of each copy's expert (k (nt
-// - 1) <= 256, one count per thread). The row words (U per lane) are loaded
+// With BP (E (nt - 1) <= 65536) the whole block sums every expert's column,
+// the first tl E words of the histogram (at most 64 counts a thread, 16 loads
+// in flight); otherwise each token's threads sum the column of each copy's
+// expert (k (nt - 1) <= 256, one count per thread). The row words (U per lane) are loaded
 // first, while the counts are on their way; the copies then go out as in
 // scatter_rows_kernel. totals[1] must be zero on entry: each block adds its
 // fully dropped tokens once.
@@ -472,7 +471,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
   constexpr int KM = 32;          // copies per token at most
   constexpr int TB = 1024 / H;    // tokens per block, all of one tile
   constexpr int PI = 256 / H;     // per-copy counts per thread at most
-  __shared__ int psum[BP ? 1024 : TB * KM], sls[TB * KM], es[TB * KM], fd[TB];
+  __shared__ int psum[BP ? 4096 : TB * KM], sls[TB * KM], es[TB * KM], fd[TB];
   const int E = tail.E, k = tail.k;
   const int64_t T = tail.T, C = tail.C;
   const int tid = threadIdx.x;
@@ -503,9 +502,16 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
     }
   }
   if constexpr (BP) {
+    // count c is tile c / E's count of expert c % E; thread i takes counts
+    // i, i + 1024, ...: with E a power of two up to 1024 all of one expert,
+    // summed in registers; otherwise the expert advances by 1024 mod E a count
     const int npre = E * tl;  // the block's first token is live
     constexpr int B = 16;
+    const bool pow2 = (E & (E - 1)) == 0 && E <= 1024;
+    const int step = 1024 % E;
+    int ex = tid % E;
     int acc = 0;
+    lds_barrier();  // psum is zero
     for (int c0 = 0; c0 < npre; c0 += B * 1024) {
       int v[B];
 #pragma unroll
@@ -513,11 +519,19 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
         const int c = c0 + i * 1024 + tid;
         v[i] = c < npre ? tile_cnt[c] : 0;
       }
+      if (pow2) {
 #pragma unroll
-      for (int i = 0; i < B; ++i) acc += v[i];
+        for (int i = 0; i < B; ++i) acc += v[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+          if (v[i]) atomicAdd(&psum[ex], v[i]);  // integer sums: any order
+          ex += step;
+          ex -= ex >= E ? E : 0;
+        }
+      }
     }
-    lds_barrier();  // psum is zero
-    if (acc) atomicAdd(&psum[tid & (E - 1)], acc);  // integer sums: any order
+    if (acc) atomicAdd(&psum[tid & (E - 1)], acc);  // pow2 only: acc stays 0 otherwise
   } else {
     const int npre = live ? k * tl : 0;
     int pj[PI], pe[PI], pv[PI];
@@ -759,9 +773,7 @@ hipError_t launch_scatter_rows(const void* x, const int32_t* idx, const int32_t*
 
 namespace {
 // each block of the one-pass kernel sums every expert's column of the earlier tiles
-bool slot_scatter_block_prefix(int64_t nt, int E) {
-  return E <= 1024 && (E & (E - 1)) == 0 && (nt - 1) * E <= 65536;
-}
+bool slot_scatter_block_prefix(int64_t nt, int E) { return E <= 4096 && (nt - 1) * E <= 65536; }
 }  // namespace
 
 bool slot_scatter_fits(int64_t T, int k, int E) {
@@ -773,10 +785,10 @@ hipError_t launch_slot_scatter(const int32_t* tile_cnt, int E, int64_t C, int P,
                                int64_t T, int32_t* tile_off, int32_t* routed, int32_t* kept, int32_t* send,
                                int64_t* totals, int bm, int32_t* mtile_off, int bm1, int32_t* mtile1,
                                int32_t* clear, int n_clear, const void* x, const int32_t* idx, int32_t* slot,
-                               int32_t* src, void* buckets, hipStream_t s) {
+                               int32_t* src, void* buckets, hipStream_t s, const int32_t* place) {
   if (!slot_scatter_fits(T, k, E) || P < 1 || P > E || n_clear < 0) return hipErrorInvalidValue;
   const int64_t nt = ceil_div(T, kTileTokens);
-  ScanTail tail{C, row_bytes, T, E, P, k, send, totals, bm, bm1, mtile_off, mtile1, nullptr, clear, n_clear};
+  ScanTail tail{C, row_bytes, T, E, P, k, send, totals, bm, bm1, mtile_off, mtile1, place, clear, n_clear};
   tail.leave_t1 = true;
   const size_t shm = (2 * static_cast<size_t>(E) + 1 + P) * sizeof(int);
   const auto* xv = static_cast<const uint4*>(x);

@@ -152,13 +152,13 @@ def test_layer_is_deterministic():
                            b[key].view(torch.uint8) if b[key].dtype == torch.bfloat16 else b[key]), key
 
 
-@pytest.mark.parametrize("T,E,one_pass", [(2000, 16, True), (9000, 16, True), (9000, 48, False)])
-def test_stage_events_change_nothing(T, E, one_pass):
+@pytest.mark.parametrize("T,E,d,one_pass", [(2000, 16, 256, True), (9000, 48, 256, True), (9000, 1024, 64, False)])
+def test_stage_events_change_nothing(T, E, d, one_pass):
     # one kernel places and copies the rows (the slots stage is empty) when
     # each block can add up the earlier tiles' counts: every expert's column
-    # (E a power of two) or, per token, its copies' experts (k (nt - 1) <= 256;
-    # 4 * 140 = 560 here is not)
-    wl = moe_inputs.custom(T=T, d=256, E=E, k=4, d_ff=256, cf=0.8, seed=78, P=4)
+    # (E (nt - 1) <= 65536) or, per token, its copies' experts (k (nt - 1) <=
+    # 256); 140 tiles of 1024 experts, 4 copies a token, is neither
+    wl = moe_inputs.custom(T=T, d=d, E=E, k=4, d_ff=d, cf=0.8, seed=78, P=4)
     dw = tuple(to_dev(a, wl.dtype) for a in wl.all_expert_weights())
     a = run_layer(wl, *dw)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(moe.STAGES))]

@@ -149,22 +149,24 @@ PERMUTE_CASES = [
     (70000, 8, 2, 1.25, 2, 8, "bf16", False),    # 1094 tiles: 69 per scan lane, past the 16 held in registers
     (3000, 4096, 4, 1.0, 8, 8, "bf16", True),    # the most experts: the scan takes them 1024 at a time
     (2000, 1000, 5, 1.5, 4, 8, "bf16", False),   # 1000 experts: a 1024-wide pass with idle lanes
-    (4160, 24, 4, 1.0, 2, 8, "bf16", True),      # last token 4 x 64 tile counts behind: the per-token limit
-    (4161, 24, 4, 1.0, 2, 8, "bf16", True),      # one token past it: scan, slots and scatter apart
-    (16385, 12, 1, 0.6, 1, 8, "bf16", True),     # k = 1, 257 tiles: the per-token limit, many drops
+    (4160, 24, 4, 1.0, 2, 8, "bf16", True),      # E not a power of two: the block sums every column
+    (16385, 12, 1, 0.6, 1, 8, "bf16", True),     # k = 1, 257 tiles, many drops
+    (4160, 4096, 4, 1.0, 8, 8, "bf16", True),    # 65 x 4096 counts: each token sums its copies' 4 x 64
+    (4161, 4096, 4, 1.0, 8, 8, "bf16", True),    # one token past both limits: scan, slots and scatter apart
     (1000, 8, 2, 1.25, 2, 2048, "bf16", True),   # one-pass rows of 256 words: a wave per token
     (300, 8, 2, 1.0, 1, 1000, "f32", False),     # 250 words: a wave per token, a ragged last word group
     (500, 16, 3, 1.0, 2, 3000, "bf16", True),    # 375 words: two waves per token
     (200, 32, 4, 1.0, 4, 7168, "bf16", True),    # 896 words: four waves per token
-    # one pass, each token summing its copies' experts over the earlier tiles (E not a power of two)
+    # one pass, each block summing every expert's column (E not a power of two; above 1024)
     (600, 48, 4, 1.0, 4, 3000, "bf16", True),
     (800, 1536, 4, 1.0, 8, 7168, "bf16", True),
-    # one pass, each block summing every expert's column: at its limit of 64 counts a thread, and past it
+    # at the block sum's limit of 64 counts a thread, and past it (then each token sums its copies')
     (4160, 1024, 2, 1.0, 8, 8, "bf16", True),
     (4161, 1024, 2, 1.0, 8, 8, "bf16", True),
     (4160, 8, 2, 1.0, 1, 4096, "bf16", True),
-    # scan, slots and scatter apart: E not a power of two and 313 tiles (20 a scan lane)
-    (20000, 48, 2, 1.0, 4, 8, "bf16", True),
+    (20000, 48, 2, 1.0, 4, 8, "bf16", True),     # 313 tiles (20 a scan lane)
+    # scan, slots and scatter apart: 78 tiles of 2048 experts ahead, 4 copies a token
+    (5000, 2048, 4, 1.0, 8, 8, "bf16", True),
 ]
 
 
