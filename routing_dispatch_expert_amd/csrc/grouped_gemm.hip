@@ -79,10 +79,15 @@ constexpr int kGroupN = 8;
 constexpr bool kPersistAt = true;
 
 // Expert, first row and column tile of live tile `lid`. Without a row-tile
-// map every one of the E groups has ceil(C / BM) row tiles.
+// map every one of the E groups has ceil(C / BM) row tiles. With the kept
+// counts (and the map) an expert's kept rows are shared evenly by its row
+// tiles, in whole 32-row blocks: S = 32 ceil(kept / (32 n)) rows each for n =
+// ceil(kept / BM) tiles, so no tile is left nearly empty (1024 rows: four of
+// 256, not 320, 320, 320 and 64); *r1_out is then the tile's row end.
 template <int BM>
 __device__ inline void tile_coords(const int32_t* __restrict__ mtile_off, int E, int nt_count, int64_t lid,
-                                   int* e_out, int* m0_out, int* nt_out, int64_t C = 0) {
+                                   int* e_out, int* m0_out, int* nt_out, int64_t C = 0,
+                                   const int32_t* __restrict__ kept = nullptr, int* r1_out = nullptr) {
   const int mt_all = static_cast<int>((C + BM - 1) / BM);
   const int e = mtile_off ? owner_expert(mtile_off, E, static_cast<int>(lid / nt_count))
                           : static_cast<int>(lid / (static_cast<int64_t>(mt_all) * nt_count));
@@ -92,8 +97,16 @@ __device__ inline void tile_coords(const int32_t* __restrict__ mtile_off, int E,
   const int64_t grp = li / (static_cast<int64_t>(mte) * kGroupN);
   const int r = static_cast<int>(li - grp * mte * kGroupN);
   *e_out = e;
-  *m0_out = (r % mte) * BM;
   *nt_out = static_cast<int>(grp * kGroupN + r / mte);
+  if (kept && mtile_off) {
+    const int n = bucket_rows(kept, e, C);
+    const int S = 32 * ((n + 32 * mte - 1) / (32 * mte));  // <= BM, as mte = ceil(n / BM)
+    *m0_out = (r % mte) * S;
+    *r1_out = min(n, *m0_out + S);
+  } else {
+    *m0_out = (r % mte) * BM;
+    if (r1_out) *r1_out = INT_MAX;
+  }
 }
 
 // Live tile of block b when the first n live tiles are spread over the XCDs
@@ -125,6 +138,7 @@ constexpr int kMaxSplit = 8;
 
 struct Work {
   int e, m0, nt;
+  int r1;  // the tile's row end (INT_MAX: the group's)
   int64_t kb, ke;
   int s, c, ti;
 };
@@ -133,7 +147,8 @@ struct Work {
 // live tile b / slices, and the caller keeps the slices' results apart.
 template <int BM>
 __device__ inline bool work_of_block(const int32_t* __restrict__ mtile_off, int E, int nt_count, int64_t nk,
-                                     int G, Work* w, int64_t C = 0, int slices = 1, int64_t bid = -1) {
+                                     int G, Work* w, int64_t C = 0, int slices = 1, int64_t bid = -1,
+                                     const int32_t* __restrict__ kept = nullptr) {
   if (bid < 0) bid = blockIdx.x;
   const int64_t live = (mtile_off ? static_cast<int64_t>(mtile_off[E]) : E * ((C + BM - 1) / BM)) * nt_count;
   if (slices > 1) {
@@ -145,7 +160,7 @@ __device__ inline bool work_of_block(const int32_t* __restrict__ mtile_off, int 
     const int64_t pairs = nk / 2;
     w->kb = 2 * (w->c * pairs / slices);
     w->ke = 2 * ((w->c + 1) * pairs / slices);
-    tile_coords<BM>(mtile_off, E, nt_count, lid, &w->e, &w->m0, &w->nt, C);
+    tile_coords<BM>(mtile_off, E, nt_count, lid, &w->e, &w->m0, &w->nt, C, kept, &w->r1);
     return true;
   }
   int64_t rem = G > 0 ? live % G : 0;
@@ -177,7 +192,7 @@ __device__ inline bool work_of_block(const int32_t* __restrict__ mtile_off, int 
     w->kb = 2 * (w->c * pairs / s);
     w->ke = 2 * ((w->c + 1) * pairs / s);
   }
-  tile_coords<BM>(mtile_off, E, nt_count, lid, &w->e, &w->m0, &w->nt, C);
+  tile_coords<BM>(mtile_off, E, nt_count, lid, &w->e, &w->m0, &w->nt, C, kept, &w->r1);
   return true;
 }
 
@@ -534,7 +549,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   constexpr bool PERSIST = AT && kPersistAt;
   for (int64_t bid = blockIdx.x;; bid += gridDim.x) {
   Work wk;
-  if (!work_of_block<BM>(mtile_off, E, nt_count, K / BK, G, &wk, C, slices, bid)) return;
+  if (!work_of_block<BM>(mtile_off, E, nt_count, K / BK, G, &wk, C, slices, bid, AT ? nullptr : kept)) return;
   const int e = __builtin_amdgcn_readfirstlane(wk.e);
   const int m0 = __builtin_amdgcn_readfirstlane(wk.m0);
   const int nt = __builtin_amdgcn_readfirstlane(wk.nt);
@@ -545,7 +560,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int64_t kb = __builtin_amdgcn_readfirstlane(static_cast<int>(wk.kb));  // stages [kb, ke): even
   const int64_t ke = AT ? 2 * ((kr_e + 2 * BK - 1) / (2 * BK))
                         : __builtin_amdgcn_readfirstlane(static_cast<int>(wk.ke));
-  const int rows = __builtin_amdgcn_readfirstlane(kept ? bucket_rows(kept, e, C) : static_cast<int>(C));
+  // rows of this tile end at r1 (its share of the expert's kept rows); those
+  // past it belong to the next tile: never multiplied, loaded or stored here
+  const int rows = __builtin_amdgcn_readfirstlane(
+      min(kept ? bucket_rows(kept, e, C) : static_cast<int>(C), wk.r1));
   const int64_t n0 = static_cast<int64_t>(nt) * BNO;
 
   const int tid = threadIdx.x;
