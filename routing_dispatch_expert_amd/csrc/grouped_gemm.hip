@@ -513,7 +513,7 @@ __device__ inline void wait_vm_lgkm0() {
 // With AT as well (weight gradients, out[e] = A_e^T B_e over each expert's
 // kept rows), A is K-major too: element (k, m) of group e at
 // A + e a_es + k lda + aoff + m, B's at B0 + e b_es + k N + n; group e
-// contracts over kk[e] rows (rounded up to whole 128-row stage pairs, the
+// contracts over kk[e] rows (rounded up to whole 64-row stages, the
 // rows past kk[e] reading as zero), every group has C (= M) output rows, and
 // kept and mtile_off are NULL.
 template <bool SWIGLU, bool BT = false, bool F32OUT = false, bool AT = false, int NW = 4, int TM_ = 4,
@@ -558,8 +558,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int ti = __builtin_amdgcn_readfirstlane(wk.ti);
   const int kr_e = AT ? __builtin_amdgcn_readfirstlane(kk[e]) : 0;  // rows this group contracts over
   const int64_t kb = __builtin_amdgcn_readfirstlane(static_cast<int>(wk.kb));  // stages [kb, ke): even
-  const int64_t ke = AT ? 2 * ((kr_e + 2 * BK - 1) / (2 * BK))
-                        : __builtin_amdgcn_readfirstlane(static_cast<int>(wk.ke));
+  // with AT, whole 64-row stages over the group's kk[e] rows (an odd count ends
+  // with a single stage)
+  const int64_t ke = AT ? (kr_e + BK - 1) / BK : __builtin_amdgcn_readfirstlane(static_cast<int>(wk.ke));
   // rows of this tile end at r1 (its share of the expert's kept rows); those
   // past it belong to the next tile: never multiplied, loaded or stored here
   const int rows = __builtin_amdgcn_readfirstlane(
@@ -770,15 +771,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
     dma(As0, Bs0, kb);
     wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
-    if constexpr (EARLY) dma(As1, Bs1, kb + 1);  // ke - kb is even and positive
+    // ke - kb is even and positive, or, with AT, positive: a stage past the
+    // group's rows (one of an odd count's) is requested at most once and reads
+    // zeros (its rows lie past kk[e], outside the buffer ranges)
+    if constexpr (EARLY) dma(As1, Bs1, kb + 1);
     fload(As0, Bs0, 0, 0);
     int64_t k = kb;
-    for (; k + 2 < ke; k += 2) {  // then k + 3 < ke as well
+    for (; k + 2 < ke; k += 2) {  // then k + 3 < ke as well, or (AT, odd count) k + 3 == ke
       stage(T_{}, T_{}, As0, Bs0, As1, Bs1, k);
       stage(T_{}, T_{}, As1, Bs1, As0, Bs0, k + 1);
     }
     stage(T_{}, F_{}, As0, Bs0, As1, Bs1, k);
-    stage(F_{}, F_{}, As1, Bs1, As0, Bs0, k + 1);
+    // an odd count (AT) has no stage k + 1: its zeros are waited for above
+    // but not multiplied
+    if (!AT || k + 1 < ke) stage(F_{}, F_{}, As1, Bs1, As0, Bs0, k + 1);
   };
   if (ke > kb) {  // with AT a group that kept no row contracts over nothing: its block is zero
     if (ta >= TM || (TM == 4 && ta == 3))
