@@ -14,6 +14,10 @@ times from HIP events recorded by the library around each stage, the
 roofline of the dominant kernel, and the CPU oracle timed on a bounded sample
 of the same workload.
 
+With --graph the timed steps are replays of one layer call captured in a HIP
+graph (the library allocates nothing and never waits on the host, so a call
+can be captured as it is); the per-stage event steps stay eager.
+
 With --replicas EXTRA a step is one call of moe_layer_forward_replicated,
 with EXTRA replicas dealt to the most loaded experts of the same batch.
 
@@ -91,6 +95,8 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a reference kernel of known traffic for hardware counters: read a buffer "
                          "of this many MiB and write its bitwise complement to another")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one layer call captured in a HIP graph instead of eager calls")
     ap.add_argument("--device-weights", action="store_true",
                     help="draw the expert weights on the device (torch's seeded generator, the same laws) "
                          "instead of on the host: for counter passes, whose figures do not depend on the "
@@ -548,12 +554,29 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    timed_step = step
+    if args.graph:
+        # one layer call captured once (the library allocates nothing and
+        # never waits on the host), replayed on the same stream
+        graph, cap = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+        cap.wait_stream(stream)
+        eager_stream = stream
+        with torch.cuda.graph(graph, stream=cap):
+            stream = torch.cuda.current_stream()
+            step()
+        stream = eager_stream
+        torch.cuda.synchronize()
+        timed_step = graph.replay
+        for _ in range(args.warmup):
+            timed_step()
+        torch.cuda.synchronize()
+
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        step()
+        timed_step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -638,7 +661,7 @@ def main():
         "data": "synthetic (seeded Gaussian inputs and random-init weights of the named shape)",
         "config": {"workload": wl.name, "T": T, "d": d, "E": E, "k": k, "d_ff": d_ff, "cf": cf, "P": P,
                    "max_ranks": wl.max_ranks, "C": C, "N_kept": n_kept, "touched_experts": touched,
-                   "dropped": totals[0], **repl_cfg},
+                   "dropped": totals[0], "launch": "hip_graph_replay" if args.graph else "eager", **repl_cfg},
         "gpu_ms_per_step": round(gpu_ms, 4),
         "assignments_per_s": round(T * k * args.steps / wall, 1),
         "layer_ms_cold_median": layer_cold,
