@@ -825,14 +825,22 @@ int moe_layer_forward_replicated(const void* x, const void* W_router, const floa
   MOE_HIP_TRY(stage_mark(MOE_STAGE_ROUTE, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SLOTS, false, s), "event");
   // the instances' slots: as in the plain layer, in one pass with the row
-  // copies where the tile histogram is short enough
+  // copies where the tile histogram is short enough. Their scan also writes
+  // GEMM 1's row-tile map when its tiles differ from GEMM 2's, and clears the
+  // GEMMs' split-K arrival counters (each split tile's last block leaves its
+  // counter at zero again), so no GEMM needs a clearing launch.
+  const int bm_gu = moe::grouped_gemm_bm_gate_up(bf16, C, d);
+  int32_t* mtile_gu = bm_gu != bm ? p.mtile_gu : nullptr;
+  moe::SplitK sk = p.split;
+  sk.zeroed = sk.tick != nullptr;
+  const int n_clear = sk.tick ? moe::kSplitUnits : 0;
   const bool one_pass = moe::slot_scatter_fits(T, k, R);
   MOE_HIP_TRY(moe::launch_tile_hist(inst, T, k, R, p.tile_cnt, s, one_pass ? slot : nullptr,
                                     one_pass ? totals + 1 : nullptr),
               "tile histogram (instances)");
   if (!one_pass) {
     MOE_HIP_TRY(moe::launch_scan(p.tile_cnt, nt, R, C, P, d * eb, k, T, p.tile_off, p.routed2, kept, send, totals,
-                                 bm, p.mtile, src, s, p.place),
+                                 bm, p.mtile, src, s, p.place, bm_gu, mtile_gu, sk.tick, n_clear),
                 "scan (instances)");
     MOE_HIP_TRY(moe::launch_slots(inst, p.tile_off, T, k, R, C, slot, src, totals, s), "slots");
   }
@@ -840,20 +848,19 @@ int moe_layer_forward_replicated(const void* x, const void* W_router, const floa
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, false, s), "event");
   if (one_pass)
     MOE_HIP_TRY(moe::launch_slot_scatter(p.tile_cnt, R, C, P, d * eb, k, T, p.tile_off, p.routed2, kept, send, totals,
-                                         bm, p.mtile, 0, nullptr, nullptr, 0, x, inst, slot, src, buckets, s, p.place),
+                                         bm, p.mtile, bm_gu, mtile_gu, sk.tick, n_clear, x, inst, slot, src, buckets,
+                                         s, p.place),
                 "slots and scatter (instances)");
   else
     MOE_HIP_TRY(moe::launch_scatter_rows(x, inst, slot, T, k, C, d * eb, buckets, s), "scatter");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_SCATTER, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, false, s), "event");
-  const int bm_gu = moe::grouped_gemm_bm_gate_up(bf16, C, d);
-  if (bm_gu != bm) MOE_HIP_TRY(moe::launch_mtile_map(kept, R, C, bm_gu, p.mtile_gu, s), "tile map (gate, up)");
-  MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, bm_gu != bm ? p.mtile_gu : p.mtile, W_gate, W_up, R, C, d, d_ff,
-                                       bf16, p.h, s, p.wmap, &p.split),
+  MOE_HIP_TRY(moe::launch_gemm_gate_up(buckets, kept, mtile_gu ? mtile_gu : p.mtile, W_gate, W_up, R, C, d, d_ff,
+                                       bf16, p.h, s, p.wmap, &sk),
               "grouped gemm (gate, up)");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_GATE_UP, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, false, s), "event");
-  MOE_HIP_TRY(moe::launch_gemm_down(p.h, kept, p.mtile, W_down, R, C, d, d_ff, bf16, p.y, s, p.wmap, &p.split, bm),
+  MOE_HIP_TRY(moe::launch_gemm_down(p.h, kept, p.mtile, W_down, R, C, d, d_ff, bf16, p.y, s, p.wmap, &sk, bm),
               "grouped gemm (down)");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_DOWN, true, s), "event");
   MOE_HIP_TRY(stage_mark(MOE_STAGE_COMBINE, false, s), "event");

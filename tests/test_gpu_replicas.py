@@ -67,6 +67,8 @@ SMALL = [
      [2, 2, 1, 1, 1, 1, 1, 3]),
     (dict(T=600, d=64, E=4, k=1, d_ff=64, cf=0.1, bias="hot0"), [9, 1, 1, 1]),      # one hot expert
     (dict(T=2048, d=256, E=4, k=2, d_ff=512, cf=0.5), [2, 2, 2, 2]),                # 256-row tiles
+    # C = 400: 256-row tiles for GEMM 1, 128-row for GEMM 2 (two row-tile maps from the scan)
+    (dict(T=1280, d=256, E=4, k=1, d_ff=256, cf=1.25), [2, 1, 1, 1]),
     (dict(T=300, d=256, E=32, k=4, d_ff=96, cf=1.0, P=8, max_ranks=2, bias="zipf1.2"), None),
 ]
 
