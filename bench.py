@@ -473,6 +473,10 @@ def main():
         print(f"bench.py runs on one GPU only: the layer here has no multi-GPU path (asked for --gpus "
               f"{args.gpus})", file=sys.stderr)
         sys.exit(2)
+    if args.graph and args.backward:
+        print("bench.py --graph times the forward only (a backward call can be captured as well; the graph tests "
+              "do)", file=sys.stderr)
+        sys.exit(2)
     import numpy as np
     import torch
 
