@@ -375,16 +375,25 @@ def run_backward(args, wl, moe, torch, np, dev, to_dev, host_w):
         train_ms = timed(lambda: (forward_keep(), step()))
         print(f"[bench] forward keeping its activations: {keep_ms:.3f} ms/step; with the backward from that "
               f"state: {train_ms:.3f} ms/step", file=sys.stderr, flush=True)
-    import oracle
-    r = oracle.layer_forward(wl.x, wl.wr, lambda e: (host_w[0][e], host_w[1][e], host_w[2][e]), T, d, d_ff, E, k,
-                             cf, wl.dtype, P=P, bias=wl.bias_vec, tokens=np.arange(0), max_ranks=wl.max_ranks)
-    n_kept = int(r["kept"].sum())
+    # the kept copies (for the algorithmic flops) from the layer forward on the GPU
+    if kept_state is None:
+        kept_count = torch.empty(E, dtype=torch.int32, device=dev)
+        fws_bytes = moe.moe_workspace_size(T, d, d_ff, E, k, cf, P, wl.dtype)
+        fws = torch.empty(fws_bytes, dtype=torch.uint8, device=dev)
+        moe.moe_layer_forward(x, wr, bias, wg, wu, wd, T, d, d_ff, E, k, cf, P, wl.max_ranks, wl.dtype,
+                              torch.empty_like(x), {"kept_count": kept_count}, fws, fws_bytes, stream)
+        del fws
+    else:
+        kept_count = kept_state["kept_count"]
+    n_kept = int(kept_count.sum().item())
     algo = 12 * n_kept * d * d_ff  # dh, dX (two), dWd, dWg, dWu: 2 N d d_ff flop each
     done = algo + (0 if args.saved else 4 * n_kept * d * d_ff)  # plus the recomputed g and u
     tf = algo / gpu_ms / 1e9
     cpu = None
     if not args.no_cpu_baseline:
-        S = min(args.cpu_sample, T, 1024)  # the fp64 backward costs about 3x the forward per token
+        import oracle
+        # the fp64 backward costs about 3x the forward per token: at most 1024 tokens
+        S = min(args.cpu_sample or 1024, T, 1024)
         sub = moe_inputs_sample(wl, S)
         print(f"[bench] timing the CPU oracle backward on {S} tokens", file=sys.stderr, flush=True)
         times = []
