@@ -490,43 +490,63 @@ __global__ __launch_bounds__(256) void router_wgrad_gather_kernel(
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc[q] = 0.f;
   float dbs = 0.f;
-  constexpr int U = 8;  // copies whose loads are in flight together
-  for (int r = r0; r < r1; r += U) {
-    float cf[U], xv[U][8];
+  // Copies whose loads are in flight together: every load of a batch is
+  // issued without a branch, so the U row loads go out back to back instead
+  // of one wait per copy. A whole batch reads U consecutive list entries; the
+  // chunk's last, partial batch loads its last copy again in the places past
+  // the end and leaves those out of the sums (a select, not a branch, so the
+  // loads stay ahead of every use). A lane past the row's end loads column 0
+  // and stores nothing.
+  constexpr int U = 8;
+  const int64_t cl = live ? c0 : 0;
+  auto batch = [&](auto whole, int r) {
+    constexpr bool W = decltype(whole)::value;
+    float cf[U];
+    uint4 xw[U][BF16 ? 1 : 2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool ok = r + u < r1;  // uniform
-      const int ci = ok ? __builtin_amdgcn_readfirstlane(lcopy[off + r + u]) : 0;
-      const int64_t t = ok ? __builtin_amdgcn_readfirstlane(ltok[off + r + u]) : 0;
-      cf[u] = ok ? dl[ci] : 0.f;
-      if (ok && live) {
-        if constexpr (BF16) {
-          const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(x) + t * d + c0);
-          const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            xv[u][2 * q] = __uint_as_float(ww[q] << 16);
-            xv[u][2 * q + 1] = __uint_as_float(ww[q] & 0xffff0000u);
-          }
-        } else {
-          const float4* px = reinterpret_cast<const float4*>(static_cast<const float*>(x) + t * d + c0);
-          const float4 a = px[0], b = px[1];
-          xv[u][0] = a.x, xv[u][1] = a.y, xv[u][2] = a.z, xv[u][3] = a.w;
-          xv[u][4] = b.x, xv[u][5] = b.y, xv[u][6] = b.z, xv[u][7] = b.w;
-        }
+      const int rr = W ? r + u : min(r + u, r1 - 1);  // uniform
+      const int ci = __builtin_amdgcn_readfirstlane(lcopy[off + rr]);
+      const int64_t t = __builtin_amdgcn_readfirstlane(ltok[off + rr]);
+      cf[u] = dl[ci];
+      if constexpr (BF16) {
+        xw[u][0] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(x) + t * d + cl);
       } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) xv[u][q] = 0.f;
+        const uint4* px = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + t * d + cl);
+        xw[u][0] = px[0];
+        xw[u][1] = px[1];
       }
     }
+    // in copy order
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (r + u >= r1) break;
+      float xv[8];
+      if constexpr (BF16) {
+        const uint32_t ww[4] = {xw[u][0].x, xw[u][0].y, xw[u][0].z, xw[u][0].w};
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = fmaf(cf[u], xv[u][q], acc[q]);
-      dbs += cf[u];
+        for (int q = 0; q < 4; ++q) {
+          xv[2 * q] = __uint_as_float(ww[q] << 16);
+          xv[2 * q + 1] = __uint_as_float(ww[q] & 0xffff0000u);
+        }
+      } else {
+        const uint32_t ww[8] = {xw[u][0].x, xw[u][0].y, xw[u][0].z, xw[u][0].w,
+                                xw[u][1].x, xw[u][1].y, xw[u][1].z, xw[u][1].w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) xv[q] = __uint_as_float(ww[q]);
+      }
+      const bool in = W || r + u < r1;  // uniform
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float f = fmaf(cf[u], xv[q], acc[q]);
+        acc[q] = in ? f : acc[q];
+      }
+      const float b = dbs + cf[u];
+      dbs = in ? b : dbs;
     }
-  }
+  };
+  int r = r0;
+  for (; r + U <= r1; r += U) batch(std::true_type{}, r);
+  if (r < r1) batch(std::false_type{}, r);
   const int64_t row = wgrad_chunk_row(route_off, e, cc) + z;
   float* pz = part + row * d;
   if (live) {
@@ -558,14 +578,30 @@ __global__ __launch_bounds__(256) void router_wgrad_sum_kernel(const float* __re
     stride = static_cast<int64_t>(E) * width;
     return nchunk;
   };
+  // The chunks are added in chunk order; their loads go out eight at a time
+  // (a hot expert has hundreds of chunks, and a chain of dependent load-adds
+  // would wait out the memory latency once per chunk).
+  auto chunk_sum = [&](const float* p, int64_t first, int64_t stride, int nz) {
+    constexpr int G = 8;
+    float s = 0.f;
+    int z = 0;
+    for (; z + G <= nz; z += G) {
+      float v[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) v[g] = p[first + (z + g) * stride];
+#pragma unroll
+      for (int g = 0; g < G; ++g) s += v[g];
+    }
+    for (; z < nz; ++z) s += p[first + z * stride];
+    return s;
+  };
   for (int64_t o = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; o < n;
        o += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    float s = 0.f;
     const int e = static_cast<int>(o / d);
     int64_t first, stride;
     const int nz = at(e, d, first, stride);
     const int64_t i = o - static_cast<int64_t>(e) * d;
-    for (int z = 0; z < nz; ++z) s += part[first + z * stride + i];  // chunk order
+    const float s = chunk_sum(part, first + i, stride, nz);
     if (BF16)
       static_cast<bf16_t*>(dwr)[o] = f32_to_bf16(s);
     else
@@ -573,11 +609,9 @@ __global__ __launch_bounds__(256) void router_wgrad_sum_kernel(const float* __re
   }
   if (db && blockIdx.x == 0)
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
-      float s = 0.f;
       int64_t first, stride;
       const int nz = at(e, 1, first, stride);
-      for (int z = 0; z < nz; ++z) s += dbpart[first + z * stride];
-      db[e] = s;
+      db[e] = chunk_sum(dbpart, first, stride, nz);
     }
 }
 
