@@ -89,11 +89,17 @@ __device__ inline void tile_coords(const int32_t* __restrict__ mtile_off, int E,
                                    int* e_out, int* m0_out, int* nt_out, int64_t C = 0,
                                    const int32_t* __restrict__ kept = nullptr, int* r1_out = nullptr) {
   const int mt_all = static_cast<int>((C + BM - 1) / BM);
-  const int e = mtile_off ? owner_expert(mtile_off, E, static_cast<int>(lid / nt_count))
-                          : static_cast<int>(lid / (static_cast<int64_t>(mt_all) * nt_count));
+  // Without a row-tile map every group has the same tiles (the weight
+  // gradients, where a tile's cost follows its group's rows of K): the groups
+  // are dealt to the 8 XCDs in turn, so XCD x (which takes a contiguous eighth
+  // of the tile ids) holds groups x, x + 8, x + 16, ... rather than a run of
+  // neighbours, and a run of heavy experts is spread over all of them.
+  const int eg = mtile_off ? owner_expert(mtile_off, E, static_cast<int>(lid / nt_count))
+                           : static_cast<int>(lid / (static_cast<int64_t>(mt_all) * nt_count));
+  const int e = (mtile_off || E % 8) ? eg : (eg % (E / 8)) * 8 + eg / (E / 8);
   const int mte = mtile_off ? mtile_off[e + 1] - mtile_off[e] : mt_all;
   const int64_t li = lid - (mtile_off ? static_cast<int64_t>(mtile_off[e]) * nt_count
-                                      : static_cast<int64_t>(e) * mt_all * nt_count);
+                                      : static_cast<int64_t>(eg) * mt_all * nt_count);
   const int64_t grp = li / (static_cast<int64_t>(mte) * kGroupN);
   const int r = static_cast<int>(li - grp * mte * kGroupN);
   *e_out = e;
