@@ -1,6 +1,7 @@
 """The layer under HIP graph capture, through the C ABI: a captured
-moe_layer_forward (or moe_layer_backward) replayed several times gives the
-eager call's outputs bit for bit on every replay.
+moe_layer_forward, moe_layer_forward_replicated or moe_layer_backward
+replayed several times gives the eager call's outputs bit for bit on every
+replay.
 
 The library allocates nothing, never synchronises with the host and clears
 its own counters with kernels, so a serving loop may capture a layer call once
@@ -143,3 +144,44 @@ def test_captured_backward_replays_bit_for_bit():
                                g_out["dW_down"], ws, n, stream)
 
     _replays_match(lambda s: call(grads, dout, s), grads, lambda: call(other, dout2, None))
+
+
+REPLICATED_CASES = [
+    # 256-row tiles with a split last round over R = 9 instances (the instance
+    # scan clears the split-K arrival counters and writes GEMM 1's tile map)
+    (dict(T=2048, d=256, E=4, k=2, d_ff=512, cf=0.5), [3, 2, 2, 2]),
+    # a skewed route with a rank limit: instances placed over 8 ranks
+    (dict(T=512, d=256, E=32, k=4, d_ff=128, cf=1.0, P=8, max_ranks=2, bias="zipf1.2"), [4, 2] + [1] * 30),
+]
+
+
+@pytest.mark.parametrize("case,reps", REPLICATED_CASES, ids=["E4-R9-split", "E32-R36-P8-zipf"])
+def test_captured_replicated_forward_replays_bit_for_bit(case, reps):
+    say(f"graph replicated forward {case} replicas {reps}")
+    wl = moe_inputs.custom(seed=23, reject=False, **case)
+    other = moe_inputs.custom(seed=24, reject=False, **case)
+    T, d, E, k, P, d_ff, cf = wl.T, wl.d, wl.E, wl.k, wl.P, wl.d_ff, wl.cf
+    C = moe.moe_capacity(T, E, k, cf)
+    R = sum(reps)
+    replicas = torch.tensor(reps, dtype=torch.int32, device="cuda")
+    x, x2 = to_dev(wl.x, wl.dtype), to_dev(other.x, wl.dtype)
+    wr = to_dev(wl.wr, wl.dtype)
+    wg, wu, wd = _weights(wl)
+    b = None if wl.bias_vec is None else torch.from_numpy(wl.bias_vec).cuda()
+    i32 = dict(dtype=torch.int32, device="cuda")
+    out = {"out": torch.empty((T, d), dtype=x.dtype, device="cuda"), "topk_idx": torch.empty((T, k), **i32),
+           "topk_w": torch.empty((T, k), dtype=torch.float32, device="cuda"), "slot": torch.empty((T, k), **i32),
+           "instance": torch.empty((T, k), **i32), "src": torch.empty((R, C), **i32),
+           "routed_count": torch.empty(E, **i32), "kept_count": torch.empty(R, **i32),
+           "send_count": torch.empty(P, **i32), "totals": torch.empty(4, dtype=torch.int64, device="cuda"),
+           "buckets": torch.empty((R, C, d), dtype=x.dtype, device="cuda")}
+    other_out = {n: torch.empty_like(t) for n, t in out.items()}
+    n = moe.moe_replicated_workspace_size(T, d, d_ff, E, k, cf, P, R, wl.dtype)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+
+    def call(xx, o, stream):
+        moe.moe_layer_forward_replicated(xx, wr, b, wg, wu, wd, T, d, d_ff, E, k, cf, P, wl.max_ranks, replicas, R,
+                                         wl.dtype, o["out"], {k_: v for k_, v in o.items() if k_ != "out"}, ws, n,
+                                         stream)
+
+    _replays_match(lambda s: call(x, out, s), out, lambda: call(x2, other_out, None))
